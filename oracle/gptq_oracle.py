@@ -1,0 +1,392 @@
+"""GPTQ per-layer quantization solver -- plain fp64 oracle (numpy / LAPACK).
+
+TEST INFRASTRUCTURE ONLY (see the package docstring): never imported by the
+product path.
+
+Sources, cited by page title and section:
+
+* "GPTQ量化算法深度解析：从Hessian曲率到大模型单卡部署" (sheratonhq.com) --
+  §2.1 (second-order objective), §2.2 (OBS compensation formula), §2.4
+  (fixed order, lazy batch update, Cholesky), §3.1 (the four-step per-layer
+  flow: H = 2XX^T + lambda*I, Cholesky, blocks of 128 columns with
+  per-column scale / round / error accumulation and one update of the later
+  columns per block, save codes + scale/zero), §3.3 (group size, desc_act,
+  damp_percent = 0.01).
+* "通义千问1.5-1.8B-Chat-GPTQ-Int4模型压缩技术解析" (deepseek.csdn.net) --
+  §2.1 (min/max range split into 2^b levels), §2.2 (scale and zero point per
+  layer or group).
+* ai.lansai.wang GPTQ guide, section "bits、group_size、sym 与 desc_act
+  分别影响什么" (the quantize_config field table).
+* "gptq-for-llama" article (ainews.cool), "工程细节" (four 4-bit codes packed
+  per 16-bit integer).
+
+Notation: W is d_out x d_in (row = output channel, column = input channel);
+X is tokens x d_in; b = bits, maxq = 2^b - 1; g = group size; B = block size.
+
+Readings taken where the pages are silent or garbled (each is listed in the
+design notes of the repository):
+
+* H is the sum 2 * sum_t x_t x_t^T (no mean); lambda = damp * mean(diag H)
+  is added to every diagonal entry.
+* The compensation uses U, the upper Cholesky factor of H_d^{-1}
+  (H_d^{-1} = U^T U): err_c = (w_c - q_c) / U_cc and w_j -= err_c * U_cj for
+  the later columns j, which is the OBS update of §2.2 with the quantized
+  value restored in its numerator.
+* Asymmetric grid: xmin = min(0, min w), xmax = max(0, max w) over the
+  group's current values, scale = (xmax - xmin)/maxq, zero = rint(-xmin/scale);
+  an all-zero group uses xmin = -1, xmax = +1.  Symmetric grid:
+  amax = max(|xmin|, xmax) (1 if zero), scale = 2*amax/maxq, zero = 2^(b-1).
+* code = clip(rint(w / scale) + zero, 0, maxq) with round-half-to-even and a
+  true division; q = scale * (code - zero).
+* Group parameters are taken when the sweep reaches the group's first column,
+  from the group's current (already compensated) values; per-row
+  quantization is one group per row, taken at column 0.
+* act-order: perm = stable argsort of -diag(H) (undamped H); groups are g
+  consecutive columns in sweep order; g_idx[perm[k]] = k // g.
+* Outputs are returned in the original column order.
+* Packing: each output row is a little-endian bit stream along d_in; code k
+  occupies bits [b*k, b*k + b) of that stream, held in 32-bit words.
+"""
+from __future__ import annotations
+
+import numpy as np
+import scipy.linalg
+
+
+class NotPositiveDefinite(ArithmeticError):
+    """The damped Hessian is not positive definite (Cholesky failed)."""
+
+
+class NonFinite(ArithmeticError):
+    """An input held NaN or Inf."""
+
+
+class InvalidArgument(ValueError):
+    """Shapes or configuration outside what the method defines."""
+
+
+# ---------------------------------------------------------------------------
+# Step 1: the Hessian of the layer-reconstruction objective.
+# ---------------------------------------------------------------------------
+
+def hessian(X) -> np.ndarray:
+    """H = 2 * X^T X in float64, X given tokens-major (n_tok x d_in).
+
+    "GPTQ量化算法深度解析" §3.1 step 1 writes H = 2XX^T + lambda*I with X laid
+    out d_in x tokens; the same matrix is 2 * sum_t x_t x_t^T.  The damping
+    term is applied separately (damp_hessian).  ``X`` may be one array or an
+    iterable of token chunks; every chunk is widened to float64 exactly before
+    the product, so bf16/fp16/fp32 inputs lose nothing on the way in.
+    """
+    chunks = [X] if isinstance(X, np.ndarray) else X
+    H = None
+    for chunk in chunks:
+        x = np.asarray(chunk, dtype=np.float64)
+        if x.ndim != 2:
+            raise InvalidArgument("X must be 2-D (tokens x d_in)")
+        if not np.all(np.isfinite(x)):
+            raise NonFinite("X holds NaN or Inf")
+        if H is None:
+            H = np.zeros((x.shape[1], x.shape[1]), dtype=np.float64)
+        H += 2.0 * (x.T @ x)
+    if H is None:
+        raise InvalidArgument("no token chunks given")
+    return H
+
+
+# ---------------------------------------------------------------------------
+# act-order (desc_act): the column order.
+# ---------------------------------------------------------------------------
+
+def act_order_permutation(H: np.ndarray) -> np.ndarray:
+    """Column order for act-order: descending diag(H), ties to the lower index.
+
+    "GPTQ量化算法深度解析" §3.3 (desc_act): the columns are processed in order
+    of their activation magnitude, most influential first.  The key is
+    diag(H)_j = 2 * sum_t x_tj^2, the channel's activation energy, taken from
+    the undamped H (damping shifts every key equally).  perm[k] is the
+    original index of the k-th swept column.
+    """
+    return np.argsort(-np.diag(H), kind="stable").astype(np.int64)
+
+
+# ---------------------------------------------------------------------------
+# Step 2: damping and the Cholesky form of the inverse Hessian.
+# ---------------------------------------------------------------------------
+
+def damp_hessian(H: np.ndarray, damp: float) -> np.ndarray:
+    """H_d = H + lambda * I with lambda = damp * mean(diag H).
+
+    "GPTQ量化算法深度解析" §3.1 step 1 (the lambda*I term keeps H invertible
+    and stable) and §3.3 (damp_percent is a ratio on the diagonal, default
+    0.01, raised to 0.1 when H is near-singular).
+    """
+    d = H.shape[0]
+    lam = damp * np.mean(np.diag(H))
+    return H + lam * np.eye(d)
+
+
+def inverse_hessian_upper(Hd: np.ndarray) -> np.ndarray:
+    """U, upper triangular with positive diagonal, such that H_d^{-1} = U^T U.
+
+    "GPTQ量化算法深度解析" §2.4 (a Cholesky factorisation replaces repeated,
+    unstable inversion) and §3.1 step 2 (factor H once, lower triangular, and
+    reuse the factor).  Taken in three plain steps: L = chol(H_d) lower;
+    H_d^{-1} = L^{-T} L^{-1}; U = chol(H_d^{-1})^T.
+    """
+    if not np.all(np.isfinite(Hd)):
+        raise NonFinite("H holds NaN or Inf")
+    try:
+        L = np.linalg.cholesky(Hd)
+    except np.linalg.LinAlgError as exc:
+        raise NotPositiveDefinite(str(exc)) from None
+    d = Hd.shape[0]
+    Linv = scipy.linalg.solve_triangular(L, np.eye(d), lower=True)
+    Hinv = Linv.T @ Linv
+    try:
+        Lh = np.linalg.cholesky(Hinv)
+    except np.linalg.LinAlgError as exc:
+        raise NotPositiveDefinite(str(exc)) from None
+    return np.ascontiguousarray(Lh.T)
+
+
+# ---------------------------------------------------------------------------
+# Step 3: the quantizer (scale / zero, rounding).
+# ---------------------------------------------------------------------------
+
+def quant_params(wg: np.ndarray, bits: int, sym: bool):
+    """Per-row (scale, zero) of one group, wg being d_out x (group width).
+
+    "通义千问...GPTQ-Int4..." §2.1: take the range from min and max and split it
+    into 2^b equal levels; §2.2: one scale and zero point per layer or group.
+    ai.lansai.wang guide, field table: ``sym`` picks a range symmetric about 0
+    or an asymmetric one with a zero point.
+    """
+    maxq = 2 ** bits - 1
+    xmin = np.minimum(wg.min(axis=1), 0.0)
+    xmax = np.maximum(wg.max(axis=1), 0.0)
+    if sym:
+        amax = np.maximum(np.abs(xmin), xmax)
+        amax = np.where(amax == 0.0, 1.0, amax)
+        scale = 2.0 * amax / maxq
+        zero = np.full_like(scale, float(2 ** (bits - 1)))
+    else:
+        dead = (xmin == 0.0) & (xmax == 0.0)
+        xmin = np.where(dead, -1.0, xmin)
+        xmax = np.where(dead, 1.0, xmax)
+        scale = (xmax - xmin) / maxq
+        zero = np.rint(-xmin / scale)
+    return scale, zero
+
+
+def quantize_column(w: np.ndarray, scale: np.ndarray, zero: np.ndarray, bits: int):
+    """code = clip(rint(w/scale) + zero, 0, maxq); q = scale * (code - zero).
+
+    "GPTQ量化算法深度解析" §3.1 step 3 (round the column to the grid) and
+    "通义千问...GPTQ-Int4..." §2.2 (dequantize with scale and zero point).
+    """
+    maxq = 2 ** bits - 1
+    code = np.clip(np.rint(w / scale) + zero, 0.0, float(maxq))
+    q = scale * (code - zero)
+    return code, q
+
+
+# ---------------------------------------------------------------------------
+# Step 3: the blocked column sweep with error compensation.
+# ---------------------------------------------------------------------------
+
+def _check_block_group(d_in: int, group_size: int, block: int) -> int:
+    """Effective group width; per-row (group_size <= 0) is one group per row."""
+    if block <= 0:
+        raise InvalidArgument("block size must be positive")
+    if group_size <= 0:
+        return d_in
+    if group_size % block != 0 and block % group_size != 0:
+        raise InvalidArgument("group_size and block must divide one another")
+    return group_size
+
+
+def sweep(W: np.ndarray, U: np.ndarray, bits: int, group_size: int, sym: bool,
+          block: int = 128):
+    """Quantize the columns of W (already in sweep order) left to right.
+
+    "GPTQ量化算法深度解析" §2.4 (fixed order; lazy batch update: errors are
+    collected inside a block and the later columns updated once per block)
+    and §3.1 step 3 (blocks of 128 columns; inside a block, per column:
+    scale, round, accumulate the error; after the block, one update of the
+    later columns).  The per-column compensation is §2.2's OBS update written
+    with U (upper Cholesky factor of H_d^{-1}).
+
+    Returns (codes, scales, zeros, w_hat, row_loss), all in sweep order;
+    scales/zeros are [n_groups][d_out]; row_loss[r] = sum_c (w_c - q_c)^2 /
+    (2 U_cc^2).
+    """
+    if bits not in (2, 3, 4, 8):
+        raise InvalidArgument("bits must be 2, 3, 4 or 8")
+    W = np.array(W, dtype=np.float64, copy=True)
+    d_out, d_in = W.shape
+    g = _check_block_group(d_in, group_size, block)
+    n_groups = -(-d_in // g)
+    codes = np.zeros((d_out, d_in), dtype=np.int64)
+    w_hat = np.zeros((d_out, d_in), dtype=np.float64)
+    scales = np.zeros((n_groups, d_out), dtype=np.float64)
+    zeros = np.zeros((n_groups, d_out), dtype=np.float64)
+    row_loss = np.zeros(d_out, dtype=np.float64)
+    scale = zero = None
+
+    for i1 in range(0, d_in, block):
+        i2 = min(i1 + block, d_in)
+        W1 = W[:, i1:i2].copy()              # the block being swept
+        Err = np.zeros((d_out, i2 - i1))     # accumulated scaled errors
+        for c in range(i1, i2):
+            k = c - i1
+            if c % g == 0:
+                # The group's current values: the part inside this block sits
+                # in W1 (already compensated by earlier columns of the block),
+                # the part past the block sits in W (all earlier blocks' lazy
+                # updates applied).
+                end = min(c + g, d_in)
+                cur = np.hstack([W1[:, k:min(end, i2) - i1], W[:, i2:max(end, i2)]])
+                scale, zero = quant_params(cur, bits, sym)
+                scales[c // g] = scale
+                zeros[c // g] = zero
+            w = W1[:, k]
+            code, q = quantize_column(w, scale, zero, bits)
+            codes[:, c] = code.astype(np.int64)
+            w_hat[:, c] = q
+            ucc = U[c, c]
+            err = (w - q) / ucc
+            W1[:, k + 1:] -= np.outer(err, U[c, c + 1:i2])
+            Err[:, k] = err
+            row_loss += (w - q) ** 2 / (2.0 * ucc * ucc)
+        # lazy batch update of every later column
+        W[:, i2:] -= Err @ U[i1:i2, i2:]
+    return codes, scales, zeros, w_hat, row_loss
+
+
+# ---------------------------------------------------------------------------
+# The whole per-layer solver (steps 1-4).
+# ---------------------------------------------------------------------------
+
+def gptq_quantize(W, H=None, *, X=None, bits=4, group_size=128, sym=False,
+                  act_order=False, block=128, damp=0.01):
+    """Quantize one linear layer; returns a dict of outputs in original order.
+
+    "GPTQ量化算法深度解析" §3.1 (the four steps per layer) with §3.3's
+    options.  Give either H (d_in x d_in, the undamped 2 X^T X) or X.
+
+    Keys: codes (int64 d_out x d_in), scales / zeros ([n_groups][d_out]),
+    g_idx (d_in), perm (d_in, perm[k] = original column swept k-th), w_hat
+    (d_out x d_in), row_loss (sum_c (w_c-q_c)^2 / (2 U_cc^2) per row),
+    loss (||(W - W_hat) X^T||_F^2 = 1/2 tr(dW H dW^T) with the undamped H),
+    U (sweep order), H (undamped, original order).
+    """
+    W0 = np.asarray(W, dtype=np.float64)
+    if W0.ndim != 2:
+        raise InvalidArgument("W must be 2-D")
+    if not np.all(np.isfinite(W0)):
+        raise NonFinite("W holds NaN or Inf")
+    if H is None:
+        if X is None:
+            raise InvalidArgument("give H or X")
+        H = hessian(X)
+    H = np.asarray(H, dtype=np.float64)
+    d_out, d_in = W0.shape
+    if H.shape != (d_in, d_in):
+        raise InvalidArgument("H must be d_in x d_in")
+    if not np.all(np.isfinite(H)):
+        raise NonFinite("H holds NaN or Inf")
+
+    if act_order:
+        perm = act_order_permutation(H)
+    else:
+        perm = np.arange(d_in, dtype=np.int64)
+    Wp = W0[:, perm]
+    Hp = H[np.ix_(perm, perm)]
+
+    U = inverse_hessian_upper(damp_hessian(Hp, damp))
+    codes_s, scales, zeros, w_hat_s, row_loss = sweep(Wp, U, bits, group_size, sym, block)
+
+    g = d_in if group_size <= 0 else group_size
+    codes = np.empty_like(codes_s)
+    w_hat = np.empty_like(w_hat_s)
+    codes[:, perm] = codes_s
+    w_hat[:, perm] = w_hat_s
+    g_idx = np.empty(d_in, dtype=np.int64)
+    g_idx[perm] = np.arange(d_in) // g
+    return dict(codes=codes, scales=scales, zeros=zeros, g_idx=g_idx, perm=perm,
+                w_hat=w_hat, row_loss=row_loss, loss=layer_loss(W0, w_hat, H),
+                U=U, H=H)
+
+
+def dequantize(codes, scales, zeros, g_idx) -> np.ndarray:
+    """W_hat[r, j] = scale[g_idx[j], r] * (code[r, j] - zero[g_idx[j], r]).
+
+    "通义千问...GPTQ-Int4..." §2.2 (dequantize back with scale and zero point);
+    "GPTQ量化算法深度解析" §3.3 (act-order needs a gather at inference, here
+    the g_idx lookup).
+    """
+    codes = np.asarray(codes, dtype=np.float64)
+    s = np.asarray(scales, dtype=np.float64)[np.asarray(g_idx)].T
+    z = np.asarray(zeros, dtype=np.float64)[np.asarray(g_idx)].T
+    return s * (codes - z)
+
+
+def layer_loss(W, W_hat, H) -> np.ndarray:
+    """Per-row reconstruction error 1/2 * (w - w_hat) H (w - w_hat)^T.
+
+    With H = 2 X^T X this is ||(w - w_hat) X^T||^2, the layer-output error
+    that "GPTQ量化算法深度解析" §2.1 puts at the centre of the objective.
+    """
+    dW = np.asarray(W_hat, dtype=np.float64) - np.asarray(W, dtype=np.float64)
+    return 0.5 * np.einsum("ij,jk,ik->i", dW, np.asarray(H, dtype=np.float64), dW)
+
+
+# ---------------------------------------------------------------------------
+# Step 4: packing.
+# ---------------------------------------------------------------------------
+
+def words_per_row(d_in: int, bits: int) -> int:
+    return -(-(d_in * bits) // 32)
+
+
+def pack(codes: np.ndarray, bits: int) -> np.ndarray:
+    """Pack integer codes into little-endian bit streams of 32-bit words.
+
+    "gptq-for-llama" article, "工程细节": four 4-bit codes share one 16-bit
+    integer.  Generalised to b bits: per output row, code k occupies bits
+    [b*k, b*k + b) of a bit stream whose bit 0 is the LSB of word 0; a 3-bit
+    code may straddle two words.  Returns uint32 [d_out][words_per_row].
+    """
+    if bits not in (2, 3, 4, 8):
+        raise InvalidArgument("bits must be 2, 3, 4 or 8")
+    c = np.asarray(codes)
+    if c.min(initial=0) < 0 or c.max(initial=0) >= (1 << bits):
+        raise InvalidArgument("code outside [0, 2^bits)")
+    d_out, d_in = c.shape
+    nw = words_per_row(d_in, bits)
+    out = np.zeros((d_out, nw), dtype=np.uint64)
+    c = c.astype(np.uint64)
+    for k in range(d_in):
+        pos = bits * k
+        wi, sh = divmod(pos, 32)
+        out[:, wi] |= (c[:, k] << np.uint64(sh)) & np.uint64(0xFFFFFFFF)
+        if sh + bits > 32:
+            out[:, wi + 1] |= c[:, k] >> np.uint64(32 - sh)
+    return out.astype(np.uint32)
+
+
+def unpack(words: np.ndarray, bits: int, d_in: int) -> np.ndarray:
+    """Inverse of pack: read code k from bits [b*k, b*k + b) of the row stream."""
+    w = np.asarray(words).astype(np.uint64)
+    d_out = w.shape[0]
+    out = np.zeros((d_out, d_in), dtype=np.int64)
+    mask = np.uint64((1 << bits) - 1)
+    for k in range(d_in):
+        pos = bits * k
+        wi, sh = divmod(pos, 32)
+        v = w[:, wi] >> np.uint64(sh)
+        if sh + bits > 32:
+            v |= w[:, wi + 1] << np.uint64(32 - sh)
+        out[:, k] = (v & mask).astype(np.int64)
+    return out

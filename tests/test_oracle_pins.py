@@ -1,0 +1,427 @@
+"""Pins of the fp64 oracle to facts outside itself (CPU only).
+
+Each test ties the oracle to a hand-worked example, a closed form, a special
+case that reduces to a simpler textbook procedure, a brute-force rendering of
+the pages' OBS formula, or an exact identity of the method, chosen so that a
+dropped term, a wrong sign or index, or a transposed operand in the oracle
+fails at least one of them.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _rand_pd(rng, d, cond_spread=1.0):
+    A = rng.standard_normal((d, 2 * d + 3))
+    D = np.exp(cond_spread * rng.standard_normal(d))
+    A = A * D[:, None]
+    return 2.0 * A @ A.T
+
+
+# ---------------------------------------------------------------------------
+# Hand-worked examples (tests/golden)
+# ---------------------------------------------------------------------------
+
+def test_hand_two_column_example():
+    g = _load("hand_2col.json")
+    out = O.gptq_quantize(np.array(g["W"]), np.array(g["H"]), bits=g["bits"],
+                          group_size=g["group_size"], sym=g["sym"],
+                          act_order=g["act_order"], block=g["block"], damp=g["damp"])
+    np.testing.assert_array_equal(out["codes"], np.array(g["codes"]))
+    np.testing.assert_allclose(out["scales"], g["scales"], rtol=1e-15)
+    np.testing.assert_array_equal(out["zeros"], g["zeros"])
+    np.testing.assert_allclose(out["w_hat"], g["w_hat"], rtol=1e-15)
+    np.testing.assert_allclose(out["row_loss"], g["row_loss"], rtol=1e-13)
+    np.testing.assert_allclose(out["U"], g["U"], rtol=1e-14, atol=1e-16)
+    np.testing.assert_allclose(out["loss"], g["row_loss"], rtol=1e-13)
+
+
+def test_quant_grid_hand_cases():
+    for case in _load("quant_grid.json")["cases"]:
+        w = np.array([case["w"]])
+        s, z = O.quant_params(w, case["bits"], case["sym"])
+        assert s[0] == pytest.approx(case["scale"], rel=1e-15), case["note"]
+        assert z[0] == case["zero"], case["note"]
+        codes = [int(O.quantize_column(np.array([x]), s, z, case["bits"])[0][0]) for x in case["w"]]
+        assert codes == case["codes"], case["note"]
+
+
+def test_pack_hand_cases():
+    for case in _load("pack_examples.json")["cases"]:
+        codes = np.array(case["codes"])
+        words = O.pack(codes, case["bits"])
+        assert words.tolist() == case["words"], case["note"]
+        back = O.unpack(words, case["bits"], codes.shape[1])
+        np.testing.assert_array_equal(back, codes)
+
+
+# ---------------------------------------------------------------------------
+# Packing
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+@pytest.mark.parametrize("d_in", [1, 31, 32, 33, 96, 257])
+def test_pack_roundtrip(bits, d_in):
+    rng = np.random.default_rng(bits * 1000 + d_in)
+    codes = rng.integers(0, 2 ** bits, size=(5, d_in))
+    words = O.pack(codes, bits)
+    assert words.shape == (5, -(-d_in * bits // 32))
+    np.testing.assert_array_equal(O.unpack(words, bits, d_in), codes)
+    # bits past the last code stay zero
+    total = d_in * bits
+    if total % 32:
+        assert np.all(words[:, -1] >> np.uint32(total % 32) == 0)
+
+
+def test_pack_4bit_is_base16_digits():
+    """4-bit words are the base-16 numbers whose digits are the codes, low first."""
+    rng = np.random.default_rng(7)
+    codes = rng.integers(0, 16, size=(3, 64))
+    words = O.pack(codes, 4)
+    for r in range(3):
+        for m in range(8):
+            expect = sum(int(codes[r, 8 * m + t]) * 16 ** t for t in range(8))
+            assert int(words[r, m]) == expect
+
+
+# ---------------------------------------------------------------------------
+# Hessian
+# ---------------------------------------------------------------------------
+
+def test_hessian_explicit_loops():
+    rng = np.random.default_rng(3)
+    X = rng.standard_normal((7, 4))
+    H = O.hessian(X)
+    for i in range(4):
+        for j in range(4):
+            s = 0.0
+            for t in range(7):
+                s += X[t, i] * X[t, j]
+            assert H[i, j] == pytest.approx(2.0 * s, rel=1e-14, abs=1e-14)
+
+
+def test_hessian_chunks_and_psd():
+    rng = np.random.default_rng(4)
+    X = rng.standard_normal((300, 20))
+    H1 = O.hessian(X)
+    H2 = O.hessian([X[:100], X[100:257], X[257:]])
+    np.testing.assert_allclose(H1, H2, rtol=1e-13, atol=1e-12)
+    np.testing.assert_array_equal(H1, H1.T)
+    assert np.linalg.eigvalsh(H1).min() > -1e-9 * np.abs(H1).max()
+
+
+# ---------------------------------------------------------------------------
+# The Cholesky form of the inverse
+# ---------------------------------------------------------------------------
+
+def test_U_is_upper_factor_of_inverse():
+    rng = np.random.default_rng(5)
+    H = _rand_pd(rng, 30, 1.0)
+    Hd = O.damp_hessian(H, 0.01)
+    U = O.inverse_hessian_upper(Hd)
+    assert np.allclose(np.tril(U, -1), 0.0)
+    assert np.all(np.diag(U) > 0)
+    np.testing.assert_allclose(U.T @ U @ Hd, np.eye(30), atol=1e-10)
+
+
+def test_U_reverse_cholesky_identity():
+    """U = J chol(J H_d J)^{-1} J, J the reversal: the 'UL' route to the same factor."""
+    rng = np.random.default_rng(6)
+    for d in (1, 2, 9, 40):
+        Hd = O.damp_hessian(_rand_pd(rng, d, 1.5), 0.01)
+        U = O.inverse_hessian_upper(Hd)
+        J = np.eye(d)[::-1]
+        Lr = np.linalg.cholesky(J @ Hd @ J)
+        U2 = J @ np.linalg.inv(Lr) @ J
+        np.testing.assert_allclose(U, U2, rtol=1e-10, atol=1e-12 * np.abs(U).max())
+
+
+def test_damp_closed_form():
+    H = np.diag([1.0, 2.0, 3.0, 6.0]) + 0.1
+    Hd = O.damp_hessian(H, 0.5)
+    lam = 0.5 * np.mean(np.diag(H))
+    np.testing.assert_allclose(np.diag(Hd) - np.diag(H), lam)
+    np.testing.assert_array_equal(Hd - np.diag(np.diag(Hd)), H - np.diag(np.diag(H)))
+
+
+# ---------------------------------------------------------------------------
+# P-RTN: with a diagonal H there is nothing to compensate.
+# ---------------------------------------------------------------------------
+
+def _rtn_in_test(W, bits, g, sym):
+    """Round-to-nearest per group from the untouched weights, written out here."""
+    d_out, d_in = W.shape
+    maxq = 2 ** bits - 1
+    codes = np.zeros_like(W, dtype=np.int64)
+    for s in range(0, d_in, g):
+        blk = W[:, s:s + g]
+        lo = np.minimum(blk.min(1), 0)
+        hi = np.maximum(blk.max(1), 0)
+        if sym:
+            a = np.maximum(-lo, hi)
+            a[a == 0] = 1
+            scale = 2 * a / maxq
+            zero = np.full(d_out, 2 ** (bits - 1))
+        else:
+            both0 = (lo == 0) & (hi == 0)
+            lo[both0], hi[both0] = -1, 1
+            scale = (hi - lo) / maxq
+            zero = np.rint(-lo / scale)
+        codes[:, s:s + g] = np.clip(np.rint(blk / scale[:, None]) + zero[:, None], 0, maxq)
+    return codes
+
+
+@pytest.mark.parametrize("bits,g,sym", [(4, -1, False), (3, 16, False), (2, 8, True), (4, 64, False)])
+def test_identity_hessian_reduces_to_rtn(bits, g, sym):
+    rng = np.random.default_rng(10 + bits)
+    W = 0.02 * rng.standard_normal((9, 64))
+    H = 3.0 * np.eye(64)
+    out = O.gptq_quantize(W, H, bits=bits, group_size=g, sym=sym, block=32, damp=0.01)
+    gg = 64 if g <= 0 else g
+    np.testing.assert_array_equal(out["codes"], _rtn_in_test(W, bits, gg, sym))
+
+
+def test_diagonal_hessian_act_order_is_rtn_on_sorted_columns():
+    rng = np.random.default_rng(11)
+    W = rng.standard_normal((6, 48))
+    dg = rng.permutation(np.arange(1, 49)).astype(float)
+    out = O.gptq_quantize(W, np.diag(dg), bits=3, group_size=16, act_order=True, block=16)
+    order = np.argsort(-dg, kind="stable")
+    np.testing.assert_array_equal(out["perm"], order)
+    expect = np.empty_like(out["codes"])
+    expect[:, order] = _rtn_in_test(W[:, order], 3, 16, False)
+    np.testing.assert_array_equal(out["codes"], expect)
+    np.testing.assert_array_equal(out["g_idx"][order], np.arange(48) // 16)
+
+
+# ---------------------------------------------------------------------------
+# P-OBS: brute-force fixed-order OBS with explicit inverses.
+# ---------------------------------------------------------------------------
+
+def _obs_bruteforce(W, Hd, bits, g, sym):
+    """Fixed-order OBS: after each column, re-invert H_d over the remaining set F."""
+    W = W.astype(float).copy()
+    d_out, d = W.shape
+    maxq = 2 ** bits - 1
+    codes = np.zeros((d_out, d), dtype=np.int64)
+    qv = np.zeros((d_out, d))
+    for q in range(d):
+        if q % g == 0:
+            blk = W[:, q:q + g]
+            lo = np.minimum(blk.min(1), 0)
+            hi = np.maximum(blk.max(1), 0)
+            if sym:
+                a = np.maximum(-lo, hi)
+                a[a == 0] = 1
+                scale, zero = 2 * a / maxq, np.full(d_out, 2.0 ** (bits - 1))
+            else:
+                both0 = (lo == 0) & (hi == 0)
+                lo[both0], hi[both0] = -1, 1
+                scale = (hi - lo) / maxq
+                zero = np.rint(-lo / scale)
+        c = np.clip(np.rint(W[:, q] / scale) + zero, 0, maxq)
+        val = scale * (c - zero)
+        codes[:, q], qv[:, q] = c, val
+        F = list(range(q, d))
+        Hinv = np.linalg.inv(Hd[np.ix_(F, F)])
+        # delta_F = -(w_q - q) / [H_F^-1]_qq * [H_F^-1]_{:, q}
+        delta = -np.outer((W[:, q] - val) / Hinv[0, 0], Hinv[:, 0])
+        W[:, F] += delta
+        W[:, q] = val
+    return codes, qv
+
+
+@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("g", [-1, 2, 4])
+def test_matches_bruteforce_obs(seed, g):
+    rng = np.random.default_rng(100 + seed)
+    d = 2 + seed  # 2..7 columns
+    W = rng.standard_normal((5, d))
+    H = _rand_pd(rng, d, 0.8)
+    for act in (False, True):
+        out = O.gptq_quantize(W, H, bits=2, group_size=g, act_order=act, block=2, damp=0.01)
+        perm = out["perm"]
+        Hd = O.damp_hessian(H[np.ix_(perm, perm)], 0.01)
+        gg = d if g <= 0 else g
+        if g > 0 and 2 % g and g % 2:
+            continue
+        c_bf, q_bf = _obs_bruteforce(W[:, perm], Hd, 2, gg, False)
+        np.testing.assert_array_equal(out["codes"][:, perm], c_bf)
+        np.testing.assert_allclose(out["w_hat"][:, perm], q_bf, rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# P-B: lazy batching changes nothing.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("g", [-1, 16])
+def test_block_size_invariance(g):
+    rng = np.random.default_rng(20)
+    X = rng.standard_normal((400, 96)) @ (rng.standard_normal((96, 96)) / 10)
+    W = 0.02 * rng.standard_normal((11, 96))
+    ref = O.gptq_quantize(W, X=X, bits=3, group_size=g, block=96)
+    for B in (1, 8, 16, 32, 48):
+        if g > 0 and g % B and B % g:
+            continue
+        out = O.gptq_quantize(W, X=X, bits=3, group_size=g, block=B)
+        np.testing.assert_array_equal(out["codes"], ref["codes"])
+        np.testing.assert_allclose(out["w_hat"], ref["w_hat"], rtol=1e-12, atol=1e-15)
+        np.testing.assert_allclose(out["scales"], ref["scales"], rtol=1e-12)
+
+
+def test_invalid_block_group_combination():
+    W = np.zeros((2, 48))
+    with pytest.raises(O.InvalidArgument):
+        O.gptq_quantize(W, np.eye(48), group_size=12, block=8)
+
+
+# ---------------------------------------------------------------------------
+# P-loss: the sweep's running loss equals the quadratic form of the change.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("act", [False, True])
+def test_loss_identity(act):
+    rng = np.random.default_rng(30)
+    X = rng.standard_normal((500, 70)) @ (np.eye(70) + 0.3 * rng.standard_normal((70, 70)))
+    W = 0.05 * rng.standard_normal((13, 70))
+    out = O.gptq_quantize(W, X=X, bits=3, group_size=-1, act_order=act, block=16)
+    p = out["perm"]
+    Hd = O.damp_hessian(out["H"][np.ix_(p, p)], 0.01)
+    dW = out["w_hat"][:, p] - W[:, p]
+    quad = 0.5 * np.einsum("ij,jk,ik->i", dW, Hd, dW)
+    np.testing.assert_allclose(out["row_loss"], quad, rtol=1e-9)
+
+
+# ---------------------------------------------------------------------------
+# P-range and dequantization.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("bits,g,sym", [(2, 8, False), (3, 16, False), (4, -1, False), (4, 32, True), (8, 16, False)])
+def test_code_range_and_dequant(bits, g, sym):
+    rng = np.random.default_rng(40 + bits)
+    X = rng.standard_t(4, size=(300, 64))
+    W = 0.02 * rng.standard_normal((10, 64))
+    out = O.gptq_quantize(W, X=X, bits=bits, group_size=g, sym=sym, act_order=True, block=16)
+    maxq = 2 ** bits - 1
+    assert out["codes"].min() >= 0 and out["codes"].max() <= maxq
+    assert np.all(out["scales"] > 0)
+    assert np.all(out["zeros"] == np.rint(out["zeros"]))
+    assert np.all((out["zeros"] >= 0) & (out["zeros"] <= maxq))
+    np.testing.assert_array_equal(
+        O.dequantize(out["codes"], out["scales"], out["zeros"], out["g_idx"]), out["w_hat"])
+
+
+# ---------------------------------------------------------------------------
+# Invariances: scale of H, rows, act-order as a relabelling.
+# ---------------------------------------------------------------------------
+
+def test_hessian_scale_by_four_is_bit_identical():
+    rng = np.random.default_rng(50)
+    X = rng.standard_normal((256, 48))
+    H = O.hessian(X)
+    W = 0.02 * rng.standard_normal((7, 48))
+    a = O.gptq_quantize(W, H, bits=4, group_size=16, act_order=True, block=16)
+    b = O.gptq_quantize(W, 4.0 * H, bits=4, group_size=16, act_order=True, block=16)
+    for k in ("codes", "scales", "zeros", "w_hat", "perm", "g_idx"):
+        np.testing.assert_array_equal(a[k], b[k])
+
+
+def test_rows_are_independent():
+    rng = np.random.default_rng(60)
+    X = rng.standard_normal((300, 40))
+    W = 0.02 * rng.standard_normal((12, 40))
+    full = O.gptq_quantize(W, X=X, bits=3, group_size=8, block=8)
+    rows = np.array([9, 2, 2, 7, 0])
+    sub = O.gptq_quantize(W[rows], X=X, bits=3, group_size=8, block=8)
+    np.testing.assert_array_equal(sub["codes"], full["codes"][rows])
+    np.testing.assert_allclose(sub["w_hat"], full["w_hat"][rows], rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(sub["scales"], full["scales"][:, rows], rtol=1e-12)
+
+
+def test_act_order_is_natural_order_on_permuted_problem():
+    rng = np.random.default_rng(70)
+    X = rng.standard_normal((300, 40)) * np.exp(rng.standard_normal(40))
+    W = 0.02 * rng.standard_normal((6, 40))
+    H = O.hessian(X)
+    a = O.gptq_quantize(W, H, bits=4, group_size=8, act_order=True, block=8)
+    p = a["perm"]
+    assert np.all(np.diff(np.diag(H)[p]) <= 0)
+    b = O.gptq_quantize(W[:, p], H[np.ix_(p, p)], bits=4, group_size=8, act_order=False, block=8)
+    np.testing.assert_array_equal(a["codes"][:, p], b["codes"])
+    np.testing.assert_array_equal(a["w_hat"][:, p], b["w_hat"])
+    np.testing.assert_array_equal(a["scales"], b["scales"])
+
+
+def test_act_order_ties_go_to_lower_index():
+    H = np.diag([1.0, 3.0, 3.0, 2.0, 3.0])
+    np.testing.assert_array_equal(O.act_order_permutation(H), [1, 2, 4, 3, 0])
+    # many ties: the order is (descending key, ascending index), by definition
+    rng = np.random.default_rng(5)
+    keys = rng.integers(0, 7, size=500).astype(float)
+    expect = sorted(range(500), key=lambda j: (-keys[j], j))
+    np.testing.assert_array_equal(O.act_order_permutation(np.diag(keys)), expect)
+
+
+# ---------------------------------------------------------------------------
+# Ragged shapes and degenerate inputs.
+# ---------------------------------------------------------------------------
+
+def test_ragged_tail_blocks_and_groups():
+    rng = np.random.default_rng(80)
+    X = rng.standard_normal((400, 75))
+    W = 0.02 * rng.standard_normal((4, 75))
+    a = O.gptq_quantize(W, X=X, bits=4, group_size=16, block=32)
+    b = O.gptq_quantize(W, X=X, bits=4, group_size=16, block=16)
+    assert a["scales"].shape == (5, 4)
+    np.testing.assert_array_equal(a["codes"], b["codes"])
+
+
+def test_dead_channel_is_kept():
+    rng = np.random.default_rng(81)
+    X = rng.standard_normal((200, 10))
+    X[:, 3] = 0.0
+    W = rng.standard_normal((3, 10))
+    out = O.gptq_quantize(W, X=X, bits=4, group_size=-1, act_order=True)
+    assert out["perm"][-1] == 3  # energy 0 is swept last
+    assert np.all(np.isfinite(out["w_hat"]))
+
+
+def test_errors():
+    with pytest.raises(O.NotPositiveDefinite):
+        O.gptq_quantize(np.ones((2, 3)), np.zeros((3, 3)), damp=0.01)
+    with pytest.raises(O.NotPositiveDefinite):
+        O.gptq_quantize(np.ones((2, 2)), np.array([[1.0, 2.0], [2.0, 1.0]]), damp=0.0)
+    with pytest.raises(O.NonFinite):
+        O.gptq_quantize(np.array([[np.nan, 1.0]]), np.eye(2))
+    with pytest.raises(O.NonFinite):
+        O.hessian(np.array([[np.inf, 1.0]]))
+    with pytest.raises(O.InvalidArgument):
+        O.gptq_quantize(np.ones((2, 3)), np.eye(3), bits=5)
+
+
+# ---------------------------------------------------------------------------
+# Quality sanity (the method's purpose, not an exact pin).
+# ---------------------------------------------------------------------------
+
+def test_gptq_not_worse_than_rtn_on_correlated_inputs():
+    rng = np.random.default_rng(90)
+    X = rng.standard_normal((1000, 64)) @ rng.standard_normal((64, 64))
+    W = 0.02 * rng.standard_normal((32, 64))
+    H = O.hessian(X)
+    out = O.gptq_quantize(W, H, bits=3, group_size=-1, block=16)
+    s, z = O.quant_params(W, 3, False)
+    rtn = s[:, None] * (np.clip(np.rint(W / s[:, None]) + z[:, None], 0, 7) - z[:, None])
+    assert out["loss"].sum() < 0.5 * O.layer_loss(W, rtn, H).sum()
+    out8 = O.gptq_quantize(W, H, bits=8, group_size=-1, block=16)
+    assert out8["loss"].sum() < 1e-3 * out["loss"].sum()

@@ -1,0 +1,185 @@
+/*
+ * gptq.h -- C ABI of libgptq_mi355x.so, GPTQ's per-layer quantization solver
+ * written for AMD MI355X (gfx950).
+ *
+ * The method (sources cited by page title and section):
+ *   "GPTQ量化算法深度解析：从Hessian曲率到大模型单卡部署" (sheratonhq.com)
+ *     §2.2  OBS-style compensation of a column's quantization error into the
+ *           columns not yet quantized;
+ *     §2.4  fixed column order, lazy batch updates per block, Cholesky form;
+ *     §3.1  per layer: H = 2XX^T + lambda*I, Cholesky, blocks of 128 columns
+ *           (per column: scale, round, accumulate the error; one update of the
+ *           later columns per block), save codes + scale/zero;
+ *     §3.3  group size, desc_act (act-order), damp_percent (default 0.01).
+ *   "通义千问1.5-1.8B-Chat-GPTQ-Int4模型压缩技术解析" (deepseek.csdn.net) §2.1-2.2:
+ *     min/max range split into 2^b levels; scale and zero point per group.
+ *   ai.lansai.wang GPTQ guide, field table ("bits、group_size、sym 与 desc_act
+ *     分别影响什么"): bits, group_size, sym, desc_act, damp_percent.
+ *   "gptq-for-llama" article (ainews.cool), "工程细节": 4-bit codes packed
+ *     four to a 16-bit integer.
+ *
+ * Conventions shared by every entry point
+ *   - All array pointers are DEVICE pointers owned by the caller; the library
+ *     allocates no memory and keeps no state between calls.
+ *   - Matrices are row-major.  W is d_out x d_in (row = output channel);
+ *     X is n_tok x d_in (row = token).
+ *   - Work is enqueued on `stream` (0 = the null stream).  Calls are
+ *     asynchronous unless their comment says "synchronous".
+ *   - Errors are returned as gptq_status; nothing is thrown across the ABI.
+ *     Arguments are validated before anything is enqueued; on a non-OK
+ *     return from validation no device memory has been touched.
+ *   - The solver computes in float64 (codes are decided in float64, the
+ *     precision of the reference oracle); the Hessian's token products are
+ *     accumulated in float32 over chunks of tokens and summed in float64,
+ *     and its diagonal in float64.
+ *   - Calls that share a workspace must not overlap.
+ */
+#ifndef GPTQ_MI355X_H
+#define GPTQ_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GPTQ_OK = 0,
+    GPTQ_ERR_INVALID_ARG = 1,  /* null pointer, bad size, unsupported bits, bad group/block */
+    GPTQ_ERR_NOT_PD = 2,       /* damped Hessian not positive definite (pivot <= 0) */
+    GPTQ_ERR_NONFINITE = 3,    /* NaN/Inf found in H (hence in X) or in W */
+    GPTQ_ERR_WORKSPACE = 4,    /* workspace pointer null or smaller than the query says */
+    GPTQ_ERR_HIP = 5,          /* a HIP runtime call failed */
+    GPTQ_ERR_UNSUPPORTED = 6   /* valid request this build does not implement */
+} gptq_status;
+
+typedef enum { GPTQ_F32 = 0, GPTQ_F16 = 1, GPTQ_BF16 = 2 } gptq_dtype;
+
+/* Quantizer configuration (the quantize_config fields of the ai.lansai.wang
+ * field table; defaults per "GPTQ量化算法深度解析" §3.3). */
+typedef struct {
+    int32_t bits;        /* 2, 3, 4 or 8: codes take values 0 .. 2^bits - 1 */
+    int32_t group_size;  /* > 0: columns per (scale, zero); <= 0: one group per row */
+    int32_t sym;         /* 0: asymmetric range with zero point; 1: symmetric */
+    int32_t act_order;   /* 0: natural column order; 1: descending diag(H) (desc_act) */
+    int32_t block_size;  /* B, columns per lazy-update block (128); must divide, or be
+                            divided by, group_size when group_size > 0; 1..128 in this
+                            build (larger: GPTQ_ERR_UNSUPPORTED) */
+    double  damp;        /* lambda = damp * mean(diag H) is added to diag H (0.01) */
+} gptq_config;
+
+/* Fills *cfg with bits 4, group 128, asymmetric, natural order, block 128, damp 0.01. */
+void gptq_config_default(gptq_config* cfg);
+
+/* ------------------------------------------------------------------------
+ * Step 1 -- Hessian accumulation ("GPTQ量化算法深度解析" §3.1 step 1).
+ *
+ *   H[i][j] += 2 * sum_t X[t][i] * X[t][j]     for i <= j (upper triangle)
+ *
+ * H: d_in x d_in float64, row stride d_in.  Only entries with i <= j are
+ * read or written; the strict lower triangle is left untouched.  The caller
+ * zeroes H before the first call; repeated calls over token chunks sum up.
+ * X: n_tok x d_in of x_dtype with row stride ld_x elements (ld_x >= d_in).
+ * Token products are exact in float32 for bf16/fp16 inputs and accumulated
+ * in float32 over chunks of at most 4096 tokens, then added to H in float64
+ * in a fixed order; the diagonal is summed in float64.  fp32 inputs are
+ * accumulated in float64 throughout.  Deterministic (bit-reproducible).
+ * NaN/Inf in X propagate into diag(H) and are reported by gptq_prepare_hinv.
+ * workspace: gptq_hessian_workspace(n_tok, d_in) bytes (may be 0 -> NULL ok).
+ * ------------------------------------------------------------------------ */
+size_t gptq_hessian_workspace(int64_t n_tok, int64_t d_in);
+gptq_status gptq_hessian_accumulate(double* H, const void* X, gptq_dtype x_dtype,
+                                    int64_t n_tok, int64_t d_in, int64_t ld_x,
+                                    void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Step 2 -- column order, damping, Cholesky form of the inverse
+ * ("GPTQ量化算法深度解析" §2.4, §3.1 steps 1-2, §3.3 desc_act and damp).
+ *
+ *   perm  = identity, or the stable order of descending diag(H) (act_order);
+ *   Hp    = H[perm][perm];  H_d = Hp + lambda*I, lambda = damp * mean(diag H);
+ *   U     = upper-triangular with positive diagonal, H_d^{-1} = U^T U.
+ *
+ * In place: on entry H holds the upper triangle of the undamped Hessian
+ * (as left by gptq_hessian_accumulate); on OK return H holds U (row stride
+ * d_in, sweep order) with its strict lower triangle set to zero.
+ * perm: d_in int32, perm[k] = original index of the k-th swept column.
+ * U is obtained as R^{-1} where H_d = R R^T, R upper (a Cholesky
+ * factorisation of the index-reversed matrix), which equals the upper
+ * Cholesky factor of H_d^{-1} (the factor is unique).
+ * Synchronous: returns GPTQ_ERR_NONFINITE if H holds NaN/Inf and
+ * GPTQ_ERR_NOT_PD if a pivot is <= 0 (e.g. all-zero H, or damp = 0 with a
+ * singular H).  The library never raises damp by itself; retrying with a
+ * larger damp (0.1 is the pages' remedy) is the caller's choice.  On error
+ * the contents of H and perm are unspecified.
+ * workspace: gptq_prepare_hinv_workspace(d_in) bytes.
+ * ------------------------------------------------------------------------ */
+size_t gptq_prepare_hinv_workspace(int64_t d_in);
+gptq_status gptq_prepare_hinv(double* H, int64_t d_in, const gptq_config* cfg,
+                              int32_t* perm, void* workspace, size_t ws_bytes,
+                              hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Step 3 -- blocked column sweep with error compensation and lazy updates
+ * ("GPTQ量化算法深度解析" §2.2, §2.4, §3.1 step 3; grid per "通义千问...
+ * GPTQ-Int4" §2.1-2.2).
+ *
+ * Columns are swept in the order perm (U is in that order).  For sweep
+ * column c, with w the column's current values:
+ *   at the first column of each group: per row, xmin = min(0, min w_group),
+ *     xmax = max(0, max w_group) over the group's current values;
+ *     asym: scale = (xmax - xmin)/maxq, zero = rint(-xmin/scale)
+ *           (xmin = -1, xmax = 1 if both are 0);
+ *     sym:  scale = 2*max(|xmin|, xmax)/maxq (amax 0 -> 1), zero = 2^(bits-1);
+ *   code = clamp(rint(w/scale) + zero, 0, maxq), q = scale*(code - zero);
+ *   err  = (w - q)/U[c][c]; later columns j of the block: w_j -= err*U[c][j];
+ *   after each block [i1,i2): W[:, i2:] -= Err * U[i1:i2, i2:].
+ *
+ * W: d_out x d_in of w_dtype, row stride ld_w (>= d_in); not modified.
+ * U, perm: as returned by gptq_prepare_hinv (U row stride d_in).
+ * Outputs, all in ORIGINAL column order:
+ *   codes   d_out x d_in uint8 (row stride d_in);
+ *   scales, zeros   n_groups x d_out float32, [group][row], n_groups =
+ *                   ceil(d_in/group_size) (1 when group_size <= 0);
+ *   g_idx   d_in int32, the group of each original column (sweep position / g);
+ *   w_hat   (nullable) d_out x d_in float32, scale*(code - zero);
+ *   row_loss (nullable) d_out float64, sum_c (w_c - q_c)^2 / (2 U_cc^2).
+ * Synchronous at the end: returns GPTQ_ERR_INVALID_ARG if perm is not a
+ * permutation of 0..d_in-1 and GPTQ_ERR_NONFINITE if W holds NaN/Inf
+ * (outputs then unspecified).
+ * workspace: gptq_quantize_layer_workspace(d_out, d_in, cfg) bytes.
+ * ------------------------------------------------------------------------ */
+size_t gptq_quantize_layer_workspace(int64_t d_out, int64_t d_in, const gptq_config* cfg);
+gptq_status gptq_quantize_layer(const void* W, gptq_dtype w_dtype, int64_t d_out, int64_t d_in,
+                                int64_t ld_w, const double* U, const int32_t* perm,
+                                const gptq_config* cfg, uint8_t* codes, float* scales,
+                                float* zeros, int32_t* g_idx, float* w_hat, double* row_loss,
+                                void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Step 4 -- packing ("gptq-for-llama" article, "工程细节").
+ *
+ * Per row, code k occupies bits [bits*k, bits*k + bits) of a little-endian
+ * bit stream (bit 0 = least significant bit of word 0); a 3-bit code may
+ * straddle two words; bits past the last code are zero.
+ * codes: d_out x d_in uint8 (row stride d_in), values < 2^bits (higher bits
+ * are masked off).  packed: d_out x gptq_packed_words_per_row(d_in, bits)
+ * uint32.  bits: 2, 3, 4 or 8.
+ * ------------------------------------------------------------------------ */
+int64_t gptq_packed_words_per_row(int64_t d_in, int32_t bits);
+gptq_status gptq_pack(const uint8_t* codes, int64_t d_out, int64_t d_in, int32_t bits,
+                      uint32_t* packed, hipStream_t stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char* gptq_status_string(gptq_status status);
+
+/* Library version as "major.minor.patch" (static string). */
+const char* gptq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GPTQ_MI355X_H */

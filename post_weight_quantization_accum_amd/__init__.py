@@ -1,0 +1,181 @@
+"""GPTQ per-layer quantization solver for AMD MI355X (gfx950).
+
+Python face of libgptq_mi355x.so.  The functions below mirror the C ABI of
+``include/gptq.h`` one to one (same names without the ``gptq_`` prefix) and
+only marshal torch tensors (device memory) and the current HIP stream into
+the library; ``quantize`` chains the four calls for one layer.
+
+Import is cheap: the shared library is loaded on first use, and a missing
+library raises instead of falling back to anything else.
+"""
+from __future__ import annotations
+
+import ctypes
+
+from . import _lib
+from ._lib import (  # noqa: F401
+    BF16, F16, F32, Config, GPTQError, InvalidArgument, NonFinite, NotPositiveDefinite,
+    Unsupported, WorkspaceError, make_config, load, version, status_string,
+)
+
+__all__ = ["hessian_accumulate", "prepare_hinv", "quantize_layer", "pack", "quantize",
+           "packed_words_per_row", "make_config", "Config", "load"]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.float16:
+        return F16
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(stream=None):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _require_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("tensors must live on the GPU")
+
+
+def _workspace(nbytes: int, device):
+    torch = _torch()
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def hessian_accumulate(H, X, stream=None):
+    """H (d_in x d_in float64, upper triangle) += 2 X^T X; X is tokens x d_in."""
+    lib = load()
+    torch = _torch()
+    _require_cuda(H, X)
+    if H.dtype != torch.float64 or not H.is_contiguous():
+        raise TypeError("H must be a contiguous float64 tensor")
+    if X.dim() != 2 or X.stride(1) != 1:
+        raise ValueError("X must be 2-D with unit column stride")
+    n_tok, d_in = X.shape
+    if H.shape != (d_in, d_in):
+        raise ValueError("H must be d_in x d_in")
+    nws = lib.gptq_hessian_workspace(n_tok, d_in)
+    ws = _workspace(nws, H.device)
+    st = lib.gptq_hessian_accumulate(_ptr(H), _ptr(X), _dtype_code(X), n_tok, d_in, X.stride(0),
+                                     _ptr(ws), nws, _stream(stream))
+    _lib.check(st, "gptq_hessian_accumulate")
+    return H
+
+
+def prepare_hinv(H, cfg: Config, perm=None, workspace=None, stream=None):
+    """In place H -> U (upper Cholesky factor of the damped, permuted inverse); returns perm."""
+    lib = load()
+    torch = _torch()
+    _require_cuda(H)
+    if H.dtype != torch.float64 or not H.is_contiguous() or H.dim() != 2 or H.shape[0] != H.shape[1]:
+        raise TypeError("H must be a square contiguous float64 tensor")
+    d = H.shape[0]
+    if perm is None:
+        perm = torch.empty(d, dtype=torch.int32, device=H.device)
+    nws = lib.gptq_prepare_hinv_workspace(d)
+    ws = workspace if workspace is not None else _workspace(nws, H.device)
+    st = lib.gptq_prepare_hinv(_ptr(H), d, ctypes.byref(cfg), _ptr(perm), _ptr(ws),
+                               ws.numel() if ws is not None else 0, _stream(stream))
+    _lib.check(st, "gptq_prepare_hinv")
+    return perm
+
+
+def n_groups(d_in: int, group_size: int) -> int:
+    return -(-d_in // group_size) if group_size > 0 else 1
+
+
+def quantize_layer(W, U, perm, cfg: Config, want_w_hat=True, want_row_loss=True, workspace=None,
+                   out=None, stream=None):
+    """Column sweep; returns dict(codes, scales, zeros, g_idx[, w_hat][, row_loss]) in original order."""
+    lib = load()
+    torch = _torch()
+    _require_cuda(W, U, perm)
+    if W.dim() != 2 or W.stride(1) != 1:
+        raise ValueError("W must be 2-D with unit column stride")
+    d_out, d_in = W.shape
+    if U.dtype != torch.float64 or U.shape != (d_in, d_in) or not U.is_contiguous():
+        raise TypeError("U must be a contiguous d_in x d_in float64 tensor")
+    if perm.dtype != torch.int32 or perm.numel() != d_in:
+        raise TypeError("perm must be int32 of length d_in")
+    dev = W.device
+    ng = n_groups(d_in, cfg.group_size)
+    if out is None:
+        out = dict(codes=torch.empty((d_out, d_in), dtype=torch.uint8, device=dev),
+                   scales=torch.empty((ng, d_out), dtype=torch.float32, device=dev),
+                   zeros=torch.empty((ng, d_out), dtype=torch.float32, device=dev),
+                   g_idx=torch.empty(d_in, dtype=torch.int32, device=dev))
+        if want_w_hat:
+            out["w_hat"] = torch.empty((d_out, d_in), dtype=torch.float32, device=dev)
+        if want_row_loss:
+            out["row_loss"] = torch.empty(d_out, dtype=torch.float64, device=dev)
+    nws = lib.gptq_quantize_layer_workspace(d_out, d_in, ctypes.byref(cfg))
+    if nws == 0:
+        raise InvalidArgument(_lib.ERR_INVALID_ARG, "gptq_quantize_layer_workspace", "invalid shape or config")
+    ws = workspace if workspace is not None else _workspace(nws, dev)
+    st = lib.gptq_quantize_layer(_ptr(W), _dtype_code(W), d_out, d_in, W.stride(0), _ptr(U), _ptr(perm),
+                                 ctypes.byref(cfg), _ptr(out["codes"]), _ptr(out["scales"]), _ptr(out["zeros"]),
+                                 _ptr(out["g_idx"]), _ptr(out.get("w_hat")), _ptr(out.get("row_loss")),
+                                 _ptr(ws), ws.numel(), _stream(stream))
+    _lib.check(st, "gptq_quantize_layer")
+    return out
+
+
+def packed_words_per_row(d_in: int, bits: int) -> int:
+    return int(load().gptq_packed_words_per_row(d_in, bits))
+
+
+def pack(codes, bits: int, out=None, stream=None):
+    """codes (d_out x d_in uint8) -> packed uint32 words, per-row little-endian bit stream."""
+    lib = load()
+    torch = _torch()
+    _require_cuda(codes)
+    if codes.dtype != torch.uint8 or not codes.is_contiguous():
+        raise TypeError("codes must be contiguous uint8")
+    d_out, d_in = codes.shape
+    wpr = packed_words_per_row(d_in, bits)
+    if out is None:
+        out = torch.empty((d_out, wpr), dtype=torch.int32, device=codes.device)
+    st = lib.gptq_pack(_ptr(codes), d_out, d_in, bits, _ptr(out), _stream(stream))
+    _lib.check(st, "gptq_pack")
+    return out
+
+
+def quantize(W, *, X=None, H=None, cfg: Config | None = None, packed=True, stream=None):
+    """One layer end to end: Hessian (from X unless H is given), prepare_hinv, sweep, pack.
+
+    Returns the dict of quantize_layer plus ``perm`` and (if packed) ``packed``.
+    H, when given, is consumed (overwritten with U).
+    """
+    torch = _torch()
+    cfg = cfg or make_config()
+    d_in = W.shape[1]
+    if H is None:
+        if X is None:
+            raise ValueError("give X or H")
+        H = torch.zeros((d_in, d_in), dtype=torch.float64, device=W.device)
+        hessian_accumulate(H, X, stream=stream)
+    perm = prepare_hinv(H, cfg, stream=stream)
+    out = quantize_layer(W, H, perm, cfg, stream=stream)
+    out["perm"] = perm
+    if packed:
+        out["packed"] = pack(out["codes"], cfg.bits, stream=stream)
+    return out

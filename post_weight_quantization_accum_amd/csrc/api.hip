@@ -1,0 +1,129 @@
+// The C ABI of libgptq_mi355x: argument validation, workspace sizing and
+// dispatch to the kernels.  Declarations and contracts are in include/gptq.h.
+#include "internal.hpp"
+
+using namespace gptq;
+
+namespace {
+
+constexpr int64_t MAX_DIM = int64_t(1) << 20;   // per-dimension sanity bound
+
+bool valid_dtype(gptq_dtype dt) { return dt == GPTQ_F32 || dt == GPTQ_F16 || dt == GPTQ_BF16; }
+
+bool valid_bits(int32_t b) { return b == 2 || b == 3 || b == 4 || b == 8; }
+
+gptq_status check_config(const gptq_config* cfg) {
+    if (!cfg) return GPTQ_ERR_INVALID_ARG;
+    if (!valid_bits(cfg->bits)) return GPTQ_ERR_INVALID_ARG;
+    if (cfg->block_size < 1) return GPTQ_ERR_INVALID_ARG;
+    if (cfg->block_size > 128) return GPTQ_ERR_UNSUPPORTED;
+    if (cfg->group_size > 0 && (cfg->group_size % cfg->block_size) != 0 &&
+        (cfg->block_size % cfg->group_size) != 0)
+        return GPTQ_ERR_INVALID_ARG;
+    if (!(cfg->damp >= 0.0) || !(cfg->damp < 1e300)) return GPTQ_ERR_INVALID_ARG;
+    return GPTQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+void gptq_config_default(gptq_config* cfg) {
+    if (!cfg) return;
+    cfg->bits = 4;
+    cfg->group_size = 128;
+    cfg->sym = 0;
+    cfg->act_order = 0;
+    cfg->block_size = 128;
+    cfg->damp = 0.01;
+}
+
+const char* gptq_status_string(gptq_status st) {
+    switch (st) {
+        case GPTQ_OK: return "ok";
+        case GPTQ_ERR_INVALID_ARG: return "invalid argument";
+        case GPTQ_ERR_NOT_PD: return "damped Hessian is not positive definite";
+        case GPTQ_ERR_NONFINITE: return "non-finite value (NaN/Inf) in the input";
+        case GPTQ_ERR_WORKSPACE: return "workspace missing or too small";
+        case GPTQ_ERR_HIP: return "HIP runtime error";
+        case GPTQ_ERR_UNSUPPORTED: return "unsupported by this build";
+    }
+    return "unknown status";
+}
+
+const char* gptq_version(void) { return "0.1.0"; }
+
+size_t gptq_hessian_workspace(int64_t n_tok, int64_t d_in) {
+    (void)n_tok;
+    (void)d_in;
+    return 0;
+}
+
+gptq_status gptq_hessian_accumulate(double* H, const void* X, gptq_dtype x_dtype, int64_t n_tok, int64_t d_in,
+                                    int64_t ld_x, void* workspace, size_t ws_bytes, hipStream_t stream) {
+    (void)workspace;
+    (void)ws_bytes;
+    if (!H || !valid_dtype(x_dtype)) return GPTQ_ERR_INVALID_ARG;
+    if (d_in <= 0 || d_in > MAX_DIM || n_tok < 0 || ld_x < d_in) return GPTQ_ERR_INVALID_ARG;
+    if (n_tok > 0 && !X) return GPTQ_ERR_INVALID_ARG;
+    return hessian_launch(H, X, x_dtype, n_tok, d_in, ld_x, stream);
+}
+
+size_t gptq_prepare_hinv_workspace(int64_t d_in) {
+    if (d_in <= 0 || d_in > MAX_DIM) return 0;
+    return hinv_workspace_bytes(d_in);
+}
+
+gptq_status gptq_prepare_hinv(double* H, int64_t d_in, const gptq_config* cfg, int32_t* perm, void* workspace,
+                              size_t ws_bytes, hipStream_t stream) {
+    if (!H || !perm) return GPTQ_ERR_INVALID_ARG;
+    if (d_in <= 0 || d_in > MAX_DIM) return GPTQ_ERR_INVALID_ARG;
+    gptq_status st = check_config(cfg);
+    if (st != GPTQ_OK) return st;
+    if (!workspace || ws_bytes < hinv_workspace_bytes(d_in)) return GPTQ_ERR_WORKSPACE;
+    int flags[N_FLAGS] = {0, 0, 0, 0};
+    st = hinv_launch(H, d_in, cfg, perm, workspace, stream, flags);
+    if (st != GPTQ_OK) return st;
+    if (flags[FLAG_NONFINITE]) return GPTQ_ERR_NONFINITE;
+    if (flags[FLAG_NOT_PD]) return GPTQ_ERR_NOT_PD;
+    return GPTQ_OK;
+}
+
+size_t gptq_quantize_layer_workspace(int64_t d_out, int64_t d_in, const gptq_config* cfg) {
+    if (d_out <= 0 || d_in <= 0 || d_out > MAX_DIM || d_in > MAX_DIM) return 0;
+    if (check_config(cfg) != GPTQ_OK) return 0;
+    return sweep_workspace_bytes(d_out, d_in, cfg);
+}
+
+gptq_status gptq_quantize_layer(const void* W, gptq_dtype w_dtype, int64_t d_out, int64_t d_in, int64_t ld_w,
+                                const double* U, const int32_t* perm, const gptq_config* cfg, uint8_t* codes,
+                                float* scales, float* zeros, int32_t* g_idx, float* w_hat, double* row_loss,
+                                void* workspace, size_t ws_bytes, hipStream_t stream) {
+    if (!W || !U || !perm || !codes || !scales || !zeros || !g_idx) return GPTQ_ERR_INVALID_ARG;
+    if (!valid_dtype(w_dtype)) return GPTQ_ERR_INVALID_ARG;
+    if (d_out <= 0 || d_in <= 0 || d_out > MAX_DIM || d_in > MAX_DIM || ld_w < d_in) return GPTQ_ERR_INVALID_ARG;
+    gptq_status st = check_config(cfg);
+    if (st != GPTQ_OK) return st;
+    if (!workspace || ws_bytes < sweep_workspace_bytes(d_out, d_in, cfg)) return GPTQ_ERR_WORKSPACE;
+    int flags[N_FLAGS] = {0, 0, 0, 0};
+    st = sweep_launch(W, w_dtype, d_out, d_in, ld_w, U, perm, cfg, codes, scales, zeros, g_idx, w_hat, row_loss,
+                      workspace, stream, flags);
+    if (st != GPTQ_OK) return st;
+    if (flags[FLAG_BAD_PERM]) return GPTQ_ERR_INVALID_ARG;
+    if (flags[FLAG_NONFINITE]) return GPTQ_ERR_NONFINITE;
+    return GPTQ_OK;
+}
+
+int64_t gptq_packed_words_per_row(int64_t d_in, int32_t bits) {
+    if (d_in < 0 || !valid_bits(bits)) return -1;
+    return ceil_div(d_in * bits, 32);
+}
+
+gptq_status gptq_pack(const uint8_t* codes, int64_t d_out, int64_t d_in, int32_t bits, uint32_t* packed,
+                      hipStream_t stream) {
+    if (!codes || !packed || !valid_bits(bits)) return GPTQ_ERR_INVALID_ARG;
+    if (d_out <= 0 || d_in <= 0 || d_out > MAX_DIM || d_in > MAX_DIM) return GPTQ_ERR_INVALID_ARG;
+    return pack_launch(codes, d_out, d_in, bits, packed, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,39 @@
+// Internal launch wrappers shared by the C-ABI translation unit.
+#pragma once
+
+#include "common.hpp"
+
+namespace gptq {
+
+// C = alpha * A * op(B) + beta * C in float64 on MFMA (64x64 output tiles).
+// A: M x K row-major (lda); op(B) = B (K x N, ldb) or B^T (B is N x K, ldb).
+// lower_tiles: only 64x64 tiles with tile_row >= tile_col are computed
+// (M == N required).  beta == 0 never reads C.  C may alias the operand it
+// overwrites only when the tile covers that operand's whole K range
+// (K <= 64 and the aliased operand is the tile's own rows/columns).
+gptq_status launch_gemm_f64(hipStream_t s, int64_t M, int64_t N, int64_t K, double alpha,
+                            const double* A, int64_t lda, const double* B, int64_t ldb,
+                            bool transB, double beta, double* C, int64_t ldc, bool lower_tiles);
+
+// Hessian: H (upper) += 2 X^T X.
+gptq_status hessian_launch(double* H, const void* X, gptq_dtype dt, int64_t n_tok, int64_t d,
+                           int64_t ld_x, hipStream_t s);
+
+// Column order, damping, Cholesky of the reversed matrix, triangular inverse,
+// rotation into U.  ws layout described in chol.hip.
+size_t hinv_workspace_bytes(int64_t d);
+gptq_status hinv_launch(double* H, int64_t d, const gptq_config* cfg, int32_t* perm,
+                        void* ws, hipStream_t s, int* host_flags);
+
+// Column sweep with lazy updates; ws layout described in sweep.hip.
+size_t sweep_workspace_bytes(int64_t d_out, int64_t d_in, const gptq_config* cfg);
+gptq_status sweep_launch(const void* W, gptq_dtype dt, int64_t d_out, int64_t d_in, int64_t ld_w,
+                         const double* U, const int32_t* perm, const gptq_config* cfg,
+                         uint8_t* codes, float* scales, float* zeros, int32_t* g_idx,
+                         float* w_hat, double* row_loss, void* ws, hipStream_t s,
+                         int* host_flags);
+
+gptq_status pack_launch(const uint8_t* codes, int64_t d_out, int64_t d_in, int32_t bits,
+                        uint32_t* packed, hipStream_t s);
+
+}  // namespace gptq

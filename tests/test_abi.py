@@ -1,0 +1,97 @@
+"""The C ABI: the library loads, exports every declared symbol, validates arguments.
+
+CPU only: no call here reaches a kernel launch (every call is rejected by
+argument validation, which happens before any HIP call).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import post_weight_quantization_accum_amd as P
+from post_weight_quantization_accum_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gptq.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"\b(gptq_[a-z_0-9]+)\s*\(", src)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = P.load()
+    declared = _declared_functions()
+    assert len(declared) >= 10
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert sorted(_lib.EXPORTS) == declared
+
+
+def test_status_strings_and_version():
+    for st in range(7):
+        assert isinstance(P.status_string(st), str) and P.status_string(st)
+    assert re.match(r"^\d+\.\d+\.\d+$", P.version())
+
+
+def test_config_default():
+    lib = P.load()
+    c = P.Config()
+    lib.gptq_config_default(ctypes.byref(c))
+    assert (c.bits, c.group_size, c.sym, c.act_order, c.block_size, c.damp) == (4, 128, 0, 0, 128, 0.01)
+
+
+def test_workspace_queries():
+    lib = P.load()
+    c = P.make_config(bits=4, group_size=128, block=128)
+    assert lib.gptq_prepare_hinv_workspace(11008) >= 11008 * 11008 * 8
+    assert lib.gptq_quantize_layer_workspace(4096, 11008, ctypes.byref(c)) >= 4096 * 11008 * 9
+    assert lib.gptq_prepare_hinv_workspace(0) == 0
+    bad = P.make_config(group_size=96, block=128)
+    assert lib.gptq_quantize_layer_workspace(8, 384, ctypes.byref(bad)) == 0
+    assert lib.gptq_packed_words_per_row(11, 3) == 2
+    assert lib.gptq_packed_words_per_row(8, 4) == 1
+    assert lib.gptq_packed_words_per_row(8, 5) == -1
+
+
+def test_argument_validation_before_any_launch():
+    lib = P.load()
+    c = P.make_config()
+    n = ctypes.c_void_p(0)
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+    assert lib.gptq_hessian_accumulate(n, fake, 2, 10, 10, 10, n, 0, n) == _lib.ERR_INVALID_ARG
+    assert lib.gptq_hessian_accumulate(fake, fake, 7, 10, 10, 10, n, 0, n) == _lib.ERR_INVALID_ARG
+    assert lib.gptq_hessian_accumulate(fake, fake, 2, 10, 10, 5, n, 0, n) == _lib.ERR_INVALID_ARG
+    assert lib.gptq_prepare_hinv(n, 10, ctypes.byref(c), fake, fake, 1 << 30, n) == _lib.ERR_INVALID_ARG
+    assert lib.gptq_prepare_hinv(fake, 10, ctypes.byref(c), fake, n, 0, n) == _lib.ERR_WORKSPACE
+    assert lib.gptq_prepare_hinv(fake, 10, ctypes.byref(c), fake, fake, 16, n) == _lib.ERR_WORKSPACE
+    b5 = P.make_config(bits=5)
+    assert lib.gptq_prepare_hinv(fake, 10, ctypes.byref(b5), fake, fake, 1 << 30, n) == _lib.ERR_INVALID_ARG
+    big_b = P.make_config(group_size=256, block=256)
+    assert lib.gptq_prepare_hinv(fake, 10, ctypes.byref(big_b), fake, fake, 1 << 30, n) == _lib.ERR_UNSUPPORTED
+    mixed = P.make_config(group_size=96, block=128)
+    args = [fake, 2, 8, 384, 384, fake, fake, ctypes.byref(mixed), fake, fake, fake, fake, n, n, fake, 1 << 30, n]
+    assert lib.gptq_quantize_layer(*args) == _lib.ERR_INVALID_ARG
+    args = [fake, 2, 8, 384, 100, fake, fake, ctypes.byref(c), fake, fake, fake, fake, n, n, fake, 1 << 30, n]
+    assert lib.gptq_quantize_layer(*args) == _lib.ERR_INVALID_ARG  # ld_w < d_in
+    args = [fake, 2, 8, 384, 384, fake, fake, ctypes.byref(c), fake, fake, fake, fake, n, n, fake, 10, n]
+    assert lib.gptq_quantize_layer(*args) == _lib.ERR_WORKSPACE
+    neg = P.make_config(damp=-0.1)
+    args = [fake, 2, 8, 384, 384, fake, fake, ctypes.byref(neg), fake, fake, fake, fake, n, n, fake, 1 << 30, n]
+    assert lib.gptq_quantize_layer(*args) == _lib.ERR_INVALID_ARG
+    assert lib.gptq_pack(n, 4, 8, 4, fake, n) == _lib.ERR_INVALID_ARG
+    assert lib.gptq_pack(fake, 4, 8, 5, fake, n) == _lib.ERR_INVALID_ARG
+    assert lib.gptq_pack(fake, 0, 8, 4, fake, n) == _lib.ERR_INVALID_ARG
+
+
+def test_python_errors_map_status():
+    with pytest.raises(P.InvalidArgument):
+        _lib.check(_lib.ERR_INVALID_ARG, "x")
+    with pytest.raises(P.NotPositiveDefinite):
+        _lib.check(_lib.ERR_NOT_PD, "x")
+    with pytest.raises(P.NonFinite):
+        _lib.check(_lib.ERR_NONFINITE, "x")

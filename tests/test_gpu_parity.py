@@ -1,0 +1,268 @@
+"""HIP path vs the fp64 oracle on identical seeded inputs (needs an MI355X).
+
+Every call goes through the C ABI (via the ctypes binding).  Shapes span
+several tiles/blocks and ragged tails.  Tolerances:
+
+* Hessian: float32 accumulation over chunks of <= 4096 tokens with exact
+  bf16/fp16 products -> relative Frobenius error <= 1e-6 (measured ~1e-7);
+  the diagonal is summed in float64 -> relative error <= 1e-12.
+* prepare_hinv and the sweep run in float64, like the oracle: U within 1e-9
+  relative (rounding order only); codes bit-identical when both sides get the
+  same U; scales/zeros equal after rounding to float32 (1 ulp allowed).
+* End to end from X: >= 99.9% codes identical and every difference <= 1
+  (the pages' tolerance), loss within 1e-3 relative.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import post_weight_quantization_accum_amd as P
+from post_weight_quantization_accum_amd import synth
+
+from _util import compare_codes, to_torch
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _layer(d_out, d_in, n_tok, dtype="bf16", dist="t4", frac=0.01, scale=30.0, seed=1, sigma=0.02):
+    return synth.make_layer(d_out, d_in, n_tok, dtype=dtype, sigma_w=sigma, dist=dist,
+                            outlier_frac=frac, outlier_scale=scale, config=90, layer=seed)
+
+
+def _gpu_hessian(L):
+    X = to_torch(L.X, L.dtype)
+    d = X.shape[1]
+    H = torch.zeros((d, d), dtype=torch.float64, device=DEV)
+    P.hessian_accumulate(H, X)
+    torch.cuda.synchronize()
+    return H
+
+
+# ---------------------------------------------------------------------------
+# Hessian
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype,d,n", [("bf16", 300, 9000), ("f16", 257, 4500), ("f32", 130, 2100),
+                                       ("bf16", 128, 32), ("bf16", 1, 7), ("f16", 383, 8200)])
+def test_hessian_matches_oracle(dtype, d, n):
+    print(f"hessian {dtype} d={d} n={n}", flush=True)
+    L = _layer(4, d, n, dtype=dtype, seed=d)
+    Href = O.hessian(L.X_f64())
+    Hg = _gpu_hessian(L).cpu().numpy()
+    iu = np.triu_indices(d)
+    err = np.linalg.norm((Hg - Href)[iu]) / np.linalg.norm(Href[iu])
+    assert err <= 1e-6, err
+    dg = np.abs(np.diag(Hg) - np.diag(Href)) / np.abs(np.diag(Href)).max()
+    assert dg.max() <= 1e-12
+    assert np.all(np.tril(Hg, -1) == 0.0)  # strict lower untouched
+
+
+def test_hessian_accumulates_over_calls_and_odd_stride():
+    L = _layer(4, 200, 6000, dtype="bf16", seed=5)
+    X = to_torch(L.X, "bf16")
+    H1 = torch.zeros((200, 200), dtype=torch.float64, device=DEV)
+    P.hessian_accumulate(H1, X[:2500])
+    P.hessian_accumulate(H1, X[2500:])
+    # odd row stride: a column slice of a wider buffer
+    wide = torch.zeros((6000, 201), dtype=torch.bfloat16, device=DEV)
+    wide[:, :200] = X
+    H2 = torch.zeros((200, 200), dtype=torch.float64, device=DEV)
+    P.hessian_accumulate(H2, wide[:, :200])
+    Href = O.hessian(L.X_f64())
+    iu = np.triu_indices(200)
+    for H in (H1, H2):
+        Hg = H.cpu().numpy()
+        assert np.linalg.norm((Hg - Href)[iu]) / np.linalg.norm(Href[iu]) <= 1e-6
+
+
+def test_hessian_deterministic():
+    L = _layer(4, 260, 5000, dtype="bf16", seed=6)
+    a = _gpu_hessian(L).cpu().numpy()
+    b = _gpu_hessian(L).cpu().numpy()
+    assert np.array_equal(a, b)
+
+
+# ---------------------------------------------------------------------------
+# prepare_hinv: order, damping, U
+# ---------------------------------------------------------------------------
+
+def _gpu_prepare(Hfull, cfg):
+    d = Hfull.shape[0]
+    H = torch.from_numpy(np.triu(Hfull)).to(DEV)
+    perm = P.prepare_hinv(H, cfg)
+    torch.cuda.synchronize()
+    return H.cpu().numpy(), perm.cpu().numpy()
+
+
+@pytest.mark.parametrize("d,act", [(1, False), (2, True), (63, True), (64, False), (65, True),
+                                   (200, True), (333, False)])
+def test_prepare_hinv_matches_oracle(d, act):
+    print(f"prepare_hinv d={d} act={act}", flush=True)
+    L = _layer(4, d, max(3 * d, 500), dtype="f32", dist="gauss_mix", frac=0.0, seed=d + 1)
+    H = O.hessian(L.X_f64())
+    cfg = P.make_config(act_order=act, damp=0.01)
+    Ug, perm = _gpu_prepare(H, cfg)
+    p = O.act_order_permutation(H) if act else np.arange(d)
+    assert np.array_equal(perm, p)
+    Uref = O.inverse_hessian_upper(O.damp_hessian(H[np.ix_(p, p)], 0.01))
+    assert np.all(np.tril(Ug, -1) == 0.0)
+    err = np.abs(Ug - Uref).max() / np.abs(Uref).max()
+    assert err <= 1e-9, err
+
+
+def test_act_order_ties_and_dead_channels():
+    d = 150
+    # three tie classes, one of them all-zero (dead channels)
+    H = np.diag(np.repeat([5.0, 3.0, 0.0], 50)[np.random.default_rng(1).permutation(d)])
+    cfg = P.make_config(act_order=True, damp=0.1)
+    Ug, perm = _gpu_prepare(H, cfg)
+    assert np.array_equal(perm, O.act_order_permutation(H))
+
+
+def test_not_pd_and_nonfinite():
+    cfg = P.make_config(damp=0.01)
+    with pytest.raises(P.NotPositiveDefinite):
+        _gpu_prepare(np.zeros((70, 70)), cfg)
+    bad = np.eye(40)
+    bad[3, 5] = bad[5, 3] = 2.0
+    with pytest.raises(P.NotPositiveDefinite):
+        _gpu_prepare(bad, P.make_config(damp=0.0))
+    nan = np.eye(40)
+    nan[2, 30] = np.nan
+    with pytest.raises(P.NonFinite):
+        _gpu_prepare(nan, cfg)
+
+
+# ---------------------------------------------------------------------------
+# Column sweep fed the oracle's U
+# ---------------------------------------------------------------------------
+
+def _sweep_case(d_out, d_in, bits, g, act, sym=False, block=128, dtype="bf16", seed=0):
+    L = _layer(d_out, d_in, max(2 * d_in, 1000), dtype=dtype, seed=100 + seed)
+    H = O.hessian(L.X_f64())
+    ref = O.gptq_quantize(L.W_f64(), H, bits=bits, group_size=g, sym=sym, act_order=act, block=block)
+    cfg = P.make_config(bits=bits, group_size=g, sym=sym, act_order=act, block=block)
+    W = to_torch(L.W, dtype)
+    U = torch.from_numpy(ref["U"]).to(DEV)
+    perm = torch.from_numpy(ref["perm"].astype(np.int32)).to(DEV)
+    out = P.quantize_layer(W, U, perm, cfg)
+    torch.cuda.synchronize()
+    return ref, {k: v.cpu().numpy() for k, v in out.items()}
+
+
+@pytest.mark.parametrize("d_out,d_in,bits,g,act,sym,block", [
+    (100, 300, 4, 128, True, False, 128),
+    (64, 256, 4, -1, False, False, 128),
+    (130, 384, 3, 64, True, False, 128),
+    (70, 200, 2, 32, False, False, 64),
+    (33, 259, 4, 256, True, False, 128),   # group spans two blocks; ragged tail
+    (40, 96, 4, 16, False, True, 32),      # symmetric
+    (20, 75, 8, 25, False, False, 25),     # odd sizes: sub-block width 1
+    (5, 40, 3, 12, True, False, 4),        # sub-block width 4
+])
+def test_sweep_matches_oracle_given_U(d_out, d_in, bits, g, act, sym, block):
+    print(f"sweep {d_out}x{d_in} b{bits} g{g} act{act} sym{sym} B{block}", flush=True)
+    ref, got = _sweep_case(d_out, d_in, bits, g, act, sym, block, seed=d_in)
+    assert np.array_equal(got["codes"], ref["codes"])
+    assert np.array_equal(got["g_idx"], ref["g_idx"])
+    np.testing.assert_allclose(got["scales"], ref["scales"].astype(np.float32), rtol=2e-7)
+    np.testing.assert_array_equal(got["zeros"], ref["zeros"].astype(np.float32))
+    np.testing.assert_allclose(got["w_hat"], ref["w_hat"].astype(np.float32), rtol=2e-7, atol=1e-30)
+    np.testing.assert_allclose(got["row_loss"], ref["row_loss"], rtol=1e-9)
+
+
+def test_sweep_fp16_and_fp32_weights():
+    for dtype in ("f16", "f32"):
+        ref, got = _sweep_case(48, 256, 4, 128, True, dtype=dtype, seed=7)
+        assert np.array_equal(got["codes"], ref["codes"]), dtype
+
+
+def test_sweep_nonfinite_weight():
+    L = _layer(8, 128, 500)
+    H = O.hessian(L.X_f64())
+    ref = O.gptq_quantize(L.W_f64(), H)
+    W = to_torch(L.W, "bf16")
+    W[3, 7] = float("nan")
+    with pytest.raises(P.NonFinite):
+        P.quantize_layer(W, torch.from_numpy(ref["U"]).to(DEV),
+                         torch.from_numpy(ref["perm"].astype(np.int32)).to(DEV), P.make_config())
+
+
+# ---------------------------------------------------------------------------
+# Packing
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+@pytest.mark.parametrize("d_in", [1, 31, 100, 257, 1024])
+def test_pack_matches_oracle(bits, d_in):
+    rng = np.random.default_rng(bits * 7 + d_in)
+    codes = rng.integers(0, 2 ** bits, size=(37, d_in)).astype(np.uint8)
+    got = P.pack(torch.from_numpy(codes).to(DEV), bits).cpu().numpy().view(np.uint32)
+    assert np.array_equal(got, O.pack(codes, bits))
+
+
+# ---------------------------------------------------------------------------
+# End to end from X
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("d_out,d_in,n,dtype,bits,g,act", [
+    (256, 256, 2048, "f32", 4, -1, False),      # workload 1, full size
+    (192, 640, 8192, "bf16", 4, 128, True),     # workload-3 recipe, reduced
+    (150, 512, 8192, "f16", 3, 128, False),     # workload-2/5 recipe, reduced
+    (96, 448, 6000, "bf16", 2, 64, True),       # workload-4 recipe, reduced
+])
+def test_end_to_end(d_out, d_in, n, dtype, bits, g, act):
+    print(f"e2e {d_out}x{d_in} n={n} {dtype} b{bits} g{g} act{act}", flush=True)
+    if dtype == "f32":
+        L = synth.make_layer(d_out, d_in, n, dtype="f32", sigma_w=0.02, dist="gauss_mix",
+                             outlier_count=4, outlier_scale=20.0, config=1, layer=0)
+    else:
+        L = _layer(d_out, d_in, n, dtype=dtype, frac=0.005, scale=50.0, seed=d_in)
+    ref = O.gptq_quantize(L.W_f64(), X=L.X_f64(), bits=bits, group_size=g, act_order=act)
+    cfg = P.make_config(bits=bits, group_size=g, act_order=act)
+    out = P.quantize(to_torch(L.W, dtype), X=to_torch(L.X, dtype), cfg=cfg)
+    torch.cuda.synchronize()
+    got = {k: v.cpu().numpy() for k, v in out.items()}
+    same, mx = compare_codes(got["codes"], ref["codes"])
+    assert same >= 0.999 and mx <= 1, (same, mx)
+    loss_g = O.layer_loss(L.W_f64(), got["w_hat"].astype(np.float64), ref["H"]).sum()
+    assert abs(loss_g - ref["loss"].sum()) <= 1e-3 * ref["loss"].sum()
+    words = got["packed"].view(np.uint32)
+    assert np.array_equal(words, O.pack(got["codes"], bits))
+    print(f"  identical {same:.6f} max diff {mx}", flush=True)
+
+
+def test_scale_invariance_and_row_subset_on_gpu():
+    L = _layer(64, 256, 3000, seed=11)
+    H = O.hessian(L.X_f64())
+    cfg = P.make_config(bits=4, group_size=64, act_order=True)
+    W = to_torch(L.W, "bf16")
+    outs = []
+    for f in (1.0, 4.0):
+        Ht = torch.from_numpy(np.triu(H) * f).to(DEV)
+        outs.append({k: v.cpu().numpy() for k, v in P.quantize(W, H=Ht, cfg=cfg).items()})
+    for k in ("codes", "scales", "zeros", "perm", "g_idx"):
+        assert np.array_equal(outs[0][k], outs[1][k]), k
+    rows = torch.tensor([5, 63, 0, 17], device=DEV)
+    sub = P.quantize(W[rows].contiguous(), H=torch.from_numpy(np.triu(H)).to(DEV), cfg=cfg)
+    assert np.array_equal(sub["codes"].cpu().numpy(), outs[0]["codes"][rows.cpu().numpy()])
+
+
+def test_sweep_rejects_bad_perm():
+    L = _layer(8, 64, 500)
+    H = O.hessian(L.X_f64())
+    ref = O.gptq_quantize(L.W_f64(), H, group_size=32, block=32)
+    W = to_torch(L.W, "bf16")
+    U = torch.from_numpy(ref["U"]).to(DEV)
+    cfg = P.make_config(group_size=32, block=32)
+    dup = torch.arange(64, dtype=torch.int32, device=DEV)
+    dup[5] = 6
+    with pytest.raises(P.InvalidArgument):
+        P.quantize_layer(W, U, dup, cfg)
+    oob = torch.arange(64, dtype=torch.int32, device=DEV)
+    oob[9] = 64
+    with pytest.raises(P.InvalidArgument):
+        P.quantize_layer(W, U, oob, cfg)

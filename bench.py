@@ -1,0 +1,215 @@
+"""Benchmark: GPTQ layer quantization of the 4096x11008 (LLaMA-7B down_proj) layer.
+
+One step = the whole per-layer path on one GPU, inputs resident in HBM:
+zero H, Hessian accumulation over 262144 bf16 tokens, act-order + damping +
+Cholesky/inverse, the blocked column sweep with lazy updates (4-bit, group
+128), and packing.  Prints one JSON line (see the keys below).
+
+    python bench.py [--gpus 1] [--steps 5] [--warmup 2] [--no-cpu-baseline]
+
+The CPU baseline is the fp64 oracle on a bounded sample of the same layer
+(token, row and column subsets, scaled to weights/s; the sample is stated in
+the output).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "GPTQ layer-quantize ms & weights/sec (4096×11008, 4-bit g128); % MFMA/HBM peak"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_F64_TFLOPS = 78.6         # MI355X fp64 (matrix and vector)
+PEAK_HBM_GBS = 8000.0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--tokens", type=int, default=None, help="override the token count (testing only)")
+    return ap.parse_args()
+
+
+def cpu_baseline(layer_w, layer_x, d_out, d_in, n_tok, q):
+    """Time the oracle on a bounded sample and scale to weights/s of the full layer."""
+    import threadpoolctl
+
+    import oracle as O
+
+    cores = len(os.sched_getaffinity(0))
+    with threadpoolctl.threadpool_limits(cores):
+        info = threadpoolctl.threadpool_info()
+        used = max([i.get("num_threads", 1) for i in info] or [1])
+        tok_s = 4096
+        rows_s = 256
+        Xs = layer_x[:tok_s]
+        t0 = time.perf_counter()
+        Hs = O.hessian(Xs)
+        t_h = (time.perf_counter() - t0) * (n_tok / tok_s)
+        H = Hs * (n_tok / tok_s)  # stands in for the full-token Hessian (same shape)
+        t0 = time.perf_counter()
+        perm = O.act_order_permutation(H)
+        U = O.inverse_hessian_upper(O.damp_hessian(H[np.ix_(perm, perm)], q.damp))
+        t_c = time.perf_counter() - t0
+        Ws = layer_w[:rows_s][:, perm]
+        t0 = time.perf_counter()
+        codes, *_ = O.sweep(Ws, U, q.bits, q.group_size, q.sym, q.block)
+        t_s = (time.perf_counter() - t0) * (d_out / rows_s)
+        t0 = time.perf_counter()
+        O.pack(codes, q.bits)
+        t_p = (time.perf_counter() - t0) * (d_out / rows_s)
+    total = t_h + t_c + t_s + t_p
+    return {
+        "value": d_out * d_in / total, "unit": "weights/s", "cores": int(used), "kind": "oracle",
+        "sample": (f"Hessian on {tok_s} of {n_tok} tokens (x{n_tok // tok_s}); order + Cholesky form on the full "
+                   f"{d_in}x{d_in} matrix; sweep and packing on {rows_s} of {d_out} rows (x{d_out // rows_s}); "
+                   f"est. full-layer seconds {total:.1f} (H {t_h:.1f}, chol {t_c:.1f}, sweep {t_s:.1f}, pack {t_p:.2f})"),
+    }
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; "
+                                   "--gpus N > 1 is not supported (single-GPU solver)"}))
+        sys.exit(2)
+
+    import torch
+
+    import post_weight_quantization_accum_amd as P
+    from post_weight_quantization_accum_amd import synth
+    from post_weight_quantization_accum_amd.configs import HEADLINE, layer_spec
+
+    cfg_id, lname = HEADLINE
+    wl, li, d_out, d_in, xl = layer_spec(cfg_id, lname)
+    q = wl.quants[0]
+    n_tok = a.tokens or wl.n_tok
+    t0 = time.perf_counter()
+    L = synth.make_layer(d_out, d_in, n_tok, dtype=wl.dtype, sigma_w=wl.sigma_w, dist=wl.dist,
+                         outlier_frac=wl.outlier_frac, outlier_scale=wl.outlier_scale, config=cfg_id,
+                         layer=li, x_layer=xl)
+    gen_s = time.perf_counter() - t0
+    log(f"inputs generated in {gen_s:.1f} s")
+    dev = torch.device("cuda:0")
+    W = torch.from_numpy(L.W.view(np.int16)).view(torch.bfloat16).to(dev)
+    X = torch.from_numpy(L.X.view(np.int16)).view(torch.bfloat16).to(dev)
+    torch.cuda.synchronize()
+
+    cfg = P.make_config(bits=q.bits, group_size=q.group_size, sym=q.sym, act_order=q.act_order,
+                        block=q.block, damp=q.damp)
+    lib = P.load()
+    import ctypes
+    H = torch.empty((d_in, d_in), dtype=torch.float64, device=dev)
+    perm = torch.empty(d_in, dtype=torch.int32, device=dev)
+    ws_h = torch.empty(lib.gptq_prepare_hinv_workspace(d_in), dtype=torch.uint8, device=dev)
+    ws_q = torch.empty(lib.gptq_quantize_layer_workspace(d_out, d_in, ctypes.byref(cfg)), dtype=torch.uint8,
+                       device=dev)
+    ng = P.n_groups(d_in, q.group_size)
+    out = dict(codes=torch.empty((d_out, d_in), dtype=torch.uint8, device=dev),
+               scales=torch.empty((ng, d_out), dtype=torch.float32, device=dev),
+               zeros=torch.empty((ng, d_out), dtype=torch.float32, device=dev),
+               g_idx=torch.empty(d_in, dtype=torch.int32, device=dev))
+    packed = torch.empty((d_out, P.packed_words_per_row(d_in, q.bits)), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+    phase_ms = {"hessian": [], "prepare_hinv": [], "quantize_layer": [], "pack": []}
+
+    def step(record):
+        if record:
+            ev[0].record(stream)
+        H.zero_()
+        P.hessian_accumulate(H, X)
+        if record:
+            ev[1].record(stream)
+        P.prepare_hinv(H, cfg, perm=perm, workspace=ws_h)
+        if record:
+            ev[2].record(stream)
+        P.quantize_layer(W, H, perm, cfg, workspace=ws_q, out=out)
+        if record:
+            ev[3].record(stream)
+        P.pack(out["codes"], q.bits, out=packed)
+        if record:
+            ev[4].record(stream)
+
+    for _ in range(a.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    log("warmup done")
+    t_start = time.perf_counter()
+    for _ in range(a.steps):
+        step(True)
+        torch.cuda.synchronize()
+        names = list(phase_ms)
+        for i, n in enumerate(names):
+            phase_ms[n].append(ev[i].elapsed_time(ev[i + 1]))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms_per_step = wall * 1000.0 / a.steps
+    phases = {k: float(np.mean(v)) for k, v in phase_ms.items()}
+
+    # Dominant kernel: the Hessian SYRK (one launch per step, after the
+    # H.zero_() fill which is timed separately below).
+    h_flops = float(n_tok) * d_in * (d_in + 1)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    hk = []
+    for _ in range(max(1, min(a.steps, 3))):
+        H.zero_()
+        e0.record(stream)
+        P.hessian_accumulate(H, X)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        hk.append(e0.elapsed_time(e1))
+    h_ms = float(np.mean(hk))
+    achieved = h_flops / (h_ms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "kernel": "hess_syrk_kernel<bf16> (Hessian, upper triangle)", "kernel_ms": round(h_ms, 3),
+                "algorithmic_flops": h_flops}
+
+    res = {
+        "metric": METRIC,
+        "value": d_out * d_in / (ms_per_step * 1e-3),
+        "unit": "weights/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 MFMA (Hessian) + f64 (solver)",
+        "data": "synthetic (seeded Student-t(4) activations with outlier channels; N(0,0.02^2) weights)",
+        "config": {"workload": f"llama-7b down_proj {d_out}x{d_in} bf16; X {n_tok}x{d_in} bf16 Student-t(4), "
+                               f"{wl.outlier_frac * 100:g}% outlier channels x{wl.outlier_scale:g}; {q.bits}-bit "
+                               f"asym g{q.group_size} act-order B{q.block} damp {q.damp}",
+                   "d_out": d_out, "d_in": d_in, "tokens": n_tok, "bits": q.bits, "group_size": q.group_size,
+                   "act_order": bool(q.act_order), "parallelism": "single GPU"},
+        "phases_ms": {k: round(v, 3) for k, v in phases.items()},
+        "roofline": roofline,
+    }
+    log(f"timed {a.steps} steps: {ms_per_step:.2f} ms/step; phases {res['phases_ms']}")
+    if not a.no_cpu_baseline:
+        log("oracle CPU baseline ...")
+        res["cpu_baseline"] = cpu_baseline(L.W_f64(), L.X_f64() if n_tok <= 8192 else
+                                           synth.to_f64(L.X[:4096], L.dtype), d_out, d_in, n_tok, q)
+    res["input_generation_s"] = round(gen_s, 1)
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

@@ -95,3 +95,12 @@ def test_python_errors_map_status():
         _lib.check(_lib.ERR_NOT_PD, "x")
     with pytest.raises(P.NonFinite):
         _lib.check(_lib.ERR_NONFINITE, "x")
+
+
+def test_hessian_workspace_required_for_16bit_inputs():
+    lib = P.load()
+    fake = ctypes.c_void_p(0x1000)
+    n = ctypes.c_void_p(0)
+    assert lib.gptq_hessian_workspace(100, 11008) >= 11008 * 8
+    assert lib.gptq_hessian_accumulate(fake, fake, _lib.BF16, 10, 16, 16, n, 0, n) == _lib.ERR_WORKSPACE
+    assert lib.gptq_hessian_accumulate(fake, fake, _lib.F16, 10, 16, 16, fake, 8, n) == _lib.ERR_WORKSPACE

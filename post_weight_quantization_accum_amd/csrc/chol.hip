@@ -12,9 +12,10 @@
 // of 4/3 d^3, all in float64.
 //
 // Blocked right-looking Cholesky and blocked forward-substitution inverse
-// with NB = 64: a one-workgroup kernel factors and inverts each 64x64
-// diagonal block in LDS; the panel solve and the trailing updates are float64
-// MFMA GEMMs (gemm_f64.hip).
+// with NB = 64 (blocks handled in pairs, so the large trailing updates run
+// with K = 128): a one-workgroup kernel factors and inverts each 64x64
+// diagonal block in LDS; the panel solves and the trailing updates are
+// float64 MFMA GEMMs (gemm_f64.hip).
 //
 // Workspace layout (byte offsets):
 //   [0, 256)             int flags[N_FLAGS]; double lambda at 64; double diag sum at 72
@@ -252,37 +253,65 @@ gptq_status hinv_launch(double* H, int64_t d, const gptq_config* cfg, int32_t* p
     hipLaunchKernelGGL(fill_zero_kernel, dim3(2048), dim3(256), 0, s, H, d * d);
     GPTQ_LAUNCH_CHECK();
 
+    // Blocked right-looking Cholesky, 64-column blocks taken in pairs: the
+    // second block of a pair is brought up to date with a thin update, so
+    // the big trailing update of the rest has K = 128.
     const int64_t nblk = ceil_div(d, NB);
-    for (int64_t k = 0; k < nblk; ++k) {
+    gptq_status st;
+    for (int64_t k = 0; k < nblk; k += 2) {
+        const int64_t o = k * NB;
         hipLaunchKernelGGL(diag_block_kernel, dim3(1), dim3(256), 0, s, L, d, k, w.dinv, H, w.flags);
         GPTQ_LAUNCH_CHECK();
-        const int64_t o = k * NB, rest = d - o - NB;
-        if (rest <= 0) break;
-        // panel: L[o+NB:, o:o+NB] <- L[o+NB:, o:o+NB] * Dinv_k^T
-        gptq_status st = launch_gemm_f64(s, rest, NB, NB, 1.0, L + (o + NB) * d + o, d,
-                                         w.dinv + k * NB * NB, NB, true, 0.0, L + (o + NB) * d + o, d, false);
+        const int64_t r1 = d - o - NB;  // rows below block k
+        if (r1 <= 0) break;
+        // panel k: L[o+NB:, o:o+NB] <- L[o+NB:, o:o+NB] * Dinv_k^T
+        st = launch_gemm_f64(s, r1, NB, NB, 1.0, L + (o + NB) * d + o, d, w.dinv + k * NB * NB, NB, true, 0.0,
+                             L + (o + NB) * d + o, d, false);
         if (st != GPTQ_OK) return st;
-        // trailing: L[o+NB:, o+NB:] -= P P^T (lower tiles)
-        st = launch_gemm_f64(s, rest, rest, NB, -1.0, L + (o + NB) * d + o, d, L + (o + NB) * d + o, d, true,
-                             1.0, L + (o + NB) * d + o + NB, d, true);
+        // block column k+1 -= panel k * (its rows of panel k)^T
+        const int64_t nb1 = (r1 < NB) ? r1 : NB;
+        st = launch_gemm_f64(s, r1, nb1, NB, -1.0, L + (o + NB) * d + o, d, L + (o + NB) * d + o, d, true, 1.0,
+                             L + (o + NB) * d + o + NB, d, false);
+        if (st != GPTQ_OK) return st;
+        hipLaunchKernelGGL(diag_block_kernel, dim3(1), dim3(256), 0, s, L, d, k + 1, w.dinv, H, w.flags);
+        GPTQ_LAUNCH_CHECK();
+        const int64_t r2 = d - o - 2 * NB;  // rows below block k+1
+        if (r2 <= 0) break;
+        st = launch_gemm_f64(s, r2, NB, NB, 1.0, L + (o + 2 * NB) * d + o + NB, d, w.dinv + (k + 1) * NB * NB, NB,
+                             true, 0.0, L + (o + 2 * NB) * d + o + NB, d, false);
+        if (st != GPTQ_OK) return st;
+        // trailing: L[o+2NB:, o+2NB:] -= P P^T, P = L[o+2NB:, o:o+2NB] (lower tiles)
+        st = launch_gemm_f64(s, r2, r2, 2 * NB, -1.0, L + (o + 2 * NB) * d + o, d, L + (o + 2 * NB) * d + o, d, true,
+                             1.0, L + (o + 2 * NB) * d + o + 2 * NB, d, true);
         if (st != GPTQ_OK) return st;
     }
-    // blocked forward substitution M = L^{-1}: for block row i (after the
-    // diagonal block inverse has been placed), M[i, :i] = Dinv_i * B[i, :i];
-    // then B[r, :i+1] -= L[r, i] * M[i, :i+1] for the rows below.
-    for (int64_t i = 0; i < nblk; ++i) {
+    // Blocked forward substitution M = L^{-1} (in H's buffer, whose diagonal
+    // blocks already hold Dinv_i): block row i becomes M[i, :i] = Dinv_i B[i, :i];
+    // rows below then lose L[r, i] M[i, :].  Block rows are taken in pairs so
+    // that the update of the rows below has K = 128.
+    for (int64_t i = 0; i < nblk; i += 2) {
         const int64_t o = i * NB;
-        const int64_t nb = (d - o < NB) ? d - o : NB;
-        gptq_status st;
+        const int64_t nb0 = (d - o < NB) ? d - o : NB;
         if (i > 0) {
-            st = launch_gemm_f64(s, nb, o, nb, 1.0, w.dinv + i * NB * NB, NB, H + o * d, d, false, 0.0,
-                                 H + o * d, d, false);
+            st = launch_gemm_f64(s, nb0, o, nb0, 1.0, w.dinv + i * NB * NB, NB, H + o * d, d, false, 0.0, H + o * d, d,
+                                 false);
             if (st != GPTQ_OK) return st;
         }
-        const int64_t rest = d - o - nb;
-        if (rest <= 0) break;
-        st = launch_gemm_f64(s, rest, o + nb, nb, -1.0, L + (o + nb) * d + o, d, H + o * d, d, false, 1.0,
-                             H + (o + nb) * d, d, false);
+        const int64_t r1 = d - o - nb0;
+        if (r1 <= 0) break;
+        const int64_t nb1 = (r1 < NB) ? r1 : NB;
+        // block row i+1: B[i+1, :i+1] -= L[i+1, i] M[i, :i+1]; then M[i+1, :i+1] = Dinv_{i+1} B[i+1, :i+1]
+        st = launch_gemm_f64(s, nb1, o + nb0, nb0, -1.0, L + (o + nb0) * d + o, d, H + o * d, d, false, 1.0,
+                             H + (o + nb0) * d, d, false);
+        if (st != GPTQ_OK) return st;
+        st = launch_gemm_f64(s, nb1, o + nb0, nb1, 1.0, w.dinv + (i + 1) * NB * NB, NB, H + (o + nb0) * d, d, false,
+                             0.0, H + (o + nb0) * d, d, false);
+        if (st != GPTQ_OK) return st;
+        const int64_t r2 = r1 - nb1;
+        if (r2 <= 0) break;
+        const int64_t kk = nb0 + nb1;
+        st = launch_gemm_f64(s, r2, o + kk, kk, -1.0, L + (o + kk) * d + o, d, H + o * d, d, false, 1.0,
+                             H + (o + kk) * d, d, false);
         if (st != GPTQ_OK) return st;
     }
     hipLaunchKernelGGL(rotate_kernel, dim3((unsigned)d), dim3(256), 0, s, H, d, L);

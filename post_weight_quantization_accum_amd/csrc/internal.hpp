@@ -5,12 +5,13 @@
 
 namespace gptq {
 
-// C = alpha * A * op(B) + beta * C in float64 on MFMA (64x64 output tiles).
+// C = alpha * A * op(B) + beta * C in float64 on MFMA (128x128 output tiles).
 // A: M x K row-major (lda); op(B) = B (K x N, ldb) or B^T (B is N x K, ldb).
-// lower_tiles: only 64x64 tiles with tile_row >= tile_col are computed
-// (M == N required).  beta == 0 never reads C.  C may alias the operand it
-// overwrites only when the tile covers that operand's whole K range
-// (K <= 64 and the aliased operand is the tile's own rows/columns).
+// lower_tiles: only 128x128 tiles with tile_row >= tile_col are computed
+// (M == N required; entries above the diagonal inside diagonal tiles are
+// written too).  beta == 0 never reads C.  C may alias an operand only where
+// every tile reads nothing but its own rows (of A) or its own columns (of
+// B): each tile reads all of K before it writes.
 gptq_status launch_gemm_f64(hipStream_t s, int64_t M, int64_t N, int64_t K, double alpha,
                             const double* A, int64_t lda, const double* B, int64_t ldb,
                             bool transB, double beta, double* C, int64_t ldc, bool lower_tiles);

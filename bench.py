@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--tokens", type=int, default=None, help="override the token count (testing only)")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="after timing, run a plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
 
 
@@ -203,6 +205,13 @@ def main():
         "roofline": roofline,
     }
     log(f"timed {a.steps} steps: {ms_per_step:.2f} ms/step; phases {res['phases_ms']}")
+    if a.calib_copy_mib:
+        src = torch.empty(a.calib_copy_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        res["calib_copy_bytes"] = int(src.numel())
+        del src, dst
     if not a.no_cpu_baseline:
         log("oracle CPU baseline ...")
         res["cpu_baseline"] = cpu_baseline(L.W_f64(), L.X_f64() if n_tok <= 8192 else

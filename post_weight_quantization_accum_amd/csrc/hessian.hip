@@ -16,8 +16,8 @@
 // agrees with a float64 reference to rounding order, so the column order
 // does not depend on float32 accumulation error.
 //
-// Tiling: 4 wave64s per workgroup, each owning a 128x128 quarter as 4x4
-// MFMA 32x32 tiles (256 float32 accumulators per lane).  X is token-major,
+// Tiling: 8 wave64s per workgroup (two per SIMD), each owning a 128x64
+// part as 4x2 MFMA 32x32 tiles (128 float32 accumulators per lane).  X is token-major,
 // while each MFMA operand is 8 consecutive tokens of one column, so every
 // thread loads an 8-token x 8-column block with 16-byte loads, transposes it
 // in registers (v_perm_b32) and writes eight 16-byte column runs into LDS
@@ -25,7 +25,8 @@
 // the writes and the operand reads).  LDS is double-buffered and the next
 // stage's global loads are in flight while the current stage is multiplied.
 // Workgroups are mapped to tiles so that the ~32 workgroups resident on one
-// XCD work on neighbouring tiles of one tile row (shared A panel in L2).
+// XCD work on a compact block of about 6x6 tiles (about 12 column panels of
+// X shared through that XCD's L2).
 //
 // fp32 activations take a float64 path (products of fp32 values are exact
 // in float64): a plain tiled float64 kernel.
@@ -41,16 +42,35 @@ constexpr int CHUNK = 32768;     // tokens accumulated in float32 before the flo
 constexpr int SP = 132;          // row stride (floats) of the staged 128x128 quarter
 constexpr int PANEL = BT * SK;   // 16-bit elements per panel buffer
 
+constexpr int BAND = 6;  // tile rows per band of the tile enumeration
+
+// Enumeration of the upper-triangle tiles in bands of BAND tile rows, column
+// by column inside a band (rows ascending within a column): a run of ~32
+// consecutive tiles covers about 6 rows x 6 columns of tiles, i.e. needs
+// about 12 column panels of X instead of ~33 for a row-major run.
 __device__ __forceinline__ void upper_tile(int64_t t, int64_t& ti, int64_t& tj, int64_t T) {
-    // row-major enumeration of the upper triangle: row ti holds T - ti tiles
-    int64_t r = 0, base = 0;
-    // closed form start, then fix up
-    while (base + (T - r) <= t) {
-        base += T - r;
-        ++r;
+    int64_t r0 = 0;
+    for (;;) {
+        const int64_t r1 = (r0 + BAND < T) ? r0 + BAND : T;
+        // tiles of this band: sum over columns c >= r0 of (min(r1-1, c) - r0 + 1)
+        const int64_t h = r1 - r0;
+        const int64_t band_tiles = h * (h + 1) / 2 + h * (T - r1);
+        if (t < band_tiles) {
+            int64_t c = r0;
+            for (;;) {
+                const int64_t cnt = ((c < r1 - 1) ? c : r1 - 1) - r0 + 1;
+                if (t < cnt) {
+                    ti = r0 + t;
+                    tj = c;
+                    return;
+                }
+                t -= cnt;
+                ++c;
+            }
+        }
+        t -= band_tiles;
+        r0 = r1;
     }
-    ti = r;
-    tj = r + (t - base);
 }
 
 template <typename Tag>
@@ -146,12 +166,12 @@ __device__ __forceinline__ void diag_accumulate(double dsq[8], const u32x4_t v[8
 }
 
 template <typename Tag, bool VEC>
-__global__ __launch_bounds__(256) void hess_syrk_kernel(double* __restrict__ H, const uint16_t* __restrict__ X,
+__global__ __launch_bounds__(512) void hess_syrk_kernel(double* __restrict__ H, const uint16_t* __restrict__ X,
                                                         int64_t n_tok, int64_t d, int64_t ld, int64_t T,
                                                         int64_t n_tiles, int64_t per_xcd) {
     extern __shared__ __attribute__((aligned(16))) uint16_t lds[];  // [2 stages][2 panels][PANEL]
     // XCD-grouped tile order: workgroup b runs on XCD b % 8; each XCD takes a
-    // contiguous range of the row-major upper-triangle enumeration.
+    // contiguous range of the banded upper-triangle enumeration.
     const int64_t b = blockIdx.x;
     const int64_t lin = (b % 8) * per_xcd + b / 8;
     if (lin >= n_tiles) return;
@@ -159,38 +179,34 @@ __global__ __launch_bounds__(256) void hess_syrk_kernel(double* __restrict__ H, 
     upper_tile(lin, ti, tj, T);
     const bool diag = (ti == tj);
 
+    // 8 waves: wave (wr, wc) owns rows wr*128..+128 and columns wc*64..+64
+    // of the tile as 4x2 MFMA 32x32 tiles.  For staging, threads 0..255 load
+    // the row panel and threads 256..511 the column panel (idle on diagonal
+    // tiles, where the two panels coincide).
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    const int wr = wave >> 1, wc = wave & 1;
-    const int tg = lane & 7, cg = wave * 8 + (lane >> 3);
-    const int64_t colA = ti * BT + cg * 8, colB = tj * BT + cg * 8;
+    const int wr = wave >> 2, wc = wave & 3;
+    const int pt = t & 255, panel = t >> 8;
+    const int tg = lane & 7, cg = (pt >> 6) * 8 + (lane >> 3);
+    const bool loader = !(diag && panel == 1);
+    const int64_t col = (panel ? tj : ti) * BT + cg * 8;
 
-    f16_t acc[4][4];
+    f16_t acc[4][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
     // this launch covers tokens [0, n_tok) of X (the caller offsets X per chunk)
     const int64_t n_stages = ceil_div(n_tok, KT);
     const uint32_t row_bytes = (uint32_t)(ld * 2);
-    const uint32_t offA = (colA < d) ? (uint32_t)(tg * 8) * row_bytes + (uint32_t)(colA * 2) : OOB;
-    const uint32_t offB = (colB < d) ? (uint32_t)(tg * 8) * row_bytes + (uint32_t)(colB * 2) : OOB;
-    u32x4_t va[8], vb[8];
-    {
-        const StageRsrc rs = stage_rsrc(X, 0, ld, n_tok);
-        load_block<VEC>(va, rs, offA, colA, d);
-        if (!diag) load_block<VEC>(vb, rs, offB, colB, d);
-    }
-    store_block(lds, va, cg, tg);
-    if (!diag) store_block(lds + PANEL, vb, cg, tg);
+    const uint32_t off = (col < d && loader) ? (uint32_t)(tg * 8) * row_bytes + (uint32_t)(col * 2) : OOB;
+    u32x4_t va[8];
+    load_block<VEC>(va, stage_rsrc(X, 0, ld, n_tok), off, col, d);
+    if (loader) store_block(lds + panel * PANEL, va, cg, tg);
     __syncthreads();
-    if (n_stages > 1) {
-        const StageRsrc rs = stage_rsrc(X, 1, ld, n_tok);
-        load_block<VEC>(va, rs, offA, colA, d);
-        if (!diag) load_block<VEC>(vb, rs, offB, colB, d);
-    }
+    if (n_stages > 1) load_block<VEC>(va, stage_rsrc(X, 1, ld, n_tok), off, col, d);
 
     for (int64_t s = 0; s < n_stages; ++s) {
         const uint16_t* bufA = lds + (s & 1) * 2 * PANEL;
@@ -198,54 +214,51 @@ __global__ __launch_bounds__(256) void hess_syrk_kernel(double* __restrict__ H, 
 #pragma unroll
         for (int ks = 0; ks < KT / 16; ++ks) {
             const int ko = ks * 16 + 8 * (lane >> 5);
-            u32x4_t a[4], bb[4];
+            u32x4_t a[4], bb[2];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < 4; ++i)
                 a[i] = *(const u32x4_t*)&bufA[(wr * 128 + i * 32 + (lane & 31)) * SK + ko];
-                bb[i] = *(const u32x4_t*)&bufB[(wc * 128 + i * 32 + (lane & 31)) * SK + ko];
-            }
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                bb[j] = *(const u32x4_t*)&bufB[(wc * 64 + j * 32 + (lane & 31)) * SK + ko];
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = mfma_32x32x16(a[i], bb[j], acc[i][j], (Tag*)nullptr);
+                for (int j = 0; j < 2; ++j) acc[i][j] = mfma_32x32x16(a[i], bb[j], acc[i][j], (Tag*)nullptr);
         }
         if (s + 1 < n_stages) {
-            uint16_t* nbuf = lds + ((s + 1) & 1) * 2 * PANEL;
-            store_block(nbuf, va, cg, tg);
-            if (!diag) store_block(nbuf + PANEL, vb, cg, tg);
-            if (s + 2 < n_stages) {
-                const StageRsrc rs = stage_rsrc(X, s + 2, ld, n_tok);
-                load_block<VEC>(va, rs, offA, colA, d);
-                if (!diag) load_block<VEC>(vb, rs, offB, colB, d);
-            }
+            if (loader) store_block(lds + ((s + 1) & 1) * 2 * PANEL + panel * PANEL, va, cg, tg);
+            if (s + 2 < n_stages) load_block<VEC>(va, stage_rsrc(X, s + 2, ld, n_tok), off, col, d);
         }
         __syncthreads();
     }
 
     // float32 tile -> float64 H (strict upper part; the diagonal comes from a
-    // float64 pass).  One wave at a time stages its 128x128 quarter in LDS,
-    // then all 256 threads add it to H with row-contiguous accesses.
+    // float64 pass).  Waves stage their 128x64 parts in LDS two at a time
+    // (one 128x128 quarter), then all threads add it to H with
+    // row-contiguous accesses.
     float* stg = (float*)lds;
 #pragma unroll 1
-    for (int w = 0; w < 4; ++w) {
-        if (wave == w) {
-            float* sl = stg + (4 * (lane >> 5)) * SP + (lane & 31);
+    for (int q = 0; q < 4; ++q) {
+        // quarter q: rows (q>>1)*128, cols (q&1)*128 -> waves wr = q>>1, wc in {2(q&1), 2(q&1)+1}
+        if (wr == (q >> 1) && (wc >> 1) == (q & 1)) {
+            float* sl = stg + (4 * (lane >> 5)) * SP + (wc & 1) * 64 + (lane & 31);
 #pragma unroll
             for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-                for (int ni = 0; ni < 4; ++ni)
+                for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
                     for (int r = 0; r < 16; ++r)
                         sl[(mi * 32 + 8 * (r >> 2) + (r & 3)) * SP + ni * 32] = acc[mi][ni][r];
         }
         __syncthreads();
-        const int64_t ib = ti * BT + (w >> 1) * 128, jb = tj * BT + (w & 1) * 128;
-        const int col = t & 127;
-        const int64_t j = jb + col;
+        const int64_t ib = ti * BT + (q >> 1) * 128, jb = tj * BT + (q & 1) * 128;
+        const int cl = t & 127;
+        const int64_t j = jb + cl;
 #pragma unroll 8
-        for (int row = t >> 7; row < 128; row += 2) {
+        for (int row = t >> 7; row < 128; row += 4) {
             const int64_t i = ib + row;
-            if (i < j && j < d) H[i * d + j] += 2.0 * (double)stg[row * SP + col];
+            if (i < j && j < d) H[i * d + j] += 2.0 * (double)stg[row * SP + cl];
         }
         __syncthreads();
     }
@@ -378,7 +391,7 @@ gptq_status hessian_launch(double* H, const void* X, gptq_dtype dt, int64_t n_to
     const int64_t T = ceil_div(d, BT);
     const int64_t n_tiles = T * (T + 1) / 2;
     const int64_t per_xcd = ceil_div(n_tiles, 8);
-    const dim3 grid((unsigned)(per_xcd * 8)), block(256);
+    const dim3 grid((unsigned)(per_xcd * 8)), block(512);
     const size_t shmem = 4 * PANEL * sizeof(uint16_t);
     const bool vec = (ld_x % 8 == 0) && (d % 8 == 0) && ((uintptr_t)X % 16 == 0);
     const uint16_t* x = (const uint16_t*)X;
@@ -390,16 +403,16 @@ gptq_status hessian_launch(double* H, const void* X, gptq_dtype dt, int64_t n_to
         GPTQ_HIP(hipFuncSetAttribute((const void*)hess_syrk_kernel<h16x8_t, false>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem));
         attr_set = true;
     }
-    const dim3 dgrid((unsigned)ceil_div(d, 256), DSPLIT);
+    const dim3 dgrid((unsigned)ceil_div(d, 256), DSPLIT), b256(256);
     if (dt == GPTQ_BF16) {
-        if (vec) hipLaunchKernelGGL((colsq_kernel<bf16x8_t, true>), dgrid, block, 0, s, x, n_tok, d, ld_x, part);
-        else hipLaunchKernelGGL((colsq_kernel<bf16x8_t, false>), dgrid, block, 0, s, x, n_tok, d, ld_x, part);
+        if (vec) hipLaunchKernelGGL((colsq_kernel<bf16x8_t, true>), dgrid, b256, 0, s, x, n_tok, d, ld_x, part);
+        else hipLaunchKernelGGL((colsq_kernel<bf16x8_t, false>), dgrid, b256, 0, s, x, n_tok, d, ld_x, part);
     } else {
-        if (vec) hipLaunchKernelGGL((colsq_kernel<h16x8_t, true>), dgrid, block, 0, s, x, n_tok, d, ld_x, part);
-        else hipLaunchKernelGGL((colsq_kernel<h16x8_t, false>), dgrid, block, 0, s, x, n_tok, d, ld_x, part);
+        if (vec) hipLaunchKernelGGL((colsq_kernel<h16x8_t, true>), dgrid, b256, 0, s, x, n_tok, d, ld_x, part);
+        else hipLaunchKernelGGL((colsq_kernel<h16x8_t, false>), dgrid, b256, 0, s, x, n_tok, d, ld_x, part);
     }
     GPTQ_LAUNCH_CHECK();
-    hipLaunchKernelGGL(colsq_finish_kernel, dim3((unsigned)ceil_div(d, 256)), block, 0, s, part, d, H);
+    hipLaunchKernelGGL(colsq_finish_kernel, dim3((unsigned)ceil_div(d, 256)), b256, 0, s, part, d, H);
     GPTQ_LAUNCH_CHECK();
     // one launch per chunk of CHUNK tokens: each adds its float32 partial
     // tiles to H in float64, in token order

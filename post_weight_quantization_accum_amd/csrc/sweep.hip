@@ -5,19 +5,24 @@
 //
 // Data layout in HBM (workspace):
 //   Wwork  d_out x d_in float64, columns in sweep order (the running W)
-//   Err    d_out x B    float64, scaled errors of the current block
+//   Err    2 x d_out x S float64, scaled errors of the current superblock (ping-pong)
 //   codes_s d_out x d_in uint8, codes in sweep order
 //   scale64 / zero64  n_groups x d_out float64
 //   row_loss64 d_out float64, pinv d_in int32, flags
 //
 // sweep_block: one wave64 per 64 rows, one lane per row.  The block's columns
-// of those rows sit in LDS as [column][row] (conflict-free per column).  The
-// block is walked in sub-blocks of SB columns held in registers: inside a
-// sub-block the compensation is applied column by column in registers; the
-// sub-block's errors then update the block's remaining columns in LDS (SB
-// fused multiply-adds per element).  The rows of U needed by a sub-block are
-// staged in LDS and read as broadcasts.  After the block, a float64 MFMA GEMM
-// applies W[:, i2:] -= Err * U[i1:i2, i2:].
+// of those rows sit in LDS as [column][row] (conflict-free per column), and
+// the block's upper triangle of U sits in LDS packed, with reciprocal
+// pivots.  The block is walked in sub-blocks of SB columns held in
+// registers: inside a sub-block the compensation is applied column by column
+// in registers; the sub-block's errors then update the block's remaining
+// columns in LDS (SB fused multiply-adds per element).
+//
+// Lazy updates are two-level (mathematically the same as one update per
+// block): after each block, a float64 MFMA GEMM updates the rest of its
+// superblock of S = 512 columns (K = B); after each superblock, one GEMM
+// with K = S updates the next superblock, and another (on a second stream,
+// overlapping the next superblock's sweep) everything after it.
 #include "internal.hpp"
 
 namespace gptq {
@@ -40,6 +45,18 @@ struct SweepWs {
 
 int64_t n_groups_of(int64_t d_in, int32_t g) { return g > 0 ? ceil_div(d_in, g) : 1; }
 
+// Columns per superblock of the two-level lazy update: blocks are swept one
+// by one and update the rest of their superblock (K = B); each finished
+// superblock updates everything after it once (K = S).  Every group must lie
+// inside one superblock or start on a superblock boundary; otherwise S = B.
+int64_t superblock_cols(int64_t d_in, const gptq_config* cfg) {
+    const int64_t B = cfg->block_size;
+    const int64_t S = B * (512 / B > 0 ? 512 / B : 1);
+    const int64_t g = cfg->group_size > 0 ? cfg->group_size : d_in;
+    if (cfg->group_size <= 0 || S % g == 0 || g % S == 0) return S;
+    return B;
+}
+
 SweepWs carve(void* ws, int64_t d_out, int64_t d_in, const gptq_config* cfg) {
     char* p = (char*)ws;
     SweepWs w;
@@ -49,7 +66,7 @@ SweepWs carve(void* ws, int64_t d_out, int64_t d_in, const gptq_config* cfg) {
     w.Wwork = (double*)(p + off);
     off = align_up(off + (size_t)d_out * d_in * 8, 256);
     w.Err = (double*)(p + off);
-    off = align_up(off + (size_t)d_out * cfg->block_size * 8, 256);
+    off = align_up(off + 2 * (size_t)d_out * superblock_cols(d_in, cfg) * 8, 256);
     w.codes_s = (uint8_t*)(p + off);
     off = align_up(off + (size_t)d_out * d_in, 256);
     const int64_t ng = n_groups_of(d_in, cfg->group_size);
@@ -66,7 +83,7 @@ SweepWs carve(void* ws, int64_t d_out, int64_t d_in, const gptq_config* cfg) {
 size_t carve_size(int64_t d_out, int64_t d_in, const gptq_config* cfg) {
     size_t off = 256;
     off = align_up(off + (size_t)d_out * d_in * 8, 256);
-    off = align_up(off + (size_t)d_out * cfg->block_size * 8, 256);
+    off = align_up(off + 2 * (size_t)d_out * superblock_cols(d_in, cfg) * 8, 256);
     off = align_up(off + (size_t)d_out * d_in, 256);
     const int64_t ng = n_groups_of(d_in, cfg->group_size);
     off = align_up(off + (size_t)ng * d_out * 8, 256);
@@ -117,16 +134,43 @@ struct QParams {
     double maxq;
 };
 
+// A non-blocking stream at the default priority plus two events, released
+// when the call returns.
+struct SideStream {
+    hipStream_t s = nullptr;
+    hipEvent_t err_ready = nullptr, far_done = nullptr;
+    hipError_t init() {
+        hipError_t e = hipStreamCreateWithFlags(&s, hipStreamNonBlocking);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&err_ready, hipEventDisableTiming);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&far_done, hipEventDisableTiming);
+        return e;
+    }
+    ~SideStream() {
+        if (s) {
+            (void)hipStreamSynchronize(s);
+            (void)hipStreamDestroy(s);
+        }
+        if (err_ready) (void)hipEventDestroy(err_ready);
+        if (far_done) (void)hipEventDestroy(far_done);
+    }
+};
+
+// Packed upper triangle of a BMAX x BMAX block: row a holds columns
+// a+1 .. BMAX-1; element (a, b) sits at upper_base(a) + b.
+__host__ __device__ __forceinline__ int upper_base(int a) { return a * (BMAX - 1) - a * (a - 1) / 2 - a - 1; }
+constexpr int UPACK = BMAX * (BMAX - 1) / 2;
+
 template <int SB>
 __global__ __launch_bounds__(ROWS) void sweep_block_kernel(double* __restrict__ Wwork, int64_t d_out, int64_t d_in,
                                                            int64_t i1, int nb, const double* __restrict__ U,
                                                            int64_t g, QParams qp, double* __restrict__ Err,
-                                                           int ldE, uint8_t* __restrict__ codes_s,
+                                                           int ldE, int errc, uint8_t* __restrict__ codes_s,
                                                            double* __restrict__ scale64, double* __restrict__ zero64,
                                                            float* __restrict__ scales, float* __restrict__ zeros,
                                                            double* __restrict__ loss64) {
     __shared__ double w1[BMAX][ROWS + 1];
-    __shared__ double us[SBMAX][BMAX];
+    __shared__ double up[UPACK];
+    __shared__ double rinv[BMAX];
     __shared__ uint8_t cb[BMAX][ROWS];
 
     const int lane = threadIdx.x;
@@ -135,11 +179,17 @@ __global__ __launch_bounds__(ROWS) void sweep_block_kernel(double* __restrict__ 
     const bool live = row < d_out;
     const int64_t i2 = i1 + nb;
 
-    // block columns of the 64 rows -> LDS [column][row]
+    // the block's columns of the 64 rows -> LDS [column][row]; the block's
+    // upper triangle of U -> packed LDS; reciprocal pivots
     for (int rr = 0; rr < ROWS; ++rr) {
         const int64_t gr = r0 + rr;
         for (int j = lane; j < nb; j += ROWS) w1[j][rr] = (gr < d_out) ? Wwork[gr * d_in + i1 + j] : 0.0;
     }
+    for (int a = 0; a < nb; ++a) {
+        const double* ur = U + (i1 + a) * d_in + i1;
+        for (int b = a + 1 + lane; b < nb; b += ROWS) up[upper_base(a) + b] = ur[b];
+    }
+    for (int a = lane; a < nb; a += ROWS) rinv[a] = 1.0 / U[(i1 + a) * d_in + i1 + a];
 
     // current group parameters of this row (kept across blocks via scale64/zero64)
     double scale = 1.0, zero = 0.0;
@@ -151,16 +201,9 @@ __global__ __launch_bounds__(ROWS) void sweep_block_kernel(double* __restrict__ 
         }
     }
     double loss = 0.0;
+    __syncthreads();
 
     for (int s0 = 0; s0 < nb; s0 += SB) {
-        __syncthreads();
-        for (int k = 0; k < SB; ++k) {
-            const int64_t c = i1 + s0 + k;
-            for (int j = s0 + lane; j < nb; j += ROWS)
-                us[k][j] = (s0 + k < nb) ? U[c * d_in + i1 + j] : 0.0;
-        }
-        __syncthreads();
-
         double wv[SB];
 #pragma unroll
         for (int k = 0; k < SB; ++k) wv[k] = (s0 + k < nb) ? w1[s0 + k][lane] : 0.0;
@@ -209,26 +252,32 @@ __global__ __launch_bounds__(ROWS) void sweep_block_kernel(double* __restrict__ 
         for (int k = 0; k < SB; ++k) {
             errs[k] = 0.0;
             if (s0 + k < nb) {
+                const int c = s0 + k;
                 const double w = wv[k];
+                // the code is decided on the correctly rounded quotient w / scale
                 double code = rint(w / scale) + zero;
                 code = fmin(fmax(code, 0.0), qp.maxq);
                 const double q = scale * (code - zero);
-                const double ucc = us[k][s0 + k];
+                const double ri = rinv[c];
                 const double diff = w - q;
-                const double err = diff / ucc;
+                const double err = diff * ri;
+                const int ub = upper_base(c);
 #pragma unroll
-                for (int kk = k + 1; kk < SB; ++kk) wv[kk] = fma(-err, us[k][s0 + kk], wv[kk]);
+                for (int kk = k + 1; kk < SB; ++kk) wv[kk] = fma(-err, up[ub + s0 + kk], wv[kk]);
                 errs[k] = err;
-                loss += diff * diff / (2.0 * ucc * ucc);
-                w1[s0 + k][lane] = err;
-                cb[s0 + k][lane] = (uint8_t)code;
+                loss += 0.5 * (diff * ri) * (diff * ri);
+                w1[c][lane] = err;
+                cb[c][lane] = (uint8_t)code;
             }
         }
         // the sub-block's errors update the rest of the block
+        int ubk[SB];
+#pragma unroll
+        for (int k = 0; k < SB; ++k) ubk[k] = upper_base(s0 + k < nb ? s0 + k : 0);
         for (int j = s0 + SB; j < nb; ++j) {
             double v = w1[j][lane];
 #pragma unroll
-            for (int k = 0; k < SB; ++k) v = fma(-errs[k], us[k][j], v);
+            for (int k = 0; k < SB; ++k) v = fma(-errs[k], up[ubk[k] + j], v);
             w1[j][lane] = v;
         }
     }
@@ -239,7 +288,7 @@ __global__ __launch_bounds__(ROWS) void sweep_block_kernel(double* __restrict__ 
         const int64_t gr = r0 + rr;
         if (gr >= d_out) break;
         for (int j = lane; j < nb; j += ROWS) {
-            Err[gr * ldE + j] = w1[j][rr];
+            Err[gr * ldE + errc + j] = w1[j][rr];
             codes_s[gr * d_in + i1 + j] = cb[j][rr];
         }
     }
@@ -304,28 +353,63 @@ gptq_status sweep_launch(const void* W, gptq_dtype dt, int64_t d_out, int64_t d_
 
     QParams qp{cfg->bits, cfg->sym, (double)((1 << cfg->bits) - 1)};
     const unsigned grid = (unsigned)ceil_div(d_out, ROWS);
-    for (int64_t i1 = 0; i1 < d_in; i1 += B) {
-        const int nb = (int)((d_in - i1 < B) ? d_in - i1 : B);
-        switch (SB) {
+    const int64_t S = superblock_cols(d_in, cfg);
+    // Groups that span several superblocks read columns past the current
+    // superblock at their first column: those must be fully updated first.
+    const bool wait_far_before_sweep = cfg->group_size > 0 && g > S;
+
+    // A second stream runs each superblock's far update (everything past
+    // the next superblock) while the next superblock is swept.
+    SideStream side;
+    GPTQ_HIP(side.init());
+    bool far_pending = false;
+    for (int64_t k = 0, a = 0; a < d_in; ++k, a += S) {
+        const int64_t e = (a + S < d_in) ? a + S : d_in;
+        double* Ek = w.Err + (k & 1) * d_out * S;
+        if (wait_far_before_sweep && far_pending) GPTQ_HIP(hipStreamWaitEvent(s, side.far_done, 0));
+        for (int64_t i1 = a; i1 < e; i1 += B) {
+            const int nb = (int)((e - i1 < B) ? e - i1 : B);
+            switch (SB) {
 #define SWEEP_CASE(n)                                                                                           \
     case n:                                                                                                     \
         hipLaunchKernelGGL(sweep_block_kernel<n>, dim3(grid), dim3(ROWS), 0, s, w.Wwork, d_out, d_in, i1, nb, U, \
-                           g, qp, w.Err, B, w.codes_s, w.scale64, w.zero64, scales, zeros, w.loss64);          \
+                           g, qp, Ek, (int)S, (int)(i1 - a), w.codes_s, w.scale64, w.zero64, scales, zeros,    \
+                           w.loss64);                                                                           \
         break;
-            SWEEP_CASE(8)
-            SWEEP_CASE(4)
-            SWEEP_CASE(2)
-            SWEEP_CASE(1)
+                SWEEP_CASE(8)
+                SWEEP_CASE(4)
+                SWEEP_CASE(2)
+                SWEEP_CASE(1)
 #undef SWEEP_CASE
+            }
+            GPTQ_LAUNCH_CHECK();
+            const int64_t i2 = i1 + nb;
+            if (i2 < e) {  // rest of this superblock, K = nb
+                gptq_status st = launch_gemm_f64(s, d_out, e - i2, nb, -1.0, Ek + (i1 - a), S, U + i1 * d_in + i2,
+                                                 d_in, false, 1.0, w.Wwork + i2, d_in, false);
+                if (st != GPTQ_OK) return st;
+            }
         }
-        GPTQ_LAUNCH_CHECK();
-        const int64_t i2 = i1 + nb;
-        if (i2 < d_in) {
-            gptq_status st = launch_gemm_f64(s, d_out, d_in - i2, nb, -1.0, w.Err, B, U + i1 * d_in + i2, d_in,
-                                             false, 1.0, w.Wwork + i2, d_in, false);
+        if (e >= d_in) break;
+        // near update: the next superblock's columns, on the main stream,
+        // after the previous far update (which also wrote them) is done
+        if (far_pending) GPTQ_HIP(hipStreamWaitEvent(s, side.far_done, 0));
+        const int64_t n_near = (S < d_in - e) ? S : d_in - e;
+        gptq_status st = launch_gemm_f64(s, d_out, n_near, e - a, -1.0, Ek, S, U + a * d_in + e, d_in, false, 1.0,
+                                         w.Wwork + e, d_in, false);
+        if (st != GPTQ_OK) return st;
+        far_pending = false;
+        if (e + n_near < d_in) {  // far update on the side stream
+            GPTQ_HIP(hipEventRecord(side.err_ready, s));
+            GPTQ_HIP(hipStreamWaitEvent(side.s, side.err_ready, 0));
+            st = launch_gemm_f64(side.s, d_out, d_in - e - n_near, e - a, -1.0, Ek, S, U + a * d_in + e + n_near,
+                                 d_in, false, 1.0, w.Wwork + e + n_near, d_in, false);
             if (st != GPTQ_OK) return st;
+            GPTQ_HIP(hipEventRecord(side.far_done, side.s));
+            far_pending = true;
         }
     }
+    if (far_pending) GPTQ_HIP(hipStreamWaitEvent(s, side.far_done, 0));
     hipLaunchKernelGGL(finalize_kernel, dim3(gx, (unsigned)d_out), dim3(256), 0, s, w.codes_s, d_out, d_in, w.pinv,
                        g, w.scale64, w.zero64, codes, w_hat, w.flags);
     GPTQ_LAUNCH_CHECK();

@@ -5,9 +5,10 @@
 
 namespace gptq {
 
-// C = alpha * A * op(B) + beta * C in float64 on MFMA (128x128 output tiles).
-// A: M x K row-major (lda); op(B) = B (K x N, ldb) or B^T (B is N x K, ldb).
-// lower_tiles: only 128x128 tiles with tile_row >= tile_col are computed
+// C = alpha * A * op(B) + beta * C in float64 on MFMA (128x128 or 64x64
+// output tiles).  A: M x K row-major (lda); op(B) = B (K x N, ldb) or B^T
+// (B is N x K, ldb).
+// lower_tiles: only tiles with tile_row >= tile_col are computed
 // (M == N required; entries above the diagonal inside diagonal tiles are
 // written too).  beta == 0 never reads C.  C may alias an operand only where
 // every tile reads nothing but its own rows (of A) or its own columns (of

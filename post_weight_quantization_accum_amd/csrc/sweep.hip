@@ -161,138 +161,145 @@ __host__ __device__ __forceinline__ int upper_base(int a) { return a * (BMAX - 1
 constexpr int UPACK = BMAX * (BMAX - 1) / 2;
 
 template <int SB>
-__global__ __launch_bounds__(ROWS) void sweep_block_kernel(double* __restrict__ Wwork, int64_t d_out, int64_t d_in,
-                                                           int64_t i1, int nb, const double* __restrict__ U,
-                                                           int64_t g, QParams qp, double* __restrict__ Err,
-                                                           int ldE, int errc, uint8_t* __restrict__ codes_s,
-                                                           double* __restrict__ scale64, double* __restrict__ zero64,
-                                                           float* __restrict__ scales, float* __restrict__ zeros,
-                                                           double* __restrict__ loss64) {
+__global__ __launch_bounds__(256) void sweep_block_kernel(double* __restrict__ Wwork, int64_t d_out, int64_t d_in,
+                                                          int64_t i1, int nb, const double* __restrict__ U,
+                                                          int64_t g, QParams qp, double* __restrict__ Err,
+                                                          int ldE, int errc, uint8_t* __restrict__ codes_s,
+                                                          double* __restrict__ scale64, double* __restrict__ zero64,
+                                                          float* __restrict__ scales, float* __restrict__ zeros,
+                                                          double* __restrict__ loss64) {
     __shared__ double w1[BMAX][ROWS + 1];
     __shared__ double up[UPACK];
     __shared__ double rinv[BMAX];
     __shared__ uint8_t cb[BMAX][ROWS];
 
-    const int lane = threadIdx.x;
+    // All four waves stage the block (many loads in flight per thread);
+    // wave 0 then sweeps it, one lane per row; all four write it back.
+    const int t = threadIdx.x;
+    const int lane = t & 63;
     const int64_t r0 = (int64_t)blockIdx.x * ROWS;
     const int64_t row = r0 + lane;
     const bool live = row < d_out;
     const int64_t i2 = i1 + nb;
 
-    // the block's columns of the 64 rows -> LDS [column][row]; the block's
-    // upper triangle of U -> packed LDS; reciprocal pivots
-    for (int rr = 0; rr < ROWS; ++rr) {
+    // the block's columns of the 64 rows -> LDS [column][row]
+#pragma unroll 16
+    for (int idx = t; idx < ROWS * BMAX; idx += 256) {
+        const int rr = idx / BMAX, j = idx % BMAX;
         const int64_t gr = r0 + rr;
-        for (int j = lane; j < nb; j += ROWS) w1[j][rr] = (gr < d_out) ? Wwork[gr * d_in + i1 + j] : 0.0;
+        if (j < nb) w1[j][rr] = (gr < d_out) ? Wwork[gr * d_in + i1 + j] : 0.0;
     }
-    for (int a = 0; a < nb; ++a) {
-        const double* ur = U + (i1 + a) * d_in + i1;
-        for (int b = a + 1 + lane; b < nb; b += ROWS) up[upper_base(a) + b] = ur[b];
+    // the block's upper triangle of U -> packed LDS; reciprocal pivots
+#pragma unroll 16
+    for (int idx = t; idx < BMAX * BMAX; idx += 256) {
+        const int a = idx / BMAX, b = idx % BMAX;
+        if (a < nb && b < nb && b > a) up[upper_base(a) + b] = U[(i1 + a) * d_in + i1 + b];
     }
-    for (int a = lane; a < nb; a += ROWS) rinv[a] = 1.0 / U[(i1 + a) * d_in + i1 + a];
-
-    // current group parameters of this row (kept across blocks via scale64/zero64)
-    double scale = 1.0, zero = 0.0;
-    {
-        const int64_t gi = i1 / g;
-        if ((i1 % g) != 0 && live) {  // group started in an earlier block
-            scale = scale64[gi * d_out + row];
-            zero = zero64[gi * d_out + row];
-        }
-    }
-    double loss = 0.0;
+    if (t < nb) rinv[t] = 1.0 / U[(i1 + t) * d_in + i1 + t];
     __syncthreads();
-
-    for (int s0 = 0; s0 < nb; s0 += SB) {
-        double wv[SB];
-#pragma unroll
-        for (int k = 0; k < SB; ++k) wv[k] = (s0 + k < nb) ? w1[s0 + k][lane] : 0.0;
-
-        const int64_t c0 = i1 + s0;
-        if (c0 % g == 0) {
-            // group parameters from the group's current values
-            double xmin = 0.0, xmax = 0.0;
-            const int64_t gend = (c0 + g < d_in) ? c0 + g : d_in;
-            const int64_t inblk_end = (gend < i2) ? gend : i2;
-            for (int64_t j = c0; j < inblk_end; ++j) {
-                const double v = w1[j - i1][lane];
-                xmin = fmin(xmin, v);
-                xmax = fmax(xmax, v);
+    if (t < ROWS) {  // wave 0: the sweep (no barriers inside)
+        // current group parameters of this row (kept across blocks via scale64/zero64)
+        double scale = 1.0, zero = 0.0;
+        {
+            const int64_t gi = i1 / g;
+            if ((i1 % g) != 0 && live) {  // group started in an earlier block
+                scale = scale64[gi * d_out + row];
+                zero = zero64[gi * d_out + row];
             }
-            if (live)
-                for (int64_t j = i2; j < gend; ++j) {
-                    const double v = Wwork[row * d_in + j];
+        }
+        double loss = 0.0;
+
+        for (int s0 = 0; s0 < nb; s0 += SB) {
+            double wv[SB];
+#pragma unroll
+            for (int k = 0; k < SB; ++k) wv[k] = (s0 + k < nb) ? w1[s0 + k][lane] : 0.0;
+
+            const int64_t c0 = i1 + s0;
+            if (c0 % g == 0) {
+                // group parameters from the group's current values
+                double xmin = 0.0, xmax = 0.0;
+                const int64_t gend = (c0 + g < d_in) ? c0 + g : d_in;
+                const int64_t inblk_end = (gend < i2) ? gend : i2;
+                for (int64_t j = c0; j < inblk_end; ++j) {
+                    const double v = w1[j - i1][lane];
                     xmin = fmin(xmin, v);
                     xmax = fmax(xmax, v);
                 }
-            if (qp.sym) {
-                double amax = fmax(-xmin, xmax);
-                if (amax == 0.0) amax = 1.0;
-                scale = 2.0 * amax / qp.maxq;
-                zero = (double)(1 << (qp.bits - 1));
-            } else {
-                if (xmin == 0.0 && xmax == 0.0) {
-                    xmin = -1.0;
-                    xmax = 1.0;
+                if (live)
+                    for (int64_t j = i2; j < gend; ++j) {
+                        const double v = Wwork[row * d_in + j];
+                        xmin = fmin(xmin, v);
+                        xmax = fmax(xmax, v);
+                    }
+                if (qp.sym) {
+                    double amax = fmax(-xmin, xmax);
+                    if (amax == 0.0) amax = 1.0;
+                    scale = 2.0 * amax / qp.maxq;
+                    zero = (double)(1 << (qp.bits - 1));
+                } else {
+                    if (xmin == 0.0 && xmax == 0.0) {
+                        xmin = -1.0;
+                        xmax = 1.0;
+                    }
+                    scale = (xmax - xmin) / qp.maxq;
+                    zero = rint(-xmin / scale);
                 }
-                scale = (xmax - xmin) / qp.maxq;
-                zero = rint(-xmin / scale);
+                if (live) {
+                    const int64_t gi = c0 / g;
+                    scale64[gi * d_out + row] = scale;
+                    zero64[gi * d_out + row] = zero;
+                    scales[gi * d_out + row] = (float)scale;
+                    zeros[gi * d_out + row] = (float)zero;
+                }
             }
-            if (live) {
-                const int64_t gi = c0 / g;
-                scale64[gi * d_out + row] = scale;
-                zero64[gi * d_out + row] = zero;
-                scales[gi * d_out + row] = (float)scale;
-                zeros[gi * d_out + row] = (float)zero;
-            }
-        }
 
-        double errs[SB];
+            double errs[SB];
 #pragma unroll
-        for (int k = 0; k < SB; ++k) {
-            errs[k] = 0.0;
-            if (s0 + k < nb) {
-                const int c = s0 + k;
-                const double w = wv[k];
-                // the code is decided on the correctly rounded quotient w / scale
-                double code = rint(w / scale) + zero;
-                code = fmin(fmax(code, 0.0), qp.maxq);
-                const double q = scale * (code - zero);
-                const double ri = rinv[c];
-                const double diff = w - q;
-                const double err = diff * ri;
-                const int ub = upper_base(c);
+            for (int k = 0; k < SB; ++k) {
+                errs[k] = 0.0;
+                if (s0 + k < nb) {
+                    const int c = s0 + k;
+                    const double w = wv[k];
+                    // the code is decided on the correctly rounded quotient w / scale
+                    double code = rint(w / scale) + zero;
+                    code = fmin(fmax(code, 0.0), qp.maxq);
+                    const double q = scale * (code - zero);
+                    const double ri = rinv[c];
+                    const double diff = w - q;
+                    const double err = diff * ri;
+                    const int ub = upper_base(c);
 #pragma unroll
-                for (int kk = k + 1; kk < SB; ++kk) wv[kk] = fma(-err, up[ub + s0 + kk], wv[kk]);
-                errs[k] = err;
-                loss += 0.5 * (diff * ri) * (diff * ri);
-                w1[c][lane] = err;
-                cb[c][lane] = (uint8_t)code;
+                    for (int kk = k + 1; kk < SB; ++kk) wv[kk] = fma(-err, up[ub + s0 + kk], wv[kk]);
+                    errs[k] = err;
+                    loss += 0.5 * (diff * ri) * (diff * ri);
+                    w1[c][lane] = err;
+                    cb[c][lane] = (uint8_t)code;
+                }
+            }
+            // the sub-block's errors update the rest of the block
+            int ubk[SB];
+#pragma unroll
+            for (int k = 0; k < SB; ++k) ubk[k] = upper_base(s0 + k < nb ? s0 + k : 0);
+            for (int j = s0 + SB; j < nb; ++j) {
+                double v = w1[j][lane];
+#pragma unroll
+                for (int k = 0; k < SB; ++k) v = fma(-errs[k], up[ubk[k] + j], v);
+                w1[j][lane] = v;
             }
         }
-        // the sub-block's errors update the rest of the block
-        int ubk[SB];
-#pragma unroll
-        for (int k = 0; k < SB; ++k) ubk[k] = upper_base(s0 + k < nb ? s0 + k : 0);
-        for (int j = s0 + SB; j < nb; ++j) {
-            double v = w1[j][lane];
-#pragma unroll
-            for (int k = 0; k < SB; ++k) v = fma(-errs[k], up[ubk[k] + j], v);
-            w1[j][lane] = v;
-        }
+        if (live) loss64[row] += loss;
     }
     __syncthreads();
-
     // Err (now in w1) and codes back to HBM, row-contiguous
-    for (int rr = 0; rr < ROWS; ++rr) {
+#pragma unroll 8
+    for (int idx = t; idx < ROWS * BMAX; idx += 256) {
+        const int rr = idx / BMAX, j = idx % BMAX;
         const int64_t gr = r0 + rr;
-        if (gr >= d_out) break;
-        for (int j = lane; j < nb; j += ROWS) {
+        if (j < nb && gr < d_out) {
             Err[gr * ldE + errc + j] = w1[j][rr];
             codes_s[gr * d_in + i1 + j] = cb[j][rr];
         }
     }
-    if (live) loss64[row] += loss;
 }
 
 // codes / w_hat in original column order.
@@ -372,7 +379,7 @@ gptq_status sweep_launch(const void* W, gptq_dtype dt, int64_t d_out, int64_t d_
             switch (SB) {
 #define SWEEP_CASE(n)                                                                                           \
     case n:                                                                                                     \
-        hipLaunchKernelGGL(sweep_block_kernel<n>, dim3(grid), dim3(ROWS), 0, s, w.Wwork, d_out, d_in, i1, nb, U, \
+        hipLaunchKernelGGL(sweep_block_kernel<n>, dim3(grid), dim3(256), 0, s, w.Wwork, d_out, d_in, i1, nb, U, \
                            g, qp, Ek, (int)S, (int)(i1 - a), w.codes_s, w.scale64, w.zero64, scales, zeros,    \
                            w.loss64);                                                                           \
         break;

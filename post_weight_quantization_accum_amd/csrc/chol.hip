@@ -11,51 +11,91 @@
 // unique upper factor with positive diagonal.  That is 2/3 d^3 flops instead
 // of 4/3 d^3, all in float64.
 //
-// Blocked right-looking Cholesky and blocked forward-substitution inverse
-// with NB = 64 (blocks handled in pairs, so the large trailing updates run
-// with K = 128): a one-workgroup kernel factors and inverts each 64x64
-// diagonal block in LDS; the panel solves and the trailing updates are
-// float64 MFMA GEMMs (gemm_f64.hip).
+// L and M come out of one recursion over halves (split at a multiple of
+// 128).  For Hr = [A11 .; A21 A22]:
+//   (L11, M11) = chol_inv(A11)
+//   L21 = A21 M11^T                   (M11^T upper: K ends at the tile's column)
+//   A22 <- A22 - L21 L21^T            (lower tiles)
+//   T   = L21 M11                     (M11 lower: K starts at the tile's column)
+//   (L22, M22) = chol_inv(A22)
+//   M21 = -M22 T                      (M22 lower: K ends at the tile's row)
+// so the big products have K up to d/2 and run near the float64 MFMA peak,
+// where a right-looking blocked factorisation would be stuck at K = 64..128.
+// The leaves are 128x128 blocks factored and inverted by one workgroup with
+// the block held in registers (8x8 per thread).  L itself is never stored:
+// only M (written into H's buffer) is needed.
 //
 // Workspace layout (byte offsets):
-//   [0, 256)             int flags[N_FLAGS]; double lambda at 64; double diag sum at 72
-//   [256, 256+P)         diagonal-block inverses, nblk x NB x NB doubles
-//   [.., + d*d*8)        Hr / L (lower triangle), later U before the copy-back
+//   [0, 256)             int flags[N_FLAGS]; double lambda at 64
+//   [256, +8d)           diag(H), contiguous (act-order keys)
+//   [.., + d*d*8)        Hr (lower triangle); T blocks replace the A21 blocks
+//   [.., + max n1*n2*8)  L21 of the node being processed
 #include "internal.hpp"
 
 namespace gptq {
 namespace {
 
-constexpr int NB = 64;
+constexpr int LEAF = 128;         // leaf block edge
+constexpr int LT = 8;             // register tile edge
+constexpr int NLT = LEAF / LT;    // register tiles per leaf edge
+constexpr int LEAF_TILES = NLT * (NLT + 1) / 2;  // lower tiles, one per thread
+constexpr int LEAF_THREADS = 192;
+constexpr int LDL = LEAF + 1;     // LDS row stride of the leaf factor (doubles)
+constexpr size_t LEAF_LDS = (size_t)(LEAF * LDL + 2 * LEAF) * sizeof(double);
+static_assert(LEAF_TILES <= LEAF_THREADS, "one lower tile per thread");
+
+void split(int64_t n, int64_t& n1, int64_t& n2) {
+    const int64_t nb = ceil_div(n, LEAF);
+    n1 = LEAF * ((nb + 1) / 2);
+    n2 = n - n1;
+}
 
 struct Ws {
     int* flags;
     double* lambda;
-    double* dinv;
+    double* diag;
     double* L;
+    double* tmp;
 };
+
+size_t l_offset(int64_t d) { return align_up(256 + (size_t)d * sizeof(double), 256); }
+size_t tmp_offset(int64_t d) { return align_up(l_offset(d) + (size_t)d * (size_t)d * sizeof(double), 256); }
+
+// Largest n1 x n2 over all nodes of the recursion (not always the top one:
+// d = 257 splits 256 + 1, and the 256 below needs 128 x 128).
+size_t tmp_doubles(int64_t n) {
+    if (n <= LEAF) return 0;
+    int64_t n1, n2;
+    split(n, n1, n2);
+    size_t m = (size_t)n1 * (size_t)n2;
+    const size_t a = tmp_doubles(n1), b = tmp_doubles(n2);
+    if (a > m) m = a;
+    if (b > m) m = b;
+    return m;
+}
 
 Ws carve(void* ws, int64_t d) {
     char* p = (char*)ws;
     Ws w;
     w.flags = (int*)p;
     w.lambda = (double*)(p + 64);
-    const int64_t nblk = ceil_div(d, NB);
-    w.dinv = (double*)(p + 256);
-    size_t off = align_up(256 + (size_t)nblk * NB * NB * sizeof(double), 256);
-    w.L = (double*)(p + off);
+    w.diag = (double*)(p + 256);
+    w.L = (double*)(p + l_offset(d));
+    w.tmp = (double*)(p + tmp_offset(d));
     return w;
 }
 
-// lambda = damp * mean(diag H); flags non-finite diagonal entries.
+// lambda = damp * mean(diag H); copies the diagonal out and flags
+// non-finite entries.
 __global__ __launch_bounds__(1024) void diag_stats_kernel(const double* __restrict__ H, int64_t d, double damp,
-                                                          double* lambda, int* flags) {
+                                                          double* lambda, double* diag, int* flags) {
     __shared__ double part[1024];
     const int t = threadIdx.x;
     double s = 0.0;
     for (int64_t i = t; i < d; i += 1024) {
         const double v = H[i * d + i];
         if (!isfinite(v)) raise_flag(flags, FLAG_NONFINITE);
+        diag[i] = v;
         s += v;
     }
     part[t] = s;
@@ -75,19 +115,19 @@ __device__ __forceinline__ bool before(double ki, int64_t i, double kj, int64_t 
     return (ki > kj) || (ki == kj && i < j);
 }
 
-__global__ __launch_bounds__(256) void rank_kernel(const double* __restrict__ H, int64_t d, int32_t* perm) {
-    __shared__ double keys[1024];
-    const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const double kj = (j < d) ? H[j * d + j] : 0.0;
+__global__ __launch_bounds__(64) void rank_kernel(const double* __restrict__ diag, int64_t d, int32_t* perm) {
+    __shared__ double keys[2048];
+    const int64_t j = (int64_t)blockIdx.x * 64 + threadIdx.x;
+    const double kj = (j < d) ? diag[j] : 0.0;
     int64_t rank = 0;
-    for (int64_t base = 0; base < d; base += 1024) {
+    for (int64_t base = 0; base < d; base += 2048) {
         __syncthreads();
-        for (int e = threadIdx.x; e < 1024; e += 256) {
+        for (int e = threadIdx.x; e < 2048; e += 64) {
             const int64_t i = base + e;
-            keys[e] = (i < d) ? H[i * d + i] : 0.0;
+            keys[e] = (i < d) ? diag[i] : 0.0;
         }
         __syncthreads();
-        const int64_t lim = (d - base < 1024) ? d - base : 1024;
+        const int64_t lim = (d - base < 2048) ? d - base : 2048;
         for (int64_t e = 0; e < lim; ++e) rank += before(keys[e], base + e, kj, j) ? 1 : 0;
     }
     if (j < d) perm[rank] = (int32_t)j;
@@ -143,180 +183,235 @@ __global__ __launch_bounds__(256) void gather_reverse_kernel(const double* __res
     }
 }
 
-// Factor the k-th 64x64 diagonal block of L in place (lower), store its
-// inverse into dinv[k] and into the diagonal block of Minv.
-__global__ __launch_bounds__(256) void diag_block_kernel(double* L, int64_t d, int64_t k, double* dinv,
-                                                         double* Minv, int* flags) {
-    __shared__ double A[NB][NB + 1];
-    __shared__ double D[NB][NB + 1];
-    __shared__ double red[4][NB];
+// Leaf of the recursion: the n x n (n <= 128) diagonal block of Hr at
+// offset o is factored, A = L L^T, and M = L^{-1} is written to the same
+// block of Mi (lower triangle, zeros above the diagonal; the padding up to
+// 128 acts as an identity block).
+//
+// Thread t < 136 holds lower register tile (rt, ct), ct <= rt, of 8x8.
+// Factor: right-looking, one column per step.  The owners of column j
+// publish it in LDS (unscaled, after the updates of steps < j); every thread
+// then applies A[r][c] -= A[r][j] A[c][j] / A[j][j] to its entries with
+// c > j, and the owners of column j+1 publish that column.  One barrier per
+// step.  The scaled column of L goes to LDS for the inverse.
+// Inverse: X = I, and for m = 0..127: X[m,:] /= L[m][m], published by the
+// owners of row m, then X[r,:] -= L[r][m] X[m,:] for r > m.
+__global__ __launch_bounds__(LEAF_THREADS) void leaf_chol_inv_kernel(const double* __restrict__ A, double* Mi,
+                                                                     int64_t d, int64_t o, int n, int* flags) {
+    extern __shared__ double smem[];
+    double* Ls = smem;                 // [LEAF][LDL]
+    double* cb = smem + LEAF * LDL;    // [2][LEAF] column / row exchange
     const int t = threadIdx.x;
-    const int64_t o = k * NB;
-    const int nb = (int)((d - o < NB) ? d - o : NB);
-    for (int e = t; e < NB * NB; e += 256) {
-        const int i = e / NB, j = e % NB;
-        double v;
-        if (i < nb && j < nb) v = (j <= i) ? L[(o + i) * d + o + j] : 0.0;
-        else v = (i == j) ? 1.0 : 0.0;
-        A[i][j] = v;
+    const bool own = t < LEAF_TILES;
+    int rt = 0, ct = 0;
+    if (own) {
+        while ((rt + 1) * (rt + 2) / 2 <= t) ++rt;
+        ct = t - rt * (rt + 1) / 2;
+    }
+    const int r0 = rt * LT, c0 = ct * LT;
+
+    double a[LT][LT];
+#pragma unroll
+    for (int i = 0; i < LT; ++i)
+#pragma unroll
+        for (int k = 0; k < LT; ++k) {
+            const int r = r0 + i, c = c0 + k;
+            double v;
+            if (r < n && c < n) v = (c <= r) ? A[(o + r) * d + o + c] : 0.0;
+            else v = (r == c) ? 1.0 : 0.0;
+            a[i][k] = v;
+        }
+    if (own && ct == 0) {
+#pragma unroll
+        for (int i = 0; i < LT; ++i) cb[r0 + i] = a[i][0];
     }
     __syncthreads();
-    // unblocked right-looking Cholesky
-    for (int j = 0; j < NB; ++j) {
-        double piv = A[j][j];
-        if (!(piv > 0.0)) {
-            if (t == 0) raise_flag(flags, isnan(piv) ? FLAG_NONFINITE : FLAG_NOT_PD);
-            piv = 1.0;
+
+    bool bad_pd = false, bad_nan = false;
+    for (int jb = 0; jb < NLT; ++jb) {
+#pragma unroll
+        for (int jj = 0; jj < LT; ++jj) {
+            const int j = jb * LT + jj;
+            const double* cj = cb + (j & 1) * LEAF;
+            double piv = cj[j];
+            if (!(piv > 0.0)) {
+                bad_nan |= isnan(piv);
+                bad_pd |= !isnan(piv);
+                piv = 1.0;
+            }
+            const double sq = sqrt(piv);
+            const double inv = 1.0 / piv;
+            const double rs = 1.0 / sq;
+            if (t < LEAF) Ls[t * LDL + j] = (t > j) ? cj[t] * rs : ((t == j) ? sq : 0.0);
+            if (own && c0 + LT - 1 > j) {
+                double cr[LT], cc[LT];
+#pragma unroll
+                for (int i = 0; i < LT; ++i) cr[i] = cj[r0 + i];
+#pragma unroll
+                for (int k = 0; k < LT; ++k) cc[k] = (c0 + k > j) ? cj[c0 + k] * inv : 0.0;
+#pragma unroll
+                for (int i = 0; i < LT; ++i)
+#pragma unroll
+                    for (int k = 0; k < LT; ++k) a[i][k] = fma(-cr[i], cc[k], a[i][k]);
+                // publish column j+1 (owned by the tiles of column tile (j+1)/8)
+                const int kn = (jj + 1) % LT;
+                const int ctn = jb + (jj + 1) / LT;
+                if (j + 1 < LEAF && ct == ctn) {
+                    double* cn = cb + ((j + 1) & 1) * LEAF;
+#pragma unroll
+                    for (int i = 0; i < LT; ++i) cn[r0 + i] = a[i][kn];
+                }
+            }
+            __syncthreads();
         }
-        const double ljj = sqrt(piv);
-        __syncthreads();
-        if (t < NB) {
-            if (t == j) A[j][j] = ljj;
-            else if (t > j) A[t][j] = A[t][j] / ljj;
-        }
-        __syncthreads();
-        {
-            const int i = t & 63, cg = t >> 6;
-            if (i > j) {
-                const double lij = A[i][j];
-                for (int c = j + 1 + cg; c <= i; c += 4) A[i][c] = fma(-lij, A[c][j], A[i][c]);
+    }
+    if (t == 0 && bad_nan) raise_flag(flags, FLAG_NONFINITE);
+    if (t == 0 && bad_pd) raise_flag(flags, FLAG_NOT_PD);
+
+    // inverse of L (Ls), in the same register tiles
+    double x[LT][LT];
+#pragma unroll
+    for (int i = 0; i < LT; ++i)
+#pragma unroll
+        for (int k = 0; k < LT; ++k) x[i][k] = (r0 + i == c0 + k) ? 1.0 : 0.0;
+    for (int mb = 0; mb < NLT; ++mb) {
+#pragma unroll
+        for (int mm = 0; mm < LT; ++mm) {
+            const int m = mb * LT + mm;
+            double* rb = cb + (m & 1) * LEAF;
+            if (own && rt == mb) {
+                const double rinv = 1.0 / Ls[m * LDL + m];
+#pragma unroll
+                for (int k = 0; k < LT; ++k) {
+                    x[mm][k] *= rinv;
+                    rb[c0 + k] = x[mm][k];
+                }
+            }
+            __syncthreads();
+            if (own && ct <= mb && r0 + LT - 1 > m) {
+                double lr[LT], xr[LT];
+#pragma unroll
+                for (int i = 0; i < LT; ++i) lr[i] = (r0 + i > m) ? Ls[(r0 + i) * LDL + m] : 0.0;
+#pragma unroll
+                for (int k = 0; k < LT; ++k) xr[k] = rb[c0 + k];
+#pragma unroll
+                for (int i = 0; i < LT; ++i)
+#pragma unroll
+                    for (int k = 0; k < LT; ++k) x[i][k] = fma(-lr[i], xr[k], x[i][k]);
             }
         }
-        __syncthreads();
     }
-    // inverse by rows: D[i][c] = (delta_ic - sum_{c<=m<i} A[i][m] D[m][c]) / A[i][i]
-    for (int i = 0; i < NB; ++i) {
-        const int c = t & 63, part = t >> 6;
-        double s = 0.0;
-        if (c < i)
-            for (int m = c + part; m < i; m += 4) s = fma(A[i][m], D[m][c], s);
-        red[part][c] = s;
-        __syncthreads();
-        if (t < NB) {
-            double v = 0.0;
-            if (t < i) v = -(((red[0][t] + red[1][t]) + red[2][t]) + red[3][t]) / A[i][i];
-            else if (t == i) v = 1.0 / A[i][i];
-            D[i][t] = v;
+    if (own) {
+#pragma unroll
+        for (int i = 0; i < LT; ++i) {
+            const int r = r0 + i;
+            if (r >= n) continue;
+#pragma unroll
+            for (int k = 0; k < LT; ++k) {
+                const int c = c0 + k;
+                if (c < n) Mi[(o + r) * d + o + c] = x[i][k];
+            }
         }
-        __syncthreads();
     }
-    double* dk = dinv + k * NB * NB;
-    for (int e = t; e < NB * NB; e += 256) {
-        const int i = e / NB, j = e % NB;
-        dk[e] = (i < nb && j < nb) ? D[i][j] : 0.0;
-        if (i < nb && j <= i) {
-            L[(o + i) * d + o + j] = A[i][j];
-            Minv[(o + i) * d + o + j] = D[i][j];
+    // zeros in the strictly upper register tiles of the block: the products
+    // that take this block as a triangular operand read them
+    for (int e = t; e < LEAF * LEAF; e += LEAF_THREADS) {
+        const int r = e / LEAF, c = e % LEAF;
+        if (r < n && c < n && c / LT > r / LT) Mi[(o + r) * d + o + c] = 0.0;
+    }
+}
+
+// U = J M J in place: the lower triangle of M (with its diagonal) moves to
+// the mirrored upper position, the strict lower triangle becomes zero.
+__global__ __launch_bounds__(256) void rotate_inplace_kernel(double* M, int64_t d) {
+    const int64_t i = blockIdx.x;
+    for (int64_t j = threadIdx.x; j <= i; j += 256) {
+        if (j < i) {
+            const double v = M[i * d + j];
+            M[(d - 1 - i) * d + (d - 1 - j)] = v;
+            M[i * d + j] = 0.0;
+        } else if (i < d - 1 - i) {
+            const int64_t k = d - 1 - i;
+            const double v = M[i * d + i];
+            M[i * d + i] = M[k * d + k];
+            M[k * d + k] = v;
         }
     }
 }
 
-__global__ __launch_bounds__(256) void fill_zero_kernel(double* p, int64_t n) {
-    const int64_t stride = (int64_t)gridDim.x * 256;
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) p[i] = 0.0;
-}
+struct Rec {
+    hipStream_t s;
+    double* L;    // Hr, lower; T blocks replace A21 blocks
+    double* M;    // inverse factor (lower)
+    double* tmp;  // L21 of the current node
+    int64_t d;
+    int* flags;
+};
 
-// U[c][j] = M[d-1-c][d-1-j] for j >= c, 0 below the diagonal.
-__global__ __launch_bounds__(256) void rotate_kernel(const double* __restrict__ M, int64_t d, double* U) {
-    const int64_t c = blockIdx.x;
-    for (int64_t j = threadIdx.x; j < d; j += 256)
-        U[c * d + j] = (j >= c) ? M[(d - 1 - c) * d + (d - 1 - j)] : 0.0;
+gptq_status chol_inv(const Rec& c, int64_t o, int64_t n) {
+    const int64_t d = c.d;
+    if (n <= LEAF) {
+        hipLaunchKernelGGL(leaf_chol_inv_kernel, dim3(1), dim3(LEAF_THREADS), LEAF_LDS, c.s, c.L, c.M, d, o, (int)n,
+                           c.flags);
+        GPTQ_LAUNCH_CHECK();
+        return GPTQ_OK;
+    }
+    int64_t n1, n2;
+    split(n, n1, n2);
+    double* A21 = c.L + (o + n1) * d + o;   // becomes T
+    double* A22 = c.L + (o + n1) * d + o + n1;
+    const double* M11 = c.M + o * d + o;
+    const double* M22 = c.M + (o + n1) * d + o + n1;
+    double* M21 = c.M + (o + n1) * d + o;
+    gptq_status st = chol_inv(c, o, n1);
+    if (st != GPTQ_OK) return st;
+    // L21 = A21 M11^T
+    st = launch_gemm_f64(c.s, n2, n1, n1, 1.0, A21, d, M11, d, true, 0.0, c.tmp, n1, false, GEMM_TRI_KEND_COL);
+    if (st != GPTQ_OK) return st;
+    // A22 -= L21 L21^T
+    st = launch_gemm_f64(c.s, n2, n2, n1, -1.0, c.tmp, n1, c.tmp, n1, true, 1.0, A22, d, true);
+    if (st != GPTQ_OK) return st;
+    // T = L21 M11 (into A21's place)
+    st = launch_gemm_f64(c.s, n2, n1, n1, 1.0, c.tmp, n1, M11, d, false, 0.0, A21, d, false, GEMM_TRI_KBEG_COL);
+    if (st != GPTQ_OK) return st;
+    st = chol_inv(c, o + n1, n2);
+    if (st != GPTQ_OK) return st;
+    // M21 = -M22 T
+    return launch_gemm_f64(c.s, n2, n1, n2, -1.0, M22, d, A21, d, false, 0.0, M21, d, false, GEMM_TRI_KEND_ROW);
 }
 
 }  // namespace
 
 size_t hinv_workspace_bytes(int64_t d) {
-    const int64_t nblk = ceil_div(d, NB);
-    return align_up(256 + (size_t)nblk * NB * NB * sizeof(double), 256) + (size_t)d * d * sizeof(double);
+    return tmp_offset(d) + tmp_doubles(d) * sizeof(double);
 }
 
 gptq_status hinv_launch(double* H, int64_t d, const gptq_config* cfg, int32_t* perm, void* ws,
                         hipStream_t s, int* host_flags) {
     Ws w = carve(ws, d);
-    double* L = w.L;
+    GPTQ_HIP(hipFuncSetAttribute((const void*)leaf_chol_inv_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                 (int)LEAF_LDS));
     GPTQ_HIP(hipMemsetAsync(w.flags, 0, 256, s));
 
-    hipLaunchKernelGGL(diag_stats_kernel, dim3(1), dim3(1024), 0, s, H, d, cfg->damp, w.lambda, w.flags);
+    hipLaunchKernelGGL(diag_stats_kernel, dim3(1), dim3(1024), 0, s, H, d, cfg->damp, w.lambda, w.diag, w.flags);
     GPTQ_LAUNCH_CHECK();
-    const unsigned gd = (unsigned)ceil_div(d, 256);
     if (cfg->act_order)
-        hipLaunchKernelGGL(rank_kernel, dim3(gd), dim3(256), 0, s, H, d, perm);
+        hipLaunchKernelGGL(rank_kernel, dim3((unsigned)ceil_div(d, 64)), dim3(64), 0, s, w.diag, d, perm);
     else
-        hipLaunchKernelGGL(iota_kernel, dim3(gd), dim3(256), 0, s, perm, d);
+        hipLaunchKernelGGL(iota_kernel, dim3((unsigned)ceil_div(d, 256)), dim3(256), 0, s, perm, d);
     GPTQ_LAUNCH_CHECK();
     const int64_t T32 = ceil_div(d, 32);
     hipLaunchKernelGGL(symmetrize_kernel, dim3((unsigned)(T32 * (T32 + 1) / 2)), dim3(256), 0, s, H, d, w.flags);
     GPTQ_LAUNCH_CHECK();
-    hipLaunchKernelGGL(gather_reverse_kernel, dim3((unsigned)d), dim3(256), 0, s, H, d, perm, w.lambda, L);
-    GPTQ_LAUNCH_CHECK();
-    // H's buffer now becomes the inverse M (lower block triangle), zero first.
-    hipLaunchKernelGGL(fill_zero_kernel, dim3(2048), dim3(256), 0, s, H, d * d);
+    hipLaunchKernelGGL(gather_reverse_kernel, dim3((unsigned)d), dim3(256), 0, s, H, d, perm, w.lambda, w.L);
     GPTQ_LAUNCH_CHECK();
 
-    // Blocked right-looking Cholesky, 64-column blocks taken in pairs: the
-    // second block of a pair is brought up to date with a thin update, so
-    // the big trailing update of the rest has K = 128.
-    const int64_t nblk = ceil_div(d, NB);
-    gptq_status st;
-    for (int64_t k = 0; k < nblk; k += 2) {
-        const int64_t o = k * NB;
-        hipLaunchKernelGGL(diag_block_kernel, dim3(1), dim3(256), 0, s, L, d, k, w.dinv, H, w.flags);
-        GPTQ_LAUNCH_CHECK();
-        const int64_t r1 = d - o - NB;  // rows below block k
-        if (r1 <= 0) break;
-        // panel k: L[o+NB:, o:o+NB] <- L[o+NB:, o:o+NB] * Dinv_k^T
-        st = launch_gemm_f64(s, r1, NB, NB, 1.0, L + (o + NB) * d + o, d, w.dinv + k * NB * NB, NB, true, 0.0,
-                             L + (o + NB) * d + o, d, false);
-        if (st != GPTQ_OK) return st;
-        // block column k+1 -= panel k * (its rows of panel k)^T
-        const int64_t nb1 = (r1 < NB) ? r1 : NB;
-        st = launch_gemm_f64(s, r1, nb1, NB, -1.0, L + (o + NB) * d + o, d, L + (o + NB) * d + o, d, true, 1.0,
-                             L + (o + NB) * d + o + NB, d, false);
-        if (st != GPTQ_OK) return st;
-        hipLaunchKernelGGL(diag_block_kernel, dim3(1), dim3(256), 0, s, L, d, k + 1, w.dinv, H, w.flags);
-        GPTQ_LAUNCH_CHECK();
-        const int64_t r2 = d - o - 2 * NB;  // rows below block k+1
-        if (r2 <= 0) break;
-        st = launch_gemm_f64(s, r2, NB, NB, 1.0, L + (o + 2 * NB) * d + o + NB, d, w.dinv + (k + 1) * NB * NB, NB,
-                             true, 0.0, L + (o + 2 * NB) * d + o + NB, d, false);
-        if (st != GPTQ_OK) return st;
-        // trailing: L[o+2NB:, o+2NB:] -= P P^T, P = L[o+2NB:, o:o+2NB] (lower tiles)
-        st = launch_gemm_f64(s, r2, r2, 2 * NB, -1.0, L + (o + 2 * NB) * d + o, d, L + (o + 2 * NB) * d + o, d, true,
-                             1.0, L + (o + 2 * NB) * d + o + 2 * NB, d, true);
-        if (st != GPTQ_OK) return st;
-    }
-    // Blocked forward substitution M = L^{-1} (in H's buffer, whose diagonal
-    // blocks already hold Dinv_i): block row i becomes M[i, :i] = Dinv_i B[i, :i];
-    // rows below then lose L[r, i] M[i, :].  Block rows are taken in pairs so
-    // that the update of the rows below has K = 128.
-    for (int64_t i = 0; i < nblk; i += 2) {
-        const int64_t o = i * NB;
-        const int64_t nb0 = (d - o < NB) ? d - o : NB;
-        if (i > 0) {
-            st = launch_gemm_f64(s, nb0, o, nb0, 1.0, w.dinv + i * NB * NB, NB, H + o * d, d, false, 0.0, H + o * d, d,
-                                 false);
-            if (st != GPTQ_OK) return st;
-        }
-        const int64_t r1 = d - o - nb0;
-        if (r1 <= 0) break;
-        const int64_t nb1 = (r1 < NB) ? r1 : NB;
-        // block row i+1: B[i+1, :i+1] -= L[i+1, i] M[i, :i+1]; then M[i+1, :i+1] = Dinv_{i+1} B[i+1, :i+1]
-        st = launch_gemm_f64(s, nb1, o + nb0, nb0, -1.0, L + (o + nb0) * d + o, d, H + o * d, d, false, 1.0,
-                             H + (o + nb0) * d, d, false);
-        if (st != GPTQ_OK) return st;
-        st = launch_gemm_f64(s, nb1, o + nb0, nb1, 1.0, w.dinv + (i + 1) * NB * NB, NB, H + (o + nb0) * d, d, false,
-                             0.0, H + (o + nb0) * d, d, false);
-        if (st != GPTQ_OK) return st;
-        const int64_t r2 = r1 - nb1;
-        if (r2 <= 0) break;
-        const int64_t kk = nb0 + nb1;
-        st = launch_gemm_f64(s, r2, o + kk, kk, -1.0, L + (o + kk) * d + o, d, H + o * d, d, false, 1.0,
-                             H + (o + kk) * d, d, false);
-        if (st != GPTQ_OK) return st;
-    }
-    hipLaunchKernelGGL(rotate_kernel, dim3((unsigned)d), dim3(256), 0, s, H, d, L);
+    // H's buffer now receives M = L^{-1} (lower), then U = J M J in place.
+    Rec c{s, w.L, H, w.tmp, d, w.flags};
+    gptq_status st = chol_inv(c, 0, d);
+    if (st != GPTQ_OK) return st;
+    hipLaunchKernelGGL(rotate_inplace_kernel, dim3((unsigned)d), dim3(256), 0, s, H, d);
     GPTQ_LAUNCH_CHECK();
-    GPTQ_HIP(hipMemcpyAsync(H, L, (size_t)d * d * sizeof(double), hipMemcpyDeviceToDevice, s));
     GPTQ_HIP(hipMemcpyAsync(host_flags, w.flags, N_FLAGS * sizeof(int), hipMemcpyDeviceToHost, s));
     GPTQ_HIP(hipStreamSynchronize(s));
     return GPTQ_OK;

@@ -1,10 +1,12 @@
 // Float64 GEMM on the gfx950 matrix cores (v_mfma_f64_16x16x4_f64).
 //
-// Serves the three dense contractions of the solver:
+// Serves the dense contractions of the solver:
 //   * the lazy block update of the weights, W[:, i2:] -= Err * U[i1:i2, i2:]
 //     ("GPTQ量化算法深度解析" §2.4 lazy batch update, §3.1 step 3);
-//   * the trailing updates of the blocked Cholesky factorisation and of the
-//     blocked triangular inverse (§2.4 / §3.1 step 2).
+//   * the off-diagonal products of the recursive Cholesky factorisation and
+//     triangular inverse (§2.4 / §3.1 step 2), where one operand is a
+//     triangular inverse: each tile then runs K only over the range where
+//     that operand is non-zero (GemmTri), which halves those products.
 //
 // One workgroup (4 wave64s) computes a 128x128 tile of C (each wave a 64x64
 // quarter as 4x4 MFMA 16x16 tiles), or a 64x64 tile when the problem has too
@@ -112,7 +114,8 @@ __global__ __launch_bounds__(256, 2) void gemm_f64_kernel(int64_t M, int64_t N, 
                                                           const double* __restrict__ A, int64_t lda,
                                                           const double* __restrict__ B, int64_t ldb,
                                                           double beta, double* C, int64_t ldc,
-                                                          int64_t tiles_n, int64_t n_tiles, int64_t per_xcd) {
+                                                          int64_t tiles_m, int64_t tiles_n, int64_t n_tiles,
+                                                          int64_t per_xcd, int tri) {
     using G = Cfg<TILE>;
     __shared__ double sA[2][KC][G::LD];
     __shared__ double sB[2][KC][G::LD];
@@ -126,8 +129,20 @@ __global__ __launch_bounds__(256, 2) void gemm_f64_kernel(int64_t M, int64_t N, 
     } else {
         tm = lin / tiles_n;
         tn = lin % tiles_n;
+        if (tri == GEMM_TRI_KEND_ROW) {
+            // work grows with the row: zig-zag the rows (last, first, second
+            // last, ...) so every XCD's contiguous share holds a balanced mix
+            tm = (tm & 1) ? (tm >> 1) : tiles_m - 1 - (tm >> 1);
+        } else if (tri == GEMM_TRI_KEND_COL) {
+            tn = tiles_n - 1 - tn;  // heaviest columns first
+        }
     }
     const int64_t m0 = tm * TILE, n0 = tn * TILE;
+    // K range of this tile: the triangular operand is zero outside it
+    int64_t kbeg = 0, kend = K;
+    if (tri == GEMM_TRI_KEND_ROW) kend = (m0 + TILE < K) ? m0 + TILE : K;
+    else if (tri == GEMM_TRI_KEND_COL) kend = (n0 + TILE < K) ? n0 + TILE : K;
+    else if (tri == GEMM_TRI_KBEG_COL) kbeg = (n0 < K) ? n0 : K;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wr = wave >> 1, wc = wave & 1;
 
@@ -137,11 +152,11 @@ __global__ __launch_bounds__(256, 2) void gemm_f64_kernel(int64_t M, int64_t N, 
 #pragma unroll
         for (int j = 0; j < G::NT; ++j) acc[i][j] = d4_t{0.0, 0.0, 0.0, 0.0};
 
-    const int64_t n_chunks = ceil_div(K, KC);
+    const int64_t n_chunks = ceil_div(kend - kbeg, KC);
     double ra[G::EPT], rb[G::EPT];
-    load_rows<TILE, VEC>(ra, A, lda, m0, M, 0, K);
-    if (TRANS_B) load_rows<TILE, VEC>(rb, B, ldb, n0, N, 0, K);
-    else load_kcols<TILE, VEC>(rb, B, ldb, 0, K, n0, N);
+    load_rows<TILE, VEC>(ra, A, lda, m0, M, kbeg, kend);
+    if (TRANS_B) load_rows<TILE, VEC>(rb, B, ldb, n0, N, kbeg, kend);
+    else load_kcols<TILE, VEC>(rb, B, ldb, kbeg, kend, n0, N);
     store_rows<TILE>(sA[0], ra);
     if (TRANS_B) store_rows<TILE>(sB[0], rb);
     else store_kcols<TILE>(sB[0], rb);
@@ -150,10 +165,10 @@ __global__ __launch_bounds__(256, 2) void gemm_f64_kernel(int64_t M, int64_t N, 
     for (int64_t c = 0; c < n_chunks; ++c) {
         const int cur = c & 1;
         if (c + 1 < n_chunks) {
-            const int64_t k0 = (c + 1) * KC;
-            load_rows<TILE, VEC>(ra, A, lda, m0, M, k0, K);
-            if (TRANS_B) load_rows<TILE, VEC>(rb, B, ldb, n0, N, k0, K);
-            else load_kcols<TILE, VEC>(rb, B, ldb, k0, K, n0, N);
+            const int64_t k0 = kbeg + (c + 1) * KC;
+            load_rows<TILE, VEC>(ra, A, lda, m0, M, k0, kend);
+            if (TRANS_B) load_rows<TILE, VEC>(rb, B, ldb, n0, N, k0, kend);
+            else load_kcols<TILE, VEC>(rb, B, ldb, k0, kend, n0, N);
         }
 #pragma unroll
         for (int kk = 0; kk < KC / 4; ++kk) {
@@ -198,38 +213,39 @@ __global__ __launch_bounds__(256, 2) void gemm_f64_kernel(int64_t M, int64_t N, 
 
 template <int TILE, bool TRANS_B, bool LOWER>
 void launch_t(hipStream_t s, bool vec, int64_t M, int64_t N, int64_t K, double alpha, const double* A, int64_t lda,
-              const double* B, int64_t ldb, double beta, double* C, int64_t ldc) {
+              const double* B, int64_t ldb, double beta, double* C, int64_t ldc, int tri) {
     const int64_t tiles_m = ceil_div(M, TILE), tiles_n = ceil_div(N, TILE);
     const int64_t n_tiles = LOWER ? tiles_m * (tiles_m + 1) / 2 : tiles_m * tiles_n;
     const int64_t per_xcd = ceil_div(n_tiles, 8);
     const dim3 grid((unsigned)(per_xcd * 8));
     if (vec)
         hipLaunchKernelGGL((gemm_f64_kernel<TILE, TRANS_B, LOWER, true>), grid, dim3(256), 0, s, M, N, K, alpha, A,
-                           lda, B, ldb, beta, C, ldc, tiles_n, n_tiles, per_xcd);
+                           lda, B, ldb, beta, C, ldc, tiles_m, tiles_n, n_tiles, per_xcd, tri);
     else
         hipLaunchKernelGGL((gemm_f64_kernel<TILE, TRANS_B, LOWER, false>), grid, dim3(256), 0, s, M, N, K, alpha, A,
-                           lda, B, ldb, beta, C, ldc, tiles_n, n_tiles, per_xcd);
+                           lda, B, ldb, beta, C, ldc, tiles_m, tiles_n, n_tiles, per_xcd, tri);
 }
 
 template <bool TRANS_B, bool LOWER>
 void launch_sel(hipStream_t s, bool vec, int64_t M, int64_t N, int64_t K, double alpha, const double* A, int64_t lda,
-                const double* B, int64_t ldb, double beta, double* C, int64_t ldc) {
+                const double* B, int64_t ldb, double beta, double* C, int64_t ldc, int tri) {
     // 128x128 tiles when there are enough of them to fill the chip twice,
     // else 64x64 tiles (4x the workgroups)
     const int64_t tm = ceil_div(M, 128), tn = ceil_div(N, 128);
     const int64_t t128 = LOWER ? tm * (tm + 1) / 2 : tm * tn;
     if (t128 >= 512)
-        launch_t<128, TRANS_B, LOWER>(s, vec, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
+        launch_t<128, TRANS_B, LOWER>(s, vec, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, tri);
     else
-        launch_t<64, TRANS_B, LOWER>(s, vec, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
+        launch_t<64, TRANS_B, LOWER>(s, vec, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, tri);
 }
 
 }  // namespace
 
 gptq_status launch_gemm_f64(hipStream_t s, int64_t M, int64_t N, int64_t K, double alpha,
                             const double* A, int64_t lda, const double* B, int64_t ldb,
-                            bool transB, double beta, double* C, int64_t ldc, bool lower_tiles) {
+                            bool transB, double beta, double* C, int64_t ldc, bool lower_tiles, GemmTri tri) {
     if (M <= 0 || N <= 0) return GPTQ_OK;
+    if (lower_tiles && tri != GEMM_TRI_NONE) return GPTQ_ERR_INVALID_ARG;
     if (K <= 0) {
         if (beta == 1.0) return GPTQ_OK;
         return GPTQ_ERR_UNSUPPORTED;
@@ -237,11 +253,11 @@ gptq_status launch_gemm_f64(hipStream_t s, int64_t M, int64_t N, int64_t K, doub
     if (lower_tiles && M != N) return GPTQ_ERR_INVALID_ARG;
     const bool vec = ((uintptr_t)A % 16 == 0) && (lda % 2 == 0) && ((uintptr_t)B % 16 == 0) && (ldb % 2 == 0);
     if (transB) {
-        if (lower_tiles) launch_sel<true, true>(s, vec, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
-        else launch_sel<true, false>(s, vec, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
+        if (lower_tiles) launch_sel<true, true>(s, vec, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, (int)tri);
+        else launch_sel<true, false>(s, vec, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, (int)tri);
     } else {
-        if (lower_tiles) launch_sel<false, true>(s, vec, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
-        else launch_sel<false, false>(s, vec, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
+        if (lower_tiles) launch_sel<false, true>(s, vec, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, (int)tri);
+        else launch_sel<false, false>(s, vec, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, (int)tri);
     }
     GPTQ_LAUNCH_CHECK();
     return GPTQ_OK;

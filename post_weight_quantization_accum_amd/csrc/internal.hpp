@@ -5,6 +5,13 @@
 
 namespace gptq {
 
+// Triangular structure of one operand, used to skip the zero part of K
+// (the operand's zero entries inside the tile's range must be stored zeros):
+//   KEND_ROW: A is lower triangular (A[m][k] = 0 for k > m): K ends at the tile's last row;
+//   KEND_COL: op(B) is upper triangular (zero for k > n): K ends at the tile's last column;
+//   KBEG_COL: op(B) is lower triangular (zero for k < n): K starts at the tile's first column.
+enum GemmTri : int { GEMM_TRI_NONE = 0, GEMM_TRI_KEND_ROW = 1, GEMM_TRI_KEND_COL = 2, GEMM_TRI_KBEG_COL = 3 };
+
 // C = alpha * A * op(B) + beta * C in float64 on MFMA (128x128 or 64x64
 // output tiles).  A: M x K row-major (lda); op(B) = B (K x N, ldb) or B^T
 // (B is N x K, ldb).
@@ -15,7 +22,8 @@ namespace gptq {
 // B): each tile reads all of K before it writes.
 gptq_status launch_gemm_f64(hipStream_t s, int64_t M, int64_t N, int64_t K, double alpha,
                             const double* A, int64_t lda, const double* B, int64_t ldb,
-                            bool transB, double beta, double* C, int64_t ldc, bool lower_tiles);
+                            bool transB, double beta, double* C, int64_t ldc, bool lower_tiles,
+                            GemmTri tri = GEMM_TRI_NONE);
 
 // Hessian: H (upper) += 2 X^T X.  part: hessian_workspace_bytes(d) bytes
 // (float64 partial column sums; unused for fp32 inputs).

@@ -21,9 +21,9 @@
 //   M21 = -M22 T                      (M22 lower: K ends at the tile's row)
 // so the big products have K up to d/2 and run near the float64 MFMA peak,
 // where a right-looking blocked factorisation would be stuck at K = 64..128.
-// The leaves are 128x128 blocks factored and inverted by one workgroup with
-// the block held in registers (8x8 per thread).  L itself is never stored:
-// only M (written into H's buffer) is needed.
+// The leaves are 128x128 blocks factored and inverted in one pass by one
+// workgroup with the block held in registers (8x8 per thread).  L itself is
+// never stored: only M (written into H's buffer) is needed.
 //
 // Workspace layout (byte offsets):
 //   [0, 256)             int flags[N_FLAGS]; double lambda at 64
@@ -38,11 +38,7 @@ namespace {
 constexpr int LEAF = 128;         // leaf block edge
 constexpr int LT = 8;             // register tile edge
 constexpr int NLT = LEAF / LT;    // register tiles per leaf edge
-constexpr int LEAF_TILES = NLT * (NLT + 1) / 2;  // lower tiles, one per thread
-constexpr int LEAF_THREADS = 192;
-constexpr int LDL = LEAF + 1;     // LDS row stride of the leaf factor (doubles)
-constexpr size_t LEAF_LDS = (size_t)(LEAF * LDL + 2 * LEAF) * sizeof(double);
-static_assert(LEAF_TILES <= LEAF_THREADS, "one lower tile per thread");
+constexpr int LEAF_THREADS = 512;  // two groups of NLT x NLT tile slots
 
 void split(int64_t n, int64_t& n1, int64_t& n2) {
     const int64_t nb = ceil_div(n, LEAF);
@@ -186,122 +182,152 @@ __global__ __launch_bounds__(256) void gather_reverse_kernel(const double* __res
 // Leaf of the recursion: the n x n (n <= 128) diagonal block of Hr at
 // offset o is factored, A = L L^T, and M = L^{-1} is written to the same
 // block of Mi (lower triangle, zeros above the diagonal; the padding up to
-// 128 acts as an identity block).
+// 128 acts as an identity block).  L itself is only ever held one column at
+// a time.
 //
-// Thread t < 136 holds lower register tile (rt, ct), ct <= rt, of 8x8.
-// Factor: right-looking, one column per step.  The owners of column j
-// publish it in LDS (unscaled, after the updates of steps < j); every thread
-// then applies A[r][c] -= A[r][j] A[c][j] / A[j][j] to its entries with
-// c > j, and the owners of column j+1 publish that column.  One barrier per
-// step.  The scaled column of L goes to LDS for the inverse.
-// Inverse: X = I, and for m = 0..127: X[m,:] /= L[m][m], published by the
-// owners of row m, then X[r,:] -= L[r][m] X[m,:] for r > m.
+// One pass over the 128 columns, one barrier per column.  Waves 0-3 hold A
+// and waves 4-7 hold X (-> L^{-1}), each thread one lower 8x8 register tile
+// (thread u of a group: column tile u/16, row tile u%16, so the tiles of a
+// column tile sit in one wave).  At column j:
+//   factor: A[r][c] -= l[r] l[c] for c > j, with l = column j of L;
+//   inverse: x_j = X[j,:] / L[j][j] is row j of L^{-1}, and
+//            X[r,:] -= l[r] x_j for r > j (forward substitution).
+// Then the wave owning column tile (j+1)/8 reads the next pivot from the
+// diagonal lane, scales column j+1 by its reciprocal square root and
+// publishes it; the owners of row j+1 of X publish that row.
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, lane);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), lane);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// 1/sqrt(p) for a positive normal p: hardware estimate and two Newton steps
+// (each squares the relative error), good to about one ulp.
+__device__ __forceinline__ double rsqrt_nr(double p) {
+    double y = __builtin_amdgcn_rsq(p);
+    const double h = 0.5 * p;
+    double e = fma(-h * y, y, 0.5);
+    y = fma(y, e, y);
+    e = fma(-h * y, y, 0.5);
+    return fma(y, e, y);
+}
+
 __global__ __launch_bounds__(LEAF_THREADS) void leaf_chol_inv_kernel(const double* __restrict__ A, double* Mi,
                                                                      int64_t d, int64_t o, int n, int* flags) {
-    extern __shared__ double smem[];
-    double* Ls = smem;                 // [LEAF][LDL]
-    double* cb = smem + LEAF * LDL;    // [2][LEAF] column / row exchange
+    __shared__ double lb[2][LEAF];  // column j of L (scaled), zero above the pivot
+    __shared__ double xb[2][LEAF];  // row j of X before scaling
+    __shared__ double rsb[2];       // 1 / L[j][j]
     const int t = threadIdx.x;
-    const bool own = t < LEAF_TILES;
-    int rt = 0, ct = 0;
-    if (own) {
-        while ((rt + 1) * (rt + 2) / 2 <= t) ++rt;
-        ct = t - rt * (rt + 1) / 2;
-    }
+    const bool inv_grp = t >= 256;
+    const int u = t & 255;
+    const int ct = u >> 4, rt = u & 15;
+    const bool own = rt >= ct;
     const int r0 = rt * LT, c0 = ct * LT;
+    const int wave = u >> 6, lane = t & 63;
 
-    double a[LT][LT];
+    double v[LT][LT];
 #pragma unroll
     for (int i = 0; i < LT; ++i)
 #pragma unroll
         for (int k = 0; k < LT; ++k) {
             const int r = r0 + i, c = c0 + k;
-            double v;
-            if (r < n && c < n) v = (c <= r) ? A[(o + r) * d + o + c] : 0.0;
-            else v = (r == c) ? 1.0 : 0.0;
-            a[i][k] = v;
+            double e = (r == c) ? 1.0 : 0.0;
+            if (!inv_grp && own && r < n && c < n) e = (c <= r) ? A[(o + r) * d + o + c] : 0.0;
+            v[i][k] = e;
         }
-    if (own && ct == 0) {
+
+    bool bad_pd = false, bad_nan = false;
+    // publish column 0 and row 0
+    if (!inv_grp && wave == 0) {
+        double piv = readlane_f64(v[0][0], 0);
+        if (!(piv > 0.0)) {
+            bad_nan |= isnan(piv);
+            bad_pd |= !isnan(piv);
+            piv = 1.0;
+        }
+        const double rs = rsqrt_nr(piv);
+        if (own && ct == 0) {
 #pragma unroll
-        for (int i = 0; i < LT; ++i) cb[r0 + i] = a[i][0];
+            for (int i = 0; i < LT; ++i) lb[0][r0 + i] = (r0 + i > 0) ? v[i][0] * rs : piv * rs;
+        }
+        if (lane == 0) rsb[0] = rs;
+    }
+    if (inv_grp && own && rt == 0) {
+#pragma unroll
+        for (int k = 0; k < LT; ++k) xb[0][c0 + k] = v[0][k];
     }
     __syncthreads();
 
-    bool bad_pd = false, bad_nan = false;
     for (int jb = 0; jb < NLT; ++jb) {
 #pragma unroll
         for (int jj = 0; jj < LT; ++jj) {
             const int j = jb * LT + jj;
-            const double* cj = cb + (j & 1) * LEAF;
-            double piv = cj[j];
-            if (!(piv > 0.0)) {
-                bad_nan |= isnan(piv);
-                bad_pd |= !isnan(piv);
-                piv = 1.0;
-            }
-            const double sq = sqrt(piv);
-            const double inv = 1.0 / piv;
-            const double rs = 1.0 / sq;
-            if (t < LEAF) Ls[t * LDL + j] = (t > j) ? cj[t] * rs : ((t == j) ? sq : 0.0);
-            if (own && c0 + LT - 1 > j) {
-                double cr[LT], cc[LT];
+            const int cur = j & 1, nxt = cur ^ 1;
+            const int kn = (jj + 1) % LT;          // register column of j+1
+            const int ctn = jb + (jj + 1) / LT;    // column / row tile of j+1
+            if (!inv_grp) {
+                if (own && c0 + LT - 1 > j) {
+                    double cr[LT], cc[LT];
 #pragma unroll
-                for (int i = 0; i < LT; ++i) cr[i] = cj[r0 + i];
+                    for (int i = 0; i < LT; ++i) cr[i] = lb[cur][r0 + i];
 #pragma unroll
-                for (int k = 0; k < LT; ++k) cc[k] = (c0 + k > j) ? cj[c0 + k] * inv : 0.0;
+                    for (int k = 0; k < LT; ++k) cc[k] = (c0 + k > j) ? lb[cur][c0 + k] : 0.0;
 #pragma unroll
-                for (int i = 0; i < LT; ++i)
+                    for (int i = 0; i < LT; ++i)
 #pragma unroll
-                    for (int k = 0; k < LT; ++k) a[i][k] = fma(-cr[i], cc[k], a[i][k]);
-                // publish column j+1 (owned by the tiles of column tile (j+1)/8)
-                const int kn = (jj + 1) % LT;
-                const int ctn = jb + (jj + 1) / LT;
-                if (j + 1 < LEAF && ct == ctn) {
-                    double* cn = cb + ((j + 1) & 1) * LEAF;
+                        for (int k = 0; k < LT; ++k) v[i][k] = fma(-cr[i], cc[k], v[i][k]);
+                }
+                if (j + 1 < LEAF && wave == (ctn >> 2)) {
+                    const int lane_d = 16 * (ctn & 3) + ctn;
+                    double piv = readlane_f64(v[kn][kn], lane_d);
+                    if (!(piv > 0.0)) {
+                        bad_nan |= isnan(piv);
+                        bad_pd |= !isnan(piv);
+                        piv = 1.0;
+                    }
+                    const double rs = rsqrt_nr(piv);
+                    if (own && ct == ctn) {
 #pragma unroll
-                    for (int i = 0; i < LT; ++i) cn[r0 + i] = a[i][kn];
+                        for (int i = 0; i < LT; ++i) {
+                            const int r = r0 + i;
+                            lb[nxt][r] = (r > j + 1) ? v[i][kn] * rs : ((r == j + 1) ? piv * rs : 0.0);
+                        }
+                    }
+                    if (lane == lane_d) rsb[nxt] = rs;
+                }
+            } else {
+                const double rs = rsb[cur];
+                if (own && ct <= jb) {
+                    double xs[LT];
+#pragma unroll
+                    for (int k = 0; k < LT; ++k) xs[k] = xb[cur][c0 + k] * rs;
+                    if (r0 + LT - 1 > j) {
+                        double lr[LT];
+#pragma unroll
+                        for (int i = 0; i < LT; ++i) lr[i] = (r0 + i > j) ? lb[cur][r0 + i] : 0.0;
+#pragma unroll
+                        for (int i = 0; i < LT; ++i)
+#pragma unroll
+                            for (int k = 0; k < LT; ++k) v[i][k] = fma(-lr[i], xs[k], v[i][k]);
+                    }
+                    if (rt == jb) {
+#pragma unroll
+                        for (int k = 0; k < LT; ++k) v[jj][k] = xs[k];
+                    }
+                }
+                if (j + 1 < LEAF && own && rt == ctn) {
+#pragma unroll
+                    for (int k = 0; k < LT; ++k) xb[nxt][c0 + k] = v[kn][k];
                 }
             }
             __syncthreads();
         }
     }
-    if (t == 0 && bad_nan) raise_flag(flags, FLAG_NONFINITE);
-    if (t == 0 && bad_pd) raise_flag(flags, FLAG_NOT_PD);
+    if (bad_nan) raise_flag(flags, FLAG_NONFINITE);
+    if (bad_pd) raise_flag(flags, FLAG_NOT_PD);
 
-    // inverse of L (Ls), in the same register tiles
-    double x[LT][LT];
-#pragma unroll
-    for (int i = 0; i < LT; ++i)
-#pragma unroll
-        for (int k = 0; k < LT; ++k) x[i][k] = (r0 + i == c0 + k) ? 1.0 : 0.0;
-    for (int mb = 0; mb < NLT; ++mb) {
-#pragma unroll
-        for (int mm = 0; mm < LT; ++mm) {
-            const int m = mb * LT + mm;
-            double* rb = cb + (m & 1) * LEAF;
-            if (own && rt == mb) {
-                const double rinv = 1.0 / Ls[m * LDL + m];
-#pragma unroll
-                for (int k = 0; k < LT; ++k) {
-                    x[mm][k] *= rinv;
-                    rb[c0 + k] = x[mm][k];
-                }
-            }
-            __syncthreads();
-            if (own && ct <= mb && r0 + LT - 1 > m) {
-                double lr[LT], xr[LT];
-#pragma unroll
-                for (int i = 0; i < LT; ++i) lr[i] = (r0 + i > m) ? Ls[(r0 + i) * LDL + m] : 0.0;
-#pragma unroll
-                for (int k = 0; k < LT; ++k) xr[k] = rb[c0 + k];
-#pragma unroll
-                for (int i = 0; i < LT; ++i)
-#pragma unroll
-                    for (int k = 0; k < LT; ++k) x[i][k] = fma(-lr[i], xr[k], x[i][k]);
-            }
-        }
-    }
-    if (own) {
+    if (inv_grp && own) {
 #pragma unroll
         for (int i = 0; i < LT; ++i) {
             const int r = r0 + i;
@@ -309,7 +335,7 @@ __global__ __launch_bounds__(LEAF_THREADS) void leaf_chol_inv_kernel(const doubl
 #pragma unroll
             for (int k = 0; k < LT; ++k) {
                 const int c = c0 + k;
-                if (c < n) Mi[(o + r) * d + o + c] = x[i][k];
+                if (c < n) Mi[(o + r) * d + o + c] = v[i][k];
             }
         }
     }
@@ -351,8 +377,7 @@ struct Rec {
 gptq_status chol_inv(const Rec& c, int64_t o, int64_t n) {
     const int64_t d = c.d;
     if (n <= LEAF) {
-        hipLaunchKernelGGL(leaf_chol_inv_kernel, dim3(1), dim3(LEAF_THREADS), LEAF_LDS, c.s, c.L, c.M, d, o, (int)n,
-                           c.flags);
+        hipLaunchKernelGGL(leaf_chol_inv_kernel, dim3(1), dim3(LEAF_THREADS), 0, c.s, c.L, c.M, d, o, (int)n, c.flags);
         GPTQ_LAUNCH_CHECK();
         return GPTQ_OK;
     }
@@ -389,8 +414,6 @@ size_t hinv_workspace_bytes(int64_t d) {
 gptq_status hinv_launch(double* H, int64_t d, const gptq_config* cfg, int32_t* perm, void* ws,
                         hipStream_t s, int* host_flags) {
     Ws w = carve(ws, d);
-    GPTQ_HIP(hipFuncSetAttribute((const void*)leaf_chol_inv_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                 (int)LEAF_LDS));
     GPTQ_HIP(hipMemsetAsync(w.flags, 0, 256, s));
 
     hipLaunchKernelGGL(diag_stats_kernel, dim3(1), dim3(1024), 0, s, H, d, cfg->damp, w.lambda, w.diag, w.flags);

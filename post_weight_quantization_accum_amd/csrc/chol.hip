@@ -28,8 +28,9 @@
 // Workspace layout (byte offsets):
 //   [0, 256)             int flags[N_FLAGS]; double lambda at 64
 //   [256, +8d)           diag(H), contiguous (act-order keys)
+//   [.., +4d)            inverse permutation
 //   [.., + d*d*8)        Hr (lower triangle); T blocks replace the A21 blocks
-//   [.., + max n1*n2*8)  L21 of the node being processed
+//   per depth k          L21 scratch, max n1*n2 doubles over the nodes at depth k
 #include "internal.hpp"
 
 namespace gptq {
@@ -46,39 +47,49 @@ void split(int64_t n, int64_t& n1, int64_t& n2) {
     n2 = n - n1;
 }
 
+constexpr int MAX_DEPTH = 16;  // d <= 2^20 gives at most 13 levels above the leaves
+
+// Per recursion depth, the largest n1 x n2 of a node there (L21 scratch).
+void depth_sizes(int64_t n, int depth, size_t* sz) {
+    if (n <= LEAF) return;
+    int64_t n1, n2;
+    split(n, n1, n2);
+    const size_t m = (size_t)n1 * (size_t)n2;
+    if (m > sz[depth]) sz[depth] = m;
+    depth_sizes(n1, depth + 1, sz);
+    depth_sizes(n2, depth + 1, sz);
+}
+
 struct Ws {
     int* flags;
     double* lambda;
     double* diag;
+    int32_t* pinv;
     double* L;
-    double* tmp;
+    double* tmp[MAX_DEPTH];
 };
 
-size_t l_offset(int64_t d) { return align_up(256 + (size_t)d * sizeof(double), 256); }
-size_t tmp_offset(int64_t d) { return align_up(l_offset(d) + (size_t)d * (size_t)d * sizeof(double), 256); }
-
-// Largest n1 x n2 over all nodes of the recursion (not always the top one:
-// d = 257 splits 256 + 1, and the 256 below needs 128 x 128).
-size_t tmp_doubles(int64_t n) {
-    if (n <= LEAF) return 0;
-    int64_t n1, n2;
-    split(n, n1, n2);
-    size_t m = (size_t)n1 * (size_t)n2;
-    const size_t a = tmp_doubles(n1), b = tmp_doubles(n2);
-    if (a > m) m = a;
-    if (b > m) m = b;
-    return m;
-}
-
-Ws carve(void* ws, int64_t d) {
-    char* p = (char*)ws;
-    Ws w;
-    w.flags = (int*)p;
-    w.lambda = (double*)(p + 64);
-    w.diag = (double*)(p + 256);
-    w.L = (double*)(p + l_offset(d));
-    w.tmp = (double*)(p + tmp_offset(d));
-    return w;
+// Layout: flags/lambda | diag (d doubles) | pinv (d ints) | Hr (d*d) | one L21
+// scratch per depth; returns the total size.
+size_t layout(int64_t d, Ws* w, char* p) {
+    size_t off = 256;
+    if (w) w->diag = (double*)(p + off);
+    off = align_up(off + (size_t)d * sizeof(double), 256);
+    if (w) w->pinv = (int32_t*)(p + off);
+    off = align_up(off + (size_t)d * sizeof(int32_t), 256);
+    if (w) w->L = (double*)(p + off);
+    off = align_up(off + (size_t)d * (size_t)d * sizeof(double), 256);
+    size_t sz[MAX_DEPTH] = {};
+    depth_sizes(d, 0, sz);
+    for (int k = 0; k < MAX_DEPTH; ++k) {
+        if (w) w->tmp[k] = (double*)(p + off);
+        off = align_up(off + sz[k] * sizeof(double), 256);
+    }
+    if (w) {
+        w->flags = (int*)p;
+        w->lambda = (double*)(p + 64);
+    }
+    return off;
 }
 
 // lambda = damp * mean(diag H); copies the diagonal out and flags
@@ -103,35 +114,54 @@ __global__ __launch_bounds__(1024) void diag_stats_kernel(const double* __restri
     if (t == 0) *lambda = damp * (part[0] / (double)d);
 }
 
-// act-order: perm[rank(j)] = j, rank by (descending diag, ascending index).
-// NaN keys sort last; the ranks always form a permutation.
-__device__ __forceinline__ bool before(double ki, int64_t i, double kj, int64_t j) {
-    const bool ni = isnan(ki), nj = isnan(kj);
-    if (ni || nj) return (ni == nj) ? (i < j) : nj;
-    return (ki > kj) || (ki == kj && i < j);
-}
-
-__global__ __launch_bounds__(64) void rank_kernel(const double* __restrict__ diag, int64_t d, int32_t* perm) {
+// act-order: perm[rank(j)] = j and pinv[j] = rank(j), rank by (descending
+// diag, ascending index).  NaN keys are counted as -inf (H with a non-finite
+// entry is rejected anyway); the ranks always form a permutation.
+// 64 columns j per block, each scanned by 4 threads over a quarter of every
+// 2048-key tile; the partial counts are summed in LDS.
+__global__ __launch_bounds__(256) void rank_kernel(const double* __restrict__ diag, int64_t d, int32_t* perm,
+                                                   int32_t* pinv) {
     __shared__ double keys[2048];
-    const int64_t j = (int64_t)blockIdx.x * 64 + threadIdx.x;
-    const double kj = (j < d) ? diag[j] : 0.0;
-    int64_t rank = 0;
+    __shared__ int part_rank[4][64];
+    const int jl = threadIdx.x & 63, part = threadIdx.x >> 6;
+    const int64_t j = (int64_t)blockIdx.x * 64 + jl;
+    double kj = (j < d) ? diag[j] : 0.0;
+    if (isnan(kj)) kj = -INFINITY;
+    int rank = 0;
     for (int64_t base = 0; base < d; base += 2048) {
         __syncthreads();
-        for (int e = threadIdx.x; e < 2048; e += 64) {
+        for (int e = threadIdx.x; e < 2048; e += 256) {
             const int64_t i = base + e;
-            keys[e] = (i < d) ? diag[i] : 0.0;
+            double v = (i < d) ? diag[i] : -INFINITY;
+            keys[e] = isnan(v) ? -INFINITY : v;
         }
         __syncthreads();
         const int64_t lim = (d - base < 2048) ? d - base : 2048;
-        for (int64_t e = 0; e < lim; ++e) rank += before(keys[e], base + e, kj, j) ? 1 : 0;
+        const int e0 = part * 512;
+        const int e1 = (e0 + 512 < lim) ? e0 + 512 : (int)lim;
+        // keys before j in the order: larger, or equal with a smaller index
+        const int64_t jrel = j - base;
+#pragma unroll 8
+        for (int e = e0; e < e1; ++e) {
+            const double ki = keys[e];
+            rank += (ki > kj || (ki == kj && e < jrel)) ? 1 : 0;
+        }
     }
-    if (j < d) perm[rank] = (int32_t)j;
+    part_rank[part][jl] = rank;
+    __syncthreads();
+    if (part == 0 && j < d) {
+        const int r = part_rank[0][jl] + part_rank[1][jl] + part_rank[2][jl] + part_rank[3][jl];
+        perm[r] = (int32_t)j;
+        pinv[j] = r;
+    }
 }
 
-__global__ void iota_kernel(int32_t* perm, int64_t d) {
+__global__ void iota_kernel(int32_t* perm, int32_t* pinv, int64_t d) {
     const int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (k < d) perm[k] = (int32_t)k;
+    if (k < d) {
+        perm[k] = (int32_t)k;
+        pinv[k] = (int32_t)k;
+    }
 }
 
 // Mirror the upper triangle into the lower one (32x32 tiles through LDS) and
@@ -164,18 +194,25 @@ __global__ __launch_bounds__(256) void symmetrize_kernel(double* H, int64_t d, i
 }
 
 // Hr[a][b] = H[p[d-1-a]][p[d-1-b]] (+ lambda on the diagonal), b <= a.
+// One block per row a reads row p[d-1-a] of the (symmetrised) H in order,
+// coalesced, and scatters entry c to b = d-1-pinv[c]; the scattered stores
+// of one row merge in L2.
 __global__ __launch_bounds__(256) void gather_reverse_kernel(const double* __restrict__ H, int64_t d,
                                                              const int32_t* __restrict__ perm,
+                                                             const int32_t* __restrict__ pinv,
                                                              const double* __restrict__ lambda, double* Hr) {
     const int64_t a = blockIdx.x;
     const int64_t pa = perm[d - 1 - a];
     const double lam = *lambda;
     const double* row = H + pa * d;
-    for (int64_t b = threadIdx.x; b <= a; b += 256) {
-        const int64_t pb = perm[d - 1 - b];
-        double v = row[pb];
-        if (b == a) v += lam;
-        Hr[a * d + b] = v;
+    double* out = Hr + a * d;
+    for (int64_t c = threadIdx.x; c < d; c += 256) {
+        const int64_t b = d - 1 - pinv[c];
+        if (b <= a) {
+            double v = row[c];
+            if (b == a) v += lam;
+            out[b] = v;
+        }
     }
 }
 
@@ -365,22 +402,48 @@ __global__ __launch_bounds__(256) void rotate_inplace_kernel(double* M, int64_t 
     }
 }
 
+// T = L21 M11 of a node does not feed the recursion into A22, only the
+// final M21 = -M22 T: it runs on a second stream, overlapping the
+// latency-bound leaves and small products of that recursion.  Each depth
+// has its own L21 scratch, so the recursion below cannot overwrite the
+// operand of a T still in flight; the events of a depth are reused only
+// after the main stream has waited for that depth's previous T.
 struct Rec {
-    hipStream_t s;
-    double* L;    // Hr, lower; T blocks replace A21 blocks
-    double* M;    // inverse factor (lower)
-    double* tmp;  // L21 of the current node
-    int64_t d;
-    int* flags;
+    hipStream_t s = nullptr, side = nullptr;
+    double* L = nullptr;    // Hr, lower; T blocks replace A21 blocks
+    double* M = nullptr;    // inverse factor (lower)
+    double* tmp[MAX_DEPTH] = {};
+    int64_t d = 0;
+    int* flags = nullptr;
+    hipEvent_t l21_ready[MAX_DEPTH] = {}, t_done[MAX_DEPTH] = {};
+    hipError_t init() {
+        hipError_t e = hipStreamCreateWithFlags(&side, hipStreamNonBlocking);
+        for (int k = 0; k < MAX_DEPTH && e == hipSuccess; ++k) {
+            e = hipEventCreateWithFlags(&l21_ready[k], hipEventDisableTiming);
+            if (e == hipSuccess) e = hipEventCreateWithFlags(&t_done[k], hipEventDisableTiming);
+        }
+        return e;
+    }
+    ~Rec() {
+        if (side) {
+            (void)hipStreamSynchronize(side);
+            (void)hipStreamDestroy(side);
+        }
+        for (int k = 0; k < MAX_DEPTH; ++k) {
+            if (l21_ready[k]) (void)hipEventDestroy(l21_ready[k]);
+            if (t_done[k]) (void)hipEventDestroy(t_done[k]);
+        }
+    }
 };
 
-gptq_status chol_inv(const Rec& c, int64_t o, int64_t n) {
+gptq_status chol_inv(const Rec& c, int64_t o, int64_t n, int depth) {
     const int64_t d = c.d;
     if (n <= LEAF) {
         hipLaunchKernelGGL(leaf_chol_inv_kernel, dim3(1), dim3(LEAF_THREADS), 0, c.s, c.L, c.M, d, o, (int)n, c.flags);
         GPTQ_LAUNCH_CHECK();
         return GPTQ_OK;
     }
+    if (depth >= MAX_DEPTH) return GPTQ_ERR_UNSUPPORTED;
     int64_t n1, n2;
     split(n, n1, n2);
     double* A21 = c.L + (o + n1) * d + o;   // becomes T
@@ -388,50 +451,62 @@ gptq_status chol_inv(const Rec& c, int64_t o, int64_t n) {
     const double* M11 = c.M + o * d + o;
     const double* M22 = c.M + (o + n1) * d + o + n1;
     double* M21 = c.M + (o + n1) * d + o;
-    gptq_status st = chol_inv(c, o, n1);
+    double* L21 = c.tmp[depth];
+    gptq_status st = chol_inv(c, o, n1, depth + 1);
     if (st != GPTQ_OK) return st;
     // L21 = A21 M11^T
-    st = launch_gemm_f64(c.s, n2, n1, n1, 1.0, A21, d, M11, d, true, 0.0, c.tmp, n1, false, GEMM_TRI_KEND_COL);
+    st = launch_gemm_f64(c.s, n2, n1, n1, 1.0, A21, d, M11, d, true, 0.0, L21, n1, false, GEMM_TRI_KEND_COL);
     if (st != GPTQ_OK) return st;
     // A22 -= L21 L21^T
-    st = launch_gemm_f64(c.s, n2, n2, n1, -1.0, c.tmp, n1, c.tmp, n1, true, 1.0, A22, d, true);
+    st = launch_gemm_f64(c.s, n2, n2, n1, -1.0, L21, n1, L21, n1, true, 1.0, A22, d, true);
     if (st != GPTQ_OK) return st;
-    // T = L21 M11 (into A21's place)
-    st = launch_gemm_f64(c.s, n2, n1, n1, 1.0, c.tmp, n1, M11, d, false, 0.0, A21, d, false, GEMM_TRI_KBEG_COL);
+    // T = L21 M11 (into A21's place), on the side stream
+    GPTQ_HIP(hipEventRecord(c.l21_ready[depth], c.s));
+    GPTQ_HIP(hipStreamWaitEvent(c.side, c.l21_ready[depth], 0));
+    st = launch_gemm_f64(c.side, n2, n1, n1, 1.0, L21, n1, M11, d, false, 0.0, A21, d, false, GEMM_TRI_KBEG_COL);
     if (st != GPTQ_OK) return st;
-    st = chol_inv(c, o + n1, n2);
+    GPTQ_HIP(hipEventRecord(c.t_done[depth], c.side));
+    st = chol_inv(c, o + n1, n2, depth + 1);
     if (st != GPTQ_OK) return st;
     // M21 = -M22 T
+    GPTQ_HIP(hipStreamWaitEvent(c.s, c.t_done[depth], 0));
     return launch_gemm_f64(c.s, n2, n1, n2, -1.0, M22, d, A21, d, false, 0.0, M21, d, false, GEMM_TRI_KEND_ROW);
 }
 
 }  // namespace
 
-size_t hinv_workspace_bytes(int64_t d) {
-    return tmp_offset(d) + tmp_doubles(d) * sizeof(double);
-}
+size_t hinv_workspace_bytes(int64_t d) { return layout(d, nullptr, nullptr); }
 
 gptq_status hinv_launch(double* H, int64_t d, const gptq_config* cfg, int32_t* perm, void* ws,
                         hipStream_t s, int* host_flags) {
-    Ws w = carve(ws, d);
+    Ws w;
+    layout(d, &w, (char*)ws);
     GPTQ_HIP(hipMemsetAsync(w.flags, 0, 256, s));
 
     hipLaunchKernelGGL(diag_stats_kernel, dim3(1), dim3(1024), 0, s, H, d, cfg->damp, w.lambda, w.diag, w.flags);
     GPTQ_LAUNCH_CHECK();
     if (cfg->act_order)
-        hipLaunchKernelGGL(rank_kernel, dim3((unsigned)ceil_div(d, 64)), dim3(64), 0, s, w.diag, d, perm);
+        hipLaunchKernelGGL(rank_kernel, dim3((unsigned)ceil_div(d, 64)), dim3(256), 0, s, w.diag, d, perm, w.pinv);
     else
-        hipLaunchKernelGGL(iota_kernel, dim3((unsigned)ceil_div(d, 256)), dim3(256), 0, s, perm, d);
+        hipLaunchKernelGGL(iota_kernel, dim3((unsigned)ceil_div(d, 256)), dim3(256), 0, s, perm, w.pinv, d);
     GPTQ_LAUNCH_CHECK();
     const int64_t T32 = ceil_div(d, 32);
     hipLaunchKernelGGL(symmetrize_kernel, dim3((unsigned)(T32 * (T32 + 1) / 2)), dim3(256), 0, s, H, d, w.flags);
     GPTQ_LAUNCH_CHECK();
-    hipLaunchKernelGGL(gather_reverse_kernel, dim3((unsigned)d), dim3(256), 0, s, H, d, perm, w.lambda, w.L);
+    hipLaunchKernelGGL(gather_reverse_kernel, dim3((unsigned)d), dim3(256), 0, s, H, d, perm, w.pinv, w.lambda,
+                       w.L);
     GPTQ_LAUNCH_CHECK();
 
     // H's buffer now receives M = L^{-1} (lower), then U = J M J in place.
-    Rec c{s, w.L, H, w.tmp, d, w.flags};
-    gptq_status st = chol_inv(c, 0, d);
+    Rec c;
+    GPTQ_HIP(c.init());
+    c.s = s;
+    c.L = w.L;
+    c.M = H;
+    for (int k = 0; k < MAX_DEPTH; ++k) c.tmp[k] = w.tmp[k];
+    c.d = d;
+    c.flags = w.flags;
+    gptq_status st = chol_inv(c, 0, d, 0);
     if (st != GPTQ_OK) return st;
     hipLaunchKernelGGL(rotate_inplace_kernel, dim3((unsigned)d), dim3(256), 0, s, H, d);
     GPTQ_LAUNCH_CHECK();

@@ -121,21 +121,27 @@ __global__ __launch_bounds__(256, 2) void gemm_f64_kernel(int64_t M, int64_t N, 
     __shared__ double sB[2][KC][G::LD];
 
     const int64_t b = blockIdx.x;
-    const int64_t lin = (b % 8) * per_xcd + b / 8;
-    if (lin >= n_tiles) return;
     int64_t tm, tn;
     if (LOWER) {
+        const int64_t lin = (b % 8) * per_xcd + b / 8;
+        if (lin >= n_tiles) return;
         tri_index(lin, tm, tn);
+    } else if (tri != GEMM_TRI_NONE && tiles_m >= 16) {
+        // triangular operand: tile work varies with the row or the column.
+        // XCD x takes row bands x, x+8, x+16, ... (whole bands: rows of A
+        // stay in its L2; every XCD gets light and heavy bands), heaviest
+        // rows / columns dispatched first.
+        const int64_t x = b % 8, q = b / 8;
+        const int64_t band = x + 8 * (q / tiles_n);
+        if (band >= tiles_m) return;
+        tm = (tri == GEMM_TRI_KEND_ROW) ? tiles_m - 1 - band : band;
+        tn = q % tiles_n;
+        if (tri == GEMM_TRI_KEND_COL) tn = tiles_n - 1 - tn;
     } else {
+        const int64_t lin = (b % 8) * per_xcd + b / 8;
+        if (lin >= n_tiles) return;
         tm = lin / tiles_n;
         tn = lin % tiles_n;
-        if (tri == GEMM_TRI_KEND_ROW) {
-            // work grows with the row: zig-zag the rows (last, first, second
-            // last, ...) so every XCD's contiguous share holds a balanced mix
-            tm = (tm & 1) ? (tm >> 1) : tiles_m - 1 - (tm >> 1);
-        } else if (tri == GEMM_TRI_KEND_COL) {
-            tn = tiles_n - 1 - tn;  // heaviest columns first
-        }
     }
     const int64_t m0 = tm * TILE, n0 = tn * TILE;
     // K range of this tile: the triangular operand is zero outside it
@@ -216,7 +222,8 @@ void launch_t(hipStream_t s, bool vec, int64_t M, int64_t N, int64_t K, double a
               const double* B, int64_t ldb, double beta, double* C, int64_t ldc, int tri) {
     const int64_t tiles_m = ceil_div(M, TILE), tiles_n = ceil_div(N, TILE);
     const int64_t n_tiles = LOWER ? tiles_m * (tiles_m + 1) / 2 : tiles_m * tiles_n;
-    const int64_t per_xcd = ceil_div(n_tiles, 8);
+    const int64_t per_xcd =
+        (!LOWER && tri != GEMM_TRI_NONE && tiles_m >= 16) ? ceil_div(tiles_m, 8) * tiles_n : ceil_div(n_tiles, 8);
     const dim3 grid((unsigned)(per_xcd * 8));
     if (vec)
         hipLaunchKernelGGL((gemm_f64_kernel<TILE, TRANS_B, LOWER, true>), grid, dim3(256), 0, s, M, N, K, alpha, A,

@@ -54,9 +54,8 @@ const char* gptq_status_string(gptq_status st) {
 const char* gptq_version(void) { return "0.1.0"; }
 
 size_t gptq_hessian_workspace(int64_t n_tok, int64_t d_in) {
-    (void)n_tok;
-    if (d_in <= 0 || d_in > MAX_DIM) return 0;
-    return hessian_workspace_bytes(d_in);
+    if (d_in <= 0 || d_in > MAX_DIM || n_tok < 0) return 0;
+    return hessian_workspace_bytes(n_tok, d_in);
 }
 
 gptq_status gptq_hessian_accumulate(double* H, const void* X, gptq_dtype x_dtype, int64_t n_tok, int64_t d_in,
@@ -64,8 +63,9 @@ gptq_status gptq_hessian_accumulate(double* H, const void* X, gptq_dtype x_dtype
     if (!H || !valid_dtype(x_dtype)) return GPTQ_ERR_INVALID_ARG;
     if (d_in <= 0 || d_in > MAX_DIM || n_tok < 0 || ld_x < d_in) return GPTQ_ERR_INVALID_ARG;
     if (n_tok > 0 && !X) return GPTQ_ERR_INVALID_ARG;
-    if (x_dtype != GPTQ_F32 && (!workspace || ws_bytes < hessian_workspace_bytes(d_in))) return GPTQ_ERR_WORKSPACE;
-    return hessian_launch(H, X, x_dtype, n_tok, d_in, ld_x, (double*)workspace, stream);
+    if (x_dtype != GPTQ_F32 && n_tok > 0 && (!workspace || ws_bytes < hessian_workspace_bytes(n_tok, d_in)))
+        return GPTQ_ERR_WORKSPACE;
+    return hessian_launch(H, X, x_dtype, n_tok, d_in, ld_x, workspace, stream);
 }
 
 size_t gptq_prepare_hinv_workspace(int64_t d_in) {

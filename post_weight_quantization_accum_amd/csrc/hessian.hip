@@ -2,31 +2,34 @@
 // upper triangle, on the gfx950 matrix cores.
 //
 // bf16 / fp16 activations: products are exact in float32, so the MFMA
-// v_mfma_f32_32x32x16_{bf16,f16} accumulates chunks of CHUNK tokens in
-// float32 registers (one launch per chunk); at the end of a launch the
+// v_mfma_f32_32x32x16_{bf16,f16} accumulates chunks of up to 32768 tokens
+// in float32 registers (one launch per chunk); at the end of a launch the
 // partial tile is added to H in float64 (a read-modify-write of the tile
-// that the workgroup owns alone, staged through LDS one wave-quarter at a
-// time); launches run in token order.
-// One workgroup owns one 256x256 tile of the upper triangle for a chunk,
-// chunks are added in token order, so the summation order is fixed and the
+// that the workgroup owns alone, staged through LDS one quarter at a time);
+// launches run in token order, so the summation order is fixed and the
 // result bit-reproducible.
 //
-// The diagonal is recomputed in float64 from the same staged values (squares
-// of bf16/fp16 values are exact in float64): the act-order key diag(H) then
+// The diagonal is recomputed in float64 from the same inputs (squares of
+// bf16/fp16 values are exact in float64): the act-order key diag(H) then
 // agrees with a float64 reference to rounding order, so the column order
 // does not depend on float32 accumulation error.
 //
-// Tiling: 8 wave64s per workgroup (two per SIMD), each owning a 128x64
-// part as 4x2 MFMA 32x32 tiles (128 float32 accumulators per lane).  X is token-major,
-// while each MFMA operand is 8 consecutive tokens of one column, so every
-// thread loads an 8-token x 8-column block with 16-byte loads, transposes it
-// in registers (v_perm_b32) and writes eight 16-byte column runs into LDS
-// laid out [column][token] (row stride 72 elements: conflict-free for both
-// the writes and the operand reads).  LDS is double-buffered and the next
-// stage's global loads are in flight while the current stage is multiplied.
+// Each MFMA operand is 8 consecutive tokens of one column, while X is
+// token-major.  A chunk is therefore first transposed (8x8 blocks in
+// registers, v_perm_b32) into a feature-major copy Xt, zero-padded to a
+// multiple of 256 features and of 32 tokens.  The SYRK kernel then streams
+// Xt straight from memory into LDS with buffer_load ... lds (no VGPR
+// staging) through a 4-stage ring of 32-token stages, three stages ahead of
+// the MFMAs, one barrier per stage.  Within a stage a feature row is 64
+// bytes (four 16-byte granules); granule g of row r is stored at slot
+// g ^ ((r >> 2) & 3), so the 32 rows read by one MFMA operand fetch hit
+// distinct banks.
+//
+// Tiling: one workgroup per 256x256 tile of the upper triangle, 8 wave64s
+// (two per SIMD), each owning a 128x64 part as 4x2 MFMA 32x32 tiles.
 // Workgroups are mapped to tiles so that the ~32 workgroups resident on one
 // XCD work on a compact block of about 6x6 tiles (about 12 column panels of
-// X shared through that XCD's L2).
+// Xt shared through that XCD's L2).
 //
 // fp32 activations take a float64 path (products of fp32 values are exact
 // in float64): a plain tiled float64 kernel.
@@ -36,11 +39,14 @@ namespace gptq {
 namespace {
 
 constexpr int BT = 256;          // tile edge
-constexpr int KT = 64;           // tokens per LDS stage
-constexpr int SK = KT + 8;       // LDS row stride in 16-bit elements (144 B)
+constexpr int KT = 32;           // tokens per LDS stage
+constexpr int NSTAGE = 4;        // LDS ring depth
 constexpr int CHUNK = 32768;     // tokens accumulated in float32 before the float64 add
 constexpr int SP = 132;          // row stride (floats) of the staged 128x128 quarter
-constexpr int PANEL = BT * SK;   // 16-bit elements per panel buffer
+constexpr int PANEL_BYTES = BT * KT * 2;           // one 256-feature x 32-token panel
+constexpr int STAGE_BYTES = 2 * PANEL_BYTES;       // row panel + column panel
+constexpr int RING_BYTES = NSTAGE * STAGE_BYTES;   // 128 KiB
+constexpr size_t XT_MAX_BYTES = (size_t)1 << 30;   // transposed-chunk scratch cap
 
 constexpr int BAND = 6;  // tile rows per band of the tile enumeration
 
@@ -80,56 +86,6 @@ __device__ __forceinline__ double elem_f64<bf16x8_t>(uint16_t b) { return bf16_b
 template <>
 __device__ __forceinline__ double elem_f64<h16x8_t>(uint16_t b) { return f16_bits_to_f64(b); }
 
-// Buffer resources for one stage: resource r starts at token row
-// s*KT + r and covers the stage's valid rows from there on, so a lane's
-// offset (token group tg*8, column col) is in range exactly when token
-// s*KT + r + tg*8 exists.  Out-of-range loads return 0 without touching
-// memory.  The row offset lives in the (uniform) resource, not in soffset,
-// because the range check applies to the vector offset only.
-struct StageRsrc {
-    __amdgpu_buffer_rsrc_t r[8];
-};
-
-__device__ __forceinline__ StageRsrc stage_rsrc(const uint16_t* X, int64_t s, int64_t ld, int64_t n_tok) {
-    StageRsrc o;
-    const int64_t t0 = s * KT;
-    int64_t rows = n_tok - t0;
-    rows = rows > KT ? KT : rows;
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-        const int64_t left = rows - r;
-        const int nrec = left > 0 ? (int)(left * ld * 2) : 0;
-        o.r[r] = __builtin_amdgcn_make_buffer_rsrc((void*)(X + (t0 + r) * ld), (short)0, nrec, 0x00020000);
-    }
-    return o;
-}
-
-constexpr uint32_t OOB = 0x80000000u;  // a byte offset beyond every resource's range
-
-// 8 tokens x 8 columns, one u32x4 (8 columns) per token.  off is the byte
-// offset of (token tg*8, column col) from a resource's first row, or OOB.
-template <bool VEC>
-__device__ __forceinline__ void load_block(u32x4_t v[8], const StageRsrc& rs, uint32_t off, int64_t col,
-                                           int64_t d) {
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-        if (VEC) {
-            v[r] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs.r[r], (int)off, 0, 0));
-        } else {
-            uint32_t e[8];
-#pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                const uint32_t o = (col + c < d) ? off + 2u * c : OOB;
-                e[c] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs.r[r], (int)o, 0, 0);
-            }
-            v[r].x = e[0] | (e[1] << 16);
-            v[r].y = e[2] | (e[3] << 16);
-            v[r].z = e[4] | (e[5] << 16);
-            v[r].w = e[6] | (e[7] << 16);
-        }
-    }
-}
-
 __device__ __forceinline__ uint32_t lo_pair(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
 __device__ __forceinline__ uint32_t hi_pair(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
 
@@ -137,58 +93,157 @@ __device__ __forceinline__ uint32_t word(const u32x4_t& v, int i) {
     return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
 }
 
-// Transpose the 8x8 block and store column runs of 8 tokens into LDS.
-__device__ __forceinline__ void store_block(uint16_t* buf, const u32x4_t v[8], int cg, int tg) {
+// Xt[f][t] = X[t][f] for one chunk: n_tok tokens, Xt row stride ch tokens,
+// zeros for t >= n_tok (up to ch) and for d <= f < d_pad; also the float64
+// sums of squares of the block's 512 tokens per feature (diagonal of H).
+// A block covers 512 tokens x 256 features in tiles of 64 tokens: a thread
+// loads 8 tokens x 8 features (16-byte loads, 32 lanes along the features:
+// 512 contiguous bytes per token row), transposes them in registers
+// (v_perm_b32), and the tile goes through LDS so that every store writes
+// whole 128-byte runs of one feature row.
+constexpr int TSPAN = 512;      // tokens per transpose block
+constexpr int TT = 64;          // tokens per tile
+constexpr int TLD = TT + 8;     // LDS row stride (16-bit elements)
+
+template <typename Tag, bool VEC>
+__global__ __launch_bounds__(256) void transpose_kernel(const uint16_t* __restrict__ X, int64_t n_tok, int64_t d,
+                                                        int64_t ld, uint16_t* __restrict__ Xt, int64_t ch,
+                                                        double* __restrict__ colsq) {
+    __shared__ __attribute__((aligned(16))) uint16_t tile[256 * TLD];
+    __shared__ double red[8][256];
+    const int t = threadIdx.x;
+    const int tg = t >> 5, fg = t & 31;
+    const int64_t fblk = (int64_t)blockIdx.y * 256;
+    const int64_t f = fblk + fg * 8;
+    double sq[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int tt = 0; tt < TSPAN / TT; ++tt) {
+        const int64_t tbase = (int64_t)blockIdx.x * TSPAN + tt * TT;
+        if (tbase >= ch) break;
+        const int64_t t0 = tbase + tg * 8;
+        u32x4_t v[8];
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const uint32_t w0 = word(v[0], p), w1 = word(v[1], p), w2 = word(v[2], p), w3 = word(v[3], p);
-        const uint32_t w4 = word(v[4], p), w5 = word(v[5], p), w6 = word(v[6], p), w7 = word(v[7], p);
-        u32x4_t lo, hi;
-        lo.x = lo_pair(w0, w1); lo.y = lo_pair(w2, w3); lo.z = lo_pair(w4, w5); lo.w = lo_pair(w6, w7);
-        hi.x = hi_pair(w0, w1); hi.y = hi_pair(w2, w3); hi.z = hi_pair(w4, w5); hi.w = hi_pair(w6, w7);
-        *(u32x4_t*)&buf[(cg * 8 + 2 * p) * SK + tg * 8] = lo;
-        *(u32x4_t*)&buf[(cg * 8 + 2 * p + 1) * SK + tg * 8] = hi;
+        for (int r = 0; r < 8; ++r) {
+            const int64_t tok = t0 + r;
+            u32x4_t x = {0u, 0u, 0u, 0u};
+            if (tok < n_tok) {
+                const uint16_t* p = X + tok * ld + f;
+                if (VEC) {
+                    if (f < d) x = *(const u32x4_t*)p;
+                } else {
+                    uint32_t e[8];
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) e[c] = (f + c < d) ? (uint32_t)p[c] : 0u;
+                    x.x = e[0] | (e[1] << 16);
+                    x.y = e[2] | (e[3] << 16);
+                    x.z = e[4] | (e[5] << 16);
+                    x.w = e[6] | (e[7] << 16);
+                }
+            }
+            v[r] = x;
+        }
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const uint32_t w = word(v[r], p);
+                const double x0 = elem_f64<Tag>((uint16_t)(w & 0xFFFFu));
+                const double x1 = elem_f64<Tag>((uint16_t)(w >> 16));
+                sq[2 * p] = fma(x0, x0, sq[2 * p]);
+                sq[2 * p + 1] = fma(x1, x1, sq[2 * p + 1]);
+            }
+        __syncthreads();  // the previous tile has been written out
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const uint32_t w0 = word(v[0], p), w1 = word(v[1], p), w2 = word(v[2], p), w3 = word(v[3], p);
+            const uint32_t w4 = word(v[4], p), w5 = word(v[5], p), w6 = word(v[6], p), w7 = word(v[7], p);
+            u32x4_t lo, hi;
+            lo.x = lo_pair(w0, w1); lo.y = lo_pair(w2, w3); lo.z = lo_pair(w4, w5); lo.w = lo_pair(w6, w7);
+            hi.x = hi_pair(w0, w1); hi.y = hi_pair(w2, w3); hi.z = hi_pair(w4, w5); hi.w = hi_pair(w6, w7);
+            *(u32x4_t*)&tile[(fg * 8 + 2 * p) * TLD + tg * 8] = lo;
+            *(u32x4_t*)&tile[(fg * 8 + 2 * p + 1) * TLD + tg * 8] = hi;
+        }
+        __syncthreads();
+        // 256 feature rows x 8 granules of 8 tokens; 8 lanes per row
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int e = k * 256 + t;
+            const int fr = e >> 3, gq = e & 7;
+            const int64_t tok = tbase + gq * 8;
+            if (tok < ch)
+                *(u32x4_t*)&Xt[(fblk + fr) * ch + tok] = *(const u32x4_t*)&tile[fr * TLD + gq * 8];
+        }
+    }
+    // column sums of squares: the 8 token groups in a fixed order
+#pragma unroll
+    for (int c = 0; c < 8; ++c) red[tg][fg * 8 + c] = sq[c];
+    __syncthreads();
+    const int64_t fc = fblk + t;
+    if (fc < d) {
+        double sum = 0.0;
+#pragma unroll
+        for (int g = 0; g < 8; ++g) sum += red[g][t];
+        colsq[(int64_t)blockIdx.x * d + fc] = sum;
     }
 }
 
-template <typename Tag>
-__device__ __forceinline__ void diag_accumulate(double dsq[8], const u32x4_t v[8]) {
-#pragma unroll
-    for (int r = 0; r < 8; ++r)
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const uint32_t w = word(v[r], p);
-            const double x0 = elem_f64<Tag>((uint16_t)(w & 0xFFFFu));
-            const double x1 = elem_f64<Tag>((uint16_t)(w >> 16));
-            dsq[2 * p] = fma(x0, x0, dsq[2 * p]);
-            dsq[2 * p + 1] = fma(x1, x1, dsq[2 * p + 1]);
-        }
+// diag(H) += 2 * sum of the chunk's per-block column sums, blocks in order.
+__global__ __launch_bounds__(256) void diag_add_kernel(const double* __restrict__ colsq, int64_t nblk, int64_t d,
+                                                       double* __restrict__ H) {
+    const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (c >= d) return;
+    double sum = 0.0;
+    for (int64_t b = 0; b < nblk; ++b) sum += colsq[b * d + c];
+    H[c * d + c] += 2.0 * sum;
 }
 
-template <typename Tag, bool VEC>
-__global__ __launch_bounds__(512) void hess_syrk_kernel(double* __restrict__ H, const uint16_t* __restrict__ X,
-                                                        int64_t n_tok, int64_t d, int64_t ld, int64_t T,
-                                                        int64_t n_tiles, int64_t per_xcd) {
-    extern __shared__ __attribute__((aligned(16))) uint16_t lds[];  // [2 stages][2 panels][PANEL]
-    // XCD-grouped tile order: workgroup b runs on XCD b % 8; each XCD takes a
-    // contiguous range of the banded upper-triangle enumeration.
-    const int64_t b = blockIdx.x;
-    const int64_t lin = (b % 8) * per_xcd + b / 8;
-    if (lin >= n_tiles) return;
-    int64_t ti, tj;
-    upper_tile(lin, ti, tj, T);
-    const bool diag = (ti == tj);
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-    // 8 waves: wave (wr, wc) owns rows wr*128..+128 and columns wc*64..+64
-    // of the tile as 4x2 MFMA 32x32 tiles.  For staging, threads 0..255 load
-    // the row panel and threads 256..511 the column panel (idle on diagonal
-    // tiles, where the two panels coincide).
+// s_waitcnt with only the vector-memory count constrained (gfx9 encoding:
+// vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14; expcnt and lgkmcnt at
+// their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// One stage of one panel: 256 feature rows x 32 tokens = 16 KiB, moved by
+// 16 wave-wide 1 KiB DMA loads; wave w issues the two that cover rows
+// 32w .. 32w+31.  Lane l of a load fills LDS granule l of its 1 KiB block:
+// row r = block_row + l/4, slot l%4, which holds token granule
+// g = slot ^ ((r >> 2) & 3) of that row.
+__device__ __forceinline__ void dma_panel_rows(__amdgpu_buffer_rsrc_t rs, char* lds_panel, int row0, int lane,
+                                               int64_t tok0, int64_t ch) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int rblk = row0 + 16 * q;
+        const int r = rblk + (lane >> 2);
+        const int g = (lane & 3) ^ ((r >> 2) & 3);
+        const uint32_t voff = (uint32_t)(((int64_t)r * ch + tok0 + 8 * g) * 2);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(lds_panel + rblk * 64), 16, (int)voff, 0, 0, 0);
+    }
+}
+
+// MFMA operand fetch: row r of a staged panel, token granule g (8 tokens).
+__device__ __forceinline__ u32x4_t lds_operand(const char* lds_panel, int r, int g) {
+    return *(const u32x4_t*)(lds_panel + r * 64 + ((g ^ ((r >> 2) & 3)) << 4));
+}
+
+template <typename Tag, bool DIAG>
+__device__ __forceinline__ void syrk_tile(double* __restrict__ H, const uint16_t* __restrict__ Xt, int64_t ch,
+                                          int64_t d, int64_t ti, int64_t tj, char* lds) {
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int wr = wave >> 2, wc = wave & 3;
-    const int pt = t & 255, panel = t >> 8;
-    const int tg = lane & 7, cg = (pt >> 6) * 8 + (lane >> 3);
-    const bool loader = !(diag && panel == 1);
-    const int64_t col = (panel ? tj : ti) * BT + cg * 8;
+    const int64_t n_st = ch / KT;
+    // one resource per panel: 256 rows of ch tokens
+    const uint32_t pbytes = (uint32_t)(BT * ch * 2);
+    const __amdgpu_buffer_rsrc_t ra =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(Xt + ti * BT * ch), (short)0, (int)pbytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rb =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(Xt + tj * BT * ch), (short)0, (int)pbytes, 0x00020000);
+    const int row0 = wave * 32;
+    // loads issued per wave per stage
+    constexpr int NLD = DIAG ? 2 : 4;
 
     f16_t acc[4][2];
 #pragma unroll
@@ -198,40 +253,40 @@ __global__ __launch_bounds__(512) void hess_syrk_kernel(double* __restrict__ H, 
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    // this launch covers tokens [0, n_tok) of X (the caller offsets X per chunk)
-    const int64_t n_stages = ceil_div(n_tok, KT);
-    const uint32_t row_bytes = (uint32_t)(ld * 2);
-    const uint32_t off = (col < d && loader) ? (uint32_t)(tg * 8) * row_bytes + (uint32_t)(col * 2) : OOB;
-    u32x4_t va[8];
-    load_block<VEC>(va, stage_rsrc(X, 0, ld, n_tok), off, col, d);
-    if (loader) store_block(lds + panel * PANEL, va, cg, tg);
-    __syncthreads();
-    if (n_stages > 1) load_block<VEC>(va, stage_rsrc(X, 1, ld, n_tok), off, col, d);
+    auto issue = [&](int64_t st) {
+        char* sb = lds + (st % NSTAGE) * STAGE_BYTES;
+        dma_panel_rows(ra, sb, row0, lane, st * KT, ch);
+        if (!DIAG) dma_panel_rows(rb, sb + PANEL_BYTES, row0, lane, st * KT, ch);
+    };
+#pragma unroll
+    for (int k = 0; k < NSTAGE - 1; ++k)
+        if (k < n_st) issue(k);
 
-    for (int64_t s = 0; s < n_stages; ++s) {
-        const uint16_t* bufA = lds + (s & 1) * 2 * PANEL;
-        const uint16_t* bufB = diag ? bufA : bufA + PANEL;
+    for (int64_t st = 0; st < n_st; ++st) {
+        // this wave's loads of stage st are done when at most the loads of
+        // the later issued stages are outstanding; then the barrier makes
+        // every wave's part visible
+        if (st + NSTAGE - 2 < n_st) wait_vmcnt<NLD * (NSTAGE - 2)>();
+        else wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();
+        if (st + NSTAGE - 1 < n_st) issue(st + NSTAGE - 1);
+        const char* pa = lds + (st % NSTAGE) * STAGE_BYTES;
+        const char* pb = DIAG ? pa : pa + PANEL_BYTES;
 #pragma unroll
         for (int ks = 0; ks < KT / 16; ++ks) {
-            const int ko = ks * 16 + 8 * (lane >> 5);
+            const int g = 2 * ks + (lane >> 5);
             u32x4_t a[4], bb[2];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                a[i] = *(const u32x4_t*)&bufA[(wr * 128 + i * 32 + (lane & 31)) * SK + ko];
+            for (int i = 0; i < 4; ++i) a[i] = lds_operand(pa, wr * 128 + i * 32 + (lane & 31), g);
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
-                bb[j] = *(const u32x4_t*)&bufB[(wc * 64 + j * 32 + (lane & 31)) * SK + ko];
+            for (int j = 0; j < 2; ++j) bb[j] = lds_operand(pb, wc * 64 + j * 32 + (lane & 31), g);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int j = 0; j < 2; ++j) acc[i][j] = mfma_32x32x16(a[i], bb[j], acc[i][j], (Tag*)nullptr);
         }
-        if (s + 1 < n_stages) {
-            if (loader) store_block(lds + ((s + 1) & 1) * 2 * PANEL + panel * PANEL, va, cg, tg);
-            if (s + 2 < n_stages) load_block<VEC>(va, stage_rsrc(X, s + 2, ld, n_tok), off, col, d);
-        }
-        __syncthreads();
     }
+    __syncthreads();
 
     // float32 tile -> float64 H (strict upper part; the diagonal comes from a
     // float64 pass).  Waves stage their 128x64 parts in LDS two at a time
@@ -240,7 +295,6 @@ __global__ __launch_bounds__(512) void hess_syrk_kernel(double* __restrict__ H, 
     float* stg = (float*)lds;
 #pragma unroll 1
     for (int q = 0; q < 4; ++q) {
-        // quarter q: rows (q>>1)*128, cols (q&1)*128 -> waves wr = q>>1, wc in {2(q&1), 2(q&1)+1}
         if (wr == (q >> 1) && (wc >> 1) == (q & 1)) {
             float* sl = stg + (4 * (lane >> 5)) * SP + (wc & 1) * 64 + (lane & 31);
 #pragma unroll
@@ -264,61 +318,20 @@ __global__ __launch_bounds__(512) void hess_syrk_kernel(double* __restrict__ H, 
     }
 }
 
-// diag(H) in float64: H[c][c] += 2 * sum_t x_tc^2.  Squares of bf16/fp16
-// values are exact in float64.  Grid (column blocks of 256, token splits);
-// each thread sums every 8th token of its split for 8 adjacent columns,
-// the 8 token lanes are reduced in LDS in a fixed order, and a second
-// kernel adds the splits in order: deterministic.
-constexpr int DSPLIT = 32;
-
-template <typename Tag, bool VEC>
-__global__ __launch_bounds__(256) void colsq_kernel(const uint16_t* __restrict__ X, int64_t n_tok, int64_t d,
-                                                    int64_t ld, double* __restrict__ part) {
-    __shared__ double red[8][256];
-    const int t = threadIdx.x, tl = t & 7, cc = t >> 3;
-    const int64_t col = (int64_t)blockIdx.x * 256 + cc * 8;
-    const int64_t per = ceil_div(n_tok, DSPLIT);
-    const int64_t t0 = (int64_t)blockIdx.y * per;
-    const int64_t t1 = (t0 + per < n_tok) ? t0 + per : n_tok;
-    double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (col < d) {
-        for (int64_t tk = t0 + tl; tk < t1; tk += 8) {
-            const uint16_t* p = X + tk * ld + col;
-            uint16_t e[8];
-            if (VEC) {
-                const u32x4_t w = *(const u32x4_t*)p;
-                e[0] = w.x & 0xFFFFu; e[1] = w.x >> 16; e[2] = w.y & 0xFFFFu; e[3] = w.y >> 16;
-                e[4] = w.z & 0xFFFFu; e[5] = w.z >> 16; e[6] = w.w & 0xFFFFu; e[7] = w.w >> 16;
-            } else {
-#pragma unroll
-                for (int c = 0; c < 8; ++c) e[c] = (col + c < d) ? p[c] : (uint16_t)0;
-            }
-#pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                const double x = elem_f64<Tag>(e[c]);
-                acc[c] = fma(x, x, acc[c]);
-            }
-        }
-    }
-#pragma unroll
-    for (int c = 0; c < 8; ++c) red[tl][cc * 8 + c] = acc[c];
-    __syncthreads();
-    const int64_t c = (int64_t)blockIdx.x * 256 + t;
-    if (c < d) {
-        double sum = 0.0;
-#pragma unroll
-        for (int g = 0; g < 8; ++g) sum += red[g][t];
-        part[(int64_t)blockIdx.y * d + c] = sum;
-    }
-}
-
-__global__ __launch_bounds__(256) void colsq_finish_kernel(const double* __restrict__ part, int64_t d,
-                                                           double* __restrict__ H) {
-    const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (c >= d) return;
-    double sum = 0.0;
-    for (int s = 0; s < DSPLIT; ++s) sum += part[(int64_t)s * d + c];
-    H[c * d + c] += 2.0 * sum;
+template <typename Tag>
+__global__ __launch_bounds__(512) void hess_syrk_kernel(double* __restrict__ H, const uint16_t* __restrict__ Xt,
+                                                        int64_t ch, int64_t d, int64_t T, int64_t n_tiles,
+                                                        int64_t per_xcd) {
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    // XCD-grouped tile order: workgroup b runs on XCD b % 8; each XCD takes a
+    // contiguous range of the banded upper-triangle enumeration.
+    const int64_t b = blockIdx.x;
+    const int64_t lin = (b % 8) * per_xcd + b / 8;
+    if (lin >= n_tiles) return;
+    int64_t ti, tj;
+    upper_tile(lin, ti, tj, T);
+    if (ti == tj) syrk_tile<Tag, true>(H, Xt, ch, d, ti, tj, lds);
+    else syrk_tile<Tag, false>(H, Xt, ch, d, ti, tj, lds);
 }
 
 // fp32 activations: float64 products and sums.  64x64 tiles of the upper
@@ -374,12 +387,30 @@ __global__ __launch_bounds__(256) void hess_f32_kernel(double* __restrict__ H, c
         }
 }
 
+// Tokens per chunk: at most CHUNK, and the transposed chunk (d_pad x ch
+// 16-bit values) stays under XT_MAX_BYTES.
+int64_t chunk_tokens(int64_t d) {
+    const int64_t d_pad = align_up((size_t)d, BT);
+    int64_t c = (int64_t)(XT_MAX_BYTES / (2 * (size_t)d_pad)) / KT * KT;
+    if (c > CHUNK) c = CHUNK;
+    if (c < KT) c = KT;
+    return c;
+}
+
+size_t part_bytes(int64_t d) { return align_up((size_t)(CHUNK / TSPAN) * d * sizeof(double), 256); }
+
 }  // namespace
 
-size_t hessian_workspace_bytes(int64_t d) { return (size_t)DSPLIT * d * sizeof(double); }
+size_t hessian_workspace_bytes(int64_t n_tok, int64_t d) {
+    const int64_t d_pad = align_up((size_t)d, BT);
+    int64_t ch = align_up((size_t)(n_tok > 0 ? n_tok : 1), KT);
+    const int64_t cmax = chunk_tokens(d);
+    if (ch > cmax) ch = cmax;
+    return part_bytes(d) + (size_t)d_pad * ch * sizeof(uint16_t);
+}
 
 gptq_status hessian_launch(double* H, const void* X, gptq_dtype dt, int64_t n_tok, int64_t d,
-                           int64_t ld_x, double* part, hipStream_t s) {
+                           int64_t ld_x, void* ws, hipStream_t s) {
     if (n_tok == 0) return GPTQ_OK;
     if (dt == GPTQ_F32) {
         const int64_t T = ceil_div(d, FT);
@@ -388,47 +419,47 @@ gptq_status hessian_launch(double* H, const void* X, gptq_dtype dt, int64_t n_to
         GPTQ_LAUNCH_CHECK();
         return GPTQ_OK;
     }
-    const int64_t T = ceil_div(d, BT);
+    double* part = (double*)ws;
+    uint16_t* xt = (uint16_t*)((char*)ws + part_bytes(d));
+    const int64_t d_pad = align_up((size_t)d, BT);
+    const int64_t T = d_pad / BT;
     const int64_t n_tiles = T * (T + 1) / 2;
     const int64_t per_xcd = ceil_div(n_tiles, 8);
-    const dim3 grid((unsigned)(per_xcd * 8)), block(512);
-    const size_t shmem = 4 * PANEL * sizeof(uint16_t);
     const bool vec = (ld_x % 8 == 0) && (d % 8 == 0) && ((uintptr_t)X % 16 == 0);
     const uint16_t* x = (const uint16_t*)X;
-    static bool attr_set = false;
-    if (!attr_set) {
-        GPTQ_HIP(hipFuncSetAttribute((const void*)hess_syrk_kernel<bf16x8_t, true>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem));
-        GPTQ_HIP(hipFuncSetAttribute((const void*)hess_syrk_kernel<bf16x8_t, false>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem));
-        GPTQ_HIP(hipFuncSetAttribute((const void*)hess_syrk_kernel<h16x8_t, true>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem));
-        GPTQ_HIP(hipFuncSetAttribute((const void*)hess_syrk_kernel<h16x8_t, false>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem));
-        attr_set = true;
-    }
-    const dim3 dgrid((unsigned)ceil_div(d, 256), DSPLIT), b256(256);
-    if (dt == GPTQ_BF16) {
-        if (vec) hipLaunchKernelGGL((colsq_kernel<bf16x8_t, true>), dgrid, b256, 0, s, x, n_tok, d, ld_x, part);
-        else hipLaunchKernelGGL((colsq_kernel<bf16x8_t, false>), dgrid, b256, 0, s, x, n_tok, d, ld_x, part);
-    } else {
-        if (vec) hipLaunchKernelGGL((colsq_kernel<h16x8_t, true>), dgrid, b256, 0, s, x, n_tok, d, ld_x, part);
-        else hipLaunchKernelGGL((colsq_kernel<h16x8_t, false>), dgrid, b256, 0, s, x, n_tok, d, ld_x, part);
-    }
-    GPTQ_LAUNCH_CHECK();
-    hipLaunchKernelGGL(colsq_finish_kernel, dim3((unsigned)ceil_div(d, 256)), b256, 0, s, part, d, H);
-    GPTQ_LAUNCH_CHECK();
-    // one launch per chunk of CHUNK tokens: each adds its float32 partial
-    // tiles to H in float64, in token order
-    for (int64_t c0 = 0; c0 < n_tok; c0 += CHUNK) {
-        const int64_t nt = (n_tok - c0 < CHUNK) ? n_tok - c0 : CHUNK;
+    GPTQ_HIP(hipFuncSetAttribute((const void*)hess_syrk_kernel<bf16x8_t>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                 RING_BYTES));
+    GPTQ_HIP(hipFuncSetAttribute((const void*)hess_syrk_kernel<h16x8_t>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                 RING_BYTES));
+    const dim3 b256(256);
+    // per chunk: transpose into Xt, then one SYRK launch that adds its
+    // float32 partial tiles to H in float64; chunks in token order
+    const int64_t cmax = chunk_tokens(d);
+    for (int64_t c0 = 0; c0 < n_tok; c0 += cmax) {
+        const int64_t nt = (n_tok - c0 < cmax) ? n_tok - c0 : cmax;
+        const int64_t ch = align_up((size_t)nt, KT);
         const uint16_t* xc = x + c0 * ld_x;
+        const int64_t nblk = ceil_div(ch, TSPAN);
+        const dim3 tgrid((unsigned)nblk, (unsigned)(d_pad / 256));
         if (dt == GPTQ_BF16) {
-            if (vec) hipLaunchKernelGGL((hess_syrk_kernel<bf16x8_t, true>), grid, block, shmem, s, H, xc, nt, d, ld_x, T, n_tiles, per_xcd);
-            else hipLaunchKernelGGL((hess_syrk_kernel<bf16x8_t, false>), grid, block, shmem, s, H, xc, nt, d, ld_x, T, n_tiles, per_xcd);
+            if (vec) hipLaunchKernelGGL((transpose_kernel<bf16x8_t, true>), tgrid, b256, 0, s, xc, nt, d, ld_x, xt, ch, part);
+            else hipLaunchKernelGGL((transpose_kernel<bf16x8_t, false>), tgrid, b256, 0, s, xc, nt, d, ld_x, xt, ch, part);
         } else {
-            if (vec) hipLaunchKernelGGL((hess_syrk_kernel<h16x8_t, true>), grid, block, shmem, s, H, xc, nt, d, ld_x, T, n_tiles, per_xcd);
-            else hipLaunchKernelGGL((hess_syrk_kernel<h16x8_t, false>), grid, block, shmem, s, H, xc, nt, d, ld_x, T, n_tiles, per_xcd);
+            if (vec) hipLaunchKernelGGL((transpose_kernel<h16x8_t, true>), tgrid, b256, 0, s, xc, nt, d, ld_x, xt, ch, part);
+            else hipLaunchKernelGGL((transpose_kernel<h16x8_t, false>), tgrid, b256, 0, s, xc, nt, d, ld_x, xt, ch, part);
         }
         GPTQ_LAUNCH_CHECK();
+        hipLaunchKernelGGL(diag_add_kernel, dim3((unsigned)ceil_div(d, 256)), b256, 0, s, part, nblk, d, H);
+        GPTQ_LAUNCH_CHECK();
+        const dim3 grid((unsigned)(per_xcd * 8)), block(512);
+        if (dt == GPTQ_BF16)
+            hipLaunchKernelGGL(hess_syrk_kernel<bf16x8_t>, grid, block, RING_BYTES, s, H, xt, ch, d, T, n_tiles,
+                               per_xcd);
+        else
+            hipLaunchKernelGGL(hess_syrk_kernel<h16x8_t>, grid, block, RING_BYTES, s, H, xt, ch, d, T, n_tiles,
+                               per_xcd);
+        GPTQ_LAUNCH_CHECK();
     }
-    GPTQ_LAUNCH_CHECK();
     return GPTQ_OK;
 }
 

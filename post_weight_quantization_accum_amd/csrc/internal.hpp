@@ -25,11 +25,12 @@ gptq_status launch_gemm_f64(hipStream_t s, int64_t M, int64_t N, int64_t K, doub
                             bool transB, double beta, double* C, int64_t ldc, bool lower_tiles,
                             GemmTri tri = GEMM_TRI_NONE);
 
-// Hessian: H (upper) += 2 X^T X.  part: hessian_workspace_bytes(d) bytes
-// (float64 partial column sums; unused for fp32 inputs).
-size_t hessian_workspace_bytes(int64_t d);
+// Hessian: H (upper) += 2 X^T X.  ws: hessian_workspace_bytes(n_tok, d)
+// bytes (float64 partial column sums of the diagonal, then the transposed
+// token chunk); unused for fp32 inputs.
+size_t hessian_workspace_bytes(int64_t n_tok, int64_t d);
 gptq_status hessian_launch(double* H, const void* X, gptq_dtype dt, int64_t n_tok, int64_t d,
-                           int64_t ld_x, double* part, hipStream_t s);
+                           int64_t ld_x, void* ws, hipStream_t s);
 
 // Column order, damping, Cholesky of the reversed matrix, triangular inverse,
 // rotation into U.  ws layout described in chol.hip.

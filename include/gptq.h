@@ -140,7 +140,8 @@ gptq_status gptq_prepare_hinv(double* H, int64_t d_in, const gptq_config* cfg,
  *   after each block [i1,i2): W[:, i2:] -= Err * U[i1:i2, i2:].
  *
  * W: d_out x d_in of w_dtype, row stride ld_w (>= d_in); not modified.
- * U, perm: as returned by gptq_prepare_hinv (U row stride d_in).
+ * U, perm: as returned by gptq_prepare_hinv (U row stride d_in; the strict
+ * lower triangle of U must be zero, as that call leaves it).
  * Outputs, all in ORIGINAL column order:
  *   codes   d_out x d_in uint8 (row stride d_in);
  *   scales, zeros   n_groups x d_out float32, [group][row], n_groups =

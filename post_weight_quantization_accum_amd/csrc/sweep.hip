@@ -10,13 +10,16 @@
 //   scale64 / zero64  n_groups x d_out float64
 //   row_loss64 d_out float64, pinv d_in int32, flags
 //
-// sweep_block: one wave64 per 64 rows, one lane per row.  The block's columns
-// of those rows sit in LDS as [column][row] (conflict-free per column), and
-// the block's upper triangle of U sits in LDS packed, with reciprocal
-// pivots.  The block is walked in sub-blocks of SB columns held in
-// registers: inside a sub-block the compensation is applied column by column
-// in registers; the sub-block's errors then update the block's remaining
-// columns in LDS (SB fused multiply-adds per element).
+// sweep_block: eight lanes per row, each holding 16 of the block's (up to)
+// 128 columns of that row in registers; 8 rows per wave (one wave per
+// workgroup, nearly no LDS, so it runs beside the GEMMs of the lazy
+// updates).  Column c is quantized by the lane owning it; its scaled error
+// reaches the other lanes of the row through a masked 8-lane sum (DPP), and
+// every lane then applies w_j -= err * U[c][j] to its 16 columns, so each
+// w_j receives the compensations of the earlier columns one by one, in
+// column order.  The row U[c][block] is read from L2, two columns ahead.
+// A finished column keeps its error in place: the later updates leave it
+// unchanged because U is zero below the diagonal.
 //
 // Lazy updates are two-level (mathematically the same as one update per
 // block): after each block, a float64 MFMA GEMM updates the rest of its
@@ -29,8 +32,9 @@ namespace gptq {
 namespace {
 
 constexpr int BMAX = 128;   // largest supported block (columns per lazy update)
-constexpr int ROWS = 64;    // rows per workgroup (one wave)
-constexpr int SBMAX = 8;
+constexpr int LPR = 8;      // lanes per row
+constexpr int CPL = BMAX / LPR;  // columns per lane
+constexpr int ROWS = 64 / LPR;   // rows per workgroup (one wave)
 
 struct SweepWs {
     int* flags;
@@ -155,82 +159,123 @@ struct SideStream {
     }
 };
 
-// Packed upper triangle of a BMAX x BMAX block: row a holds columns
-// a+1 .. BMAX-1; element (a, b) sits at upper_base(a) + b.
-__host__ __device__ __forceinline__ int upper_base(int a) { return a * (BMAX - 1) - a * (a - 1) / 2 - a - 1; }
-constexpr int UPACK = BMAX * (BMAX - 1) / 2;
+// DPP helpers on doubles (two 32-bit moves).
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, 0xF, 0xF, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, 0xF, 0xF, false);
+    return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+constexpr int DPP_XOR1 = 0xB1;         // quad_perm (1,0,3,2)
+constexpr int DPP_XOR2 = 0x4E;         // quad_perm (2,3,0,1)
+constexpr int DPP_HALF_MIRROR = 0x141; // lane i <-> 7-i within each group of 8
 
-template <int SB>
-__global__ __launch_bounds__(256) void sweep_block_kernel(double* __restrict__ Wwork, int64_t d_out, int64_t d_in,
-                                                          int64_t i1, int nb, const double* __restrict__ U,
-                                                          int64_t g, QParams qp, double* __restrict__ Err,
-                                                          int ldE, int errc, uint8_t* __restrict__ codes_s,
-                                                          double* __restrict__ scale64, double* __restrict__ zero64,
-                                                          float* __restrict__ scales, float* __restrict__ zeros,
-                                                          double* __restrict__ loss64) {
-    __shared__ double w1[BMAX][ROWS + 1];
-    __shared__ double up[UPACK];
+__device__ __forceinline__ double row_sum8(double x) {
+    x += dpp_f64<DPP_XOR1>(x);
+    x += dpp_f64<DPP_XOR2>(x);
+    return x + dpp_f64<DPP_HALF_MIRROR>(x);
+}
+__device__ __forceinline__ double row_min8(double x) {
+    x = fmin(x, dpp_f64<DPP_XOR1>(x));
+    x = fmin(x, dpp_f64<DPP_XOR2>(x));
+    return fmin(x, dpp_f64<DPP_HALF_MIRROR>(x));
+}
+__device__ __forceinline__ double row_max8(double x) {
+    x = fmax(x, dpp_f64<DPP_XOR1>(x));
+    x = fmax(x, dpp_f64<DPP_XOR2>(x));
+    return fmax(x, dpp_f64<DPP_HALF_MIRROR>(x));
+}
+
+template <int SEG, bool FULL>
+__global__ __launch_bounds__(64) void sweep_block_kernel(double* __restrict__ Wwork, int64_t d_out, int64_t d_in,
+                                                         int64_t i1, int nb, const double* __restrict__ U,
+                                                         int64_t g, QParams qp, double* __restrict__ Err,
+                                                         int ldE, int errc, uint8_t* __restrict__ codes_s,
+                                                         double* __restrict__ scale64, double* __restrict__ zero64,
+                                                         float* __restrict__ scales, float* __restrict__ zeros,
+                                                         double* __restrict__ loss64) {
     __shared__ double rinv[BMAX];
-    __shared__ uint8_t cb[BMAX][ROWS];
-
-    // All four waves stage the block (many loads in flight per thread);
-    // wave 0 then sweeps it, one lane per row; all four write it back.
-    const int t = threadIdx.x;
-    const int lane = t & 63;
-    const int64_t r0 = (int64_t)blockIdx.x * ROWS;
-    const int64_t row = r0 + lane;
+    const int lane = threadIdx.x;
+    const int part = lane & (LPR - 1);
+    const int64_t row = (int64_t)blockIdx.x * ROWS + (lane >> 3);
     const bool live = row < d_out;
     const int64_t i2 = i1 + nb;
-
-    // the block's columns of the 64 rows -> LDS [column][row]
-#pragma unroll 16
-    for (int idx = t; idx < ROWS * BMAX; idx += 256) {
-        const int rr = idx / BMAX, j = idx % BMAX;
-        const int64_t gr = r0 + rr;
-        if (j < nb) w1[j][rr] = (gr < d_out) ? Wwork[gr * d_in + i1 + j] : 0.0;
-    }
-    // the block's upper triangle of U -> packed LDS; reciprocal pivots
-#pragma unroll 16
-    for (int idx = t; idx < BMAX * BMAX; idx += 256) {
-        const int a = idx / BMAX, b = idx % BMAX;
-        if (a < nb && b < nb && b > a) up[upper_base(a) + b] = U[(i1 + a) * d_in + i1 + b];
-    }
-    if (t < nb) rinv[t] = 1.0 / U[(i1 + t) * d_in + i1 + t];
-    __syncthreads();
-    if (t < ROWS) {  // wave 0: the sweep (no barriers inside)
-        // current group parameters of this row (kept across blocks via scale64/zero64)
-        double scale = 1.0, zero = 0.0;
-        {
-            const int64_t gi = i1 / g;
-            if ((i1 % g) != 0 && live) {  // group started in an earlier block
-                scale = scale64[gi * d_out + row];
-                zero = zero64[gi * d_out + row];
-            }
-        }
-        double loss = 0.0;
-
-        for (int s0 = 0; s0 < nb; s0 += SB) {
-            double wv[SB];
+    const int cbase = part * CPL;  // first block column of this lane
+    const int nbm = nb - 1;
+    const double* Ub = U + i1 * d_in + i1;
+    // this lane's part of U row c (columns clamped into the block)
+    auto load_urow = [&](double (&u)[CPL], int c) {
+        const double* p = Ub + (int64_t)(c < nbm ? c : nbm) * d_in;
 #pragma unroll
-            for (int k = 0; k < SB; ++k) wv[k] = (s0 + k < nb) ? w1[s0 + k][lane] : 0.0;
+        for (int kk = 0; kk < CPL; ++kk) {
+            const int j = cbase + kk;
+            u[kk] = p[FULL ? j : (j < nbm ? j : nbm)];
+        }
+    };
 
-            const int64_t c0 = i1 + s0;
-            if (c0 % g == 0) {
-                // group parameters from the group's current values
+    for (int c = lane; c < nb; c += 64) rinv[c] = 1.0 / Ub[(int64_t)c * d_in + c];
+
+    double w[CPL];
+    {
+        const int64_t rr = live ? row : d_out - 1;
+        const double* wrow = Wwork + rr * d_in + i1;
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) {
+            const int j = cbase + k;
+            const double x = wrow[FULL ? j : (j < nbm ? j : nbm)];
+            w[k] = (live && (FULL || j < nb)) ? x : 0.0;
+        }
+    }
+    uint32_t pk[CPL / 4];
+#pragma unroll
+    for (int k = 0; k < CPL / 4; ++k) pk[k] = 0u;
+
+    // current group parameters of this row (a group begun in an earlier
+    // block is continued)
+    double scale = 1.0, zero = 0.0;
+    const int64_t rem = i1 % g;
+    if (rem != 0 && live) {
+        scale = scale64[(i1 / g) * d_out + row];
+        zero = zero64[(i1 / g) * d_out + row];
+    }
+    int next_gs = (int)(rem == 0 ? 0 : g - rem);      // block column of the next group start
+    int64_t next_gi = i1 / g + (rem == 0 ? 0 : 1);  // and its group index
+    double loss = 0.0;
+
+    // U rows of the next two columns in flight
+    double ua[CPL], ub[CPL];
+    load_urow(ua, 0);
+    load_urow(ub, 1);
+    __syncthreads();
+
+    for (int P = 0; P < LPR; ++P) {
+        if (P * CPL >= nb) break;
+#pragma unroll
+        for (int s0 = 0; s0 < CPL; s0 += SEG) {
+            const int cs = P * CPL + s0;
+            if (!FULL && cs >= nb) break;
+            if (cs == next_gs) {
+                // group parameters from the group's current values: block
+                // columns [cs, cend) in registers, later columns from Wwork
+                const int64_t gend = (i1 + cs + g < d_in) ? i1 + cs + g : d_in;
+                const int cend = (gend - i1 < nb) ? (int)(gend - i1) : nb;
                 double xmin = 0.0, xmax = 0.0;
-                const int64_t gend = (c0 + g < d_in) ? c0 + g : d_in;
-                const int64_t inblk_end = (gend < i2) ? gend : i2;
-                for (int64_t j = c0; j < inblk_end; ++j) {
-                    const double v = w1[j - i1][lane];
-                    xmin = fmin(xmin, v);
-                    xmax = fmax(xmax, v);
+#pragma unroll
+                for (int kk = 0; kk < CPL; ++kk) {
+                    const int j = cbase + kk;
+                    const bool in = j >= cs && j < cend;
+                    xmin = fmin(xmin, in ? w[kk] : 0.0);
+                    xmax = fmax(xmax, in ? w[kk] : 0.0);
                 }
                 if (live)
-                    for (int64_t j = i2; j < gend; ++j) {
+                    for (int64_t j = i2 + part; j < gend; j += LPR) {
                         const double v = Wwork[row * d_in + j];
                         xmin = fmin(xmin, v);
                         xmax = fmax(xmax, v);
                     }
+                xmin = row_min8(xmin);
+                xmax = row_max8(xmax);
                 if (qp.sym) {
                     double amax = fmax(-xmin, xmax);
                     if (amax == 0.0) amax = 1.0;
@@ -244,62 +289,61 @@ __global__ __launch_bounds__(256) void sweep_block_kernel(double* __restrict__ W
                     scale = (xmax - xmin) / qp.maxq;
                     zero = rint(-xmin / scale);
                 }
-                if (live) {
-                    const int64_t gi = c0 / g;
-                    scale64[gi * d_out + row] = scale;
-                    zero64[gi * d_out + row] = zero;
-                    scales[gi * d_out + row] = (float)scale;
-                    zeros[gi * d_out + row] = (float)zero;
+                if (live && part == 0) {
+                    scale64[next_gi * d_out + row] = scale;
+                    zero64[next_gi * d_out + row] = zero;
+                    scales[next_gi * d_out + row] = (float)scale;
+                    zeros[next_gi * d_out + row] = (float)zero;
                 }
+                next_gs = cs + (int)g;
+                ++next_gi;
             }
+#pragma unroll
+            for (int kq = 0; kq < SEG; ++kq) {
+                const int k = s0 + kq;
+                const int c = P * CPL + k;
+                if (!FULL && c >= nb) break;
+                // even columns use ua, odd ub; the buffer is refilled with
+                // the row two columns ahead once this column has used it
+                double (&u)[CPL] = (k & 1) ? ub : ua;
+                const double ri = rinv[c];
+                // quantize column c (meaningful in the owner lane, part == P);
+                // the code is decided on the correctly rounded quotient w / scale
+                const double x = w[k];
+                double code = rint(x / scale) + zero;
+                code = fmin(fmax(code, 0.0), qp.maxq);
+                const double q = scale * (code - zero);
+                const double diff = x - q;
+                const double t = diff * ri;
+                const bool own = part == P;
+                const double err = row_sum8(own ? t : 0.0);
+                loss = own ? fma(0.5 * t, t, loss) : loss;
+                pk[k >> 2] = own ? (pk[k >> 2] | ((uint32_t)code << (8 * (k & 3)))) : pk[k >> 2];
+                // compensation of the later columns of the block (earlier
+                // columns meet zeros of U below the diagonal)
+#pragma unroll
+                for (int kk = 0; kk < CPL; ++kk) w[kk] = fma(-err, u[kk], w[kk]);
+                w[k] = own ? err : w[k];
+                load_urow(u, c + 2);
+            }
+        }
+    }
 
-            double errs[SB];
+    // errors and codes of this row's columns back to HBM
+    if (live) {
+        double* erow = Err + row * ldE + errc + cbase;
+        uint8_t* crow = codes_s + row * d_in + i1 + cbase;
 #pragma unroll
-            for (int k = 0; k < SB; ++k) {
-                errs[k] = 0.0;
-                if (s0 + k < nb) {
-                    const int c = s0 + k;
-                    const double w = wv[k];
-                    // the code is decided on the correctly rounded quotient w / scale
-                    double code = rint(w / scale) + zero;
-                    code = fmin(fmax(code, 0.0), qp.maxq);
-                    const double q = scale * (code - zero);
-                    const double ri = rinv[c];
-                    const double diff = w - q;
-                    const double err = diff * ri;
-                    const int ub = upper_base(c);
-#pragma unroll
-                    for (int kk = k + 1; kk < SB; ++kk) wv[kk] = fma(-err, up[ub + s0 + kk], wv[kk]);
-                    errs[k] = err;
-                    loss += 0.5 * (diff * ri) * (diff * ri);
-                    w1[c][lane] = err;
-                    cb[c][lane] = (uint8_t)code;
-                }
-            }
-            // the sub-block's errors update the rest of the block
-            int ubk[SB];
-#pragma unroll
-            for (int k = 0; k < SB; ++k) ubk[k] = upper_base(s0 + k < nb ? s0 + k : 0);
-            for (int j = s0 + SB; j < nb; ++j) {
-                double v = w1[j][lane];
-#pragma unroll
-                for (int k = 0; k < SB; ++k) v = fma(-errs[k], up[ubk[k] + j], v);
-                w1[j][lane] = v;
+        for (int k = 0; k < CPL; ++k) {
+            if (FULL || cbase + k < nb) {
+                erow[k] = w[k];
+                crow[k] = (uint8_t)(pk[k >> 2] >> (8 * (k & 3)));
             }
         }
-        if (live) loss64[row] += loss;
     }
-    __syncthreads();
-    // Err (now in w1) and codes back to HBM, row-contiguous
-#pragma unroll 8
-    for (int idx = t; idx < ROWS * BMAX; idx += 256) {
-        const int rr = idx / BMAX, j = idx % BMAX;
-        const int64_t gr = r0 + rr;
-        if (j < nb && gr < d_out) {
-            Err[gr * ldE + errc + j] = w1[j][rr];
-            codes_s[gr * d_in + i1 + j] = cb[j][rr];
-        }
-    }
+    // row loss: the eight parts summed in a fixed order
+    loss = row_sum8(loss);
+    if (live && part == 0) loss64[row] += loss;
 }
 
 // codes / w_hat in original column order.
@@ -342,6 +386,9 @@ gptq_status sweep_launch(const void* W, gptq_dtype dt, int64_t d_out, int64_t d_
     SweepWs w = carve(ws, d_out, d_in, cfg);
     const int64_t g = cfg->group_size > 0 ? cfg->group_size : d_in;
     const int B = cfg->block_size;
+    // group starts fall on multiples of SEG block columns
+    int SEG = CPL;
+    while (SEG > 1 && ((B % SEG) != 0 || (cfg->group_size > 0 && (g % SEG) != 0))) SEG >>= 1;
     GPTQ_HIP(hipMemsetAsync(w.flags, 0, 256, s));
 
     const unsigned gx = (unsigned)ceil_div(d_in, 256);
@@ -352,11 +399,6 @@ gptq_status sweep_launch(const void* W, gptq_dtype dt, int64_t d_out, int64_t d_
     GPTQ_LAUNCH_CHECK();
     hipLaunchKernelGGL(pinv_kernel, dim3(gx), dim3(256), 0, s, perm, d_in, g, w.pinv, g_idx);
     GPTQ_LAUNCH_CHECK();
-
-    // sub-block width: the largest of 8, 4, 2, 1 dividing B and (when
-    // grouped) the group size, so every group starts on a sub-block boundary
-    int SB = 8;
-    while (SB > 1 && ((B % SB) != 0 || (cfg->group_size > 0 && (g % SB) != 0))) SB >>= 1;
 
     QParams qp{cfg->bits, cfg->sym, (double)((1 << cfg->bits) - 1)};
     const unsigned grid = (unsigned)ceil_div(d_out, ROWS);
@@ -376,17 +418,24 @@ gptq_status sweep_launch(const void* W, gptq_dtype dt, int64_t d_out, int64_t d_
         if (wait_far_before_sweep && far_pending) GPTQ_HIP(hipStreamWaitEvent(s, side.far_done, 0));
         for (int64_t i1 = a; i1 < e; i1 += B) {
             const int nb = (int)((e - i1 < B) ? e - i1 : B);
-            switch (SB) {
-#define SWEEP_CASE(n)                                                                                           \
-    case n:                                                                                                     \
-        hipLaunchKernelGGL(sweep_block_kernel<n>, dim3(grid), dim3(256), 0, s, w.Wwork, d_out, d_in, i1, nb, U, \
-                           g, qp, Ek, (int)S, (int)(i1 - a), w.codes_s, w.scale64, w.zero64, scales, zeros,    \
-                           w.loss64);                                                                           \
+            const bool full = nb == BMAX;
+            switch (SEG * 2 + (full ? 1 : 0)) {
+#define SWEEP_CASE(n, f)                                                                                      \
+    case n * 2 + f:                                                                                           \
+        hipLaunchKernelGGL((sweep_block_kernel<n, f>), dim3(grid), dim3(64), 0, s, w.Wwork, d_out, d_in, i1, \
+                           nb, U, g, qp, Ek, (int)S, (int)(i1 - a), w.codes_s, w.scale64, w.zero64, scales,  \
+                           zeros, w.loss64);                                                                  \
         break;
-                SWEEP_CASE(8)
-                SWEEP_CASE(4)
-                SWEEP_CASE(2)
-                SWEEP_CASE(1)
+                SWEEP_CASE(16, 1)
+                SWEEP_CASE(16, 0)
+                SWEEP_CASE(8, 1)
+                SWEEP_CASE(8, 0)
+                SWEEP_CASE(4, 1)
+                SWEEP_CASE(4, 0)
+                SWEEP_CASE(2, 1)
+                SWEEP_CASE(2, 0)
+                SWEEP_CASE(1, 1)
+                SWEEP_CASE(1, 0)
 #undef SWEEP_CASE
             }
             GPTQ_LAUNCH_CHECK();

@@ -96,6 +96,18 @@ gptq_status gptq_hessian_accumulate(double* H, const void* X, gptq_dtype x_dtype
                                     int64_t n_tok, int64_t d_in, int64_t ld_x,
                                     void* workspace, size_t ws_bytes, hipStream_t stream);
 
+/* Measurement variant of gptq_hessian_accumulate: the same kernels in the
+ * same launch configuration on the same stream, with HIP events recorded
+ * around each launch of the Hessian product kernel (one per token chunk).
+ * Synchronous.  On OK, *syrk_ms (host) holds the mean duration of those
+ * launches in milliseconds and *n_launches (host) their number.  Returns
+ * GPTQ_ERR_INVALID_ARG for null output pointers, otherwise as
+ * gptq_hessian_accumulate, or GPTQ_ERR_HIP if an event call fails. */
+gptq_status gptq_hessian_accumulate_timed(double* H, const void* X, gptq_dtype x_dtype,
+                                          int64_t n_tok, int64_t d_in, int64_t ld_x,
+                                          void* workspace, size_t ws_bytes, hipStream_t stream,
+                                          double* syrk_ms, int64_t* n_launches);
+
 /* ------------------------------------------------------------------------
  * Step 2 -- column order, damping, Cholesky form of the inverse
  * ("GPTQ量化算法深度解析" §2.4, §3.1 steps 1-2, §3.3 desc_act and damp).

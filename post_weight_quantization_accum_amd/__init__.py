@@ -18,7 +18,7 @@ from ._lib import (  # noqa: F401
     Unsupported, WorkspaceError, make_config, load, version, status_string,
 )
 
-__all__ = ["hessian_accumulate", "prepare_hinv", "quantize_layer", "pack", "quantize",
+__all__ = ["hessian_accumulate", "hessian_accumulate_timed", "prepare_hinv", "quantize_layer", "pack", "quantize",
            "packed_words_per_row", "make_config", "Config", "load"]
 
 
@@ -79,6 +79,28 @@ def hessian_accumulate(H, X, stream=None):
                                      _ptr(ws), nws, _stream(stream))
     _lib.check(st, "gptq_hessian_accumulate")
     return H
+
+
+def hessian_accumulate_timed(H, X, stream=None):
+    """hessian_accumulate with HIP events around each Hessian product launch
+    (synchronous); returns (mean launch ms, number of launches)."""
+    lib = load()
+    torch = _torch()
+    _require_cuda(H, X)
+    if H.dtype != torch.float64 or not H.is_contiguous():
+        raise TypeError("H must be a contiguous float64 tensor")
+    if X.dim() != 2 or X.stride(1) != 1:
+        raise ValueError("X must be 2-D with unit column stride")
+    n_tok, d_in = X.shape
+    if H.shape != (d_in, d_in):
+        raise ValueError("H must be d_in x d_in")
+    nws = lib.gptq_hessian_workspace(n_tok, d_in)
+    ws = _workspace(nws, H.device)
+    ms, n = ctypes.c_double(0.0), ctypes.c_int64(0)
+    st = lib.gptq_hessian_accumulate_timed(_ptr(H), _ptr(X), _dtype_code(X), n_tok, d_in, X.stride(0),
+                                           _ptr(ws), nws, _stream(stream), ctypes.byref(ms), ctypes.byref(n))
+    _lib.check(st, "gptq_hessian_accumulate_timed")
+    return ms.value, n.value
 
 
 def prepare_hinv(H, cfg: Config, perm=None, workspace=None, stream=None):

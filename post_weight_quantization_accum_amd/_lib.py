@@ -20,7 +20,7 @@ F32, F16, BF16 = 0, 1, 2
 
 # Every symbol include/gptq.h declares.
 EXPORTS = (
-    "gptq_config_default", "gptq_hessian_workspace", "gptq_hessian_accumulate",
+    "gptq_config_default", "gptq_hessian_workspace", "gptq_hessian_accumulate", "gptq_hessian_accumulate_timed",
     "gptq_prepare_hinv_workspace", "gptq_prepare_hinv", "gptq_quantize_layer_workspace",
     "gptq_quantize_layer", "gptq_packed_words_per_row", "gptq_pack", "gptq_status_string",
     "gptq_version",
@@ -91,6 +91,9 @@ def load(path: str | None = None):
     lib.gptq_hessian_workspace.restype = sz
     lib.gptq_hessian_accumulate.argtypes = [vp, vp, ctypes.c_int, i64, i64, i64, vp, sz, vp]
     lib.gptq_hessian_accumulate.restype = ctypes.c_int
+    lib.gptq_hessian_accumulate_timed.argtypes = [vp, vp, ctypes.c_int, i64, i64, i64, vp, sz, vp,
+                                                  ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
+    lib.gptq_hessian_accumulate_timed.restype = ctypes.c_int
     lib.gptq_prepare_hinv_workspace.argtypes = [i64]
     lib.gptq_prepare_hinv_workspace.restype = sz
     lib.gptq_prepare_hinv.argtypes = [vp, i64, cfgp, vp, vp, sz, vp]

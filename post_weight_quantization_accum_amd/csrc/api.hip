@@ -1,5 +1,7 @@
 // The C ABI of libgptq_mi355x: argument validation, workspace sizing and
 // dispatch to the kernels.  Declarations and contracts are in include/gptq.h.
+#include <vector>
+
 #include "internal.hpp"
 
 using namespace gptq;
@@ -66,6 +68,37 @@ gptq_status gptq_hessian_accumulate(double* H, const void* X, gptq_dtype x_dtype
     if (x_dtype != GPTQ_F32 && n_tok > 0 && (!workspace || ws_bytes < hessian_workspace_bytes(n_tok, d_in)))
         return GPTQ_ERR_WORKSPACE;
     return hessian_launch(H, X, x_dtype, n_tok, d_in, ld_x, workspace, stream);
+}
+
+gptq_status gptq_hessian_accumulate_timed(double* H, const void* X, gptq_dtype x_dtype, int64_t n_tok,
+                                          int64_t d_in, int64_t ld_x, void* workspace, size_t ws_bytes,
+                                          hipStream_t stream, double* syrk_ms, int64_t* n_launches) {
+    if (!syrk_ms || !n_launches) return GPTQ_ERR_INVALID_ARG;
+    if (!H || !valid_dtype(x_dtype)) return GPTQ_ERR_INVALID_ARG;
+    if (d_in <= 0 || d_in > MAX_DIM || n_tok < 0 || ld_x < d_in) return GPTQ_ERR_INVALID_ARG;
+    if (n_tok > 0 && !X) return GPTQ_ERR_INVALID_ARG;
+    if (x_dtype != GPTQ_F32 && n_tok > 0 && (!workspace || ws_bytes < hessian_workspace_bytes(n_tok, d_in)))
+        return GPTQ_ERR_WORKSPACE;
+    const int64_t n = hessian_syrk_launches(n_tok, x_dtype, d_in);
+    *syrk_ms = 0.0;
+    *n_launches = n;
+    if (n == 0) return GPTQ_OK;
+    std::vector<hipEvent_t> ev((size_t)(2 * n), nullptr);
+    gptq_status st = GPTQ_OK;
+    for (auto& e : ev)
+        if (hipEventCreate(&e) != hipSuccess) st = GPTQ_ERR_HIP;
+    if (st == GPTQ_OK) st = hessian_launch(H, X, x_dtype, n_tok, d_in, ld_x, workspace, stream, ev.data());
+    if (st == GPTQ_OK && hipStreamSynchronize(stream) != hipSuccess) st = GPTQ_ERR_HIP;
+    double total = 0.0;
+    for (int64_t i = 0; st == GPTQ_OK && i < n; ++i) {
+        float ms = 0.0f;
+        if (hipEventElapsedTime(&ms, ev[2 * i], ev[2 * i + 1]) != hipSuccess) st = GPTQ_ERR_HIP;
+        total += ms;
+    }
+    for (auto& e : ev)
+        if (e) (void)hipEventDestroy(e);
+    if (st == GPTQ_OK) *syrk_ms = total / (double)n;
+    return st;
 }
 
 size_t gptq_prepare_hinv_workspace(int64_t d_in) {

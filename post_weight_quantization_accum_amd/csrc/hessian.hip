@@ -409,14 +409,21 @@ size_t hessian_workspace_bytes(int64_t n_tok, int64_t d) {
     return part_bytes(d) + (size_t)d_pad * ch * sizeof(uint16_t);
 }
 
+int64_t hessian_syrk_launches(int64_t n_tok, gptq_dtype dt, int64_t d) {
+    if (n_tok <= 0) return 0;
+    return dt == GPTQ_F32 ? 1 : ceil_div(n_tok, chunk_tokens(d));
+}
+
 gptq_status hessian_launch(double* H, const void* X, gptq_dtype dt, int64_t n_tok, int64_t d,
-                           int64_t ld_x, void* ws, hipStream_t s) {
+                           int64_t ld_x, void* ws, hipStream_t s, hipEvent_t* ev) {
     if (n_tok == 0) return GPTQ_OK;
     if (dt == GPTQ_F32) {
         const int64_t T = ceil_div(d, FT);
+        if (ev) GPTQ_HIP(hipEventRecord(ev[0], s));
         hipLaunchKernelGGL(hess_f32_kernel, dim3((unsigned)(T * (T + 1) / 2)), dim3(256), 0, s, H,
                            (const float*)X, n_tok, d, ld_x);
         GPTQ_LAUNCH_CHECK();
+        if (ev) GPTQ_HIP(hipEventRecord(ev[1], s));
         return GPTQ_OK;
     }
     double* part = (double*)ws;
@@ -435,7 +442,7 @@ gptq_status hessian_launch(double* H, const void* X, gptq_dtype dt, int64_t n_to
     // per chunk: transpose into Xt, then one SYRK launch that adds its
     // float32 partial tiles to H in float64; chunks in token order
     const int64_t cmax = chunk_tokens(d);
-    for (int64_t c0 = 0; c0 < n_tok; c0 += cmax) {
+    for (int64_t c0 = 0, ci = 0; c0 < n_tok; c0 += cmax, ++ci) {
         const int64_t nt = (n_tok - c0 < cmax) ? n_tok - c0 : cmax;
         const int64_t ch = align_up((size_t)nt, KT);
         const uint16_t* xc = x + c0 * ld_x;
@@ -452,6 +459,7 @@ gptq_status hessian_launch(double* H, const void* X, gptq_dtype dt, int64_t n_to
         hipLaunchKernelGGL(diag_add_kernel, dim3((unsigned)ceil_div(d, 256)), b256, 0, s, part, nblk, d, H);
         GPTQ_LAUNCH_CHECK();
         const dim3 grid((unsigned)(per_xcd * 8)), block(512);
+        if (ev) GPTQ_HIP(hipEventRecord(ev[2 * ci], s));
         if (dt == GPTQ_BF16)
             hipLaunchKernelGGL(hess_syrk_kernel<bf16x8_t>, grid, block, RING_BYTES, s, H, xt, ch, d, T, n_tiles,
                                per_xcd);
@@ -459,6 +467,7 @@ gptq_status hessian_launch(double* H, const void* X, gptq_dtype dt, int64_t n_to
             hipLaunchKernelGGL(hess_syrk_kernel<h16x8_t>, grid, block, RING_BYTES, s, H, xt, ch, d, T, n_tiles,
                                per_xcd);
         GPTQ_LAUNCH_CHECK();
+        if (ev) GPTQ_HIP(hipEventRecord(ev[2 * ci + 1], s));
     }
     return GPTQ_OK;
 }

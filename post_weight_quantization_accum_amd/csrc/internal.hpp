@@ -28,9 +28,12 @@ gptq_status launch_gemm_f64(hipStream_t s, int64_t M, int64_t N, int64_t K, doub
 // Hessian: H (upper) += 2 X^T X.  ws: hessian_workspace_bytes(n_tok, d)
 // bytes (float64 partial column sums of the diagonal, then the transposed
 // token chunk); unused for fp32 inputs.
+// ev: null, or 2 * hessian_syrk_launches(...) events recorded around each
+// SYRK launch (start, end) on s.
 size_t hessian_workspace_bytes(int64_t n_tok, int64_t d);
+int64_t hessian_syrk_launches(int64_t n_tok, gptq_dtype dt, int64_t d);
 gptq_status hessian_launch(double* H, const void* X, gptq_dtype dt, int64_t n_tok, int64_t d,
-                           int64_t ld_x, void* ws, hipStream_t s);
+                           int64_t ld_x, void* ws, hipStream_t s, hipEvent_t* ev = nullptr);
 
 // Column order, damping, Cholesky of the reversed matrix, triangular inverse,
 // rotation into U.  ws layout described in chol.hip.

@@ -83,13 +83,14 @@ void gptq_config_default(gptq_config* cfg);
  * zeroes H before the first call; repeated calls over token chunks sum up.
  * X: n_tok x d_in of x_dtype with row stride ld_x elements (ld_x >= d_in).
  * Token products are exact in float32 for bf16/fp16 inputs and accumulated
- * in float32 over chunks of at most 4096 tokens, then added to H in float64
- * in a fixed order; the diagonal is summed in float64 (32 token splits,
- * added in order).  fp32 inputs are
- * accumulated in float64 throughout.  Deterministic (bit-reproducible).
+ * in float32 over chunks of at most 32768 tokens (fewer when d_in > 16384),
+ * then added to H in float64 in token order; the diagonal is summed in
+ * float64 (per 512 tokens, then in order).  fp32 inputs are accumulated in
+ * float64 throughout.  Deterministic (bit-reproducible).
  * NaN/Inf in X propagate into diag(H) and are reported by gptq_prepare_hinv.
- * workspace: gptq_hessian_workspace(n_tok, d_in) bytes (float64 partial
- * column sums of the diagonal; may be NULL for fp32 inputs).
+ * workspace: gptq_hessian_workspace(n_tok, d_in) bytes (a transposed copy of
+ * one token chunk and float64 column sums; may be NULL for fp32 inputs or
+ * n_tok = 0).  Calls on one workspace must not overlap.
  * ------------------------------------------------------------------------ */
 size_t gptq_hessian_workspace(int64_t n_tok, int64_t d_in);
 gptq_status gptq_hessian_accumulate(double* H, const void* X, gptq_dtype x_dtype,

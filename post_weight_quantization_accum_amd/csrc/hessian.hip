@@ -17,13 +17,14 @@
 // Each MFMA operand is 8 consecutive tokens of one column, while X is
 // token-major.  A chunk is therefore first transposed (8x8 blocks in
 // registers, v_perm_b32) into a feature-major copy Xt, zero-padded to a
-// multiple of 256 features and of 32 tokens.  The SYRK kernel then streams
+// multiple of 256 features and of 64 tokens.  The SYRK kernel then streams
 // Xt straight from memory into LDS with buffer_load ... lds (no VGPR
-// staging) through a 4-stage ring of 32-token stages, three stages ahead of
-// the MFMAs, one barrier per stage.  Within a stage a feature row is 64
-// bytes (four 16-byte granules); granule g of row r is stored at slot
-// g ^ ((r >> 2) & 3), so the 32 rows read by one MFMA operand fetch hit
-// distinct banks.
+// staging) through a ring of two 64-token stages (64 KiB each), one stage
+// ahead of the MFMAs, one barrier per stage; the MFMA operands are
+// software-pipelined in registers one k-step ahead, across the barrier.
+// Within a stage a feature row is 128 bytes (eight 16-byte granules);
+// granule g of row r is stored at slot g ^ ((r >> 1) & 7), so the rows read
+// by one MFMA operand fetch hit distinct banks.
 //
 // Tiling: one workgroup per 256x256 tile of the upper triangle, 8 wave64s
 // (two per SIMD), each owning a 128x64 part as 4x2 MFMA 32x32 tiles.
@@ -39,8 +40,17 @@ namespace gptq {
 namespace {
 
 constexpr int BT = 256;          // tile edge
-constexpr int KT = 32;           // tokens per LDS stage
-constexpr int NSTAGE = 4;        // LDS ring depth
+#ifndef GPTQ_KT
+#define GPTQ_KT 64
+#endif
+#ifndef GPTQ_NSTAGE
+#define GPTQ_NSTAGE 2
+#endif
+constexpr int KT = GPTQ_KT;           // tokens per LDS stage
+constexpr int NSTAGE = GPTQ_NSTAGE;   // LDS ring depth
+constexpr int GR = KT / 8;            // 16-byte token granules per feature row of a stage
+constexpr int RPB = 128 / KT;         // feature rows per 256-byte bank window
+constexpr int DMA_ROWS = 512 / KT;    // feature rows per 1 KiB wave-wide DMA load
 constexpr int CHUNK = 32768;     // tokens accumulated in float32 before the float64 add
 constexpr int SP = 132;          // row stride (floats) of the staged 128x128 quarter
 constexpr int PANEL_BYTES = BT * KT * 2;           // one 256-feature x 32-token panel
@@ -207,33 +217,40 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-// One stage of one panel: 256 feature rows x 32 tokens = 16 KiB, moved by
-// 16 wave-wide 1 KiB DMA loads; wave w issues the two that cover rows
-// 32w .. 32w+31.  Lane l of a load fills LDS granule l of its 1 KiB block:
-// row r = block_row + l/4, slot l%4, which holds token granule
-// g = slot ^ ((r >> 2) & 3) of that row.
+// s_waitcnt lgkmcnt(0) only (vmcnt and expcnt at their maxima).
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14)); }
+
+// One stage of one panel: 256 feature rows x KT tokens, moved by wave-wide
+// 1 KiB DMA loads of DMA_ROWS rows each; a call covers 32 rows.  Lane l of a
+// load fills LDS granule l of its 1 KiB block: row r = block_row + l/GR,
+// slot l%GR, which holds token granule g = slot ^ swz(r) of that row.
+__device__ __forceinline__ int swz(int r) { return (r / RPB) % GR; }
+
 __device__ __forceinline__ void dma_panel_rows(__amdgpu_buffer_rsrc_t rs, char* lds_panel, int row0, int lane,
                                                int64_t tok0, int64_t ch) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const int rblk = row0 + 16 * q;
-        const int r = rblk + (lane >> 2);
-        const int g = (lane & 3) ^ ((r >> 2) & 3);
+    for (int q = 0; q < 32 / DMA_ROWS; ++q) {
+        const int rblk = row0 + DMA_ROWS * q;
+        const int r = rblk + lane / GR;
+        const int g = (lane % GR) ^ swz(r);
         const uint32_t voff = (uint32_t)(((int64_t)r * ch + tok0 + 8 * g) * 2);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(lds_panel + rblk * 64), 16, (int)voff, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(lds_panel + rblk * (KT * 2)), 16, (int)voff, 0, 0,
+                                                 0);
     }
 }
 
 // MFMA operand fetch: row r of a staged panel, token granule g (8 tokens).
 __device__ __forceinline__ u32x4_t lds_operand(const char* lds_panel, int r, int g) {
-    return *(const u32x4_t*)(lds_panel + r * 64 + ((g ^ ((r >> 2) & 3)) << 4));
+    return *(const u32x4_t*)(lds_panel + r * (KT * 2) + ((g ^ swz(r)) << 4));
 }
 
-template <typename Tag, bool DIAG>
+template <typename Tag, bool DIAG, int NW>
 __device__ __forceinline__ void syrk_tile(double* __restrict__ H, const uint16_t* __restrict__ Xt, int64_t ch,
                                           int64_t d, int64_t ti, int64_t tj, char* lds) {
+    constexpr int WCOLS = 512 / NW, NTL = WCOLS / 32, NCW = BT / WCOLS;
+    constexpr int RPW = BT / NW;  // panel rows loaded per wave (multiple of 32)
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    const int wr = wave >> 2, wc = wave & 3;
+    const int wr = wave / NCW, wc = wave % NCW;
     const int64_t n_st = ch / KT;
     // one resource per panel: 256 rows of ch tokens
     const uint32_t pbytes = (uint32_t)(BT * ch * 2);
@@ -241,66 +258,90 @@ __device__ __forceinline__ void syrk_tile(double* __restrict__ H, const uint16_t
         __builtin_amdgcn_make_buffer_rsrc((void*)(Xt + ti * BT * ch), (short)0, (int)pbytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t rb =
         __builtin_amdgcn_make_buffer_rsrc((void*)(Xt + tj * BT * ch), (short)0, (int)pbytes, 0x00020000);
-    const int row0 = wave * 32;
+    const int row0 = wave * RPW;
     // loads issued per wave per stage
-    constexpr int NLD = DIAG ? 2 : 4;
+    constexpr int NLD = (DIAG ? 1 : 2) * (RPW / DMA_ROWS);
 
-    f16_t acc[4][2];
+    f16_t acc[4][NTL];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < NTL; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
     auto issue = [&](int64_t st) {
         char* sb = lds + (st % NSTAGE) * STAGE_BYTES;
-        dma_panel_rows(ra, sb, row0, lane, st * KT, ch);
-        if (!DIAG) dma_panel_rows(rb, sb + PANEL_BYTES, row0, lane, st * KT, ch);
-    };
 #pragma unroll
-    for (int k = 0; k < NSTAGE - 1; ++k)
-        if (k < n_st) issue(k);
-
-    for (int64_t st = 0; st < n_st; ++st) {
-        // this wave's loads of stage st are done when at most the loads of
-        // the later issued stages are outstanding; then the barrier makes
-        // every wave's part visible
-        if (st + NSTAGE - 2 < n_st) wait_vmcnt<NLD * (NSTAGE - 2)>();
-        else wait_vmcnt<0>();
-        __builtin_amdgcn_s_barrier();
-        if (st + NSTAGE - 1 < n_st) issue(st + NSTAGE - 1);
+        for (int rr = 0; rr < RPW; rr += 32) {
+            dma_panel_rows(ra, sb, row0 + rr, lane, st * KT, ch);
+            if (!DIAG) dma_panel_rows(rb, sb + PANEL_BYTES, row0 + rr, lane, st * KT, ch);
+        }
+    };
+    auto read_ops = [&](u32x4_t (&a)[4], u32x4_t (&bb)[NTL], int64_t st, int ks) {
         const char* pa = lds + (st % NSTAGE) * STAGE_BYTES;
         const char* pb = DIAG ? pa : pa + PANEL_BYTES;
+        const int g = 2 * ks + (lane >> 5);
 #pragma unroll
-        for (int ks = 0; ks < KT / 16; ++ks) {
-            const int g = 2 * ks + (lane >> 5);
-            u32x4_t a[4], bb[2];
+        for (int i = 0; i < 4; ++i) a[i] = lds_operand(pa, wr * 128 + i * 32 + (lane & 31), g);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) a[i] = lds_operand(pa, wr * 128 + i * 32 + (lane & 31), g);
+        for (int j = 0; j < NTL; ++j) bb[j] = lds_operand(pb, wc * WCOLS + j * 32 + (lane & 31), g);
+    };
+    // all NSTAGE ring slots in flight; stage 0 visible to every wave
 #pragma unroll
-            for (int j = 0; j < 2; ++j) bb[j] = lds_operand(pb, wc * 64 + j * 32 + (lane & 31), g);
+    for (int k = 0; k < NSTAGE; ++k)
+        if (k < n_st) issue(k);
+    if (n_st >= NSTAGE) wait_vmcnt<NLD * (NSTAGE - 1)>();
+    else wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+
+    // Software pipeline over k-steps: the operands of the next k-step are
+    // read while the current one's MFMAs run.  At a stage boundary this
+    // wave's reads of the finished stage are complete before the barrier,
+    // so the slot is refilled right after it, and the last k-step's MFMAs
+    // cover the first reads of the new stage.
+    constexpr int KPS = KT / 16;
+    static_assert(KPS % 2 == 0, "operand double buffer alternates per k-step");
+    u32x4_t a0[4], b0[NTL], a1[4], b1[NTL];
+    read_ops(a0, b0, 0, 0);
+    for (int64_t st = 0; st < n_st; ++st) {
+#pragma unroll
+        for (int ks = 0; ks < KPS; ++ks) {
+            u32x4_t (&ac)[4] = (ks & 1) ? a1 : a0;
+            u32x4_t (&bc)[NTL] = (ks & 1) ? b1 : b0;
+            u32x4_t (&an)[4] = (ks & 1) ? a0 : a1;
+            u32x4_t (&bn)[NTL] = (ks & 1) ? b0 : b1;
+            if (ks + 1 < KPS) {
+                read_ops(an, bn, st, ks + 1);
+            } else if (st + 1 < n_st) {
+                wait_lgkm0();
+                if (st + NSTAGE - 1 < n_st) wait_vmcnt<NLD * (NSTAGE - 2)>();
+                else wait_vmcnt<0>();
+                __builtin_amdgcn_s_barrier();
+                if (st + NSTAGE < n_st) issue(st + NSTAGE);
+                read_ops(an, bn, st + 1, 0);
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int j = 0; j < 2; ++j) acc[i][j] = mfma_32x32x16(a[i], bb[j], acc[i][j], (Tag*)nullptr);
+                for (int j = 0; j < NTL; ++j) acc[i][j] = mfma_32x32x16(ac[i], bc[j], acc[i][j], (Tag*)nullptr);
         }
     }
     __syncthreads();
 
     // float32 tile -> float64 H (strict upper part; the diagonal comes from a
-    // float64 pass).  Waves stage their 128x64 parts in LDS two at a time
-    // (one 128x128 quarter), then all threads add it to H with
+    // float64 pass).  The 128x128 quarters are staged in LDS one at a time
+    // by the waves that own them, then all threads add the quarter to H with
     // row-contiguous accesses.
     float* stg = (float*)lds;
 #pragma unroll 1
     for (int q = 0; q < 4; ++q) {
-        if (wr == (q >> 1) && (wc >> 1) == (q & 1)) {
-            float* sl = stg + (4 * (lane >> 5)) * SP + (wc & 1) * 64 + (lane & 31);
+        if (wr == (q >> 1) && (wc * WCOLS) / 128 == (q & 1)) {
+            float* sl = stg + (4 * (lane >> 5)) * SP + (wc * WCOLS) % 128 + (lane & 31);
 #pragma unroll
             for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-                for (int ni = 0; ni < 2; ++ni)
+                for (int ni = 0; ni < NTL; ++ni)
 #pragma unroll
                     for (int r = 0; r < 16; ++r)
                         sl[(mi * 32 + 8 * (r >> 2) + (r & 3)) * SP + ni * 32] = acc[mi][ni][r];
@@ -310,7 +351,7 @@ __device__ __forceinline__ void syrk_tile(double* __restrict__ H, const uint16_t
         const int cl = t & 127;
         const int64_t j = jb + cl;
 #pragma unroll 8
-        for (int row = t >> 7; row < 128; row += 4) {
+        for (int row = t >> 7; row < 128; row += NW / 2) {
             const int64_t i = ib + row;
             if (i < j && j < d) H[i * d + j] += 2.0 * (double)stg[row * SP + cl];
         }
@@ -318,10 +359,10 @@ __device__ __forceinline__ void syrk_tile(double* __restrict__ H, const uint16_t
     }
 }
 
-template <typename Tag>
-__global__ __launch_bounds__(512) void hess_syrk_kernel(double* __restrict__ H, const uint16_t* __restrict__ Xt,
-                                                        int64_t ch, int64_t d, int64_t T, int64_t n_tiles,
-                                                        int64_t per_xcd) {
+template <typename Tag, int NW>
+__global__ __launch_bounds__(NW * 64) void hess_syrk_kernel(double* __restrict__ H, const uint16_t* __restrict__ Xt,
+                                                            int64_t ch, int64_t d, int64_t T, int64_t n_tiles,
+                                                            int64_t per_xcd) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
     // XCD-grouped tile order: workgroup b runs on XCD b % 8; each XCD takes a
     // contiguous range of the banded upper-triangle enumeration.
@@ -330,9 +371,11 @@ __global__ __launch_bounds__(512) void hess_syrk_kernel(double* __restrict__ H, 
     if (lin >= n_tiles) return;
     int64_t ti, tj;
     upper_tile(lin, ti, tj, T);
-    if (ti == tj) syrk_tile<Tag, true>(H, Xt, ch, d, ti, tj, lds);
-    else syrk_tile<Tag, false>(H, Xt, ch, d, ti, tj, lds);
+    if (ti == tj) syrk_tile<Tag, true, NW>(H, Xt, ch, d, ti, tj, lds);
+    else syrk_tile<Tag, false, NW>(H, Xt, ch, d, ti, tj, lds);
 }
+
+constexpr int SYRK_WAVES = 8;
 
 // fp32 activations: float64 products and sums.  64x64 tiles of the upper
 // triangle, 256 threads, each thread a 4x4 block, 16 tokens per stage.
@@ -434,10 +477,10 @@ gptq_status hessian_launch(double* H, const void* X, gptq_dtype dt, int64_t n_to
     const int64_t per_xcd = ceil_div(n_tiles, 8);
     const bool vec = (ld_x % 8 == 0) && (d % 8 == 0) && ((uintptr_t)X % 16 == 0);
     const uint16_t* x = (const uint16_t*)X;
-    GPTQ_HIP(hipFuncSetAttribute((const void*)hess_syrk_kernel<bf16x8_t>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                 RING_BYTES));
-    GPTQ_HIP(hipFuncSetAttribute((const void*)hess_syrk_kernel<h16x8_t>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                 RING_BYTES));
+    GPTQ_HIP(hipFuncSetAttribute((const void*)hess_syrk_kernel<bf16x8_t, SYRK_WAVES>,
+                                 hipFuncAttributeMaxDynamicSharedMemorySize, RING_BYTES));
+    GPTQ_HIP(hipFuncSetAttribute((const void*)hess_syrk_kernel<h16x8_t, SYRK_WAVES>,
+                                 hipFuncAttributeMaxDynamicSharedMemorySize, RING_BYTES));
     const dim3 b256(256);
     // per chunk: transpose into Xt, then one SYRK launch that adds its
     // float32 partial tiles to H in float64; chunks in token order
@@ -458,14 +501,14 @@ gptq_status hessian_launch(double* H, const void* X, gptq_dtype dt, int64_t n_to
         GPTQ_LAUNCH_CHECK();
         hipLaunchKernelGGL(diag_add_kernel, dim3((unsigned)ceil_div(d, 256)), b256, 0, s, part, nblk, d, H);
         GPTQ_LAUNCH_CHECK();
-        const dim3 grid((unsigned)(per_xcd * 8)), block(512);
+        const dim3 grid((unsigned)(per_xcd * 8)), block(SYRK_WAVES * 64);
         if (ev) GPTQ_HIP(hipEventRecord(ev[2 * ci], s));
         if (dt == GPTQ_BF16)
-            hipLaunchKernelGGL(hess_syrk_kernel<bf16x8_t>, grid, block, RING_BYTES, s, H, xt, ch, d, T, n_tiles,
-                               per_xcd);
+            hipLaunchKernelGGL((hess_syrk_kernel<bf16x8_t, SYRK_WAVES>), grid, block, RING_BYTES, s, H, xt, ch, d, T,
+                               n_tiles, per_xcd);
         else
-            hipLaunchKernelGGL(hess_syrk_kernel<h16x8_t>, grid, block, RING_BYTES, s, H, xt, ch, d, T, n_tiles,
-                               per_xcd);
+            hipLaunchKernelGGL((hess_syrk_kernel<h16x8_t, SYRK_WAVES>), grid, block, RING_BYTES, s, H, xt, ch, d, T,
+                               n_tiles, per_xcd);
         GPTQ_LAUNCH_CHECK();
         if (ev) GPTQ_HIP(hipEventRecord(ev[2 * ci + 1], s));
     }

@@ -21,9 +21,9 @@
 //   M21 = -M22 T                      (M22 lower: K ends at the tile's row)
 // so the big products have K up to d/2 and run near the float64 MFMA peak,
 // where a right-looking blocked factorisation would be stuck at K = 64..128.
-// The leaves are 128x128 blocks factored and inverted in one pass by one
-// workgroup with the block held in registers (8x8 per thread).  L itself is
-// never stored: only M (written into H's buffer) is needed.
+// The leaves are 128x128 blocks factored and inverted by one workgroup in
+// LDS (16x16 inner blocks; see leaf_blocked_kernel).  L itself is never
+// stored outside the leaves: only M (written into H's buffer) is needed.
 //
 // Workspace layout (byte offsets):
 //   [0, 256)             int flags[N_FLAGS]; double lambda at 64
@@ -37,9 +37,6 @@ namespace gptq {
 namespace {
 
 constexpr int LEAF = 128;         // leaf block edge
-constexpr int LT = 8;             // register tile edge
-constexpr int NLT = LEAF / LT;    // register tiles per leaf edge
-constexpr int LEAF_THREADS = 512;  // two groups of NLT x NLT tile slots
 
 void split(int64_t n, int64_t& n1, int64_t& n2) {
     const int64_t nb = ceil_div(n, LEAF);
@@ -216,22 +213,6 @@ __global__ __launch_bounds__(256) void gather_reverse_kernel(const double* __res
     }
 }
 
-// Leaf of the recursion: the n x n (n <= 128) diagonal block of Hr at
-// offset o is factored, A = L L^T, and M = L^{-1} is written to the same
-// block of Mi (lower triangle, zeros above the diagonal; the padding up to
-// 128 acts as an identity block).  L itself is only ever held one column at
-// a time.
-//
-// One pass over the 128 columns, one barrier per column.  Waves 0-3 hold A
-// and waves 4-7 hold X (-> L^{-1}), each thread one lower 8x8 register tile
-// (thread u of a group: column tile u/16, row tile u%16, so the tiles of a
-// column tile sit in one wave).  At column j:
-//   factor: A[r][c] -= l[r] l[c] for c > j, with l = column j of L;
-//   inverse: x_j = X[j,:] / L[j][j] is row j of L^{-1}, and
-//            X[r,:] -= l[r] x_j for r > j (forward substitution).
-// Then the wave owning column tile (j+1)/8 reads the next pivot from the
-// diagonal lane, scales column j+1 by its reciprocal square root and
-// publishes it; the owners of row j+1 of X publish that row.
 __device__ __forceinline__ double readlane_f64(double v, int lane) {
     const uint64_t b = __builtin_bit_cast(uint64_t, v);
     const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, lane);
@@ -250,137 +231,237 @@ __device__ __forceinline__ double rsqrt_nr(double p) {
     return fma(y, e, y);
 }
 
-__global__ __launch_bounds__(LEAF_THREADS) void leaf_chol_inv_kernel(const double* __restrict__ A, double* Mi,
-                                                                     int64_t d, int64_t o, int n, int* flags) {
-    __shared__ double lb[2][LEAF];  // column j of L (scaled), zero above the pivot
-    __shared__ double xb[2][LEAF];  // row j of X before scaling
-    __shared__ double rsb[2];       // 1 / L[j][j]
-    const int t = threadIdx.x;
-    const bool inv_grp = t >= 256;
-    const int u = t & 255;
-    const int ct = u >> 4, rt = u & 15;
-    const bool own = rt >= ct;
-    const int r0 = rt * LT, c0 = ct * LT;
-    const int wave = u >> 6, lane = t & 63;
+// Leaf of the recursion: the n x n (n <= 128) diagonal block of Hr at
+// offset o is factored, A = L L^T, and M = L^{-1} is written to the same
+// block of Mi (lower, zeros above the diagonal; the padding up to 128 acts
+// as an identity block), with the 128x128 block in LDS and 16x16 inner
+// blocks.  L is formed in place (lower triangle); M is formed along
+// by forward elimination: R starts as the identity, and at block step k
+// block row k of M is Dinv_k R_k (Dinv_k the inverse of the diagonal
+// factor) while the rows below lose L[r][k-block] M_k.  The off-diagonal
+// blocks of R / M live transposed in the free upper triangle of the LDS
+// block; M's diagonal blocks are the Dinv_k.
+//   setup: wave 0 factors diagonal block 0;
+//   block step k: (A) rows below get L[r][k-block] = A[r][k-block] Dinv_k^T,
+//                     and block row k of M = Dinv_k R_k;
+//                 (B) wave 0 updates diagonal block k+1 and factors it while
+//                     the other waves update the rest of the trailing lower
+//                     part and the rows of R below block k.
+// The 16x16 factor: one wave, lane = (row r, 4 columns), column j of L and
+// row j of its inverse exchanged through LDS inside the wave.
+constexpr int LB = 16;               // inner block edge
+constexpr int NIB = LEAF / LB;       // inner blocks per edge
+constexpr int LDA = LEAF + 1;        // LDS row stride (doubles)
+constexpr size_t LEAF_LDS = (size_t)(LEAF * LDA + NIB * LB * LB + 2 * LB) * sizeof(double);
 
-    double v[LT][LT];
+// Factor the 16x16 diagonal block at (k0, k0) of As in place (lower) and
+// write the inverse of the factor to dinv (16x16, zeros above).  Wave 0.
+__device__ __forceinline__ void diag16(double* As, int k0, double* dinv, double* colb, double* rowb, int lane,
+                                       bool& bad_pd, bool& bad_nan) {
+    // A wave executes its LDS operations in order; compiler memory barriers
+    // between the stores and the loads of a step (and before the next
+    // step's stores) keep the compiler from reusing earlier loaded values.
+    const int r = lane >> 2, cg = lane & 3;
+    double a[4], x[4];
 #pragma unroll
-    for (int i = 0; i < LT; ++i)
+    for (int q = 0; q < 4; ++q) {
+        const int c = 4 * cg + q;
+        const double v = As[(k0 + r) * LDA + k0 + c];
+        a[q] = (c <= r) ? v : 0.0;
+        x[q] = (c == r) ? 1.0 : 0.0;
+    }
 #pragma unroll
-        for (int k = 0; k < LT; ++k) {
-            const int r = r0 + i, c = c0 + k;
-            double e = (r == c) ? 1.0 : 0.0;
-            if (!inv_grp && own && r < n && c < n) e = (c <= r) ? A[(o + r) * d + o + c] : 0.0;
-            v[i][k] = e;
-        }
-
-    bool bad_pd = false, bad_nan = false;
-    // publish column 0 and row 0
-    if (!inv_grp && wave == 0) {
-        double piv = readlane_f64(v[0][0], 0);
+    for (int j = 0; j < LB; ++j) {
+        double piv = readlane_f64(a[j & 3], 4 * j + (j >> 2));
         if (!(piv > 0.0)) {
             bad_nan |= isnan(piv);
             bad_pd |= !isnan(piv);
             piv = 1.0;
         }
         const double rs = rsqrt_nr(piv);
-        if (own && ct == 0) {
+        const bool owner = cg == (j >> 2);
+        const double lv = (r > j) ? a[j & 3] * rs : ((r == j) ? piv * rs : 0.0);
+        a[j & 3] = owner ? lv : a[j & 3];
+        if (owner) colb[r] = lv;
 #pragma unroll
-            for (int i = 0; i < LT; ++i) lb[0][r0 + i] = (r0 + i > 0) ? v[i][0] * rs : piv * rs;
+        for (int q = 0; q < 4; ++q) x[q] = (r == j) ? x[q] * rs : x[q];
+        if (r == j) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) rowb[4 * cg + q] = x[q];
         }
-        if (lane == 0) rsb[0] = rs;
-    }
-    if (inv_grp && own && rt == 0) {
+        asm volatile("" ::: "memory");
+        const double lr = colb[r];
 #pragma unroll
-        for (int k = 0; k < LT; ++k) xb[0][c0 + k] = v[0][k];
+        for (int q = 0; q < 4; ++q) {
+            const int c = 4 * cg + q;
+            const double lcv = colb[c];
+            const double xsv = rowb[c];
+            a[q] = fma(-lr, (c > j) ? lcv : 0.0, a[q]);
+            x[q] = fma(-lr, (r > j) ? xsv : 0.0, x[q]);
+        }
+        asm volatile("" ::: "memory");
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int c = 4 * cg + q;
+        if (c <= r) As[(k0 + r) * LDA + k0 + c] = a[q];
+        dinv[r * LB + c] = x[q];
+    }
+}
+
+__global__ __launch_bounds__(512) void leaf_blocked_kernel(const double* __restrict__ A, double* Mi, int64_t d,
+                                                           int64_t o, int n, int* flags) {
+    extern __shared__ double sm[];
+    double* As = sm;                        // [LEAF][LDA]: L (lower); R / M transposed (upper)
+    double* Dv = sm + LEAF * LDA;           // [NIB][LB][LB]: inverses of the diagonal factors
+    double* colb = Dv + NIB * LB * LB;      // [LB] column exchange of the 16x16 factor
+    double* rowb = colb + LB;               // [LB] row exchange of its inverse
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+
+    // Hr block (lower; identity padding); R = I: zeros above the diagonal
+    for (int e = t; e < LEAF * LEAF; e += 512) {
+        const int r = e >> 7, c = e & (LEAF - 1);
+        double v = 0.0;
+        if (c <= r) {
+            if (r < n && c < n) v = A[(o + r) * d + o + c];
+            else v = (r == c) ? 1.0 : 0.0;
+        }
+        As[r * LDA + c] = v;
     }
     __syncthreads();
+    bool bad_pd = false, bad_nan = false;
+    if (wave == 0) diag16(As, 0, Dv, colb, rowb, lane, bad_pd, bad_nan);
+    __syncthreads();
 
-    for (int jb = 0; jb < NLT; ++jb) {
+    for (int kb = 0; kb < NIB; ++kb) {
+        const int k0 = kb * LB;
+        const int rows = LEAF - k0 - LB;   // rows below the block
+        const double* dk = Dv + kb * LB * LB;
+        // (A) panel of L: one thread per row below; block row kb of M:
+        //     M[k0+r][c] = sum_{q<=r} Dinv_k[r][q] R[k0+q][c], one thread per column c < k0
+        if (t < rows) {
+            const int r = k0 + LB + t;
+            double a[LB];
 #pragma unroll
-        for (int jj = 0; jj < LT; ++jj) {
-            const int j = jb * LT + jj;
-            const int cur = j & 1, nxt = cur ^ 1;
-            const int kn = (jj + 1) % LT;          // register column of j+1
-            const int ctn = jb + (jj + 1) / LT;    // column / row tile of j+1
-            if (!inv_grp) {
-                if (own && c0 + LT - 1 > j) {
-                    double cr[LT], cc[LT];
+            for (int k = 0; k < LB; ++k) a[k] = As[r * LDA + k0 + k];
 #pragma unroll
-                    for (int i = 0; i < LT; ++i) cr[i] = lb[cur][r0 + i];
+            for (int c = 0; c < LB; ++c) {
+                double s = 0.0;
 #pragma unroll
-                    for (int k = 0; k < LT; ++k) cc[k] = (c0 + k > j) ? lb[cur][c0 + k] : 0.0;
+                for (int k = 0; k <= c; ++k) s = fma(a[k], dk[c * LB + k], s);
+                As[r * LDA + k0 + c] = s;
+            }
+        } else if (t >= 128 && t - 128 < k0) {
+            const int c = t - 128;   // R[k0+q][c] stored at As[c][k0+q]
+            double rv[LB];
 #pragma unroll
-                    for (int i = 0; i < LT; ++i)
+            for (int q = 0; q < LB; ++q) rv[q] = As[c * LDA + k0 + q];
 #pragma unroll
-                        for (int k = 0; k < LT; ++k) v[i][k] = fma(-cr[i], cc[k], v[i][k]);
-                }
-                if (j + 1 < LEAF && wave == (ctn >> 2)) {
-                    const int lane_d = 16 * (ctn & 3) + ctn;
-                    double piv = readlane_f64(v[kn][kn], lane_d);
-                    if (!(piv > 0.0)) {
-                        bad_nan |= isnan(piv);
-                        bad_pd |= !isnan(piv);
-                        piv = 1.0;
-                    }
-                    const double rs = rsqrt_nr(piv);
-                    if (own && ct == ctn) {
+            for (int rr = 0; rr < LB; ++rr) {
+                double s = 0.0;
 #pragma unroll
-                        for (int i = 0; i < LT; ++i) {
-                            const int r = r0 + i;
-                            lb[nxt][r] = (r > j + 1) ? v[i][kn] * rs : ((r == j + 1) ? piv * rs : 0.0);
+                for (int q = 0; q <= rr; ++q) s = fma(dk[rr * LB + q], rv[q], s);
+                As[c * LDA + k0 + rr] = s;
+            }
+        }
+        __syncthreads();
+        if (rows == 0) break;
+        // (B)
+        if (wave == 0) {
+            // diagonal block kb+1 loses L[.][k-block] L[.][k-block]^T, then is factored
+            const int b0 = k0 + LB;
+            for (int e = lane; e < LB * LB; e += 64) {
+                const int r = e >> 4, c = e & (LB - 1);
+                if (c > r) continue;
+                double s = 0.0;
+#pragma unroll
+                for (int k = 0; k < LB; ++k) s = fma(As[(b0 + r) * LDA + k0 + k], As[(b0 + c) * LDA + k0 + k], s);
+                As[(b0 + r) * LDA + b0 + c] -= s;
+            }
+            asm volatile("" ::: "memory");
+            diag16(As, b0, Dv + (kb + 1) * LB * LB, colb, rowb, lane, bad_pd, bad_nan);
+        } else {
+            const int tt = t - 64;   // 448 threads
+            // trailing lower part below/right of block kb+1's diagonal block:
+            // rows and columns >= k0+16, 4x4 tiles, except the 10 tiles of the
+            // diagonal block kb+1 (handled by wave 0)
+            const int T4 = rows / 4;
+            const int ntl = T4 * (T4 + 1) / 2;
+            // rows of R below block kb: R[r][c] -= sum_q L[r][k0+q] M[k0+q][c], c < k0+16,
+            // R[r][c] at As[c][r]; M[k0+q][c] = Dinv_k[q][c-k0] for c >= k0, else As[c][k0+q]
+            const int C4 = (k0 + LB) / 4;
+            const int nx = T4 * C4;
+            for (int w = tt; w < ntl + nx; w += 448) {
+                if (w < ntl) {
+                    int ti = 0;
+                    while ((ti + 1) * (ti + 2) / 2 <= w) ++ti;
+                    const int tj = w - ti * (ti + 1) / 2;
+                    if (ti < 4) continue;  // the diagonal block kb+1 (tiles 0..9)
+                    const int r0 = k0 + LB + 4 * ti, c0 = k0 + LB + 4 * tj;
+                    double acc[4][4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
+#pragma unroll 4
+                    for (int k = 0; k < LB; ++k) {
+                        double lr[4], lc[4];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            lr[i] = As[(r0 + i) * LDA + k0 + k];
+                            lc[i] = As[(c0 + i) * LDA + k0 + k];
                         }
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) acc[i][j] = fma(lr[i], lc[j], acc[i][j]);
                     }
-                    if (lane == lane_d) rsb[nxt] = rs;
-                }
-            } else {
-                const double rs = rsb[cur];
-                if (own && ct <= jb) {
-                    double xs[LT];
 #pragma unroll
-                    for (int k = 0; k < LT; ++k) xs[k] = xb[cur][c0 + k] * rs;
-                    if (r0 + LT - 1 > j) {
-                        double lr[LT];
+                    for (int i = 0; i < 4; ++i)
 #pragma unroll
-                        for (int i = 0; i < LT; ++i) lr[i] = (r0 + i > j) ? lb[cur][r0 + i] : 0.0;
+                        for (int j = 0; j < 4; ++j) As[(r0 + i) * LDA + c0 + j] -= acc[i][j];
+                } else {
+                    const int x = w - ntl;
+                    const int r0 = k0 + LB + 4 * (x / C4), c0 = 4 * (x % C4);
+                    const bool diagc = c0 >= k0;   // columns inside block kb: M = Dinv_k
+                    double acc[4][4];
 #pragma unroll
-                        for (int i = 0; i < LT; ++i)
+                    for (int i = 0; i < 4; ++i)
 #pragma unroll
-                            for (int k = 0; k < LT; ++k) v[i][k] = fma(-lr[i], xs[k], v[i][k]);
+                        for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
+#pragma unroll 4
+                    for (int q = 0; q < LB; ++q) {
+                        double lr[4], mq[4];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) lr[i] = As[(r0 + i) * LDA + k0 + q];
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            mq[j] = diagc ? dk[q * LB + (c0 - k0) + j] : As[(c0 + j) * LDA + k0 + q];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) acc[i][j] = fma(lr[i], mq[j], acc[i][j]);
                     }
-                    if (rt == jb) {
 #pragma unroll
-                        for (int k = 0; k < LT; ++k) v[jj][k] = xs[k];
-                    }
-                }
-                if (j + 1 < LEAF && own && rt == ctn) {
+                    for (int i = 0; i < 4; ++i)
 #pragma unroll
-                    for (int k = 0; k < LT; ++k) xb[nxt][c0 + k] = v[kn][k];
+                        for (int j = 0; j < 4; ++j) As[(c0 + j) * LDA + r0 + i] -= acc[i][j];
                 }
             }
-            __syncthreads();
         }
+        __syncthreads();
     }
     if (bad_nan) raise_flag(flags, FLAG_NONFINITE);
     if (bad_pd) raise_flag(flags, FLAG_NOT_PD);
 
-    if (inv_grp && own) {
-#pragma unroll
-        for (int i = 0; i < LT; ++i) {
-            const int r = r0 + i;
-            if (r >= n) continue;
-#pragma unroll
-            for (int k = 0; k < LT; ++k) {
-                const int c = c0 + k;
-                if (c < n) Mi[(o + r) * d + o + c] = v[i][k];
-            }
-        }
-    }
-    // zeros in the strictly upper register tiles of the block: the products
-    // that take this block as a triangular operand read them
-    for (int e = t; e < LEAF * LEAF; e += LEAF_THREADS) {
-        const int r = e / LEAF, c = e % LEAF;
-        if (r < n && c < n && c / LT > r / LT) Mi[(o + r) * d + o + c] = 0.0;
+    // write M (lower, zeros above the diagonal) for the n x n part
+    for (int e = t; e < LEAF * LEAF; e += 512) {
+        const int r = e >> 7, c = e & (LEAF - 1);
+        if (r >= n || c >= n) continue;
+        double v = 0.0;
+        if (r / LB == c / LB) v = Dv[((r / LB) * LB + (r % LB)) * LB + (c % LB)];
+        else if (r > c) v = As[c * LDA + r];
+        Mi[(o + r) * d + o + c] = v;
     }
 }
 
@@ -439,7 +520,7 @@ struct Rec {
 gptq_status chol_inv(const Rec& c, int64_t o, int64_t n, int depth) {
     const int64_t d = c.d;
     if (n <= LEAF) {
-        hipLaunchKernelGGL(leaf_chol_inv_kernel, dim3(1), dim3(LEAF_THREADS), 0, c.s, c.L, c.M, d, o, (int)n, c.flags);
+        hipLaunchKernelGGL(leaf_blocked_kernel, dim3(1), dim3(512), LEAF_LDS, c.s, c.L, c.M, d, o, (int)n, c.flags);
         GPTQ_LAUNCH_CHECK();
         return GPTQ_OK;
     }
@@ -481,6 +562,8 @@ gptq_status hinv_launch(double* H, int64_t d, const gptq_config* cfg, int32_t* p
                         hipStream_t s, int* host_flags) {
     Ws w;
     layout(d, &w, (char*)ws);
+    GPTQ_HIP(hipFuncSetAttribute((const void*)leaf_blocked_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                 (int)LEAF_LDS));
     GPTQ_HIP(hipMemsetAsync(w.flags, 0, 256, s));
 
     hipLaunchKernelGGL(diag_stats_kernel, dim3(1), dim3(1024), 0, s, H, d, cfg->damp, w.lambda, w.diag, w.flags);

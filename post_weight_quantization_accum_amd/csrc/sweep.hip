@@ -23,7 +23,7 @@
 //
 // Lazy updates are two-level (mathematically the same as one update per
 // block): after each block, a float64 MFMA GEMM updates the rest of its
-// superblock of S = 512 columns (K = B); after each superblock, one GEMM
+// superblock of S = 1024 columns (K = B); after each superblock, one GEMM
 // with K = S updates the next superblock, and another (on a second stream,
 // overlapping the next superblock's sweep) everything after it.
 #include "internal.hpp"
@@ -55,7 +55,10 @@ int64_t n_groups_of(int64_t d_in, int32_t g) { return g > 0 ? ceil_div(d_in, g) 
 // inside one superblock or start on a superblock boundary; otherwise S = B.
 int64_t superblock_cols(int64_t d_in, const gptq_config* cfg) {
     const int64_t B = cfg->block_size;
-    const int64_t S = B * (512 / B > 0 ? 512 / B : 1);
+#ifndef GPTQ_SUPER
+#define GPTQ_SUPER 1024
+#endif
+    const int64_t S = B * (GPTQ_SUPER / B > 0 ? GPTQ_SUPER / B : 1);
     const int64_t g = cfg->group_size > 0 ? cfg->group_size : d_in;
     if (cfg->group_size <= 0 || S % g == 0 || g % S == 0) return S;
     return B;

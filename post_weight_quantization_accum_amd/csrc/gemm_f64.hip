@@ -132,11 +132,21 @@ __global__ __launch_bounds__(256, 2) void gemm_f64_kernel(int64_t M, int64_t N, 
         // stay in its L2; every XCD gets light and heavy bands), heaviest
         // rows / columns dispatched first.
         const int64_t x = b % 8, q = b / 8;
-        const int64_t band = x + 8 * (q / tiles_n);
-        if (band >= tiles_m) return;
-        tm = (tri == GEMM_TRI_KEND_ROW) ? tiles_m - 1 - band : band;
-        tn = q % tiles_n;
-        if (tri == GEMM_TRI_KEND_COL) tn = tiles_n - 1 - tn;
+        if (tri == GEMM_TRI_KEND_ROW) {
+            // work grows with the row: bands in descending order
+            const int64_t band = x + 8 * (q / tiles_n);
+            if (band >= tiles_m) return;
+            tm = tiles_m - 1 - band;
+            tn = q % tiles_n;
+        } else {
+            // work varies along the columns: column-major over this XCD's
+            // bands, heaviest columns first
+            const int64_t nb = (tiles_m - x + 7) / 8;  // bands of this XCD
+            if (nb <= 0 || q >= nb * tiles_n) return;
+            tm = x + 8 * (q % nb);
+            const int64_t ci = q / nb;
+            tn = (tri == GEMM_TRI_KEND_COL) ? tiles_n - 1 - ci : ci;
+        }
     } else {
         const int64_t lin = (b % 8) * per_xcd + b / 8;
         if (lin >= n_tiles) return;

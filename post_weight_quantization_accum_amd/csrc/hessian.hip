@@ -17,7 +17,11 @@
 // Each MFMA operand is 8 consecutive tokens of one column, while X is
 // token-major.  A chunk is therefore first transposed (8x8 blocks in
 // registers, v_perm_b32) into a feature-major copy Xt, zero-padded to a
-// multiple of 256 features and of 64 tokens.  The SYRK kernel then streams
+// multiple of 256 features and of 64 tokens, stored stage-major: the 64
+// tokens of all features for one stage form one contiguous block, so the
+// stage of one 256-feature panel is 32 KiB of consecutive memory (few pages
+// and DRAM rows per stage, instead of 256 rows a chunk-length apart).  The
+// SYRK kernel then streams
 // Xt straight from memory into LDS with buffer_load ... lds (no VGPR
 // staging) through a ring of two 64-token stages (64 KiB each), one stage
 // ahead of the MFMAs, one barrier per stage; the MFMA operands are
@@ -103,8 +107,9 @@ __device__ __forceinline__ uint32_t word(const u32x4_t& v, int i) {
     return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
 }
 
-// Xt[f][t] = X[t][f] for one chunk: n_tok tokens, Xt row stride ch tokens,
-// zeros for t >= n_tok (up to ch) and for d <= f < d_pad; also the float64
+// Xt[t / KT][f][t % KT] = X[t][f] for one chunk (stage-major: the KT tokens
+// of all d_pad features for one stage are one contiguous block), n_tok
+// tokens, zeros for t >= n_tok (up to ch) and for d <= f < d_pad; also the float64
 // sums of squares of the block's 512 tokens per feature (diagonal of H).
 // A block covers 512 tokens x 256 features in tiles of 64 tokens: a thread
 // loads 8 tokens x 8 features (16-byte loads, 32 lanes along the features:
@@ -118,7 +123,8 @@ constexpr int TLD = TT + 8;     // LDS row stride (16-bit elements)
 template <typename Tag, bool VEC>
 __global__ __launch_bounds__(256) void transpose_kernel(const uint16_t* __restrict__ X, int64_t n_tok, int64_t d,
                                                         int64_t ld, uint16_t* __restrict__ Xt, int64_t ch,
-                                                        double* __restrict__ colsq) {
+                                                        int64_t d_pad, double* __restrict__ colsq) {
+    static_assert(TT == KT, "a transpose tile is one stage");
     __shared__ __attribute__((aligned(16))) uint16_t tile[256 * TLD];
     __shared__ double red[8][256];
     const int t = threadIdx.x;
@@ -180,7 +186,8 @@ __global__ __launch_bounds__(256) void transpose_kernel(const uint16_t* __restri
             const int fr = e >> 3, gq = e & 7;
             const int64_t tok = tbase + gq * 8;
             if (tok < ch)
-                *(u32x4_t*)&Xt[(fblk + fr) * ch + tok] = *(const u32x4_t*)&tile[fr * TLD + gq * 8];
+                *(u32x4_t*)&Xt[((tbase / KT) * d_pad + fblk + fr) * KT + gq * 8] =
+                    *(const u32x4_t*)&tile[fr * TLD + gq * 8];
         }
     }
     // column sums of squares: the 8 token groups in a fixed order
@@ -227,15 +234,15 @@ __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (
 __device__ __forceinline__ int swz(int r) { return (r / RPB) % GR; }
 
 __device__ __forceinline__ void dma_panel_rows(__amdgpu_buffer_rsrc_t rs, char* lds_panel, int row0, int lane,
-                                               int64_t tok0, int64_t ch) {
+                                               uint32_t prow, uint32_t soff) {
 #pragma unroll
     for (int q = 0; q < 32 / DMA_ROWS; ++q) {
         const int rblk = row0 + DMA_ROWS * q;
         const int r = rblk + lane / GR;
         const int g = (lane % GR) ^ swz(r);
-        const uint32_t voff = (uint32_t)(((int64_t)r * ch + tok0 + 8 * g) * 2);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(lds_panel + rblk * (KT * 2)), 16, (int)voff, 0, 0,
-                                                 0);
+        const uint32_t voff = ((prow + (uint32_t)r) * KT + 8 * g) * 2;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(lds_panel + rblk * (KT * 2)), 16, (int)voff,
+                                                 (int)soff, 0, 0);
     }
 }
 
@@ -245,19 +252,19 @@ __device__ __forceinline__ u32x4_t lds_operand(const char* lds_panel, int r, int
 }
 
 template <typename Tag, bool DIAG, int NW>
-__device__ __forceinline__ void syrk_tile(double* __restrict__ H, const uint16_t* __restrict__ Xt, int64_t ch,
+__device__ __forceinline__ void syrk_tile(double* __restrict__ H, const uint16_t* __restrict__ Xt, int64_t ch, int64_t d_pad,
                                           int64_t d, int64_t ti, int64_t tj, char* lds) {
     constexpr int WCOLS = 512 / NW, NTL = WCOLS / 32, NCW = BT / WCOLS;
     constexpr int RPW = BT / NW;  // panel rows loaded per wave (multiple of 32)
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int wr = wave / NCW, wc = wave % NCW;
     const int64_t n_st = ch / KT;
-    // one resource per panel: 256 rows of ch tokens
-    const uint32_t pbytes = (uint32_t)(BT * ch * 2);
-    const __amdgpu_buffer_rsrc_t ra =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(Xt + ti * BT * ch), (short)0, (int)pbytes, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rb =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(Xt + tj * BT * ch), (short)0, (int)pbytes, 0x00020000);
+    // one resource over the chunk; a stage of one panel is 256 consecutive
+    // rows of KT tokens, at byte offset (st * d_pad + panel row) * KT * 2
+    const uint32_t stage_bytes = (uint32_t)(d_pad * KT * 2);
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)Xt, (short)0, (int)(stage_bytes * (uint32_t)n_st), 0x00020000);
+    const uint32_t pa_row = (uint32_t)(ti * BT), pb_row = (uint32_t)(tj * BT);
     const int row0 = wave * RPW;
     // loads issued per wave per stage
     constexpr int NLD = (DIAG ? 1 : 2) * (RPW / DMA_ROWS);
@@ -274,8 +281,8 @@ __device__ __forceinline__ void syrk_tile(double* __restrict__ H, const uint16_t
         char* sb = lds + (st % NSTAGE) * STAGE_BYTES;
 #pragma unroll
         for (int rr = 0; rr < RPW; rr += 32) {
-            dma_panel_rows(ra, sb, row0 + rr, lane, st * KT, ch);
-            if (!DIAG) dma_panel_rows(rb, sb + PANEL_BYTES, row0 + rr, lane, st * KT, ch);
+            dma_panel_rows(rs, sb, row0 + rr, lane, pa_row, (uint32_t)st * stage_bytes);
+            if (!DIAG) dma_panel_rows(rs, sb + PANEL_BYTES, row0 + rr, lane, pb_row, (uint32_t)st * stage_bytes);
         }
     };
     auto read_ops = [&](u32x4_t (&a)[4], u32x4_t (&bb)[NTL], int64_t st, int ks) {
@@ -361,7 +368,8 @@ __device__ __forceinline__ void syrk_tile(double* __restrict__ H, const uint16_t
 
 template <typename Tag, int NW>
 __global__ __launch_bounds__(NW * 64) void hess_syrk_kernel(double* __restrict__ H, const uint16_t* __restrict__ Xt,
-                                                            int64_t ch, int64_t d, int64_t T, int64_t n_tiles,
+                                                            int64_t ch, int64_t d_pad, int64_t d, int64_t T,
+                                                            int64_t n_tiles,
                                                             int64_t per_xcd) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
     // XCD-grouped tile order: workgroup b runs on XCD b % 8; each XCD takes a
@@ -371,11 +379,14 @@ __global__ __launch_bounds__(NW * 64) void hess_syrk_kernel(double* __restrict__
     if (lin >= n_tiles) return;
     int64_t ti, tj;
     upper_tile(lin, ti, tj, T);
-    if (ti == tj) syrk_tile<Tag, true, NW>(H, Xt, ch, d, ti, tj, lds);
-    else syrk_tile<Tag, false, NW>(H, Xt, ch, d, ti, tj, lds);
+    if (ti == tj) syrk_tile<Tag, true, NW>(H, Xt, ch, d_pad, d, ti, tj, lds);
+    else syrk_tile<Tag, false, NW>(H, Xt, ch, d_pad, d, ti, tj, lds);
 }
 
-constexpr int SYRK_WAVES = 8;
+#ifndef GPTQ_SYRK_WAVES
+#define GPTQ_SYRK_WAVES 8
+#endif
+constexpr int SYRK_WAVES = GPTQ_SYRK_WAVES;
 
 // fp32 activations: float64 products and sums.  64x64 tiles of the upper
 // triangle, 256 threads, each thread a 4x4 block, 16 tokens per stage.
@@ -492,11 +503,11 @@ gptq_status hessian_launch(double* H, const void* X, gptq_dtype dt, int64_t n_to
         const int64_t nblk = ceil_div(ch, TSPAN);
         const dim3 tgrid((unsigned)nblk, (unsigned)(d_pad / 256));
         if (dt == GPTQ_BF16) {
-            if (vec) hipLaunchKernelGGL((transpose_kernel<bf16x8_t, true>), tgrid, b256, 0, s, xc, nt, d, ld_x, xt, ch, part);
-            else hipLaunchKernelGGL((transpose_kernel<bf16x8_t, false>), tgrid, b256, 0, s, xc, nt, d, ld_x, xt, ch, part);
+            if (vec) hipLaunchKernelGGL((transpose_kernel<bf16x8_t, true>), tgrid, b256, 0, s, xc, nt, d, ld_x, xt, ch, d_pad, part);
+            else hipLaunchKernelGGL((transpose_kernel<bf16x8_t, false>), tgrid, b256, 0, s, xc, nt, d, ld_x, xt, ch, d_pad, part);
         } else {
-            if (vec) hipLaunchKernelGGL((transpose_kernel<h16x8_t, true>), tgrid, b256, 0, s, xc, nt, d, ld_x, xt, ch, part);
-            else hipLaunchKernelGGL((transpose_kernel<h16x8_t, false>), tgrid, b256, 0, s, xc, nt, d, ld_x, xt, ch, part);
+            if (vec) hipLaunchKernelGGL((transpose_kernel<h16x8_t, true>), tgrid, b256, 0, s, xc, nt, d, ld_x, xt, ch, d_pad, part);
+            else hipLaunchKernelGGL((transpose_kernel<h16x8_t, false>), tgrid, b256, 0, s, xc, nt, d, ld_x, xt, ch, d_pad, part);
         }
         GPTQ_LAUNCH_CHECK();
         hipLaunchKernelGGL(diag_add_kernel, dim3((unsigned)ceil_div(d, 256)), b256, 0, s, part, nblk, d, H);
@@ -504,10 +515,10 @@ gptq_status hessian_launch(double* H, const void* X, gptq_dtype dt, int64_t n_to
         const dim3 grid((unsigned)(per_xcd * 8)), block(SYRK_WAVES * 64);
         if (ev) GPTQ_HIP(hipEventRecord(ev[2 * ci], s));
         if (dt == GPTQ_BF16)
-            hipLaunchKernelGGL((hess_syrk_kernel<bf16x8_t, SYRK_WAVES>), grid, block, RING_BYTES, s, H, xt, ch, d, T,
+            hipLaunchKernelGGL((hess_syrk_kernel<bf16x8_t, SYRK_WAVES>), grid, block, RING_BYTES, s, H, xt, ch, d_pad, d, T,
                                n_tiles, per_xcd);
         else
-            hipLaunchKernelGGL((hess_syrk_kernel<h16x8_t, SYRK_WAVES>), grid, block, RING_BYTES, s, H, xt, ch, d, T,
+            hipLaunchKernelGGL((hess_syrk_kernel<h16x8_t, SYRK_WAVES>), grid, block, RING_BYTES, s, H, xt, ch, d_pad, d, T,
                                n_tiles, per_xcd);
         GPTQ_LAUNCH_CHECK();
         if (ev) GPTQ_HIP(hipEventRecord(ev[2 * ci + 1], s));

@@ -227,40 +227,48 @@ __global__ __launch_bounds__(256, 2) void gemm_f64_kernel(int64_t M, int64_t N, 
         }
 }
 
+// LDS a workgroup must hold so that only one fits on a CU (160 KiB each).
+constexpr size_t CU_LDS = 160 * 1024;
+
 template <int TILE, bool TRANS_B, bool LOWER>
 void launch_t(hipStream_t s, bool vec, int64_t M, int64_t N, int64_t K, double alpha, const double* A, int64_t lda,
-              const double* B, int64_t ldb, double beta, double* C, int64_t ldc, int tri) {
+              const double* B, int64_t ldb, double beta, double* C, int64_t ldc, int tri, bool one_per_cu) {
     const int64_t tiles_m = ceil_div(M, TILE), tiles_n = ceil_div(N, TILE);
     const int64_t n_tiles = LOWER ? tiles_m * (tiles_m + 1) / 2 : tiles_m * tiles_n;
     const int64_t per_xcd =
         (!LOWER && tri != GEMM_TRI_NONE && tiles_m >= 16) ? ceil_div(tiles_m, 8) * tiles_n : ceil_div(n_tiles, 8);
     const dim3 grid((unsigned)(per_xcd * 8));
+    // one_per_cu: unused dynamic LDS beyond half a CU's, so that a second
+    // workgroup of this launch never shares the CU (room for other streams)
+    constexpr size_t static_lds = 2 * 2 * KC * Cfg<TILE>::LD * sizeof(double);
+    const size_t pad = one_per_cu ? CU_LDS / 2 + 1024 - static_lds : 0;
     if (vec)
-        hipLaunchKernelGGL((gemm_f64_kernel<TILE, TRANS_B, LOWER, true>), grid, dim3(256), 0, s, M, N, K, alpha, A,
-                           lda, B, ldb, beta, C, ldc, tiles_m, tiles_n, n_tiles, per_xcd, tri);
+        hipLaunchKernelGGL((gemm_f64_kernel<TILE, TRANS_B, LOWER, true>), grid, dim3(256), pad, s, M, N, K, alpha,
+                           A, lda, B, ldb, beta, C, ldc, tiles_m, tiles_n, n_tiles, per_xcd, tri);
     else
-        hipLaunchKernelGGL((gemm_f64_kernel<TILE, TRANS_B, LOWER, false>), grid, dim3(256), 0, s, M, N, K, alpha, A,
-                           lda, B, ldb, beta, C, ldc, tiles_m, tiles_n, n_tiles, per_xcd, tri);
+        hipLaunchKernelGGL((gemm_f64_kernel<TILE, TRANS_B, LOWER, false>), grid, dim3(256), pad, s, M, N, K, alpha,
+                           A, lda, B, ldb, beta, C, ldc, tiles_m, tiles_n, n_tiles, per_xcd, tri);
 }
 
 template <bool TRANS_B, bool LOWER>
 void launch_sel(hipStream_t s, bool vec, int64_t M, int64_t N, int64_t K, double alpha, const double* A, int64_t lda,
-                const double* B, int64_t ldb, double beta, double* C, int64_t ldc, int tri) {
+                const double* B, int64_t ldb, double beta, double* C, int64_t ldc, int tri, bool one_per_cu) {
     // 128x128 tiles when there are enough of them to fill the chip twice,
     // else 64x64 tiles (4x the workgroups)
     const int64_t tm = ceil_div(M, 128), tn = ceil_div(N, 128);
     const int64_t t128 = LOWER ? tm * (tm + 1) / 2 : tm * tn;
     if (t128 >= 512)
-        launch_t<128, TRANS_B, LOWER>(s, vec, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, tri);
+        launch_t<128, TRANS_B, LOWER>(s, vec, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, tri, one_per_cu);
     else
-        launch_t<64, TRANS_B, LOWER>(s, vec, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, tri);
+        launch_t<64, TRANS_B, LOWER>(s, vec, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, tri, one_per_cu);
 }
 
 }  // namespace
 
 gptq_status launch_gemm_f64(hipStream_t s, int64_t M, int64_t N, int64_t K, double alpha,
                             const double* A, int64_t lda, const double* B, int64_t ldb,
-                            bool transB, double beta, double* C, int64_t ldc, bool lower_tiles, GemmTri tri) {
+                            bool transB, double beta, double* C, int64_t ldc, bool lower_tiles, GemmTri tri,
+                            bool one_per_cu) {
     if (M <= 0 || N <= 0) return GPTQ_OK;
     if (lower_tiles && tri != GEMM_TRI_NONE) return GPTQ_ERR_INVALID_ARG;
     if (K <= 0) {
@@ -270,11 +278,15 @@ gptq_status launch_gemm_f64(hipStream_t s, int64_t M, int64_t N, int64_t K, doub
     if (lower_tiles && M != N) return GPTQ_ERR_INVALID_ARG;
     const bool vec = ((uintptr_t)A % 16 == 0) && (lda % 2 == 0) && ((uintptr_t)B % 16 == 0) && (ldb % 2 == 0);
     if (transB) {
-        if (lower_tiles) launch_sel<true, true>(s, vec, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, (int)tri);
-        else launch_sel<true, false>(s, vec, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, (int)tri);
+        if (lower_tiles)
+            launch_sel<true, true>(s, vec, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, (int)tri, one_per_cu);
+        else
+            launch_sel<true, false>(s, vec, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, (int)tri, one_per_cu);
     } else {
-        if (lower_tiles) launch_sel<false, true>(s, vec, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, (int)tri);
-        else launch_sel<false, false>(s, vec, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, (int)tri);
+        if (lower_tiles)
+            launch_sel<false, true>(s, vec, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, (int)tri, one_per_cu);
+        else
+            launch_sel<false, false>(s, vec, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, (int)tri, one_per_cu);
     }
     GPTQ_LAUNCH_CHECK();
     return GPTQ_OK;

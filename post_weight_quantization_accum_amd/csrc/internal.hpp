@@ -20,10 +20,12 @@ enum GemmTri : int { GEMM_TRI_NONE = 0, GEMM_TRI_KEND_ROW = 1, GEMM_TRI_KEND_COL
 // written too).  beta == 0 never reads C.  C may alias an operand only where
 // every tile reads nothing but its own rows (of A) or its own columns (of
 // B): each tile reads all of K before it writes.
+// one_per_cu: at most one workgroup of this launch per CU, which leaves
+// registers and LDS on every CU to kernels of other streams.
 gptq_status launch_gemm_f64(hipStream_t s, int64_t M, int64_t N, int64_t K, double alpha,
                             const double* A, int64_t lda, const double* B, int64_t ldb,
                             bool transB, double beta, double* C, int64_t ldc, bool lower_tiles,
-                            GemmTri tri = GEMM_TRI_NONE);
+                            GemmTri tri = GEMM_TRI_NONE, bool one_per_cu = false);
 
 // Hessian: H (upper) += 2 X^T X.  ws: hessian_workspace_bytes(n_tok, d)
 // bytes (float64 partial column sums of the diagonal, then the transposed

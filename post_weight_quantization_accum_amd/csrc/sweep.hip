@@ -11,14 +11,16 @@
 //   row_loss64 d_out float64, pinv d_in int32, flags
 //
 // sweep_block: eight lanes per row, each holding 16 of the block's (up to)
-// 128 columns of that row in registers; 8 rows per wave (one wave per
-// workgroup, nearly no LDS, so it runs beside the GEMMs of the lazy
-// updates).  Column c is quantized by the lane owning it; its scaled error
-// reaches the other lanes of the row through a masked 8-lane sum (DPP), and
-// every lane then applies w_j -= err * U[c][j] to its 16 columns, so each
-// w_j receives the compensations of the earlier columns one by one, in
-// column order.  The row U[c][block] is read from L2, two columns ahead.
-// A finished column keeps its error in place: the later updates leave it
+// 128 columns of that row in registers; 8 rows per wave, 16 rows per
+// workgroup.  The upper triangle of the block's U (73 KiB with the zero
+// padding of its 16-column panels) is staged in LDS once per workgroup, so
+// the serial column loop reads U rows at LDS latency; one such workgroup
+// fits on a CU beside a float64 GEMM workgroup of another stream.  Column c
+// is quantized by the lane owning it; its scaled error reaches the other
+// lanes of the row through a masked 8-lane sum (DPP), and every lane then
+// applies w_j -= err * U[c][j] to its 16 columns, so each w_j receives the
+// compensations of the earlier columns one by one, in column order.  A
+// finished column keeps its error in place: the later updates leave it
 // unchanged because U is zero below the diagonal.
 //
 // Lazy updates are two-level (mathematically the same as one update per
@@ -34,7 +36,16 @@ namespace {
 constexpr int BMAX = 128;   // largest supported block (columns per lazy update)
 constexpr int LPR = 8;      // lanes per row
 constexpr int CPL = BMAX / LPR;  // columns per lane
-constexpr int ROWS = 64 / LPR;   // rows per workgroup (one wave)
+constexpr int SWAVES = 2;        // waves per workgroup
+constexpr int ROWS = SWAVES * 64 / LPR;   // rows per workgroup
+// U block in LDS, one panel per lane part p (block columns 16p..16p+15):
+// rows 0..16p+15 of the panel (the rows below are zero in U), 16 doubles
+// each; then one zero row for the parts whose panel has ended; then the
+// reciprocal diagonal.
+constexpr int UP_DOUBLES = CPL * CPL * LPR * (LPR + 1) / 2;   // 9216
+constexpr int UZERO = UP_DOUBLES;
+constexpr size_t SWEEP_LDS = (size_t)(UP_DOUBLES + CPL + BMAX) * sizeof(double);   // 73 KiB
+__host__ __device__ constexpr int panel_base(int p) { return CPL * CPL * p * (p + 1) / 2; }
 
 struct SweepWs {
     int* flags;
@@ -191,33 +202,66 @@ __device__ __forceinline__ double row_max8(double x) {
 }
 
 template <int SEG, bool FULL>
-__global__ __launch_bounds__(64) void sweep_block_kernel(double* __restrict__ Wwork, int64_t d_out, int64_t d_in,
+__global__ __launch_bounds__(SWAVES * 64) void sweep_block_kernel(double* __restrict__ Wwork, int64_t d_out, int64_t d_in,
                                                          int64_t i1, int nb, const double* __restrict__ U,
                                                          int64_t g, QParams qp, double* __restrict__ Err,
                                                          int ldE, int errc, uint8_t* __restrict__ codes_s,
                                                          double* __restrict__ scale64, double* __restrict__ zero64,
                                                          float* __restrict__ scales, float* __restrict__ zeros,
                                                          double* __restrict__ loss64) {
-    __shared__ double rinv[BMAX];
-    const int lane = threadIdx.x;
+    extern __shared__ __attribute__((aligned(16))) double sweep_lds[];
+    double* rinv = sweep_lds + UP_DOUBLES + CPL;
+    const int tid = threadIdx.x, lane = tid & 63;
     const int part = lane & (LPR - 1);
-    const int64_t row = (int64_t)blockIdx.x * ROWS + (lane >> 3);
+    const int64_t row = (int64_t)blockIdx.x * ROWS + (tid >> 3);
     const bool live = row < d_out;
     const int64_t i2 = i1 + nb;
     const int cbase = part * CPL;  // first block column of this lane
     const int nbm = nb - 1;
     const double* Ub = U + i1 * d_in + i1;
-    // this lane's part of U row c (columns clamped into the block)
-    auto load_urow = [&](double (&u)[CPL], int c) {
-        const double* p = Ub + (int64_t)(c < nbm ? c : nbm) * d_in;
+
+    // stage the panels (zeros outside the nb x nb block) and 1 / U[c][c]:
+    // every load of a thread issued before the first store
+    constexpr int NSTG = UP_DOUBLES / 2 / (SWAVES * 64);   // 36 double pairs per thread
+    static_assert(NSTG * SWAVES * 64 * 2 == UP_DOUBLES, "staging covers the panels");
+    {
+        double2 v[NSTG];
 #pragma unroll
-        for (int kk = 0; kk < CPL; ++kk) {
-            const int j = cbase + kk;
-            u[kk] = p[FULL ? j : (j < nbm ? j : nbm)];
+        for (int it = 0; it < NSTG; ++it) {
+            const int e = tid + it * SWAVES * 64;
+            int p = 0;
+#pragma unroll
+            for (int q = 1; q < LPR; ++q) p += (2 * e >= panel_base(q)) ? 1 : 0;
+            const int off = 2 * e - panel_base(p);
+            const int r = off / CPL, j = CPL * p + off % CPL;
+            const bool rok = r < nb;
+            const double* src = Ub + (int64_t)(rok ? r : 0) * d_in + j;
+            if (FULL) {
+                v[it].x = rok ? src[0] : 0.0;
+                v[it].y = rok ? src[1] : 0.0;
+            } else {
+                v[it].x = (rok && j < nb) ? src[0] : 0.0;
+                v[it].y = (rok && j + 1 < nb) ? src[1] : 0.0;
+            }
+        }
+#pragma unroll
+        for (int it = 0; it < NSTG; ++it) *(double2*)&sweep_lds[2 * (tid + it * SWAVES * 64)] = v[it];
+    }
+    if (tid < CPL) sweep_lds[UZERO + tid] = 0.0;
+    for (int c = tid; c < nb; c += SWAVES * 64) rinv[c] = 1.0 / Ub[(int64_t)c * d_in + c];
+    __syncthreads();
+    // this lane's part of U row c: its panel row, or the zero row once the
+    // panel has ended (c > 16 part + 15)
+    const double* my_panel = sweep_lds + panel_base(part);
+    auto load_urow = [&](double (&u)[CPL], int c) {
+        const double* p = (c < cbase + CPL) ? my_panel + c * CPL : sweep_lds + UZERO;
+#pragma unroll
+        for (int kk = 0; kk < CPL; kk += 2) {
+            const double2 v = *(const double2*)(p + kk);
+            u[kk] = v.x;
+            u[kk + 1] = v.y;
         }
     };
-
-    for (int c = lane; c < nb; c += 64) rinv[c] = 1.0 / Ub[(int64_t)c * d_in + c];
 
     double w[CPL];
     {
@@ -246,11 +290,10 @@ __global__ __launch_bounds__(64) void sweep_block_kernel(double* __restrict__ Ww
     int64_t next_gi = i1 / g + (rem == 0 ? 0 : 1);  // and its group index
     double loss = 0.0;
 
-    // U rows of the next two columns in flight
+    // U rows of the next two columns in registers
     double ua[CPL], ub[CPL];
     load_urow(ua, 0);
     load_urow(ub, 1);
-    __syncthreads();
 
     for (int P = 0; P < LPR; ++P) {
         if (P * CPL >= nb) break;
@@ -405,6 +448,20 @@ gptq_status sweep_launch(const void* W, gptq_dtype dt, int64_t d_out, int64_t d_
 
     QParams qp{cfg->bits, cfg->sym, (double)((1 << cfg->bits) - 1)};
     const unsigned grid = (unsigned)ceil_div(d_out, ROWS);
+#define SWEEP_ATTR(n, f)                                                                                        \
+    GPTQ_HIP(hipFuncSetAttribute((const void*)sweep_block_kernel<n, f>, hipFuncAttributeMaxDynamicSharedMemorySize, \
+                                 (int)SWEEP_LDS));
+    SWEEP_ATTR(16, true)
+    SWEEP_ATTR(16, false)
+    SWEEP_ATTR(8, true)
+    SWEEP_ATTR(8, false)
+    SWEEP_ATTR(4, true)
+    SWEEP_ATTR(4, false)
+    SWEEP_ATTR(2, true)
+    SWEEP_ATTR(2, false)
+    SWEEP_ATTR(1, true)
+    SWEEP_ATTR(1, false)
+#undef SWEEP_ATTR
     const int64_t S = superblock_cols(d_in, cfg);
     // Groups that span several superblocks read columns past the current
     // superblock at their first column: those must be fully updated first.
@@ -425,7 +482,8 @@ gptq_status sweep_launch(const void* W, gptq_dtype dt, int64_t d_out, int64_t d_
             switch (SEG * 2 + (full ? 1 : 0)) {
 #define SWEEP_CASE(n, f)                                                                                      \
     case n * 2 + f:                                                                                           \
-        hipLaunchKernelGGL((sweep_block_kernel<n, f>), dim3(grid), dim3(64), 0, s, w.Wwork, d_out, d_in, i1, \
+        hipLaunchKernelGGL((sweep_block_kernel<n, f>), dim3(grid), dim3(SWAVES * 64), SWEEP_LDS, s, w.Wwork,     \
+                           d_out, d_in, i1,                                                                 \
                            nb, U, g, qp, Ek, (int)S, (int)(i1 - a), w.codes_s, w.scale64, w.zero64, scales,  \
                            zeros, w.loss64);                                                                  \
         break;
@@ -462,7 +520,7 @@ gptq_status sweep_launch(const void* W, gptq_dtype dt, int64_t d_out, int64_t d_
             GPTQ_HIP(hipEventRecord(side.err_ready, s));
             GPTQ_HIP(hipStreamWaitEvent(side.s, side.err_ready, 0));
             st = launch_gemm_f64(side.s, d_out, d_in - e - n_near, e - a, -1.0, Ek, S, U + a * d_in + e + n_near,
-                                 d_in, false, 1.0, w.Wwork + e + n_near, d_in, false);
+                                 d_in, false, 1.0, w.Wwork + e + n_near, d_in, false, GEMM_TRI_NONE, true);
             if (st != GPTQ_OK) return st;
             GPTQ_HIP(hipEventRecord(side.far_done, side.s));
             far_pending = true;

@@ -220,8 +220,17 @@ __device__ __forceinline__ double readlane_f64(double v, int lane) {
     return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 }
 
-// 1/sqrt(p) for a positive normal p: hardware estimate and two Newton steps
-// (each squares the relative error), good to about one ulp.
+// Value of v in lane src (ds_bpermute, no LDS memory involved).
+__device__ __forceinline__ double bperm_f64(double v, int src) {
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    const int a = src << 2;
+    const int lo = __builtin_amdgcn_ds_bpermute(a, (int)(uint32_t)b);
+    const int hi = __builtin_amdgcn_ds_bpermute(a, (int)(uint32_t)(b >> 32));
+    return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+
+// 1/sqrt(p) and 1/p for a positive normal p: hardware estimate and two
+// Newton steps (each squares the relative error), good to about one ulp.
 __device__ __forceinline__ double rsqrt_nr(double p) {
     double y = __builtin_amdgcn_rsq(p);
     const double h = 0.5 * p;
@@ -230,222 +239,242 @@ __device__ __forceinline__ double rsqrt_nr(double p) {
     e = fma(-h * y, y, 0.5);
     return fma(y, e, y);
 }
+__device__ __forceinline__ double rcp_nr(double p) {
+    double y = __builtin_amdgcn_rcp(p);
+    double e = fma(-p, y, 1.0);
+    y = fma(y, e, y);
+    e = fma(-p, y, 1.0);
+    return fma(y, e, y);
+}
 
 // Leaf of the recursion: the n x n (n <= 128) diagonal block of Hr at
 // offset o is factored, A = L L^T, and M = L^{-1} is written to the same
 // block of Mi (lower, zeros above the diagonal; the padding up to 128 acts
 // as an identity block), with the 128x128 block in LDS and 16x16 inner
-// blocks.  L is formed in place (lower triangle); M is formed along
-// by forward elimination: R starts as the identity, and at block step k
-// block row k of M is Dinv_k R_k (Dinv_k the inverse of the diagonal
-// factor) while the rows below lose L[r][k-block] M_k.  The off-diagonal
-// blocks of R / M live transposed in the free upper triangle of the LDS
-// block; M's diagonal blocks are the Dinv_k.
+// blocks.  L is formed in place (lower triangle); M is formed along by
+// forward elimination: R starts as the identity, and at block step k block
+// row k of M is Dinv_k R_k (Dinv_k the inverse of the diagonal factor)
+// while the rows below lose L[r][k-block] M_k.  The off-diagonal blocks of
+// R / M live transposed in the free upper triangle of the LDS block; M's
+// diagonal blocks are the Dinv_k.
 //   setup: wave 0 factors diagonal block 0;
-//   block step k: (A) rows below get L[r][k-block] = A[r][k-block] Dinv_k^T,
-//                     and block row k of M = Dinv_k R_k;
+//   block step k: (A) seven 16x16 tiles, one per wave: the row tiles of L
+//                     below block k (L = A Dinv_k^T) and the column tiles
+//                     of block row k of M (Dinv_k R_k);
 //                 (B) wave 0 updates diagonal block k+1 and factors it while
 //                     the other waves update the rest of the trailing lower
 //                     part and the rows of R below block k.
-// The 16x16 factor: one wave, lane = (row r, 4 columns), column j of L and
-// row j of its inverse exchanged through LDS inside the wave.
+// Every 16x16 product runs on the float64 matrix cores (four
+// v_mfma_f64_16x16x4 for K = 16); the row stride of 130 doubles makes the
+// operand fetches (16 rows x 2 k per 32 lanes) hit distinct LDS banks.
+// The 16x16 diagonal factor is split into 8x8 halves with one element per
+// lane (see diag8).
 constexpr int LB = 16;               // inner block edge
 constexpr int NIB = LEAF / LB;       // inner blocks per edge
-constexpr int LDA = LEAF + 1;        // LDS row stride (doubles)
-constexpr size_t LEAF_LDS = (size_t)(LEAF * LDA + NIB * LB * LB + 2 * LB) * sizeof(double);
+constexpr int LDA = LEAF + 2;        // LDS row stride (doubles)
+constexpr int DLD = LB + 1;          // row stride of the stored diagonal inverses
+constexpr int DSZ = LB * DLD;
+constexpr int SC8 = 8 * 9;           // one 8x8 scratch matrix, row stride 9
+constexpr size_t LEAF_LDS = (size_t)(LEAF * LDA + NIB * DSZ + 4 * SC8) * sizeof(double);
 
-// Factor the 16x16 diagonal block at (k0, k0) of As in place (lower) and
-// write the inverse of the factor to dinv (16x16, zeros above).  Wave 0.
-__device__ __forceinline__ void diag16(double* As, int k0, double* dinv, double* colb, double* rowb, int lane,
-                                       bool& bad_pd, bool& bad_nan) {
-    // A wave executes its LDS operations in order; compiler memory barriers
-    // between the stores and the loads of a step (and before the next
-    // step's stores) keep the compiler from reusing earlier loaded values.
-    const int r = lane >> 2, cg = lane & 3;
-    double a[4], x[4];
+__device__ __forceinline__ d4_t mfma4(double a, double b, d4_t c) { return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0); }
+
+// 16x16 tile of a product with K = 16 on the matrix cores: element (i, k) of
+// the left operand at pa[i * sa_r + k * sa_k], element (k, j) of the right
+// operand at pb[j * sb_c + k * sb_k]; acc[r] = C[4r + lane/16][lane%16].
+__device__ __forceinline__ d4_t tile16(const double* pa, int sa_r, int sa_k, const double* pb, int sb_c, int sb_k,
+                                       int lane) {
+    const int r = lane & 15, kq = lane >> 4;
+    double av[4], bv[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int c = 4 * cg + q;
-        const double v = As[(k0 + r) * LDA + k0 + c];
-        a[q] = (c <= r) ? v : 0.0;
-        x[q] = (c == r) ? 1.0 : 0.0;
+    for (int s = 0; s < 4; ++s) {
+        av[s] = pa[r * sa_r + (4 * s + kq) * sa_k];
+        bv[s] = pb[r * sb_c + (4 * s + kq) * sb_k];
     }
+    d4_t acc = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-    for (int j = 0; j < LB; ++j) {
-        double piv = readlane_f64(a[j & 3], 4 * j + (j >> 2));
+    for (int s = 0; s < 4; ++s) acc = mfma4(av[s], bv[s], acc);
+    return acc;
+}
+
+// 8x8 factor in one wave, lane = 8i + j holding the symmetric A[i][j]:
+// a = L[i][j] on return (meaningful for j <= i), x = L^{-1}[i][j] (zero for
+// j > i).  Step J eliminates with the unscaled column, a[i][j] -=
+// a[i][J] a[J][j] / p_J (the same update as with the scaled column of L),
+// and x[i] -= (a[i][J] / p_J) x[J]; the scale 1/sqrt(p_J) of column J of L
+// and of row J of the inverse is applied at the end.  Row J and column J
+// arrive through ds_bpermute, the pivot through readlane.
+__device__ __forceinline__ void diag8(double& a, double& x, int lane, bool& bad_pd, bool& bad_nan) {
+    const int i = lane >> 3, j = lane & 7;
+    x = (i == j) ? 1.0 : 0.0;
+    double pvi = 1.0, pvj = 1.0;   // pivots of this lane's row and column
+#pragma unroll
+    for (int J = 0; J < 8; ++J) {
+        const double colr = bperm_f64(a, (lane & ~7) + J);   // a[i][J]
+        const double colc = bperm_f64(a, 8 * J + j);         // a[J][j]
+        const double xrow = bperm_f64(x, 8 * J + j);         // x[J][j]
+        double piv = readlane_f64(a, 9 * J);
         if (!(piv > 0.0)) {
             bad_nan |= isnan(piv);
             bad_pd |= !isnan(piv);
             piv = 1.0;
         }
-        const double rs = rsqrt_nr(piv);
-        const bool owner = cg == (j >> 2);
-        const double lv = (r > j) ? a[j & 3] * rs : ((r == j) ? piv * rs : 0.0);
-        a[j & 3] = owner ? lv : a[j & 3];
-        if (owner) colb[r] = lv;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) x[q] = (r == j) ? x[q] * rs : x[q];
-        if (r == j) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) rowb[4 * cg + q] = x[q];
-        }
-        asm volatile("" ::: "memory");
-        const double lr = colb[r];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int c = 4 * cg + q;
-            const double lcv = colb[c];
-            const double xsv = rowb[c];
-            a[q] = fma(-lr, (c > j) ? lcv : 0.0, a[q]);
-            x[q] = fma(-lr, (r > j) ? xsv : 0.0, x[q]);
-        }
-        asm volatile("" ::: "memory");
+        const double cr = (i > J) ? colr * rcp_nr(piv) : 0.0;
+        a = fma(-cr, (j > J) ? colc : 0.0, a);
+        x = fma(-cr, xrow, x);
+        pvi = (i == J) ? piv : pvi;
+        pvj = (j == J) ? piv : pvj;
     }
+    a *= rsqrt_nr(pvj);
+    x *= rsqrt_nr(pvi);
+}
+
+// Factor the 16x16 diagonal block at (b0, b0) of As in place (lower) and
+// write the inverse of the factor to D (row stride DLD, zeros above the
+// diagonal).  Wave 0.  With A = [A11 .; A21 A22]: L11, X11 = L11^{-1};
+// L21 = A21 X11^T; L22, X22 from A22 - L21 L21^T; X21 = -X22 (L21 X11).
+// The 8x8 intermediates go through LDS scratch; a wave executes its LDS
+// operations in order, and compiler memory barriers keep the compiler from
+// reusing values loaded before a store.
+__device__ __forceinline__ void diag16(double* As, int b0, double* D, double* sc, int lane, bool& bad_pd,
+                                       bool& bad_nan) {
+    const int i = lane >> 3, j = lane & 7;
+    double* SX11 = sc;
+    double* SL21 = sc + SC8;
+    double* ST = sc + 2 * SC8;
+    double* SX22 = sc + 3 * SC8;
+    double a11 = (j <= i) ? As[(b0 + i) * LDA + b0 + j] : As[(b0 + j) * LDA + b0 + i];
+    double a22 = (j <= i) ? As[(b0 + 8 + i) * LDA + b0 + 8 + j] : As[(b0 + 8 + j) * LDA + b0 + 8 + i];
+    double a21[8];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int c = 4 * cg + q;
-        if (c <= r) As[(k0 + r) * LDA + k0 + c] = a[q];
-        dinv[r * LB + c] = x[q];
+    for (int k = 0; k < 8; ++k) a21[k] = As[(b0 + 8 + i) * LDA + b0 + k];
+    double x11;
+    diag8(a11, x11, lane, bad_pd, bad_nan);
+    SX11[i * 9 + j] = x11;
+    asm volatile("" ::: "memory");
+    double l21 = 0.0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) l21 = fma(a21[k], SX11[j * 9 + k], l21);
+    SL21[i * 9 + j] = l21;
+    asm volatile("" ::: "memory");
+    double s22 = 0.0, tt = 0.0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const double li = SL21[i * 9 + k];
+        s22 = fma(li, SL21[j * 9 + k], s22);
+        tt = fma(li, SX11[k * 9 + j], tt);
     }
+    a22 -= s22;
+    ST[i * 9 + j] = tt;
+    double x22;
+    diag8(a22, x22, lane, bad_pd, bad_nan);
+    SX22[i * 9 + j] = x22;
+    asm volatile("" ::: "memory");
+    double x21 = 0.0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) x21 = fma(SX22[i * 9 + k], ST[k * 9 + j], x21);
+    if (j <= i) {
+        As[(b0 + i) * LDA + b0 + j] = a11;
+        As[(b0 + 8 + i) * LDA + b0 + 8 + j] = a22;
+    }
+    As[(b0 + 8 + i) * LDA + b0 + j] = l21;
+    D[i * DLD + j] = x11;
+    D[i * DLD + 8 + j] = 0.0;
+    D[(8 + i) * DLD + j] = -x21;
+    D[(8 + i) * DLD + 8 + j] = x22;
+    asm volatile("" ::: "memory");
 }
 
 __global__ __launch_bounds__(512) void leaf_blocked_kernel(const double* __restrict__ A, double* Mi, int64_t d,
                                                            int64_t o, int n, int* flags) {
     extern __shared__ double sm[];
-    double* As = sm;                        // [LEAF][LDA]: L (lower); R / M transposed (upper)
-    double* Dv = sm + LEAF * LDA;           // [NIB][LB][LB]: inverses of the diagonal factors
-    double* colb = Dv + NIB * LB * LB;      // [LB] column exchange of the 16x16 factor
-    double* rowb = colb + LB;               // [LB] row exchange of its inverse
+    double* As = sm;                 // [LEAF][LDA]: L (lower); R / M transposed (upper, off-diagonal blocks)
+    double* Dv = sm + LEAF * LDA;    // [NIB][LB][DLD]: inverses of the diagonal factors
+    double* sc = Dv + NIB * DSZ;     // 8x8 scratch of the diagonal factor
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    constexpr int PER = LEAF * LEAF / 512;   // elements per thread when the block moves
 
-    // Hr block (lower; identity padding); R = I: zeros above the diagonal
-    for (int e = t; e < LEAF * LEAF; e += 512) {
-        const int r = e >> 7, c = e & (LEAF - 1);
-        double v = 0.0;
-        if (c <= r) {
-            if (r < n && c < n) v = A[(o + r) * d + o + c];
-            else v = (r == c) ? 1.0 : 0.0;
+    // Hr block (lower; identity padding), zeros above the diagonal; all
+    // loads of a thread issued before its stores
+    {
+        double v[PER];
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            const int e = t + 512 * q;
+            const int r = e >> 7, c = e & (LEAF - 1);
+            const bool in = c <= r && r < n && c < n;
+            const double x = A[(o + (in ? r : 0)) * d + o + (in ? c : 0)];
+            v[q] = in ? x : ((c == r) ? 1.0 : 0.0);
         }
-        As[r * LDA + c] = v;
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            const int e = t + 512 * q;
+            As[(e >> 7) * LDA + (e & (LEAF - 1))] = v[q];
+        }
     }
     __syncthreads();
     bool bad_pd = false, bad_nan = false;
-    if (wave == 0) diag16(As, 0, Dv, colb, rowb, lane, bad_pd, bad_nan);
+    if (wave == 0) diag16(As, 0, Dv, sc, lane, bad_pd, bad_nan);
     __syncthreads();
 
     for (int kb = 0; kb < NIB; ++kb) {
         const int k0 = kb * LB;
-        const int rows = LEAF - k0 - LB;   // rows below the block
-        const double* dk = Dv + kb * LB * LB;
-        // (A) panel of L: one thread per row below; block row kb of M:
-        //     M[k0+r][c] = sum_{q<=r} Dinv_k[r][q] R[k0+q][c], one thread per column c < k0
-        if (t < rows) {
-            const int r = k0 + LB + t;
-            double a[LB];
+        const double* dk = Dv + kb * DSZ;
+        // (A) wave w < 7: row tile w of L below block kb, or column tile of
+        //     block row kb of M (M[k0+r][c] = sum_q Dinv_k[r][q] R[k0+q][c],
+        //     R[k0+q][c] stored at As[c][k0+q])
+        if (wave < NIB - 1) {
+            const int nbelow = NIB - 1 - kb;
+            if (wave < nbelow) {
+                const int r0 = k0 + LB + LB * wave;
+                const d4_t acc = tile16(As + r0 * LDA + k0, LDA, 1, dk, DLD, 1, lane);
 #pragma unroll
-            for (int k = 0; k < LB; ++k) a[k] = As[r * LDA + k0 + k];
+                for (int r = 0; r < 4; ++r) As[(r0 + 4 * r + (lane >> 4)) * LDA + k0 + (lane & 15)] = acc[r];
+            } else {
+                const int c0 = LB * (wave - nbelow);
+                const d4_t acc = tile16(dk, DLD, 1, As + c0 * LDA + k0, LDA, 1, lane);
 #pragma unroll
-            for (int c = 0; c < LB; ++c) {
-                double s = 0.0;
-#pragma unroll
-                for (int k = 0; k <= c; ++k) s = fma(a[k], dk[c * LB + k], s);
-                As[r * LDA + k0 + c] = s;
-            }
-        } else if (t >= 128 && t - 128 < k0) {
-            const int c = t - 128;   // R[k0+q][c] stored at As[c][k0+q]
-            double rv[LB];
-#pragma unroll
-            for (int q = 0; q < LB; ++q) rv[q] = As[c * LDA + k0 + q];
-#pragma unroll
-            for (int rr = 0; rr < LB; ++rr) {
-                double s = 0.0;
-#pragma unroll
-                for (int q = 0; q <= rr; ++q) s = fma(dk[rr * LB + q], rv[q], s);
-                As[c * LDA + k0 + rr] = s;
+                for (int r = 0; r < 4; ++r) As[(c0 + (lane & 15)) * LDA + k0 + 4 * r + (lane >> 4)] = acc[r];
             }
         }
         __syncthreads();
-        if (rows == 0) break;
+        if (kb == NIB - 1) break;
         // (B)
+        const int b0 = k0 + LB;
         if (wave == 0) {
             // diagonal block kb+1 loses L[.][k-block] L[.][k-block]^T, then is factored
-            const int b0 = k0 + LB;
-            for (int e = lane; e < LB * LB; e += 64) {
-                const int r = e >> 4, c = e & (LB - 1);
-                if (c > r) continue;
-                double s = 0.0;
+            const d4_t acc = tile16(As + b0 * LDA + k0, LDA, 1, As + b0 * LDA + k0, LDA, 1, lane);
 #pragma unroll
-                for (int k = 0; k < LB; ++k) s = fma(As[(b0 + r) * LDA + k0 + k], As[(b0 + c) * LDA + k0 + k], s);
-                As[(b0 + r) * LDA + b0 + c] -= s;
-            }
+            for (int r = 0; r < 4; ++r) As[(b0 + 4 * r + (lane >> 4)) * LDA + b0 + (lane & 15)] -= acc[r];
             asm volatile("" ::: "memory");
-            diag16(As, b0, Dv + (kb + 1) * LB * LB, colb, rowb, lane, bad_pd, bad_nan);
+            diag16(As, b0, Dv + (kb + 1) * DSZ, sc, lane, bad_pd, bad_nan);
         } else {
-            const int tt = t - 64;   // 448 threads
-            // trailing lower part below/right of block kb+1's diagonal block:
-            // rows and columns >= k0+16, 4x4 tiles, except the 10 tiles of the
-            // diagonal block kb+1 (handled by wave 0)
-            const int T4 = rows / 4;
-            const int ntl = T4 * (T4 + 1) / 2;
-            // rows of R below block kb: R[r][c] -= sum_q L[r][k0+q] M[k0+q][c], c < k0+16,
-            // R[r][c] at As[c][r]; M[k0+q][c] = Dinv_k[q][c-k0] for c >= k0, else As[c][k0+q]
-            const int C4 = (k0 + LB) / 4;
-            const int nx = T4 * C4;
-            for (int w = tt; w < ntl + nx; w += 448) {
-                if (w < ntl) {
+            // waves 1..7: tiles (ti, tj) of the trailing lower part below
+            // block kb (ti >= tj, except the diagonal tile of block kb+1),
+            // then tiles of R below block kb: R[r][c] -= sum_q L[r][k0+q]
+            // M[k0+q][c] for c < k0+16 (M = Dinv_k inside block kb)
+            const int T = NIB - 1 - kb;
+            const int ntr = T * (T + 1) / 2 - 1;
+            const int nr = T * (kb + 1);
+            for (int w = wave - 1; w < ntr + nr; w += NIB - 1) {
+                if (w < ntr) {
+                    const int x = w + 1;
                     int ti = 0;
-                    while ((ti + 1) * (ti + 2) / 2 <= w) ++ti;
-                    const int tj = w - ti * (ti + 1) / 2;
-                    if (ti < 4) continue;  // the diagonal block kb+1 (tiles 0..9)
-                    const int r0 = k0 + LB + 4 * ti, c0 = k0 + LB + 4 * tj;
-                    double acc[4][4];
+                    while ((ti + 1) * (ti + 2) / 2 <= x) ++ti;
+                    const int tj = x - ti * (ti + 1) / 2;
+                    const int i0 = b0 + LB * ti, j0 = b0 + LB * tj;
+                    const d4_t acc = tile16(As + i0 * LDA + k0, LDA, 1, As + j0 * LDA + k0, LDA, 1, lane);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
-#pragma unroll 4
-                    for (int k = 0; k < LB; ++k) {
-                        double lr[4], lc[4];
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            lr[i] = As[(r0 + i) * LDA + k0 + k];
-                            lc[i] = As[(c0 + i) * LDA + k0 + k];
-                        }
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-#pragma unroll
-                            for (int j = 0; j < 4; ++j) acc[i][j] = fma(lr[i], lc[j], acc[i][j]);
-                    }
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) As[(r0 + i) * LDA + c0 + j] -= acc[i][j];
+                    for (int r = 0; r < 4; ++r) As[(i0 + 4 * r + (lane >> 4)) * LDA + j0 + (lane & 15)] -= acc[r];
                 } else {
-                    const int x = w - ntl;
-                    const int r0 = k0 + LB + 4 * (x / C4), c0 = 4 * (x % C4);
-                    const bool diagc = c0 >= k0;   // columns inside block kb: M = Dinv_k
-                    double acc[4][4];
+                    const int x = w - ntr;
+                    const int ti = x / (kb + 1), tc = x % (kb + 1);
+                    const int r0 = b0 + LB * ti, c0 = LB * tc;
+                    d4_t acc;
+                    if (tc == kb) acc = tile16(As + r0 * LDA + k0, LDA, 1, dk, 1, DLD, lane);
+                    else acc = tile16(As + r0 * LDA + k0, LDA, 1, As + c0 * LDA + k0, LDA, 1, lane);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
-#pragma unroll 4
-                    for (int q = 0; q < LB; ++q) {
-                        double lr[4], mq[4];
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) lr[i] = As[(r0 + i) * LDA + k0 + q];
-#pragma unroll
-                        for (int j = 0; j < 4; ++j)
-                            mq[j] = diagc ? dk[q * LB + (c0 - k0) + j] : As[(c0 + j) * LDA + k0 + q];
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-#pragma unroll
-                            for (int j = 0; j < 4; ++j) acc[i][j] = fma(lr[i], mq[j], acc[i][j]);
-                    }
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) As[(c0 + j) * LDA + r0 + i] -= acc[i][j];
+                    for (int r = 0; r < 4; ++r) As[(c0 + (lane & 15)) * LDA + r0 + 4 * r + (lane >> 4)] -= acc[r];
                 }
             }
         }
@@ -455,13 +484,23 @@ __global__ __launch_bounds__(512) void leaf_blocked_kernel(const double* __restr
     if (bad_pd) raise_flag(flags, FLAG_NOT_PD);
 
     // write M (lower, zeros above the diagonal) for the n x n part
-    for (int e = t; e < LEAF * LEAF; e += 512) {
-        const int r = e >> 7, c = e & (LEAF - 1);
-        if (r >= n || c >= n) continue;
-        double v = 0.0;
-        if (r / LB == c / LB) v = Dv[((r / LB) * LB + (r % LB)) * LB + (c % LB)];
-        else if (r > c) v = As[c * LDA + r];
-        Mi[(o + r) * d + o + c] = v;
+    {
+        double v[PER];
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            const int e = t + 512 * q;
+            const int r = e >> 7, c = e & (LEAF - 1);
+            double x = 0.0;
+            if (r / LB == c / LB) x = Dv[(r / LB) * DSZ + (r % LB) * DLD + (c % LB)];
+            else if (r > c) x = As[c * LDA + r];
+            v[q] = x;
+        }
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            const int e = t + 512 * q;
+            const int r = e >> 7, c = e & (LEAF - 1);
+            if (r < n && c < n) Mi[(o + r) * d + o + c] = v[q];
+        }
     }
 }
 

@@ -213,6 +213,29 @@ __global__ __launch_bounds__(256) void gather_reverse_kernel(const double* __res
     }
 }
 
+// The same gather with the source row staged in LDS (d doubles, up to
+// GATHER_LDS_MAX): row p[d-1-a] is read in order, then row a of Hr is
+// written in order, b = 0..a, each value picked from LDS at p[d-1-b].
+constexpr int64_t GATHER_LDS_MAX = 19456;   // 152 KiB of LDS
+__global__ __launch_bounds__(512) void gather_rows_lds_kernel(const double* __restrict__ H, int64_t d,
+                                                              const int32_t* __restrict__ perm,
+                                                              const double* __restrict__ lambda, double* Hr) {
+    extern __shared__ double srow[];
+    const int64_t a = blockIdx.x;
+    const double* row = H + (int64_t)perm[d - 1 - a] * d;
+#pragma unroll 8
+    for (int64_t c = threadIdx.x; c < d; c += 512) srow[c] = row[c];
+    __syncthreads();
+    const double lam = *lambda;
+    double* out = Hr + a * d;
+#pragma unroll 4
+    for (int64_t b = threadIdx.x; b <= a; b += 512) {
+        double v = srow[perm[d - 1 - b]];
+        if (b == a) v += lam;
+        out[b] = v;
+    }
+}
+
 __device__ __forceinline__ double readlane_f64(double v, int lane) {
     const uint64_t b = __builtin_bit_cast(uint64_t, v);
     const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, lane);
@@ -615,8 +638,15 @@ gptq_status hinv_launch(double* H, int64_t d, const gptq_config* cfg, int32_t* p
     const int64_t T32 = ceil_div(d, 32);
     hipLaunchKernelGGL(symmetrize_kernel, dim3((unsigned)(T32 * (T32 + 1) / 2)), dim3(256), 0, s, H, d, w.flags);
     GPTQ_LAUNCH_CHECK();
-    hipLaunchKernelGGL(gather_reverse_kernel, dim3((unsigned)d), dim3(256), 0, s, H, d, perm, w.pinv, w.lambda,
-                       w.L);
+    if (d <= GATHER_LDS_MAX) {
+        const size_t lds = (size_t)d * sizeof(double);
+        GPTQ_HIP(hipFuncSetAttribute((const void*)gather_rows_lds_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)lds));
+        hipLaunchKernelGGL(gather_rows_lds_kernel, dim3((unsigned)d), dim3(512), lds, s, H, d, perm, w.lambda, w.L);
+    } else {
+        hipLaunchKernelGGL(gather_reverse_kernel, dim3((unsigned)d), dim3(256), 0, s, H, d, perm, w.pinv, w.lambda,
+                           w.L);
+    }
     GPTQ_LAUNCH_CHECK();
 
     // H's buffer now receives M = L^{-1} (lower), then U = J M J in place.

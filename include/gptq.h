@@ -89,8 +89,10 @@ void gptq_config_default(gptq_config* cfg);
  * float64 throughout.  Deterministic (bit-reproducible).
  * NaN/Inf in X propagate into diag(H) and are reported by gptq_prepare_hinv.
  * workspace: gptq_hessian_workspace(n_tok, d_in) bytes (a transposed copy of
- * one token chunk and float64 column sums; may be NULL for fp32 inputs or
- * n_tok = 0).  Calls on one workspace must not overlap.
+ * one token chunk and float64 column sums; two such slots when n_tok spans
+ * more than one chunk, the next chunk being transposed while the current
+ * one is multiplied; may be NULL for fp32 inputs or n_tok = 0).  Calls on
+ * one workspace must not overlap.
  * ------------------------------------------------------------------------ */
 size_t gptq_hessian_workspace(int64_t n_tok, int64_t d_in);
 gptq_status gptq_hessian_accumulate(double* H, const void* X, gptq_dtype x_dtype,

@@ -120,20 +120,25 @@ constexpr int TSPAN = 512;      // tokens per transpose block
 constexpr int TT = 64;          // tokens per tile
 constexpr int TLD = TT + 8;     // LDS row stride (16-bit elements)
 
+constexpr size_t TILE_BYTES = 256 * TLD * sizeof(uint16_t);
+constexpr size_t TRANSPOSE_LDS = TILE_BYTES + 8 * 256 * sizeof(double);
+
+// One transpose block (token block bx, feature block by) by 256 threads
+// (t = 0..255) with LDS tile / red; barriers are those of the whole
+// workgroup, so every thread of it calls this with the same bx.  active =
+// false: the threads take part in the barriers only.
 template <typename Tag, bool VEC>
-__global__ __launch_bounds__(256) void transpose_kernel(const uint16_t* __restrict__ X, int64_t n_tok, int64_t d,
-                                                        int64_t ld, uint16_t* __restrict__ Xt, int64_t ch,
-                                                        int64_t d_pad, double* __restrict__ colsq) {
+__device__ __forceinline__ void transpose_block(const uint16_t* __restrict__ X, int64_t n_tok, int64_t d, int64_t ld,
+                                                uint16_t* __restrict__ Xt, int64_t ch, int64_t d_pad,
+                                                double* __restrict__ colsq, int64_t bx, int64_t by, bool active, int t,
+                                                uint16_t* tile, double (*red)[256]) {
     static_assert(TT == KT, "a transpose tile is one stage");
-    __shared__ __attribute__((aligned(16))) uint16_t tile[256 * TLD];
-    __shared__ double red[8][256];
-    const int t = threadIdx.x;
     const int tg = t >> 5, fg = t & 31;
-    const int64_t fblk = (int64_t)blockIdx.y * 256;
+    const int64_t fblk = by * 256;
     const int64_t f = fblk + fg * 8;
     double sq[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     for (int tt = 0; tt < TSPAN / TT; ++tt) {
-        const int64_t tbase = (int64_t)blockIdx.x * TSPAN + tt * TT;
+        const int64_t tbase = bx * TSPAN + tt * TT;
         if (tbase >= ch) break;
         const int64_t t0 = tbase + tg * 8;
         u32x4_t v[8];
@@ -141,7 +146,7 @@ __global__ __launch_bounds__(256) void transpose_kernel(const uint16_t* __restri
         for (int r = 0; r < 8; ++r) {
             const int64_t tok = t0 + r;
             u32x4_t x = {0u, 0u, 0u, 0u};
-            if (tok < n_tok) {
+            if (active && tok < n_tok) {
                 const uint16_t* p = X + tok * ld + f;
                 if (VEC) {
                     if (f < d) x = *(const u32x4_t*)p;
@@ -185,7 +190,7 @@ __global__ __launch_bounds__(256) void transpose_kernel(const uint16_t* __restri
             const int e = k * 256 + t;
             const int fr = e >> 3, gq = e & 7;
             const int64_t tok = tbase + gq * 8;
-            if (tok < ch)
+            if (active && tok < ch)
                 *(u32x4_t*)&Xt[((tbase / KT) * d_pad + fblk + fr) * KT + gq * 8] =
                     *(const u32x4_t*)&tile[fr * TLD + gq * 8];
         }
@@ -195,12 +200,21 @@ __global__ __launch_bounds__(256) void transpose_kernel(const uint16_t* __restri
     for (int c = 0; c < 8; ++c) red[tg][fg * 8 + c] = sq[c];
     __syncthreads();
     const int64_t fc = fblk + t;
-    if (fc < d) {
+    if (active && fc < d) {
         double sum = 0.0;
 #pragma unroll
         for (int g = 0; g < 8; ++g) sum += red[g][t];
-        colsq[(int64_t)blockIdx.x * d + fc] = sum;
+        colsq[bx * d + fc] = sum;
     }
+}
+
+template <typename Tag, bool VEC>
+__global__ __launch_bounds__(256) void transpose_kernel(const uint16_t* __restrict__ X, int64_t n_tok, int64_t d,
+                                                        int64_t ld, uint16_t* __restrict__ Xt, int64_t ch,
+                                                        int64_t d_pad, double* __restrict__ colsq) {
+    __shared__ __attribute__((aligned(16))) char tl[TRANSPOSE_LDS];
+    transpose_block<Tag, VEC>(X, n_tok, d, ld, Xt, ch, d_pad, colsq, blockIdx.x, blockIdx.y, true, threadIdx.x,
+                              (uint16_t*)tl, (double(*)[256])(tl + TILE_BYTES));
 }
 
 // diag(H) += 2 * sum of the chunk's per-block column sums, blocks in order.
@@ -366,15 +380,36 @@ __device__ __forceinline__ void syrk_tile(double* __restrict__ H, const uint16_t
     }
 }
 
-template <typename Tag, int NW>
+// The next chunk, transposed by the workgroups past the tiles of a launch.
+struct NextChunk {
+    const uint16_t* X;   // its first token row
+    int64_t n_tok, ld, ch;
+    uint16_t* Xt;
+    double* colsq;
+};
+
+template <typename Tag, int NW, bool VEC>
 __global__ __launch_bounds__(NW * 64) void hess_syrk_kernel(double* __restrict__ H, const uint16_t* __restrict__ Xt,
                                                             int64_t ch, int64_t d_pad, int64_t d, int64_t T,
-                                                            int64_t n_tiles,
-                                                            int64_t per_xcd) {
+                                                            int64_t n_tiles, int64_t per_xcd, NextChunk nx) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
+    const int64_t b = blockIdx.x;
+    if (b >= per_xcd * 8) {
+        // Past the tiles: the next chunk's transpose, two 256-feature blocks
+        // of one token block per workgroup.  These workgroups are dispatched
+        // last and fill the CUs that the last round of tiles leaves idle.
+        static_assert(NW * 64 == 512, "two transpose halves of 256 threads");
+        const int64_t nby = d_pad / 256, npair = (nby + 1) / 2;
+        const int64_t q = b - per_xcd * 8;
+        const int half = (int)(threadIdx.x >> 8);
+        const int64_t by = 2 * (q % npair) + half;
+        char* h = lds + half * (RING_BYTES / 2);
+        transpose_block<Tag, VEC>(nx.X, nx.n_tok, d, nx.ld, nx.Xt, nx.ch, d_pad, nx.colsq, q / npair, by, by < nby,
+                                  (int)(threadIdx.x & 255), (uint16_t*)h, (double(*)[256])(h + TILE_BYTES));
+        return;
+    }
     // XCD-grouped tile order: workgroup b runs on XCD b % 8; each XCD takes a
     // contiguous range of the banded upper-triangle enumeration.
-    const int64_t b = blockIdx.x;
     const int64_t lin = (b % 8) * per_xcd + b / 8;
     if (lin >= n_tiles) return;
     int64_t ti, tj;
@@ -455,12 +490,20 @@ size_t part_bytes(int64_t d) { return align_up((size_t)(CHUNK / TSPAN) * d * siz
 
 }  // namespace
 
-size_t hessian_workspace_bytes(int64_t n_tok, int64_t d) {
+namespace {
+// One chunk's slot of the workspace: column sums, then the transposed chunk.
+size_t slot_bytes(int64_t n_tok, int64_t d) {
     const int64_t d_pad = align_up((size_t)d, BT);
     int64_t ch = align_up((size_t)(n_tok > 0 ? n_tok : 1), KT);
     const int64_t cmax = chunk_tokens(d);
     if (ch > cmax) ch = cmax;
     return part_bytes(d) + (size_t)d_pad * ch * sizeof(uint16_t);
+}
+}  // namespace
+
+size_t hessian_workspace_bytes(int64_t n_tok, int64_t d) {
+    const int nslots = (n_tok > chunk_tokens(d)) ? 2 : 1;
+    return nslots * slot_bytes(n_tok, d);
 }
 
 int64_t hessian_syrk_launches(int64_t n_tok, gptq_dtype dt, int64_t d) {
@@ -480,48 +523,74 @@ gptq_status hessian_launch(double* H, const void* X, gptq_dtype dt, int64_t n_to
         if (ev) GPTQ_HIP(hipEventRecord(ev[1], s));
         return GPTQ_OK;
     }
-    double* part = (double*)ws;
-    uint16_t* xt = (uint16_t*)((char*)ws + part_bytes(d));
+    const size_t slot = slot_bytes(n_tok, d);
     const int64_t d_pad = align_up((size_t)d, BT);
     const int64_t T = d_pad / BT;
     const int64_t n_tiles = T * (T + 1) / 2;
     const int64_t per_xcd = ceil_div(n_tiles, 8);
     const bool vec = (ld_x % 8 == 0) && (d % 8 == 0) && ((uintptr_t)X % 16 == 0);
+    const bool bf = dt == GPTQ_BF16;
     const uint16_t* x = (const uint16_t*)X;
-    GPTQ_HIP(hipFuncSetAttribute((const void*)hess_syrk_kernel<bf16x8_t, SYRK_WAVES>,
-                                 hipFuncAttributeMaxDynamicSharedMemorySize, RING_BYTES));
-    GPTQ_HIP(hipFuncSetAttribute((const void*)hess_syrk_kernel<h16x8_t, SYRK_WAVES>,
-                                 hipFuncAttributeMaxDynamicSharedMemorySize, RING_BYTES));
-    const dim3 b256(256);
-    // per chunk: transpose into Xt, then one SYRK launch that adds its
-    // float32 partial tiles to H in float64; chunks in token order
+    const void* syrk = bf ? (vec ? (const void*)hess_syrk_kernel<bf16x8_t, SYRK_WAVES, true>
+                                 : (const void*)hess_syrk_kernel<bf16x8_t, SYRK_WAVES, false>)
+                          : (vec ? (const void*)hess_syrk_kernel<h16x8_t, SYRK_WAVES, true>
+                                 : (const void*)hess_syrk_kernel<h16x8_t, SYRK_WAVES, false>);
+    GPTQ_HIP(hipFuncSetAttribute(syrk, hipFuncAttributeMaxDynamicSharedMemorySize, RING_BYTES));
+    const dim3 b256(256), dgrid((unsigned)ceil_div(d, 256));
     const int64_t cmax = chunk_tokens(d);
-    for (int64_t c0 = 0, ci = 0; c0 < n_tok; c0 += cmax, ++ci) {
-        const int64_t nt = (n_tok - c0 < cmax) ? n_tok - c0 : cmax;
-        const int64_t ch = align_up((size_t)nt, KT);
-        const uint16_t* xc = x + c0 * ld_x;
-        const int64_t nblk = ceil_div(ch, TSPAN);
+    const int64_t npair = (d_pad / 256 + 1) / 2;
+    auto slot_part = [&](int64_t ci) { return (double*)((char*)ws + (ci & 1) * slot); };
+    auto slot_xt = [&](int64_t ci) { return (uint16_t*)((char*)ws + (ci & 1) * slot + part_bytes(d)); };
+    auto chunk_nt = [&](int64_t c0) { return (n_tok - c0 < cmax) ? n_tok - c0 : cmax; };
+    // Chunk 0 is transposed on its own; chunk ci+1 by the workgroups past
+    // the tiles of chunk ci's product launch, into the other workspace
+    // slot.  Each chunk's diagonal sums are added after its transpose, in
+    // token order.
+    {
+        const int64_t nt = chunk_nt(0), ch = align_up((size_t)nt, KT), nblk = ceil_div(ch, TSPAN);
         const dim3 tgrid((unsigned)nblk, (unsigned)(d_pad / 256));
-        if (dt == GPTQ_BF16) {
-            if (vec) hipLaunchKernelGGL((transpose_kernel<bf16x8_t, true>), tgrid, b256, 0, s, xc, nt, d, ld_x, xt, ch, d_pad, part);
-            else hipLaunchKernelGGL((transpose_kernel<bf16x8_t, false>), tgrid, b256, 0, s, xc, nt, d, ld_x, xt, ch, d_pad, part);
+        uint16_t* xt = slot_xt(0);
+        double* part = slot_part(0);
+        if (bf) {
+            if (vec) hipLaunchKernelGGL((transpose_kernel<bf16x8_t, true>), tgrid, b256, 0, s, x, nt, d, ld_x, xt, ch, d_pad, part);
+            else hipLaunchKernelGGL((transpose_kernel<bf16x8_t, false>), tgrid, b256, 0, s, x, nt, d, ld_x, xt, ch, d_pad, part);
         } else {
-            if (vec) hipLaunchKernelGGL((transpose_kernel<h16x8_t, true>), tgrid, b256, 0, s, xc, nt, d, ld_x, xt, ch, d_pad, part);
-            else hipLaunchKernelGGL((transpose_kernel<h16x8_t, false>), tgrid, b256, 0, s, xc, nt, d, ld_x, xt, ch, d_pad, part);
+            if (vec) hipLaunchKernelGGL((transpose_kernel<h16x8_t, true>), tgrid, b256, 0, s, x, nt, d, ld_x, xt, ch, d_pad, part);
+            else hipLaunchKernelGGL((transpose_kernel<h16x8_t, false>), tgrid, b256, 0, s, x, nt, d, ld_x, xt, ch, d_pad, part);
         }
         GPTQ_LAUNCH_CHECK();
-        hipLaunchKernelGGL(diag_add_kernel, dim3((unsigned)ceil_div(d, 256)), b256, 0, s, part, nblk, d, H);
+        hipLaunchKernelGGL(diag_add_kernel, dgrid, b256, 0, s, part, nblk, d, H);
         GPTQ_LAUNCH_CHECK();
-        const dim3 grid((unsigned)(per_xcd * 8)), block(SYRK_WAVES * 64);
+    }
+    for (int64_t c0 = 0, ci = 0; c0 < n_tok; c0 += cmax, ++ci) {
+        const int64_t ch = align_up((size_t)chunk_nt(c0), KT);
+        NextChunk nx{nullptr, 0, ld_x, 0, nullptr, nullptr};
+        int64_t n_tr = 0, nblk_next = 0;
+        if (c0 + cmax < n_tok) {
+            nx.X = x + (c0 + cmax) * ld_x;
+            nx.n_tok = chunk_nt(c0 + cmax);
+            nx.ch = align_up((size_t)nx.n_tok, KT);
+            nx.Xt = slot_xt(ci + 1);
+            nx.colsq = slot_part(ci + 1);
+            nblk_next = ceil_div(nx.ch, TSPAN);
+            n_tr = nblk_next * npair;
+        }
+        const dim3 grid((unsigned)(per_xcd * 8 + n_tr)), block(SYRK_WAVES * 64);
+        uint16_t* xt = slot_xt(ci);
         if (ev) GPTQ_HIP(hipEventRecord(ev[2 * ci], s));
-        if (dt == GPTQ_BF16)
-            hipLaunchKernelGGL((hess_syrk_kernel<bf16x8_t, SYRK_WAVES>), grid, block, RING_BYTES, s, H, xt, ch, d_pad, d, T,
-                               n_tiles, per_xcd);
-        else
-            hipLaunchKernelGGL((hess_syrk_kernel<h16x8_t, SYRK_WAVES>), grid, block, RING_BYTES, s, H, xt, ch, d_pad, d, T,
-                               n_tiles, per_xcd);
+        if (bf) {
+            if (vec) hipLaunchKernelGGL((hess_syrk_kernel<bf16x8_t, SYRK_WAVES, true>), grid, block, RING_BYTES, s, H, xt, ch, d_pad, d, T, n_tiles, per_xcd, nx);
+            else hipLaunchKernelGGL((hess_syrk_kernel<bf16x8_t, SYRK_WAVES, false>), grid, block, RING_BYTES, s, H, xt, ch, d_pad, d, T, n_tiles, per_xcd, nx);
+        } else {
+            if (vec) hipLaunchKernelGGL((hess_syrk_kernel<h16x8_t, SYRK_WAVES, true>), grid, block, RING_BYTES, s, H, xt, ch, d_pad, d, T, n_tiles, per_xcd, nx);
+            else hipLaunchKernelGGL((hess_syrk_kernel<h16x8_t, SYRK_WAVES, false>), grid, block, RING_BYTES, s, H, xt, ch, d_pad, d, T, n_tiles, per_xcd, nx);
+        }
         GPTQ_LAUNCH_CHECK();
         if (ev) GPTQ_HIP(hipEventRecord(ev[2 * ci + 1], s));
+        if (n_tr > 0) {
+            hipLaunchKernelGGL(diag_add_kernel, dgrid, b256, 0, s, slot_part(ci + 1), nblk_next, d, H);
+            GPTQ_LAUNCH_CHECK();
+        }
     }
     return GPTQ_OK;
 }

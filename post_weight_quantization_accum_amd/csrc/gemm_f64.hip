@@ -208,23 +208,33 @@ __global__ __launch_bounds__(256, 2) void gemm_f64_kernel(int64_t M, int64_t N, 
         __syncthreads();
     }
 
+    // C = alpha * acc + beta * C.  The C values of MFMA row group mi + 1 are
+    // loaded before group mi is stored, so the reads of the read-modify-write
+    // overlap instead of waiting one by one (the compiler cannot reorder a
+    // load of C after a store to C).
+    const int64_t mrow = m0 + wr * G::WT + (lane >> 4), ncol = n0 + wc * G::WT + (lane & 15);
+    double cv[2][4][G::NT];
+    auto load_c = [&](double (&dst)[4][G::NT], int mi) {
 #pragma unroll
-    for (int mi = 0; mi < G::NT; ++mi)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int64_t m = m0 + wr * G::WT + mi * 16 + 4 * r + (lane >> 4);
-            if (m >= M) continue;
+        for (int r = 0; r < 4; ++r)
 #pragma unroll
             for (int ni = 0; ni < G::NT; ++ni) {
-                const int64_t n = n0 + wc * G::WT + ni * 16 + (lane & 15);
-                if (n < N) {
-                    double* p = C + m * ldc + n;
-                    double v = alpha * acc[mi][ni][r];
-                    if (beta != 0.0) v += beta * (*p);
-                    *p = v;
-                }
+                const int64_t m = mrow + mi * 16 + 4 * r, n = ncol + ni * 16;
+                dst[r][ni] = (beta != 0.0 && m < M && n < N) ? C[m * ldc + n] : 0.0;
             }
-        }
+    };
+    load_c(cv[0], 0);
+#pragma unroll
+    for (int mi = 0; mi < G::NT; ++mi) {
+        if (mi + 1 < G::NT) load_c(cv[(mi + 1) & 1], mi + 1);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int ni = 0; ni < G::NT; ++ni) {
+                const int64_t m = mrow + mi * 16 + 4 * r, n = ncol + ni * 16;
+                if (m < M && n < N) C[m * ldc + n] = alpha * acc[mi][ni][r] + beta * cv[mi & 1][r][ni];
+            }
+    }
 }
 
 // LDS a workgroup must hold so that only one fits on a CU (160 KiB each).

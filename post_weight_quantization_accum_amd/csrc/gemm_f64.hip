@@ -237,6 +237,93 @@ __global__ __launch_bounds__(256, 2) void gemm_f64_kernel(int64_t M, int64_t N, 
     }
 }
 
+// Small products (M, N <= SMALL_MN: the lower levels of the recursive
+// factorisation): one wave per 16x16 tile of C, operands straight from
+// memory (L2) into MFMA registers, 64 values of K per group with the next
+// group's loads in flight while the current one multiplies; no LDS and no
+// barriers, so a launch costs about one memory round trip plus its MFMAs.
+// Per-tile K ranges for triangular operands at 16-column granularity.
+constexpr int64_t SMALL_MN = 256;
+
+template <bool TRANS_B, bool LOWER>
+__global__ __launch_bounds__(256) void gemm_f64_small_kernel(int64_t M, int64_t N, int64_t K, double alpha,
+                                                             const double* __restrict__ A, int64_t lda,
+                                                             const double* __restrict__ B, int64_t ldb, double beta,
+                                                             double* C, int64_t ldc, int64_t tiles_m, int64_t tiles_n,
+                                                             int tri) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t t = (int64_t)blockIdx.x * 4 + wave;
+    int64_t tm, tn;
+    if (LOWER) {
+        if (t >= tiles_m * (tiles_m + 1) / 2) return;
+        tri_index(t, tm, tn);
+    } else {
+        if (t >= tiles_m * tiles_n) return;
+        tm = t / tiles_n;
+        tn = t % tiles_n;
+    }
+    const int64_t m0 = tm * 16, n0 = tn * 16;
+    int64_t kbeg = 0, kend = K;
+    if (tri == GEMM_TRI_KEND_ROW) kend = (m0 + 16 < K) ? m0 + 16 : K;
+    else if (tri == GEMM_TRI_KEND_COL) kend = (n0 + 16 < K) ? n0 + 16 : K;
+    else if (tri == GEMM_TRI_KBEG_COL) kbeg = (n0 < K) ? n0 : K;
+    const int r = lane & 15, kq = lane >> 4;
+    const int64_t m = m0 + r, n = n0 + r;
+    const double* pa = A + (m < M ? m : 0) * lda;
+    const double* pb = TRANS_B ? B + (n < N ? n : 0) * ldb : B + (n < N ? n : 0);
+    // operand k of this lane: A[m][k] and op(B)[k][n]; zero outside the ranges
+    constexpr int G = 4;   // MFMA K-steps of 16 per group
+    auto load_group = [&](double (&a)[G][4], double (&b)[G][4], int64_t k0) {
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int64_t k = k0 + 16 * g + 4 * q + kq;
+                const bool kok = k < kend;
+                a[g][q] = (kok && m < M) ? pa[k] : 0.0;
+                b[g][q] = (kok && n < N) ? (TRANS_B ? pb[k] : pb[k * ldb]) : 0.0;
+            }
+    };
+    double a0[G][4], b0[G][4], a1[G][4], b1[G][4];
+    d4_t acc = {0.0, 0.0, 0.0, 0.0};
+    const int64_t ngroups = (kend > kbeg) ? ceil_div(kend - kbeg, 16 * G) : 0;
+    if (ngroups > 0) load_group(a0, b0, kbeg);
+    for (int64_t gi = 0; gi < ngroups; gi += 2) {
+        if (gi + 1 < ngroups) load_group(a1, b1, kbeg + (gi + 1) * 16 * G);
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc = mfma_f64_16x16x4(a0[g][q], b0[g][q], acc);
+        if (gi + 1 >= ngroups) break;
+        if (gi + 2 < ngroups) load_group(a0, b0, kbeg + (gi + 2) * 16 * G);
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc = mfma_f64_16x16x4(a1[g][q], b1[g][q], acc);
+    }
+    // result element i of this lane: C[m0 + 4i + kq][n0 + r]; C read before any store
+    double cv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int64_t mi = m0 + 4 * i + kq;
+        cv[i] = (beta != 0.0 && mi < M && n < N) ? C[mi * ldc + n] : 0.0;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int64_t mi = m0 + 4 * i + kq;
+        if (mi < M && n < N) C[mi * ldc + n] = alpha * acc[i] + beta * cv[i];
+    }
+}
+
+template <bool TRANS_B, bool LOWER>
+void launch_small(hipStream_t s, int64_t M, int64_t N, int64_t K, double alpha, const double* A, int64_t lda,
+                  const double* B, int64_t ldb, double beta, double* C, int64_t ldc, int tri) {
+    const int64_t tiles_m = ceil_div(M, 16), tiles_n = ceil_div(N, 16);
+    const int64_t n_tiles = LOWER ? tiles_m * (tiles_m + 1) / 2 : tiles_m * tiles_n;
+    hipLaunchKernelGGL((gemm_f64_small_kernel<TRANS_B, LOWER>), dim3((unsigned)ceil_div(n_tiles, 4)), dim3(256), 0,
+                       s, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, tiles_m, tiles_n, tri);
+}
+
 // LDS a workgroup must hold so that only one fits on a CU (160 KiB each).
 constexpr size_t CU_LDS = 160 * 1024;
 
@@ -286,6 +373,17 @@ gptq_status launch_gemm_f64(hipStream_t s, int64_t M, int64_t N, int64_t K, doub
         return GPTQ_ERR_UNSUPPORTED;
     }
     if (lower_tiles && M != N) return GPTQ_ERR_INVALID_ARG;
+    if (M <= SMALL_MN && N <= SMALL_MN) {
+        if (transB) {
+            if (lower_tiles) launch_small<true, true>(s, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, (int)tri);
+            else launch_small<true, false>(s, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, (int)tri);
+        } else {
+            if (lower_tiles) launch_small<false, true>(s, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, (int)tri);
+            else launch_small<false, false>(s, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, (int)tri);
+        }
+        GPTQ_LAUNCH_CHECK();
+        return GPTQ_OK;
+    }
     const bool vec = ((uintptr_t)A % 16 == 0) && (lda % 2 == 0) && ((uintptr_t)B % 16 == 0) && (ldb % 2 == 0);
     if (transB) {
         if (lower_tiles)

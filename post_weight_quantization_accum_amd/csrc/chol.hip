@@ -600,6 +600,17 @@ gptq_status chol_inv(const Rec& c, int64_t o, int64_t n, int depth) {
     // L21 = A21 M11^T
     st = launch_gemm_f64(c.s, n2, n1, n1, 1.0, A21, d, M11, d, true, 0.0, L21, n1, false, GEMM_TRI_KEND_COL);
     if (st != GPTQ_OK) return st;
+    if (n1 <= 256 && n2 <= 256) {
+        // small node: A22 -= L21 L21^T and T = L21 M11 in one launch, all on
+        // the main stream (no cross-stream events on the short chain)
+        const GemmCall syrk{n2, n2, n1, -1.0, L21, n1, L21, n1, true, 1.0, A22, d, true, GEMM_TRI_NONE};
+        const GemmCall tprod{n2, n1, n1, 1.0, L21, n1, M11, d, false, 0.0, A21, d, false, GEMM_TRI_KBEG_COL};
+        st = launch_gemm_f64_pair(c.s, syrk, tprod);
+        if (st != GPTQ_OK) return st;
+        st = chol_inv(c, o + n1, n2, depth + 1);
+        if (st != GPTQ_OK) return st;
+        return launch_gemm_f64(c.s, n2, n1, n2, -1.0, M22, d, A21, d, false, 0.0, M21, d, false, GEMM_TRI_KEND_ROW);
+    }
     // A22 -= L21 L21^T
     st = launch_gemm_f64(c.s, n2, n2, n1, -1.0, L21, n1, L21, n1, true, 1.0, A22, d, true);
     if (st != GPTQ_OK) return st;

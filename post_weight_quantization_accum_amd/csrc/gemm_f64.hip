@@ -245,32 +245,47 @@ __global__ __launch_bounds__(256, 2) void gemm_f64_kernel(int64_t M, int64_t N, 
 // Per-tile K ranges for triangular operands at 16-column granularity.
 constexpr int64_t SMALL_MN = 256;
 
+struct SmallArgs {
+    int64_t M, N, K;
+    double alpha;
+    const double* A;
+    int64_t lda;
+    const double* B;
+    int64_t ldb;
+    double beta;
+    double* C;
+    int64_t ldc, tiles_m, tiles_n, n_tiles;
+    int tri;
+};
+
+SmallArgs small_args(int64_t M, int64_t N, int64_t K, double alpha, const double* A, int64_t lda, const double* B,
+                     int64_t ldb, double beta, double* C, int64_t ldc, bool lower, int tri) {
+    const int64_t tm = ceil_div(M, 16), tn = ceil_div(N, 16);
+    return SmallArgs{M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, tm, tn, lower ? tm * (tm + 1) / 2 : tm * tn, tri};
+}
+
+// Tile t of one small product, computed by the calling wave.
 template <bool TRANS_B, bool LOWER>
-__global__ __launch_bounds__(256) void gemm_f64_small_kernel(int64_t M, int64_t N, int64_t K, double alpha,
-                                                             const double* __restrict__ A, int64_t lda,
-                                                             const double* __restrict__ B, int64_t ldb, double beta,
-                                                             double* C, int64_t ldc, int64_t tiles_m, int64_t tiles_n,
-                                                             int tri) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t t = (int64_t)blockIdx.x * 4 + wave;
+__device__ __forceinline__ void small_tile(const SmallArgs& p, int64_t t, int lane) {
+    if (t >= p.n_tiles) return;
     int64_t tm, tn;
     if (LOWER) {
-        if (t >= tiles_m * (tiles_m + 1) / 2) return;
         tri_index(t, tm, tn);
     } else {
-        if (t >= tiles_m * tiles_n) return;
-        tm = t / tiles_n;
-        tn = t % tiles_n;
+        tm = t / p.tiles_n;
+        tn = t % p.tiles_n;
     }
+    const int64_t M = p.M, N = p.N, K = p.K;
     const int64_t m0 = tm * 16, n0 = tn * 16;
     int64_t kbeg = 0, kend = K;
-    if (tri == GEMM_TRI_KEND_ROW) kend = (m0 + 16 < K) ? m0 + 16 : K;
-    else if (tri == GEMM_TRI_KEND_COL) kend = (n0 + 16 < K) ? n0 + 16 : K;
-    else if (tri == GEMM_TRI_KBEG_COL) kbeg = (n0 < K) ? n0 : K;
+    if (p.tri == GEMM_TRI_KEND_ROW) kend = (m0 + 16 < K) ? m0 + 16 : K;
+    else if (p.tri == GEMM_TRI_KEND_COL) kend = (n0 + 16 < K) ? n0 + 16 : K;
+    else if (p.tri == GEMM_TRI_KBEG_COL) kbeg = (n0 < K) ? n0 : K;
     const int r = lane & 15, kq = lane >> 4;
     const int64_t m = m0 + r, n = n0 + r;
-    const double* pa = A + (m < M ? m : 0) * lda;
-    const double* pb = TRANS_B ? B + (n < N ? n : 0) * ldb : B + (n < N ? n : 0);
+    const double* pa = p.A + (m < M ? m : 0) * p.lda;
+    const double* pb = TRANS_B ? p.B + (n < N ? n : 0) * p.ldb : p.B + (n < N ? n : 0);
+    const int64_t ldb = p.ldb;
     // operand k of this lane: A[m][k] and op(B)[k][n]; zero outside the ranges
     constexpr int G = 4;   // MFMA K-steps of 16 per group
     auto load_group = [&](double (&a)[G][4], double (&b)[G][4], int64_t k0) {
@@ -306,22 +321,36 @@ __global__ __launch_bounds__(256) void gemm_f64_small_kernel(int64_t M, int64_t 
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int64_t mi = m0 + 4 * i + kq;
-        cv[i] = (beta != 0.0 && mi < M && n < N) ? C[mi * ldc + n] : 0.0;
+        cv[i] = (p.beta != 0.0 && mi < M && n < N) ? p.C[mi * p.ldc + n] : 0.0;
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int64_t mi = m0 + 4 * i + kq;
-        if (mi < M && n < N) C[mi * ldc + n] = alpha * acc[i] + beta * cv[i];
+        if (mi < M && n < N) p.C[mi * p.ldc + n] = p.alpha * acc[i] + p.beta * cv[i];
     }
+}
+
+template <bool TRANS_B, bool LOWER>
+__global__ __launch_bounds__(256) void gemm_f64_small_kernel(SmallArgs p) {
+    small_tile<TRANS_B, LOWER>(p, (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6), threadIdx.x & 63);
+}
+
+// Two independent small products in one launch: a symmetric update
+// (lower tiles, op(B) = B^T) and a plain product; the workgroups of the
+// second follow those of the first.
+__global__ __launch_bounds__(256) void gemm_f64_small_pair_kernel(SmallArgs p1, SmallArgs p2, int64_t nb1) {
+    const int64_t b = blockIdx.x;
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    if (b < nb1) small_tile<true, true>(p1, b * 4 + w, lane);
+    else small_tile<false, false>(p2, (b - nb1) * 4 + w, lane);
 }
 
 template <bool TRANS_B, bool LOWER>
 void launch_small(hipStream_t s, int64_t M, int64_t N, int64_t K, double alpha, const double* A, int64_t lda,
                   const double* B, int64_t ldb, double beta, double* C, int64_t ldc, int tri) {
-    const int64_t tiles_m = ceil_div(M, 16), tiles_n = ceil_div(N, 16);
-    const int64_t n_tiles = LOWER ? tiles_m * (tiles_m + 1) / 2 : tiles_m * tiles_n;
-    hipLaunchKernelGGL((gemm_f64_small_kernel<TRANS_B, LOWER>), dim3((unsigned)ceil_div(n_tiles, 4)), dim3(256), 0,
-                       s, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, tiles_m, tiles_n, tri);
+    const SmallArgs p = small_args(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, LOWER, tri);
+    hipLaunchKernelGGL((gemm_f64_small_kernel<TRANS_B, LOWER>), dim3((unsigned)ceil_div(p.n_tiles, 4)), dim3(256),
+                       0, s, p);
 }
 
 // LDS a workgroup must hold so that only one fits on a CU (160 KiB each).
@@ -396,6 +425,19 @@ gptq_status launch_gemm_f64(hipStream_t s, int64_t M, int64_t N, int64_t K, doub
         else
             launch_sel<false, false>(s, vec, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, (int)tri, one_per_cu);
     }
+    GPTQ_LAUNCH_CHECK();
+    return GPTQ_OK;
+}
+
+gptq_status launch_gemm_f64_pair(hipStream_t s, const GemmCall& x, const GemmCall& y) {
+    const bool small = x.M <= SMALL_MN && x.N <= SMALL_MN && y.M <= SMALL_MN && y.N <= SMALL_MN;
+    if (!small || !x.transB || !x.lower_tiles || x.tri != GEMM_TRI_NONE || y.transB || y.lower_tiles ||
+        x.M != x.N || x.M <= 0 || y.M <= 0 || y.N <= 0 || x.K < 0 || y.K < 0)
+        return GPTQ_ERR_UNSUPPORTED;
+    const SmallArgs p1 = small_args(x.M, x.N, x.K, x.alpha, x.A, x.lda, x.B, x.ldb, x.beta, x.C, x.ldc, true, x.tri);
+    const SmallArgs p2 = small_args(y.M, y.N, y.K, y.alpha, y.A, y.lda, y.B, y.ldb, y.beta, y.C, y.ldc, false, y.tri);
+    const int64_t nb1 = ceil_div(p1.n_tiles, 4), nb2 = ceil_div(p2.n_tiles, 4);
+    hipLaunchKernelGGL(gemm_f64_small_pair_kernel, dim3((unsigned)(nb1 + nb2)), dim3(256), 0, s, p1, p2, nb1);
     GPTQ_LAUNCH_CHECK();
     return GPTQ_OK;
 }

@@ -27,6 +27,27 @@ gptq_status launch_gemm_f64(hipStream_t s, int64_t M, int64_t N, int64_t K, doub
                             bool transB, double beta, double* C, int64_t ldc, bool lower_tiles,
                             GemmTri tri = GEMM_TRI_NONE, bool one_per_cu = false);
 
+// Two independent small products (both with M, N <= 256) in one launch:
+// x a symmetric update (lower_tiles, transB, no triangular range), y a plain
+// product (no transB, no lower_tiles, any triangular range).  Anything else
+// returns GPTQ_ERR_UNSUPPORTED.  K = 0 products write beta * C (not read when
+// beta == 0).
+struct GemmCall {
+    int64_t M, N, K;
+    double alpha;
+    const double* A;
+    int64_t lda;
+    const double* B;
+    int64_t ldb;
+    bool transB;
+    double beta;
+    double* C;
+    int64_t ldc;
+    bool lower_tiles;
+    GemmTri tri;
+};
+gptq_status launch_gemm_f64_pair(hipStream_t s, const GemmCall& x, const GemmCall& y);
+
 // Hessian: H (upper) += 2 X^T X.  ws: hessian_workspace_bytes(n_tok, d)
 // bytes (float64 partial column sums of the diagonal, then the transposed
 // token chunk); unused for fp32 inputs.

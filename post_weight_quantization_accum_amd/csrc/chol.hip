@@ -600,7 +600,7 @@ gptq_status chol_inv(const Rec& c, int64_t o, int64_t n, int depth) {
     // L21 = A21 M11^T
     st = launch_gemm_f64(c.s, n2, n1, n1, 1.0, A21, d, M11, d, true, 0.0, L21, n1, false, GEMM_TRI_KEND_COL);
     if (st != GPTQ_OK) return st;
-    if (n1 <= 256 && n2 <= 256) {
+    if (n1 <= 512 && n2 <= 512) {
         // small node: A22 -= L21 L21^T and T = L21 M11 in one launch, all on
         // the main stream (no cross-stream events on the short chain)
         const GemmCall syrk{n2, n2, n1, -1.0, L21, n1, L21, n1, true, 1.0, A22, d, true, GEMM_TRI_NONE};

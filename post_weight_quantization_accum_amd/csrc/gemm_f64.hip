@@ -243,7 +243,7 @@ __global__ __launch_bounds__(256, 2) void gemm_f64_kernel(int64_t M, int64_t N, 
 // group's loads in flight while the current one multiplies; no LDS and no
 // barriers, so a launch costs about one memory round trip plus its MFMAs.
 // Per-tile K ranges for triangular operands at 16-column granularity.
-constexpr int64_t SMALL_MN = 256;
+constexpr int64_t SMALL_MN = 512;
 
 struct SmallArgs {
     int64_t M, N, K;

@@ -27,7 +27,7 @@ gptq_status launch_gemm_f64(hipStream_t s, int64_t M, int64_t N, int64_t K, doub
                             bool transB, double beta, double* C, int64_t ldc, bool lower_tiles,
                             GemmTri tri = GEMM_TRI_NONE, bool one_per_cu = false);
 
-// Two independent small products (both with M, N <= 256) in one launch:
+// Two independent small products (both with M, N <= 512) in one launch:
 // x a symmetric update (lower_tiles, transB, no triangular range), y a plain
 // product (no transB, no lower_tiles, any triangular range).  Anything else
 // returns GPTQ_ERR_UNSUPPORTED.  K = 0 products write beta * C (not read when

@@ -280,10 +280,11 @@ __global__ __launch_bounds__(SWAVES * 64) void sweep_block_kernel(double* __rest
 
     // current group parameters of this row (a group begun in an earlier
     // block is continued)
-    double scale = 1.0, zero = 0.0;
+    double scale = 1.0, zero = 0.0, rscale = 1.0;
     const int64_t rem = i1 % g;
     if (rem != 0 && live) {
         scale = scale64[(i1 / g) * d_out + row];
+        rscale = 1.0 / scale;
         zero = zero64[(i1 / g) * d_out + row];
     }
     int next_gs = (int)(rem == 0 ? 0 : g - rem);      // block column of the next group start
@@ -335,6 +336,7 @@ __global__ __launch_bounds__(SWAVES * 64) void sweep_block_kernel(double* __rest
                     scale = (xmax - xmin) / qp.maxq;
                     zero = rint(-xmin / scale);
                 }
+                rscale = 1.0 / scale;
                 if (live && part == 0) {
                     scale64[next_gi * d_out + row] = scale;
                     zero64[next_gi * d_out + row] = zero;
@@ -354,9 +356,15 @@ __global__ __launch_bounds__(SWAVES * 64) void sweep_block_kernel(double* __rest
                 double (&u)[CPL] = (k & 1) ? ub : ua;
                 const double ri = rinv[c];
                 // quantize column c (meaningful in the owner lane, part == P);
-                // the code is decided on the correctly rounded quotient w / scale
+                // the code is decided on the correctly rounded quotient w / scale.
+                // y = w * (1/scale) is within 2^-51 |y| of that quotient, so
+                // their nearest integers agree unless y lies within 2^-40
+                // max(1, |y|) of a half-integer; only then is the quotient
+                // formed (divergent, rare).
                 const double x = w[k];
-                double code = rint(x / scale) + zero;
+                double y = x * rscale;
+                if (fabs(y - floor(y) - 0.5) <= 0x1p-40 * fmax(1.0, fabs(y))) y = x / scale;
+                double code = rint(y) + zero;
                 code = fmin(fmax(code, 0.0), qp.maxq);
                 const double q = scale * (code - zero);
                 const double diff = x - q;

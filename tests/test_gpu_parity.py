@@ -177,6 +177,27 @@ def test_sweep_matches_oracle_given_U(d_out, d_in, bits, g, act, sym, block):
     np.testing.assert_allclose(got["row_loss"], ref["row_loss"], rtol=1e-9)
 
 
+def test_sweep_exact_ties_round_half_even():
+    # One-hot tokens make H, and so U, diagonal: no compensation crosses
+    # columns and every weight reaches the quantizer as written.  Each
+    # 128-column group holds 0 and 15 (4-bit asym: scale 1, zero 0) and
+    # otherwise k + 0.5, so every other quotient is an exact tie, decided
+    # half-to-even as in the oracle.
+    d_out, d_in = 24, 256
+    rng = np.random.default_rng(5)
+    W = rng.integers(0, 15, size=(d_out, d_in)).astype(np.float64) + 0.5
+    W[:, 0::128] = 0.0
+    W[:, 1::128] = 15.0
+    H = O.hessian(np.eye(d_in))
+    ref = O.gptq_quantize(W, H, bits=4, group_size=128, act_order=False)
+    assert np.array_equal(ref["codes"], np.rint(W).astype(ref["codes"].dtype))
+    cfg = P.make_config(bits=4, group_size=128, act_order=False)
+    out = P.quantize_layer(torch.from_numpy(W.astype(np.float32)).to(DEV), torch.from_numpy(ref["U"]).to(DEV),
+                           torch.from_numpy(ref["perm"].astype(np.int32)).to(DEV), cfg)
+    torch.cuda.synchronize()
+    assert np.array_equal(out["codes"].cpu().numpy(), ref["codes"])
+
+
 def test_sweep_fp16_and_fp32_weights():
     for dtype in ("f16", "f32"):
         ref, got = _sweep_case(48, 256, 4, 128, True, dtype=dtype, seed=7)

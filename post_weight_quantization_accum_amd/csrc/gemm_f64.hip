@@ -128,24 +128,57 @@ __global__ __launch_bounds__(256, 2) void gemm_f64_kernel(int64_t M, int64_t N, 
         tri_index(lin, tm, tn);
     } else if (tri != GEMM_TRI_NONE && tiles_m >= 16) {
         // triangular operand: tile work varies with the row or the column.
-        // XCD x takes row bands x, x+8, x+16, ... (whole bands: rows of A
-        // stay in its L2; every XCD gets light and heavy bands), heaviest
-        // rows / columns dispatched first.
+        // Balanced over the XCDs: with f = tiles_m / 8, XCD x takes f whole
+        // row bands (rows of A stay in its L2), and the tiles of the
+        // remaining r = tiles_m % 8 bands are dealt out by column: tile
+        // (leftover band j, column c) goes to XCD (c + 3j) mod 8.  Heaviest
+        // tiles are dispatched first.
         const int64_t x = b % 8, q = b / 8;
+        const int64_t f = tiles_m / 8, r = tiles_m % 8;
+        // leftover band j whose tile in column c belongs to this XCD (3 * 3 = 1 mod 8)
+        auto left_j = [&](int64_t c) { return (3 * (x - c % 8) % 8 + 8) % 8; };
         if (tri == GEMM_TRI_KEND_ROW) {
-            // work grows with the row: bands in descending order
-            const int64_t band = x + 8 * (q / tiles_n);
-            if (band >= tiles_m) return;
-            tm = tiles_m - 1 - band;
-            tn = q % tiles_n;
+            // work grows with the row.  Whole bands by rank (0 = heaviest,
+            // tm = tiles_m - 1 - rank), boustrophedon over the XCDs; the
+            // leftover bands are the lightest rows, their tiles last.
+            if (q < f * tiles_n) {
+                const int64_t k = q / tiles_n;
+                const int64_t rank = (k & 1) ? 8 * k + 7 - x : 8 * k + x;
+                tm = tiles_m - 1 - rank;
+                tn = q % tiles_n;
+            } else {
+                int64_t rest = q - f * tiles_n;
+                tm = -1;
+                for (int64_t c = 0; c < tiles_n; ++c) {
+                    const int64_t j = left_j(c);
+                    if (j >= r) continue;
+                    if (rest == 0) {
+                        tm = r - 1 - j;   // leftover ranks 8f + j, lightest rows
+                        tn = c;
+                        break;
+                    }
+                    --rest;
+                }
+                if (tm < 0) return;
+            }
         } else {
-            // work varies along the columns: column-major over this XCD's
-            // bands, heaviest columns first
-            const int64_t nb = (tiles_m - x + 7) / 8;  // bands of this XCD
-            if (nb <= 0 || q >= nb * tiles_n) return;
-            tm = x + 8 * (q % nb);
-            const int64_t ci = q / nb;
-            tn = (tri == GEMM_TRI_KEND_COL) ? tiles_n - 1 - ci : ci;
+            // work varies along the columns: column-major, heaviest column
+            // first; per column the XCD's f whole bands, then its leftover
+            // tile of that column if it has one
+            int64_t rest = q;
+            tm = -1;
+            for (int64_t ci = 0; ci < tiles_n; ++ci) {
+                const int64_t c = (tri == GEMM_TRI_KEND_COL) ? tiles_n - 1 - ci : ci;
+                const int64_t j = left_j(c);
+                const int64_t cnt = f + (j < r ? 1 : 0);
+                if (rest < cnt) {
+                    tm = (rest < f) ? x + 8 * rest : 8 * f + j;
+                    tn = c;
+                    break;
+                }
+                rest -= cnt;
+            }
+            if (tm < 0) return;
         }
     } else {
         const int64_t lin = (b % 8) * per_xcd + b / 8;
@@ -361,8 +394,9 @@ void launch_t(hipStream_t s, bool vec, int64_t M, int64_t N, int64_t K, double a
               const double* B, int64_t ldb, double beta, double* C, int64_t ldc, int tri, bool one_per_cu) {
     const int64_t tiles_m = ceil_div(M, TILE), tiles_n = ceil_div(N, TILE);
     const int64_t n_tiles = LOWER ? tiles_m * (tiles_m + 1) / 2 : tiles_m * tiles_n;
-    const int64_t per_xcd =
-        (!LOWER && tri != GEMM_TRI_NONE && tiles_m >= 16) ? ceil_div(tiles_m, 8) * tiles_n : ceil_div(n_tiles, 8);
+    // per XCD: whole bands plus at most one leftover tile per column (triangular case)
+    const int64_t per_xcd = (!LOWER && tri != GEMM_TRI_NONE && tiles_m >= 16) ? (tiles_m / 8 + 1) * tiles_n
+                                                                              : ceil_div(n_tiles, 8);
     const dim3 grid((unsigned)(per_xcd * 8));
     // one_per_cu: unused dynamic LDS beyond half a CU's, so that a second
     // workgroup of this launch never shares the CU (room for other streams)

@@ -116,6 +116,23 @@ def test_prepare_hinv_matches_oracle(d, act):
     assert err <= 1e-9, err
 
 
+@pytest.mark.parametrize("d,act", [(2100, True), (4700, False)])
+def test_prepare_hinv_large_matches_oracle(d, act):
+    # sizes whose top products run on the LDS-tiled GEMM (64- and
+    # 128-column tiles, triangular K ranges, XCD-balanced tile lists)
+    print(f"prepare_hinv d={d} act={act}", flush=True)
+    L = _layer(4, d, d + 300, dtype="f32", dist="gauss_mix", frac=0.0, seed=d + 1)
+    H = O.hessian(L.X_f64())
+    cfg = P.make_config(act_order=act, damp=0.01)
+    Ug, perm = _gpu_prepare(H, cfg)
+    p = O.act_order_permutation(H) if act else np.arange(d)
+    assert np.array_equal(perm, p)
+    Uref = O.inverse_hessian_upper(O.damp_hessian(H[np.ix_(p, p)], 0.01))
+    assert np.all(np.tril(Ug, -1) == 0.0)
+    err = np.abs(Ug - Uref).max() / np.abs(Uref).max()
+    assert err <= 1e-9, err
+
+
 def test_act_order_ties_and_dead_channels():
     d = 150
     # three tie classes, one of them all-zero (dead channels)

@@ -325,31 +325,34 @@ __device__ __forceinline__ d4_t tile16(const double* pa, int sa_r, int sa_k, con
 // j > i).  Step J eliminates with the unscaled column, a[i][j] -=
 // a[i][J] a[J][j] / p_J (the same update as with the scaled column of L),
 // and x[i] -= (a[i][J] / p_J) x[J]; the scale 1/sqrt(p_J) of column J of L
-// and of row J of the inverse is applied at the end.  Row J and column J
-// arrive through ds_bpermute, the pivot through readlane.
+// and of row J of the inverse is applied at the end, where the pivots are
+// also checked.  Row J and column J arrive through ds_bpermute, the pivot
+// through readlane.
 __device__ __forceinline__ void diag8(double& a, double& x, int lane, bool& bad_pd, bool& bad_nan) {
     const int i = lane >> 3, j = lane & 7;
     x = (i == j) ? 1.0 : 0.0;
-    double pvi = 1.0, pvj = 1.0;   // pivots of this lane's row and column
+    double pv[8], pu[8];   // pivots as found, and as used (1 in place of a bad one)
 #pragma unroll
     for (int J = 0; J < 8; ++J) {
         const double colr = bperm_f64(a, (lane & ~7) + J);   // a[i][J]
         const double colc = bperm_f64(a, 8 * J + j);         // a[J][j]
         const double xrow = bperm_f64(x, 8 * J + j);         // x[J][j]
-        double piv = readlane_f64(a, 9 * J);
-        if (!(piv > 0.0)) {
-            bad_nan |= isnan(piv);
-            bad_pd |= !isnan(piv);
-            piv = 1.0;
-        }
-        const double cr = (i > J) ? colr * rcp_nr(piv) : 0.0;
+        pv[J] = readlane_f64(a, 9 * J);
+        pu[J] = (pv[J] > 0.0) ? pv[J] : 1.0;
+        const double cr = (i > J) ? colr * rcp_nr(pu[J]) : 0.0;
         a = fma(-cr, (j > J) ? colc : 0.0, a);
         x = fma(-cr, xrow, x);
-        pvi = (i == J) ? piv : pvi;
-        pvj = (j == J) ? piv : pvj;
     }
-    a *= rsqrt_nr(pvj);
-    x *= rsqrt_nr(pvi);
+    double pi = pu[0], pj = pu[0];
+#pragma unroll
+    for (int J = 0; J < 8; ++J) {
+        pi = (i == J) ? pu[J] : pi;
+        pj = (j == J) ? pu[J] : pj;
+        bad_nan |= isnan(pv[J]);
+        bad_pd |= !(pv[J] > 0.0) && !isnan(pv[J]);
+    }
+    a *= rsqrt_nr(pj);
+    x *= rsqrt_nr(pi);
 }
 
 // Factor the 16x16 diagonal block at (b0, b0) of As in place (lower) and

@@ -6,6 +6,12 @@ Cholesky/inverse, the blocked column sweep with lazy updates (4-bit, group
 128), and packing.  Prints one JSON line (see the keys below).
 
     python bench.py [--gpus 1] [--steps 5] [--warmup 2] [--no-cpu-baseline]
+    python bench.py --workload dequant [--steps 5] [--no-cpu-baseline]
+
+The second form measures the product with the packed layer instead (decode:
+one token against the same 4096x11008 layer packed at 4 bits, g128,
+act-order in quantization order, activations gathered through perm); the
+default line carries a short summary of it under "dequant_matmul".
 
 The CPU baseline is the fp64 oracle on a bounded sample of the same layer
 (token, row and column subsets, scaled to weights/s; the sample is stated in
@@ -71,6 +77,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--tokens", type=int, default=None, help="override the token count (testing only)")
+    ap.add_argument("--workload", choices=("quantize", "dequant"), default="quantize")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after timing, run a plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -113,12 +120,133 @@ def cpu_baseline(layer_w, layer_x, d_out, d_in, n_tok, q):
     }
 
 
+DQ_COPIES = 16   # distinct packed layers cycled through (406 MB > the 256 MB last-level cache)
+
+
+def dequant_bytes(d_out, d_in, bits, n_groups, n_tok):
+    """Algorithmic HBM bytes of one product: packed words, scales and zeros,
+    perm, activations (bf16) and outputs (float32), each once."""
+    wpr = -(-(d_in * bits) // 32)
+    return d_out * wpr * 4 + 2 * n_groups * d_out * 4 + d_in * 4 + n_tok * d_in * 2 + n_tok * d_out * 4
+
+
+def dequant_measure(d_out, d_in, bits, gs, token_counts, rounds, cpu=False):
+    """Time gptq_dequant_matmul on DQ_COPIES copies of one packed layer, cycled
+    so that every launch reads its weights from HBM.  Each round of
+    DQ_COPIES launches is captured once in a HIP graph and replayed; HIP
+    events on the replay stream bracket `rounds` replays."""
+    import torch
+
+    import post_weight_quantization_accum_amd as P
+    from post_weight_quantization_accum_amd import synth
+
+    dev = torch.device("cuda:0")
+    n_max = max(token_counts)
+    L = synth.make_packed_layer(d_out, d_in, n_max, bits=bits, group_size=gs, dtype="bf16", seed=4242)
+    codes = torch.from_numpy(L.codes).to(dev)
+    perm = torch.from_numpy(L.perm).to(dev)
+    packed0 = P.pack_permuted(codes, bits, perm)
+    del codes
+    sc0 = torch.from_numpy(L.scales).to(dev)
+    z0 = torch.from_numpy(L.zeros).to(dev)
+    layers = [(packed0.clone(), sc0.clone(), z0.clone(), perm.clone()) for _ in range(DQ_COPIES)]
+    X = torch.from_numpy(L.X.view(np.int16)).view(torch.bfloat16).to(dev)
+    ng = sc0.shape[0]
+    out = {}
+    for n in token_counts:
+        Xn = X[:n]
+        Y = torch.empty((n, d_out), dtype=torch.float32, device=dev)
+
+        def one_round():
+            for pk, sc, z, pm in layers:
+                P.dequant_matmul(Xn, pk, bits, sc, z, perm=pm, group_size=gs, out=Y)
+
+        one_round()
+        torch.cuda.synchronize()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            one_round()
+        torch.cuda.current_stream().wait_stream(s)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            one_round()
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        cur = torch.cuda.current_stream()
+        e0.record(cur)
+        for _ in range(rounds):
+            g.replay()
+        e1.record(cur)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (rounds * DQ_COPIES)
+        # eager launches (ctypes call per product) for comparison
+        e0.record(cur)
+        for _ in range(max(1, rounds // 4)):
+            one_round()
+        e1.record(cur)
+        torch.cuda.synchronize()
+        us_eager = e0.elapsed_time(e1) * 1e3 / (max(1, rounds // 4) * DQ_COPIES)
+        nbytes = dequant_bytes(d_out, d_in, bits, ng, n)
+        out[n] = {"us_per_launch": round(us, 3), "us_per_launch_eager": round(us_eager, 3),
+                  "GBps": round(nbytes / (us * 1e-6) / 1e9, 1), "bytes": nbytes}
+        del g
+    res = {"layer": f"{d_out}x{d_in}", "bits": bits, "group_size": gs, "copies": DQ_COPIES, "rounds": rounds,
+           "by_tokens": out}
+    if cpu:
+        import oracle as O
+        t0 = time.perf_counter()
+        words = O.pack_permuted(L.codes, bits, L.perm)
+        t_pack = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        O.dequant_matmul(L.X_f64()[:1], words, bits, d_in, L.scales, L.zeros, perm=L.perm, group_size=gs)
+        t_mm = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": round(1.0 / t_mm, 4), "unit": "products/s (1 token)",
+                               "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+                               "sample": f"one full 1-token product {d_out}x{d_in} ({t_mm:.2f} s; "
+                                         f"packing in quantization order {t_pack:.2f} s, not counted)"}
+    return res
+
+
+def dequant_main(a):
+    from post_weight_quantization_accum_amd.configs import HEADLINE, layer_spec
+
+    cfg_id, lname = HEADLINE
+    wl, li, d_out, d_in, xl = layer_spec(cfg_id, lname)
+    q = wl.quants[0]
+    rounds = max(10, 20 * a.steps)
+    r = dequant_measure(d_out, d_in, q.bits, q.group_size, (1, 4, 16), rounds, cpu=not a.no_cpu_baseline)
+    d1 = r["by_tokens"][1]
+    ng = -(-d_in // q.group_size)
+    res = {
+        "metric": "W4A16 dequant-GEMM decode (4096x11008, 4-bit g128 act-order, 1 token): HBM GB/s",
+        "value": d1["GBps"], "unit": "GB/s", "n_gpus": 1, "steps": rounds, "warmup": 1,
+        "ms_per_step": round(d1["us_per_launch"] * 1e-3, 6), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16 x / 4-bit codes, f32 accumulate", "data": "synthetic",
+        "config": {"workload": f"product with the packed {d_out}x{d_in} layer, {q.bits}-bit g{q.group_size} "
+                               f"act-order (sorted packing, perm gather), bf16 activations, 1 token; "
+                               f"{DQ_COPIES} layer copies cycled", "d_out": d_out, "d_in": d_in, "tokens": 1},
+        "roofline": {"bound": "hbm", "achieved": d1["GBps"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(d1["GBps"] / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel": "dequant_block_kernel<4,1,bf16>", "launch_us": d1["us_per_launch"],
+                     "algorithmic_bytes_per_launch": dequant_bytes(d_out, d_in, q.bits, ng, 1)},
+        "by_tokens": r["by_tokens"],
+    }
+    if "cpu_baseline" in r:
+        res["cpu_baseline"] = r["cpu_baseline"]
+    print(json.dumps(res))
+
+
 def main():
     a = parse()
     if a.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; "
                                    "--gpus N > 1 is not supported (single-GPU solver)"}))
         sys.exit(2)
+    if a.workload == "dequant":
+        dequant_main(a)
+        return
 
     import torch
 
@@ -234,6 +362,10 @@ def main():
         "roofline": roofline,
     }
     log(f"timed {a.steps} steps: {ms_per_step:.2f} ms/step; phases {res['phases_ms']}")
+    log("product with the packed layer ...")
+    dq = dequant_measure(d_out, d_in, q.bits, q.group_size, (1, 16), 20)
+    res["dequant_matmul"] = {"workload": "1 and 16 tokens x packed 4096x11008 4-bit g128 act-order (sorted), bf16",
+                             "by_tokens": dq["by_tokens"], "peak_GBps": PEAK_HBM_GBS}
     if a.calib_copy_mib:
         src = torch.empty(a.calib_copy_mib << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)

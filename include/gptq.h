@@ -190,6 +190,62 @@ int64_t gptq_packed_words_per_row(int64_t d_in, int32_t bits);
 gptq_status gptq_pack(const uint8_t* codes, int64_t d_out, int64_t d_in, int32_t bits,
                       uint32_t* packed, hipStream_t stream);
 
+/* Packing in a given column order: stream position k of every row holds the
+ * code of column perm[k] ("GPTQ量化算法深度解析" §3.3: with act-order the
+ * columns of a group are scattered, and inference gathers them; packing in
+ * the quantization order makes each group consecutive again, so that
+ * gptq_dequant_matmul gathers activations instead of scales).
+ * perm: device int32[d_in], a permutation of 0..d_in-1 (the perm that
+ * gptq_prepare_hinv returns); an entry outside [0, d_in) packs code 0.
+ * Otherwise as gptq_pack.  Asynchronous. */
+gptq_status gptq_pack_permuted(const uint8_t* codes, int64_t d_out, int64_t d_in, int32_t bits,
+                               const int32_t* perm, uint32_t* packed, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Product with the quantized weights ("通义千问1.5-1.8B-Chat-GPTQ-Int4模型
+ * 压缩技术解析" §2.2: the integer codes with their per-group scale and zero
+ * point are turned back into weights for the computation, activations stay
+ * in 16-bit; "gptq-for-llama" article, "工程细节": matrix products run
+ * directly on the packed words):
+ *
+ *   Y[t][r] = sum_{k < d_in} X[t][a(k)] * scale[g(k)][r] * (c_r(k) - zero[g(k)][r])
+ *
+ * with c_r(k) the code at stream position k of packed row r (the layout of
+ * gptq_pack).  Three forms of the column order:
+ *   perm == NULL, g_idx == NULL: a(k) = k,       g(k) = k / group_size;
+ *   perm == NULL, g_idx != NULL: a(k) = k,       g(k) = g_idx[k]
+ *                                (original order, as gptq_quantize_layer
+ *                                 writes codes and g_idx);
+ *   perm != NULL, g_idx == NULL: a(k) = perm[k], g(k) = k / group_size
+ *                                (words from gptq_pack_permuted, same perm).
+ * group_size <= 0 (or >= d_in): one group, g(k) = 0.
+ *
+ * X: device, n_tok x d_in, row stride ld_x elements, bf16 / f16 / f32.
+ * packed: device uint32, d_out x gptq_packed_words_per_row(d_in, bits).
+ * scales, zeros: device float32 [n_groups][d_out]; zeros hold the integer
+ * zero points.  n_groups: ceil(d_in / group_size) (1 for one group), or with
+ * g_idx the caller's group count (g_idx entries in [0, n_groups)).
+ * Y: device float32, n_tok x d_out, row stride ld_y; overwritten.
+ * Arithmetic: float32 throughout.  With bf16 / f16 activations, no g_idx and
+ * a group size that is a multiple of 32 (or one group), the codes enter
+ * half-precision dot products exactly as 2^bits + c and the offset is
+ * removed per 32 columns in float32 (8-bit codes with bf16 activations take
+ * the per-column route); otherwise each weight is formed once in float32.
+ * Errors (before any launch): GPTQ_ERR_INVALID_ARG for a bad dtype or bits,
+ * sizes outside [0, 2^20] (d_in >= 1), ld_x < d_in, ld_y < d_out, both perm
+ * and g_idx given, an n_groups that does not match, or a null pointer;
+ * GPTQ_ERR_UNSUPPORTED when the per-column route would need more than
+ * gptq_dequant_max_groups() groups.  perm or g_idx entries out of range are
+ * not read through: they make the affected outputs NaN.  n_tok == 0 or
+ * d_out == 0: nothing is launched.  Asynchronous on `stream`; no allocation.
+ * ------------------------------------------------------------------------ */
+int64_t gptq_dequant_max_groups(void);
+gptq_status gptq_dequant_matmul(const void* X, gptq_dtype x_dtype, int64_t n_tok, int64_t d_in,
+                                int64_t ld_x, const uint32_t* packed, int32_t bits,
+                                const float* scales, const float* zeros, int64_t n_groups,
+                                const int32_t* g_idx, const int32_t* perm, int32_t group_size,
+                                int64_t d_out, float* Y, int64_t ld_y, hipStream_t stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* gptq_status_string(gptq_status status);
 

@@ -26,6 +26,8 @@ from .gptq_oracle import (  # noqa: F401
     gptq_quantize,
     pack,
     unpack,
+    pack_permuted,
+    dequant_matmul,
     dequantize,
     layer_loss,
     words_per_row,

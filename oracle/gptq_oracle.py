@@ -18,7 +18,10 @@ Sources, cited by page title and section:
 * ai.lansai.wang GPTQ guide, section "bits、group_size、sym 与 desc_act
   分别影响什么" (the quantize_config field table).
 * "gptq-for-llama" article (ainews.cool), "工程细节" (four 4-bit codes packed
-  per 16-bit integer).
+  per 16-bit integer; matrix products run on the packed codes).
+* Inference with the packed layer: "通义千问..." §2.2 (codes are turned back
+  into weights with their group's scale and zero point for the computation)
+  and "GPTQ量化算法深度解析" §3.3 (act-order costs a gather at inference).
 
 Notation: W is d_out x d_in (row = output channel, column = input channel);
 X is tokens x d_in; b = bits, maxq = 2^b - 1; g = group size; B = block size.
@@ -390,3 +393,51 @@ def unpack(words: np.ndarray, bits: int, d_in: int) -> np.ndarray:
             v |= w[:, wi + 1] << np.uint64(32 - sh)
         out[:, k] = (v & mask).astype(np.int64)
     return out
+
+
+# ---------------------------------------------------------------------------
+# Inference: the product with the packed layer.
+# ---------------------------------------------------------------------------
+
+def pack_permuted(codes: np.ndarray, bits: int, perm) -> np.ndarray:
+    """Pack the columns in the order perm: stream position k of every row
+    holds the code of column perm[k].
+
+    With act-order ("GPTQ量化算法深度解析" §3.3) the columns of one group are
+    scattered over the original order; in the quantization order they are
+    consecutive again, and inference gathers the activations instead.
+    """
+    return pack(np.asarray(codes)[:, np.asarray(perm)], bits)
+
+
+def dequant_matmul(X, words, bits: int, d_in: int, scales, zeros, *, g_idx=None,
+                   perm=None, group_size: int = -1) -> np.ndarray:
+    """Y = X W_hat^T with W_hat read back from packed words, in float64.
+
+    "通义千问..." §2.2: the integer codes with the per-group scale and zero
+    point are turned back into weights (W_hat = scale * (code - zero)) for the
+    computation, the activations keep their precision; "gptq-for-llama"
+    article, "工程细节": the product runs on the packed codes.
+
+    Stream position k of a packed row holds the code of activation column
+    a(k), in group g(k):
+      g_idx given:  a(k) = k,       g(k) = g_idx[k]   (original order);
+      perm given:   a(k) = perm[k], g(k) = k // group_size (sorted order);
+      neither:      a(k) = k,       g(k) = k // group_size.
+    group_size <= 0 (or >= d_in) means one group.  X: tokens x d_in.
+    """
+    if g_idx is not None and perm is not None:
+        raise InvalidArgument("give g_idx or perm, not both")
+    codes = unpack(words, bits, d_in)
+    k = np.arange(d_in)
+    if g_idx is not None:
+        g = np.asarray(g_idx, dtype=np.int64)
+    elif 0 < group_size < d_in:
+        g = k // group_size
+    else:
+        g = np.zeros(d_in, dtype=np.int64)
+    W_stream = dequantize(codes, scales, zeros, g)
+    X64 = np.asarray(X, dtype=np.float64)
+    if perm is not None:
+        X64 = X64[:, np.asarray(perm, dtype=np.int64)]
+    return X64 @ W_stream.T

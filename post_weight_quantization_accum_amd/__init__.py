@@ -19,7 +19,8 @@ from ._lib import (  # noqa: F401
 )
 
 __all__ = ["hessian_accumulate", "hessian_accumulate_timed", "prepare_hinv", "quantize_layer", "pack", "quantize",
-           "packed_words_per_row", "make_config", "Config", "load"]
+           "pack_permuted", "dequant_matmul", "dequant_max_groups", "packed_words_per_row", "make_config",
+           "Config", "load"]
 
 
 def _torch():
@@ -178,6 +179,65 @@ def pack(codes, bits: int, out=None, stream=None):
         out = torch.empty((d_out, wpr), dtype=torch.int32, device=codes.device)
     st = lib.gptq_pack(_ptr(codes), d_out, d_in, bits, _ptr(out), _stream(stream))
     _lib.check(st, "gptq_pack")
+    return out
+
+
+def pack_permuted(codes, bits: int, perm, out=None, stream=None):
+    """Pack with stream position k of every row holding column perm[k]."""
+    lib = load()
+    torch = _torch()
+    _require_cuda(codes, perm)
+    if codes.dtype != torch.uint8 or not codes.is_contiguous():
+        raise TypeError("codes must be contiguous uint8")
+    d_out, d_in = codes.shape
+    if perm.dtype != torch.int32 or perm.numel() != d_in or not perm.is_contiguous():
+        raise TypeError("perm must be contiguous int32 of length d_in")
+    wpr = packed_words_per_row(d_in, bits)
+    if out is None:
+        out = torch.empty((d_out, wpr), dtype=torch.int32, device=codes.device)
+    st = lib.gptq_pack_permuted(_ptr(codes), d_out, d_in, bits, _ptr(perm), _ptr(out), _stream(stream))
+    _lib.check(st, "gptq_pack_permuted")
+    return out
+
+
+def dequant_max_groups() -> int:
+    return int(load().gptq_dequant_max_groups())
+
+
+def dequant_matmul(X, packed, bits: int, scales, zeros, *, g_idx=None, perm=None, group_size: int = -1,
+                   out=None, stream=None):
+    """Y = X W_hat^T (float32, tokens x d_out) straight from packed words.
+
+    X: tokens x d_in (bf16 / f16 / f32, unit column stride); packed: d_out x
+    words-per-row int32/uint32 words; scales, zeros: [n_groups][d_out] float32.
+    g_idx (original order) or perm (words from pack_permuted) select the
+    column order, as in gptq_dequant_matmul.
+    """
+    lib = load()
+    torch = _torch()
+    _require_cuda(X, packed, scales, zeros, g_idx, perm)
+    if X.dim() != 2 or X.stride(1) != 1:
+        raise ValueError("X must be 2-D with unit column stride")
+    n_tok, d_in = X.shape
+    if packed.dim() != 2 or not packed.is_contiguous() or packed.element_size() != 4:
+        raise TypeError("packed must be a contiguous 2-D tensor of 32-bit words")
+    d_out = packed.shape[0]
+    if packed.shape[1] != packed_words_per_row(d_in, bits):
+        raise ValueError("packed has the wrong number of words per row")
+    for name, t in (("scales", scales), ("zeros", zeros)):
+        if t.dtype != torch.float32 or not t.is_contiguous() or t.dim() != 2 or t.shape[1] != d_out:
+            raise TypeError(f"{name} must be contiguous float32 [n_groups][d_out]")
+    for name, t in (("g_idx", g_idx), ("perm", perm)):
+        if t is not None and (t.dtype != torch.int32 or t.numel() != d_in or not t.is_contiguous()):
+            raise TypeError(f"{name} must be contiguous int32 of length d_in")
+    if out is None:
+        out = torch.empty((n_tok, d_out), dtype=torch.float32, device=X.device)
+    if out.dtype != torch.float32 or out.dim() != 2 or out.stride(1) != 1 or out.shape != (n_tok, d_out):
+        raise TypeError("out must be float32 tokens x d_out with unit column stride")
+    st = lib.gptq_dequant_matmul(_ptr(X), _dtype_code(X), n_tok, d_in, X.stride(0), _ptr(packed), bits,
+                                 _ptr(scales), _ptr(zeros), scales.shape[0], _ptr(g_idx), _ptr(perm),
+                                 int(group_size), d_out, _ptr(out), out.stride(0), _stream(stream))
+    _lib.check(st, "gptq_dequant_matmul")
     return out
 
 

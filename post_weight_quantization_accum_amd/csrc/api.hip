@@ -155,7 +155,33 @@ gptq_status gptq_pack(const uint8_t* codes, int64_t d_out, int64_t d_in, int32_t
                       hipStream_t stream) {
     if (!codes || !packed || !valid_bits(bits)) return GPTQ_ERR_INVALID_ARG;
     if (d_out <= 0 || d_in <= 0 || d_out > MAX_DIM || d_in > MAX_DIM) return GPTQ_ERR_INVALID_ARG;
-    return pack_launch(codes, d_out, d_in, bits, packed, stream);
+    return pack_launch(codes, d_out, d_in, bits, nullptr, packed, stream);
+}
+
+gptq_status gptq_pack_permuted(const uint8_t* codes, int64_t d_out, int64_t d_in, int32_t bits, const int32_t* perm,
+                               uint32_t* packed, hipStream_t stream) {
+    if (!codes || !packed || !perm || !valid_bits(bits)) return GPTQ_ERR_INVALID_ARG;
+    if (d_out <= 0 || d_in <= 0 || d_out > MAX_DIM || d_in > MAX_DIM) return GPTQ_ERR_INVALID_ARG;
+    return pack_launch(codes, d_out, d_in, bits, perm, packed, stream);
+}
+
+int64_t gptq_dequant_max_groups(void) { return dequant_max_groups(); }
+
+gptq_status gptq_dequant_matmul(const void* X, gptq_dtype x_dtype, int64_t n_tok, int64_t d_in, int64_t ld_x,
+                                const uint32_t* packed, int32_t bits, const float* scales, const float* zeros,
+                                int64_t n_groups, const int32_t* g_idx, const int32_t* perm, int32_t group_size,
+                                int64_t d_out, float* Y, int64_t ld_y, hipStream_t stream) {
+    if (!valid_dtype(x_dtype) || !valid_bits(bits)) return GPTQ_ERR_INVALID_ARG;
+    if (n_tok < 0 || d_in <= 0 || d_out < 0 || n_tok > MAX_DIM || d_in > MAX_DIM || d_out > MAX_DIM)
+        return GPTQ_ERR_INVALID_ARG;
+    if (ld_x < d_in || ld_y < d_out) return GPTQ_ERR_INVALID_ARG;
+    if (g_idx && perm) return GPTQ_ERR_INVALID_ARG;
+    const int64_t expect = (group_size > 0) ? ceil_div(d_in, group_size) : 1;
+    if (g_idx ? (n_groups < 1 || n_groups > d_in) : (n_groups != expect)) return GPTQ_ERR_INVALID_ARG;
+    if (n_tok == 0 || d_out == 0) return GPTQ_OK;
+    if (!X || !packed || !scales || !zeros || !Y) return GPTQ_ERR_INVALID_ARG;
+    return dequant_matmul_launch(X, x_dtype, n_tok, d_in, ld_x, packed, bits, scales, zeros, n_groups, g_idx, perm,
+                                 group_size, d_out, Y, ld_y, stream);
 }
 
 }  // extern "C"

@@ -72,7 +72,17 @@ gptq_status sweep_launch(const void* W, gptq_dtype dt, int64_t d_out, int64_t d_
                          float* w_hat, double* row_loss, void* ws, hipStream_t s,
                          int* host_flags);
 
-gptq_status pack_launch(const uint8_t* codes, int64_t d_out, int64_t d_in, int32_t bits,
+// perm: null (stream order = column order) or stream position -> column.
+gptq_status pack_launch(const uint8_t* codes, int64_t d_out, int64_t d_in, int32_t bits, const int32_t* perm,
                         uint32_t* packed, hipStream_t s);
+
+// Y = X W_hat^T from packed words (dequant.hip).  perm and g_idx as in
+// gptq_dequant_matmul; arguments already validated.
+int64_t dequant_max_groups();
+bool dequant_uses_block_path(gptq_dtype dt, int32_t bits, int64_t d_in, int64_t group_size, bool has_g_idx);
+gptq_status dequant_matmul_launch(const void* X, gptq_dtype dt, int64_t n_tok, int64_t d_in, int64_t ld_x,
+                                  const uint32_t* packed, int32_t bits, const float* scales, const float* zeros,
+                                  int64_t n_groups, const int32_t* g_idx, const int32_t* perm, int64_t group_size,
+                                  int64_t d_out, float* Y, int64_t ld_y, hipStream_t s);
 
 }  // namespace gptq

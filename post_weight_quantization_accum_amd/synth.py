@@ -24,6 +24,14 @@ even to the layer's dtype):
 
 Seeds: seed_w = 1000*config + 10*layer, seed_x = seed_w + 1,
 seed_o = seed_w + 2.
+
+Packed layers (inputs of the product with quantized weights), from
+``Generator(PCG64(seed))`` in this order: codes uniform on [0, 2^bits)
+(uint8, d_out x d_in); scales log-uniform on [1e-3, 5e-2] (float32,
+[n_groups][d_out]); zero points uniform integers on [0, 2^bits) (stored as
+float32); a uniformly random permutation of the d_in columns (int32, the
+column order of an act-order layer).  Activations: ``gen_activations`` with
+seed + 1 (Student-t, 1% outlier channels x 20 by default).
 """
 from __future__ import annotations
 
@@ -166,3 +174,33 @@ def make_layer(d_out: int, d_in: int, n_tok: int, *, dtype: str, sigma_w: float,
                                       outlier_scale=outlier_scale, seed_outliers=seed_x + 1,
                                       threads=threads)
     return Layer(W=W, X=X, dtype=dtype, outliers=outl, clamps=clamps)
+
+
+@dataclasses.dataclass
+class PackedLayer:
+    """Host arrays of a quantized layer: integer codes (uint8 d_out x d_in),
+    scales and zeros (float32 [n_groups][d_out]), a column permutation
+    (int32 d_in) and activations ``X`` in the stored form of ``dtype``."""
+    codes: np.ndarray
+    scales: np.ndarray
+    zeros: np.ndarray
+    perm: np.ndarray
+    X: np.ndarray
+    dtype: str
+
+    def X_f64(self) -> np.ndarray:
+        return to_f64(self.X, self.dtype)
+
+
+def make_packed_layer(d_out: int, d_in: int, n_tok: int, *, bits: int, group_size: int, dtype: str,
+                      dist: str = "t4", outlier_frac: float = 0.01, outlier_scale: float = 20.0,
+                      seed: int = 0) -> PackedLayer:
+    rng = np.random.Generator(np.random.PCG64(seed))
+    n_groups = -(-d_in // group_size) if 0 < group_size < d_in else 1
+    codes = rng.integers(0, 1 << bits, size=(d_out, d_in), dtype=np.uint8)
+    scales = np.exp(rng.uniform(np.log(1e-3), np.log(5e-2), size=(n_groups, d_out))).astype(np.float32)
+    zeros = rng.integers(0, 1 << bits, size=(n_groups, d_out)).astype(np.float32)
+    perm = rng.permutation(d_in).astype(np.int32)
+    X, _, _ = gen_activations(n_tok, d_in, dist, dtype, seed + 1, outlier_frac=outlier_frac,
+                              outlier_scale=outlier_scale)
+    return PackedLayer(codes=codes, scales=scales, zeros=zeros, perm=perm, X=X, dtype=dtype)

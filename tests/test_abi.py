@@ -86,6 +86,41 @@ def test_argument_validation_before_any_launch():
     assert lib.gptq_pack(n, 4, 8, 4, fake, n) == _lib.ERR_INVALID_ARG
     assert lib.gptq_pack(fake, 4, 8, 5, fake, n) == _lib.ERR_INVALID_ARG
     assert lib.gptq_pack(fake, 0, 8, 4, fake, n) == _lib.ERR_INVALID_ARG
+    assert lib.gptq_pack_permuted(fake, 4, 8, 4, n, fake, n) == _lib.ERR_INVALID_ARG  # perm missing
+    assert lib.gptq_pack_permuted(fake, 4, 8, 3 + 3, fake, fake, n) == _lib.ERR_INVALID_ARG
+
+
+def _dq(**kw):
+    # gptq_dequant_matmul with valid arguments unless overridden
+    fake = ctypes.c_void_p(0x1000)
+    a = dict(X=fake, dt=2, n_tok=1, d_in=256, ld_x=256, packed=fake, bits=4, scales=fake, zeros=fake,
+             n_groups=2, g_idx=None, perm=None, gs=128, d_out=64, Y=fake, ld_y=64)
+    a.update(kw)
+    return P.load().gptq_dequant_matmul(a["X"], a["dt"], a["n_tok"], a["d_in"], a["ld_x"], a["packed"], a["bits"],
+                                        a["scales"], a["zeros"], a["n_groups"], a["g_idx"], a["perm"], a["gs"],
+                                        a["d_out"], a["Y"], a["ld_y"], None)
+
+
+def test_dequant_matmul_validation_before_any_launch():
+    fake = ctypes.c_void_p(0x1000)
+    assert P.dequant_max_groups() == 2048
+    assert _dq(bits=5) == _lib.ERR_INVALID_ARG
+    assert _dq(dt=7) == _lib.ERR_INVALID_ARG
+    assert _dq(ld_x=255) == _lib.ERR_INVALID_ARG
+    assert _dq(ld_y=63) == _lib.ERR_INVALID_ARG
+    assert _dq(d_in=0) == _lib.ERR_INVALID_ARG
+    assert _dq(n_tok=-1) == _lib.ERR_INVALID_ARG
+    assert _dq(g_idx=fake, perm=fake) == _lib.ERR_INVALID_ARG
+    assert _dq(n_groups=3) == _lib.ERR_INVALID_ARG            # ceil(256 / 128) = 2
+    assert _dq(gs=-1, n_groups=2) == _lib.ERR_INVALID_ARG     # one group
+    assert _dq(g_idx=fake, n_groups=0) == _lib.ERR_INVALID_ARG
+    assert _dq(X=None) == _lib.ERR_INVALID_ARG
+    assert _dq(Y=None) == _lib.ERR_INVALID_ARG
+    # the per-column route keeps [group][row] scales of 8 rows in LDS: bounded group count
+    assert _dq(d_in=8192, ld_x=8192, g_idx=fake, n_groups=4096) == _lib.ERR_UNSUPPORTED
+    # empty products launch nothing
+    assert _dq(n_tok=0) == _lib.OK
+    assert _dq(d_out=0, ld_y=0) == _lib.OK
 
 
 def test_python_errors_map_status():

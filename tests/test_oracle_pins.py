@@ -425,3 +425,78 @@ def test_gptq_not_worse_than_rtn_on_correlated_inputs():
     assert out["loss"].sum() < 0.5 * O.layer_loss(W, rtn, H).sum()
     out8 = O.gptq_quantize(W, H, bits=8, group_size=-1, block=16)
     assert out8["loss"].sum() < 1e-3 * out["loss"].sum()
+
+
+# ---------------------------------------------------------------------------
+# Product with the packed layer (inference side of the packed format).
+# ---------------------------------------------------------------------------
+
+def test_dequant_matmul_hand_example():
+    g = _load("dequant_hand.json")
+    codes = np.array(g["codes"])
+    words = O.pack(codes, g["bits"])
+    assert words.shape == (1, 1) and int(words[0, 0]) == int(g["word_hex"], 16)
+    n = codes.shape[1]
+    g_idx = np.arange(n) // g["group_size"]
+    W_hat = O.dequantize(codes, np.array(g["scales"]), np.array(g["zeros"]), g_idx)
+    assert np.array_equal(W_hat, np.array(g["w_hat"]))
+    for kw in (dict(group_size=g["group_size"]), dict(g_idx=g_idx)):
+        y = O.dequant_matmul(np.array(g["x"]), words, g["bits"], n, np.array(g["scales"]),
+                             np.array(g["zeros"]), **kw)
+        assert np.array_equal(y, np.array(g["y"]))
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+def test_dequant_matmul_unit_tokens_brute_force(bits):
+    # one-hot tokens pick single columns: Y[j, r] is the weight of column j in
+    # row r, checked element by element from the integer codes (no unpacking)
+    rng = np.random.default_rng(300 + bits)
+    d_out, d_in, n_groups = 5, 37, 4
+    codes = rng.integers(0, 1 << bits, size=(d_out, d_in))
+    g_idx = rng.integers(0, n_groups, size=d_in)
+    scales = rng.uniform(0.01, 2.0, size=(n_groups, d_out))
+    zeros = rng.integers(0, 1 << bits, size=(n_groups, d_out)).astype(np.float64)
+    Y = O.dequant_matmul(np.eye(d_in), O.pack(codes, bits), bits, d_in, scales, zeros, g_idx=g_idx)
+    for j in range(d_in):
+        for r in range(d_out):
+            want = scales[g_idx[j], r] * (int(codes[r, j]) - zeros[g_idx[j], r])
+            assert Y[j, r] == want
+
+
+def test_dequant_matmul_integer_exact():
+    # integer activations, unit scales: every sum is an exact integer,
+    # compared with Python integers
+    rng = np.random.default_rng(311)
+    bits, d_out, d_in, gs = 3, 4, 50, 16
+    codes = rng.integers(0, 8, size=(d_out, d_in))
+    ng = -(-d_in // gs)
+    zeros = rng.integers(0, 8, size=(ng, d_out)).astype(np.float64)
+    X = rng.integers(-9, 10, size=(3, d_in)).astype(np.float64)
+    Y = O.dequant_matmul(X, O.pack(codes, bits), bits, d_in, np.ones((ng, d_out)), zeros, group_size=gs)
+    for t in range(3):
+        for r in range(d_out):
+            want = sum(int(X[t, j]) * (int(codes[r, j]) - int(zeros[j // gs, r])) for j in range(d_in))
+            assert Y[t, r] == want
+
+
+@pytest.mark.parametrize("bits,gs", [(4, 16), (3, 8), (2, -1)])
+def test_dequant_matmul_reproduces_solver_weights(bits, gs):
+    # the packed words with scales/zeros/g_idx reproduce the weights the
+    # column sweep chose (w_hat = scale*(code - zero) taken inside the sweep),
+    # in the original order with g_idx and in the sorted order with perm
+    rng = np.random.default_rng(320 + bits)
+    d_out, d_in = 6, 48
+    X = rng.standard_normal((200, d_in)) * np.exp(rng.standard_normal(d_in))
+    W = rng.standard_normal((d_out, d_in))
+    out = O.gptq_quantize(W, X=X, bits=bits, group_size=gs, act_order=True, block=16)
+    assert not np.array_equal(out["perm"], np.arange(d_in))
+    want = X @ out["w_hat"].T
+    y1 = O.dequant_matmul(X, O.pack(out["codes"], bits), bits, d_in, out["scales"], out["zeros"],
+                          g_idx=out["g_idx"])
+    y2 = O.dequant_matmul(X, O.pack_permuted(out["codes"], bits, out["perm"]), bits, d_in, out["scales"],
+                          out["zeros"], perm=out["perm"], group_size=gs)
+    np.testing.assert_allclose(y1, want, rtol=1e-12, atol=1e-12 * np.abs(want).max())
+    np.testing.assert_allclose(y2, want, rtol=1e-12, atol=1e-12 * np.abs(want).max())
+    # sorted packing = packing of the permuted code matrix, read back position by position
+    back = O.unpack(O.pack_permuted(out["codes"], bits, out["perm"]), bits, d_in)
+    assert np.array_equal(back, out["codes"][:, out["perm"]])

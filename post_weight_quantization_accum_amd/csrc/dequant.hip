@@ -57,7 +57,6 @@ struct DqArgs {
     float* Y;
     int64_t ld_y;
     int xvec;                    // X 16-byte aligned rows (bf16 / f16 only)
-    int wvec;                    // packed rows aligned for vector word loads
 };
 
 // Activation storage types: raw 16-bit patterns for bf16 and f16, float for f32.
@@ -114,6 +113,14 @@ __device__ __forceinline__ int pair_col_b(int i) {
     }
 }
 
+// (x & m) | c in one instruction (VOP3 v_and_or_b32: the mask from an SGPR,
+// the exponent bits from a VGPR).
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t m, uint32_t c) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(m), "v"(c));
+    return r;
+}
+
 // Pair i of one row's block as two half-precision values (2^b + c_a, 2^b + c_b).
 template <int BITS, typename T>
 __device__ __forceinline__ uint32_t code_pair(const uint32_t (&w)[BITS], int i) {
@@ -129,38 +136,52 @@ __device__ __forceinline__ uint32_t code_pair(const uint32_t (&w)[BITS], int i) 
         constexpr uint32_t M1 = ((1u << BITS) - 1u) << SH;
         constexpr uint32_t MASK = M1 | (M1 << 16);
         const int m = i / H, p = BITS * (i % H);
-        const uint32_t v = (p >= SH) ? (w[m] >> (p - SH)) : (w[m] << (SH - p));
-        return (v & MASK) | EXPO;
+        const uint32_t v = (p == SH) ? w[m] : ((p > SH) ? (w[m] >> (p - SH)) : (w[m] << (SH - p)));
+        return and_or(v, MASK, EXPO);
     }
 }
 
-// The `bits` words of block blk of one row (zeros past the row's end).
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x3_t __attribute__((ext_vector_type(3)));
+
+// Buffer resource over the packed rows from r0 to the end of the matrix (at
+// most 2 GiB: a workgroup reads 8 rows).  Offsets past its end read zeros,
+// so the loads need no branches: rows past d_out read zeros, and a block
+// that runs past the end of a row reads words of the next row, which meet
+// activations that are zero there.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t words_rsrc(const DqArgs& a, int64_t r0) {
+    const int64_t bytes = (a.d_out - r0) * a.wpr * 4;
+    const int n = bytes > 0x7FFFFFF0 ? 0x7FFFFFF0 : (int)bytes;
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(a.packed + r0 * a.wpr), (short)0, n, 0x00020000);
+}
+
+// the `bits` words of block blk of the 8 rows
 template <int BITS>
-__device__ __forceinline__ void load_words(const DqArgs& a, int64_t row, bool row_ok, int64_t blk,
-                                           uint32_t (&w)[BITS]) {
-    const int64_t w0 = blk * BITS;
-    const uint32_t* p = a.packed + row * a.wpr + w0;
-    if (row_ok && a.wvec && w0 + BITS <= a.wpr) {
-        if constexpr (BITS == 2) {
-            const uint2 v = *(const uint2*)p;
-            w[0] = v.x;
-            w[1] = v.y;
-        } else if constexpr (BITS == 4 || BITS == 8) {
+__device__ __forceinline__ void load_block_words(__amdgpu_buffer_rsrc_t rs, uint32_t row_bytes, uint32_t blk,
+                                                 uint32_t (&w)[RW][BITS]) {
+    const uint32_t off = blk * (uint32_t)(BITS * 4);
 #pragma unroll
-            for (int q = 0; q < BITS; q += 4) {
-                const uint4 v = *(const uint4*)(p + q);
-                w[q] = v.x;
-                w[q + 1] = v.y;
-                w[q + 2] = v.z;
-                w[q + 3] = v.w;
-            }
+    for (int rr = 0; rr < RW; ++rr) {
+        const uint32_t o = off + (uint32_t)rr * row_bytes;
+        if constexpr (BITS == 2) {
+            const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(rs, o, 0, 0);
+            w[rr][0] = v.x;
+            w[rr][1] = v.y;
+        } else if constexpr (BITS == 3) {
+            const u32x3_t v = __builtin_amdgcn_raw_buffer_load_b96(rs, o, 0, 0);
+            w[rr][0] = v.x;
+            w[rr][1] = v.y;
+            w[rr][2] = v.z;
         } else {
 #pragma unroll
-            for (int q = 0; q < BITS; ++q) w[q] = p[q];
+            for (int q = 0; q < BITS; q += 4) {
+                const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rs, o + 4 * q, 0, 0);
+                w[rr][q] = v.x;
+                w[rr][q + 1] = v.y;
+                w[rr][q + 2] = v.z;
+                w[rr][q + 3] = v.w;
+            }
         }
-    } else {
-#pragma unroll
-        for (int q = 0; q < BITS; ++q) w[q] = (row_ok && w0 + q < a.wpr) ? p[q] : 0u;
     }
 }
 
@@ -230,6 +251,8 @@ __global__ __launch_bounds__(DQ_THREADS) void dequant_block_kernel(DqArgs a) {
     const int nt = (a.n_tok - t0 < TM) ? (int)(a.n_tok - t0) : TM;
     const uint16_t* X = (const uint16_t*)a.X;
     constexpr float OFF = (float)(1 << BITS);
+    const __amdgpu_buffer_rsrc_t rs = words_rsrc(a, r0);
+    const uint32_t row_bytes = (uint32_t)a.wpr * 4;
 
     float acc[TM][RW];
 #pragma unroll
@@ -241,8 +264,7 @@ __global__ __launch_bounds__(DQ_THREADS) void dequant_block_kernel(DqArgs a) {
     for (int64_t blk = tid; blk < nblk; blk += DQ_THREADS) {
         const int64_t j0 = blk * 32;
         uint32_t wd[RW][BITS];
-#pragma unroll
-        for (int rr = 0; rr < RW; ++rr) load_words<BITS>(a, r0 + rr, rr < nr, blk, wd[rr]);
+        load_block_words<BITS>(rs, row_bytes, (uint32_t)blk, wd);
         const int64_t g = j0 / a.gsize;
         float sv[RW], ov[RW];
 #pragma unroll
@@ -324,6 +346,8 @@ __global__ __launch_bounds__(DQ_THREADS) void dequant_col_kernel(DqArgs a) {
     const int64_t r0 = (int64_t)blockIdx.x * RW, t0 = blockIdx.y;
     const int nr = (a.d_out - r0 < RW) ? (int)(a.d_out - r0) : RW;
     const typename T::store* xr = (const typename T::store*)a.X + t0 * a.ld_x;
+    const __amdgpu_buffer_rsrc_t rs = words_rsrc(a, r0);
+    const uint32_t row_bytes = (uint32_t)a.wpr * 4;
     float* s_lds = sz;
     float* z_lds = sz + a.n_groups * RW;
     for (int64_t e = tid; e < a.n_groups * RW; e += DQ_THREADS) {
@@ -342,8 +366,7 @@ __global__ __launch_bounds__(DQ_THREADS) void dequant_col_kernel(DqArgs a) {
     for (int64_t blk = tid; blk < nblk; blk += DQ_THREADS) {
         const int64_t j0 = blk * 32;
         uint32_t wd[RW][BITS];
-#pragma unroll
-        for (int rr = 0; rr < RW; ++rr) load_words<BITS>(a, r0 + rr, rr < nr, blk, wd[rr]);
+        load_block_words<BITS>(rs, row_bytes, (uint32_t)blk, wd);
         // group (LDS row offset) and activation of each column of the block
         int32_t gk[32];
         float xk[32];
@@ -398,10 +421,353 @@ gptq_status launch_col(const DqArgs& a, hipStream_t s) {
     return GPTQ_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Block route with the activations and the group parameters staged in LDS.
+//
+// Each workgroup first copies, with coalesced loads, the scales and
+// (2^b + zero) of its 8 rows ([group][row] floats) and the activations of its
+// tokens in stream order (gathered through perm when given: the activation
+// row goes to LDS whole, then each stream position reads its column from
+// there) into LDS; 32-column blocks sit 80 bytes apart, which keeps the
+// 16-byte LDS reads of consecutive lanes on distinct banks.  The lanes then
+// read only their packed words from global memory (one block ahead) and
+// everything else from LDS.  Used whenever the staging fits in LDS.
+// ---------------------------------------------------------------------------
+constexpr int XS_STRIDE = 40;                   // 16-bit slots per 32-column block (64 B + 16 B pad)
+constexpr size_t STAGED_LDS_MAX = 150 * 1024;
+
+struct StagedLayout {
+    size_t o_off, xs_off, xf_off, total;
+};
+
+__host__ __device__ inline StagedLayout staged_layout(int64_t n_groups, int64_t nblk, int64_t d_in, int tm,
+                                                      bool perm) {
+    StagedLayout L;
+    L.o_off = (size_t)n_groups * 2 * RW * sizeof(float);
+    L.xs_off = align_up(2 * L.o_off, 16);
+    L.xf_off = L.xs_off + align_up((size_t)tm * nblk * XS_STRIDE * 2, 16);
+    L.total = L.xf_off + (perm ? align_up((size_t)d_in * 2, 16) : 0);
+    return L;
+}
+
+// One activation row (d_in 16-bit values, zeros up to n) from global memory
+// into LDS: element k goes to dst[(k / 32) * XS_STRIDE + k % 32] (blocked) or
+// dst[k] (flat).  Loads are issued in batches (clamped addresses, unused
+// values dropped) so that their latencies overlap.
+template <bool BLOCKED>
+__device__ __forceinline__ uint16_t* slot(uint16_t* dst, uint32_t k) {
+    return BLOCKED ? dst + (k >> 5) * XS_STRIDE + (k & 31) : dst + k;
+}
+
+// skip_pc: whole pieces [0, skip_pc) are already stored (vector route only).
+template <bool BLOCKED, int NT>
+__device__ __forceinline__ void copy_row(const DqArgs& a, const uint16_t* __restrict__ xr, uint16_t* dst,
+                                         uint32_t n, int tid, uint32_t skip_pc) {
+    const uint32_t d_in = (uint32_t)a.d_in;
+    uint32_t done = 0;
+    if (a.xvec) {
+        // whole 16-byte pieces of 8 columns
+        const uint32_t npc = d_in / 8;
+        constexpr int B = 8;
+        for (uint32_t p0 = skip_pc + tid; p0 < npc; p0 += NT * B) {
+            uint4 v[B];
+#pragma unroll
+            for (int i = 0; i < B; ++i) {
+                const uint32_t p = p0 + NT * i;
+                v[i] = *(const uint4*)(xr + 8 * (p < npc ? p : 0));
+            }
+#pragma unroll
+            for (int i = 0; i < B; ++i) {
+                const uint32_t p = p0 + NT * i;
+                if (p < npc) *(uint4*)slot<BLOCKED>(dst, 8 * p) = v[i];
+            }
+        }
+        done = 8 * npc;
+    }
+    constexpr int B = 8;
+    for (uint32_t k0 = done + tid; k0 < n; k0 += NT * B) {
+        uint16_t v[B];
+#pragma unroll
+        for (int i = 0; i < B; ++i) {
+            const uint32_t k = k0 + NT * i;
+            v[i] = xr[k < d_in ? k : 0];
+        }
+#pragma unroll
+        for (int i = 0; i < B; ++i) {
+            const uint32_t k = k0 + NT * i;
+            if (k < n) *slot<BLOCKED>(dst, k) = k < d_in ? v[i] : (uint16_t)0;
+        }
+    }
+}
+
+// 512 threads: two halves of 256 lanes, each half owning 8 of the
+// workgroup's 16 rows and sharing the staged activations.
+constexpr int ST_THREADS = 512;
+constexpr int ST_ROWS = 2 * RW;
+
+template <int BITS, int TM, typename T>
+__global__ __launch_bounds__(ST_THREADS) void dequant_staged_kernel(DqArgs a) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    __shared__ float red[ST_THREADS / 64][64];
+    const int tid = threadIdx.x, half = tid >> 8;
+    // lane index within the half; the second half counts down, so that lanes
+    // with one block more than the others (the low lane indices) sit in waves
+    // 0-1 of the first half and waves 6-7 of the second: on different SIMDs
+    const int tl = half ? 255 - (tid & 255) : tid;
+    const int64_t rw0 = (int64_t)blockIdx.x * ST_ROWS;              // first row of the workgroup
+    const int64_t r0 = rw0 + half * RW;                             // first row of this half
+    const int nrw = (a.d_out - rw0 < ST_ROWS) ? (int)(a.d_out - rw0) : ST_ROWS;
+    const int nr = (a.d_out - r0 < RW) ? (a.d_out - r0 > 0 ? (int)(a.d_out - r0) : 0) : RW;
+    const int64_t t0 = (int64_t)blockIdx.y * TM;
+    const int nt = (a.n_tok - t0 < TM) ? (int)(a.n_tok - t0) : TM;
+    const uint32_t nblk = (uint32_t)ceil_div(a.d_in, 32);
+    const StagedLayout Ly = staged_layout(a.n_groups, nblk, a.d_in, TM, a.perm != nullptr);
+    float* s_l = (float*)lds;                                       // [group][16] scales
+    float* o_l = (float*)(lds + Ly.o_off);                          // [group][16] 2^b + zero
+    uint16_t* xs = (uint16_t*)(lds + Ly.xs_off);
+    uint16_t* xf = (uint16_t*)(lds + Ly.xf_off);
+    const uint16_t* X = (const uint16_t*)a.X;
+    constexpr float OFF = (float)(1 << BITS);
+    const __amdgpu_buffer_rsrc_t rs = words_rsrc(a, r0 < a.d_out ? r0 : a.d_out);
+    const uint32_t row_bytes = (uint32_t)a.wpr * 4;
+    const uint32_t d_in = (uint32_t)a.d_in;
+    const uint32_t ncol = nblk * 32;
+    const uint32_t nsz = (uint32_t)a.n_groups * ST_ROWS;
+    const uint32_t npc = a.xvec ? d_in / 8 : 0;       // whole 16-byte pieces of an activation row
+
+    // Phase 1: the first batch of every staging load, then the packed words of
+    // the lane's first two blocks, all in flight together.
+    constexpr int BS = 4, BX = 4, BP = 24;
+    float sv0[BS], zv0[BS];
+#pragma unroll
+    for (int i = 0; i < BS; ++i) {
+        const uint32_t e = tid + ST_THREADS * i;
+        const int64_t idx = (e < nsz && (int)(e % ST_ROWS) < nrw) ? (int64_t)(e / ST_ROWS) * a.d_out + rw0 + e % ST_ROWS : 0;
+        sv0[i] = a.scales[idx];
+        zv0[i] = a.zeros[idx];
+    }
+    // token t0 (it exists: nt >= 1); whole 16-byte pieces through a
+    // bounds-checked buffer, so that the loads need no branch
+    const uint16_t* xr0 = X + t0 * a.ld_x;
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)xr0, (short)0, (int)(npc * 16),
+                                                                       0x00020000);
+    u32x4_t xv0[BX];
+#pragma unroll
+    for (int i = 0; i < BX; ++i) xv0[i] = __builtin_amdgcn_raw_buffer_load_b128(rx, (tid + ST_THREADS * i) * 16, 0, 0);
+    int32_t cp[BP];
+    if (a.perm) {
+#pragma unroll
+        for (int i = 0; i < BP; ++i) {
+            const uint32_t k = tid + ST_THREADS * i;
+            cp[i] = a.perm[k < d_in ? k : 0];
+        }
+    }
+    uint32_t blk = tl;
+    uint32_t wd[RW][BITS], wn[RW][BITS];
+    load_block_words<BITS>(rs, row_bytes, blk, wd);
+    load_block_words<BITS>(rs, row_bytes, blk + 256, wn);
+
+    // Phase 2: LDS stores; anything past the first batch is staged in batches.
+#pragma unroll
+    for (int i = 0; i < BS; ++i) {
+        const uint32_t e = tid + ST_THREADS * i;
+        const bool ok = e < nsz && (int)(e % ST_ROWS) < nrw;
+        if (e < nsz) {
+            s_l[e] = ok ? sv0[i] : 0.0f;
+            o_l[e] = OFF + (ok ? zv0[i] : 0.0f);
+        }
+    }
+    for (uint32_t e0 = tid + ST_THREADS * BS; e0 < nsz; e0 += ST_THREADS * BS) {
+        float sv[BS], zv[BS];
+#pragma unroll
+        for (int i = 0; i < BS; ++i) {
+            const uint32_t e = e0 + ST_THREADS * i;
+            const bool ok = e < nsz && (int)(e % ST_ROWS) < nrw;
+            const int64_t idx = ok ? (int64_t)(e / ST_ROWS) * a.d_out + rw0 + e % ST_ROWS : 0;
+            const float sl = a.scales[idx], zl = a.zeros[idx];
+            sv[i] = ok ? sl : 0.0f;
+            zv[i] = ok ? zl : 0.0f;
+        }
+#pragma unroll
+        for (int i = 0; i < BS; ++i) {
+            const uint32_t e = e0 + ST_THREADS * i;
+            if (e < nsz) {
+                s_l[e] = sv[i];
+                o_l[e] = OFF + zv[i];
+            }
+        }
+    }
+    // activations in stream order.  Token t0: its row (natural order: straight
+    // into the blocked slots; with perm: flat, then gathered) from the
+    // registers of phase 1.
+    {
+        uint16_t* dst0 = a.perm ? xf : xs;
+#pragma unroll
+        for (int i = 0; i < BX; ++i) {
+            const uint32_t p = tid + ST_THREADS * i;
+            if (p < npc) {
+                uint16_t* q = a.perm ? xf + 8 * p : slot<true>(xs, 8 * p);
+                *(u32x4_t*)q = xv0[i];
+            }
+        }
+        if (a.perm) copy_row<false, ST_THREADS>(a, xr0, dst0, d_in, tid, ST_THREADS * BX);
+        else copy_row<true, ST_THREADS>(a, xr0, dst0, ncol, tid, ST_THREADS * BX);
+    }
+    for (int t = 0; t < TM; ++t) {
+        const bool tok = t < nt;
+        const uint16_t* xr = X + (t0 + t) * a.ld_x;
+        uint16_t* xst = xs + (size_t)t * nblk * XS_STRIDE;
+        if (!a.perm) {
+            if (t == 0) continue;
+            if (tok) copy_row<true, ST_THREADS>(a, xr, xst, ncol, tid, 0);
+            else
+                for (uint32_t k = tid; k < ncol; k += ST_THREADS) *slot<true>(xst, k) = 0;
+        } else {
+            if (t > 0) {
+                __syncthreads();               // the previous token's gather is done with xf
+                if (tok) copy_row<false, ST_THREADS>(a, xr, xf, d_in, tid, 0);
+            }
+            __syncthreads();
+            if (t > 0) {
+#pragma unroll
+                for (int i = 0; i < BP; ++i) {
+                    const uint32_t k = tid + ST_THREADS * i;
+                    cp[i] = a.perm[k < d_in ? k : 0];
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < BP; ++i) {
+                const uint32_t k = tid + ST_THREADS * i;
+                if (k < ncol) {
+                    uint16_t v = 0;
+                    if (tok && k < d_in) v = ((uint32_t)cp[i] < d_in) ? xf[cp[i]] : (uint16_t)T::NAN_BITS;
+                    *slot<true>(xst, k) = v;
+                }
+            }
+            constexpr int B = 8;
+            for (uint32_t k0 = tid + ST_THREADS * BP; k0 < ncol; k0 += ST_THREADS * B) {
+                int32_t c[B];
+#pragma unroll
+                for (int i = 0; i < B; ++i) {
+                    const uint32_t k = k0 + ST_THREADS * i;
+                    c[i] = a.perm[k < d_in ? k : 0];
+                }
+#pragma unroll
+                for (int i = 0; i < B; ++i) {
+                    const uint32_t k = k0 + ST_THREADS * i;
+                    if (k < ncol) {
+                        uint16_t v = 0;
+                        if (tok && k < d_in) v = ((uint32_t)c[i] < d_in) ? xf[c[i]] : (uint16_t)T::NAN_BITS;
+                        *slot<true>(xst, k) = v;
+                    }
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    float acc[TM][RW];
+#pragma unroll
+    for (int t = 0; t < TM; ++t)
+#pragma unroll
+        for (int rr = 0; rr < RW; ++rr) acc[t][rr] = 0.0f;
+
+    const bool one_group = a.gsize >= a.d_in;
+    const uint32_t bpg = (uint32_t)(a.gsize >> 5);   // blocks per group (a multiple of 32 columns here)
+    const float* s_h = s_l + half * RW;
+    const float* o_h = o_l + half * RW;
+    for (; blk < nblk; blk += 256) {
+        const uint32_t g = one_group ? 0u : blk / bpg;
+        const float4 s0 = *(const float4*)&s_h[g * ST_ROWS], s1 = *(const float4*)&s_h[g * ST_ROWS + 4];
+        const float4 o0 = *(const float4*)&o_h[g * ST_ROWS], o1 = *(const float4*)&o_h[g * ST_ROWS + 4];
+        const float sv[RW] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+        const float ov[RW] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
+        uint32_t xp[TM][16];
+        float xsum[TM];
+#pragma unroll
+        for (int t = 0; t < TM; ++t) {
+            const uint4* q = (const uint4*)(xs + ((size_t)t * nblk + blk) * XS_STRIDE);
+            uint32_t dd[16];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint4 v = q[i];
+                dd[4 * i] = v.x;
+                dd[4 * i + 1] = v.y;
+                dd[4 * i + 2] = v.z;
+                dd[4 * i + 3] = v.w;
+            }
+            float sx = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int ca = pair_col_a<BITS>(i), cb = pair_col_b<BITS>(i);
+                xp[t][i] = __builtin_amdgcn_perm(dd[cb >> 1], dd[ca >> 1], (ca & 1) ? 0x07060302u : 0x05040100u);
+                sx = T::dot2(xp[t][i], T::ONES, sx);
+            }
+            xsum[t] = sx;
+        }
+#pragma unroll
+        for (int rr = 0; rr < RW; ++rr) {
+            uint32_t cpr[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) cpr[i] = code_pair<BITS, T>(wd[rr], i);
+#pragma unroll
+            for (int t = 0; t < TM; ++t) {
+                float d = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) d = T::dot2(xp[t][i], cpr[i], d);
+                acc[t][rr] = fmaf(sv[rr], fmaf(-ov[rr], xsum[t], d), acc[t][rr]);
+            }
+        }
+#pragma unroll
+        for (int rr = 0; rr < RW; ++rr)
+#pragma unroll
+            for (int q = 0; q < BITS; ++q) wd[rr][q] = wn[rr][q];
+        load_block_words<BITS>(rs, row_bytes, blk + 2 * 256, wn);
+    }
+
+    // per half: exchange inside each wave, then the half's 4 waves meet in LDS
+    constexpr int NV = TM * RW;
+    float v[NV];
+#pragma unroll
+    for (int e = 0; e < NV; ++e) v[e] = acc[e / RW][e % RW];
+    const int lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+    for (int h = NV / 2; h >= 1; h >>= 1) {
+        const bool up = (lane & h) != 0;
+#pragma unroll
+        for (int e = 0; e < h; ++e) {
+            const float keep = up ? v[e + h] : v[e];
+            const float give = up ? v[e] : v[e + h];
+            v[e] = keep + __shfl_xor(give, h, 64);
+        }
+    }
+#pragma unroll
+    for (int m = NV; m < 64; m <<= 1) v[0] += __shfl_xor(v[0], m, 64);
+    red[wave][lane] = v[0];
+    __syncthreads();
+    if (tl < NV) {
+        float sum = 0.0f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) sum += red[half * 4 + w][tl];
+        const int t = tl / RW, rr = tl % RW;
+        if (t < nt && rr < nr) a.Y[(t0 + t) * a.ld_y + r0 + rr] = sum;
+    }
+}
+
 template <int BITS, int TM, typename T>
 gptq_status launch_block(const DqArgs& a, hipStream_t s) {
     const dim3 grid((unsigned)ceil_div(a.d_out, RW), (unsigned)ceil_div(a.n_tok, TM));
-    hipLaunchKernelGGL((dequant_block_kernel<BITS, TM, T>), grid, dim3(DQ_THREADS), 0, s, a);
+    const StagedLayout Ly = staged_layout(a.n_groups, ceil_div(a.d_in, 32), a.d_in, TM, a.perm != nullptr);
+    if (Ly.total <= STAGED_LDS_MAX) {
+        static const hipError_t attr = hipFuncSetAttribute((const void*)dequant_staged_kernel<BITS, TM, T>,
+                                                           hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                           (int)STAGED_LDS_MAX);
+        if (attr != hipSuccess) return GPTQ_ERR_HIP;
+        const dim3 grid_s((unsigned)ceil_div(a.d_out, ST_ROWS), (unsigned)ceil_div(a.n_tok, TM));
+        hipLaunchKernelGGL((dequant_staged_kernel<BITS, TM, T>), grid_s, dim3(ST_THREADS), Ly.total, s, a);
+    } else {
+        hipLaunchKernelGGL((dequant_block_kernel<BITS, TM, T>), grid, dim3(DQ_THREADS), 0, s, a);
+    }
     GPTQ_LAUNCH_CHECK();
     return GPTQ_OK;
 }
@@ -469,9 +835,6 @@ gptq_status dequant_matmul_launch(const void* X, gptq_dtype dt, int64_t n_tok, i
     a.ld_y = ld_y;
     const size_t xb = dt == GPTQ_F32 ? 4 : 2;
     a.xvec = (dt != GPTQ_F32) && ((uintptr_t)X % 16 == 0) && ((ld_x * (int64_t)xb) % 16 == 0);
-    const size_t wal = bits == 2 ? 8 : (bits == 3 ? 4 : 16);
-    const int64_t wmul = bits == 2 ? 2 : (bits == 3 ? 1 : 4);
-    a.wvec = ((uintptr_t)packed % wal == 0) && (a.wpr % wmul == 0);
     const bool block_path = dequant_uses_block_path(dt, bits, d_in, group_size, g_idx != nullptr);
     if (!block_path && n_groups > DQ_MAX_GROUPS) return GPTQ_ERR_UNSUPPORTED;
     // the grid's y dimension (token tiles) stays below 65536: larger token

@@ -40,28 +40,32 @@ PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hess_syrk_kernel_4096x11008_traffic.json")
 TRAFFIC_SOURCES = ("post_weight_quantization_accum_amd/csrc/hessian.hip",
                    "post_weight_quantization_accum_amd/csrc/common.hpp")
+DQ_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "dequant_staged_kernel_4096x11008_traffic.json")
+DQ_TRAFFIC_SOURCES = ("post_weight_quantization_accum_amd/csrc/dequant.hip",
+                      "post_weight_quantization_accum_amd/csrc/common.hpp",
+                      "post_weight_quantization_accum_amd/csrc/internal.hpp")
 
 
-def source_digest():
+def source_digest(sources=TRAFFIC_SOURCES):
     import hashlib
     h = hashlib.sha256()
-    for rel in TRAFFIC_SOURCES:
+    for rel in sources:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def measured_traffic():
-    """HBM bytes per launch of the Hessian product kernel, from the committed
-    rocprofv3 counter runs (FETCH_SIZE and WRITE_SIZE, each scaled by the
-    reading of a plain copy of known size); None if the kernel source has
-    changed since they were taken."""
+def measured_traffic(path=TRAFFIC_FILE, sources=TRAFFIC_SOURCES):
+    """HBM bytes per launch of a kernel, from the committed rocprofv3 counter
+    runs (FETCH_SIZE and WRITE_SIZE, each scaled by the reading of a plain
+    copy of known size); None if the kernel source has changed since they
+    were taken."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("source_sha256") != source_digest():
+    if t.get("source_sha256") != source_digest(sources):
         return None
     return t.get("bytes_per_launch")
 
@@ -78,6 +82,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--tokens", type=int, default=None, help="override the token count (testing only)")
     ap.add_argument("--workload", choices=("quantize", "dequant"), default="quantize")
+    ap.add_argument("--rounds", type=int, default=None, help="dequant workload: timed rounds per token count")
+    ap.add_argument("--dq-tokens", type=str, default="1,4,16", help="dequant workload: token counts")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after timing, run a plain device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -215,8 +221,11 @@ def dequant_main(a):
     cfg_id, lname = HEADLINE
     wl, li, d_out, d_in, xl = layer_spec(cfg_id, lname)
     q = wl.quants[0]
-    rounds = max(10, 20 * a.steps)
-    r = dequant_measure(d_out, d_in, q.bits, q.group_size, (1, 4, 16), rounds, cpu=not a.no_cpu_baseline)
+    rounds = a.rounds or max(10, 20 * a.steps)
+    toks = tuple(int(t) for t in a.dq_tokens.split(","))
+    if 1 not in toks:
+        toks = (1,) + toks
+    r = dequant_measure(d_out, d_in, q.bits, q.group_size, toks, rounds, cpu=not a.no_cpu_baseline)
     d1 = r["by_tokens"][1]
     ng = -(-d_in // q.group_size)
     res = {
@@ -228,13 +237,21 @@ def dequant_main(a):
                                f"act-order (sorted packing, perm gather), bf16 activations, 1 token; "
                                f"{DQ_COPIES} layer copies cycled", "d_out": d_out, "d_in": d_in, "tokens": 1},
         "roofline": {"bound": "hbm", "achieved": d1["GBps"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(d1["GBps"] / PEAK_HBM_GBS, 4), "traffic": None,
-                     "kernel": "dequant_block_kernel<4,1,bf16>", "launch_us": d1["us_per_launch"],
+                     "frac": round(d1["GBps"] / PEAK_HBM_GBS, 4),
+                     "traffic": measured_traffic(DQ_TRAFFIC_FILE, DQ_TRAFFIC_SOURCES),
+                     "kernel": "dequant_staged_kernel<4,1,bf16>", "launch_us": d1["us_per_launch"],
                      "algorithmic_bytes_per_launch": dequant_bytes(d_out, d_in, q.bits, ng, 1)},
         "by_tokens": r["by_tokens"],
     }
     if "cpu_baseline" in r:
         res["cpu_baseline"] = r["cpu_baseline"]
+    if a.calib_copy_mib:
+        import torch
+        src = torch.empty(a.calib_copy_mib << 20, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        res["calib_copy_bytes"] = int(src.numel())
     print(json.dumps(res))
 
 

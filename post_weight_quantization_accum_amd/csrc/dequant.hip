@@ -155,11 +155,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t words_rsrc(const DqArgs& a, in
     return __builtin_amdgcn_make_buffer_rsrc((void*)(a.packed + r0 * a.wpr), (short)0, n, 0x00020000);
 }
 
-// the `bits` words of block blk of the 8 rows
+// the `bits` words of block blk of the 8 rows; a block past the row's last
+// (blk >= nblk) gets an offset past the buffer's end: zeros, no memory access
 template <int BITS>
 __device__ __forceinline__ void load_block_words(__amdgpu_buffer_rsrc_t rs, uint32_t row_bytes, uint32_t blk,
-                                                 uint32_t (&w)[RW][BITS]) {
-    const uint32_t off = blk * (uint32_t)(BITS * 4);
+                                                 uint32_t nblk, uint32_t (&w)[RW][BITS]) {
+    const uint32_t off = blk < nblk ? blk * (uint32_t)(BITS * 4) : 0x80000000u;
 #pragma unroll
     for (int rr = 0; rr < RW; ++rr) {
         const uint32_t o = off + (uint32_t)rr * row_bytes;
@@ -264,7 +265,7 @@ __global__ __launch_bounds__(DQ_THREADS) void dequant_block_kernel(DqArgs a) {
     for (int64_t blk = tid; blk < nblk; blk += DQ_THREADS) {
         const int64_t j0 = blk * 32;
         uint32_t wd[RW][BITS];
-        load_block_words<BITS>(rs, row_bytes, (uint32_t)blk, wd);
+        load_block_words<BITS>(rs, row_bytes, (uint32_t)blk, (uint32_t)nblk, wd);
         const int64_t g = j0 / a.gsize;
         float sv[RW], ov[RW];
 #pragma unroll
@@ -366,7 +367,7 @@ __global__ __launch_bounds__(DQ_THREADS) void dequant_col_kernel(DqArgs a) {
     for (int64_t blk = tid; blk < nblk; blk += DQ_THREADS) {
         const int64_t j0 = blk * 32;
         uint32_t wd[RW][BITS];
-        load_block_words<BITS>(rs, row_bytes, (uint32_t)blk, wd);
+        load_block_words<BITS>(rs, row_bytes, (uint32_t)blk, (uint32_t)nblk, wd);
         // group (LDS row offset) and activation of each column of the block
         int32_t gk[32];
         float xk[32];
@@ -564,8 +565,8 @@ __global__ __launch_bounds__(ST_THREADS) void dequant_staged_kernel(DqArgs a) {
     }
     uint32_t blk = tl;
     uint32_t wd[RW][BITS], wn[RW][BITS];
-    load_block_words<BITS>(rs, row_bytes, blk, wd);
-    load_block_words<BITS>(rs, row_bytes, blk + 256, wn);
+    load_block_words<BITS>(rs, row_bytes, blk, nblk, wd);
+    load_block_words<BITS>(rs, row_bytes, blk + 256, nblk, wn);
 
     // Phase 2: LDS stores; anything past the first batch is staged in batches.
 #pragma unroll
@@ -722,7 +723,7 @@ __global__ __launch_bounds__(ST_THREADS) void dequant_staged_kernel(DqArgs a) {
         for (int rr = 0; rr < RW; ++rr)
 #pragma unroll
             for (int q = 0; q < BITS; ++q) wd[rr][q] = wn[rr][q];
-        load_block_words<BITS>(rs, row_bytes, blk + 2 * 256, wn);
+        load_block_words<BITS>(rs, row_bytes, blk + 2 * 256, nblk, wn);
     }
 
     // per half: exchange inside each wave, then the half's 4 waves meet in LDS

@@ -1,0 +1,228 @@
+"""Workload 5 (OPT-175B-shaped block quantized in sequence) on the GPU (needs an MI355X).
+
+* A block in sequence at reduced width (hidden 256, ffn 1024, 4096 fp16
+  tokens, 3-bit, group 128, natural order): q, k, v are quantized on H(X0);
+  A = X0 W_v^T with the quantized v, out is quantized on H(A); h1 = X0 +
+  A W_out^T, fc1 on H(h1); fc2 on H(relu(h1 W_fc1^T)).  Every product uses
+  the already-quantized weights, computed by gptq_dequant_matmul from the
+  packed words (identity attention, residual, no layer norm: the reading of
+  "GPTQ论文复现指南" §3.2's --true-sequential taken for this harness).
+  Per layer the oracle quantizes the same weights from the same activations
+  (the GPU chain's activations, handed over as data): given the GPU's own
+  Hessian of them, codes >= 99.99% identical and the loss within 1e-6; from
+  its own float64 Hessian (downstream inputs have nearly singular Hessians,
+  where the GPU's float32 chunk sums move codes), codes >= 99% identical with
+  differences <= 2 and the layer loss within 1e-2.  The chain products are
+  checked against the oracle's product from the same packed layer.  The
+  oracle's own chain (its own quantized weights and float64 products) must
+  reach the same total loss within 1e-2.
+* The widest layer at full size: fc2, 12288 x 49152, its float64 Hessian
+  (19.3 GB) from 16384 tokens of the workload's activation recipe.  The
+  oracle cannot factor 49152^2 in a test, so: sampled Hessian entries
+  against float64 dot products of the same tokens; U^T U H_d = I on sampled
+  columns (H_d from the GPU's own Hessian); the sweep of 6 sampled rows by
+  the oracle given the GPU's U, bit-identical codes; properties of all rows.
+"""
+import time
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import post_weight_quantization_accum_amd as P
+from post_weight_quantization_accum_amd import synth
+
+from _util import compare_codes
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _f16_to_torch(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def _quantize_on(W16, X16, cfg):
+    """Quantize W (fp16, device) on the Hessian of X (fp16, device)."""
+    out = P.quantize(W16, X=X16, cfg=cfg, packed=True)
+    torch.cuda.synchronize()
+    return out
+
+
+def _product(Xd, out, bits, gs):
+    return P.dequant_matmul(Xd, out["packed"], bits, out["scales"], out["zeros"], group_size=gs)
+
+
+def test_block_in_sequence_reduced():
+    bits, gs, h, ffn, n = 3, 128, 256, 1024, 4096
+    cfg = P.make_config(bits=bits, group_size=gs, act_order=False, block=128, damp=0.01)
+    X0, _, _ = synth.gen_activations(n, h, "t4", "f16", seed=5001, outlier_count=1, outlier_scale=100.0)
+    Ws = {name: synth.gen_weights(d_out, d_in, 0.01, "f16", 5010 + i)
+          for i, (name, d_out, d_in) in enumerate((("q", h, h), ("k", h, h), ("v", h, h), ("out", h, h),
+                                                    ("fc1", ffn, h), ("fc2", h, ffn)))}
+    X0d = _f16_to_torch(X0)
+    inputs, outs = {}, {}
+    for name in ("q", "k", "v"):
+        inputs[name] = X0d
+        outs[name] = _quantize_on(_f16_to_torch(Ws[name]), X0d, cfg)
+    A = _product(X0d, outs["v"], bits, gs)
+    Ad = A.half()
+    inputs["out"] = Ad
+    outs["out"] = _quantize_on(_f16_to_torch(Ws["out"]), Ad, cfg)
+    h1 = (X0d.float() + _product(Ad, outs["out"], bits, gs)).half()
+    inputs["fc1"] = h1
+    outs["fc1"] = _quantize_on(_f16_to_torch(Ws["fc1"]), h1, cfg)
+    r = torch.relu(_product(h1, outs["fc1"], bits, gs)).half()
+    inputs["fc2"] = r
+    outs["fc2"] = _quantize_on(_f16_to_torch(Ws["fc2"]), r, cfg)
+    torch.cuda.synchronize()
+
+    # per layer, on the same weights and the same activations:
+    # (a) the oracle given the GPU's own Hessian of those activations: the
+    #     solver decides in float64 on both sides, so codes and loss agree;
+    # (b) the oracle from its own float64 Hessian.  The GPU's Hessian sums
+    #     each chunk in float32; downstream of the first layers the inputs
+    #     are projections of X0 (A: dominated by X0's outlier channel; fc2's:
+    #     ReLU of a rank-256 map into 1024 dimensions), whose Hessians are
+    #     close to singular, and there those rounding differences move codes
+    #     (0.05% of out's, 0.4% of fc2's, some by 2 after a cascade) and,
+    #     through the compensated values, the scales.  Bounds: codes >= 99%
+    #     identical with differences <= 2, layer loss within 1e-2.
+    total_gpu = 0.0
+    for name in ("q", "k", "v", "out", "fc1", "fc2"):
+        Xd = inputs[name]
+        Xl = Xd.cpu().numpy().astype(np.float64)
+        W64 = Ws[name].astype(np.float64)
+        got = {k: v.cpu().numpy() for k, v in outs[name].items()}
+        Hg = torch.zeros((Xl.shape[1], Xl.shape[1]), dtype=torch.float64, device=DEV)
+        P.hessian_accumulate(Hg, Xd)
+        Hg = Hg.cpu().numpy()
+        Hg = np.triu(Hg) + np.triu(Hg, 1).T
+        ref_h = O.gptq_quantize(W64, Hg, bits=bits, group_size=gs, act_order=False, block=128, damp=0.01)
+        same_h, mx_h = compare_codes(got["codes"], ref_h["codes"])
+        lg_h = O.layer_loss(W64, got["w_hat"].astype(np.float64), Hg).sum()
+        assert same_h >= 0.9999 and mx_h <= 1, name
+        assert abs(lg_h - ref_h["loss"].sum()) <= 1e-6 * ref_h["loss"].sum(), name
+        ref = O.gptq_quantize(W64, X=Xl, bits=bits, group_size=gs, act_order=False, block=128, damp=0.01)
+        same, mx = compare_codes(got["codes"], ref["codes"])
+        row_g = O.layer_loss(W64, got["w_hat"].astype(np.float64), ref["H"])
+        row_o = ref["loss"]
+        agree = np.all(got["codes"] == ref["codes"], axis=1)
+        loss_g, loss_o = row_g.sum(), row_o.sum()
+        print(f"{name}: given the GPU's H identical {same_h:.5f}; from X identical {same:.5f} max diff {mx} "
+              f"rows differing {int((~agree).sum())} loss gpu {loss_g:.6g} oracle {loss_o:.6g}", flush=True)
+        assert same >= 0.99 and mx <= 2, name
+        assert abs(loss_g - loss_o) <= 1e-2 * loss_o, name
+        total_gpu += loss_g
+    # the chain products against the oracle's product from the same packed layer
+    for name, Xd, Y in (("v", X0d, A), ("fc1", h1, None)):
+        o = {k: v.cpu().numpy() for k, v in outs[name].items()}
+        X64 = Xd.cpu().numpy().astype(np.float64)
+        ref_y = O.dequant_matmul(X64, o["packed"].view(np.uint32), bits, X64.shape[1], o["scales"], o["zeros"],
+                                 group_size=gs)
+        got_y = (Y if Y is not None else _product(Xd, outs[name], bits, gs)).cpu().numpy().astype(np.float64)
+        # the float32 bound of the product (see tests/test_gpu_dequant.py):
+        # (96 + 32 nb) u sum_k |x_k| s (c + z + 2^(b+1)), nb blocks per lane
+        g = np.arange(X64.shape[1]) // gs
+        S = o["scales"].astype(np.float64)[g].T
+        Z = o["zeros"].astype(np.float64)[g].T
+        A = np.abs(X64) @ (S * (o["codes"].astype(np.float64) + Z + 2.0 ** (bits + 1))).T
+        nb = -(-(-(-X64.shape[1] // 32)) // 256)
+        assert np.all(np.abs(got_y - ref_y) <= (96 + 32 * nb) * 2.0 ** -24 * A), name
+
+    # the oracle's own chain (its quantized weights, float64 products, fp16 activations)
+    def q(name, X64):
+        return O.gptq_quantize(Ws[name].astype(np.float64), X=X64, bits=bits, group_size=gs, act_order=False,
+                               block=128, damp=0.01)
+
+    def f16(a):
+        return a.astype(np.float16).astype(np.float64)
+
+    X064 = X0.astype(np.float64)
+    total_o = 0.0
+    rv = None
+    for name in ("q", "k", "v"):
+        rr_ = q(name, X064)
+        total_o += rr_["loss"].sum()
+        if name == "v":
+            rv = rr_
+    Ao = f16(X064 @ rv["w_hat"].T)
+    ro = q("out", Ao)
+    total_o += ro["loss"].sum()
+    h1o = f16(X064 + Ao @ ro["w_hat"].T)
+    r1 = q("fc1", h1o)
+    total_o += r1["loss"].sum()
+    r2 = q("fc2", f16(np.maximum(h1o @ r1["w_hat"].T, 0.0)))
+    total_o += r2["loss"].sum()
+    print(f"chain loss gpu {total_gpu:.6g} oracle chain {total_o:.6g}", flush=True)
+    assert abs(total_gpu - total_o) <= 1e-2 * total_o
+
+
+@pytest.mark.timeout(900)
+def test_fc2_full_size_solver():
+    d_out, d_in, n_tok, bits, gs = 12288, 49152, 16384, 3, 128
+    t0 = time.time()
+    L = synth.make_layer(d_out, d_in, n_tok, dtype="f16", sigma_w=0.01, dist="t4", outlier_frac=0.001,
+                         outlier_scale=100.0, config=5, layer=5)
+    print(f"fc2 inputs generated in {time.time() - t0:.1f} s", flush=True)
+    cfg = P.make_config(bits=bits, group_size=gs, act_order=False, block=128, damp=0.01)
+    X = _f16_to_torch(L.X)
+    W = _f16_to_torch(L.W)
+    H = torch.zeros((d_in, d_in), dtype=torch.float64, device=DEV)
+    P.hessian_accumulate(H, X)
+    H0 = H.clone()
+    torch.cuda.synchronize()
+    t0 = time.time()
+    out = P.quantize(W, H=H, cfg=cfg)
+    torch.cuda.synchronize()
+    print(f"fc2 prepare + quantize + pack on the GPU {time.time() - t0:.1f} s", flush=True)
+
+    # sampled Hessian entries against float64 dot products of the same tokens
+    rng = np.random.default_rng(49152)
+    ii = rng.integers(0, d_in, 300)
+    jj = rng.integers(0, d_in, 300)
+    ii, jj = np.minimum(ii, jj), np.maximum(ii, jj)
+    cols = np.unique(np.concatenate([ii, jj]))
+    Xc = {c: L.X[:, c].astype(np.float64) for c in cols}
+    got_h = H0[torch.from_numpy(ii).to(DEV), torch.from_numpy(jj).to(DEV)].cpu().numpy()
+    want_h = np.array([2.0 * Xc[i] @ Xc[j] for i, j in zip(ii, jj)])
+    dia = np.array([2.0 * Xc[i] @ Xc[i] for i in ii])
+    djj = np.array([2.0 * Xc[j] @ Xc[j] for j in jj])
+    assert np.all(np.abs(got_h - want_h) <= 1e-6 * np.sqrt(dia * djj) + 1e-300)
+
+    # U^T U H_d = I on sampled columns, H_d from the GPU's Hessian (upper triangle + lambda I)
+    U = H                     # prepare_hinv left U here (natural order)
+    diag = torch.diagonal(H0)
+    lam = 0.01 * diag.mean()
+    for j in (0, 1, 4097, 30000, d_in - 1):
+        v = torch.mv(U.t(), U[:, j].contiguous())
+        hv = torch.mv(H0, v) + torch.mv(H0.t(), v) - diag * v + lam * v
+        e = torch.zeros_like(hv)
+        e[j] = 1.0
+        res = (hv - e).abs().max().item()
+        print(f"column {j}: max |H_d U^T U e_j - e_j| = {res:.3e}", flush=True)
+        assert res <= 1e-6
+    assert torch.all(torch.diagonal(U) > 0)
+
+    # the oracle's sweep of sampled rows given the GPU's U
+    t0 = time.time()
+    Uh = U.cpu().numpy()
+    rows = np.sort(rng.choice(d_out, 6, replace=False))
+    W64 = L.W[rows].astype(np.float64)
+    codes, scales, zeros, w_hat, row_loss = O.sweep(W64, Uh, bits, gs, False, 128)
+    print(f"oracle sweep of {len(rows)} rows {time.time() - t0:.1f} s", flush=True)
+    got = {k: out[k].cpu().numpy() for k in ("codes", "scales", "zeros", "row_loss", "w_hat", "g_idx", "perm")}
+    assert np.array_equal(got["perm"], np.arange(d_in))
+    assert np.array_equal(got["codes"][rows], codes)
+    np.testing.assert_allclose(got["scales"][:, rows], scales.astype(np.float32), rtol=2e-7)
+    np.testing.assert_array_equal(got["zeros"][:, rows], zeros.astype(np.float32))
+    np.testing.assert_allclose(got["row_loss"][rows], row_loss, rtol=1e-9)
+    # properties of all rows
+    assert got["codes"].max() <= 2 ** bits - 1
+    assert np.array_equal(got["g_idx"], np.arange(d_in) // gs)
+    packed = out["packed"][:16].cpu().numpy().view(np.uint32)
+    assert np.array_equal(O.unpack(packed, bits, d_in), got["codes"][:16])
+    deq = O.dequantize(got["codes"][:16], got["scales"][:, :16], got["zeros"][:, :16], got["g_idx"])
+    np.testing.assert_allclose(got["w_hat"][:16], deq, rtol=1e-6, atol=1e-12)

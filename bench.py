@@ -81,7 +81,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--tokens", type=int, default=None, help="override the token count (testing only)")
-    ap.add_argument("--workload", choices=("quantize", "dequant"), default="quantize")
+    ap.add_argument("--workload", choices=("quantize", "dequant", "shapes"), default="quantize")
     ap.add_argument("--rounds", type=int, default=None, help="dequant workload: timed rounds per token count")
     ap.add_argument("--dq-tokens", type=str, default="1,4,16", help="dequant workload: token counts")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -124,6 +124,33 @@ def cpu_baseline(layer_w, layer_x, d_out, d_in, n_tok, q):
                    f"{d_in}x{d_in} matrix; sweep and packing on {rows_s} of {d_out} rows (x{d_out // rows_s}); "
                    f"est. full-layer seconds {total:.1f} (H {t_h:.1f}, chol {t_c:.1f}, sweep {t_s:.1f}, pack {t_p:.2f})"),
     }
+
+
+def phase_rooflines(d_out, d_in, n_tok, bits, block, phases_ms, x_bytes=2):
+    """Each phase's algorithmic work over its measured time, against the peak
+    that bounds it (the solver runs in float64: its phases are priced at the
+    float64 peak)."""
+    h_flops = float(n_tok) * d_in * (d_in + 1)
+    chol_flops = 2.0 / 3.0 * float(d_in) ** 3              # Cholesky + triangular inverse
+    lazy = 0.0
+    for i1 in range(0, d_in, block):
+        i2 = min(i1 + block, d_in)
+        lazy += 2.0 * d_out * (i2 - i1) * (d_in - i2)
+    sweep_flops = lazy + float(d_out) * d_in * (block - 1)
+    pack_bytes = d_out * d_in * (1 + bits / 8)
+
+    def fl(flops, ms, peak):
+        a = flops / (ms * 1e-3) / 1e12
+        return {"achieved": round(a, 2), "peak": peak, "unit": "TFLOP/s", "frac": round(a / peak, 4),
+                "algorithmic_flops": flops}
+    out = {"hessian": dict(fl(h_flops, phases_ms["hessian"], PEAK_BF16_TFLOPS if x_bytes == 2 else PEAK_F64_TFLOPS),
+                           bound="mfma"),
+           "prepare_hinv": dict(fl(chol_flops, phases_ms["prepare_hinv"], PEAK_F64_TFLOPS), bound="mfma (fp64)"),
+           "quantize_layer": dict(fl(sweep_flops, phases_ms["quantize_layer"], PEAK_F64_TFLOPS), bound="mfma (fp64)")}
+    gbs = pack_bytes / (phases_ms["pack"] * 1e-3) / 1e9
+    out["pack"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                   "frac": round(gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": pack_bytes}
+    return out
 
 
 DQ_COPIES = 16   # distinct packed layers cycled through (406 MB > the 256 MB last-level cache)
@@ -255,6 +282,70 @@ def dequant_main(a):
     print(json.dumps(res))
 
 
+def shapes_main(a):
+    """Every distinct layer shape of the five workloads at its full size
+    (token count, dtype, quantizer), one layer-quantize step each after a
+    warm-up; inputs drawn on the device (normal weights, normal activations:
+    the times do not depend on the values)."""
+    import torch
+
+    import post_weight_quantization_accum_amd as P
+    from post_weight_quantization_accum_amd.configs import WORKLOADS
+
+    dev = torch.device("cuda:0")
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+    rows = []
+    for cid, wl in WORKLOADS.items():
+        seen = set()
+        for (name, d_out, d_in, _xl) in wl.layers:
+            if (d_out, d_in) in seen:
+                continue
+            seen.add((d_out, d_in))
+            for q in wl.quants:
+                log(f"workload {cid} {name} {d_out}x{d_in} {q.bits}-bit g{q.group_size}")
+                g = torch.Generator(device=dev)
+                g.manual_seed(1000 * cid + d_in)
+                X = (torch.randn((wl.n_tok, d_in), generator=g, device=dev) * 0.5).to(tdt[wl.dtype])
+                W = (torch.randn((d_out, d_in), generator=g, device=dev) * wl.sigma_w).to(tdt[wl.dtype])
+                cfg = P.make_config(bits=q.bits, group_size=q.group_size, sym=q.sym, act_order=q.act_order,
+                                    block=q.block, damp=q.damp)
+                H = torch.empty((d_in, d_in), dtype=torch.float64, device=dev)
+                ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+                times = []
+                for it in range(1 + max(1, a.steps // 2)):
+                    ev[0].record()
+                    H.zero_()
+                    P.hessian_accumulate(H, X)
+                    ev[1].record()
+                    perm = P.prepare_hinv(H, cfg)
+                    ev[2].record()
+                    out = P.quantize_layer(W, H, perm, cfg, want_w_hat=False, want_row_loss=False)
+                    ev[3].record()
+                    P.pack(out["codes"], q.bits)
+                    ev[4].record()
+                    torch.cuda.synchronize()
+                    if it > 0:
+                        times.append([ev[i].elapsed_time(ev[i + 1]) for i in range(4)])
+                t = np.mean(np.array(times), axis=0)
+                ph = dict(zip(("hessian", "prepare_hinv", "quantize_layer", "pack"), (float(v) for v in t)))
+                total = float(sum(t))
+                rows.append({"workload": cid, "layer": name, "d_out": d_out, "d_in": d_in, "tokens": wl.n_tok,
+                             "dtype": wl.dtype, "bits": q.bits, "group_size": q.group_size,
+                             "act_order": bool(q.act_order), "ms": round(total, 3),
+                             "solver_only_ms": round(total - ph["hessian"], 3),
+                             "phases_ms": {k: round(v, 3) for k, v in ph.items()},
+                             "weights_per_s": d_out * d_in / (total * 1e-3),
+                             "phase_roofline": phase_rooflines(d_out, d_in, wl.n_tok, q.bits, q.block, ph,
+                                                               x_bytes=4 if wl.dtype == "f32" else 2)})
+                log(f"  {total:.2f} ms (H {ph['hessian']:.2f}, prepare {ph['prepare_hinv']:.2f}, "
+                    f"quantize {ph['quantize_layer']:.2f}, pack {ph['pack']:.3f})")
+                del X, W, H, out, perm
+                torch.cuda.empty_cache()
+    print(json.dumps({"metric": "GPTQ layer-quantize ms per distinct layer shape (workloads 1-5)",
+                      "unit": "ms", "higher_is_better": False, "n_gpus": 1, "data": "synthetic (device normal)",
+                      "shapes": rows}))
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -263,6 +354,9 @@ def main():
         sys.exit(2)
     if a.workload == "dequant":
         dequant_main(a)
+        return
+    if a.workload == "shapes":
+        shapes_main(a)
         return
 
     import torch
@@ -376,6 +470,8 @@ def main():
                    "d_out": d_out, "d_in": d_in, "tokens": n_tok, "bits": q.bits, "group_size": q.group_size,
                    "act_order": bool(q.act_order), "parallelism": "single GPU"},
         "phases_ms": {k: round(v, 3) for k, v in phases.items()},
+        "solver_only_ms": round(phases["prepare_hinv"] + phases["quantize_layer"] + phases["pack"], 3),
+        "phase_roofline": phase_rooflines(d_out, d_in, n_tok, q.bits, q.block, phases),
         "roofline": roofline,
     }
     log(f"timed {a.steps} steps: {ms_per_step:.2f} ms/step; phases {res['phases_ms']}")

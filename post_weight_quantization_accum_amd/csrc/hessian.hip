@@ -265,19 +265,23 @@ __device__ __forceinline__ u32x4_t lds_operand(const char* lds_panel, int r, int
     return *(const u32x4_t*)(lds_panel + r * (KT * 2) + ((g ^ swz(r)) << 4));
 }
 
+// Stages [st0, st1) of the chunk.  part == null: the tile's float32 sums are
+// added to H; otherwise they are written to part (256x256 floats, row-major)
+// for a fixed-order reduction over the token slices of a tile.
 template <typename Tag, bool DIAG, int NW>
 __device__ __forceinline__ void syrk_tile(double* __restrict__ H, const uint16_t* __restrict__ Xt, int64_t ch, int64_t d_pad,
-                                          int64_t d, int64_t ti, int64_t tj, char* lds) {
+                                          int64_t d, int64_t ti, int64_t tj, char* lds, int64_t st0, int64_t st1,
+                                          float* __restrict__ part) {
     constexpr int WCOLS = 512 / NW, NTL = WCOLS / 32, NCW = BT / WCOLS;
     constexpr int RPW = BT / NW;  // panel rows loaded per wave (multiple of 32)
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int wr = wave / NCW, wc = wave % NCW;
-    const int64_t n_st = ch / KT;
+    const int64_t n_st = st1 - st0;     // stages of this workgroup (local index st = 0 .. n_st-1)
     // one resource over the chunk; a stage of one panel is 256 consecutive
     // rows of KT tokens, at byte offset (st * d_pad + panel row) * KT * 2
     const uint32_t stage_bytes = (uint32_t)(d_pad * KT * 2);
     const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)Xt, (short)0, (int)(stage_bytes * (uint32_t)n_st), 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc((void*)Xt, (short)0, (int)(stage_bytes * (uint32_t)(ch / KT)), 0x00020000);
     const uint32_t pa_row = (uint32_t)(ti * BT), pb_row = (uint32_t)(tj * BT);
     const int row0 = wave * RPW;
     // loads issued per wave per stage
@@ -295,8 +299,8 @@ __device__ __forceinline__ void syrk_tile(double* __restrict__ H, const uint16_t
         char* sb = lds + (st % NSTAGE) * STAGE_BYTES;
 #pragma unroll
         for (int rr = 0; rr < RPW; rr += 32) {
-            dma_panel_rows(rs, sb, row0 + rr, lane, pa_row, (uint32_t)st * stage_bytes);
-            if (!DIAG) dma_panel_rows(rs, sb + PANEL_BYTES, row0 + rr, lane, pb_row, (uint32_t)st * stage_bytes);
+            dma_panel_rows(rs, sb, row0 + rr, lane, pa_row, (uint32_t)(st0 + st) * stage_bytes);
+            if (!DIAG) dma_panel_rows(rs, sb + PANEL_BYTES, row0 + rr, lane, pb_row, (uint32_t)(st0 + st) * stage_bytes);
         }
     };
     auto read_ops = [&](u32x4_t (&a)[4], u32x4_t (&bb)[NTL], int64_t st, int ks) {
@@ -350,6 +354,21 @@ __device__ __forceinline__ void syrk_tile(double* __restrict__ H, const uint16_t
     }
     __syncthreads();
 
+    if (part) {
+        // lane l holds C[8*(r/4) + 4*(l/32) + r%4][l%32] of each 32x32 block
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < NTL; ++ni)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = wr * 128 + mi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                    const int col = wc * WCOLS + ni * 32 + (lane & 31);
+                    part[row * BT + col] = acc[mi][ni][r];
+                }
+        return;
+    }
+
     // float32 tile -> float64 H (strict upper part; the diagonal comes from a
     // float64 pass).  The 128x128 quarters are staged in LDS one at a time
     // by the waves that own them, then all threads add the quarter to H with
@@ -388,10 +407,15 @@ struct NextChunk {
     double* colsq;
 };
 
+// S > 1 (few tiles): each tile's stages are split into S consecutive token
+// slices, one workgroup each, writing float32 partial tiles to part (slice s
+// of tile t at part + (t * S + s) * 256 * 256); syrk_slices_add_kernel then
+// adds them to H in slice order.
 template <typename Tag, int NW, bool VEC>
 __global__ __launch_bounds__(NW * 64) void hess_syrk_kernel(double* __restrict__ H, const uint16_t* __restrict__ Xt,
                                                             int64_t ch, int64_t d_pad, int64_t d, int64_t T,
-                                                            int64_t n_tiles, int64_t per_xcd, NextChunk nx) {
+                                                            int64_t n_tiles, int64_t per_xcd, NextChunk nx,
+                                                            int64_t S, float* __restrict__ part) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
     const int64_t b = blockIdx.x;
     if (b >= per_xcd * 8) {
@@ -411,11 +435,36 @@ __global__ __launch_bounds__(NW * 64) void hess_syrk_kernel(double* __restrict__
     // XCD-grouped tile order: workgroup b runs on XCD b % 8; each XCD takes a
     // contiguous range of the banded upper-triangle enumeration.
     const int64_t lin = (b % 8) * per_xcd + b / 8;
-    if (lin >= n_tiles) return;
+    if (lin >= n_tiles * S) return;
+    const int64_t tile = lin / S, sl = lin % S, n_st = ch / KT;
+    const int64_t st0 = sl * n_st / S, st1 = (sl + 1) * n_st / S;
+    float* pt = (S > 1) ? part + lin * (int64_t)(BT * BT) : nullptr;
     int64_t ti, tj;
-    upper_tile(lin, ti, tj, T);
-    if (ti == tj) syrk_tile<Tag, true, NW>(H, Xt, ch, d_pad, d, ti, tj, lds);
-    else syrk_tile<Tag, false, NW>(H, Xt, ch, d_pad, d, ti, tj, lds);
+    upper_tile(tile, ti, tj, T);
+    if (ti == tj) syrk_tile<Tag, true, NW>(H, Xt, ch, d_pad, d, ti, tj, lds, st0, st1, pt);
+    else syrk_tile<Tag, false, NW>(H, Xt, ch, d_pad, d, ti, tj, lds, st0, st1, pt);
+}
+
+// H (strict upper) += 2 * sum over the S slices of each tile, in slice order,
+// in float64.  One workgroup per 4 rows of a tile, one thread per column.
+__global__ __launch_bounds__(256) void syrk_slices_add_kernel(double* __restrict__ H, const float* __restrict__ part,
+                                                              int64_t T, int64_t S, int64_t d) {
+    const int64_t tile = blockIdx.x / (BT / 4), rq = blockIdx.x % (BT / 4);
+    int64_t ti, tj;
+    upper_tile(tile, ti, tj, T);
+    const int c = threadIdx.x;
+    const int64_t j = tj * BT + c;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int row = (int)rq * 4 + k;
+        const int64_t i = ti * BT + row;
+        if (i < j && j < d) {
+            const float* p = part + tile * S * (int64_t)(BT * BT) + row * BT + c;
+            double sum = 0.0;
+            for (int64_t s = 0; s < S; ++s) sum += (double)p[s * (int64_t)(BT * BT)];
+            H[i * d + j] += 2.0 * sum;
+        }
+    }
 }
 
 #ifndef GPTQ_SYRK_WAVES
@@ -476,17 +525,31 @@ __global__ __launch_bounds__(256) void hess_f32_kernel(double* __restrict__ H, c
         }
 }
 
-// Tokens per chunk: at most CHUNK, and the transposed chunk (d_pad x ch
+// Fewer upper tiles than this: each tile's tokens are split over several
+// workgroups (token slices), ceil(512 / tiles) of them.
+constexpr int64_t SLICE_TILES = 128;
+
+int64_t tile_count(int64_t d) {
+    const int64_t T = align_up((size_t)d, BT) / BT;
+    return T * (T + 1) / 2;
+}
+
+// Tokens per chunk: every float32 sum covers at most CHUNK tokens (one tile,
+// or one token slice of a sliced tile), and the transposed chunk (d_pad x ch
 // 16-bit values) stays under XT_MAX_BYTES.
 int64_t chunk_tokens(int64_t d) {
     const int64_t d_pad = align_up((size_t)d, BT);
+    const int64_t n_tiles = tile_count(d);
     int64_t c = (int64_t)(XT_MAX_BYTES / (2 * (size_t)d_pad)) / KT * KT;
-    if (c > CHUNK) c = CHUNK;
+    const int64_t lim = n_tiles < SLICE_TILES ? CHUNK * ceil_div(512, n_tiles) : CHUNK;
+    if (c > lim) c = lim;
     if (c < KT) c = KT;
     return c;
 }
 
-size_t part_bytes(int64_t d) { return align_up((size_t)(CHUNK / TSPAN) * d * sizeof(double), 256); }
+size_t part_bytes(int64_t d) {
+    return align_up((size_t)ceil_div(chunk_tokens(d), TSPAN) * d * sizeof(double), 256);
+}
 
 }  // namespace
 
@@ -499,11 +562,29 @@ size_t slot_bytes(int64_t n_tok, int64_t d) {
     if (ch > cmax) ch = cmax;
     return part_bytes(d) + (size_t)d_pad * ch * sizeof(uint16_t);
 }
+
+// Token slices per tile: few tiles (small d) would leave most CUs idle, so
+// each tile's chunk is split over S workgroups.
+int64_t syrk_slices(int64_t n_tiles, int64_t n_st) {
+    if (n_tiles >= SLICE_TILES) return 1;
+    int64_t S = ceil_div(512, n_tiles);
+    if (S > n_st) S = n_st;
+    return S < 1 ? 1 : S;
+}
+
+// float32 partial tiles for the largest chunk of this call (zero if unsliced)
+size_t slices_bytes(int64_t n_tok, int64_t d) {
+    const int64_t T = align_up((size_t)d, BT) / BT, n_tiles = T * (T + 1) / 2;
+    int64_t ch = align_up((size_t)(n_tok > 0 ? n_tok : 1), KT);
+    if (ch > chunk_tokens(d)) ch = chunk_tokens(d);
+    const int64_t S = syrk_slices(n_tiles, ch / KT);
+    return S > 1 ? (size_t)n_tiles * S * BT * BT * sizeof(float) : 0;
+}
 }  // namespace
 
 size_t hessian_workspace_bytes(int64_t n_tok, int64_t d) {
     const int nslots = (n_tok > chunk_tokens(d)) ? 2 : 1;
-    return nslots * slot_bytes(n_tok, d);
+    return nslots * slot_bytes(n_tok, d) + slices_bytes(n_tok, d);
 }
 
 int64_t hessian_syrk_launches(int64_t n_tok, gptq_dtype dt, int64_t d) {
@@ -524,10 +605,10 @@ gptq_status hessian_launch(double* H, const void* X, gptq_dtype dt, int64_t n_to
         return GPTQ_OK;
     }
     const size_t slot = slot_bytes(n_tok, d);
+    float* part = (float*)((char*)ws + ((n_tok > chunk_tokens(d)) ? 2 : 1) * slot);
     const int64_t d_pad = align_up((size_t)d, BT);
     const int64_t T = d_pad / BT;
     const int64_t n_tiles = T * (T + 1) / 2;
-    const int64_t per_xcd = ceil_div(n_tiles, 8);
     const bool vec = (ld_x % 8 == 0) && (d % 8 == 0) && ((uintptr_t)X % 16 == 0);
     const bool bf = dt == GPTQ_BF16;
     const uint16_t* x = (const uint16_t*)X;
@@ -575,17 +656,24 @@ gptq_status hessian_launch(double* H, const void* X, gptq_dtype dt, int64_t n_to
             nblk_next = ceil_div(nx.ch, TSPAN);
             n_tr = nblk_next * npair;
         }
+        const int64_t S = syrk_slices(n_tiles, ch / KT);
+        const int64_t per_xcd = ceil_div(n_tiles * S, 8);
         const dim3 grid((unsigned)(per_xcd * 8 + n_tr)), block(SYRK_WAVES * 64);
         uint16_t* xt = slot_xt(ci);
         if (ev) GPTQ_HIP(hipEventRecord(ev[2 * ci], s));
         if (bf) {
-            if (vec) hipLaunchKernelGGL((hess_syrk_kernel<bf16x8_t, SYRK_WAVES, true>), grid, block, RING_BYTES, s, H, xt, ch, d_pad, d, T, n_tiles, per_xcd, nx);
-            else hipLaunchKernelGGL((hess_syrk_kernel<bf16x8_t, SYRK_WAVES, false>), grid, block, RING_BYTES, s, H, xt, ch, d_pad, d, T, n_tiles, per_xcd, nx);
+            if (vec) hipLaunchKernelGGL((hess_syrk_kernel<bf16x8_t, SYRK_WAVES, true>), grid, block, RING_BYTES, s, H, xt, ch, d_pad, d, T, n_tiles, per_xcd, nx, S, part);
+            else hipLaunchKernelGGL((hess_syrk_kernel<bf16x8_t, SYRK_WAVES, false>), grid, block, RING_BYTES, s, H, xt, ch, d_pad, d, T, n_tiles, per_xcd, nx, S, part);
         } else {
-            if (vec) hipLaunchKernelGGL((hess_syrk_kernel<h16x8_t, SYRK_WAVES, true>), grid, block, RING_BYTES, s, H, xt, ch, d_pad, d, T, n_tiles, per_xcd, nx);
-            else hipLaunchKernelGGL((hess_syrk_kernel<h16x8_t, SYRK_WAVES, false>), grid, block, RING_BYTES, s, H, xt, ch, d_pad, d, T, n_tiles, per_xcd, nx);
+            if (vec) hipLaunchKernelGGL((hess_syrk_kernel<h16x8_t, SYRK_WAVES, true>), grid, block, RING_BYTES, s, H, xt, ch, d_pad, d, T, n_tiles, per_xcd, nx, S, part);
+            else hipLaunchKernelGGL((hess_syrk_kernel<h16x8_t, SYRK_WAVES, false>), grid, block, RING_BYTES, s, H, xt, ch, d_pad, d, T, n_tiles, per_xcd, nx, S, part);
         }
         GPTQ_LAUNCH_CHECK();
+        if (S > 1) {
+            hipLaunchKernelGGL(syrk_slices_add_kernel, dim3((unsigned)(n_tiles * (BT / 4))), dim3(BT), 0, s, H, part, T,
+                               S, d);
+            GPTQ_LAUNCH_CHECK();
+        }
         if (ev) GPTQ_HIP(hipEventRecord(ev[2 * ci + 1], s));
         if (n_tr > 0) {
             hipLaunchKernelGGL(diag_add_kernel, dgrid, b256, 0, s, slot_part(ci + 1), nblk_next, d, H);

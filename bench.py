@@ -81,7 +81,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--tokens", type=int, default=None, help="override the token count (testing only)")
-    ap.add_argument("--workload", choices=("quantize", "dequant", "shapes"), default="quantize")
+    ap.add_argument("--workload", choices=("quantize", "dequant", "shapes", "stack"), default="quantize")
+    ap.add_argument("--blocks", type=int, default=2, help="stack workload: decoder blocks")
+    ap.add_argument("--stack-tokens", type=int, default=2048, help="stack workload: calibration tokens")
     ap.add_argument("--rounds", type=int, default=None, help="dequant workload: timed rounds per token count")
     ap.add_argument("--dq-tokens", type=str, default="1,4,16", help="dequant workload: token counts")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -346,6 +348,53 @@ def shapes_main(a):
                       "shapes": rows}))
 
 
+def stack_main(a):
+    """Blocks of workload 5's shape (hidden 12288, ffn 49152, fp16, 3-bit
+    g128) quantized in sequence by the sequential driver: every layer's
+    Hessian from the already-quantized upstream outputs, products from the
+    packed words.  Weights and X0 drawn on the device."""
+    import torch
+
+    import post_weight_quantization_accum_amd as P
+    from post_weight_quantization_accum_amd import sequential as S
+    from post_weight_quantization_accum_amd.configs import WORKLOADS
+
+    wl = WORKLOADS[5]
+    q = wl.quants[0]
+    hidden, ffn = 12288, 49152
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(5005)
+    cfg = P.make_config(bits=q.bits, group_size=q.group_size, sym=q.sym, act_order=q.act_order, block=q.block,
+                        damp=q.damp)
+
+    def block(hh, ff):
+        def w(o, i):
+            return (torch.randn((o, i), generator=g, device=dev) * wl.sigma_w).half()
+        return S.Block(q=w(hh, hh), k=w(hh, hh), v=w(hh, hh), out=w(hh, hh), fc1=w(ff, hh), fc2=w(hh, ff))
+
+    # warm-up on a small stack (first launches, allocator)
+    S.quantize_stack([block(256, 1024)], torch.randn((2048, 256), generator=g, device=dev).half(), cfg,
+                     want_w_hat=False)
+    blocks = [block(hidden, ffn) for _ in range(a.blocks)]
+    X0 = torch.randn((a.stack_tokens, hidden), generator=g, device=dev).half()
+    torch.cuda.synchronize()
+    stats = S.new_stats()
+    t0 = time.perf_counter()
+    _, Xout = S.quantize_stack(blocks, X0, cfg, stats, want_w_hat=False)
+    torch.cuda.synchronize()
+    total = time.perf_counter() - t0
+    n_w = a.blocks * (4 * hidden * hidden + 2 * hidden * ffn)
+    print(json.dumps({"metric": "sequential quantization of decoder blocks (workload 5 shapes)",
+                      "value": n_w / total, "unit": "weights/s", "n_gpus": 1, "higher_is_better": True,
+                      "s_total": round(total, 3), "s_per_block": round(total / a.blocks, 3),
+                      "breakdown_s": {k.replace("_ms", ""): round(v / 1e3, 3) for k, v in stats.items()},
+                      "config": {"workload": f"{a.blocks} blocks, hidden {hidden}, ffn {ffn}, fp16, {q.bits}-bit "
+                                             f"g{q.group_size}, {a.stack_tokens} calibration tokens",
+                                 "weights": n_w},
+                      "data": "synthetic (device normal)", "output_finite": bool(torch.isfinite(Xout).all())}))
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -357,6 +406,9 @@ def main():
         return
     if a.workload == "shapes":
         shapes_main(a)
+        return
+    if a.workload == "stack":
+        stack_main(a)
         return
 
     import torch

@@ -28,6 +28,8 @@ from .gptq_oracle import (  # noqa: F401
     unpack,
     pack_permuted,
     dequant_matmul,
+    round_to_dtype,
+    quantize_block_chain,
     dequantize,
     layer_loss,
     words_per_row,

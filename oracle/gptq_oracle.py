@@ -441,3 +441,52 @@ def dequant_matmul(X, words, bits: int, d_in: int, scales, zeros, *, g_idx=None,
     if perm is not None:
         X64 = X64[:, np.asarray(perm, dtype=np.int64)]
     return X64 @ W_stream.T
+
+
+# ---------------------------------------------------------------------------
+# Layers in sequence.
+# ---------------------------------------------------------------------------
+
+def round_to_dtype(a, dtype: str) -> np.ndarray:
+    """Round float64 values to the activation dtype and back (nearest, ties
+    to even): "f32", "f16", or "bf16" (through float32, then the upper 16
+    bits of the float32 pattern with round-to-nearest-even)."""
+    a = np.asarray(a, dtype=np.float64)
+    if dtype == "f16":
+        return a.astype(np.float16).astype(np.float64)
+    f = a.astype(np.float32)
+    if dtype == "f32":
+        return f.astype(np.float64)
+    u = f.view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return (r.astype(np.uint32)).view(np.float32).astype(np.float64)
+
+
+def quantize_block_chain(Ws: dict, X, dtype: str, **q):
+    """One decoder block quantized in sequence ("GPTQ量化算法深度解析" §3.1,
+    layers one after another; "GPTQ论文复现指南" §3.2, --true-sequential:
+    each layer sees the already-quantized outputs of the layers before it).
+    With no attention or normalisation details on the pages the block is a
+    plain chain: q, k, v on H(X); A = X W_v^T -> out; h1 = X + A W_out^T ->
+    fc1; r = relu(h1 W_fc1^T) -> fc2; the block's output h1 + r W_fc2^T.
+    Products use the quantized weights in float64; every activation that
+    feeds a Hessian or a product is rounded to `dtype`.
+    Returns (per-layer gptq_quantize outputs, per-layer inputs, output)."""
+    X = np.asarray(X, dtype=np.float64)
+    res, inputs = {}, {}
+    H = hessian(X)
+    for n in ("q", "k", "v"):
+        res[n] = gptq_quantize(Ws[n], H, **q)
+        inputs[n] = X
+    A = round_to_dtype(X @ res["v"]["w_hat"].T, dtype)
+    res["out"] = gptq_quantize(Ws["out"], X=A, **q)
+    inputs["out"] = A
+    h1 = X + A @ res["out"]["w_hat"].T
+    h1r = round_to_dtype(h1, dtype)
+    res["fc1"] = gptq_quantize(Ws["fc1"], X=h1r, **q)
+    inputs["fc1"] = h1r
+    r = round_to_dtype(np.maximum(h1r @ res["fc1"]["w_hat"].T, 0.0), dtype)
+    res["fc2"] = gptq_quantize(Ws["fc2"], X=r, **q)
+    inputs["fc2"] = r
+    out = round_to_dtype(h1 + r @ res["fc2"]["w_hat"].T, dtype)
+    return res, inputs, out

@@ -500,3 +500,49 @@ def test_dequant_matmul_reproduces_solver_weights(bits, gs):
     # sorted packing = packing of the permuted code matrix, read back position by position
     back = O.unpack(O.pack_permuted(out["codes"], bits, out["perm"]), bits, d_in)
     assert np.array_equal(back, out["codes"][:, out["perm"]])
+
+
+# ---------------------------------------------------------------------------
+# Layers in sequence.
+# ---------------------------------------------------------------------------
+
+def _on_grid_weights(rng, d_out, d_in, s):
+    # every row holds codes 0..15 around zero point 8, so min/max of the row
+    # map exactly onto the 4-bit grid: quantization (and compensation) is exact
+    c = rng.integers(0, 16, size=(d_out, d_in))
+    c[:, 0], c[:, 1] = 0, 15
+    return s * (c - 8.0)
+
+
+@pytest.mark.parametrize("act_order", [False, True])
+def test_block_chain_reduces_to_float_block_when_lossless(act_order):
+    rng = np.random.default_rng(700)
+    h, ffn, n = 16, 32, 400
+    s = 2.0 ** -6
+    Ws = {"q": _on_grid_weights(rng, h, h, s), "k": _on_grid_weights(rng, h, h, s),
+          "v": _on_grid_weights(rng, h, h, s), "out": _on_grid_weights(rng, h, h, s),
+          "fc1": _on_grid_weights(rng, ffn, h, s), "fc2": _on_grid_weights(rng, h, ffn, s)}
+    X = O.round_to_dtype(rng.standard_normal((n, h)), "f16")
+    res, inputs, out = O.quantize_block_chain(Ws, X, "f16", bits=4, group_size=-1, act_order=act_order,
+                                              block=8, damp=0.01)
+    for name in Ws:
+        assert np.array_equal(res[name]["w_hat"], Ws[name]), name
+    # the float block written out directly
+    r16 = lambda a: a.astype(np.float16).astype(np.float64)  # noqa: E731
+    A = r16(X @ Ws["v"].T)
+    h1 = X + A @ Ws["out"].T
+    h1r = r16(h1)
+    r = r16(np.maximum(h1r @ Ws["fc1"].T, 0.0))
+    want = r16(h1 + r @ Ws["fc2"].T)
+    assert np.array_equal(inputs["out"], A)
+    assert np.array_equal(inputs["fc1"], h1r)
+    assert np.array_equal(inputs["fc2"], r)
+    assert np.array_equal(out, want)
+
+
+def test_round_to_dtype_bf16_ties_and_range():
+    # bf16 keeps 8 significant bits: 1 + 2^-8 is a tie between 1 and 1 + 2^-7 (even: 1);
+    # 1 + 3 * 2^-8 ties up to 1 + 2^-6 (even mantissa)
+    v = np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, 1.0 + 2.0 ** -8 + 2.0 ** -20, -2.5])
+    got = O.round_to_dtype(v, "bf16")
+    assert np.array_equal(got, [1.0, 1.0 + 2.0 ** -6, 1.0 + 2.0 ** -7, -2.5])

@@ -62,6 +62,7 @@ struct DqArgs {
 // Activation storage types: raw 16-bit patterns for bf16 and f16, float for f32.
 struct Bf16 {
     typedef uint16_t store;
+    typedef bf16x8_t mfma_tag;
     static constexpr int MB = 7, BIAS = 127;
     static constexpr uint32_t NAN_BITS = 0x7FC0u, ONES = 0x3F803F80u;
     static __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
@@ -71,6 +72,7 @@ struct Bf16 {
 };
 struct F16 {
     typedef uint16_t store;
+    typedef h16x8_t mfma_tag;
     static constexpr int MB = 10, BIAS = 15;
     static constexpr uint32_t NAN_BITS = 0x7E00u, ONES = 0x3C003C00u;
     static __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
@@ -755,6 +757,263 @@ __global__ __launch_bounds__(ST_THREADS) void dequant_staged_kernel(DqArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Many tokens: the same arithmetic on the matrix cores.
+//
+// A workgroup computes 128 tokens x 128 rows.  Per 32-column block it stages
+// the activations (A operands) and the rows' codes as exact half-precision
+// values 2^b + c (B operands) in LDS, in MFMA operand order, and each of its
+// four waves runs a 64x64 tile with v_mfma_f32_32x32x16.  The products of one
+// group accumulate in float32 by themselves; at the group's end each lane
+// adds s * (P - (2^b + z) * sum x) to its float32 output, with sum x taken
+// from the A operands (v_dot2 with ones) and moved to the output layout by
+// lane shuffles.  The next block's global loads are in flight while the
+// current block computes (two LDS buffers, one barrier per block).
+// ---------------------------------------------------------------------------
+constexpr int MM_TILE = 128;
+constexpr int MM_THREADS = 256;
+constexpr int MM_OP_BYTES = 2 * 4 * 64 * 16;       // [k-step][32-wide tile][lane][16 B]
+constexpr int MM_STAGE_BYTES = 2 * MM_OP_BYTES;    // A, then B
+constexpr int64_t MM_MIN_TOKENS = 128;
+
+// The 16 codes 16h .. 16h+15 of a 32-column block (h = 0, 1), as two B
+// operands: op[q] holds codes 8q .. 8q+7 as values 2^b + c.
+template <int BITS, typename T>
+__device__ __forceinline__ void mm_code_operands(const uint32_t (&w)[BITS], int h, u32x4_t (&op)[2]) {
+    constexpr int SH = T::MB - BITS;
+    constexpr uint32_t E = (uint32_t)(T::BIAS + BITS) << T::MB;
+    constexpr uint32_t M = (1u << BITS) - 1u;
+    uint64_t win0, win1 = 0;
+    if constexpr (BITS == 2) {
+        win0 = h ? w[1] : w[0];
+    } else if constexpr (BITS == 3) {
+        const uint64_t lo = ((uint64_t)w[1] << 32) | w[0], hi = ((uint64_t)w[2] << 32) | w[1];
+        win0 = h ? (hi >> 16) : lo;
+    } else if constexpr (BITS == 4) {
+        win0 = h ? (((uint64_t)w[3] << 32) | w[2]) : (((uint64_t)w[1] << 32) | w[0]);
+    } else {
+        win0 = h ? (((uint64_t)w[5] << 32) | w[4]) : (((uint64_t)w[1] << 32) | w[0]);
+        win1 = h ? (((uint64_t)w[7] << 32) | w[6]) : (((uint64_t)w[3] << 32) | w[2]);
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        uint32_t v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int e0 = 8 * q + 2 * j, e1 = e0 + 1;
+            uint32_t c0, c1;
+            if constexpr (BITS == 8) {
+                c0 = (uint32_t)(((e0 < 8 ? win0 : win1) >> (8 * (e0 & 7))) & M);
+                c1 = (uint32_t)(((e1 < 8 ? win0 : win1) >> (8 * (e1 & 7))) & M);
+            } else {
+                c0 = (uint32_t)((win0 >> (BITS * e0)) & M);
+                c1 = (uint32_t)((win0 >> (BITS * e1)) & M);
+            }
+            v[j] = (E | (c0 << SH)) | ((E | (c1 << SH)) << 16);
+        }
+        op[q] = u32x4_t{v[0], v[1], v[2], v[3]};
+    }
+}
+
+template <int BITS, typename T>
+__global__ __launch_bounds__(MM_THREADS, 2) void dequant_mfma_kernel(DqArgs a, int64_t n_mt, int64_t n_rt,
+                                                                     int64_t per_xcd) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds_u8[];
+    char* lds = (char*)lds_u8;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // XCD-grouped order: the row tiles of one token tile run on one XCD
+    const int64_t b = blockIdx.x;
+    const int64_t lin = (b % 8) * per_xcd + b / 8;
+    if (lin >= n_mt * n_rt) return;
+    const int64_t mt = lin / n_rt, rt = lin % n_rt;
+    const int64_t t0 = mt * MM_TILE, n0 = rt * MM_TILE;
+    const uint16_t* X = (const uint16_t*)a.X;
+    const uint32_t d_in = (uint32_t)a.d_in;
+    const uint32_t nkb = (uint32_t)ceil_div(a.d_in, 32);
+    const uint32_t bpg = a.gsize >= a.d_in ? nkb : (uint32_t)(a.gsize >> 5);
+    constexpr float OFF = (float)(1 << BITS);
+    const __amdgpu_buffer_rsrc_t rs = words_rsrc(a, n0 < a.d_out ? n0 : a.d_out);
+    const uint32_t row_bytes = (uint32_t)a.wpr * 4;
+
+    // staging assignments: two 16-byte activation pieces per thread (token
+    // p >> 2, columns 8 (p & 3) ..), and one row's half block of codes
+    const int srow = tid >> 1, sh = tid & 1;
+    auto load_x = [&](uint32_t kb, u32x4_t (&xv)[2]) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int p = tid + MM_THREADS * j, t = p >> 2, q = p & 3;
+            const int64_t tok = t0 + t;
+            const uint32_t k = kb * 32 + 8 * q;
+            const uint16_t* xr = X + tok * a.ld_x + k;
+            if (tok < a.n_tok && a.xvec && k + 8 <= d_in) {
+                xv[j] = *(const u32x4_t*)xr;
+            } else {
+                uint32_t e[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) e[i] = (tok < a.n_tok && k + i < d_in) ? xr[i] : 0u;
+                xv[j] = u32x4_t{e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16)};
+            }
+        }
+    };
+    auto load_w = [&](uint32_t kb, uint32_t (&w)[BITS]) {
+        const uint32_t o = (uint32_t)srow * row_bytes + kb * (uint32_t)(BITS * 4);
+        if constexpr (BITS == 2) {
+            const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(rs, o, 0, 0);
+            w[0] = v.x;
+            w[1] = v.y;
+        } else if constexpr (BITS == 3) {
+            const u32x3_t v = __builtin_amdgcn_raw_buffer_load_b96(rs, o, 0, 0);
+            w[0] = v.x;
+            w[1] = v.y;
+            w[2] = v.z;
+        } else {
+#pragma unroll
+            for (int q = 0; q < BITS; q += 4) {
+                const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rs, o + 4 * q, 0, 0);
+                w[q] = v.x;
+                w[q + 1] = v.y;
+                w[q + 2] = v.z;
+                w[q + 3] = v.w;
+            }
+        }
+    };
+    auto store_stage = [&](int buf, const u32x4_t (&xv)[2], const uint32_t (&w)[BITS]) {
+        char* st = lds + buf * MM_STAGE_BYTES;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int p = tid + MM_THREADS * j, t = p >> 2, q = p & 3;
+            const int ks = q >> 1, kh = q & 1;
+            *(u32x4_t*)(st + (((ks * 4 + (t >> 5)) * 64) + (t & 31) + 32 * kh) * 16) = xv[j];
+        }
+        u32x4_t op[2];
+        mm_code_operands<BITS, T>(w, sh, op);
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+            *(u32x4_t*)(st + MM_OP_BYTES + (((sh * 4 + (srow >> 5)) * 64) + (srow & 31) + 32 * kh) * 16) = op[kh];
+    };
+
+    const int wm = wave >> 1, wn = wave & 1;     // the wave's 64x64: token tiles 2wm, 2wm+1; row tiles 2wn, 2wn+1
+    f16_t acc[2][2], accg[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                acc[i][j][r] = 0.0f;
+                accg[i][j][r] = 0.0f;
+            }
+    float xpart[2] = {0.0f, 0.0f};
+    float sv[2], ov[2];
+    auto load_group_params = [&](uint32_t g) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int64_t row = n0 + (2 * wn + j) * 32 + (lane & 31);
+            const bool ok = row < a.d_out;
+            const int64_t idx = ok ? (int64_t)g * a.d_out + row : 0;
+            const float sl = a.scales[idx], zl = a.zeros[idx];
+            sv[j] = ok ? sl : 0.0f;
+            ov[j] = OFF + (ok ? zl : 0.0f);
+        }
+    };
+
+    {
+        u32x4_t xv[2];
+        uint32_t w[BITS];
+        load_x(0, xv);
+        load_w(0, w);
+        store_stage(0, xv, w);
+    }
+    load_group_params(0);
+    __syncthreads();
+    for (uint32_t kb = 0; kb < nkb; ++kb) {
+        const bool more = kb + 1 < nkb;
+        u32x4_t xv[2];
+        uint32_t w[BITS];
+        if (more) {
+            load_x(kb + 1, xv);
+            load_w(kb + 1, w);
+        }
+        const char* st = lds + (kb & 1) * MM_STAGE_BYTES;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            u32x4_t av[2], bv[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) av[i] = *(const u32x4_t*)(st + ((ks * 4 + 2 * wm + i) * 64 + lane) * 16);
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                bv[j] = *(const u32x4_t*)(st + MM_OP_BYTES + ((ks * 4 + 2 * wn + j) * 64 + lane) * 16);
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) accg[i][j] = mfma_32x32x16(av[i], bv[j], accg[i][j], (typename T::mfma_tag*)nullptr);
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                xpart[i] = T::dot2(av[i].x, T::ONES, xpart[i]);
+                xpart[i] = T::dot2(av[i].y, T::ONES, xpart[i]);
+                xpart[i] = T::dot2(av[i].z, T::ONES, xpart[i]);
+                xpart[i] = T::dot2(av[i].w, T::ONES, xpart[i]);
+            }
+        }
+        if ((kb + 1) % bpg == 0 || !more) {
+            // group end: acc += s * (P - (2^b + z) * sum x); the token of
+            // element r of lane l is 8 (r / 4) + 4 (l / 32) + r % 4
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const float xt = xpart[i] + __shfl_xor(xpart[i], 32, 64);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float x = __shfl(xt, 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3), 64);
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        acc[i][j][r] = fmaf(sv[j], fmaf(-ov[j], x, accg[i][j][r]), acc[i][j][r]);
+                        accg[i][j][r] = 0.0f;
+                    }
+                }
+                xpart[i] = 0.0f;
+            }
+            if (more) load_group_params((kb + 1) / bpg);
+        }
+        if (more) store_stage((kb + 1) & 1, xv, w);
+        __syncthreads();
+    }
+    // outputs: element r of lane l of tile (i, j) is token 8 (r / 4) + 4 (l / 32) + r % 4, row l % 32
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int64_t row = n0 + (2 * wn + j) * 32 + (lane & 31);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int64_t tok = t0 + (2 * wm + i) * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                if (tok < a.n_tok && row < a.d_out) a.Y[tok * a.ld_y + row] = acc[i][j][r];
+            }
+        }
+}
+
+template <int BITS, typename T>
+gptq_status launch_mfma(const DqArgs& a, hipStream_t s) {
+    const int64_t n_mt = ceil_div(a.n_tok, MM_TILE), n_rt = ceil_div(a.d_out, MM_TILE);
+    const int64_t per_xcd = ceil_div(n_mt * n_rt, 8);
+    hipLaunchKernelGGL((dequant_mfma_kernel<BITS, T>), dim3((unsigned)(per_xcd * 8)), dim3(MM_THREADS),
+                       2 * MM_STAGE_BYTES, s, a, n_mt, n_rt, per_xcd);
+    GPTQ_LAUNCH_CHECK();
+    return GPTQ_OK;
+}
+
+template <typename T>
+gptq_status by_bits_mfma(const DqArgs& a, int bits, hipStream_t s) {
+    switch (bits) {
+        case 2: return launch_mfma<2, T>(a, s);
+        case 3: return launch_mfma<3, T>(a, s);
+        case 4: return launch_mfma<4, T>(a, s);
+        case 8:
+            if constexpr (T::MB - 8 >= 0) return launch_mfma<8, T>(a, s);
+            break;
+    }
+    return GPTQ_ERR_INVALID_ARG;
+}
+
 template <int BITS, int TM, typename T>
 gptq_status launch_block(const DqArgs& a, hipStream_t s) {
     const dim3 grid((unsigned)ceil_div(a.d_out, RW), (unsigned)ceil_div(a.n_tok, TM));
@@ -838,6 +1097,11 @@ gptq_status dequant_matmul_launch(const void* X, gptq_dtype dt, int64_t n_tok, i
     a.xvec = (dt != GPTQ_F32) && ((uintptr_t)X % 16 == 0) && ((ld_x * (int64_t)xb) % 16 == 0);
     const bool block_path = dequant_uses_block_path(dt, bits, d_in, group_size, g_idx != nullptr);
     if (!block_path && n_groups > DQ_MAX_GROUPS) return GPTQ_ERR_UNSUPPORTED;
+    if (block_path && !perm && n_tok >= MM_MIN_TOKENS) {
+        // many tokens in natural order: matrix cores (grid in x only)
+        if (dt == GPTQ_BF16) return by_bits_mfma<Bf16>(a, bits, s);
+        return by_bits_mfma<F16>(a, bits, s);
+    }
     // the grid's y dimension (token tiles) stays below 65536: larger token
     // counts go in several launches
     const int64_t tm = block_path ? (n_tok == 1 ? 1 : 4) : 1;

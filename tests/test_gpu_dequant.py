@@ -54,13 +54,29 @@ def _stream_order(L, mode, group_size):
     return L.codes, np.arange(d_in) // gs, np.arange(d_in)
 
 
-def _bound(L, X64, mode, group_size, bits):
+MM_MIN_TOKENS = 128   # natural order, block route: the matrix-core route from this many tokens
+
+
+def _mfma_route(L, mode, group_size, dtype, bits):
+    d_in = L.codes.shape[1]
+    block = dtype != "f32" and not (dtype == "bf16" and bits == 8) and mode != "g_idx" and \
+        (group_size <= 0 or group_size >= d_in or group_size % 32 == 0)
+    return block and mode == "natural" and L.X.shape[0] >= MM_MIN_TOKENS
+
+
+def _bound(L, X64, mode, group_size, bits, dtype=None):
     c, g, a = _stream_order(L, mode, group_size)
     S = L.scales.astype(np.float64)[g].T            # d_out x d_in, stream order
     Z = L.zeros.astype(np.float64)[g].T
     mag = S * (c.astype(np.float64) + Z + 2.0 ** (bits + 1))
     A = np.abs(X64[:, a]) @ mag.T
     d_in = L.codes.shape[1]
+    if dtype is not None and _mfma_route(L, mode, group_size, dtype, bits):
+        # matrix cores: a group's products summed in float32 (<= glen roundings),
+        # its sum of x by v_dot2 (<= glen), two FMAs, one addition per group
+        glen = group_size if 0 < group_size < d_in else d_in
+        ng = -(-d_in // glen)
+        return (2 * glen + ng + 8) * U32 * A
     nb = -(-(-(-d_in // 32)) // 256)
     return (96 + 32 * nb) * U32 * A
 
@@ -115,6 +131,13 @@ CASES = [
     (4, "f16", "natural", 25, 1, 19, 500),      # column route, group size not a multiple of 32
     (2, "f32", "perm", 16, 4, 8, 300),          # column route with the gather
     (4, "f16", "g_idx", 32, 2, 9, 33),          # tiny: one full block plus one column
+    # many tokens in natural order: the matrix-core route (128x128 tiles)
+    (4, "bf16", "natural", 128, 300, 200, 1000),    # ragged token, row and column tiles
+    (3, "f16", "natural", 64, 129, 130, 777),
+    (2, "bf16", "natural", -1, 128, 64, 96),
+    (8, "f16", "natural", 128, 256, 72, 640),
+    (4, "f16", "natural", 32, 1000, 384, 2048),
+    (3, "bf16", "natural", 96, 170, 257, 2000),
 ]
 
 
@@ -124,7 +147,7 @@ def test_dequant_matmul_matches_oracle(bits, dtype, mode, gs, n_tok, d_out, d_in
     L = synth.make_packed_layer(d_out, d_in, n_tok, bits=bits, group_size=gs, dtype=dtype,
                                 seed=bits * 1000 + d_in)
     Y, ref, X64 = _run(L, mode, bits, gs)
-    tol = _bound(L, X64, mode, gs, bits)
+    tol = _bound(L, X64, mode, gs, bits, dtype)
     err = np.abs(Y - ref)
     assert np.all(np.isfinite(Y))
     assert np.all(err <= tol), f"max err/tol {np.max(err / tol):.3g}"
@@ -149,12 +172,14 @@ def test_dequant_matmul_strided_unaligned_activations():
     (4, "bf16", "natural", 128, 1111), (8, "f16", "perm", 128, 1111),
     (4, "bf16", "g_idx", 128, 1111), (8, "bf16", "natural", 128, 1280), (3, "f32", "perm", 40, 1111),
 ])
-def test_dequant_matmul_exact_on_integer_data(bits, dtype, mode, gs, d_in):
+@pytest.mark.parametrize("n_tok", [5, 200])
+def test_dequant_matmul_exact_on_integer_data(bits, dtype, mode, gs, d_in, n_tok):
     # integer activations in [-8, 8] and scales 2^-3 or 2^-5: every partial
     # sum is a multiple of 2^-5 below 2^19, exact in float32 and float64.
     # d_in = 1280 keeps the activation rows 16-byte aligned (vector loads and
-    # byte permutes), 1111 takes the element-wise loads and a ragged block.
-    d_out, n_tok = 29, 5
+    # byte permutes), 1111 takes the element-wise loads and a ragged block;
+    # 200 tokens take the matrix-core route in natural order.
+    d_out = 29
     L = synth.make_packed_layer(d_out, d_in, n_tok, bits=bits, group_size=gs, dtype=dtype, seed=500 + bits)
     rng = np.random.default_rng(900 + bits)
     xi = rng.integers(-8, 9, size=(n_tok, d_in)).astype(np.float32)
@@ -162,6 +187,17 @@ def test_dequant_matmul_exact_on_integer_data(bits, dtype, mode, gs, d_in):
     L.scales = np.where(rng.random(L.scales.shape) < 0.5, 2.0 ** -3, 2.0 ** -5).astype(np.float32)
     Y, ref, _ = _run(L, mode, bits, gs)
     assert np.array_equal(Y, ref)
+
+
+def test_dequant_matmul_headline_layer_many_tokens():
+    # 4096 x 11008, 4-bit g128, natural order, 512 tokens: the matrix-core route
+    d_out, d_in, bits, gs, n_tok = 4096, 11008, 4, 128, 512
+    L = synth.make_packed_layer(d_out, d_in, n_tok, bits=bits, group_size=gs, dtype="bf16", seed=512)
+    Y, ref, X64 = _run(L, "natural", bits, gs)
+    err = np.abs(Y - ref)
+    tol = _bound(L, X64, "natural", gs, bits, "bf16")
+    assert np.all(err <= tol), f"max err/tol {np.max(err / tol):.3g}"
+    assert np.median(err / np.maximum(np.abs(ref), 1e-30)) < 1e-5
 
 
 @pytest.mark.parametrize("mode", ["perm", "g_idx"])

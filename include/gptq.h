@@ -230,7 +230,9 @@ gptq_status gptq_pack_permuted(const uint8_t* codes, int64_t d_out, int64_t d_in
  * a group size that is a multiple of 32 (or one group), the codes enter
  * half-precision dot products exactly as 2^bits + c and the offset is
  * removed per 32 columns in float32 (8-bit codes with bf16 activations take
- * the per-column route); otherwise each weight is formed once in float32.
+ * the per-column route); from 128 tokens on, without perm, the same values
+ * go through the matrix cores with float32 sums per group; otherwise each
+ * weight is formed once in float32.
  * Errors (before any launch): GPTQ_ERR_INVALID_ARG for a bad dtype or bits,
  * sizes outside [0, 2^20] (d_in >= 1), ld_x < d_in, ld_y < d_out, both perm
  * and g_idx given, an n_groups that does not match, or a null pointer;
@@ -239,6 +241,19 @@ gptq_status gptq_pack_permuted(const uint8_t* codes, int64_t d_out, int64_t d_in
  * not read through: they make the affected outputs NaN.  n_tok == 0 or
  * d_out == 0: nothing is launched.  Asynchronous on `stream`; no allocation.
  * ------------------------------------------------------------------------ */
+/* Column gather Xg[t][k] = X[t][perm[k]] ("GPTQ量化算法深度解析" §3.3:
+ * act-order puts a gather in front of inference).  With the words from
+ * gptq_pack_permuted, gptq_dequant_matmul(Xg, ..., perm = NULL, g_idx =
+ * NULL) computes the same product as with perm, and from 128 tokens on it
+ * takes the matrix-core route.  X: device, n_tok x d_in, row stride ld_x;
+ * Xg: device, n_tok x d_in, row stride ld_g (caller-owned, not aliasing X);
+ * both of x_dtype.  perm entries outside [0, d_in) give NaN.
+ * Errors: GPTQ_ERR_INVALID_ARG for a bad dtype, sizes, strides or a null
+ * pointer (n_tok == 0: nothing is launched).  Asynchronous. */
+gptq_status gptq_gather_columns(const void* X, gptq_dtype x_dtype, int64_t n_tok, int64_t d_in,
+                                int64_t ld_x, const int32_t* perm, void* Xg, int64_t ld_g,
+                                hipStream_t stream);
+
 int64_t gptq_dequant_max_groups(void);
 gptq_status gptq_dequant_matmul(const void* X, gptq_dtype x_dtype, int64_t n_tok, int64_t d_in,
                                 int64_t ld_x, const uint32_t* packed, int32_t bits,

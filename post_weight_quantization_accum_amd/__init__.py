@@ -19,7 +19,7 @@ from ._lib import (  # noqa: F401
 )
 
 __all__ = ["hessian_accumulate", "hessian_accumulate_timed", "prepare_hinv", "quantize_layer", "pack", "quantize",
-           "pack_permuted", "dequant_matmul", "dequant_max_groups", "packed_words_per_row", "make_config",
+           "pack_permuted", "dequant_matmul", "dequant_max_groups", "gather_columns", "packed_words_per_row", "make_config",
            "Config", "load"]
 
 
@@ -238,6 +238,26 @@ def dequant_matmul(X, packed, bits: int, scales, zeros, *, g_idx=None, perm=None
                                  _ptr(scales), _ptr(zeros), scales.shape[0], _ptr(g_idx), _ptr(perm),
                                  int(group_size), d_out, _ptr(out), out.stride(0), _stream(stream))
     _lib.check(st, "gptq_dequant_matmul")
+    return out
+
+
+def gather_columns(X, perm, out=None, stream=None):
+    """Xg[t][k] = X[t][perm[k]] (the activations in quantization order)."""
+    lib = load()
+    torch = _torch()
+    _require_cuda(X, perm)
+    if X.dim() != 2 or X.stride(1) != 1:
+        raise ValueError("X must be 2-D with unit column stride")
+    n_tok, d_in = X.shape
+    if perm.dtype != torch.int32 or perm.numel() != d_in or not perm.is_contiguous():
+        raise TypeError("perm must be contiguous int32 of length d_in")
+    if out is None:
+        out = torch.empty((n_tok, d_in), dtype=X.dtype, device=X.device)
+    if out.dtype != X.dtype or out.shape != X.shape or out.stride(1) != 1:
+        raise TypeError("out must match X in dtype and shape, with unit column stride")
+    st = lib.gptq_gather_columns(_ptr(X), _dtype_code(X), n_tok, d_in, X.stride(0), _ptr(perm), _ptr(out),
+                                 out.stride(0), _stream(stream))
+    _lib.check(st, "gptq_gather_columns")
     return out
 
 

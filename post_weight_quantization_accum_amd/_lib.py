@@ -23,7 +23,8 @@ EXPORTS = (
     "gptq_config_default", "gptq_hessian_workspace", "gptq_hessian_accumulate", "gptq_hessian_accumulate_timed",
     "gptq_prepare_hinv_workspace", "gptq_prepare_hinv", "gptq_quantize_layer_workspace",
     "gptq_quantize_layer", "gptq_packed_words_per_row", "gptq_pack", "gptq_pack_permuted",
-    "gptq_dequant_max_groups", "gptq_dequant_matmul", "gptq_status_string", "gptq_version",
+    "gptq_dequant_max_groups", "gptq_dequant_matmul", "gptq_gather_columns", "gptq_status_string",
+    "gptq_version",
 )
 
 
@@ -114,6 +115,8 @@ def load(path: str | None = None):
     lib.gptq_dequant_matmul.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, i32, vp, vp, i64, vp, vp, i32, i64,
                                         vp, i64, vp]
     lib.gptq_dequant_matmul.restype = ctypes.c_int
+    lib.gptq_gather_columns.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, vp, i64, vp]
+    lib.gptq_gather_columns.restype = ctypes.c_int
     _lib = lib
     return lib
 

@@ -167,6 +167,16 @@ gptq_status gptq_pack_permuted(const uint8_t* codes, int64_t d_out, int64_t d_in
 
 int64_t gptq_dequant_max_groups(void) { return dequant_max_groups(); }
 
+gptq_status gptq_gather_columns(const void* X, gptq_dtype x_dtype, int64_t n_tok, int64_t d_in, int64_t ld_x,
+                                const int32_t* perm, void* Xg, int64_t ld_g, hipStream_t stream) {
+    if (!valid_dtype(x_dtype)) return GPTQ_ERR_INVALID_ARG;
+    if (n_tok < 0 || d_in <= 0 || n_tok > (int64_t(1) << 32) || d_in > MAX_DIM) return GPTQ_ERR_INVALID_ARG;
+    if (ld_x < d_in || ld_g < d_in) return GPTQ_ERR_INVALID_ARG;
+    if (n_tok == 0) return GPTQ_OK;
+    if (!X || !perm || !Xg) return GPTQ_ERR_INVALID_ARG;
+    return gather_columns_launch(X, x_dtype, n_tok, d_in, ld_x, perm, Xg, ld_g, stream);
+}
+
 gptq_status gptq_dequant_matmul(const void* X, gptq_dtype x_dtype, int64_t n_tok, int64_t d_in, int64_t ld_x,
                                 const uint32_t* packed, int32_t bits, const float* scales, const float* zeros,
                                 int64_t n_groups, const int32_t* g_idx, const int32_t* perm, int32_t group_size,

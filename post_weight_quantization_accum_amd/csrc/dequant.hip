@@ -1062,7 +1062,57 @@ gptq_status dispatch_block(const DqArgs& a, gptq_dtype dt, int bits, hipStream_t
     return by_bits_block<TM, F16>(a, bits, s);
 }
 
+// ---------------------------------------------------------------------------
+// Column gather Xg[t][k] = X[t][perm[k]] ("GPTQ量化算法深度解析" §3.3: with
+// act-order, inference gathers the activations into the quantization order).
+// A workgroup owns 16 token rows and walks the columns in chunks of 4096:
+// the chunk's perm entries go to LDS once, then every row is gathered with
+// coalesced writes (the reads stay inside one row).
+// ---------------------------------------------------------------------------
+constexpr int GA_ROWS = 16, GA_CHUNK = 4096;
+
+template <typename E>
+__global__ __launch_bounds__(256) void gather_columns_kernel(const E* __restrict__ X, int64_t n_tok, int64_t d_in,
+                                                             int64_t ld_x, const int32_t* __restrict__ perm,
+                                                             E* __restrict__ Xg, int64_t ld_g, E nan_value) {
+    __shared__ int32_t pl[GA_CHUNK];
+    const int tid = threadIdx.x;
+    const int64_t r0 = (int64_t)blockIdx.x * GA_ROWS;
+    for (int64_t c0 = 0; c0 < d_in; c0 += GA_CHUNK) {
+        const int nc = (d_in - c0 < GA_CHUNK) ? (int)(d_in - c0) : GA_CHUNK;
+        __syncthreads();
+        for (int k = tid; k < nc; k += 256) pl[k] = perm[c0 + k];
+        __syncthreads();
+        for (int rr = 0; rr < GA_ROWS; ++rr) {
+            const int64_t t = r0 + rr;
+            if (t >= n_tok) break;
+            const E* xr = X + t * ld_x;
+            E* gr = Xg + t * ld_g + c0;
+            for (int k = tid; k < nc; k += 256) {
+                const int32_t p = pl[k];
+                gr[k] = ((uint32_t)p < (uint64_t)d_in) ? xr[p] : nan_value;
+            }
+        }
+    }
+}
+
 }  // namespace
+
+gptq_status gather_columns_launch(const void* X, gptq_dtype dt, int64_t n_tok, int64_t d_in, int64_t ld_x,
+                                  const int32_t* perm, void* Xg, int64_t ld_g, hipStream_t s) {
+    if (n_tok == 0) return GPTQ_OK;
+    const dim3 grid((unsigned)ceil_div(n_tok, GA_ROWS));
+    if (dt == GPTQ_F32) {
+        hipLaunchKernelGGL(gather_columns_kernel<float>, grid, dim3(256), 0, s, (const float*)X, n_tok, d_in, ld_x,
+                           perm, (float*)Xg, ld_g, __builtin_nanf(""));
+    } else {
+        const uint16_t nan16 = dt == GPTQ_BF16 ? (uint16_t)Bf16::NAN_BITS : (uint16_t)F16::NAN_BITS;
+        hipLaunchKernelGGL(gather_columns_kernel<uint16_t>, grid, dim3(256), 0, s, (const uint16_t*)X, n_tok, d_in,
+                           ld_x, perm, (uint16_t*)Xg, ld_g, nan16);
+    }
+    GPTQ_LAUNCH_CHECK();
+    return GPTQ_OK;
+}
 
 int64_t dequant_max_groups() { return DQ_MAX_GROUPS; }
 

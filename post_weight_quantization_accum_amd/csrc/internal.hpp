@@ -79,6 +79,8 @@ gptq_status pack_launch(const uint8_t* codes, int64_t d_out, int64_t d_in, int32
 // Y = X W_hat^T from packed words (dequant.hip).  perm and g_idx as in
 // gptq_dequant_matmul; arguments already validated.
 int64_t dequant_max_groups();
+gptq_status gather_columns_launch(const void* X, gptq_dtype dt, int64_t n_tok, int64_t d_in, int64_t ld_x,
+                                  const int32_t* perm, void* Xg, int64_t ld_g, hipStream_t s);
 bool dequant_uses_block_path(gptq_dtype dt, int32_t bits, int64_t d_in, int64_t group_size, bool has_g_idx);
 gptq_status dequant_matmul_launch(const void* X, gptq_dtype dt, int64_t n_tok, int64_t d_in, int64_t ld_x,
                                   const uint32_t* packed, int32_t bits, const float* scales, const float* zeros,

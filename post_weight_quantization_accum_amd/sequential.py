@@ -17,7 +17,7 @@ layer norm, ReLU as in OPT):
 
 Every product uses the already-quantized weights, computed by
 gptq_dequant_matmul from the packed words (with act-order: packed in
-quantization order, activations gathered through perm).  Products come out
+quantization order, activations gathered into that order first).  Products come out
 in float32; residual sums are taken in float32 and every activation that
 feeds a Hessian or a product is rounded to the stack's dtype.  All steps of
 the method run in the library; this module only sequences the calls and
@@ -27,7 +27,8 @@ from __future__ import annotations
 
 import dataclasses
 
-from . import dequant_matmul, hessian_accumulate, load, pack, pack_permuted, prepare_hinv, quantize_layer
+from . import (dequant_matmul, gather_columns, hessian_accumulate, load, pack, pack_permuted, prepare_hinv,
+               quantize_layer)
 
 LAYERS = ("q", "k", "v", "out", "fc1", "fc2")
 
@@ -90,7 +91,11 @@ def _product(X, q, cfg, stats: dict | None):
     if stats is not None:
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-    if cfg.act_order:
+    if cfg.act_order and X.shape[0] >= 128:
+        # many tokens: gather once into quantization order, then the matrix-core route
+        Y = dequant_matmul(gather_columns(X, q["perm"]), q["packed"], cfg.bits, q["scales"], q["zeros"],
+                           group_size=cfg.group_size)
+    elif cfg.act_order:
         Y = dequant_matmul(X, q["packed"], cfg.bits, q["scales"], q["zeros"], perm=q["perm"],
                            group_size=cfg.group_size)
     else:

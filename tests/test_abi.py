@@ -118,6 +118,12 @@ def test_dequant_matmul_validation_before_any_launch():
     assert _dq(Y=None) == _lib.ERR_INVALID_ARG
     # the per-column route keeps [group][row] scales of 8 rows in LDS: bounded group count
     assert _dq(d_in=8192, ld_x=8192, g_idx=fake, n_groups=4096) == _lib.ERR_UNSUPPORTED
+    # the column gather
+    lib = P.load()
+    assert lib.gptq_gather_columns(fake, 7, 4, 8, 8, fake, fake, 8, None) == _lib.ERR_INVALID_ARG
+    assert lib.gptq_gather_columns(fake, 2, 4, 8, 7, fake, fake, 8, None) == _lib.ERR_INVALID_ARG
+    assert lib.gptq_gather_columns(fake, 2, 4, 8, 8, None, fake, 8, None) == _lib.ERR_INVALID_ARG
+    assert lib.gptq_gather_columns(fake, 2, 0, 8, 8, fake, fake, 8, None) == _lib.OK
     # empty products launch nothing
     assert _dq(n_tok=0) == _lib.OK
     assert _dq(d_out=0, ld_y=0) == _lib.OK

@@ -260,3 +260,47 @@ def test_quantized_layer_product_end_to_end():
     scale = np.abs(L.X_f64()[:3]) @ np.abs(out["w_hat"].double().cpu().numpy()).T
     for got in (Y, Y2):
         assert np.all(np.abs(got.double().cpu().numpy() - want) <= 1e-5 * scale)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_gather_columns_exact(dtype):
+    n_tok, d_in = 37, 5000      # two column chunks of 4096, ragged rows
+    L = synth.make_packed_layer(4, d_in, n_tok, bits=4, group_size=128, dtype=dtype, seed=41)
+    X = to_torch(L.X, dtype)
+    perm = torch.from_numpy(L.perm).to(DEV)
+    G = P.gather_columns(X, perm)
+    torch.cuda.synchronize()
+    want = X.cpu()[:, torch.from_numpy(L.perm).long()]
+    assert torch.equal(G.cpu().view(torch.int16) if dtype != "f32" else G.cpu(),
+                       want.view(torch.int16) if dtype != "f32" else want)
+    bad = L.perm.copy()
+    bad[123] = d_in
+    G = P.gather_columns(X, torch.from_numpy(bad).to(DEV)).float().cpu()
+    assert torch.isnan(G[:, 123]).all() and not torch.isnan(G[:, :123]).any()
+
+
+def test_act_order_many_tokens_through_gather():
+    # act-order layer packed in quantization order, 300 tokens: gather the
+    # activations, then the matrix-core route without perm; equals the
+    # oracle's product with perm
+    bits, gs, n_tok, d_out, d_in = 4, 128, 300, 200, 1536
+    L = synth.make_packed_layer(d_out, d_in, n_tok, bits=bits, group_size=gs, dtype="bf16", seed=300)
+    codes = torch.from_numpy(L.codes).to(DEV)
+    perm = torch.from_numpy(L.perm).to(DEV)
+    packed = P.pack_permuted(codes, bits, perm)
+    X = to_torch(L.X, "bf16")
+    scales = torch.from_numpy(L.scales).to(DEV)
+    zeros = torch.from_numpy(L.zeros).to(DEV)
+    Y = P.dequant_matmul(P.gather_columns(X, perm), packed, bits, scales, zeros, group_size=gs)
+    torch.cuda.synchronize()
+    X64 = L.X_f64()
+    ref = O.dequant_matmul(X64, O.pack_permuted(L.codes, bits, L.perm), bits, d_in, L.scales, L.zeros,
+                           perm=L.perm, group_size=gs)
+    # bound of the matrix-core route on the gathered activations (stream order)
+    Xs = X64[:, L.perm]
+    g = np.arange(d_in) // gs
+    S = L.scales.astype(np.float64)[g].T
+    Z = L.zeros.astype(np.float64)[g].T
+    A = np.abs(Xs) @ (S * (L.codes[:, L.perm].astype(np.float64) + Z + 2.0 ** (bits + 1))).T
+    tol = (2 * gs + d_in // gs + 8) * U32 * A
+    assert np.all(np.abs(Y.cpu().numpy() - ref) <= tol)

@@ -30,6 +30,8 @@
 //   activations, 8-bit codes with bf16 activations): per column the group is
 //   looked up, the scales and zeros of the workgroup's rows come from LDS
 //   ([group][row]), w = s * (c - z) in float32 and one FMA per token.
+#include <type_traits>
+
 #include "internal.hpp"
 
 namespace gptq {
@@ -783,6 +785,25 @@ __device__ __forceinline__ void mm_code_operands(const uint32_t (&w)[BITS], int 
     constexpr int SH = T::MB - BITS;
     constexpr uint32_t E = (uint32_t)(T::BIAS + BITS) << T::MB;
     constexpr uint32_t M = (1u << BITS) - 1u;
+    if constexpr (BITS == 4) {
+        // a word holds 8 consecutive codes; even / odd nibbles to bytes, then
+        // one byte permute pairs codes (2j, 2j+1) into the two halves
+        constexpr uint32_t EE = E | (E << 16);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const uint32_t wq = h ? w[2 + q] : w[q];
+            const uint32_t ev = wq & 0x0F0F0F0Fu, od = (wq >> 4) & 0x0F0F0F0Fu;
+            uint32_t v[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                // bytes: ev.byte j, zero, od.byte j, zero
+                const uint32_t pr = __builtin_amdgcn_perm(od, ev, 0x0C000C00u | (uint32_t)j | ((uint32_t)(4 + j) << 16));
+                v[j] = (pr << SH) | EE;
+            }
+            op[q] = u32x4_t{v[0], v[1], v[2], v[3]};
+        }
+        return;
+    }
     uint64_t win0, win1 = 0;
     if constexpr (BITS == 2) {
         win0 = h ? w[1] : w[0];
@@ -815,7 +836,10 @@ __device__ __forceinline__ void mm_code_operands(const uint32_t (&w)[BITS], int 
     }
 }
 
-template <int BITS, typename T>
+// XV: activation rows 16-byte aligned and d_in a multiple of 8, so every
+// 16-byte piece is either whole or past the row's end (vector loads, no
+// branches); otherwise element-wise loads.
+template <int BITS, typename T, bool XV>
 __global__ __launch_bounds__(MM_THREADS, 2) void dequant_mfma_kernel(DqArgs a, int64_t n_mt, int64_t n_rt,
                                                                      int64_t per_xcd) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds_u8[];
@@ -831,6 +855,7 @@ __global__ __launch_bounds__(MM_THREADS, 2) void dequant_mfma_kernel(DqArgs a, i
     const uint32_t d_in = (uint32_t)a.d_in;
     const uint32_t nkb = (uint32_t)ceil_div(a.d_in, 32);
     const uint32_t bpg = a.gsize >= a.d_in ? nkb : (uint32_t)(a.gsize >> 5);
+    const uint32_t ngr = (uint32_t)ceil_div(nkb, bpg);
     constexpr float OFF = (float)(1 << BITS);
     const __amdgpu_buffer_rsrc_t rs = words_rsrc(a, n0 < a.d_out ? n0 : a.d_out);
     const uint32_t row_bytes = (uint32_t)a.wpr * 4;
@@ -838,19 +863,27 @@ __global__ __launch_bounds__(MM_THREADS, 2) void dequant_mfma_kernel(DqArgs a, i
     // staging assignments: two 16-byte activation pieces per thread (token
     // p >> 2, columns 8 (p & 3) ..), and one row's half block of codes
     const int srow = tid >> 1, sh = tid & 1;
+    const uint16_t* xrow[2];
+    bool tok_ok[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int p = tid + MM_THREADS * j, t = p >> 2;
+        const int64_t tok = t0 + t;
+        tok_ok[j] = tok < a.n_tok;
+        xrow[j] = X + (tok_ok[j] ? tok : 0) * a.ld_x + 8 * (p & 3);
+    }
     auto load_x = [&](uint32_t kb, u32x4_t (&xv)[2]) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const int p = tid + MM_THREADS * j, t = p >> 2, q = p & 3;
-            const int64_t tok = t0 + t;
-            const uint32_t k = kb * 32 + 8 * q;
-            const uint16_t* xr = X + tok * a.ld_x + k;
-            if (tok < a.n_tok && a.xvec && k + 8 <= d_in) {
-                xv[j] = *(const u32x4_t*)xr;
+            const uint32_t k = kb * 32 + 8 * ((tid + MM_THREADS * j) & 3);
+            if constexpr (XV) {
+                const bool ok = tok_ok[j] && k < d_in;
+                const u32x4_t v = *(const u32x4_t*)(xrow[j] + (ok ? kb * 32 : 0));
+                xv[j] = ok ? v : u32x4_t{0u, 0u, 0u, 0u};
             } else {
                 uint32_t e[8];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) e[i] = (tok < a.n_tok && k + i < d_in) ? xr[i] : 0u;
+                for (int i = 0; i < 8; ++i) e[i] = (tok_ok[j] && k + i < d_in) ? xrow[j][kb * 32 + i] : 0u;
                 xv[j] = u32x4_t{e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16)};
             }
         }
@@ -899,42 +932,13 @@ __global__ __launch_bounds__(MM_THREADS, 2) void dequant_mfma_kernel(DqArgs a, i
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                acc[i][j][r] = 0.0f;
-                accg[i][j][r] = 0.0f;
-            }
-    float xpart[2] = {0.0f, 0.0f};
-    float sv[2], ov[2];
-    auto load_group_params = [&](uint32_t g) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int64_t row = n0 + (2 * wn + j) * 32 + (lane & 31);
-            const bool ok = row < a.d_out;
-            const int64_t idx = ok ? (int64_t)g * a.d_out + row : 0;
-            const float sl = a.scales[idx], zl = a.zeros[idx];
-            sv[j] = ok ? sl : 0.0f;
-            ov[j] = OFF + (ok ? zl : 0.0f);
-        }
-    };
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    const f16_t zero16 = {};
 
-    {
-        u32x4_t xv[2];
-        uint32_t w[BITS];
-        load_x(0, xv);
-        load_w(0, w);
-        store_stage(0, xv, w);
-    }
-    load_group_params(0);
-    __syncthreads();
-    for (uint32_t kb = 0; kb < nkb; ++kb) {
-        const bool more = kb + 1 < nkb;
-        u32x4_t xv[2];
-        uint32_t w[BITS];
-        if (more) {
-            load_x(kb + 1, xv);
-            load_w(kb + 1, w);
-        }
-        const char* st = lds + (kb & 1) * MM_STAGE_BYTES;
+    // one k-block from LDS buffer `buf`; FIRST: the group's first block (its
+    // first MFMA starts from zero)
+    auto compute = [&](int buf, float (&xpart)[2], auto first) {
+        const char* st = lds + buf * MM_STAGE_BYTES;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             u32x4_t av[2], bv[2];
@@ -946,36 +950,63 @@ __global__ __launch_bounds__(MM_THREADS, 2) void dequant_mfma_kernel(DqArgs a, i
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int j = 0; j < 2; ++j) accg[i][j] = mfma_32x32x16(av[i], bv[j], accg[i][j], (typename T::mfma_tag*)nullptr);
+                for (int j = 0; j < 2; ++j)
+                    accg[i][j] = mfma_32x32x16(av[i], bv[j], (decltype(first)::value && ks == 0) ? zero16 : accg[i][j],
+                                               (typename T::mfma_tag*)nullptr);
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
-                xpart[i] = T::dot2(av[i].x, T::ONES, xpart[i]);
-                xpart[i] = T::dot2(av[i].y, T::ONES, xpart[i]);
-                xpart[i] = T::dot2(av[i].z, T::ONES, xpart[i]);
-                xpart[i] = T::dot2(av[i].w, T::ONES, xpart[i]);
+                float x = (decltype(first)::value && ks == 0) ? 0.0f : xpart[i];
+                x = T::dot2(av[i].x, T::ONES, x);
+                x = T::dot2(av[i].y, T::ONES, x);
+                x = T::dot2(av[i].z, T::ONES, x);
+                xpart[i] = T::dot2(av[i].w, T::ONES, x);
             }
         }
-        if ((kb + 1) % bpg == 0 || !more) {
-            // group end: acc += s * (P - (2^b + z) * sum x); the token of
-            // element r of lane l is 8 (r / 4) + 4 (l / 32) + r % 4
+    };
+
+    u32x4_t xv[2];
+    uint32_t w[BITS];
+    load_x(0, xv);
+    load_w(0, w);
+    store_stage(0, xv, w);
+    __syncthreads();
+    uint32_t kb = 0;
+    for (uint32_t g = 0; g < ngr; ++g) {
+        // the group's scales and 2^b + zero for the wave's two row tiles
+        float sv[2], ov[2];
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const float xt = xpart[i] + __shfl_xor(xpart[i], 32, 64);
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float x = __shfl(xt, 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3), 64);
-#pragma unroll
-                    for (int j = 0; j < 2; ++j) {
-                        acc[i][j][r] = fmaf(sv[j], fmaf(-ov[j], x, accg[i][j][r]), acc[i][j][r]);
-                        accg[i][j][r] = 0.0f;
-                    }
-                }
-                xpart[i] = 0.0f;
-            }
-            if (more) load_group_params((kb + 1) / bpg);
+        for (int j = 0; j < 2; ++j) {
+            const int64_t row = n0 + (2 * wn + j) * 32 + (lane & 31);
+            const bool ok = row < a.d_out;
+            const int64_t idx = ok ? (int64_t)g * a.d_out + row : 0;
+            const float sl = a.scales[idx], zl = a.zeros[idx];
+            sv[j] = ok ? sl : 0.0f;
+            ov[j] = OFF + (ok ? zl : 0.0f);
         }
-        if (more) store_stage((kb + 1) & 1, xv, w);
-        __syncthreads();
+        const uint32_t kend = (kb + bpg < nkb) ? kb + bpg : nkb;
+        float xpart[2];
+        for (bool first = true; kb < kend; ++kb, first = false) {
+            // next block's loads in flight (the last block reloads itself)
+            const uint32_t kn = (kb + 1 < nkb) ? kb + 1 : kb;
+            load_x(kn, xv);
+            load_w(kn, w);
+            if (first) compute(kb & 1, xpart, std::true_type{});
+            else compute(kb & 1, xpart, std::false_type{});
+            if (kb + 1 < nkb) store_stage((kb + 1) & 1, xv, w);
+            __syncthreads();
+        }
+        // group end: acc += s * (P - (2^b + z) * sum x); the token of element
+        // r of lane l is 8 (r / 4) + 4 (l / 32) + r % 4
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const float xt = xpart[i] + __shfl_xor(xpart[i], 32, 64);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float x = __shfl(xt, 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3), 64);
+#pragma unroll
+                for (int j = 0; j < 2; ++j) acc[i][j][r] = fmaf(sv[j], fmaf(-ov[j], x, accg[i][j][r]), acc[i][j][r]);
+            }
+        }
     }
     // outputs: element r of lane l of tile (i, j) is token 8 (r / 4) + 4 (l / 32) + r % 4, row l % 32
 #pragma unroll
@@ -995,8 +1026,13 @@ template <int BITS, typename T>
 gptq_status launch_mfma(const DqArgs& a, hipStream_t s) {
     const int64_t n_mt = ceil_div(a.n_tok, MM_TILE), n_rt = ceil_div(a.d_out, MM_TILE);
     const int64_t per_xcd = ceil_div(n_mt * n_rt, 8);
-    hipLaunchKernelGGL((dequant_mfma_kernel<BITS, T>), dim3((unsigned)(per_xcd * 8)), dim3(MM_THREADS),
-                       2 * MM_STAGE_BYTES, s, a, n_mt, n_rt, per_xcd);
+    const dim3 grid((unsigned)(per_xcd * 8)), block(MM_THREADS);
+    if (a.xvec && a.d_in % 8 == 0)
+        hipLaunchKernelGGL((dequant_mfma_kernel<BITS, T, true>), grid, block, 2 * MM_STAGE_BYTES, s, a, n_mt, n_rt,
+                           per_xcd);
+    else
+        hipLaunchKernelGGL((dequant_mfma_kernel<BITS, T, false>), grid, block, 2 * MM_STAGE_BYTES, s, a, n_mt, n_rt,
+                           per_xcd);
     GPTQ_LAUNCH_CHECK();
     return GPTQ_OK;
 }

@@ -80,6 +80,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dequant", action="store_true", help="skip the summary of the packed-layer product")
     ap.add_argument("--tokens", type=int, default=None, help="override the token count (testing only)")
     ap.add_argument("--workload", choices=("quantize", "dequant", "shapes", "stack"), default="quantize")
     ap.add_argument("--blocks", type=int, default=2, help="stack workload: decoder blocks")
@@ -527,10 +528,11 @@ def main():
         "roofline": roofline,
     }
     log(f"timed {a.steps} steps: {ms_per_step:.2f} ms/step; phases {res['phases_ms']}")
-    log("product with the packed layer ...")
-    dq = dequant_measure(d_out, d_in, q.bits, q.group_size, (1, 16), 20)
-    res["dequant_matmul"] = {"workload": "1 and 16 tokens x packed 4096x11008 4-bit g128 act-order (sorted), bf16",
-                             "by_tokens": dq["by_tokens"], "peak_GBps": PEAK_HBM_GBS}
+    if not a.no_dequant:
+        log("product with the packed layer ...")
+        dq = dequant_measure(d_out, d_in, q.bits, q.group_size, (1, 16), 20)
+        res["dequant_matmul"] = {"workload": "1 and 16 tokens x packed 4096x11008 4-bit g128 act-order (sorted), "
+                                             "bf16", "by_tokens": dq["by_tokens"], "peak_GBps": PEAK_HBM_GBS}
     if a.calib_copy_mib:
         src = torch.empty(a.calib_copy_mib << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)

@@ -199,13 +199,12 @@ def quantize_column(w: np.ndarray, scale: np.ndarray, zero: np.ndarray, bits: in
 # ---------------------------------------------------------------------------
 
 def _check_block_group(d_in: int, group_size: int, block: int) -> int:
-    """Effective group width; per-row (group_size <= 0) is one group per row."""
+    """Effective group width; per-row (group_size <= 0) is one group per row.
+    Any positive block works with any group width (lazy batching is exact)."""
     if block <= 0:
         raise InvalidArgument("block size must be positive")
     if group_size <= 0:
         return d_in
-    if group_size % block != 0 and block % group_size != 0:
-        raise InvalidArgument("group_size and block must divide one another")
     return group_size
 
 
@@ -245,11 +244,15 @@ def sweep(W: np.ndarray, U: np.ndarray, bits: int, group_size: int, sym: bool,
             k = c - i1
             if c % g == 0:
                 # The group's current values: the part inside this block sits
-                # in W1 (already compensated by earlier columns of the block),
-                # the part past the block sits in W (all earlier blocks' lazy
-                # updates applied).
+                # in W1 (already compensated by earlier columns of the block);
+                # the part past the block sits in W, which holds every earlier
+                # block's lazy update but not yet this block's, so the errors
+                # of this block's finished columns are applied to it here.
+                # Lazy batching thus stays exactly the per-column algorithm
+                # for any block size, also when a group crosses the block end.
                 end = min(c + g, d_in)
-                cur = np.hstack([W1[:, k:min(end, i2) - i1], W[:, i2:max(end, i2)]])
+                past = W[:, i2:max(end, i2)] - Err[:, :k] @ U[i1:c, i2:max(end, i2)]
+                cur = np.hstack([W1[:, k:min(end, i2) - i1], past])
                 scale, zero = quant_params(cur, bits, sym)
                 scales[c // g] = scale
                 zeros[c // g] = zero

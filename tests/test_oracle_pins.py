@@ -265,25 +265,45 @@ def test_matches_bruteforce_obs(seed, g):
 # P-B: lazy batching changes nothing.
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("g", [-1, 16])
+@pytest.mark.parametrize("g", [-1, 16, 12])
 def test_block_size_invariance(g):
+    """Any block size, also one that neither divides nor is divided by the
+    group width (groups then begin inside a block and run past its end):
+    the codes do not change, since lazy batching is the per-column
+    algorithm reordered (B = 1 is the unbatched sweep)."""
     rng = np.random.default_rng(20)
     X = rng.standard_normal((400, 96)) @ (rng.standard_normal((96, 96)) / 10)
     W = 0.02 * rng.standard_normal((11, 96))
-    ref = O.gptq_quantize(W, X=X, bits=3, group_size=g, block=96)
-    for B in (1, 8, 16, 32, 48):
-        if g > 0 and g % B and B % g:
-            continue
+    ref = O.gptq_quantize(W, X=X, bits=3, group_size=g, block=1)
+    for B in (5, 7, 8, 16, 20, 32, 48, 96):
         out = O.gptq_quantize(W, X=X, bits=3, group_size=g, block=B)
         np.testing.assert_array_equal(out["codes"], ref["codes"])
         np.testing.assert_allclose(out["w_hat"], ref["w_hat"], rtol=1e-12, atol=1e-15)
         np.testing.assert_allclose(out["scales"], ref["scales"], rtol=1e-12)
 
 
-def test_invalid_block_group_combination():
+def test_group_crossing_block_end_uses_compensated_values():
+    """Worked by hand: d_in = 4, block 3, groups {0, 1} and {2, 3}, 2-bit
+    asymmetric, U = I except U[0][3] = 5, one row w = (0.22, 0.3, 0, 0).
+    Group {0, 1}: scale 0.3/3 = 0.1, zero 0; column 0 gets code 2, error
+    0.02, so column 3 (past the block) holds 0 - 5 * 0.02 = -0.1 by the time
+    group {2, 3} begins at column 2: range [-0.1, 0] -> scale 0.1/3, zero 3;
+    column 2 -> code 3, column 3 -> code 0.  With the uncompensated value the
+    group would be all zeros (scale 2/3, zero 2)."""
+    U = np.eye(4)
+    U[0, 3] = 5.0
+    W = np.array([[0.22, 0.3, 0.0, 0.0]])
+    codes, scales, zeros, w_hat, _ = O.sweep(W, U, 2, 2, False, block=3)
+    np.testing.assert_allclose(scales[:, 0], [0.1, 0.1 / 3.0], rtol=1e-12)
+    np.testing.assert_array_equal(zeros[:, 0], [0.0, 3.0])
+    np.testing.assert_array_equal(codes[0], [2, 3, 3, 0])
+    np.testing.assert_allclose(w_hat[0], [0.2, 0.3, 0.0, -0.1], rtol=1e-12, atol=1e-15)
+
+
+def test_invalid_block_size():
     W = np.zeros((2, 48))
     with pytest.raises(O.InvalidArgument):
-        O.gptq_quantize(W, np.eye(48), group_size=12, block=8)
+        O.gptq_quantize(W, np.eye(48), group_size=12, block=0)
 
 
 # ---------------------------------------------------------------------------

@@ -64,9 +64,12 @@ typedef struct {
     int32_t group_size;  /* > 0: columns per (scale, zero); <= 0: one group per row */
     int32_t sym;         /* 0: asymmetric range with zero point; 1: symmetric */
     int32_t act_order;   /* 0: natural column order; 1: descending diag(H) (desc_act) */
-    int32_t block_size;  /* B, columns per lazy-update block (128); must divide, or be
-                            divided by, group_size when group_size > 0; 1..128 in this
-                            build (larger: GPTQ_ERR_UNSUPPORTED) */
+    int32_t block_size;  /* B, columns per lazy-update block (128); 1..128 in this build
+                            (larger: GPTQ_ERR_UNSUPPORTED).  Any B gives the codes of
+                            the per-column sweep, also when B and group_size do not
+                            divide one another (a group that begins inside a block
+                            and runs past its end sees its later columns with the
+                            block's pending compensation applied) */
     double  damp;        /* lambda = damp * mean(diag H) is added to diag H (0.01) */
 } gptq_config;
 

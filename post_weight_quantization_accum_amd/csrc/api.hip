@@ -19,9 +19,6 @@ gptq_status check_config(const gptq_config* cfg) {
     if (!valid_bits(cfg->bits)) return GPTQ_ERR_INVALID_ARG;
     if (cfg->block_size < 1) return GPTQ_ERR_INVALID_ARG;
     if (cfg->block_size > 128) return GPTQ_ERR_UNSUPPORTED;
-    if (cfg->group_size > 0 && (cfg->group_size % cfg->block_size) != 0 &&
-        (cfg->block_size % cfg->group_size) != 0)
-        return GPTQ_ERR_INVALID_ARG;
     if (!(cfg->damp >= 0.0) || !(cfg->damp < 1e300)) return GPTQ_ERR_INVALID_ARG;
     return GPTQ_OK;
 }

@@ -115,9 +115,12 @@ __global__ __launch_bounds__(256, 2) void gemm_f64_kernel(int64_t M, int64_t N, 
                                                           const double* __restrict__ B, int64_t ldb,
                                                           double beta, double* C, int64_t ldc,
                                                           int64_t tiles_m, int64_t tiles_n, int64_t n_tiles,
-                                                          int64_t per_xcd, int tri) {
+                                                          int64_t per_xcd, int tri, int prio) {
     using G = Cfg<TILE>;
     __shared__ double sA[2][KC][G::LD];
+    // prio: issue priority over the waves of a one-per-CU launch (the far
+    // lazy update on a second stream, which shares every CU with this one)
+    if (prio) __builtin_amdgcn_s_setprio(2);
     __shared__ double sB[2][KC][G::LD];
 
     const int64_t b = blockIdx.x;
@@ -404,10 +407,10 @@ void launch_t(hipStream_t s, bool vec, int64_t M, int64_t N, int64_t K, double a
     const size_t pad = one_per_cu ? CU_LDS / 2 + 1024 - static_lds : 0;
     if (vec)
         hipLaunchKernelGGL((gemm_f64_kernel<TILE, TRANS_B, LOWER, true>), grid, dim3(256), pad, s, M, N, K, alpha,
-                           A, lda, B, ldb, beta, C, ldc, tiles_m, tiles_n, n_tiles, per_xcd, tri);
+                           A, lda, B, ldb, beta, C, ldc, tiles_m, tiles_n, n_tiles, per_xcd, tri, one_per_cu ? 0 : 1);
     else
         hipLaunchKernelGGL((gemm_f64_kernel<TILE, TRANS_B, LOWER, false>), grid, dim3(256), pad, s, M, N, K, alpha,
-                           A, lda, B, ldb, beta, C, ldc, tiles_m, tiles_n, n_tiles, per_xcd, tri);
+                           A, lda, B, ldb, beta, C, ldc, tiles_m, tiles_n, n_tiles, per_xcd, tri, one_per_cu ? 0 : 1);
 }
 
 template <bool TRANS_B, bool LOWER>

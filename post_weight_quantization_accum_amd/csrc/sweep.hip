@@ -72,6 +72,18 @@ int64_t superblock_cols(int64_t d_in, const gptq_config* cfg) {
     const int64_t S = B * (GPTQ_SUPER / B > 0 ? GPTQ_SUPER / B : 1);
     const int64_t g = cfg->group_size > 0 ? cfg->group_size : d_in;
     if (cfg->group_size <= 0 || S % g == 0 || g % S == 0) return S;
+    // otherwise the largest multiple of lcm(B, g) up to GPTQ_SUPER, so that
+    // no group crosses a superblock end (a group crossing a block end reads
+    // columns of its own superblock, which the in-superblock updates keep
+    // current up to the block being swept)
+    int64_t a = B, b = g;
+    while (b != 0) {
+        const int64_t t = a % b;
+        a = b;
+        b = t;
+    }
+    const int64_t l = B / a * g;
+    if (l <= GPTQ_SUPER) return GPTQ_SUPER / l * l;
     return B;
 }
 
@@ -210,6 +222,9 @@ __global__ __launch_bounds__(SWAVES * 64) void sweep_block_kernel(double* __rest
                                                          float* __restrict__ scales, float* __restrict__ zeros,
                                                          double* __restrict__ loss64) {
     extern __shared__ __attribute__((aligned(16))) double sweep_lds[];
+    // the sweep is the serial chain of the layer: its waves take issue
+    // priority over GEMM waves of the other stream on the same SIMD
+    __builtin_amdgcn_s_setprio(3);
     double* rinv = sweep_lds + UP_DOUBLES + CPL;
     const int tid = threadIdx.x, lane = tid & 63;
     const int part = lane & (LPR - 1);
@@ -315,12 +330,33 @@ __global__ __launch_bounds__(SWAVES * 64) void sweep_block_kernel(double* __rest
                     xmin = fmin(xmin, in ? w[kk] : 0.0);
                     xmax = fmax(xmax, in ? w[kk] : 0.0);
                 }
-                if (live)
+                if (live && cs > 0 && gend > i2) {
+                    // a group begun inside the block and running past its
+                    // end: the columns past the block still lack the
+                    // compensation of this block's finished columns (their
+                    // lazy update comes after the block), so it is applied
+                    // here: v_j = W_j - sum over finished c of err_c U[c][j],
+                    // each lane summing over its own columns, then the row
+                    for (int64_t j = i2; j < gend; ++j) {
+                        double p = 0.0;
+#pragma unroll
+                        for (int kk = 0; kk < CPL; ++kk) {
+                            const int col = cbase + kk;
+                            const bool done = col < cs;
+                            const double u = Ub[(int64_t)(done ? col : 0) * d_in + (j - i1)];
+                            p = done ? fma(w[kk], u, p) : p;
+                        }
+                        const double v = Wwork[row * d_in + j] - row_sum8(p);
+                        xmin = fmin(xmin, v);
+                        xmax = fmax(xmax, v);
+                    }
+                } else if (live) {
                     for (int64_t j = i2 + part; j < gend; j += LPR) {
                         const double v = Wwork[row * d_in + j];
                         xmin = fmin(xmin, v);
                         xmax = fmax(xmax, v);
                     }
+                }
                 xmin = row_min8(xmin);
                 xmax = row_max8(xmax);
                 if (qp.sym) {

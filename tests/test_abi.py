@@ -51,8 +51,9 @@ def test_workspace_queries():
     assert lib.gptq_prepare_hinv_workspace(11008) >= 11008 * 11008 * 8
     assert lib.gptq_quantize_layer_workspace(4096, 11008, ctypes.byref(c)) >= 4096 * 11008 * 9
     assert lib.gptq_prepare_hinv_workspace(0) == 0
-    bad = P.make_config(group_size=96, block=128)
-    assert lib.gptq_quantize_layer_workspace(8, 384, ctypes.byref(bad)) == 0
+    mixed = P.make_config(group_size=96, block=128)   # neither divides the other: accepted
+    assert lib.gptq_quantize_layer_workspace(8, 384, ctypes.byref(mixed)) >= 8 * 384 * 9
+    assert lib.gptq_quantize_layer_workspace(8, 384, ctypes.byref(P.make_config(block=0))) == 0
     assert lib.gptq_packed_words_per_row(11, 3) == 2
     assert lib.gptq_packed_words_per_row(8, 4) == 1
     assert lib.gptq_packed_words_per_row(8, 5) == -1
@@ -73,8 +74,8 @@ def test_argument_validation_before_any_launch():
     assert lib.gptq_prepare_hinv(fake, 10, ctypes.byref(b5), fake, fake, 1 << 30, n) == _lib.ERR_INVALID_ARG
     big_b = P.make_config(group_size=256, block=256)
     assert lib.gptq_prepare_hinv(fake, 10, ctypes.byref(big_b), fake, fake, 1 << 30, n) == _lib.ERR_UNSUPPORTED
-    mixed = P.make_config(group_size=96, block=128)
-    args = [fake, 2, 8, 384, 384, fake, fake, ctypes.byref(mixed), fake, fake, fake, fake, n, n, fake, 1 << 30, n]
+    b0 = P.make_config(group_size=96, block=0)
+    args = [fake, 2, 8, 384, 384, fake, fake, ctypes.byref(b0), fake, fake, fake, fake, n, n, fake, 1 << 30, n]
     assert lib.gptq_quantize_layer(*args) == _lib.ERR_INVALID_ARG
     args = [fake, 2, 8, 384, 100, fake, fake, ctypes.byref(c), fake, fake, fake, fake, n, n, fake, 1 << 30, n]
     assert lib.gptq_quantize_layer(*args) == _lib.ERR_INVALID_ARG  # ld_w < d_in

@@ -182,6 +182,14 @@ def _sweep_case(d_out, d_in, bits, g, act, sym=False, block=128, dtype="bf16", s
     (40, 96, 4, 16, False, True, 32),      # symmetric
     (20, 75, 8, 25, False, False, 25),     # odd sizes: sub-block width 1
     (5, 40, 3, 12, True, False, 4),        # sub-block width 4
+    # block and group widths that do not divide one another: groups begin
+    # inside a block and run past its end
+    (96, 1000, 4, 96, True, False, 128),   # superblocks of lcm multiples, ragged tail
+    (64, 700, 3, 48, False, False, 128),
+    (50, 600, 4, 200, True, False, 128),   # group wider than a block, across two block ends
+    (40, 333, 2, 100, True, False, 64),
+    (30, 250, 4, 30, False, True, 32),     # symmetric, sub-block width 2
+    (12, 60, 3, 12, False, False, 5),      # odd block, sub-block width 1
 ])
 def test_sweep_matches_oracle_given_U(d_out, d_in, bits, g, act, sym, block):
     print(f"sweep {d_out}x{d_in} b{bits} g{g} act{act} sym{sym} B{block}", flush=True)

@@ -10,42 +10,55 @@
 //   scale64 / zero64  n_groups x d_out float64
 //   row_loss64 d_out float64, pinv d_in int32, flags
 //
-// sweep_block: eight lanes per row, each holding 16 of the block's (up to)
-// 128 columns of that row in registers; 8 rows per wave, 16 rows per
-// workgroup.  The upper triangle of the block's U (73 KiB with the zero
-// padding of its 16-column panels) is staged in LDS once per workgroup, so
+// sweep_block: sixteen lanes per row (one DPP row), lane p holding block
+// columns p, p + 16, ..., p + 112 of that row in registers; 4 rows per wave,
+// 16 rows per workgroup.  The upper triangle of the block's U (73 KiB: row c
+// from column 16 floor(c / 16) on) is staged in LDS once per workgroup, so
 // the serial column loop reads U rows at LDS latency; one such workgroup
 // fits on a CU beside a float64 GEMM workgroup of another stream.  Column c
 // is quantized by the lane owning it; its scaled error reaches the other
-// lanes of the row through a masked 8-lane sum (DPP), and every lane then
-// applies w_j -= err * U[c][j] to its 16 columns, so each w_j receives the
-// compensations of the earlier columns one by one, in column order.  A
-// finished column keeps its error in place: the later updates leave it
-// unchanged because U is zero below the diagonal.
+// lanes of the row by a DPP row broadcast, and every lane then applies
+// w_j -= err * U[c][j] to its registers from c / 16 on (the earlier ones
+// hold finished columns only), so each w_j receives the compensations of
+// the earlier columns one by one, in column order.  A finished column keeps
+// its error in place: the later updates leave it unchanged because U is zero
+// below the diagonal.  The column loop is unrolled, so register indices and
+// the broadcast lane are constants.
 //
 // Lazy updates are two-level (mathematically the same as one update per
 // block): after each block, a float64 MFMA GEMM updates the rest of its
 // superblock of S = 1024 columns (K = B); after each superblock, one GEMM
 // with K = S updates the next superblock, and another (on a second stream,
 // overlapping the next superblock's sweep) everything after it.
+#include <utility>
+
 #include "internal.hpp"
 
 namespace gptq {
 namespace {
 
 constexpr int BMAX = 128;   // largest supported block (columns per lazy update)
-constexpr int LPR = 8;      // lanes per row
-constexpr int CPL = BMAX / LPR;  // columns per lane
-constexpr int SWAVES = 2;        // waves per workgroup
+constexpr int LPR = 16;     // lanes per row: one DPP row of 16 lanes
+constexpr int CPL = BMAX / LPR;  // columns per lane: lane p holds block columns p, p + 16, ..., p + 112
+constexpr int SWAVES = 4;        // waves per workgroup
 constexpr int ROWS = SWAVES * 64 / LPR;   // rows per workgroup
-// U block in LDS, one panel per lane part p (block columns 16p..16p+15):
-// rows 0..16p+15 of the panel (the rows below are zero in U), 16 doubles
-// each; then one zero row for the parts whose panel has ended; then the
-// reciprocal diagonal.
-constexpr int UP_DOUBLES = CPL * CPL * LPR * (LPR + 1) / 2;   // 9216
-constexpr int UZERO = UP_DOUBLES;
-constexpr size_t SWEEP_LDS = (size_t)(UP_DOUBLES + CPL + BMAX) * sizeof(double);   // 73 KiB
-__host__ __device__ constexpr int panel_base(int p) { return CPL * CPL * p * (p + 1) / 2; }
+// U block in LDS: row c = 16 m + j keeps its columns 16 m .. 127 (the
+// columns whose lane register a later update still touches; the ones below
+// the diagonal are U's zeros), so lane p finds U[c][16 m' + p] (m' >= m) at
+// 16 (m' - m) + p of the row; then the reciprocal diagonal.
+__host__ __device__ constexpr int seg_len(int m) { return BMAX - LPR * m; }
+__host__ __device__ constexpr int seg_base(int m) { return LPR * (BMAX * m - 8 * m * (m - 1)); }
+constexpr int UP_DOUBLES = seg_base(CPL);   // 9216
+constexpr size_t SWEEP_LDS = (size_t)(UP_DOUBLES + BMAX) * sizeof(double);   // 73 KiB
+static_assert(seg_base(1) == LPR * seg_len(0), "row segments of the first register group");
+// double pairs staged per thread for register group m, and their running index
+__host__ __device__ constexpr int stage_iters(int m) { return (LPR * seg_len(m) / 2 + SWAVES * 64 - 1) / (SWAVES * 64); }
+__host__ __device__ constexpr int stage_first(int m) { return m == 0 ? 0 : stage_first(m - 1) + stage_iters(m - 1); }
+__host__ __device__ constexpr int stage_group(int k) {   // register group of staged pair slot k
+    int m = 0;
+    while (m + 1 < CPL && stage_first(m + 1) <= k) ++m;
+    return m;
+}
 
 struct SweepWs {
     int* flags;
@@ -197,20 +210,38 @@ constexpr int DPP_XOR1 = 0xB1;         // quad_perm (1,0,3,2)
 constexpr int DPP_XOR2 = 0x4E;         // quad_perm (2,3,0,1)
 constexpr int DPP_HALF_MIRROR = 0x141; // lane i <-> 7-i within each group of 8
 
-__device__ __forceinline__ double row_sum8(double x) {
+constexpr int DPP_MIRROR = 0x140;      // lane i <-> 15-i within each row of 16
+constexpr int DPP_ROW_BCAST = 0x150;   // + n: lane n of each row of 16 to the whole row
+
+// f(integral_constant<int, c>) for c = 0 .. BMAX-1, in order.
+template <typename F, int... Cs>
+__device__ __forceinline__ void for_each_col_(F&& f, std::integer_sequence<int, Cs...>) {
+    (f(std::integral_constant<int, Cs>{}), ...);
+}
+template <typename F>
+__device__ __forceinline__ void for_each_col(F&& f) {
+    for_each_col_(f, std::make_integer_sequence<int, BMAX>{});
+}
+
+// Reductions over the 16 lanes of a row; every lane ends with the same bits
+// (each step combines two equal partial results in both orders).
+__device__ __forceinline__ double row_sum16(double x) {
     x += dpp_f64<DPP_XOR1>(x);
     x += dpp_f64<DPP_XOR2>(x);
-    return x + dpp_f64<DPP_HALF_MIRROR>(x);
+    x += dpp_f64<DPP_HALF_MIRROR>(x);
+    return x + dpp_f64<DPP_MIRROR>(x);
 }
-__device__ __forceinline__ double row_min8(double x) {
+__device__ __forceinline__ double row_min16(double x) {
     x = fmin(x, dpp_f64<DPP_XOR1>(x));
     x = fmin(x, dpp_f64<DPP_XOR2>(x));
-    return fmin(x, dpp_f64<DPP_HALF_MIRROR>(x));
+    x = fmin(x, dpp_f64<DPP_HALF_MIRROR>(x));
+    return fmin(x, dpp_f64<DPP_MIRROR>(x));
 }
-__device__ __forceinline__ double row_max8(double x) {
+__device__ __forceinline__ double row_max16(double x) {
     x = fmax(x, dpp_f64<DPP_XOR1>(x));
     x = fmax(x, dpp_f64<DPP_XOR2>(x));
-    return fmax(x, dpp_f64<DPP_HALF_MIRROR>(x));
+    x = fmax(x, dpp_f64<DPP_HALF_MIRROR>(x));
+    return fmax(x, dpp_f64<DPP_MIRROR>(x));
 }
 
 template <int SEG, bool FULL>
@@ -225,83 +256,83 @@ __global__ __launch_bounds__(SWAVES * 64) void sweep_block_kernel(double* __rest
     // the sweep is the serial chain of the layer: its waves take issue
     // priority over GEMM waves of the other stream on the same SIMD
     __builtin_amdgcn_s_setprio(3);
-    double* rinv = sweep_lds + UP_DOUBLES + CPL;
+    double* rinv = sweep_lds + UP_DOUBLES;
     const int tid = threadIdx.x, lane = tid & 63;
-    const int part = lane & (LPR - 1);
-    const int64_t row = (int64_t)blockIdx.x * ROWS + (tid >> 3);
+    const int p = lane & (LPR - 1);   // place in the row: block columns p + 16 m
+    const int64_t row = (int64_t)blockIdx.x * ROWS + (tid >> 4);
     const bool live = row < d_out;
     const int64_t i2 = i1 + nb;
-    const int cbase = part * CPL;  // first block column of this lane
-    const int nbm = nb - 1;
     const double* Ub = U + i1 * d_in + i1;
 
-    // stage the panels (zeros outside the nb x nb block) and 1 / U[c][c]:
-    // every load of a thread issued before the first store
-    constexpr int NSTG = UP_DOUBLES / 2 / (SWAVES * 64);   // 36 double pairs per thread
-    static_assert(NSTG * SWAVES * 64 * 2 == UP_DOUBLES, "staging covers the panels");
-    {
-        double2 v[NSTG];
-#pragma unroll
-        for (int it = 0; it < NSTG; ++it) {
-            const int e = tid + it * SWAVES * 64;
-            int p = 0;
-#pragma unroll
-            for (int q = 1; q < LPR; ++q) p += (2 * e >= panel_base(q)) ? 1 : 0;
-            const int off = 2 * e - panel_base(p);
-            const int r = off / CPL, j = CPL * p + off % CPL;
-            const bool rok = r < nb;
-            const double* src = Ub + (int64_t)(rok ? r : 0) * d_in + j;
-            if (FULL) {
-                v[it].x = rok ? src[0] : 0.0;
-                v[it].y = rok ? src[1] : 0.0;
-            } else {
-                v[it].x = (rok && j < nb) ? src[0] : 0.0;
-                v[it].y = (rok && j + 1 < nb) ? src[1] : 0.0;
-            }
-        }
-#pragma unroll
-        for (int it = 0; it < NSTG; ++it) *(double2*)&sweep_lds[2 * (tid + it * SWAVES * 64)] = v[it];
-    }
-    if (tid < CPL) sweep_lds[UZERO + tid] = 0.0;
-    for (int c = tid; c < nb; c += SWAVES * 64) rinv[c] = 1.0 / Ub[(int64_t)c * d_in + c];
-    __syncthreads();
-    // this lane's part of U row c: its panel row, or the zero row once the
-    // panel has ended (c > 16 part + 15)
-    const double* my_panel = sweep_lds + panel_base(part);
-    auto load_urow = [&](double (&u)[CPL], int c) {
-        const double* p = (c < cbase + CPL) ? my_panel + c * CPL : sweep_lds + UZERO;
-#pragma unroll
-        for (int kk = 0; kk < CPL; kk += 2) {
-            const double2 v = *(const double2*)(p + kk);
-            u[kk] = v.x;
-            u[kk + 1] = v.y;
-        }
-    };
-
+    // All global loads of the prologue are issued together (one memory
+    // round trip): this row's weights, the parameters of a group begun in
+    // an earlier block, the running loss, U's diagonal and the U block.
     double w[CPL];
     {
         const int64_t rr = live ? row : d_out - 1;
         const double* wrow = Wwork + rr * d_in + i1;
 #pragma unroll
-        for (int k = 0; k < CPL; ++k) {
-            const int j = cbase + k;
-            const double x = wrow[FULL ? j : (j < nbm ? j : nbm)];
-            w[k] = (live && (FULL || j < nb)) ? x : 0.0;
+        for (int mm = 0; mm < CPL; ++mm) {
+            const int j = p + LPR * mm;
+            const double x = wrow[FULL ? j : (j < nb ? j : 0)];
+            w[mm] = (live && (FULL || j < nb)) ? x : 0.0;
         }
     }
-    uint32_t pk[CPL / 4];
-#pragma unroll
-    for (int k = 0; k < CPL / 4; ++k) pk[k] = 0u;
-
-    // current group parameters of this row (a group begun in an earlier
-    // block is continued)
     double scale = 1.0, zero = 0.0, rscale = 1.0;
     const int64_t rem = i1 % g;
     if (rem != 0 && live) {
         scale = scale64[(i1 / g) * d_out + row];
-        rscale = 1.0 / scale;
         zero = zero64[(i1 / g) * d_out + row];
     }
+    const double loss_in = (live && p == 0) ? loss64[row] : 0.0;
+    const double udiag = (tid < nb) ? Ub[(int64_t)tid * d_in + tid] : 1.0;
+    // stage the row segments (zeros outside the nb x nb block) and
+    // 1 / U[c][c]: every load of a thread issued before the first store
+    {
+        constexpr int NV = stage_first(CPL);
+        double2 v[NV];
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+            const int m = stage_group(k), it = k - stage_first(m);
+            const int q = tid + it * SWAVES * 64;          // pair within register group m
+            const int off = 2 * q;
+            const int r = LPR * m + off / seg_len(m);      // U row (block index)
+            const int j = LPR * m + off % seg_len(m);      // U column (block index), even
+            const bool in = q < LPR * seg_len(m) / 2;
+            const bool r_ok = in && r < nb;
+            const double* src = Ub + (int64_t)(r_ok ? r : 0) * d_in;
+            double x, y;
+            if (FULL) {
+                x = r_ok ? src[j] : 0.0;
+                y = r_ok ? src[j + 1] : 0.0;
+            } else {
+                x = (r_ok && j < nb) ? src[j < nb ? j : 0] : 0.0;
+                y = (r_ok && j + 1 < nb) ? src[j + 1 < nb ? j + 1 : 0] : 0.0;
+            }
+            v[k] = double2{x, y};
+        }
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+            const int m = stage_group(k), it = k - stage_first(m);
+            const int q = tid + it * SWAVES * 64;
+            if (q < LPR * seg_len(m) / 2) *(double2*)&sweep_lds[seg_base(m) + 2 * q] = v[k];
+        }
+    }
+    static_assert(BMAX <= SWAVES * 64, "one diagonal entry per thread");
+    if (tid < nb) rinv[tid] = 1.0 / udiag;
+    if (rem != 0 && live) rscale = 1.0 / scale;
+    __syncthreads();
+    // U row c's entries for this lane's registers m' >= c / 16
+    auto load_urow = [&](double (&u)[CPL], int c) __attribute__((always_inline)) {
+        const int m = c / LPR;
+        const double* r = sweep_lds + seg_base(m) + (c % LPR) * seg_len(m) + p;
+#pragma unroll
+        for (int mm = 0; mm < CPL; ++mm)
+            if (mm >= m) u[mm] = r[LPR * (mm - m)];
+    };
+
+    uint32_t pk[CPL / 4] = {0u, 0u};
+    static_assert(CPL == 8, "two code words per lane");
     int next_gs = (int)(rem == 0 ? 0 : g - rem);      // block column of the next group start
     int64_t next_gi = i1 / g + (rem == 0 ? 0 : 1);  // and its group index
     double loss = 0.0;
@@ -310,130 +341,137 @@ __global__ __launch_bounds__(SWAVES * 64) void sweep_block_kernel(double* __rest
     double ua[CPL], ub[CPL];
     load_urow(ua, 0);
     load_urow(ub, 1);
+    double ria = rinv[0], rib = rinv[1];
 
-    for (int P = 0; P < LPR; ++P) {
-        if (P * CPL >= nb) break;
+    // one call per block column c, as a compile-time constant
+    for_each_col([&](auto cc) __attribute__((always_inline)) {
+        constexpr int c = decltype(cc)::value;
+        constexpr int m = c / LPR, j = c % LPR;
+        if (!FULL && c >= nb) return;
+        if (c % SEG == 0 && c == next_gs) {
+            // group parameters from the group's current values: block
+            // columns [c, cend) in registers, later columns from Wwork
+            const int64_t gend = (i1 + c + g < d_in) ? i1 + c + g : d_in;
+            const int cend = (gend - i1 < nb) ? (int)(gend - i1) : nb;
+            double xmin = 0.0, xmax = 0.0;
 #pragma unroll
-        for (int s0 = 0; s0 < CPL; s0 += SEG) {
-            const int cs = P * CPL + s0;
-            if (!FULL && cs >= nb) break;
-            if (cs == next_gs) {
-                // group parameters from the group's current values: block
-                // columns [cs, cend) in registers, later columns from Wwork
-                const int64_t gend = (i1 + cs + g < d_in) ? i1 + cs + g : d_in;
-                const int cend = (gend - i1 < nb) ? (int)(gend - i1) : nb;
-                double xmin = 0.0, xmax = 0.0;
-#pragma unroll
-                for (int kk = 0; kk < CPL; ++kk) {
-                    const int j = cbase + kk;
-                    const bool in = j >= cs && j < cend;
-                    xmin = fmin(xmin, in ? w[kk] : 0.0);
-                    xmax = fmax(xmax, in ? w[kk] : 0.0);
-                }
-                if (live && cs > 0 && gend > i2) {
-                    // a group begun inside the block and running past its
-                    // end: the columns past the block still lack the
-                    // compensation of this block's finished columns (their
-                    // lazy update comes after the block), so it is applied
-                    // here: v_j = W_j - sum over finished c of err_c U[c][j],
-                    // each lane summing over its own columns, then the row
-                    for (int64_t j = i2; j < gend; ++j) {
-                        double p = 0.0;
-#pragma unroll
-                        for (int kk = 0; kk < CPL; ++kk) {
-                            const int col = cbase + kk;
-                            const bool done = col < cs;
-                            const double u = Ub[(int64_t)(done ? col : 0) * d_in + (j - i1)];
-                            p = done ? fma(w[kk], u, p) : p;
-                        }
-                        const double v = Wwork[row * d_in + j] - row_sum8(p);
-                        xmin = fmin(xmin, v);
-                        xmax = fmax(xmax, v);
-                    }
-                } else if (live) {
-                    for (int64_t j = i2 + part; j < gend; j += LPR) {
-                        const double v = Wwork[row * d_in + j];
-                        xmin = fmin(xmin, v);
-                        xmax = fmax(xmax, v);
-                    }
-                }
-                xmin = row_min8(xmin);
-                xmax = row_max8(xmax);
-                if (qp.sym) {
-                    double amax = fmax(-xmin, xmax);
-                    if (amax == 0.0) amax = 1.0;
-                    scale = 2.0 * amax / qp.maxq;
-                    zero = (double)(1 << (qp.bits - 1));
-                } else {
-                    if (xmin == 0.0 && xmax == 0.0) {
-                        xmin = -1.0;
-                        xmax = 1.0;
-                    }
-                    scale = (xmax - xmin) / qp.maxq;
-                    zero = rint(-xmin / scale);
-                }
-                rscale = 1.0 / scale;
-                if (live && part == 0) {
-                    scale64[next_gi * d_out + row] = scale;
-                    zero64[next_gi * d_out + row] = zero;
-                    scales[next_gi * d_out + row] = (float)scale;
-                    zeros[next_gi * d_out + row] = (float)zero;
-                }
-                next_gs = cs + (int)g;
-                ++next_gi;
+            for (int mm = 0; mm < CPL; ++mm) {
+                const int col = p + LPR * mm;
+                const bool in = col >= c && col < cend;
+                xmin = fmin(xmin, in ? w[mm] : 0.0);
+                xmax = fmax(xmax, in ? w[mm] : 0.0);
             }
+            if (live && c > 0 && gend > i2) {
+                // a group begun inside the block and running past its end:
+                // the columns past the block still lack the compensation of
+                // this block's finished columns (their lazy update comes
+                // after the block), so it is applied here: v_j = W_j - sum
+                // over finished c' of err_c' U[c'][j], each lane summing
+                // over its own columns, then the row
+                for (int64_t jj = i2; jj < gend; ++jj) {
+                    double ps = 0.0;
 #pragma unroll
-            for (int kq = 0; kq < SEG; ++kq) {
-                const int k = s0 + kq;
-                const int c = P * CPL + k;
-                if (!FULL && c >= nb) break;
-                // even columns use ua, odd ub; the buffer is refilled with
-                // the row two columns ahead once this column has used it
-                double (&u)[CPL] = (k & 1) ? ub : ua;
-                const double ri = rinv[c];
-                // quantize column c (meaningful in the owner lane, part == P);
-                // the code is decided on the correctly rounded quotient w / scale.
-                // y = w * (1/scale) is within 2^-51 |y| of that quotient, so
-                // their nearest integers agree unless y lies within 2^-40
-                // max(1, |y|) of a half-integer; only then is the quotient
-                // formed (divergent, rare).
-                const double x = w[k];
-                double y = x * rscale;
-                if (fabs(y - floor(y) - 0.5) <= 0x1p-40 * fmax(1.0, fabs(y))) y = x / scale;
-                double code = rint(y) + zero;
-                code = fmin(fmax(code, 0.0), qp.maxq);
-                const double q = scale * (code - zero);
-                const double diff = x - q;
-                const double t = diff * ri;
-                const bool own = part == P;
-                const double err = row_sum8(own ? t : 0.0);
-                loss = own ? fma(0.5 * t, t, loss) : loss;
-                pk[k >> 2] = own ? (pk[k >> 2] | ((uint32_t)code << (8 * (k & 3)))) : pk[k >> 2];
-                // compensation of the later columns of the block (earlier
-                // columns meet zeros of U below the diagonal)
-#pragma unroll
-                for (int kk = 0; kk < CPL; ++kk) w[kk] = fma(-err, u[kk], w[kk]);
-                w[k] = own ? err : w[k];
-                load_urow(u, c + 2);
+                    for (int mm = 0; mm < CPL; ++mm) {
+                        const int col = p + LPR * mm;
+                        const bool done = col < c;
+                        const double u = Ub[(int64_t)(done ? col : 0) * d_in + (jj - i1)];
+                        ps = done ? fma(w[mm], u, ps) : ps;
+                    }
+                    const double v = Wwork[row * d_in + jj] - row_sum16(ps);
+                    xmin = fmin(xmin, v);
+                    xmax = fmax(xmax, v);
+                }
+            } else if (live) {
+                for (int64_t jj = i2 + p; jj < gend; jj += LPR) {
+                    const double v = Wwork[row * d_in + jj];
+                    xmin = fmin(xmin, v);
+                    xmax = fmax(xmax, v);
+                }
             }
+            xmin = row_min16(xmin);
+            xmax = row_max16(xmax);
+            if (qp.sym) {
+                double amax = fmax(-xmin, xmax);
+                if (amax == 0.0) amax = 1.0;
+                scale = 2.0 * amax / qp.maxq;
+                zero = (double)(1 << (qp.bits - 1));
+            } else {
+                if (xmin == 0.0 && xmax == 0.0) {
+                    xmin = -1.0;
+                    xmax = 1.0;
+                }
+                scale = (xmax - xmin) / qp.maxq;
+                zero = rint(-xmin / scale);
+            }
+            rscale = 1.0 / scale;
+            if (live && p == 0) {
+                scale64[next_gi * d_out + row] = scale;
+                zero64[next_gi * d_out + row] = zero;
+                scales[next_gi * d_out + row] = (float)scale;
+                zeros[next_gi * d_out + row] = (float)zero;
+            }
+            next_gs = c + (int)g;
+            ++next_gi;
         }
-    }
+        // even columns use ua / ria, odd ub / rib; the buffers are refilled
+        // with the row two columns ahead once this column has used them
+        double (&u)[CPL] = (c & 1) ? ub : ua;
+        double& ri = (c & 1) ? rib : ria;
+        // quantize column c (meaningful in the owner lane, p == j); the
+        // code is decided on the correctly rounded quotient w / scale.
+        // y = w * (1/scale) is within 2^-51 |y| of that quotient, so their
+        // nearest integers agree unless y lies within 2^-40 max(1, |y|) of
+        // a half-integer; only then is the column redone from the quotient
+        // (divergent, rare), off the common path's dependency chain.
+        const double x = w[m];
+        const double y = x * rscale;
+        double code = fmin(fmax(rint(y) + zero, 0.0), qp.maxq);
+        double t = (x - scale * (code - zero)) * ri;
+        if (fabs(y - floor(y) - 0.5) <= 0x1p-40 * fmax(1.0, fabs(y))) {
+            asm volatile("");   // a real branch: the division is not worth computing in every column
+            code = fmin(fmax(rint(x / scale) + zero, 0.0), qp.maxq);
+            t = (x - scale * (code - zero)) * ri;
+        }
+        const bool own = p == j;
+        // the owner's scaled error to its whole row (DPP row broadcast)
+        const double err = dpp_f64<DPP_ROW_BCAST + j>(t);
+        loss = own ? fma(0.5 * t, t, loss) : loss;
+        pk[m >> 2] = own ? (pk[m >> 2] | ((uint32_t)code << (8 * (m & 3)))) : pk[m >> 2];
+        // fold the loss and the code in now: deferred to the end, every
+        // column's t and code would stay live
+        asm volatile("" : "+v"(loss), "+v"(pk[m >> 2]));
+        // compensation of the later columns of the block: registers m' >= m
+        // (in register m, the finished columns meet zeros of U below the
+        // diagonal; earlier registers hold finished columns only)
+#pragma unroll
+        for (int mm = 0; mm < CPL; ++mm)
+            if (mm >= m) w[mm] = fma(-err, u[mm], w[mm]);
+        w[m] = own ? err : w[m];
+        if (c + 2 < BMAX) {
+            load_urow(u, c + 2);
+            ri = rinv[c + 2];
+        }
+        // keep the U row loads two columns ahead, not hoisted further (the
+        // unrolled sequence would otherwise hold many rows in registers)
+        asm volatile("" ::: "memory");
+    });
 
     // errors and codes of this row's columns back to HBM
     if (live) {
-        double* erow = Err + row * ldE + errc + cbase;
-        uint8_t* crow = codes_s + row * d_in + i1 + cbase;
+        double* erow = Err + row * ldE + errc;
+        uint8_t* crow = codes_s + row * d_in + i1;
 #pragma unroll
-        for (int k = 0; k < CPL; ++k) {
-            if (FULL || cbase + k < nb) {
-                erow[k] = w[k];
-                crow[k] = (uint8_t)(pk[k >> 2] >> (8 * (k & 3)));
+        for (int mm = 0; mm < CPL; ++mm) {
+            const int col = p + LPR * mm;
+            if (FULL || col < nb) {
+                erow[col] = w[mm];
+                crow[col] = (uint8_t)(pk[mm >> 2] >> (8 * (mm & 3)));
             }
         }
     }
-    // row loss: the eight parts summed in a fixed order
-    loss = row_sum8(loss);
-    if (live && part == 0) loss64[row] += loss;
+    // row loss: the sixteen parts summed in a fixed order
+    loss = row_sum16(loss);
+    if (live && p == 0) loss64[row] = loss_in + loss;
 }
 
 // codes / w_hat in original column order.

@@ -213,14 +213,14 @@ constexpr int DPP_HALF_MIRROR = 0x141; // lane i <-> 7-i within each group of 8
 constexpr int DPP_MIRROR = 0x140;      // lane i <-> 15-i within each row of 16
 constexpr int DPP_ROW_BCAST = 0x150;   // + n: lane n of each row of 16 to the whole row
 
-// f(integral_constant<int, c>) for c = 0 .. BMAX-1, in order.
-template <typename F, int... Cs>
-__device__ __forceinline__ void for_each_col_(F&& f, std::integer_sequence<int, Cs...>) {
-    (f(std::integral_constant<int, Cs>{}), ...);
+// f(integral_constant<int, i>) for i = 0 .. N-1, in order.
+template <typename F, int... Is>
+__device__ __forceinline__ void for_each_seq(F&& f, std::integer_sequence<int, Is...>) {
+    (f(std::integral_constant<int, Is>{}), ...);
 }
-template <typename F>
-__device__ __forceinline__ void for_each_col(F&& f) {
-    for_each_col_(f, std::make_integer_sequence<int, BMAX>{});
+template <int N, typename F>
+__device__ __forceinline__ void for_each_n(F&& f) {
+    for_each_seq(f, std::make_integer_sequence<int, N>{});
 }
 
 // Reductions over the 16 lanes of a row; every lane ends with the same bits
@@ -278,45 +278,61 @@ __global__ __launch_bounds__(SWAVES * 64) void sweep_block_kernel(double* __rest
             w[mm] = (live && (FULL || j < nb)) ? x : 0.0;
         }
     }
-    double scale = 1.0, zero = 0.0, rscale = 1.0;
     const int64_t rem = i1 % g;
-    if (rem != 0 && live) {
-        scale = scale64[(i1 / g) * d_out + row];
-        zero = zero64[(i1 / g) * d_out + row];
-    }
-    const double loss_in = (live && p == 0) ? loss64[row] : 0.0;
-    const double udiag = (tid < nb) ? Ub[(int64_t)tid * d_in + tid] : 1.0;
+    const int64_t rrow = live ? row : 0;
+    const double scale_in = scale64[(i1 / g) * d_out + rrow], zero_in = zero64[(i1 / g) * d_out + rrow];
+    double scale = (rem != 0 && live) ? scale_in : 1.0, zero = (rem != 0 && live) ? zero_in : 0.0, rscale = 1.0;
+    const double loss_l = loss64[rrow];
+    const double loss_in = (live && p == 0) ? loss_l : 0.0;
+    const int dt = tid < nb ? tid : 0;
+    const double udiag_l = Ub[(uint32_t)dt * (uint32_t)d_in + dt];
+    const double udiag = (tid < nb) ? udiag_l : 1.0;
     // stage the row segments (zeros outside the nb x nb block) and
     // 1 / U[c][c]: every load of a thread issued before the first store
     {
         constexpr int NV = stage_first(CPL);
         double2 v[NV];
-#pragma unroll
-        for (int k = 0; k < NV; ++k) {
-            const int m = stage_group(k), it = k - stage_first(m);
+        const bool even_rows = ((d_in | i1) & 1) == 0 && ((uintptr_t)U & 15) == 0;
+        // slot k of the staging registers: pair q of register group m (both
+        // compile-time constants, so the divisions by the segment length fold)
+        for_each_n<NV>([&](auto kk) __attribute__((always_inline)) {
+            constexpr int k = decltype(kk)::value;
+            constexpr int m = stage_group(k), it = k - stage_first(m);
+            constexpr int L = seg_len(m);
             const int q = tid + it * SWAVES * 64;          // pair within register group m
             const int off = 2 * q;
-            const int r = LPR * m + off / seg_len(m);      // U row (block index)
-            const int j = LPR * m + off % seg_len(m);      // U column (block index), even
-            const bool in = q < LPR * seg_len(m) / 2;
+            const int r = LPR * m + off / L;               // U row (block index)
+            const int j = LPR * m + off % L;               // U column (block index), even
+            const bool in = q < LPR * L / 2;
             const bool r_ok = in && r < nb;
-            const double* src = Ub + (int64_t)(r_ok ? r : 0) * d_in;
+            // r < 128 and d_in <= 2^20: the row offset fits 32 bits
+            const double* src = Ub + (uint32_t)(r_ok ? r : 0) * (uint32_t)d_in;
             double x, y;
-            if (FULL) {
-                x = r_ok ? src[j] : 0.0;
-                y = r_ok ? src[j + 1] : 0.0;
+            // loads from clamped (in-range) addresses, unconditionally, so
+            // that all of them are in flight together; unused values dropped
+            if (FULL && even_rows) {
+                // 16-byte aligned: the block starts at an even column and every row
+                // at an even offset
+                const double2 u2 = *(const double2*)(src + j);
+                x = r_ok ? u2.x : 0.0;
+                y = r_ok ? u2.y : 0.0;
+            } else if (FULL) {
+                const double xl = src[j], yl = src[j + 1];
+                x = r_ok ? xl : 0.0;
+                y = r_ok ? yl : 0.0;
             } else {
-                x = (r_ok && j < nb) ? src[j < nb ? j : 0] : 0.0;
-                y = (r_ok && j + 1 < nb) ? src[j + 1 < nb ? j + 1 : 0] : 0.0;
+                const double xl = src[j < nb ? j : 0], yl = src[j + 1 < nb ? j + 1 : 0];
+                x = (r_ok && j < nb) ? xl : 0.0;
+                y = (r_ok && j + 1 < nb) ? yl : 0.0;
             }
             v[k] = double2{x, y};
-        }
-#pragma unroll
-        for (int k = 0; k < NV; ++k) {
-            const int m = stage_group(k), it = k - stage_first(m);
+        });
+        for_each_n<NV>([&](auto kk) __attribute__((always_inline)) {
+            constexpr int k = decltype(kk)::value;
+            constexpr int m = stage_group(k), it = k - stage_first(m);
             const int q = tid + it * SWAVES * 64;
             if (q < LPR * seg_len(m) / 2) *(double2*)&sweep_lds[seg_base(m) + 2 * q] = v[k];
-        }
+        });
     }
     static_assert(BMAX <= SWAVES * 64, "one diagonal entry per thread");
     if (tid < nb) rinv[tid] = 1.0 / udiag;
@@ -344,7 +360,7 @@ __global__ __launch_bounds__(SWAVES * 64) void sweep_block_kernel(double* __rest
     double ria = rinv[0], rib = rinv[1];
 
     // one call per block column c, as a compile-time constant
-    for_each_col([&](auto cc) __attribute__((always_inline)) {
+    for_each_n<BMAX>([&](auto cc) __attribute__((always_inline)) {
         constexpr int c = decltype(cc)::value;
         constexpr int m = c / LPR, j = c % LPR;
         if (!FULL && c >= nb) return;

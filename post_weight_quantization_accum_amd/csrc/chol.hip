@@ -423,13 +423,15 @@ __global__ __launch_bounds__(512) void leaf_blocked_kernel(const double* __restr
     // Hr block (lower; identity padding), zeros above the diagonal; all
     // loads of a thread issued before its stores
     {
+        // r < 128 and d <= 2^20: offsets from the block's corner fit 32 bits
+        const double* Ab = A + o * d + o;
         double v[PER];
 #pragma unroll
         for (int q = 0; q < PER; ++q) {
             const int e = t + 512 * q;
             const int r = e >> 7, c = e & (LEAF - 1);
             const bool in = c <= r && r < n && c < n;
-            const double x = A[(o + (in ? r : 0)) * d + o + (in ? c : 0)];
+            const double x = Ab[(uint32_t)(in ? r : 0) * (uint32_t)d + (uint32_t)(in ? c : 0)];
             v[q] = in ? x : ((c == r) ? 1.0 : 0.0);
         }
 #pragma unroll
@@ -509,23 +511,25 @@ __global__ __launch_bounds__(512) void leaf_blocked_kernel(const double* __restr
     if (bad_nan) raise_flag(flags, FLAG_NONFINITE);
     if (bad_pd) raise_flag(flags, FLAG_NOT_PD);
 
-    // write M (lower, zeros above the diagonal) for the n x n part
+    // write M (lower, zeros above the diagonal) for the n x n part; both
+    // candidate LDS values are read unconditionally (in range for any r, c)
+    // so that the reads are in flight together
     {
+        double* Mb = Mi + o * d + o;
         double v[PER];
 #pragma unroll
         for (int q = 0; q < PER; ++q) {
             const int e = t + 512 * q;
             const int r = e >> 7, c = e & (LEAF - 1);
-            double x = 0.0;
-            if (r / LB == c / LB) x = Dv[(r / LB) * DSZ + (r % LB) * DLD + (c % LB)];
-            else if (r > c) x = As[c * LDA + r];
-            v[q] = x;
+            const double xd = Dv[(r / LB) * DSZ + (r % LB) * DLD + (c % LB)];
+            const double xa = As[c * LDA + r];
+            v[q] = (r / LB == c / LB) ? xd : ((r > c) ? xa : 0.0);
         }
 #pragma unroll
         for (int q = 0; q < PER; ++q) {
             const int e = t + 512 * q;
             const int r = e >> 7, c = e & (LEAF - 1);
-            if (r < n && c < n) Mi[(o + r) * d + o + c] = v[q];
+            if (r < n && c < n) Mb[(uint32_t)r * (uint32_t)d + (uint32_t)c] = v[q];
         }
     }
 }

@@ -202,8 +202,10 @@ struct SideStream {
 template <int CTRL>
 __device__ __forceinline__ double dpp_f64(double v) {
     const uint64_t b = __builtin_bit_cast(uint64_t, v);
-    const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, 0xF, 0xF, false);
-    const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, 0xF, 0xF, false);
+    // every control used here reads a lane of the same row: the "old" operand
+    // is never taken (the source itself, so that no register is cleared)
+    const int lo = __builtin_amdgcn_update_dpp((int)(uint32_t)b, (int)(uint32_t)b, CTRL, 0xF, 0xF, false);
+    const int hi = __builtin_amdgcn_update_dpp((int)(uint32_t)(b >> 32), (int)(uint32_t)(b >> 32), CTRL, 0xF, 0xF, false);
     return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
 }
 constexpr int DPP_XOR1 = 0xB1;         // quad_perm (1,0,3,2)
@@ -348,16 +350,15 @@ __global__ __launch_bounds__(SWAVES * 64) void sweep_block_kernel(double* __rest
     };
 
     uint32_t pk[CPL / 4] = {0u, 0u};
-    static_assert(CPL == 8, "two code words per lane");
     int next_gs = (int)(rem == 0 ? 0 : g - rem);      // block column of the next group start
     int64_t next_gi = i1 / g + (rem == 0 ? 0 : 1);  // and its group index
-    double loss = 0.0;
 
     // U rows of the next two columns in registers
     double ua[CPL], ub[CPL];
     load_urow(ua, 0);
     load_urow(ub, 1);
     double ria = rinv[0], rib = rinv[1];
+    double xn = 0.0;   // the next column's weight in its owner lane
 
     // one call per block column c, as a compile-time constant
     for_each_n<BMAX>([&](auto cc) __attribute__((always_inline)) {
@@ -439,11 +440,18 @@ __global__ __launch_bounds__(SWAVES * 64) void sweep_block_kernel(double* __rest
         // nearest integers agree unless y lies within 2^-40 max(1, |y|) of
         // a half-integer; only then is the column redone from the quotient
         // (divergent, rare), off the common path's dependency chain.
-        const double x = w[m];
+        // w[m] as the previous column left it before its owner's select
+        // (which only changes that owner's lane, not this column's owner)
+        const double x = (c == 0) ? w[0] : xn;
         const double y = x * rscale;
-        double code = fmin(fmax(rint(y) + zero, 0.0), qp.maxq);
+        const double ry = rint(y);
+        double code = fmin(fmax(ry + zero, 0.0), qp.maxq);
         double t = (x - scale * (code - zero)) * ri;
-        if (fabs(y - floor(y) - 0.5) <= 0x1p-40 * fmax(1.0, fabs(y))) {
+        // the common path's result is formed before the rare branch, which
+        // then stays off the dependency chain
+        asm volatile("" : "+v"(t), "+v"(code));
+        // distance of y to the nearest half-integer: 0.5 - |y - rint(y)| (exact)
+        if (fabs(y - ry) >= fma(-0x1p-40, fmax(1.0, fabs(y)), 0.5)) {
             asm volatile("");   // a real branch: the division is not worth computing in every column
             code = fmin(fmax(rint(x / scale) + zero, 0.0), qp.maxq);
             t = (x - scale * (code - zero)) * ri;
@@ -451,24 +459,27 @@ __global__ __launch_bounds__(SWAVES * 64) void sweep_block_kernel(double* __rest
         const bool own = p == j;
         // the owner's scaled error to its whole row (DPP row broadcast)
         const double err = dpp_f64<DPP_ROW_BCAST + j>(t);
-        loss = own ? fma(0.5 * t, t, loss) : loss;
+        // the code goes into this lane's code bytes now (deferred, every
+        // column's code would stay live); the owner's scaled error t stays in
+        // w[m] below, and the row loss is summed from those at the end
         pk[m >> 2] = own ? (pk[m >> 2] | ((uint32_t)code << (8 * (m & 3)))) : pk[m >> 2];
-        // fold the loss and the code in now: deferred to the end, every
-        // column's t and code would stay live
-        asm volatile("" : "+v"(loss), "+v"(pk[m >> 2]));
+        asm volatile("" : "+v"(pk[m >> 2]));
         // compensation of the later columns of the block: registers m' >= m
         // (in register m, the finished columns meet zeros of U below the
         // diagonal; earlier registers hold finished columns only)
 #pragma unroll
         for (int mm = 0; mm < CPL; ++mm)
             if (mm >= m) w[mm] = fma(-err, u[mm], w[mm]);
+        if (c + 1 < BMAX) xn = w[(c + 1) / LPR];
         w[m] = own ? err : w[m];
         if (c + 2 < BMAX) {
             load_urow(u, c + 2);
             ri = rinv[c + 2];
         }
         // keep the U row loads two columns ahead, not hoisted further (the
-        // unrolled sequence would otherwise hold many rows in registers)
+        // unrolled sequence would otherwise hold many rows in registers, and
+        // a kernel this wide would keep a GEMM workgroup of the other stream
+        // off the CU)
         asm volatile("" ::: "memory");
     });
 
@@ -485,7 +496,12 @@ __global__ __launch_bounds__(SWAVES * 64) void sweep_block_kernel(double* __rest
             }
         }
     }
-    // row loss: the sixteen parts summed in a fixed order
+    // row loss: sum over the row's columns of t^2 / 2, t = (w - q) / U[c][c]
+    // (now in w), each lane over its columns in column order, then the
+    // sixteen parts in a fixed order
+    double loss = 0.0;
+#pragma unroll
+    for (int mm = 0; mm < CPL; ++mm) loss = fma(0.5 * w[mm], w[mm], loss);
     loss = row_sum16(loss);
     if (live && p == 0) loss64[row] = loss_in + loss;
 }

@@ -190,6 +190,8 @@ def _sweep_case(d_out, d_in, bits, g, act, sym=False, block=128, dtype="bf16", s
     (40, 333, 2, 100, True, False, 64),
     (30, 250, 4, 30, False, True, 32),     # symmetric, sub-block width 2
     (12, 60, 3, 12, False, False, 5),      # odd block, sub-block width 1
+    (9, 21, 3, 6, True, False, 1),         # one column per block
+    (7, 50, 4, 10, False, False, 3),       # block 3, group 10
 ])
 def test_sweep_matches_oracle_given_U(d_out, d_in, bits, g, act, sym, block):
     print(f"sweep {d_out}x{d_in} b{bits} g{g} act{act} sym{sym} B{block}", flush=True)

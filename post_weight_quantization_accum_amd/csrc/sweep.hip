@@ -154,6 +154,49 @@ __global__ __launch_bounds__(256) void convert_kernel(const void* __restrict__ W
     Wwork[r * d_in + k] = v;
 }
 
+// The same with one workgroup per row: the row is read in order into LDS
+// (its bytes in 4-byte words), then gathered from there, so that the global
+// reads are coalesced instead of scattered along the row.
+constexpr size_t CONVERT_LDS_MAX = 64 * 1024;
+__global__ __launch_bounds__(256) void convert_rows_lds_kernel(const void* __restrict__ W, gptq_dtype dt,
+                                                               int64_t d_in, int64_t ld_w,
+                                                               const int32_t* __restrict__ perm, double* Wwork,
+                                                               double* loss64, int* flags) {
+    extern __shared__ uint32_t crow[];
+    const int64_t r = blockIdx.x;
+    const int tid = threadIdx.x;
+    const size_t esz = dt == GPTQ_F32 ? 4 : 2;
+    const uint32_t nw = (uint32_t)((d_in * (int64_t)esz + 3) / 4);   // words holding the row
+    const char* src = (const char*)W + r * ld_w * (int64_t)esz;
+    const bool aligned = ((uintptr_t)src & 3) == 0;
+    for (uint32_t q = tid; q < nw; q += 256) {
+        uint32_t v;
+        if (aligned && (int64_t)(4 * q + 4) <= d_in * (int64_t)esz) {
+            v = ((const uint32_t*)src)[q];
+        } else {   // unaligned row start or the last partial word: byte by byte
+            v = 0;
+            for (int b = 0; b < 4; ++b)
+                if ((int64_t)(4 * q + b) < d_in * (int64_t)esz) v |= (uint32_t)(uint8_t)src[4 * q + b] << (8 * b);
+        }
+        crow[q] = v;
+    }
+    if (tid == 0) loss64[r] = 0.0;
+    __syncthreads();
+    bool bad_perm = false, nonfinite = false;
+    for (int64_t k = tid; k < d_in; k += 256) {
+        int64_t p = perm[k];
+        if (p < 0 || p >= d_in) {
+            bad_perm = true;
+            p = 0;
+        }
+        const double v = load_as_f64(crow, p, dt);
+        nonfinite |= !isfinite(v);
+        Wwork[r * d_in + k] = v;
+    }
+    if (bad_perm) raise_flag(flags, FLAG_BAD_PERM);
+    if (nonfinite) raise_flag(flags, FLAG_NONFINITE);
+}
+
 __global__ void fill_neg_kernel(int32_t* p, int64_t n) {
     const int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (k < n) p[k] = -1;
@@ -552,8 +595,15 @@ gptq_status sweep_launch(const void* W, gptq_dtype dt, int64_t d_out, int64_t d_
     GPTQ_HIP(hipMemsetAsync(w.flags, 0, 256, s));
 
     const unsigned gx = (unsigned)ceil_div(d_in, 256);
-    hipLaunchKernelGGL(convert_kernel, dim3(gx, (unsigned)d_out), dim3(256), 0, s, W, dt, d_out, d_in, ld_w, perm,
-                       w.Wwork, w.loss64, w.flags);
+    const size_t row_bytes = (size_t)d_in * (dt == GPTQ_F32 ? 4 : 2);
+    if (row_bytes <= CONVERT_LDS_MAX) {
+        const size_t lds = align_up(row_bytes, 4);
+        hipLaunchKernelGGL(convert_rows_lds_kernel, dim3((unsigned)d_out), dim3(256), lds, s, W, dt, d_in, ld_w, perm,
+                           w.Wwork, w.loss64, w.flags);
+    } else {
+        hipLaunchKernelGGL(convert_kernel, dim3(gx, (unsigned)d_out), dim3(256), 0, s, W, dt, d_out, d_in, ld_w, perm,
+                           w.Wwork, w.loss64, w.flags);
+    }
     GPTQ_LAUNCH_CHECK();
     hipLaunchKernelGGL(fill_neg_kernel, dim3(gx), dim3(256), 0, s, w.pinv, d_in);
     GPTQ_LAUNCH_CHECK();

@@ -571,6 +571,43 @@ __global__ __launch_bounds__(256) void finalize_kernel(const uint8_t* __restrict
     }
 }
 
+// The same with one workgroup per row: the row's codes (sweep order) and
+// its group parameters are read in order into LDS, then gathered from there.
+__global__ __launch_bounds__(256) void finalize_rows_lds_kernel(const uint8_t* __restrict__ codes_s, int64_t d_out,
+                                                                int64_t d_in, const int32_t* __restrict__ pinv,
+                                                                int64_t g, int64_t ng,
+                                                                const double* __restrict__ scale64,
+                                                                const double* __restrict__ zero64, uint8_t* codes,
+                                                                float* w_hat, int* flags) {
+    extern __shared__ double fl[];          // [ng] scales, [ng] zeros, then the codes
+    uint8_t* cl = (uint8_t*)(fl + 2 * ng);
+    const int64_t r = blockIdx.x;
+    const int tid = threadIdx.x;
+    const uint8_t* src = codes_s + r * d_in;
+    for (int64_t k = tid; k < d_in; k += 256) cl[k] = src[k];
+    if (w_hat)
+        for (int64_t q = tid; q < ng; q += 256) {
+            fl[q] = scale64[q * d_out + r];
+            fl[ng + q] = zero64[q * d_out + r];
+        }
+    __syncthreads();
+    bool bad = false;
+    for (int64_t j = tid; j < d_in; j += 256) {
+        int64_t k = pinv[j];
+        if (k < 0 || k >= d_in) {
+            bad = true;
+            k = 0;
+        }
+        const uint8_t c = cl[k];
+        codes[r * d_in + j] = c;
+        if (w_hat) {
+            const int64_t gi = k / g;
+            w_hat[r * d_in + j] = (float)(fl[gi] * ((double)c - fl[ng + gi]));
+        }
+    }
+    if (bad) raise_flag(flags, FLAG_BAD_PERM);
+}
+
 __global__ void copy_loss_kernel(const double* __restrict__ src, double* dst, int64_t n) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i < n) dst[i] = src[i];
@@ -691,8 +728,15 @@ gptq_status sweep_launch(const void* W, gptq_dtype dt, int64_t d_out, int64_t d_
         }
     }
     if (far_pending) GPTQ_HIP(hipStreamWaitEvent(s, side.far_done, 0));
-    hipLaunchKernelGGL(finalize_kernel, dim3(gx, (unsigned)d_out), dim3(256), 0, s, w.codes_s, d_out, d_in, w.pinv,
-                       g, w.scale64, w.zero64, codes, w_hat, w.flags);
+    const int64_t ng = n_groups_of(d_in, cfg->group_size);
+    const size_t fin_lds = (size_t)ng * 16 + (size_t)d_in;
+    if (fin_lds <= CONVERT_LDS_MAX) {
+        hipLaunchKernelGGL(finalize_rows_lds_kernel, dim3((unsigned)d_out), dim3(256), fin_lds, s, w.codes_s, d_out,
+                           d_in, w.pinv, g, ng, w.scale64, w.zero64, codes, w_hat, w.flags);
+    } else {
+        hipLaunchKernelGGL(finalize_kernel, dim3(gx, (unsigned)d_out), dim3(256), 0, s, w.codes_s, d_out, d_in,
+                           w.pinv, g, w.scale64, w.zero64, codes, w_hat, w.flags);
+    }
     GPTQ_LAUNCH_CHECK();
     if (row_loss) {
         hipLaunchKernelGGL(copy_loss_kernel, dim3((unsigned)ceil_div(d_out, 256)), dim3(256), 0, s, w.loss64,

@@ -264,6 +264,7 @@ def test_pack_matches_oracle(bits, d_in):
     (192, 640, 8192, "bf16", 4, 128, True),     # workload-3 recipe, reduced
     (150, 512, 8192, "f16", 3, 128, False),     # workload-2/5 recipe, reduced
     (96, 448, 6000, "bf16", 2, 64, True),       # workload-4 recipe, reduced
+    (128, 600, 6000, "bf16", 3, 96, True),      # group 96 with block 128: groups cross block ends
 ])
 def test_end_to_end(d_out, d_in, n, dtype, bits, g, act):
     print(f"e2e {d_out}x{d_in} n={n} {dtype} b{bits} g{g} act{act}", flush=True)

@@ -10,6 +10,7 @@ library raises instead of falling back to anything else.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 
 from . import _lib
@@ -49,6 +50,15 @@ def _stream(stream=None):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _alloc_on(stream):
+    """Allocations made inside belong to ``stream`` (the caching allocator
+    then never hands their memory to other work before the stream's queued
+    kernels are done with it); torch's current stream when None."""
+    if stream is None:
+        return contextlib.nullcontext()
+    return _torch().cuda.stream(stream)
+
+
 def _require_cuda(*ts):
     for t in ts:
         if t is not None and not t.is_cuda:
@@ -75,7 +85,8 @@ def hessian_accumulate(H, X, stream=None):
     if H.shape != (d_in, d_in):
         raise ValueError("H must be d_in x d_in")
     nws = lib.gptq_hessian_workspace(n_tok, d_in)
-    ws = _workspace(nws, H.device)
+    with _alloc_on(stream):
+        ws = _workspace(nws, H.device)
     st = lib.gptq_hessian_accumulate(_ptr(H), _ptr(X), _dtype_code(X), n_tok, d_in, X.stride(0),
                                      _ptr(ws), nws, _stream(stream))
     _lib.check(st, "gptq_hessian_accumulate")
@@ -96,7 +107,8 @@ def hessian_accumulate_timed(H, X, stream=None):
     if H.shape != (d_in, d_in):
         raise ValueError("H must be d_in x d_in")
     nws = lib.gptq_hessian_workspace(n_tok, d_in)
-    ws = _workspace(nws, H.device)
+    with _alloc_on(stream):
+        ws = _workspace(nws, H.device)
     ms, n = ctypes.c_double(0.0), ctypes.c_int64(0)
     st = lib.gptq_hessian_accumulate_timed(_ptr(H), _ptr(X), _dtype_code(X), n_tok, d_in, X.stride(0),
                                            _ptr(ws), nws, _stream(stream), ctypes.byref(ms), ctypes.byref(n))
@@ -112,10 +124,11 @@ def prepare_hinv(H, cfg: Config, perm=None, workspace=None, stream=None):
     if H.dtype != torch.float64 or not H.is_contiguous() or H.dim() != 2 or H.shape[0] != H.shape[1]:
         raise TypeError("H must be a square contiguous float64 tensor")
     d = H.shape[0]
-    if perm is None:
-        perm = torch.empty(d, dtype=torch.int32, device=H.device)
     nws = lib.gptq_prepare_hinv_workspace(d)
-    ws = workspace if workspace is not None else _workspace(nws, H.device)
+    with _alloc_on(stream):
+        if perm is None:
+            perm = torch.empty(d, dtype=torch.int32, device=H.device)
+        ws = workspace if workspace is not None else _workspace(nws, H.device)
     st = lib.gptq_prepare_hinv(_ptr(H), d, ctypes.byref(cfg), _ptr(perm), _ptr(ws),
                                ws.numel() if ws is not None else 0, _stream(stream))
     _lib.check(st, "gptq_prepare_hinv")
@@ -141,19 +154,20 @@ def quantize_layer(W, U, perm, cfg: Config, want_w_hat=True, want_row_loss=True,
         raise TypeError("perm must be int32 of length d_in")
     dev = W.device
     ng = n_groups(d_in, cfg.group_size)
-    if out is None:
-        out = dict(codes=torch.empty((d_out, d_in), dtype=torch.uint8, device=dev),
-                   scales=torch.empty((ng, d_out), dtype=torch.float32, device=dev),
-                   zeros=torch.empty((ng, d_out), dtype=torch.float32, device=dev),
-                   g_idx=torch.empty(d_in, dtype=torch.int32, device=dev))
-        if want_w_hat:
-            out["w_hat"] = torch.empty((d_out, d_in), dtype=torch.float32, device=dev)
-        if want_row_loss:
-            out["row_loss"] = torch.empty(d_out, dtype=torch.float64, device=dev)
     nws = lib.gptq_quantize_layer_workspace(d_out, d_in, ctypes.byref(cfg))
     if nws == 0:
         raise InvalidArgument(_lib.ERR_INVALID_ARG, "gptq_quantize_layer_workspace", "invalid shape or config")
-    ws = workspace if workspace is not None else _workspace(nws, dev)
+    with _alloc_on(stream):
+        if out is None:
+            out = dict(codes=torch.empty((d_out, d_in), dtype=torch.uint8, device=dev),
+                       scales=torch.empty((ng, d_out), dtype=torch.float32, device=dev),
+                       zeros=torch.empty((ng, d_out), dtype=torch.float32, device=dev),
+                       g_idx=torch.empty(d_in, dtype=torch.int32, device=dev))
+            if want_w_hat:
+                out["w_hat"] = torch.empty((d_out, d_in), dtype=torch.float32, device=dev)
+            if want_row_loss:
+                out["row_loss"] = torch.empty(d_out, dtype=torch.float64, device=dev)
+        ws = workspace if workspace is not None else _workspace(nws, dev)
     st = lib.gptq_quantize_layer(_ptr(W), _dtype_code(W), d_out, d_in, W.stride(0), _ptr(U), _ptr(perm),
                                  ctypes.byref(cfg), _ptr(out["codes"]), _ptr(out["scales"]), _ptr(out["zeros"]),
                                  _ptr(out["g_idx"]), _ptr(out.get("w_hat")), _ptr(out.get("row_loss")),
@@ -176,7 +190,8 @@ def pack(codes, bits: int, out=None, stream=None):
     d_out, d_in = codes.shape
     wpr = packed_words_per_row(d_in, bits)
     if out is None:
-        out = torch.empty((d_out, wpr), dtype=torch.int32, device=codes.device)
+        with _alloc_on(stream):
+            out = torch.empty((d_out, wpr), dtype=torch.int32, device=codes.device)
     st = lib.gptq_pack(_ptr(codes), d_out, d_in, bits, _ptr(out), _stream(stream))
     _lib.check(st, "gptq_pack")
     return out
@@ -194,7 +209,8 @@ def pack_permuted(codes, bits: int, perm, out=None, stream=None):
         raise TypeError("perm must be contiguous int32 of length d_in")
     wpr = packed_words_per_row(d_in, bits)
     if out is None:
-        out = torch.empty((d_out, wpr), dtype=torch.int32, device=codes.device)
+        with _alloc_on(stream):
+            out = torch.empty((d_out, wpr), dtype=torch.int32, device=codes.device)
     st = lib.gptq_pack_permuted(_ptr(codes), d_out, d_in, bits, _ptr(perm), _ptr(out), _stream(stream))
     _lib.check(st, "gptq_pack_permuted")
     return out
@@ -231,7 +247,8 @@ def dequant_matmul(X, packed, bits: int, scales, zeros, *, g_idx=None, perm=None
         if t is not None and (t.dtype != torch.int32 or t.numel() != d_in or not t.is_contiguous()):
             raise TypeError(f"{name} must be contiguous int32 of length d_in")
     if out is None:
-        out = torch.empty((n_tok, d_out), dtype=torch.float32, device=X.device)
+        with _alloc_on(stream):
+            out = torch.empty((n_tok, d_out), dtype=torch.float32, device=X.device)
     if out.dtype != torch.float32 or out.dim() != 2 or out.stride(1) != 1 or out.shape != (n_tok, d_out):
         raise TypeError("out must be float32 tokens x d_out with unit column stride")
     st = lib.gptq_dequant_matmul(_ptr(X), _dtype_code(X), n_tok, d_in, X.stride(0), _ptr(packed), bits,
@@ -252,7 +269,8 @@ def gather_columns(X, perm, out=None, stream=None):
     if perm.dtype != torch.int32 or perm.numel() != d_in or not perm.is_contiguous():
         raise TypeError("perm must be contiguous int32 of length d_in")
     if out is None:
-        out = torch.empty((n_tok, d_in), dtype=X.dtype, device=X.device)
+        with _alloc_on(stream):
+            out = torch.empty((n_tok, d_in), dtype=X.dtype, device=X.device)
     if out.dtype != X.dtype or out.shape != X.shape or out.stride(1) != 1:
         raise TypeError("out must match X in dtype and shape, with unit column stride")
     st = lib.gptq_gather_columns(_ptr(X), _dtype_code(X), n_tok, d_in, X.stride(0), _ptr(perm), _ptr(out),
@@ -273,7 +291,8 @@ def quantize(W, *, X=None, H=None, cfg: Config | None = None, packed=True, strea
     if H is None:
         if X is None:
             raise ValueError("give X or H")
-        H = torch.zeros((d_in, d_in), dtype=torch.float64, device=W.device)
+        with _alloc_on(stream):
+            H = torch.zeros((d_in, d_in), dtype=torch.float64, device=W.device)
         hessian_accumulate(H, X, stream=stream)
     perm = prepare_hinv(H, cfg, stream=stream)
     out = quantize_layer(W, H, perm, cfg, stream=stream)

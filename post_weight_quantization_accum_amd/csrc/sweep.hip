@@ -75,8 +75,9 @@ int64_t n_groups_of(int64_t d_in, int32_t g) { return g > 0 ? ceil_div(d_in, g) 
 
 // Columns per superblock of the two-level lazy update: blocks are swept one
 // by one and update the rest of their superblock (K = B); each finished
-// superblock updates everything after it once (K = S).  Every group must lie
-// inside one superblock or start on a superblock boundary; otherwise S = B.
+// superblock updates everything after it once (K = S).  Where a group may
+// cross a superblock end (S % g != 0), the sweep of each superblock waits
+// for the previous far update.
 int64_t superblock_cols(int64_t d_in, const gptq_config* cfg) {
     const int64_t B = cfg->block_size;
 #ifndef GPTQ_SUPER
@@ -664,9 +665,11 @@ gptq_status sweep_launch(const void* W, gptq_dtype dt, int64_t d_out, int64_t d_
     SWEEP_ATTR(1, false)
 #undef SWEEP_ATTR
     const int64_t S = superblock_cols(d_in, cfg);
-    // Groups that span several superblocks read columns past the current
-    // superblock at their first column: those must be fully updated first.
-    const bool wait_far_before_sweep = cfg->group_size > 0 && g > S;
+    // A group that runs past the end of its superblock (groups wider than a
+    // superblock, or superblocks of one block when lcm(B, g) exceeds the
+    // superblock cap) reads columns of later superblocks at its first
+    // column; the far update that writes those columns must be done first.
+    const bool wait_far_before_sweep = cfg->group_size > 0 && S % g != 0;
 
     // A second stream runs each superblock's far update (everything past
     // the next superblock) while the next superblock is swept.

@@ -192,6 +192,11 @@ def _sweep_case(d_out, d_in, bits, g, act, sym=False, block=128, dtype="bf16", s
     (12, 60, 3, 12, False, False, 5),      # odd block, sub-block width 1
     (9, 21, 3, 6, True, False, 1),         # one column per block
     (7, 50, 4, 10, False, False, 3),       # block 3, group 10
+    # lcm(B, g) beyond the superblock cap: superblocks of one block, groups
+    # crossing superblock ends while far updates are pending (d_in > 3B)
+    (64, 1000, 4, 100, True, False, 128),
+    (48, 900, 3, 120, False, False, 128),
+    (40, 700, 4, 64, False, False, 100),
 ])
 def test_sweep_matches_oracle_given_U(d_out, d_in, bits, g, act, sym, block):
     print(f"sweep {d_out}x{d_in} b{bits} g{g} act{act} sym{sym} B{block}", flush=True)

@@ -147,12 +147,33 @@ def test_U_reverse_cholesky_identity():
         np.testing.assert_allclose(U, U2, rtol=1e-10, atol=1e-12 * np.abs(U).max())
 
 
-def test_damp_closed_form():
-    H = np.diag([1.0, 2.0, 3.0, 6.0]) + 0.1
-    Hd = O.damp_hessian(H, 0.5)
-    lam = 0.5 * np.mean(np.diag(H))
-    np.testing.assert_allclose(np.diag(Hd) - np.diag(H), lam)
-    np.testing.assert_array_equal(Hd - np.diag(np.diag(Hd)), H - np.diag(np.diag(H)))
+def test_damp_hand_values():
+    g = _load("damp_hand.json")["damp_only"]
+    Hd = O.damp_hessian(np.array(g["H"]), g["damp"])
+    np.testing.assert_allclose(Hd, np.array(g["Hd"]), rtol=1e-15, atol=0)
+
+
+def test_damp_hand_sweep():
+    # a two-column layer swept with damp 0.5: lambda shows in U and row_loss
+    g = _load("damp_hand.json")["sweep"]
+    out = O.gptq_quantize(np.array(g["W"]), np.array(g["H"]), bits=g["bits"], group_size=-1,
+                          act_order=False, block=128, damp=g["damp"])
+    np.testing.assert_allclose(out["U"], np.array(g["U"]), rtol=1e-14, atol=1e-17)
+    np.testing.assert_array_equal(out["codes"], np.array(g["codes"]))
+    np.testing.assert_allclose(out["scales"], np.array(g["scales"]), rtol=1e-15)
+    np.testing.assert_array_equal(out["zeros"], np.array(g["zeros"]))
+    np.testing.assert_allclose(out["w_hat"], np.array(g["w_hat"]), rtol=1e-15)
+    np.testing.assert_allclose(out["row_loss"], g["row_loss"], rtol=1e-13)
+    np.testing.assert_allclose(out["loss"], g["loss"], rtol=1e-13)
+
+
+def test_damp_shifts_the_spectrum():
+    # H + lambda*I has the eigenvalues of H shifted by lambda = damp * tr(H) / d
+    rng = np.random.default_rng(3)
+    H = _rand_pd(rng, 7, 1.0)
+    ev = np.linalg.eigvalsh(H)
+    evd = np.linalg.eigvalsh(O.damp_hessian(H, 0.01))
+    np.testing.assert_allclose(evd - ev, 0.01 * np.trace(H) / 7, rtol=1e-12)
 
 
 # ---------------------------------------------------------------------------

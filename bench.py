@@ -37,7 +37,7 @@ PEAK_F64_TFLOPS = 78.6         # MI355X fp64 (matrix and vector)
 PEAK_HBM_GBS = 8000.0
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hess_syrk_kernel_4096x11008_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hess_tile_kernel_4096x11008_traffic.json")
 TRAFFIC_SOURCES = ("post_weight_quantization_accum_amd/csrc/hessian.hip",
                    "post_weight_quantization_accum_amd/csrc/common.hpp")
 DQ_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "dequant_staged_kernel_4096x11008_traffic.json")
@@ -485,22 +485,25 @@ def main():
     ms_per_step = wall * 1000.0 / a.steps
     phases = {k: float(np.mean(v)) for k, v in phase_ms.items()}
 
-    # Dominant kernel: the Hessian product (hess_syrk_kernel), one launch
-    # per 32768-token chunk.  Its launches are timed with HIP events on the
-    # stream they run on (same kernels and launch configuration as above).
+    # Dominant kernel: the Hessian product (hess_tile_kernel).  One launch
+    # runs up to 1792 (256x128 tile, 32768-token window) work items; the
+    # launches of one Hessian are timed with HIP events on the stream they
+    # run on (same kernels and launch configuration as above).  Algorithmic
+    # work: n_tok * d_in * (d_in + 1) flops for the whole Hessian (2 flops
+    # per product over the upper triangle with the diagonal), divided evenly
+    # over the launches for the per-launch figure.
     hk, nl = [], 0
     for _ in range(max(1, min(a.steps, 3))):
         H.zero_()
         ms, nl = P.hessian_accumulate_timed(H, X)
         hk.append(ms)
     h_ms = float(np.mean(hk))
-    tok_per_launch = n_tok / nl
-    h_flops = float(tok_per_launch) * d_in * (d_in + 1)   # 2 flops per product, upper triangle with diagonal
+    h_flops = float(n_tok) * d_in * (d_in + 1) / nl
     achieved = h_flops / (h_ms * 1e-3) / 1e12
     traffic = measured_traffic()
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                "kernel": "hess_syrk_kernel<bf16> (Hessian product, upper triangle)",
+                "kernel": "hess_tile_kernel<bf16> (Hessian product, 256x128 tiles of the upper triangle)",
                 "launch_ms": round(h_ms, 4), "launches_per_step": nl,
                 "algorithmic_flops_per_launch": h_flops}
 

@@ -1,6 +1,6 @@
 """Build libgptq_mi355x.so (gfx950) in-tree with hipcc.
 
-Usage: python -m post_weight_quantization_accum_amd.build [--jobs N]
+Usage: python -m post_weight_quantization_accum_amd.build [--jobs N] [--incremental]
 """
 from __future__ import annotations
 
@@ -26,8 +26,12 @@ FLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
+def _compile(src: str, incremental: bool = False) -> str:
     obj = os.path.join(OBJ, os.path.basename(src) + ".o")
+    if incremental and os.path.exists(obj):
+        deps = [src] + glob.glob(os.path.join(CSRC, "*.hpp")) + glob.glob(os.path.join(HERE, "..", "include", "*.h"))
+        if all(os.path.getmtime(d) <= os.path.getmtime(obj) for d in deps):
+            return obj
     cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -36,12 +40,13 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(jobs: int | None = None, verbose: bool = False) -> str:
+def build(jobs: int | None = None, verbose: bool = False, incremental: bool = False) -> str:
+    """Compile every source (incremental: only those newer than their object)."""
     os.makedirs(OBJ, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     jobs = jobs or min(8, len(srcs))
     with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, srcs))
+        objs = list(ex.map(lambda s: _compile(s, incremental), srcs))
     tmp = LIB + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -56,6 +61,7 @@ def build(jobs: int | None = None, verbose: bool = False) -> str:
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=None)
+    ap.add_argument("--incremental", action="store_true", help="recompile only sources newer than their objects")
     a = ap.parse_args()
-    build(a.jobs, verbose=True)
+    build(a.jobs, verbose=True, incremental=a.incremental)
     sys.exit(0)

@@ -76,7 +76,7 @@ gptq_status gptq_hessian_accumulate_timed(double* H, const void* X, gptq_dtype x
     if (n_tok > 0 && !X) return GPTQ_ERR_INVALID_ARG;
     if (x_dtype != GPTQ_F32 && n_tok > 0 && (!workspace || ws_bytes < hessian_workspace_bytes(n_tok, d_in)))
         return GPTQ_ERR_WORKSPACE;
-    const int64_t n = hessian_syrk_launches(n_tok, x_dtype, d_in);
+    const int64_t n = hessian_syrk_launches(n_tok, x_dtype, d_in, ld_x, X);
     *syrk_ms = 0.0;
     *n_launches = n;
     if (n == 0) return GPTQ_OK;

@@ -49,12 +49,12 @@ struct GemmCall {
 gptq_status launch_gemm_f64_pair(hipStream_t s, const GemmCall& x, const GemmCall& y);
 
 // Hessian: H (upper) += 2 X^T X.  ws: hessian_workspace_bytes(n_tok, d)
-// bytes (float64 partial column sums of the diagonal, then the transposed
-// token chunk); unused for fp32 inputs.
-// ev: null, or 2 * hessian_syrk_launches(...) events recorded around each
-// SYRK launch (start, end) on s.
+// bytes (float64 partial tiles of narrow layers; an aligned copy of a token
+// chunk for inputs whose rows are not 16-byte aligned); unused for fp32
+// inputs.  ev: null, or 2 * hessian_syrk_launches(...) events recorded
+// around each launch of the Hessian product kernel (start, end) on s.
 size_t hessian_workspace_bytes(int64_t n_tok, int64_t d);
-int64_t hessian_syrk_launches(int64_t n_tok, gptq_dtype dt, int64_t d);
+int64_t hessian_syrk_launches(int64_t n_tok, gptq_dtype dt, int64_t d, int64_t ld_x, const void* X);
 gptq_status hessian_launch(double* H, const void* X, gptq_dtype dt, int64_t n_tok, int64_t d,
                            int64_t ld_x, void* ws, hipStream_t s, hipEvent_t* ev = nullptr);
 

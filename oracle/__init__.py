@@ -22,6 +22,7 @@ from .gptq_oracle import (  # noqa: F401
     inverse_hessian_upper,
     quant_params,
     quantize_column,
+    tie_margin,
     sweep,
     gptq_quantize,
     pack,

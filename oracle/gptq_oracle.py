@@ -194,6 +194,18 @@ def quantize_column(w: np.ndarray, scale: np.ndarray, zero: np.ndarray, bits: in
     return code, q
 
 
+def tie_margin(w: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    """Distance of w/scale from the nearest rounding boundary (a
+    half-integer), in code units: 0 at an exact tie, 1/2 on a grid point.
+
+    Diagnostic for comparing two implementations: a code can only differ
+    between two correct sweeps whose compensated values differ by rounding
+    if this margin is that small.
+    """
+    y = w / scale
+    return 0.5 - np.abs(y - np.rint(y))
+
+
 # ---------------------------------------------------------------------------
 # Step 3: the blocked column sweep with error compensation.
 # ---------------------------------------------------------------------------
@@ -209,7 +221,7 @@ def _check_block_group(d_in: int, group_size: int, block: int) -> int:
 
 
 def sweep(W: np.ndarray, U: np.ndarray, bits: int, group_size: int, sym: bool,
-          block: int = 128):
+          block: int = 128, force=None, margins: bool = False):
     """Quantize the columns of W (already in sweep order) left to right.
 
     "GPTQ量化算法深度解析" §2.4 (fixed order; lazy batch update: errors are
@@ -222,6 +234,14 @@ def sweep(W: np.ndarray, U: np.ndarray, bits: int, group_size: int, sym: bool,
     Returns (codes, scales, zeros, w_hat, row_loss), all in sweep order;
     scales/zeros are [n_groups][d_out]; row_loss[r] = sum_c (w_c - q_c)^2 /
     (2 U_cc^2).
+
+    Two diagnostics for comparisons with another implementation (they leave
+    the arithmetic above untouched): ``margins=True`` appends the tie margin
+    of every code (tie_margin of the value quantized, d_out x d_in);
+    ``force`` maps a sweep column c to (rows, codes): those rows take the
+    given codes at column c instead of their rounded value, and the sweep
+    continues from the resulting quantized value, which replays another
+    implementation's decision at a rounding tie.
     """
     if bits not in (2, 3, 4, 8):
         raise InvalidArgument("bits must be 2, 3, 4 or 8")
@@ -234,6 +254,7 @@ def sweep(W: np.ndarray, U: np.ndarray, bits: int, group_size: int, sym: bool,
     scales = np.zeros((n_groups, d_out), dtype=np.float64)
     zeros = np.zeros((n_groups, d_out), dtype=np.float64)
     row_loss = np.zeros(d_out, dtype=np.float64)
+    margin = np.zeros((d_out, d_in), dtype=np.float64) if margins else None
     scale = zero = None
 
     for i1 in range(0, d_in, block):
@@ -258,6 +279,12 @@ def sweep(W: np.ndarray, U: np.ndarray, bits: int, group_size: int, sym: bool,
                 zeros[c // g] = zero
             w = W1[:, k]
             code, q = quantize_column(w, scale, zero, bits)
+            if margins:
+                margin[:, c] = tie_margin(w, scale)
+            if force is not None and c in force:
+                rows, fc = force[c]
+                code[rows] = fc
+                q[rows] = scale[rows] * (code[rows] - zero[rows])
             codes[:, c] = code.astype(np.int64)
             w_hat[:, c] = q
             ucc = U[c, c]
@@ -267,6 +294,8 @@ def sweep(W: np.ndarray, U: np.ndarray, bits: int, group_size: int, sym: bool,
             row_loss += (w - q) ** 2 / (2.0 * ucc * ucc)
         # lazy batch update of every later column
         W[:, i2:] -= Err @ U[i1:i2, i2:]
+    if margins:
+        return codes, scales, zeros, w_hat, row_loss, margin
     return codes, scales, zeros, w_hat, row_loss
 
 

@@ -24,3 +24,85 @@ def compare_codes(got: np.ndarray, ref: np.ndarray):
     same = float(np.mean(got == ref))
     mx = int(np.abs(got - ref).max()) if got.size else 0
     return same, mx
+
+
+def tie_replay(O, Wp, U, codes_gpu_p, bits, group_size, sym=False, block=128, tau=1e-4, max_forces=32):
+    """Classify GPU-vs-oracle code differences by rounding ties and replay.
+
+    Wp, codes_gpu_p: weights and GPU codes in sweep order (columns permuted
+    by perm); U: the oracle's own factor.  Rows are independent given U, so
+    each differing row is replayed on its own: the oracle sweep is re-run
+    taking the GPU's code at the row's first remaining difference, which is
+    accepted only if the oracle's value there lies within ``tau`` code units
+    of a rounding boundary and the codes differ by one (a tie decided the
+    other way); repeated until the row agrees or a difference is not such a
+    tie.  Returns a dict:
+      same_raw, maxdiff_raw, rows_differing: the raw comparison;
+      ties: [(row, col, margin)] forced decisions; other: [(row, col, margin,
+      delta)] differences that are not ties (a failure);
+      codes, scales, zeros, w_hat, row_loss: the oracle's outputs (sweep
+      order) after the replay, every row included.
+    """
+    import numpy as np
+    codes_gpu_p = np.asarray(codes_gpu_p).astype(np.int64)
+    base = O.sweep(Wp, U, bits, group_size, sym, block, margins=True)
+    codes, scales, zeros, w_hat, row_loss, margin = [np.array(a, copy=True) for a in base]
+    same_raw = float(np.mean(codes == codes_gpu_p))
+    maxdiff_raw = int(np.abs(codes - codes_gpu_p).max()) if codes.size else 0
+    rows = np.nonzero((codes != codes_gpu_p).any(axis=1))[0]
+    ties, other = [], []
+    for r in rows:
+        force = {}
+        cr, mr = codes[r:r + 1], margin[r:r + 1]
+        out = None
+        for _ in range(max_forces):
+            d = np.nonzero(cr[0] != codes_gpu_p[r])[0]
+            if d.size == 0:
+                break
+            c = int(d[0])
+            delta = int(codes_gpu_p[r, c] - cr[0, c])
+            m = float(mr[0, c])
+            if abs(delta) != 1 or m >= tau:
+                other.append((int(r), c, m, delta))
+                break
+            ties.append((int(r), c, m))
+            force[c] = (np.array([0]), np.array([float(codes_gpu_p[r, c])]))
+            out = O.sweep(Wp[r:r + 1], U, bits, group_size, sym, block, force=force, margins=True)
+            cr, mr = out[0], out[5]
+        if out is not None:
+            codes[r], w_hat[r], row_loss[r] = out[0][0], out[3][0], out[4][0]
+            scales[:, r], zeros[:, r] = out[1][:, 0], out[2][:, 0]
+    return dict(same_raw=same_raw, maxdiff_raw=maxdiff_raw, rows_differing=int(rows.size), ties=ties,
+                other=other, codes=codes, scales=scales, zeros=zeros, w_hat=w_hat, row_loss=row_loss)
+
+
+def assert_from_x_parity(O, W64, H, got, bits, group_size, act_order, sym=False, block=128, damp=0.01, name=""):
+    """The GPU layer (got: original-order outputs) against the oracle run from
+    the same activations' float64 Hessian H: every differing code is a
+    rounding tie decided the other way (or follows from one in its row, as
+    the replay shows); after the replay the codes are identical, scales
+    within 1e-5 relative, zero points equal, and the layer loss within 1e-3
+    relative.  Returns the replay summary (raw numbers included)."""
+    import numpy as np
+    ref = O.gptq_quantize(W64, H, bits=bits, group_size=group_size, sym=sym, act_order=act_order, block=block,
+                          damp=damp)
+    perm = ref["perm"]
+    assert np.array_equal(np.asarray(got["perm"]).astype(np.int64), perm), name
+    rp = tie_replay(O, W64[:, perm], ref["U"], np.asarray(got["codes"])[:, perm], bits, group_size, sym, block)
+    assert not rp["other"], (name, rp["other"][:5])
+    assert np.array_equal(rp["codes"], np.asarray(got["codes"])[:, perm].astype(np.int64)), name
+    sc_g = np.asarray(got["scales"]).astype(np.float64)
+    np.testing.assert_allclose(sc_g, rp["scales"], rtol=1e-5, atol=0, err_msg=name)
+    np.testing.assert_array_equal(np.asarray(got["zeros"]).astype(np.float64), rp["zeros"], err_msg=name)
+    loss_g = O.layer_loss(W64, np.asarray(got["w_hat"]).astype(np.float64), H).sum()
+    w_hat_o = np.empty_like(rp["w_hat"])
+    w_hat_o[:, perm] = rp["w_hat"]
+    loss_o = O.layer_loss(W64, w_hat_o, H).sum()
+    loss_raw = ref["loss"].sum()
+    assert abs(loss_g - loss_o) <= 1e-3 * loss_o, (name, loss_g, loss_o)
+    rp.update(loss_gpu=float(loss_g), loss_replayed=float(loss_o), loss_oracle=float(loss_raw), ref=ref)
+    print(f"{name}: identical {rp['same_raw']:.6f} (max diff {rp['maxdiff_raw']}, rows differing "
+          f"{rp['rows_differing']}, ties replayed {len(rp['ties'])}, min tie margin "
+          f"{min([t[2] for t in rp['ties']], default=float('nan')):.2e}); loss gpu {loss_g:.6g} oracle "
+          f"{loss_raw:.6g} replayed {loss_o:.6g}", flush=True)
+    return rp

@@ -1,6 +1,6 @@
 """Workload 5 (OPT-175B-shaped block quantized in sequence) on the GPU (needs an MI355X).
 
-* A block in sequence at reduced width (hidden 256, ffn 1024, 4096 fp16
+* A block in sequence at reduced width (hidden 256, ffn 1024, 32768 fp16
   tokens, 3-bit, group 128, natural order): q, k, v are quantized on H(X0);
   A = X0 W_v^T with the quantized v, out is quantized on H(A); h1 = X0 +
   A W_out^T, fc1 on H(h1); fc2 on H(relu(h1 W_fc1^T)).  Every product uses
@@ -8,14 +8,18 @@
   packed words (identity attention, residual, no layer norm: the reading of
   "GPTQ论文复现指南" §3.2's --true-sequential taken for this harness).
   Per layer the oracle quantizes the same weights from the same activations
-  (the GPU chain's activations, handed over as data): given the GPU's own
-  Hessian of them, codes >= 99.99% identical and the loss within 1e-6; from
-  its own float64 Hessian (downstream inputs have nearly singular Hessians,
-  where the GPU's float32 chunk sums move codes), codes >= 99% identical with
-  differences <= 2 and the layer loss within 1e-2.  The chain products are
-  checked against the oracle's product from the same packed layer.  The
-  oracle's own chain (its own quantized weights and float64 products) must
-  reach the same total loss within 1e-2.
+  (the GPU chain's activations, handed over as data):
+  - given the GPU's own Hessian of them: codes >= 99.99% identical, loss
+    within 1e-6;
+  - from its own float64 Hessian: >= 99.9% of codes identical, every
+    difference <= 1, layer loss within 1e-3; every differing code is a
+    rounding tie decided the other way or follows from one in its row (the
+    oracle replayed with the GPU's decision at that tie reproduces the row),
+    and after the replay scales are within 1e-5 relative and zero points
+    equal.
+  The chain products are checked against the oracle's product from the same
+  packed layer, and the oracle's own chain (its own quantized weights and
+  float64 products) must reach the same total loss within 1e-3.
 * The widest layer at full size: fc2, 12288 x 49152, its float64 Hessian
   (19.3 GB) from 16384 tokens of the workload's activation recipe.  The
   oracle cannot factor 49152^2 in a test, so: sampled Hessian entries
@@ -33,7 +37,7 @@ import oracle as O
 import post_weight_quantization_accum_amd as P
 from post_weight_quantization_accum_amd import synth
 
-from _util import compare_codes
+from _util import assert_from_x_parity, compare_codes
 
 pytestmark = pytest.mark.gpu
 
@@ -56,7 +60,7 @@ def _product(Xd, out, bits, gs):
 
 
 def test_block_in_sequence_reduced():
-    bits, gs, h, ffn, n = 3, 128, 256, 1024, 4096
+    bits, gs, h, ffn, n = 3, 128, 256, 1024, 32768
     cfg = P.make_config(bits=bits, group_size=gs, act_order=False, block=128, damp=0.01)
     X0, _, _ = synth.gen_activations(n, h, "t4", "f16", seed=5001, outlier_count=1, outlier_scale=100.0)
     Ws = {name: synth.gen_weights(d_out, d_in, 0.01, "f16", 5010 + i)
@@ -79,17 +83,10 @@ def test_block_in_sequence_reduced():
     outs["fc2"] = _quantize_on(_f16_to_torch(Ws["fc2"]), r, cfg)
     torch.cuda.synchronize()
 
-    # per layer, on the same weights and the same activations:
-    # (a) the oracle given the GPU's own Hessian of those activations: the
-    #     solver decides in float64 on both sides, so codes and loss agree;
-    # (b) the oracle from its own float64 Hessian.  The GPU's Hessian sums
-    #     each chunk in float32; downstream of the first layers the inputs
-    #     are projections of X0 (A: dominated by X0's outlier channel; fc2's:
-    #     ReLU of a rank-256 map into 1024 dimensions), whose Hessians are
-    #     close to singular, and there those rounding differences move codes
-    #     (0.05% of out's, 0.4% of fc2's, some by 2 after a cascade) and,
-    #     through the compensated values, the scales.  Bounds: codes >= 99%
-    #     identical with differences <= 2, layer loss within 1e-2.
+    # per layer, on the same weights and the same activations: (a) the oracle
+    # given the GPU's own Hessian of them (the solver decides in float64 on
+    # both sides, so codes and loss agree); (b) the oracle from its own
+    # float64 Hessian, with the tie replay for any difference
     total_gpu = 0.0
     for name in ("q", "k", "v", "out", "fc1", "fc2"):
         Xd = inputs[name]
@@ -105,17 +102,11 @@ def test_block_in_sequence_reduced():
         lg_h = O.layer_loss(W64, got["w_hat"].astype(np.float64), Hg).sum()
         assert same_h >= 0.9999 and mx_h <= 1, name
         assert abs(lg_h - ref_h["loss"].sum()) <= 1e-6 * ref_h["loss"].sum(), name
-        ref = O.gptq_quantize(W64, X=Xl, bits=bits, group_size=gs, act_order=False, block=128, damp=0.01)
-        same, mx = compare_codes(got["codes"], ref["codes"])
-        row_g = O.layer_loss(W64, got["w_hat"].astype(np.float64), ref["H"])
-        row_o = ref["loss"]
-        agree = np.all(got["codes"] == ref["codes"], axis=1)
-        loss_g, loss_o = row_g.sum(), row_o.sum()
-        print(f"{name}: given the GPU's H identical {same_h:.5f}; from X identical {same:.5f} max diff {mx} "
-              f"rows differing {int((~agree).sum())} loss gpu {loss_g:.6g} oracle {loss_o:.6g}", flush=True)
-        assert same >= 0.99 and mx <= 2, name
-        assert abs(loss_g - loss_o) <= 1e-2 * loss_o, name
-        total_gpu += loss_g
+        H = O.hessian(Xl)
+        rp = assert_from_x_parity(O, W64, H, got, bits, gs, False, name=f"{name} from X")
+        assert rp["same_raw"] >= 0.999 and rp["maxdiff_raw"] <= 1, name
+        assert abs(rp["loss_gpu"] - rp["loss_oracle"]) <= 1e-3 * rp["loss_oracle"], name
+        total_gpu += rp["loss_gpu"]
     # the chain products against the oracle's product from the same packed layer
     for name, Xd, Y in (("v", X0d, A), ("fc1", h1, None)):
         o = {k: v.cpu().numpy() for k, v in outs[name].items()}
@@ -157,7 +148,7 @@ def test_block_in_sequence_reduced():
     r2 = q("fc2", f16(np.maximum(h1o @ r1["w_hat"].T, 0.0)))
     total_o += r2["loss"].sum()
     print(f"chain loss gpu {total_gpu:.6g} oracle chain {total_o:.6g}", flush=True)
-    assert abs(total_gpu - total_o) <= 1e-2 * total_o
+    assert abs(total_gpu - total_o) <= 1e-3 * total_o
 
 
 @pytest.mark.timeout(900)

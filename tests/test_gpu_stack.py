@@ -2,19 +2,20 @@
 (post_weight_quantization_accum_amd.sequential) against the oracle's block
 chain (needs an MI355X).
 
-Two blocks of hidden 256 / ffn 1024 on 4096 tokens, in the recipes of
+Two blocks of hidden 256 / ffn 1024 on 16384 tokens, in the recipes of
 workload 5 (fp16, 3-bit g128, natural order) and workload 3 (bf16, 4-bit
 g128, act-order: the products gather activations through perm).  Every
 layer is checked on the GPU's own activations (handed to the oracle as
 data):
 * given the GPU's Hessian of them, codes >= 99.99% identical, loss to 1e-6;
-* from the oracle's float64 Hessian, codes >= 99% identical, differences
-  <= 2, layer loss within 1e-2 (downstream Hessians are close to singular,
-  where the GPU's float32 chunk sums move codes);
+* from the oracle's float64 Hessian: >= 99.9% of codes identical, every
+  difference <= 1, layer loss within 1e-3; every differing code is a
+  rounding tie decided the other way or follows from one (tie replay), and
+  after the replay scales are within 1e-5 relative and zero points equal;
 * each block's output equals the float64 recomputation from the GPU's own
   intermediate activations and packed layers, to the dtype's rounding plus
   the product's float32 bound.
-The oracle's own two-block chain reaches the same total loss within 2e-2.
+The oracle's own two-block chain reaches the same total loss within 1e-3.
 """
 import numpy as np
 import pytest
@@ -25,7 +26,7 @@ import post_weight_quantization_accum_amd as P
 from post_weight_quantization_accum_amd import sequential as S
 from post_weight_quantization_accum_amd import synth
 
-from _util import compare_codes, to_torch
+from _util import assert_from_x_parity, compare_codes, to_torch
 
 pytestmark = pytest.mark.gpu
 
@@ -56,7 +57,7 @@ def _product_bound(X64, q, bits, gs, perm):
 
 @pytest.mark.parametrize("dtype,bits,act", [("f16", 3, False), ("bf16", 4, True)])
 def test_two_block_stack(dtype, bits, act):
-    gs, h, ffn, n, nblocks = 128, 256, 1024, 4096, 2
+    gs, h, ffn, n, nblocks = 128, 256, 1024, 16384, 2
     cfg = P.make_config(bits=bits, group_size=gs, act_order=act, block=128, damp=0.01)
     X0, _, _ = synth.gen_activations(n, h, "t4", dtype, seed=6001, outlier_count=1, outlier_scale=50.0)
     shapes = (("q", h, h), ("k", h, h), ("v", h, h), ("out", h, h), ("fc1", ffn, h), ("fc2", h, ffn))
@@ -85,15 +86,11 @@ def test_two_block_stack(dtype, bits, act):
             lg_h = O.layer_loss(W64[name], got[name]["w_hat"].astype(np.float64), Hg).sum()
             assert same_h >= 0.9999 and mx_h <= 1, (b, name)
             assert abs(lg_h - ref_h["loss"].sum()) <= 1e-6 * ref_h["loss"].sum(), (b, name)
-            ref = O.gptq_quantize(W64[name], X=Xl, **q)
-            same, mx = compare_codes(got[name]["codes"], ref["codes"])
-            lg = O.layer_loss(W64[name], got[name]["w_hat"].astype(np.float64), ref["H"]).sum()
-            lo = ref["loss"].sum()
-            print(f"block {b} {name}: given H {same_h:.5f}; from X {same:.5f} (max diff {mx}); "
-                  f"loss {lg:.6g} vs {lo:.6g}", flush=True)
-            assert same >= 0.99 and mx <= 2, (b, name)
-            assert abs(lg - lo) <= 1e-2 * lo, (b, name)
-            total_gpu += lg
+            rp = assert_from_x_parity(O, W64[name], O.hessian(Xl), got[name], bits, gs, act,
+                                      name=f"block {b} {name} from X")
+            assert rp["same_raw"] >= 0.999 and rp["maxdiff_raw"] <= 1, (b, name)
+            assert abs(rp["loss_gpu"] - rp["loss_oracle"]) <= 1e-3 * rp["loss_oracle"], (b, name)
+            total_gpu += rp["loss_gpu"]
         # the block's output from the GPU's own intermediates, in float64
         X64 = _to_f64(X_in)
         h1 = X64.copy()
@@ -119,4 +116,4 @@ def test_two_block_stack(dtype, bits, act):
         res_o, _, Xo = O.quantize_block_chain(W64, Xo, dtype, **q)
         total_o += sum(res_o[name]["loss"].sum() for name in S.LAYERS)
     print(f"stack loss gpu {total_gpu:.6g} oracle chain {total_o:.6g}", flush=True)
-    assert abs(total_gpu - total_o) <= 2e-2 * total_o
+    assert abs(total_gpu - total_o) <= 1e-3 * total_o

@@ -587,3 +587,70 @@ def test_round_to_dtype_bf16_ties_and_range():
     v = np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, 1.0 + 2.0 ** -8 + 2.0 ** -20, -2.5])
     got = O.round_to_dtype(v, "bf16")
     assert np.array_equal(got, [1.0, 1.0 + 2.0 ** -6, 1.0 + 2.0 ** -7, -2.5])
+
+
+# ---------------------------------------------------------------------------
+# Diagnostics used by the GPU parity tests: tie margins and forced decisions
+# ---------------------------------------------------------------------------
+
+def test_tie_margin_hand_values():
+    w = np.array([0.25, 0.3, 0.35, -0.25, 0.1])
+    s = np.full(5, 0.1)
+    # w/scale = 2.5 (tie), 3.0 (grid point), 3.5 (tie), -2.5 (tie), 1.0
+    np.testing.assert_allclose(O.tie_margin(w, s), [0.0, 0.5, 0.0, 0.0, 0.5], atol=1e-12)
+    np.testing.assert_allclose(O.tie_margin(np.array([0.275]), np.array([0.1])), [0.25], atol=1e-12)
+
+
+def test_forced_natural_codes_change_nothing():
+    rng = np.random.default_rng(21)
+    W = rng.normal(0, 0.02, (6, 40))
+    H = _rand_pd(rng, 40, 1.0)
+    U = O.inverse_hessian_upper(O.damp_hessian(H, 0.01))
+    base = O.sweep(W, U, 3, 16, False, 16)
+    force = {c: (np.arange(6), base[0][:, c].astype(np.float64)) for c in (0, 7, 19, 39)}
+    out = O.sweep(W, U, 3, 16, False, 16, force=force)
+    for a, b in zip(base, out):
+        np.testing.assert_array_equal(a, b)
+
+
+def test_forced_code_with_diagonal_hessian_changes_only_that_code():
+    # H proportional to I: no compensation, so a forced code changes only
+    # itself (and its reconstruction); every other code stays round-to-nearest
+    rng = np.random.default_rng(22)
+    W = rng.normal(0, 0.02, (4, 32))
+    U = O.inverse_hessian_upper(O.damp_hessian(3.0 * np.eye(32), 0.0))
+    base = O.sweep(W, U, 4, 16, False, 16)
+    c0 = base[0][2, 5]
+    alt = c0 + 1 if c0 < 15 else c0 - 1
+    out = O.sweep(W, U, 4, 16, False, 16, force={5: (np.array([2]), np.array([float(alt)]))})
+    want = base[0].copy()
+    want[2, 5] = alt
+    np.testing.assert_array_equal(out[0], want)
+    assert out[3][2, 5] == pytest.approx(base[1][0, 2] * (alt - base[2][0, 2]), rel=1e-15)
+
+
+def test_tie_replay_explains_a_planted_tie_and_rejects_a_non_tie():
+    import sys
+    sys.path.insert(0, os.path.dirname(__file__))
+    from _util import tie_replay
+    rng = np.random.default_rng(23)
+    W = rng.normal(0, 0.02, (12, 96))
+    H = _rand_pd(rng, 96, 1.5)
+    U = O.inverse_hessian_upper(O.damp_hessian(H, 0.01))
+    base = O.sweep(W, U, 3, 32, False, 32, margins=True)
+    codes, m = base[0], base[5]
+    inner = (codes > 0) & (codes < 7)
+    r, c = np.unravel_index(np.argmin(np.where(inner, m, 1.0)), m.shape)
+    alt = codes[r, c] + (1 if W[r, c] > 0 else -1)
+    # another sweep that decided (r, c) the other way: explained by one tie
+    other_sweep = O.sweep(W, U, 3, 32, False, 32, force={int(c): (np.array([r]), np.array([float(alt)]))})
+    rp = tie_replay(O, W, U, other_sweep[0], 3, 32, block=32, tau=max(2 * m[r, c], 1e-12))
+    assert rp["other"] == [] and len(rp["ties"]) >= 1 and rp["ties"][0][:2] == (r, c)
+    assert np.array_equal(rp["codes"], other_sweep[0])
+    # a code off by one far from any tie is not explained
+    bad = codes.copy()
+    far = np.argmax(np.where(inner, m, -1.0))
+    rb, cb = np.unravel_index(far, m.shape)
+    bad[rb, cb] += 1
+    rp = tie_replay(O, W, U, bad, 3, 32, block=32)
+    assert rp["other"] and rp["other"][0][:2] == (rb, cb)

@@ -374,7 +374,8 @@ def layer_loss(W, W_hat, H) -> np.ndarray:
     that "GPTQ量化算法深度解析" §2.1 puts at the centre of the objective.
     """
     dW = np.asarray(W_hat, dtype=np.float64) - np.asarray(W, dtype=np.float64)
-    return 0.5 * np.einsum("ij,jk,ik->i", dW, np.asarray(H, dtype=np.float64), dW)
+    # row r: 1/2 * (dW H)_r . dW_r, the product dW H by the library's matmul
+    return 0.5 * np.einsum("ij,ij->i", dW @ np.asarray(H, dtype=np.float64), dW)
 
 
 # ---------------------------------------------------------------------------

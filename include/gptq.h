@@ -114,6 +114,25 @@ gptq_status gptq_hessian_accumulate_timed(double* H, const void* X, gptq_dtype x
                                           void* workspace, size_t ws_bytes, hipStream_t stream,
                                           double* syrk_ms, int64_t* n_launches);
 
+/* Allocation-free variant of gptq_hessian_accumulate, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  Same arguments and result as
+ * gptq_hessian_accumulate, minus the workspace: its scratch memory is a
+ * fixed device array of GPTQ_NOALLOC_SCRATCH_BYTES bytes inside the library
+ * (one per GPU, held until the process ends).  Narrow layers then sum fewer,
+ * longer token windows per partial tile (results agree with
+ * gptq_hessian_accumulate to float64 rounding; identical when its plan fits
+ * the array); inputs whose rows are not 16-byte aligned are copied in
+ * chunks of at most a quarter of the array.  Calls nothing that allocates.
+ * Returns GPTQ_ERR_WORKSPACE if such a copied chunk of 256 tokens does not
+ * fit (misaligned rows wider than 32768 elements), GPTQ_ERR_HIP if the
+ * array's address cannot be obtained.  All calls on one GPU share its
+ * array: calls that overlap on one GPU race. */
+#define GPTQ_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+gptq_status gptq_hessian_accumulate_noalloc(double* H, const void* X, gptq_dtype x_dtype,
+                                            int64_t n_tok, int64_t d_in, int64_t ld_x,
+                                            hipStream_t stream);
+
 /* ------------------------------------------------------------------------
  * Step 2 -- column order, damping, Cholesky form of the inverse
  * ("GPTQ量化算法深度解析" §2.4, §3.1 steps 1-2, §3.3 desc_act and damp).

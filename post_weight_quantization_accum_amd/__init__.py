@@ -19,7 +19,7 @@ from ._lib import (  # noqa: F401
     Unsupported, WorkspaceError, make_config, load, version, status_string,
 )
 
-__all__ = ["hessian_accumulate", "hessian_accumulate_timed", "prepare_hinv", "quantize_layer", "pack", "quantize",
+__all__ = ["hessian_accumulate", "hessian_accumulate_timed", "hessian_accumulate_noalloc", "prepare_hinv", "quantize_layer", "pack", "quantize",
            "pack_permuted", "dequant_matmul", "dequant_max_groups", "gather_columns", "packed_words_per_row", "make_config",
            "Config", "load"]
 
@@ -114,6 +114,25 @@ def hessian_accumulate_timed(H, X, stream=None):
                                            _ptr(ws), nws, _stream(stream), ctypes.byref(ms), ctypes.byref(n))
     _lib.check(st, "gptq_hessian_accumulate_timed")
     return ms.value, n.value
+
+
+def hessian_accumulate_noalloc(H, X, stream=None):
+    """hessian_accumulate through the allocation-free entry point: no
+    workspace (the library's fixed per-GPU scratch array instead)."""
+    lib = load()
+    torch = _torch()
+    _require_cuda(H, X)
+    if H.dtype != torch.float64 or not H.is_contiguous():
+        raise TypeError("H must be a contiguous float64 tensor")
+    if X.dim() != 2 or X.stride(1) != 1:
+        raise ValueError("X must be 2-D with unit column stride")
+    n_tok, d_in = X.shape
+    if H.shape != (d_in, d_in):
+        raise ValueError("H must be d_in x d_in")
+    st = lib.gptq_hessian_accumulate_noalloc(_ptr(H), _ptr(X), _dtype_code(X), n_tok, d_in, X.stride(0),
+                                             _stream(stream))
+    _lib.check(st, "gptq_hessian_accumulate_noalloc")
+    return H
 
 
 def prepare_hinv(H, cfg: Config, perm=None, workspace=None, stream=None):

@@ -21,6 +21,7 @@ F32, F16, BF16 = 0, 1, 2
 # Every symbol include/gptq.h declares.
 EXPORTS = (
     "gptq_config_default", "gptq_hessian_workspace", "gptq_hessian_accumulate", "gptq_hessian_accumulate_timed",
+    "gptq_hessian_accumulate_noalloc",
     "gptq_prepare_hinv_workspace", "gptq_prepare_hinv", "gptq_quantize_layer_workspace",
     "gptq_quantize_layer", "gptq_packed_words_per_row", "gptq_pack", "gptq_pack_permuted",
     "gptq_dequant_max_groups", "gptq_dequant_matmul", "gptq_gather_columns", "gptq_status_string",
@@ -95,6 +96,8 @@ def load(path: str | None = None):
     lib.gptq_hessian_accumulate_timed.argtypes = [vp, vp, ctypes.c_int, i64, i64, i64, vp, sz, vp,
                                                   ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
     lib.gptq_hessian_accumulate_timed.restype = ctypes.c_int
+    lib.gptq_hessian_accumulate_noalloc.argtypes = [vp, vp, ctypes.c_int, i64, i64, i64, vp]
+    lib.gptq_hessian_accumulate_noalloc.restype = ctypes.c_int
     lib.gptq_prepare_hinv_workspace.argtypes = [i64]
     lib.gptq_prepare_hinv_workspace.restype = sz
     lib.gptq_prepare_hinv.argtypes = [vp, i64, cfgp, vp, vp, sz, vp]

@@ -532,9 +532,19 @@ __global__ __launch_bounds__(256) void hess_f32_kernel(double* __restrict__ H, c
 // Host-side planning
 // ---------------------------------------------------------------------------
 
+// Workspace budget of one call: at most max_items partial tiles (0: as many
+// as the plan wants) and an aligned copy of at most `repack` bytes.
+struct Budget {
+    int64_t max_items;
+    size_t repack;
+};
+constexpr Budget DEFAULT_BUDGET{0, REPACK_BYTES};
+
 // Work plan of one pass.  Full mode: windows of WIN_MAX tokens; partial
-// mode: windows short enough for about 512 items.  win_cap bounds a window
-// so that its byte offsets fit in 31 bits.
+// mode: windows short enough for about 512 items (fewer if the budget
+// holds fewer partial tiles; with room for less than one window of them the
+// pass runs in full mode, one window of tiles per launch).  win_cap bounds a
+// window so that its byte offsets fit in 31 bits.
 struct Plan {
     Grid g;
     bool partial;
@@ -546,15 +556,16 @@ int64_t window_cap(int64_t ld) {
     return cap < RUN_TOK ? RUN_TOK : cap;
 }
 
-Plan make_plan(int64_t n_tok, int64_t d, int64_t win_cap) {
+Plan make_plan(int64_t n_tok, int64_t d, int64_t win_cap, int64_t max_items) {
     Plan p;
     p.g = tile_grid(d);
-    p.partial = p.g.n_tiles < PART_TILES;
+    p.partial = p.g.n_tiles < PART_TILES && (max_items == 0 || max_items >= p.g.n_tiles);
     int64_t win = WIN_MAX;
     if (p.partial) {
         int64_t nw = ceil_div(512, p.g.n_tiles);
         const int64_t runs = ceil_div(n_tok, RUN_TOK);
         if (nw > runs) nw = runs;
+        if (max_items > 0 && nw > max_items / p.g.n_tiles) nw = max_items / p.g.n_tiles;
         if (nw < 1) nw = 1;
         win = ceil_div(ceil_div(n_tok, nw), RUN_TOK) * RUN_TOK;
     }
@@ -562,14 +573,15 @@ Plan make_plan(int64_t n_tok, int64_t d, int64_t win_cap) {
     p.win = win;
     p.n_win = ceil_div(n_tok, win);
     p.n_items = p.n_win * p.g.n_tiles;
-    p.per_launch = p.partial ? p.n_items : (p.g.n_tiles / 256) * 256;
+    if (p.partial) p.per_launch = p.n_items;
+    else p.per_launch = p.g.n_tiles >= 256 ? (p.g.n_tiles / 256) * 256 : p.g.n_tiles;
     return p;
 }
 
 constexpr int64_t NO_CAP = int64_t(1) << 62;
 
-size_t part_bytes(int64_t n_tok, int64_t d) {
-    const Plan p = make_plan(n_tok, d, NO_CAP);
+size_t part_bytes(int64_t n_tok, int64_t d, const Budget& b) {
+    const Plan p = make_plan(n_tok, d, NO_CAP, b.max_items);
     return p.partial ? (size_t)p.n_items * PART_ELEMS * sizeof(double) : 0;
 }
 
@@ -578,15 +590,15 @@ bool aligned_input(const void* X, int64_t d, int64_t ld) {
     return (ld % 8 == 0) && (d % 8 == 0) && ((uintptr_t)X % 16 == 0) && ld <= (int64_t(1) << 21);
 }
 
-int64_t repack_tokens(int64_t d) {
+int64_t repack_tokens(int64_t d, const Budget& b) {
     const int64_t ldd = ceil_div(d, 8) * 8;
-    int64_t t = (int64_t)(REPACK_BYTES / (2 * (size_t)ldd)) / RUN_TOK * RUN_TOK;
+    int64_t t = (int64_t)(b.repack / (2 * (size_t)ldd)) / RUN_TOK * RUN_TOK;
     return t < RUN_TOK ? RUN_TOK : t;
 }
 
-size_t repack_bytes(int64_t n_tok, int64_t d) {
+size_t repack_bytes(int64_t n_tok, int64_t d, const Budget& b) {
     const int64_t ldd = ceil_div(d, 8) * 8;
-    int64_t nt = repack_tokens(d);
+    int64_t nt = repack_tokens(d, b);
     if (nt > n_tok) nt = n_tok;
     return align_up((size_t)nt * ldd * 2, 256);
 }
@@ -594,17 +606,17 @@ size_t repack_bytes(int64_t n_tok, int64_t d) {
 // Token chunks of one aligned call: one chunk, unless the window cap forces
 // partial-mode windows shorter than planned (then chunks of as many capped
 // windows as the workspace holds).
-int64_t aligned_chunk(int64_t n_tok, int64_t d, int64_t ld) {
-    const Plan p0 = make_plan(n_tok, d, NO_CAP);
+int64_t aligned_chunk(int64_t n_tok, int64_t d, int64_t ld, const Budget& b) {
+    const Plan p0 = make_plan(n_tok, d, NO_CAP, b.max_items);
     const int64_t cap = window_cap(ld);
     return (p0.partial && p0.win > cap) ? p0.n_win * cap : n_tok;
 }
 
-int64_t launches_aligned(int64_t n_tok, int64_t d, int64_t ld) {
+int64_t launches_aligned(int64_t n_tok, int64_t d, int64_t ld, const Budget& b) {
     int64_t n = 0;
-    const int64_t chunk = aligned_chunk(n_tok, d, ld);
+    const int64_t chunk = aligned_chunk(n_tok, d, ld, b);
     for (int64_t c0 = 0; c0 < n_tok; c0 += chunk) {
-        const Plan p = make_plan((n_tok - c0 < chunk) ? n_tok - c0 : chunk, d, window_cap(ld));
+        const Plan p = make_plan((n_tok - c0 < chunk) ? n_tok - c0 : chunk, d, window_cap(ld), b.max_items);
         n += ceil_div(p.n_items, p.per_launch);
     }
     return n;
@@ -613,14 +625,14 @@ int64_t launches_aligned(int64_t n_tok, int64_t d, int64_t ld) {
 // H += 2 X^T X for 16-byte aligned rows (ld and d multiples of 8).
 template <typename Tag>
 gptq_status hess_aligned(double* H, const uint16_t* X, int64_t n_tok, int64_t d, int64_t ld, double* part,
-                         hipStream_t s, hipEvent_t* ev, int64_t& ev_i) {
+                         const Budget& bud, hipStream_t s, hipEvent_t* ev, int64_t& ev_i) {
     if (n_tok <= 0) return GPTQ_OK;
     GPTQ_HIP(hipFuncSetAttribute((const void*)hess_tile_kernel<Tag>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                  LDS_B));
-    const int64_t chunk = aligned_chunk(n_tok, d, ld);
+    const int64_t chunk = aligned_chunk(n_tok, d, ld, bud);
     for (int64_t c0 = 0; c0 < n_tok; c0 += chunk) {
         const int64_t nt = (n_tok - c0 < chunk) ? n_tok - c0 : chunk;
-        const Plan p = make_plan(nt, d, window_cap(ld));
+        const Plan p = make_plan(nt, d, window_cap(ld), bud.max_items);
         HessArgs A{H, X + c0 * ld, ld, d, nt, p.win, p.g.RB, p.g.CB, p.g.n_tiles, 0, 0, p.partial ? part : nullptr};
         for (int64_t i0 = 0; i0 < p.n_items; i0 += p.per_launch) {
             A.item0 = i0;
@@ -640,31 +652,18 @@ gptq_status hess_aligned(double* H, const uint16_t* X, int64_t n_tok, int64_t d,
     return GPTQ_OK;
 }
 
-}  // namespace
-
-size_t hessian_workspace_bytes(int64_t n_tok, int64_t d) {
-    if (n_tok <= 0) return 0;
-    // aligned inputs: the partial tiles of the call; misaligned ones: the
-    // aligned copy of one token chunk plus that chunk's partial tiles (the
-    // query does not know the alignment of X, so it covers both)
-    const size_t a = part_bytes(n_tok, d);
-    const int64_t nr = repack_tokens(d) < n_tok ? repack_tokens(d) : n_tok;
-    const size_t b = repack_bytes(n_tok, d) + part_bytes(nr, d);
-    return align_up((a > b ? a : b) + 256, 256);
-}
-
-int64_t hessian_syrk_launches(int64_t n_tok, gptq_dtype dt, int64_t d, int64_t ld_x, const void* X) {
+int64_t launches(int64_t n_tok, gptq_dtype dt, int64_t d, int64_t ld_x, const void* X, const Budget& b) {
     if (n_tok <= 0) return 0;
     if (dt == GPTQ_F32) return 1;
-    if (aligned_input(X, d, ld_x)) return launches_aligned(n_tok, d, ld_x);
-    const int64_t ldd = ceil_div(d, 8) * 8, rt = repack_tokens(d);
+    if (aligned_input(X, d, ld_x)) return launches_aligned(n_tok, d, ld_x, b);
+    const int64_t ldd = ceil_div(d, 8) * 8, rt = repack_tokens(d, b);
     int64_t n = 0;
-    for (int64_t c0 = 0; c0 < n_tok; c0 += rt) n += launches_aligned((n_tok - c0 < rt) ? n_tok - c0 : rt, d, ldd);
+    for (int64_t c0 = 0; c0 < n_tok; c0 += rt) n += launches_aligned((n_tok - c0 < rt) ? n_tok - c0 : rt, d, ldd, b);
     return n;
 }
 
-gptq_status hessian_launch(double* H, const void* X, gptq_dtype dt, int64_t n_tok, int64_t d,
-                           int64_t ld_x, void* ws, hipStream_t s, hipEvent_t* ev) {
+gptq_status launch_with_budget(double* H, const void* X, gptq_dtype dt, int64_t n_tok, int64_t d, int64_t ld_x,
+                               void* ws, const Budget& bud, hipStream_t s, hipEvent_t* ev) {
     if (n_tok == 0) return GPTQ_OK;
     if (dt == GPTQ_F32) {
         const int64_t T = ceil_div(d, FT);
@@ -679,24 +678,67 @@ gptq_status hessian_launch(double* H, const void* X, gptq_dtype dt, int64_t n_to
     int64_t ev_i = 0;
     if (aligned_input(X, d, ld_x)) {
         double* part = (double*)ws;
-        return bf ? hess_aligned<bf16x8_t>(H, (const uint16_t*)X, n_tok, d, ld_x, part, s, ev, ev_i)
-                  : hess_aligned<h16x8_t>(H, (const uint16_t*)X, n_tok, d, ld_x, part, s, ev, ev_i);
+        return bf ? hess_aligned<bf16x8_t>(H, (const uint16_t*)X, n_tok, d, ld_x, part, bud, s, ev, ev_i)
+                  : hess_aligned<h16x8_t>(H, (const uint16_t*)X, n_tok, d, ld_x, part, bud, s, ev, ev_i);
     }
     // misaligned rows: chunks copied into an aligned, zero-padded buffer
-    const int64_t ldd = ceil_div(d, 8) * 8, rt = repack_tokens(d);
+    const int64_t ldd = ceil_div(d, 8) * 8, rt = repack_tokens(d, bud);
     uint16_t* xr = (uint16_t*)ws;
-    double* part = (double*)((char*)ws + repack_bytes(n_tok, d));
+    double* part = (double*)((char*)ws + repack_bytes(n_tok, d, bud));
     for (int64_t c0 = 0; c0 < n_tok; c0 += rt) {
         const int64_t nt = (n_tok - c0 < rt) ? n_tok - c0 : rt;
         const int64_t nblk = ceil_div(nt * ldd, 256);
         hipLaunchKernelGGL(repack_kernel, dim3((unsigned)(nblk < 8192 ? nblk : 8192)), dim3(256), 0, s,
                            (const uint16_t*)X + c0 * ld_x, ld_x, d, nt, xr, ldd);
         GPTQ_LAUNCH_CHECK();
-        gptq_status st = bf ? hess_aligned<bf16x8_t>(H, xr, nt, d, ldd, part, s, ev, ev_i)
-                            : hess_aligned<h16x8_t>(H, xr, nt, d, ldd, part, s, ev, ev_i);
+        gptq_status st = bf ? hess_aligned<bf16x8_t>(H, xr, nt, d, ldd, part, bud, s, ev, ev_i)
+                            : hess_aligned<h16x8_t>(H, xr, nt, d, ldd, part, bud, s, ev, ev_i);
         if (st != GPTQ_OK) return st;
     }
     return GPTQ_OK;
+}
+
+}  // namespace
+
+size_t hessian_workspace_bytes(int64_t n_tok, int64_t d) {
+    if (n_tok <= 0) return 0;
+    // aligned inputs: the partial tiles of the call; misaligned ones: the
+    // aligned copy of one token chunk plus that chunk's partial tiles (the
+    // query does not know the alignment of X, so it covers both)
+    const Budget& b = DEFAULT_BUDGET;
+    const size_t a = part_bytes(n_tok, d, b);
+    const int64_t nr = repack_tokens(d, b) < n_tok ? repack_tokens(d, b) : n_tok;
+    const size_t r = repack_bytes(n_tok, d, b) + part_bytes(nr, d, b);
+    return align_up((a > r ? a : r) + 256, 256);
+}
+
+int64_t hessian_syrk_launches(int64_t n_tok, gptq_dtype dt, int64_t d, int64_t ld_x, const void* X) {
+    return launches(n_tok, dt, d, ld_x, X, DEFAULT_BUDGET);
+}
+
+gptq_status hessian_launch(double* H, const void* X, gptq_dtype dt, int64_t n_tok, int64_t d,
+                           int64_t ld_x, void* ws, hipStream_t s, hipEvent_t* ev) {
+    return launch_with_budget(H, X, dt, n_tok, d, ld_x, ws, DEFAULT_BUDGET, s, ev);
+}
+
+gptq_status hessian_launch_scratch(double* H, const void* X, gptq_dtype dt, int64_t n_tok, int64_t d,
+                                   int64_t ld_x, void* scratch, size_t scratch_bytes, hipStream_t s) {
+    if (n_tok == 0 || dt == GPTQ_F32) return launch_with_budget(H, X, dt, n_tok, d, ld_x, nullptr, DEFAULT_BUDGET, s,
+                                                                nullptr);
+    // split the scratch: an aligned copy of a token chunk (misaligned rows
+    // only; a chunk of at least one 256-token run must fit), then as many
+    // partial tiles as the rest holds
+    Budget b{0, 0};
+    size_t rest = scratch_bytes;
+    if (!aligned_input(X, d, ld_x)) {
+        b.repack = scratch_bytes / 4;
+        const int64_t ldd = ceil_div(d, 8) * 8;
+        if ((size_t)RUN_TOK * ldd * 2 > b.repack) return GPTQ_ERR_WORKSPACE;
+        rest -= repack_bytes(n_tok, d, b);
+    }
+    b.max_items = (int64_t)(rest / (PART_ELEMS * sizeof(double)));
+    if (b.max_items < 1) b.max_items = 1;   // below one window of tiles the pass uses no partial tiles
+    return launch_with_budget(H, X, dt, n_tok, d, ld_x, scratch, b, s, nullptr);
 }
 
 }  // namespace gptq

@@ -57,6 +57,12 @@ size_t hessian_workspace_bytes(int64_t n_tok, int64_t d);
 int64_t hessian_syrk_launches(int64_t n_tok, gptq_dtype dt, int64_t d, int64_t ld_x, const void* X);
 gptq_status hessian_launch(double* H, const void* X, gptq_dtype dt, int64_t n_tok, int64_t d,
                            int64_t ld_x, void* ws, hipStream_t s, hipEvent_t* ev = nullptr);
+// The same product with all scratch memory taken from `scratch` (scratch_bytes
+// bytes): fewer partial tiles (longer windows, or one window of tiles per
+// launch) and shorter copied chunks when they do not fit.  GPTQ_ERR_WORKSPACE
+// if a misaligned input's 256-token chunk does not fit in a quarter of it.
+gptq_status hessian_launch_scratch(double* H, const void* X, gptq_dtype dt, int64_t n_tok, int64_t d,
+                                   int64_t ld_x, void* scratch, size_t scratch_bytes, hipStream_t s);
 
 // Column order, damping, Cholesky of the reversed matrix, triangular inverse,
 // rotation into U.  ws layout described in chol.hip.

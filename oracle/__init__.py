@@ -24,6 +24,7 @@ from .gptq_oracle import (  # noqa: F401
     quantize_column,
     tie_margin,
     sweep,
+    static_group_params,
     gptq_quantize,
     pack,
     unpack,

@@ -46,6 +46,14 @@ design notes of the repository):
   quantization is one group per row, taken at column 0.
 * act-order: perm = stable argsort of -diag(H) (undamped H); groups are g
   consecutive columns in sweep order; g_idx[perm[k]] = k // g.
+* Static groups (an option; the field table's desc_act row notes that the
+  order choice can change compatibility and execution cost, and
+  "GPTQ量化算法深度解析" §3.3 says act-order costs a gather at inference):
+  groups are g consecutive columns in the ORIGINAL order, g_idx[j] = j // g,
+  and every group's (scale, zero) is taken before the sweep from the
+  weights as given (nothing compensated yet); act-order then only decides
+  the order of the sweep, and each column is quantized with the parameters
+  of its original-order group.
 * Outputs are returned in the original column order.
 * Packing: each output row is a little-endian bit stream along d_in; code k
   occupies bits [b*k, b*k + b) of that stream, held in 32-bit words.
@@ -220,8 +228,24 @@ def _check_block_group(d_in: int, group_size: int, block: int) -> int:
     return group_size
 
 
+def static_group_params(W: np.ndarray, bits: int, group_size: int, sym: bool):
+    """(scales, zeros), each [n_groups][d_out], of the static-groups option:
+    group G holds original columns G*g .. min((G+1)*g, d_in) - 1 and takes
+    its parameters from W as given, before the sweep (reading stated in the
+    module docstring; the grid itself is quant_params')."""
+    W = np.asarray(W, dtype=np.float64)
+    d_out, d_in = W.shape
+    g = d_in if group_size <= 0 else group_size
+    n_groups = -(-d_in // g)
+    scales = np.zeros((n_groups, d_out))
+    zeros = np.zeros((n_groups, d_out))
+    for G in range(n_groups):
+        scales[G], zeros[G] = quant_params(W[:, G * g:min((G + 1) * g, d_in)], bits, sym)
+    return scales, zeros
+
+
 def sweep(W: np.ndarray, U: np.ndarray, bits: int, group_size: int, sym: bool,
-          block: int = 128, force=None, margins: bool = False):
+          block: int = 128, force=None, margins: bool = False, static=None):
     """Quantize the columns of W (already in sweep order) left to right.
 
     "GPTQ量化算法深度解析" §2.4 (fixed order; lazy batch update: errors are
@@ -242,6 +266,11 @@ def sweep(W: np.ndarray, U: np.ndarray, bits: int, group_size: int, sym: bool,
     given codes at column c instead of their rounded value, and the sweep
     continues from the resulting quantized value, which replays another
     implementation's decision at a rounding tie.
+
+    ``static = (scales, zeros, col_group)`` selects the static-groups option:
+    sweep column c is quantized with scales[col_group[c]], zeros[col_group[c]]
+    (fixed before the sweep, see static_group_params) and no parameters are
+    taken during the sweep; the returned scales / zeros are the given ones.
     """
     if bits not in (2, 3, 4, 8):
         raise InvalidArgument("bits must be 2, 3, 4 or 8")
@@ -256,6 +285,10 @@ def sweep(W: np.ndarray, U: np.ndarray, bits: int, group_size: int, sym: bool,
     row_loss = np.zeros(d_out, dtype=np.float64)
     margin = np.zeros((d_out, d_in), dtype=np.float64) if margins else None
     scale = zero = None
+    if static is not None:
+        st_scales, st_zeros, col_group = static
+        scales = np.array(st_scales, dtype=np.float64, copy=True)
+        zeros = np.array(st_zeros, dtype=np.float64, copy=True)
 
     for i1 in range(0, d_in, block):
         i2 = min(i1 + block, d_in)
@@ -263,7 +296,9 @@ def sweep(W: np.ndarray, U: np.ndarray, bits: int, group_size: int, sym: bool,
         Err = np.zeros((d_out, i2 - i1))     # accumulated scaled errors
         for c in range(i1, i2):
             k = c - i1
-            if c % g == 0:
+            if static is not None:
+                scale, zero = scales[col_group[c]], zeros[col_group[c]]
+            elif c % g == 0:
                 # The group's current values: the part inside this block sits
                 # in W1 (already compensated by earlier columns of the block);
                 # the part past the block sits in W, which holds every earlier
@@ -304,7 +339,7 @@ def sweep(W: np.ndarray, U: np.ndarray, bits: int, group_size: int, sym: bool,
 # ---------------------------------------------------------------------------
 
 def gptq_quantize(W, H=None, *, X=None, bits=4, group_size=128, sym=False,
-                  act_order=False, block=128, damp=0.01):
+                  act_order=False, block=128, damp=0.01, static_groups=False):
     """Quantize one linear layer; returns a dict of outputs in original order.
 
     "GPTQ量化算法深度解析" §3.1 (the four steps per layer) with §3.3's
@@ -314,7 +349,8 @@ def gptq_quantize(W, H=None, *, X=None, bits=4, group_size=128, sym=False,
     g_idx (d_in), perm (d_in, perm[k] = original column swept k-th), w_hat
     (d_out x d_in), row_loss (sum_c (w_c-q_c)^2 / (2 U_cc^2) per row),
     loss (||(W - W_hat) X^T||_F^2 = 1/2 tr(dW H dW^T) with the undamped H),
-    U (sweep order), H (undamped, original order).
+    U (sweep order), H (undamped, original order).  ``static_groups``: the
+    static-groups option (module docstring): g_idx[j] = j // g.
     """
     W0 = np.asarray(W, dtype=np.float64)
     if W0.ndim != 2:
@@ -340,15 +376,22 @@ def gptq_quantize(W, H=None, *, X=None, bits=4, group_size=128, sym=False,
     Hp = H[np.ix_(perm, perm)]
 
     U = inverse_hessian_upper(damp_hessian(Hp, damp))
-    codes_s, scales, zeros, w_hat_s, row_loss = sweep(Wp, U, bits, group_size, sym, block)
-
     g = d_in if group_size <= 0 else group_size
+    static = None
+    if static_groups:
+        st_scales, st_zeros = static_group_params(W0, bits, group_size, sym)
+        static = (st_scales, st_zeros, perm // g)
+    codes_s, scales, zeros, w_hat_s, row_loss = sweep(Wp, U, bits, group_size, sym, block, static=static)
+
     codes = np.empty_like(codes_s)
     w_hat = np.empty_like(w_hat_s)
     codes[:, perm] = codes_s
     w_hat[:, perm] = w_hat_s
     g_idx = np.empty(d_in, dtype=np.int64)
-    g_idx[perm] = np.arange(d_in) // g
+    if static_groups:
+        g_idx[:] = np.arange(d_in) // g
+    else:
+        g_idx[perm] = np.arange(d_in) // g
     return dict(codes=codes, scales=scales, zeros=zeros, g_idx=g_idx, perm=perm,
                 w_hat=w_hat, row_loss=row_loss, loss=layer_loss(W0, w_hat, H),
                 U=U, H=H)

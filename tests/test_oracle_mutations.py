@@ -51,6 +51,13 @@ MUTATIONS = [
      "out[:, wi] |= (c[:, k] << np.uint64(32 - bits - sh if sh + bits <= 32 else sh)) & np.uint64(0xFFFFFFFF)"),
     ("loss from the damped Hessian", "loss=layer_loss(W0, w_hat, H)",
      "loss=layer_loss(W0, w_hat, damp_hessian(H, damp))"),
+    ("static groups looked up by sweep position", "static = (st_scales, st_zeros, perm // g)",
+     "static = (st_scales, st_zeros, np.arange(d_in) // g)"),
+    ("static group parameters from the permuted weights", "static_group_params(W0, bits, group_size, sym)",
+     "static_group_params(Wp, bits, group_size, sym)"),
+    ("static g_idx in sweep order", "        g_idx[:] = np.arange(d_in) // g\n    else:",
+     "        g_idx[perm] = np.arange(d_in) // g\n    else:"),
+    ("static group parameters retaken during the sweep", "elif c % g == 0:", "if c % g == 0:"),
 ]
 
 

@@ -654,3 +654,121 @@ def test_tie_replay_explains_a_planted_tie_and_rejects_a_non_tie():
     bad[rb, cb] += 1
     rp = tie_replay(O, W, U, bad, 3, 32, block=32)
     assert rp["other"] and rp["other"][0][:2] == (rb, cb)
+
+
+# ---------------------------------------------------------------------------
+# Static groups: groups of g consecutive ORIGINAL columns, parameters from the
+# untouched weights before the sweep, act-order only ordering the sweep.
+# ---------------------------------------------------------------------------
+
+def test_static_groups_hand_examples():
+    g = _load("static_groups_hand.json")
+    a = g["case_a"]
+    out = O.gptq_quantize(np.array(a["W"]), np.diag(a["H_diag"]), bits=a["bits"], group_size=a["group_size"],
+                          sym=a["sym"], act_order=a["act_order"], block=a["block"], damp=a["damp"],
+                          static_groups=True)
+    np.testing.assert_array_equal(out["perm"], a["perm"])
+    np.testing.assert_array_equal(out["codes"], a["codes"])
+    np.testing.assert_allclose(out["w_hat"], a["w_hat"], rtol=1e-15, atol=1e-16)
+    np.testing.assert_allclose(out["scales"], a["scales"], rtol=1e-15)
+    np.testing.assert_array_equal(out["zeros"], a["zeros"])
+    np.testing.assert_array_equal(out["g_idx"], a["g_idx"])
+    np.testing.assert_allclose(out["row_loss"], a["row_loss"], rtol=1e-13)
+    np.testing.assert_allclose(out["loss"], a["loss"], rtol=1e-13)
+    # the default grouping of the same problem differs (sweep-order groups)
+    dyn = O.gptq_quantize(np.array(a["W"]), np.diag(a["H_diag"]), bits=2, group_size=2, act_order=True)
+    assert not np.array_equal(dyn["codes"], out["codes"])
+
+    b = g["case_b"]
+    W = np.array(b["W"])
+    s, z = O.static_group_params(W, b["bits"], b["group_size"], b["sym"])
+    np.testing.assert_allclose(s, b["scales"], rtol=1e-15)
+    np.testing.assert_array_equal(z, b["zeros"])
+    codes, scales, zeros, w_hat, row_loss = O.sweep(W, np.array(b["U"]), b["bits"], b["group_size"], b["sym"],
+                                                    b["block"], static=(s, z, np.array(b["col_group"])))
+    np.testing.assert_array_equal(codes, b["codes"])
+    np.testing.assert_allclose(w_hat, b["w_hat"], rtol=1e-15)
+    np.testing.assert_allclose(row_loss, b["row_loss"], rtol=1e-13)
+    np.testing.assert_allclose(scales, b["scales"], rtol=1e-15)
+
+
+@pytest.mark.parametrize("bits,g,sym", [(4, 16, False), (3, 8, True), (2, 12, False)])
+def test_static_groups_diagonal_hessian_is_rtn_in_original_order(bits, g, sym):
+    """With nothing to compensate, static groups are plain round-to-nearest
+    over consecutive original columns, whatever order the sweep takes."""
+    rng = np.random.default_rng(30 + bits)
+    W = rng.standard_normal((7, 48))
+    dg = rng.permutation(np.arange(1, 49)).astype(float)
+    out = O.gptq_quantize(W, np.diag(dg), bits=bits, group_size=g, sym=sym, act_order=True, block=16,
+                          static_groups=True)
+    np.testing.assert_array_equal(out["codes"], _rtn_in_test(W, bits, g, sym))
+    np.testing.assert_array_equal(out["g_idx"], np.arange(48) // g)
+    assert not np.array_equal(out["perm"], np.arange(48))
+
+
+def _grid_in_test(blk, bits, sym):
+    maxq = 2 ** bits - 1
+    lo = np.minimum(blk.min(1), 0)
+    hi = np.maximum(blk.max(1), 0)
+    if sym:
+        a = np.maximum(-lo, hi)
+        a[a == 0] = 1
+        return 2 * a / maxq, np.full(len(blk), 2.0 ** (bits - 1))
+    both0 = (lo == 0) & (hi == 0)
+    lo[both0], hi[both0] = -1, 1
+    scale = (hi - lo) / maxq
+    return scale, np.rint(-lo / scale)
+
+
+def _obs_bruteforce_fixed_grid(W, Hd, bits, col_params):
+    """Fixed-order OBS with explicit inverses, column q quantized on the given grid."""
+    W = W.astype(float).copy()
+    d_out, d = W.shape
+    maxq = 2 ** bits - 1
+    codes = np.zeros((d_out, d), dtype=np.int64)
+    qv = np.zeros((d_out, d))
+    for q in range(d):
+        scale, zero = col_params[q]
+        c = np.clip(np.rint(W[:, q] / scale) + zero, 0, maxq)
+        val = scale * (c - zero)
+        codes[:, q], qv[:, q] = c, val
+        F = list(range(q, d))
+        Hinv = np.linalg.inv(Hd[np.ix_(F, F)])
+        W[:, F] -= np.outer((W[:, q] - val) / Hinv[0, 0], Hinv[:, 0])
+        W[:, q] = val
+    return codes, qv
+
+
+@pytest.mark.parametrize("seed", range(4))
+@pytest.mark.parametrize("g", [2, 3])
+def test_static_groups_match_bruteforce_obs(seed, g):
+    rng = np.random.default_rng(200 + seed)
+    d = 4 + seed
+    W = rng.standard_normal((5, d))
+    H = _rand_pd(rng, d, 0.8)
+    for act in (False, True):
+        out = O.gptq_quantize(W, H, bits=2, group_size=g, act_order=act, block=2, damp=0.01, static_groups=True)
+        perm = out["perm"]
+        Hd = O.damp_hessian(H[np.ix_(perm, perm)], 0.01)
+        grids = [_grid_in_test(W[:, s:s + g], 2, False) for s in range(0, d, g)]
+        col_params = [grids[perm[k] // g] for k in range(d)]
+        c_bf, q_bf = _obs_bruteforce_fixed_grid(W[:, perm], Hd, 2, col_params)
+        np.testing.assert_array_equal(out["codes"][:, perm], c_bf)
+        np.testing.assert_allclose(out["w_hat"][:, perm], q_bf, rtol=1e-12, atol=1e-12)
+        np.testing.assert_array_equal(out["g_idx"], np.arange(d) // g)
+
+
+def test_static_groups_per_row_and_block_invariance():
+    """Per-row grouping takes its one group from the untouched row either
+    way; and lazy batching still changes nothing."""
+    rng = np.random.default_rng(31)
+    X = rng.standard_normal((300, 40)) @ (rng.standard_normal((40, 40)) / 6)
+    W = 0.05 * rng.standard_normal((6, 40))
+    for act in (False, True):
+        a = O.gptq_quantize(W, X=X, bits=3, group_size=-1, act_order=act, static_groups=True)
+        b = O.gptq_quantize(W, X=X, bits=3, group_size=-1, act_order=act)
+        np.testing.assert_array_equal(a["codes"], b["codes"])
+        ref = O.gptq_quantize(W, X=X, bits=3, group_size=8, act_order=act, block=1, static_groups=True)
+        for B in (3, 8, 13, 40):
+            out = O.gptq_quantize(W, X=X, bits=3, group_size=8, act_order=act, block=B, static_groups=True)
+            np.testing.assert_array_equal(out["codes"], ref["codes"])

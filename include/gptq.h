@@ -70,10 +70,22 @@ typedef struct {
                             divide one another (a group that begins inside a block
                             and runs past its end sees its later columns with the
                             block's pending compensation applied) */
+    int32_t static_groups; /* 0: groups of group_size consecutive SWEEP-order columns,
+                            each group's (scale, zero) taken when the sweep reaches
+                            its first column from the compensated values; 1: groups
+                            of group_size consecutive ORIGINAL columns (g_idx[j] =
+                            j / group_size, no gather at inference), every group's
+                            (scale, zero) taken before the sweep from W as given;
+                            act_order then only orders the sweep.  The option the
+                            desc_act row of the ai.lansai.wang field table points
+                            at (order vs. compatibility and execution cost; act-
+                            order's inference gather: "GPTQ量化算法深度解析" §3.3).
+                            Same as 0 when group_size <= 0 */
     double  damp;        /* lambda = damp * mean(diag H) is added to diag H (0.01) */
 } gptq_config;
 
-/* Fills *cfg with bits 4, group 128, asymmetric, natural order, block 128, damp 0.01. */
+/* Fills *cfg with bits 4, group 128, asymmetric, natural order, block 128,
+ * dynamic groups, damp 0.01. */
 void gptq_config_default(gptq_config* cfg);
 
 /* ------------------------------------------------------------------------
@@ -183,7 +195,8 @@ gptq_status gptq_prepare_hinv(double* H, int64_t d_in, const gptq_config* cfg,
  *   codes   d_out x d_in uint8 (row stride d_in);
  *   scales, zeros   n_groups x d_out float32, [group][row], n_groups =
  *                   ceil(d_in/group_size) (1 when group_size <= 0);
- *   g_idx   d_in int32, the group of each original column (sweep position / g);
+ *   g_idx   d_in int32, the group of each original column (sweep position / g;
+ *           with static_groups, original column / g);
  *   w_hat   (nullable) d_out x d_in float32, scale*(code - zero);
  *   row_loss (nullable) d_out float64, sum_c (w_c - q_c)^2 / (2 U_cc^2).
  * Synchronous at the end: returns GPTQ_ERR_INVALID_ARG if perm is not a

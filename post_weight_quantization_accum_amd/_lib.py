@@ -62,11 +62,14 @@ _EXC = {ERR_INVALID_ARG: InvalidArgument, ERR_NOT_PD: NotPositiveDefinite, ERR_N
 class Config(ctypes.Structure):
     """gptq_config."""
     _fields_ = [("bits", ctypes.c_int32), ("group_size", ctypes.c_int32), ("sym", ctypes.c_int32),
-                ("act_order", ctypes.c_int32), ("block_size", ctypes.c_int32), ("damp", ctypes.c_double)]
+                ("act_order", ctypes.c_int32), ("block_size", ctypes.c_int32), ("static_groups", ctypes.c_int32),
+                ("damp", ctypes.c_double)]
 
 
-def make_config(bits=4, group_size=128, sym=False, act_order=False, block=128, damp=0.01) -> Config:
-    return Config(int(bits), int(group_size), int(bool(sym)), int(bool(act_order)), int(block), float(damp))
+def make_config(bits=4, group_size=128, sym=False, act_order=False, block=128, damp=0.01,
+                static_groups=False) -> Config:
+    return Config(int(bits), int(group_size), int(bool(sym)), int(bool(act_order)), int(block),
+                  int(bool(static_groups)), float(damp))
 
 
 _lib = None

@@ -1,10 +1,30 @@
 // The C ABI of libgptq_mi355x: argument validation, workspace sizing and
 // dispatch to the kernels.  Declarations and contracts are in include/gptq.h.
+#include <mutex>
+#include <tuple>
 #include <vector>
 
 #include "internal.hpp"
 
 using namespace gptq;
+
+namespace gptq {
+
+hipError_t ensure_lds_limit(const void* kernel, int bytes) {
+    static std::mutex mu;
+    static std::vector<std::tuple<int, const void*, int>> done;   // (device, kernel, bytes) already set
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lk(mu);
+    for (const auto& t : done)
+        if (std::get<0>(t) == dev && std::get<1>(t) == kernel && std::get<2>(t) >= bytes) return hipSuccess;
+    e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess) done.emplace_back(dev, kernel, bytes);
+    return e;
+}
+
+}  // namespace gptq
 
 namespace {
 
@@ -19,6 +39,7 @@ gptq_status check_config(const gptq_config* cfg) {
     if (!valid_bits(cfg->bits)) return GPTQ_ERR_INVALID_ARG;
     if (cfg->block_size < 1) return GPTQ_ERR_INVALID_ARG;
     if (cfg->block_size > 128) return GPTQ_ERR_UNSUPPORTED;
+    if (cfg->static_groups != 0 && cfg->static_groups != 1) return GPTQ_ERR_INVALID_ARG;
     if (!(cfg->damp >= 0.0) || !(cfg->damp < 1e300)) return GPTQ_ERR_INVALID_ARG;
     return GPTQ_OK;
 }
@@ -34,6 +55,7 @@ void gptq_config_default(gptq_config* cfg) {
     cfg->sym = 0;
     cfg->act_order = 0;
     cfg->block_size = 128;
+    cfg->static_groups = 0;
     cfg->damp = 0.01;
 }
 

@@ -566,7 +566,9 @@ struct Rec {
     int64_t d = 0;
     int* flags = nullptr;
     hipEvent_t l21_ready[MAX_DEPTH] = {}, t_done[MAX_DEPTH] = {};
+    // created on first use: factors of at most 1024 columns never need them
     hipError_t init() {
+        if (side) return hipSuccess;
         hipError_t e = hipStreamCreateWithFlags(&side, hipStreamNonBlocking);
         for (int k = 0; k < MAX_DEPTH && e == hipSuccess; ++k) {
             e = hipEventCreateWithFlags(&l21_ready[k], hipEventDisableTiming);
@@ -586,7 +588,7 @@ struct Rec {
     }
 };
 
-gptq_status chol_inv(const Rec& c, int64_t o, int64_t n, int depth) {
+gptq_status chol_inv(Rec& c, int64_t o, int64_t n, int depth) {
     const int64_t d = c.d;
     if (n <= LEAF) {
         hipLaunchKernelGGL(leaf_blocked_kernel, dim3(1), dim3(512), LEAF_LDS, c.s, c.L, c.M, d, o, (int)n, c.flags);
@@ -622,6 +624,7 @@ gptq_status chol_inv(const Rec& c, int64_t o, int64_t n, int depth) {
     st = launch_gemm_f64(c.s, n2, n2, n1, -1.0, L21, n1, L21, n1, true, 1.0, A22, d, true);
     if (st != GPTQ_OK) return st;
     // T = L21 M11 (into A21's place), on the side stream
+    GPTQ_HIP(c.init());
     GPTQ_HIP(hipEventRecord(c.l21_ready[depth], c.s));
     GPTQ_HIP(hipStreamWaitEvent(c.side, c.l21_ready[depth], 0));
     st = launch_gemm_f64(c.side, n2, n1, n1, 1.0, L21, n1, M11, d, false, 0.0, A21, d, false, GEMM_TRI_KBEG_COL);
@@ -642,8 +645,7 @@ gptq_status hinv_launch(double* H, int64_t d, const gptq_config* cfg, int32_t* p
                         hipStream_t s, int* host_flags) {
     Ws w;
     layout(d, &w, (char*)ws);
-    GPTQ_HIP(hipFuncSetAttribute((const void*)leaf_blocked_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                 (int)LEAF_LDS));
+    GPTQ_HIP(ensure_lds_limit((const void*)leaf_blocked_kernel, (int)LEAF_LDS));
     GPTQ_HIP(hipMemsetAsync(w.flags, 0, 256, s));
 
     hipLaunchKernelGGL(diag_stats_kernel, dim3(1), dim3(1024), 0, s, H, d, cfg->damp, w.lambda, w.diag, w.flags);
@@ -658,8 +660,7 @@ gptq_status hinv_launch(double* H, int64_t d, const gptq_config* cfg, int32_t* p
     GPTQ_LAUNCH_CHECK();
     if (d <= GATHER_LDS_MAX) {
         const size_t lds = (size_t)d * sizeof(double);
-        GPTQ_HIP(hipFuncSetAttribute((const void*)gather_rows_lds_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     (int)lds));
+        GPTQ_HIP(ensure_lds_limit((const void*)gather_rows_lds_kernel, (int)lds));
         hipLaunchKernelGGL(gather_rows_lds_kernel, dim3((unsigned)d), dim3(512), lds, s, H, d, perm, w.lambda, w.L);
     } else {
         hipLaunchKernelGGL(gather_reverse_kernel, dim3((unsigned)d), dim3(256), 0, s, H, d, perm, w.pinv, w.lambda,
@@ -669,7 +670,6 @@ gptq_status hinv_launch(double* H, int64_t d, const gptq_config* cfg, int32_t* p
 
     // H's buffer now receives M = L^{-1} (lower), then U = J M J in place.
     Rec c;
-    GPTQ_HIP(c.init());
     c.s = s;
     c.L = w.L;
     c.M = H;

@@ -415,10 +415,7 @@ template <int BITS, typename T>
 gptq_status launch_col(const DqArgs& a, hipStream_t s) {
     const size_t lds = (size_t)a.n_groups * RW * 2 * sizeof(float);
     if (lds > 48 * 1024) {
-        static const hipError_t attr = hipFuncSetAttribute(
-            (const void*)dequant_col_kernel<BITS, T>, hipFuncAttributeMaxDynamicSharedMemorySize,
-            (int)(DQ_MAX_GROUPS * RW * 2 * sizeof(float)));
-        if (attr != hipSuccess) return GPTQ_ERR_HIP;
+        GPTQ_HIP(ensure_lds_limit((const void*)dequant_col_kernel<BITS, T>, (int)(DQ_MAX_GROUPS * RW * 2 * sizeof(float))));
     }
     const dim3 grid((unsigned)ceil_div(a.d_out, RW), (unsigned)a.n_tok);
     hipLaunchKernelGGL((dequant_col_kernel<BITS, T>), grid, dim3(DQ_THREADS), lds, s, a);
@@ -1055,10 +1052,7 @@ gptq_status launch_block(const DqArgs& a, hipStream_t s) {
     const dim3 grid((unsigned)ceil_div(a.d_out, RW), (unsigned)ceil_div(a.n_tok, TM));
     const StagedLayout Ly = staged_layout(a.n_groups, ceil_div(a.d_in, 32), a.d_in, TM, a.perm != nullptr);
     if (Ly.total <= STAGED_LDS_MAX) {
-        static const hipError_t attr = hipFuncSetAttribute((const void*)dequant_staged_kernel<BITS, TM, T>,
-                                                           hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                           (int)STAGED_LDS_MAX);
-        if (attr != hipSuccess) return GPTQ_ERR_HIP;
+        GPTQ_HIP(ensure_lds_limit((const void*)dequant_staged_kernel<BITS, TM, T>, (int)STAGED_LDS_MAX));
         const dim3 grid_s((unsigned)ceil_div(a.d_out, ST_ROWS), (unsigned)ceil_div(a.n_tok, TM));
         hipLaunchKernelGGL((dequant_staged_kernel<BITS, TM, T>), grid_s, dim3(ST_THREADS), Ly.total, s, a);
     } else {

@@ -69,15 +69,21 @@ constexpr int STAGE_B = KT * (ROW_B + COL_B);  // 48 KiB
 constexpr int RING_B = NSTAGE * STAGE_B;       // 96 KiB
 constexpr int SQ_B = 4 * TR * 8;               // float64 sums of squares (4 token groups x 256 features)
 constexpr int LDS_B = RING_B + SQ_B;
-constexpr int RUN_TOK = 256;                   // tokens per float32 run
-constexpr int FOLD = RUN_TOK / KT;             // stages per float32 run
+#ifndef GPTQ_HFOLD
+#define GPTQ_HFOLD (256 / GPTQ_HKT)
+#endif
+constexpr int FOLD = GPTQ_HFOLD;               // stages per float32 run
+constexpr int RUN_TOK = FOLD * KT;             // tokens per float32 run
 constexpr int DMA_PER_STAGE = WROWS / 2 + WROWS / 4;   // buffer_load ... lds per wave per stage
 static_assert(KT == 32 || KT == 64, "stage of 32 or 64 tokens");
 static_assert(LDS_B <= 160 * 1024, "LDS of one CU");
 // the ring slot of a stage is a compile-time constant in the unrolled run
 constexpr bool SLOT_STATIC = FOLD % NSTAGE == 0;
 constexpr int BAND = 4;                        // row blocks per band of the tile enumeration
-constexpr int64_t WIN_MAX = 32768;             // tokens per window (full mode)
+#ifndef GPTQ_HWIN
+#define GPTQ_HWIN 32768
+#endif
+constexpr int64_t WIN_MAX = GPTQ_HWIN / RUN_TOK * RUN_TOK;   // tokens per window (full mode)
 constexpr int64_t PART_TILES = 256;            // fewer tiles: partial-tile mode
 constexpr size_t PART_ELEMS = (size_t)TR * TC + TR;   // one partial tile + its diagonal sums
 constexpr size_t REPACK_BYTES = (size_t)64 << 20;     // aligned copy of a misaligned input
@@ -627,8 +633,7 @@ template <typename Tag>
 gptq_status hess_aligned(double* H, const uint16_t* X, int64_t n_tok, int64_t d, int64_t ld, double* part,
                          const Budget& bud, hipStream_t s, hipEvent_t* ev, int64_t& ev_i) {
     if (n_tok <= 0) return GPTQ_OK;
-    GPTQ_HIP(hipFuncSetAttribute((const void*)hess_tile_kernel<Tag>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                 LDS_B));
+    GPTQ_HIP(ensure_lds_limit((const void*)hess_tile_kernel<Tag>, (int)LDS_B));
     const int64_t chunk = aligned_chunk(n_tok, d, ld, bud);
     for (int64_t c0 = 0; c0 < n_tok; c0 += chunk) {
         const int64_t nt = (n_tok - c0 < chunk) ? n_tok - c0 : chunk;

@@ -5,6 +5,11 @@
 
 namespace gptq {
 
+// Raises a kernel's dynamic LDS limit to at least `bytes` on the current
+// device, calling the runtime only the first time for that (device, kernel,
+// size): the attribute persists, and the call costs a runtime lookup.
+hipError_t ensure_lds_limit(const void* kernel, int bytes);
+
 // Triangular structure of one operand, used to skip the zero part of K
 // (the operand's zero entries inside the tile's range must be stored zeros):
 //   KEND_ROW: A is lower triangular (A[m][k] = 0 for k > m): K ends at the tile's last row;

@@ -30,6 +30,12 @@
 // superblock of S = 1024 columns (K = B); after each superblock, one GEMM
 // with K = S updates the next superblock, and another (on a second stream,
 // overlapping the next superblock's sweep) everything after it.
+//
+// Static groups: every group's (scale, zero) comes first, from W as given,
+// per group of consecutive original columns (one wave per row and group);
+// the sweep kernel then holds, per lane, the parameters of the columns it
+// owns (loaded once per block through the group of each sweep column) and
+// takes none during the sweep.
 #include <utility>
 
 #include "internal.hpp"
@@ -69,6 +75,7 @@ struct SweepWs {
     double* zero64;
     double* loss64;
     int32_t* pinv;
+    int32_t* gsw;   // group of each sweep column (static groups)
 };
 
 int64_t n_groups_of(int64_t d_in, int32_t g) { return g > 0 ? ceil_div(d_in, g) : 1; }
@@ -85,7 +92,7 @@ int64_t superblock_cols(int64_t d_in, const gptq_config* cfg) {
 #endif
     const int64_t S = B * (GPTQ_SUPER / B > 0 ? GPTQ_SUPER / B : 1);
     const int64_t g = cfg->group_size > 0 ? cfg->group_size : d_in;
-    if (cfg->group_size <= 0 || S % g == 0 || g % S == 0) return S;
+    if (cfg->group_size <= 0 || cfg->static_groups || S % g == 0 || g % S == 0) return S;
     // otherwise the largest multiple of lcm(B, g) up to GPTQ_SUPER, so that
     // no group crosses a superblock end (a group crossing a block end reads
     // columns of its own superblock, which the in-superblock updates keep
@@ -121,6 +128,8 @@ SweepWs carve(void* ws, int64_t d_out, int64_t d_in, const gptq_config* cfg) {
     w.loss64 = (double*)(p + off);
     off = align_up(off + (size_t)d_out * 8, 256);
     w.pinv = (int32_t*)(p + off);
+    off = align_up(off + (size_t)d_in * 4, 256);
+    w.gsw = (int32_t*)(p + off);
     return w;
 }
 
@@ -133,6 +142,7 @@ size_t carve_size(int64_t d_out, int64_t d_in, const gptq_config* cfg) {
     off = align_up(off + (size_t)ng * d_out * 8, 256);
     off = align_up(off + (size_t)ng * d_out * 8, 256);
     off = align_up(off + (size_t)d_out * 8, 256);
+    off = align_up(off + (size_t)d_in * 4, 256);
     off = align_up(off + (size_t)d_in * 4, 256);
     return off;
 }
@@ -203,16 +213,23 @@ __global__ void fill_neg_kernel(int32_t* p, int64_t n) {
     if (k < n) p[k] = -1;
 }
 
-// pinv[perm[k]] = k, g_idx[perm[k]] = k / g; out-of-range entries are skipped
-// (convert_kernel flags them), duplicates leave a -1 that finalize flags.
-__global__ void pinv_kernel(const int32_t* __restrict__ perm, int64_t d_in, int64_t g, int32_t* pinv,
-                            int32_t* g_idx) {
+// pinv[perm[k]] = k; g_idx[perm[k]] = k / g, or with static groups
+// g_idx[j] = j / g and gsw[k] = perm[k] / g (the group of sweep column k).
+// Out-of-range entries are skipped (convert_kernel flags them; gsw then
+// names group 0), duplicates leave a -1 that finalize flags.
+__global__ void pinv_kernel(const int32_t* __restrict__ perm, int64_t d_in, int64_t g, bool stat, int32_t* pinv,
+                            int32_t* g_idx, int32_t* gsw) {
     const int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (k >= d_in) return;
     const int32_t j = perm[k];
-    if (j < 0 || j >= d_in) return;
+    const bool ok = j >= 0 && j < d_in;
+    if (stat) {
+        gsw[k] = ok ? (int32_t)(j / g) : 0;
+        g_idx[k] = (int32_t)(k / g);
+    }
+    if (!ok) return;
     pinv[j] = (int32_t)k;
-    g_idx[j] = (int32_t)(k / g);
+    if (!stat) g_idx[j] = (int32_t)(k / g);
 }
 
 struct QParams {
@@ -221,12 +238,66 @@ struct QParams {
     double maxq;
 };
 
-// A non-blocking stream at the default priority plus two events, released
-// when the call returns.
+// (scale, zero) of a group whose values span [xmin, xmax] (0 included).
+__device__ __forceinline__ void grid_params(double xmin, double xmax, const QParams& qp, double& scale,
+                                            double& zero) {
+    if (qp.sym) {
+        double amax = fmax(-xmin, xmax);
+        if (amax == 0.0) amax = 1.0;
+        scale = 2.0 * amax / qp.maxq;
+        zero = (double)(1 << (qp.bits - 1));
+    } else {
+        if (xmin == 0.0 && xmax == 0.0) {
+            xmin = -1.0;
+            xmax = 1.0;
+        }
+        scale = (xmax - xmin) / qp.maxq;
+        zero = rint(-xmin / scale);
+    }
+}
+
+// Static groups: (scale, zero) of row r and original-order group G (columns
+// G*g .. min((G+1)*g, d_in) - 1) from W as given; one wave per (r, G), the
+// groups of one row on consecutive waves.
+__global__ __launch_bounds__(256) void static_params_kernel(const void* __restrict__ W, gptq_dtype dt,
+                                                            int64_t d_out, int64_t d_in, int64_t ld_w, int64_t g,
+                                                            int64_t ng, QParams qp, double* __restrict__ scale64,
+                                                            double* __restrict__ zero64, float* __restrict__ scales,
+                                                            float* __restrict__ zeros) {
+    const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (wid >= d_out * ng) return;   // whole waves
+    const int64_t r = wid / ng, G = wid % ng;
+    const int64_t c0 = G * g, c1 = (c0 + g < d_in) ? c0 + g : d_in;
+    double xmin = 0.0, xmax = 0.0;
+    for (int64_t c = c0 + lane; c < c1; c += 64) {
+        const double v = load_as_f64(W, r * ld_w + c, dt);
+        xmin = fmin(xmin, v);
+        xmax = fmax(xmax, v);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        xmin = fmin(xmin, __shfl_xor(xmin, o));
+        xmax = fmax(xmax, __shfl_xor(xmax, o));
+    }
+    if (lane == 0) {
+        double scale, zero;
+        grid_params(xmin, xmax, qp, scale, zero);
+        scale64[G * d_out + r] = scale;
+        zero64[G * d_out + r] = zero;
+        scales[G * d_out + r] = (float)scale;
+        zeros[G * d_out + r] = (float)zero;
+    }
+}
+
+// A non-blocking stream at the default priority plus two events, created
+// on first use (layers of at most two superblocks never need them) and
+// released when the call returns.
 struct SideStream {
     hipStream_t s = nullptr;
     hipEvent_t err_ready = nullptr, far_done = nullptr;
     hipError_t init() {
+        if (s) return hipSuccess;
         hipError_t e = hipStreamCreateWithFlags(&s, hipStreamNonBlocking);
         if (e == hipSuccess) e = hipEventCreateWithFlags(&err_ready, hipEventDisableTiming);
         if (e == hipSuccess) e = hipEventCreateWithFlags(&far_done, hipEventDisableTiming);
@@ -290,14 +361,14 @@ __device__ __forceinline__ double row_max16(double x) {
     return fmax(x, dpp_f64<DPP_MIRROR>(x));
 }
 
-template <int SEG, bool FULL>
+template <int SEG, bool FULL, bool STATIC>
 __global__ __launch_bounds__(SWAVES * 64) void sweep_block_kernel(double* __restrict__ Wwork, int64_t d_out, int64_t d_in,
                                                          int64_t i1, int nb, const double* __restrict__ U,
                                                          int64_t g, QParams qp, double* __restrict__ Err,
                                                          int ldE, int errc, uint8_t* __restrict__ codes_s,
                                                          double* __restrict__ scale64, double* __restrict__ zero64,
                                                          float* __restrict__ scales, float* __restrict__ zeros,
-                                                         double* __restrict__ loss64) {
+                                                         double* __restrict__ loss64, const int32_t* __restrict__ gsw) {
     extern __shared__ __attribute__((aligned(16))) double sweep_lds[];
     // the sweep is the serial chain of the layer: its waves take issue
     // priority over GEMM waves of the other stream on the same SIMD
@@ -328,6 +399,22 @@ __global__ __launch_bounds__(SWAVES * 64) void sweep_block_kernel(double* __rest
     const int64_t rrow = live ? row : 0;
     const double scale_in = scale64[(i1 / g) * d_out + rrow], zero_in = zero64[(i1 / g) * d_out + rrow];
     double scale = (rem != 0 && live) ? scale_in : 1.0, zero = (rem != 0 && live) ? zero_in : 0.0, rscale = 1.0;
+    // static groups: the parameters of this lane's columns (the group of
+    // each sweep column, then that group's scale and zero for this row)
+    double sc[STATIC ? CPL : 1], ze[STATIC ? CPL : 1], rsc[STATIC ? CPL : 1];
+    if constexpr (STATIC) {
+        int32_t gc[CPL];
+#pragma unroll
+        for (int mm = 0; mm < CPL; ++mm) {
+            const int j = p + LPR * mm;
+            gc[mm] = gsw[i1 + ((FULL || j < nb) ? j : 0)];
+        }
+#pragma unroll
+        for (int mm = 0; mm < CPL; ++mm) {
+            sc[mm] = scale64[(int64_t)gc[mm] * d_out + rrow];
+            ze[mm] = zero64[(int64_t)gc[mm] * d_out + rrow];
+        }
+    }
     const double loss_l = loss64[rrow];
     const double loss_in = (live && p == 0) ? loss_l : 0.0;
     const int dt = tid < nb ? tid : 0;
@@ -383,6 +470,10 @@ __global__ __launch_bounds__(SWAVES * 64) void sweep_block_kernel(double* __rest
     static_assert(BMAX <= SWAVES * 64, "one diagonal entry per thread");
     if (tid < nb) rinv[tid] = 1.0 / udiag;
     if (rem != 0 && live) rscale = 1.0 / scale;
+    if constexpr (STATIC) {
+#pragma unroll
+        for (int mm = 0; mm < CPL; ++mm) rsc[mm] = 1.0 / sc[mm];
+    }
     __syncthreads();
     // U row c's entries for this lane's registers m' >= c / 16
     auto load_urow = [&](double (&u)[CPL], int c) __attribute__((always_inline)) {
@@ -409,7 +500,7 @@ __global__ __launch_bounds__(SWAVES * 64) void sweep_block_kernel(double* __rest
         constexpr int c = decltype(cc)::value;
         constexpr int m = c / LPR, j = c % LPR;
         if (!FULL && c >= nb) return;
-        if (c % SEG == 0 && c == next_gs) {
+        if (!STATIC && c % SEG == 0 && c == next_gs) {
             // group parameters from the group's current values: block
             // columns [c, cend) in registers, later columns from Wwork
             const int64_t gend = (i1 + c + g < d_in) ? i1 + c + g : d_in;
@@ -451,19 +542,7 @@ __global__ __launch_bounds__(SWAVES * 64) void sweep_block_kernel(double* __rest
             }
             xmin = row_min16(xmin);
             xmax = row_max16(xmax);
-            if (qp.sym) {
-                double amax = fmax(-xmin, xmax);
-                if (amax == 0.0) amax = 1.0;
-                scale = 2.0 * amax / qp.maxq;
-                zero = (double)(1 << (qp.bits - 1));
-            } else {
-                if (xmin == 0.0 && xmax == 0.0) {
-                    xmin = -1.0;
-                    xmax = 1.0;
-                }
-                scale = (xmax - xmin) / qp.maxq;
-                zero = rint(-xmin / scale);
-            }
+            grid_params(xmin, xmax, qp, scale, zero);
             rscale = 1.0 / scale;
             if (live && p == 0) {
                 scale64[next_gi * d_out + row] = scale;
@@ -487,18 +566,22 @@ __global__ __launch_bounds__(SWAVES * 64) void sweep_block_kernel(double* __rest
         // w[m] as the previous column left it before its owner's select
         // (which only changes that owner's lane, not this column's owner)
         const double x = (c == 0) ? w[0] : xn;
-        const double y = x * rscale;
+        // this column's grid (static groups: the owner lane's column m)
+        const double cs = STATIC ? sc[STATIC ? m : 0] : scale;
+        const double cz = STATIC ? ze[STATIC ? m : 0] : zero;
+        const double cr = STATIC ? rsc[STATIC ? m : 0] : rscale;
+        const double y = x * cr;
         const double ry = rint(y);
-        double code = fmin(fmax(ry + zero, 0.0), qp.maxq);
-        double t = (x - scale * (code - zero)) * ri;
+        double code = fmin(fmax(ry + cz, 0.0), qp.maxq);
+        double t = (x - cs * (code - cz)) * ri;
         // the common path's result is formed before the rare branch, which
         // then stays off the dependency chain
         asm volatile("" : "+v"(t), "+v"(code));
         // distance of y to the nearest half-integer: 0.5 - |y - rint(y)| (exact)
         if (fabs(y - ry) >= fma(-0x1p-40, fmax(1.0, fabs(y)), 0.5)) {
             asm volatile("");   // a real branch: the division is not worth computing in every column
-            code = fmin(fmax(rint(x / scale) + zero, 0.0), qp.maxq);
-            t = (x - scale * (code - zero)) * ri;
+            code = fmin(fmax(rint(x / cs) + cz, 0.0), qp.maxq);
+            t = (x - cs * (code - cz)) * ri;
         }
         const bool own = p == j;
         // the owner's scaled error to its whole row (DPP row broadcast)
@@ -553,7 +636,7 @@ __global__ __launch_bounds__(SWAVES * 64) void sweep_block_kernel(double* __rest
 // codes / w_hat in original column order.
 __global__ __launch_bounds__(256) void finalize_kernel(const uint8_t* __restrict__ codes_s, int64_t d_out,
                                                        int64_t d_in, const int32_t* __restrict__ pinv, int64_t g,
-                                                       const double* __restrict__ scale64,
+                                                       bool stat, const double* __restrict__ scale64,
                                                        const double* __restrict__ zero64, uint8_t* codes,
                                                        float* w_hat, int* flags) {
     const int64_t r = blockIdx.y;
@@ -567,7 +650,7 @@ __global__ __launch_bounds__(256) void finalize_kernel(const uint8_t* __restrict
     const uint8_t c = codes_s[r * d_in + k];
     codes[r * d_in + j] = c;
     if (w_hat) {
-        const int64_t gi = k / g;
+        const int64_t gi = (stat ? j : k) / g;
         w_hat[r * d_in + j] = (float)(scale64[gi * d_out + r] * ((double)c - zero64[gi * d_out + r]));
     }
 }
@@ -576,7 +659,7 @@ __global__ __launch_bounds__(256) void finalize_kernel(const uint8_t* __restrict
 // its group parameters are read in order into LDS, then gathered from there.
 __global__ __launch_bounds__(256) void finalize_rows_lds_kernel(const uint8_t* __restrict__ codes_s, int64_t d_out,
                                                                 int64_t d_in, const int32_t* __restrict__ pinv,
-                                                                int64_t g, int64_t ng,
+                                                                int64_t g, int64_t ng, bool stat,
                                                                 const double* __restrict__ scale64,
                                                                 const double* __restrict__ zero64, uint8_t* codes,
                                                                 float* w_hat, int* flags) {
@@ -602,7 +685,7 @@ __global__ __launch_bounds__(256) void finalize_rows_lds_kernel(const uint8_t* _
         const uint8_t c = cl[k];
         codes[r * d_in + j] = c;
         if (w_hat) {
-            const int64_t gi = k / g;
+            const int64_t gi = (stat ? j : k) / g;
             w_hat[r * d_in + j] = (float)(fl[gi] * ((double)c - fl[ng + gi]));
         }
     }
@@ -627,6 +710,10 @@ gptq_status sweep_launch(const void* W, gptq_dtype dt, int64_t d_out, int64_t d_
     SweepWs w = carve(ws, d_out, d_in, cfg);
     const int64_t g = cfg->group_size > 0 ? cfg->group_size : d_in;
     const int B = cfg->block_size;
+    // per-row static groups are the dynamic per-row group (taken at column 0
+    // from the untouched row either way)
+    const bool stat = cfg->static_groups != 0 && cfg->group_size > 0;
+    const int64_t ng = n_groups_of(d_in, cfg->group_size);
     // group starts fall on multiples of SEG block columns
     int SEG = CPL;
     while (SEG > 1 && ((B % SEG) != 0 || (cfg->group_size > 0 && (g % SEG) != 0))) SEG >>= 1;
@@ -645,14 +732,18 @@ gptq_status sweep_launch(const void* W, gptq_dtype dt, int64_t d_out, int64_t d_
     GPTQ_LAUNCH_CHECK();
     hipLaunchKernelGGL(fill_neg_kernel, dim3(gx), dim3(256), 0, s, w.pinv, d_in);
     GPTQ_LAUNCH_CHECK();
-    hipLaunchKernelGGL(pinv_kernel, dim3(gx), dim3(256), 0, s, perm, d_in, g, w.pinv, g_idx);
+    hipLaunchKernelGGL(pinv_kernel, dim3(gx), dim3(256), 0, s, perm, d_in, g, stat, w.pinv, g_idx, w.gsw);
     GPTQ_LAUNCH_CHECK();
 
     QParams qp{cfg->bits, cfg->sym, (double)((1 << cfg->bits) - 1)};
+    if (stat) {
+        if (ceil_div(d_out * ng, 4) > INT32_MAX) return GPTQ_ERR_UNSUPPORTED;
+        hipLaunchKernelGGL(static_params_kernel, dim3((unsigned)ceil_div(d_out * ng, 4)), dim3(256), 0, s, W, dt,
+                           d_out, d_in, ld_w, g, ng, qp, w.scale64, w.zero64, scales, zeros);
+        GPTQ_LAUNCH_CHECK();
+    }
     const unsigned grid = (unsigned)ceil_div(d_out, ROWS);
-#define SWEEP_ATTR(n, f)                                                                                        \
-    GPTQ_HIP(hipFuncSetAttribute((const void*)sweep_block_kernel<n, f>, hipFuncAttributeMaxDynamicSharedMemorySize, \
-                                 (int)SWEEP_LDS));
+#define SWEEP_ATTR(n, f) GPTQ_HIP(ensure_lds_limit((const void*)sweep_block_kernel<n, f, false>, (int)SWEEP_LDS));
     SWEEP_ATTR(16, true)
     SWEEP_ATTR(16, false)
     SWEEP_ATTR(8, true)
@@ -664,17 +755,18 @@ gptq_status sweep_launch(const void* W, gptq_dtype dt, int64_t d_out, int64_t d_
     SWEEP_ATTR(1, true)
     SWEEP_ATTR(1, false)
 #undef SWEEP_ATTR
+    GPTQ_HIP(ensure_lds_limit((const void*)sweep_block_kernel<16, true, true>, (int)SWEEP_LDS));
+    GPTQ_HIP(ensure_lds_limit((const void*)sweep_block_kernel<16, false, true>, (int)SWEEP_LDS));
     const int64_t S = superblock_cols(d_in, cfg);
     // A group that runs past the end of its superblock (groups wider than a
     // superblock, or superblocks of one block when lcm(B, g) exceeds the
     // superblock cap) reads columns of later superblocks at its first
     // column; the far update that writes those columns must be done first.
-    const bool wait_far_before_sweep = cfg->group_size > 0 && S % g != 0;
+    const bool wait_far_before_sweep = !stat && cfg->group_size > 0 && S % g != 0;
 
     // A second stream runs each superblock's far update (everything past
     // the next superblock) while the next superblock is swept.
     SideStream side;
-    GPTQ_HIP(side.init());
     bool far_pending = false;
     for (int64_t k = 0, a = 0; a < d_in; ++k, a += S) {
         const int64_t e = (a + S < d_in) ? a + S : d_in;
@@ -683,14 +775,17 @@ gptq_status sweep_launch(const void* W, gptq_dtype dt, int64_t d_out, int64_t d_
         for (int64_t i1 = a; i1 < e; i1 += B) {
             const int nb = (int)((e - i1 < B) ? e - i1 : B);
             const bool full = nb == BMAX;
-            switch (SEG * 2 + (full ? 1 : 0)) {
-#define SWEEP_CASE(n, f)                                                                                      \
-    case n * 2 + f:                                                                                           \
-        hipLaunchKernelGGL((sweep_block_kernel<n, f>), dim3(grid), dim3(SWAVES * 64), SWEEP_LDS, s, w.Wwork,     \
+            switch (stat ? -1 - (full ? 1 : 0) : SEG * 2 + (full ? 1 : 0)) {
+#define SWEEP_CASE_T(n, f, t, label)                                                                         \
+    case label:                                                                                               \
+        hipLaunchKernelGGL((sweep_block_kernel<n, f, t>), dim3(grid), dim3(SWAVES * 64), SWEEP_LDS, s, w.Wwork,  \
                            d_out, d_in, i1,                                                                 \
                            nb, U, g, qp, Ek, (int)S, (int)(i1 - a), w.codes_s, w.scale64, w.zero64, scales,  \
-                           zeros, w.loss64);                                                                  \
+                           zeros, w.loss64, w.gsw);                                                           \
         break;
+#define SWEEP_CASE(n, f) SWEEP_CASE_T(n, f, false, n * 2 + f)
+                SWEEP_CASE_T(16, true, true, -2)
+                SWEEP_CASE_T(16, false, true, -1)
                 SWEEP_CASE(16, 1)
                 SWEEP_CASE(16, 0)
                 SWEEP_CASE(8, 1)
@@ -702,6 +797,7 @@ gptq_status sweep_launch(const void* W, gptq_dtype dt, int64_t d_out, int64_t d_
                 SWEEP_CASE(1, 1)
                 SWEEP_CASE(1, 0)
 #undef SWEEP_CASE
+#undef SWEEP_CASE_T
             }
             GPTQ_LAUNCH_CHECK();
             const int64_t i2 = i1 + nb;
@@ -721,6 +817,7 @@ gptq_status sweep_launch(const void* W, gptq_dtype dt, int64_t d_out, int64_t d_
         if (st != GPTQ_OK) return st;
         far_pending = false;
         if (e + n_near < d_in) {  // far update on the side stream
+            GPTQ_HIP(side.init());
             GPTQ_HIP(hipEventRecord(side.err_ready, s));
             GPTQ_HIP(hipStreamWaitEvent(side.s, side.err_ready, 0));
             st = launch_gemm_f64(side.s, d_out, d_in - e - n_near, e - a, -1.0, Ek, S, U + a * d_in + e + n_near,
@@ -731,14 +828,13 @@ gptq_status sweep_launch(const void* W, gptq_dtype dt, int64_t d_out, int64_t d_
         }
     }
     if (far_pending) GPTQ_HIP(hipStreamWaitEvent(s, side.far_done, 0));
-    const int64_t ng = n_groups_of(d_in, cfg->group_size);
     const size_t fin_lds = (size_t)ng * 16 + (size_t)d_in;
     if (fin_lds <= CONVERT_LDS_MAX) {
         hipLaunchKernelGGL(finalize_rows_lds_kernel, dim3((unsigned)d_out), dim3(256), fin_lds, s, w.codes_s, d_out,
-                           d_in, w.pinv, g, ng, w.scale64, w.zero64, codes, w_hat, w.flags);
+                           d_in, w.pinv, g, ng, stat, w.scale64, w.zero64, codes, w_hat, w.flags);
     } else {
         hipLaunchKernelGGL(finalize_kernel, dim3(gx, (unsigned)d_out), dim3(256), 0, s, w.codes_s, d_out, d_in,
-                           w.pinv, g, w.scale64, w.zero64, codes, w_hat, w.flags);
+                           w.pinv, g, stat, w.scale64, w.zero64, codes, w_hat, w.flags);
     }
     GPTQ_LAUNCH_CHECK();
     if (row_loss) {

@@ -26,7 +26,8 @@ def compare_codes(got: np.ndarray, ref: np.ndarray):
     return same, mx
 
 
-def tie_replay(O, Wp, U, codes_gpu_p, bits, group_size, sym=False, block=128, tau=1e-4, max_forces=32):
+def tie_replay(O, Wp, U, codes_gpu_p, bits, group_size, sym=False, block=128, tau=1e-4, max_forces=32,
+               static=None):
     """Classify GPU-vs-oracle code differences by rounding ties and replay.
 
     Wp, codes_gpu_p: weights and GPU codes in sweep order (columns permuted
@@ -42,10 +43,12 @@ def tie_replay(O, Wp, U, codes_gpu_p, bits, group_size, sym=False, block=128, ta
       delta)] differences that are not ties (a failure);
       codes, scales, zeros, w_hat, row_loss: the oracle's outputs (sweep
       order) after the replay, every row included.
+    ``static``: the oracle sweep's static-groups argument (scales, zeros,
+    group of each sweep column), for every row of Wp.
     """
     import numpy as np
     codes_gpu_p = np.asarray(codes_gpu_p).astype(np.int64)
-    base = O.sweep(Wp, U, bits, group_size, sym, block, margins=True)
+    base = O.sweep(Wp, U, bits, group_size, sym, block, margins=True, static=static)
     codes, scales, zeros, w_hat, row_loss, margin = [np.array(a, copy=True) for a in base]
     same_raw = float(np.mean(codes == codes_gpu_p))
     maxdiff_raw = int(np.abs(codes - codes_gpu_p).max()) if codes.size else 0
@@ -53,6 +56,7 @@ def tie_replay(O, Wp, U, codes_gpu_p, bits, group_size, sym=False, block=128, ta
     ties, other = [], []
     if rows.size:
         Wr, gr = Wp[rows], codes_gpu_p[rows]
+        st_r = None if static is None else (static[0][:, rows], static[1][:, rows], static[2])
         cr, mr = codes[rows], margin[rows]
         forced = {}                       # column -> {local row: code}
         active = np.ones(rows.size, dtype=bool)
@@ -77,7 +81,7 @@ def tie_replay(O, Wp, U, codes_gpu_p, bits, group_size, sym=False, block=128, ta
             if not new:
                 break
             force = {c: (np.array(list(v)), np.array(list(v.values()))) for c, v in forced.items()}
-            out = O.sweep(Wr, U, bits, group_size, sym, block, force=force, margins=True)
+            out = O.sweep(Wr, U, bits, group_size, sym, block, force=force, margins=True, static=st_r)
             cr, mr = out[0], out[5]
         if out is not None:
             codes[rows], w_hat[rows], row_loss[rows] = out[0], out[3], out[4]
@@ -86,14 +90,17 @@ def tie_replay(O, Wp, U, codes_gpu_p, bits, group_size, sym=False, block=128, ta
                 other=other, codes=codes, scales=scales, zeros=zeros, w_hat=w_hat, row_loss=row_loss)
 
 
-def assert_from_x_parity(O, W64, H, got, bits, group_size, act_order, sym=False, block=128, damp=0.01, name=""):
+def assert_from_x_parity(O, W64, H, got, bits, group_size, act_order, sym=False, block=128, damp=0.01, name="",
+                         static_groups=False):
     """The GPU layer (got: original-order outputs) against the oracle run from
     the same activations' float64 Hessian H, step by step as the oracle's
     gptq_quantize takes them (order, damping, U, sweep): every differing code
     is a rounding tie decided the other way (or follows from one in its row,
     as the replay shows); after the replay the codes are identical, scales
     within 1e-5 relative, zero points equal, and the layer loss within 1e-3
-    relative.  Returns the replay summary (raw numbers included)."""
+    relative.  Returns the replay summary (raw numbers included).
+    ``static_groups``: the static-groups option (groups of original columns,
+    parameters from W64 as given)."""
     import time
 
     import numpy as np
@@ -103,15 +110,21 @@ def assert_from_x_parity(O, W64, H, got, bits, group_size, act_order, sym=False,
     assert np.array_equal(np.asarray(got["perm"]).astype(np.int64), perm), name
     U = O.inverse_hessian_upper(O.damp_hessian(H[np.ix_(perm, perm)], damp))
     print(f"{name}: oracle order and U in {time.time() - t0:.1f} s", flush=True)
+    static = None
+    if static_groups and group_size > 0:
+        st_s, st_z = O.static_group_params(W64, bits, group_size, sym)
+        static = (st_s, st_z, perm // group_size)
+        assert np.array_equal(np.asarray(got["g_idx"]), np.arange(d_in) // group_size), name
     t0 = time.time()
-    rp = tie_replay(O, W64[:, perm], U, np.asarray(got["codes"])[:, perm], bits, group_size, sym, block)
+    rp = tie_replay(O, W64[:, perm], U, np.asarray(got["codes"])[:, perm], bits, group_size, sym, block,
+                    static=static)
     print(f"{name}: oracle sweep of {W64.shape[0]} rows and tie replay in {time.time() - t0:.1f} s", flush=True)
     assert not rp["other"], (name, rp["other"][:5])
     assert np.array_equal(rp["codes"], np.asarray(got["codes"])[:, perm].astype(np.int64)), name
     sc_g = np.asarray(got["scales"]).astype(np.float64)
     np.testing.assert_allclose(sc_g, rp["scales"], rtol=1e-5, atol=0, err_msg=name)
     np.testing.assert_array_equal(np.asarray(got["zeros"]).astype(np.float64), rp["zeros"], err_msg=name)
-    base = O.sweep(W64[:, perm], U, bits, group_size, sym, block) if rp["rows_differing"] else None
+    base = O.sweep(W64[:, perm], U, bits, group_size, sym, block, static=static) if rp["rows_differing"] else None
     loss_g = O.layer_loss(W64, np.asarray(got["w_hat"]).astype(np.float64), H).sum()
     w_hat_o = np.empty_like(rp["w_hat"])
     w_hat_o[:, perm] = rp["w_hat"]

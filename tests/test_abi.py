@@ -41,8 +41,11 @@ def test_status_strings_and_version():
 def test_config_default():
     lib = P.load()
     c = P.Config()
+    c.static_groups = 7   # overwritten by the default
     lib.gptq_config_default(ctypes.byref(c))
-    assert (c.bits, c.group_size, c.sym, c.act_order, c.block_size, c.damp) == (4, 128, 0, 0, 128, 0.01)
+    assert (c.bits, c.group_size, c.sym, c.act_order, c.block_size, c.static_groups, c.damp) == \
+        (4, 128, 0, 0, 128, 0, 0.01)
+    assert ctypes.sizeof(P.Config) == 32 and P.Config.damp.offset == 24
 
 
 def test_workspace_queries():
@@ -54,6 +57,11 @@ def test_workspace_queries():
     mixed = P.make_config(group_size=96, block=128)   # neither divides the other: accepted
     assert lib.gptq_quantize_layer_workspace(8, 384, ctypes.byref(mixed)) >= 8 * 384 * 9
     assert lib.gptq_quantize_layer_workspace(8, 384, ctypes.byref(P.make_config(block=0))) == 0
+    bad = P.make_config()
+    bad.static_groups = 2
+    assert lib.gptq_quantize_layer_workspace(8, 384, ctypes.byref(bad)) == 0
+    st = P.make_config(group_size=96, block=128, static_groups=True)
+    assert lib.gptq_quantize_layer_workspace(8, 384, ctypes.byref(st)) >= 8 * 384 * 9
     assert lib.gptq_packed_words_per_row(11, 3) == 2
     assert lib.gptq_packed_words_per_row(8, 4) == 1
     assert lib.gptq_packed_words_per_row(8, 5) == -1

@@ -177,11 +177,12 @@ def test_not_pd_and_nonfinite():
 # Column sweep fed the oracle's U
 # ---------------------------------------------------------------------------
 
-def _sweep_case(d_out, d_in, bits, g, act, sym=False, block=128, dtype="bf16", seed=0):
+def _sweep_case(d_out, d_in, bits, g, act, sym=False, block=128, dtype="bf16", seed=0, static_groups=False):
     L = _layer(d_out, d_in, max(2 * d_in, 1000), dtype=dtype, seed=100 + seed)
     H = O.hessian(L.X_f64())
-    ref = O.gptq_quantize(L.W_f64(), H, bits=bits, group_size=g, sym=sym, act_order=act, block=block)
-    cfg = P.make_config(bits=bits, group_size=g, sym=sym, act_order=act, block=block)
+    ref = O.gptq_quantize(L.W_f64(), H, bits=bits, group_size=g, sym=sym, act_order=act, block=block,
+                          static_groups=static_groups)
+    cfg = P.make_config(bits=bits, group_size=g, sym=sym, act_order=act, block=block, static_groups=static_groups)
     W = to_torch(L.W, dtype)
     U = torch.from_numpy(ref["U"]).to(DEV)
     perm = torch.from_numpy(ref["perm"].astype(np.int32)).to(DEV)
@@ -224,6 +225,36 @@ def test_sweep_matches_oracle_given_U(d_out, d_in, bits, g, act, sym, block):
     np.testing.assert_array_equal(got["zeros"], ref["zeros"].astype(np.float32))
     np.testing.assert_allclose(got["w_hat"], ref["w_hat"].astype(np.float32), rtol=2e-7, atol=1e-30)
     np.testing.assert_allclose(got["row_loss"], ref["row_loss"], rtol=1e-9)
+
+
+@pytest.mark.parametrize("d_out,d_in,bits,g,act,sym,block", [
+    (100, 300, 4, 128, True, False, 128),  # ragged last group
+    (130, 384, 3, 64, True, False, 128),
+    (40, 96, 4, 16, False, True, 32),      # symmetric, natural order
+    (96, 1000, 4, 96, True, False, 128),   # groups crossing block ends, ragged tail
+    (50, 600, 4, 200, True, False, 128),   # group wider than a block
+    (64, 1000, 4, 100, True, False, 128),  # groups crossing superblock ends
+    (20, 75, 8, 25, False, False, 25),     # 8-bit, partial blocks
+    (9, 21, 3, 6, True, False, 1),         # one column per block
+    (64, 256, 4, -1, True, False, 128),    # per-row: the same as the default grouping
+])
+def test_static_groups_sweep_matches_oracle_given_U(d_out, d_in, bits, g, act, sym, block):
+    """Static groups: parameters per group of original columns from W as
+    given, act-order only ordering the sweep, g_idx = j // g."""
+    print(f"static sweep {d_out}x{d_in} b{bits} g{g} act{act} sym{sym} B{block}", flush=True)
+    ref, got = _sweep_case(d_out, d_in, bits, g, act, sym, block, seed=d_in + 1, static_groups=True)
+    assert np.array_equal(got["codes"], ref["codes"])
+    assert np.array_equal(got["g_idx"], ref["g_idx"])
+    if g > 0:
+        assert np.array_equal(got["g_idx"], np.arange(d_in) // g)
+    np.testing.assert_allclose(got["scales"], ref["scales"].astype(np.float32), rtol=2e-7)
+    np.testing.assert_array_equal(got["zeros"], ref["zeros"].astype(np.float32))
+    np.testing.assert_allclose(got["w_hat"], ref["w_hat"].astype(np.float32), rtol=2e-7, atol=1e-30)
+    np.testing.assert_allclose(got["row_loss"], ref["row_loss"], rtol=1e-9)
+    if act and g > 0 and d_out * d_in >= 10000:
+        dyn = O.gptq_quantize(_layer(d_out, d_in, max(2 * d_in, 1000), seed=100 + d_in + 1).W_f64(), H=ref["H"],
+                              bits=bits, group_size=g, sym=sym, act_order=act, block=block)
+        assert not np.array_equal(dyn["codes"], got["codes"])   # the option changes the result
 
 
 @pytest.mark.parametrize("bits,g,sym", [(4, 32, False), (3, 64, True), (2, -1, False)])
@@ -344,6 +375,44 @@ def test_end_to_end(d_out, d_in, n, dtype, bits, g, act):
     assert np.array_equal(words, O.pack(got["codes"], bits))
     assert_from_x_parity(O, L.W_f64(), ref["H"], got, bits, g, act, name=f"{d_out}x{d_in}")
     print(f"  identical {same:.6f} max diff {mx}", flush=True)
+
+
+@pytest.mark.parametrize("d_out,d_in,n,dtype,bits,g", [
+    (192, 640, 8192, "bf16", 4, 128),   # workload-3 recipe, reduced
+    (96, 448, 6000, "bf16", 2, 64),     # workload-4 recipe, reduced
+    (128, 600, 6000, "f16", 3, 96),     # groups crossing block ends, ragged last group
+])
+def test_static_groups_end_to_end(d_out, d_in, n, dtype, bits, g):
+    """Static groups with act-order from X: the same acceptance as the
+    default grouping, and the product from the packed words needs no
+    gather (g_idx = j // g: the plain original-order product)."""
+    print(f"static e2e {d_out}x{d_in} n={n} {dtype} b{bits} g{g}", flush=True)
+    L = _layer(d_out, d_in, n, dtype=dtype, frac=0.005, scale=50.0, seed=d_in + 3)
+    ref = O.gptq_quantize(L.W_f64(), X=L.X_f64(), bits=bits, group_size=g, act_order=True, static_groups=True)
+    cfg = P.make_config(bits=bits, group_size=g, act_order=True, static_groups=True)
+    out = P.quantize(to_torch(L.W, dtype), X=to_torch(L.X, dtype), cfg=cfg)
+    torch.cuda.synchronize()
+    got = {k: v.cpu().numpy() for k, v in out.items()}
+    same, mx = compare_codes(got["codes"], ref["codes"])
+    assert same >= 0.999 and mx <= 1, (same, mx)
+    rp = assert_from_x_parity(O, L.W_f64(), ref["H"], got, bits, g, True, name=f"static {d_out}x{d_in}",
+                              static_groups=True)
+    assert rp["same_raw"] >= 0.999
+    Xt = to_torch(L.X[:300], dtype)
+    Y = P.dequant_matmul(Xt, out["packed"], bits, out["scales"], out["zeros"], group_size=g)
+    torch.cuda.synchronize()
+    want = O.dequant_matmul(L.X_f64()[:300], O.pack(got["codes"], bits), bits, d_in, got["scales"].astype(np.float64),
+                            got["zeros"].astype(np.float64), g_idx=np.arange(d_in) // g)
+    # float32 error bound of the product (either route: the matrix-core one
+    # sums a group's products in float32, the block route chains v_dot2 and
+    # FMAs), elementwise with A = sum_k |x_k| s_k (c_k + z_k + 2^(b+1))
+    S = got["scales"].astype(np.float64)[np.arange(d_in) // g].T
+    Z = got["zeros"].astype(np.float64)[np.arange(d_in) // g].T
+    A = np.abs(L.X_f64()[:300]) @ (S * (got["codes"] + Z + 2.0 ** (bits + 1))).T
+    ng = -(-d_in // g)
+    nb = -(-(-(-d_in // 32)) // 256)
+    tol = (max(2 * g + ng + 8, 96 + 32 * nb)) * 2.0 ** -24 * A
+    assert np.all(np.abs(Y.cpu().numpy() - want) <= tol)
 
 
 def test_scale_invariance_and_row_subset_on_gpu():

@@ -170,7 +170,14 @@ def dequant_measure(d_out, d_in, bits, gs, token_counts, rounds, cpu=False):
     """Time gptq_dequant_matmul on DQ_COPIES copies of one packed layer, cycled
     so that every launch reads its weights from HBM.  Each round of
     DQ_COPIES launches is captured once in a HIP graph and replayed; HIP
-    events on the replay stream bracket `rounds` replays."""
+    events on the replay stream bracket `rounds` replays.  Three routes per
+    token count:
+      perm:    act-order layer packed in quantization order, the product
+               gathering the activations itself (the per-token kernels);
+      gather:  the same layer, gptq_gather_columns first, then the
+               natural-order product (the matrix cores from 2 tokens on);
+      natural: a layer packed in original order (no act-order, or static
+               groups with act-order): no gather."""
     import torch
 
     import post_weight_quantization_accum_amd as P
@@ -182,52 +189,63 @@ def dequant_measure(d_out, d_in, bits, gs, token_counts, rounds, cpu=False):
     codes = torch.from_numpy(L.codes).to(dev)
     perm = torch.from_numpy(L.perm).to(dev)
     packed0 = P.pack_permuted(codes, bits, perm)
+    packed_nat = P.pack(codes, bits)
     del codes
     sc0 = torch.from_numpy(L.scales).to(dev)
     z0 = torch.from_numpy(L.zeros).to(dev)
-    layers = [(packed0.clone(), sc0.clone(), z0.clone(), perm.clone()) for _ in range(DQ_COPIES)]
+    layers = [(packed0.clone(), sc0.clone(), z0.clone(), perm.clone(), packed_nat.clone()) for _ in range(DQ_COPIES)]
+    del packed_nat
     X = torch.from_numpy(L.X.view(np.int16)).view(torch.bfloat16).to(dev)
     ng = sc0.shape[0]
     out = {}
     for n in token_counts:
         Xn = X[:n]
+        Xg = torch.empty((n, d_in), dtype=torch.bfloat16, device=dev)
         Y = torch.empty((n, d_out), dtype=torch.float32, device=dev)
 
-        def one_round():
-            for pk, sc, z, pm in layers:
-                P.dequant_matmul(Xn, pk, bits, sc, z, perm=pm, group_size=gs, out=Y)
+        def rounds_of(mode):
+            def one_round():
+                for pk, sc, z, pm, pkn in layers:
+                    if mode == "perm":
+                        P.dequant_matmul(Xn, pk, bits, sc, z, perm=pm, group_size=gs, out=Y)
+                    elif mode == "gather":
+                        P.gather_columns(Xn, pm, out=Xg)
+                        P.dequant_matmul(Xg, pk, bits, sc, z, group_size=gs, out=Y)
+                    else:
+                        P.dequant_matmul(Xn, pkn, bits, sc, z, group_size=gs, out=Y)
+            return one_round
 
-        one_round()
-        torch.cuda.synchronize()
-        s = torch.cuda.Stream()
-        s.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s):
+        row = {}
+        for mode in ("perm", "gather", "natural"):
+            one_round = rounds_of(mode)
             one_round()
-        torch.cuda.current_stream().wait_stream(s)
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            one_round()
-        g.replay()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        cur = torch.cuda.current_stream()
-        e0.record(cur)
-        for _ in range(rounds):
+            torch.cuda.synchronize()
+            s = torch.cuda.Stream()
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                one_round()
+            torch.cuda.current_stream().wait_stream(s)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                one_round()
             g.replay()
-        e1.record(cur)
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / (rounds * DQ_COPIES)
-        # eager launches (ctypes call per product) for comparison
-        e0.record(cur)
-        for _ in range(max(1, rounds // 4)):
-            one_round()
-        e1.record(cur)
-        torch.cuda.synchronize()
-        us_eager = e0.elapsed_time(e1) * 1e3 / (max(1, rounds // 4) * DQ_COPIES)
-        nbytes = dequant_bytes(d_out, d_in, bits, ng, n)
-        out[n] = {"us_per_launch": round(us, 3), "us_per_launch_eager": round(us_eager, 3),
-                  "GBps": round(nbytes / (us * 1e-6) / 1e9, 1), "bytes": nbytes}
-        del g
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            cur = torch.cuda.current_stream()
+            e0.record(cur)
+            for _ in range(rounds):
+                g.replay()
+            e1.record(cur)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / (rounds * DQ_COPIES)
+            del g
+            nbytes = dequant_bytes(d_out, d_in, bits, ng, n)
+            if mode == "natural":
+                nbytes -= d_in * 4   # no perm
+            row[mode] = {"us_per_launch": round(us, 3), "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+                         "bytes": nbytes}
+        best = min(("perm", "gather"), key=lambda m: row[m]["us_per_launch"])
+        out[n] = dict(row["perm"], routes=row, act_order_best=best)
     res = {"layer": f"{d_out}x{d_in}", "bits": bits, "group_size": gs, "copies": DQ_COPIES, "rounds": rounds,
            "by_tokens": out}
     if cpu:

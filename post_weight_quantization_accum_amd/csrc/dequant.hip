@@ -1047,6 +1047,286 @@ gptq_status by_bits_mfma(const DqArgs& a, int bits, hipStream_t s) {
     return GPTQ_ERR_INVALID_ARG;
 }
 
+// ---------------------------------------------------------------------------
+// Few tokens (2 .. 127) on the matrix cores.
+//
+// The weights are read once per 16 TT tokens (TT = 1, 2 or 4 tiles of 16),
+// so the packed words are again the bytes that matter; the matrix cores only
+// spare the per-token dot products.  A workgroup owns 16 weight rows and up
+// to 16 TT tokens, and its FW_WAVES waves split the 32-column blocks of the
+// rows between them (contiguous ranges; a group cut by a range end is
+// corrected per part, which is exact since s (P - (2^b + z) sum x) is linear
+// in P and sum x).  Each wave runs TT 16x16 tiles with v_mfma_f32_16x16x32
+// (one instruction per tile and block, all sharing the block's B operand)
+// and takes its operands straight from memory into registers, several blocks
+// ahead, without LDS: lane l holds token l % 16 (of each tile) and columns
+// 8 (l / 16) .. + 7 of the block (A: 16 bytes of the activation row) and row
+// l % 16 with the same columns (B: the codes as exact half-precision values
+// 2^b + c, from one load of the packed row).  At the end the waves' tiles
+// are added in wave order through LDS (deterministic).
+// ---------------------------------------------------------------------------
+constexpr int FW_WAVES = 8;
+constexpr int FW_THREADS = 64 * FW_WAVES;
+#ifndef GPTQ_FW_MIN
+#define GPTQ_FW_MIN 2
+#endif
+constexpr int64_t FW_MIN_TOKENS = GPTQ_FW_MIN;   // below: the per-token kernels
+
+typedef float f4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f4_t mfma_16x16x32(u32x4_t a, u32x4_t b, f4_t c, bf16x8_t*) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                   c, 0, 0, 0);
+}
+__device__ __forceinline__ f4_t mfma_16x16x32(u32x4_t a, u32x4_t b, f4_t c, h16x8_t*) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h16x8_t, a), __builtin_bit_cast(h16x8_t, b), c,
+                                                  0, 0, 0);
+}
+
+// The 8 codes held in the low 8 * BITS bits of `win` as a B operand of
+// exact values 2^b + c (pairs of half-precision lanes).
+template <int BITS, typename T>
+__device__ __forceinline__ u32x4_t codes8_operand(uint64_t win) {
+    constexpr int SH = T::MB - BITS;
+    constexpr uint32_t E = (uint32_t)(T::BIAS + BITS) << T::MB;
+    constexpr uint32_t EE = E | (E << 16);
+    constexpr uint32_t M = (1u << BITS) - 1u;
+    uint32_t v[4];
+    if constexpr (BITS == 4) {
+        const uint32_t x = (uint32_t)win;
+        const uint32_t ev = x & 0x0F0F0F0Fu, od = (x >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            // bytes: ev.byte j, zero, od.byte j, zero
+            const uint32_t pr = __builtin_amdgcn_perm(od, ev, 0x0C000C00u | (uint32_t)j | ((uint32_t)(4 + j) << 16));
+            v[j] = (pr << SH) | EE;
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t c0 = (uint32_t)(win >> (BITS * (2 * j))) & M;
+            const uint32_t c1 = (uint32_t)(win >> (BITS * (2 * j + 1))) & M;
+            v[j] = (c0 << SH) | (c1 << (SH + 16)) | EE;
+        }
+    }
+    return u32x4_t{v[0], v[1], v[2], v[3]};
+}
+
+// blocks whose loads are in flight per wave
+__host__ __device__ constexpr int fw_depth(int tt) { return tt >= 4 ? 4 : 8; }
+
+template <int BITS, typename T, bool XV, int TT>
+__global__ __launch_bounds__(FW_THREADS) void dequant_mfma_few_kernel(DqArgs a, int64_t n_rt, int64_t n_mt,
+                                                                      int64_t per_xcd) {
+    constexpr int DEPTH = fw_depth(TT);
+    __shared__ float red[FW_WAVES - 1][TT][4][64];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // XCD-grouped order: the token tiles of one row tile run on one XCD
+    const int64_t b = blockIdx.x;
+    const int64_t lin = (b % 8) * per_xcd + b / 8;
+    if (lin >= n_rt * n_mt) return;
+    const int64_t rt = lin / n_mt, mt = lin % n_mt;
+    const int64_t n0 = rt * 16, t0 = mt * 16 * TT;
+    const int li = lane & 15, q = lane >> 4;          // token / row, and the lane's 8-column part of a block
+    const uint32_t d_in = (uint32_t)a.d_in;
+    const uint32_t nkb = (uint32_t)ceil_div(a.d_in, 32);
+    const uint32_t bpg = a.gsize >= a.d_in ? nkb : (uint32_t)(a.gsize >> 5);
+    const uint32_t kb_lo = (uint32_t)((uint64_t)nkb * wave / FW_WAVES);
+    const uint32_t kb_hi = (uint32_t)((uint64_t)nkb * (wave + 1) / FW_WAVES);
+    constexpr float OFF = (float)(1 << BITS);
+
+    bool tok_ok[TT];
+    const uint16_t* xrow[TT];
+#pragma unroll
+    for (int t = 0; t < TT; ++t) {
+        const int64_t tok = t0 + 16 * t + li;
+        tok_ok[t] = tok < a.n_tok;
+        xrow[t] = (const uint16_t*)a.X + (tok_ok[t] ? tok : 0) * a.ld_x;
+    }
+    const __amdgpu_buffer_rsrc_t rs = words_rsrc(a, n0 < a.d_out ? n0 : a.d_out);
+    const uint32_t row_off = (uint32_t)li * (uint32_t)a.wpr * 4;   // rows past d_out: past the buffer's end
+    const int64_t row = n0 + li;
+    const bool row_ok = row < a.d_out;
+
+    // raw loads of block kb for this lane: its 8 activations of each token
+    // tile, the words holding its 8 codes, and its row's scale and zero point
+    // of the block's group.  Every load is unconditional (clamped addresses)
+    // and its value is only used (masked, shifted) when the block is
+    // computed, so that a ring slot is consumed before it is refilled and
+    // keeps its registers.
+    struct Ops {
+        u32x4_t x[TT];
+        u32x2_t w;
+        float s, z;
+    };
+    auto load = [&](uint32_t kb, Ops& o) {
+        const uint32_t k = kb * 32 + 8 * q;   // first column of the lane's 8
+#pragma unroll
+        for (int t = 0; t < TT; ++t) {
+            if constexpr (XV) {
+                o.x[t] = *(const u32x4_t*)(xrow[t] + (k < d_in ? k : 0));
+            } else {
+                uint32_t e[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) e[i] = xrow[t][k + i < d_in ? k + i : 0];
+                o.x[t] = u32x4_t{e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16)};
+            }
+        }
+        const uint32_t bit = (uint32_t)BITS * k;   // bit offset of the lane's first code in its row
+        if constexpr (BITS == 4) {
+            o.w.x = __builtin_amdgcn_raw_buffer_load_b32(rs, row_off + (bit >> 5) * 4, 0, 0);
+        } else {
+            o.w = __builtin_amdgcn_raw_buffer_load_b64(rs, row_off + (bit >> 5) * 4, 0, 0);
+        }
+        const int64_t idx = (int64_t)(kb / bpg) * a.d_out + (row_ok ? row : 0);
+        o.s = a.scales[idx];
+        o.z = a.zeros[idx];
+    };
+    // the lane's activations of block kb in tile t (zeros past d_in or past the last token)
+    auto acts = [&](uint32_t kb, const Ops& o, int t) -> u32x4_t {
+        const uint32_t k = kb * 32 + 8 * q;
+        if constexpr (XV) {
+            return (tok_ok[t] && k < d_in) ? o.x[t] : u32x4_t{0u, 0u, 0u, 0u};
+        } else {
+            // element i of the lane's 8 is zero past d_in
+            uint32_t m[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                m[i] = (tok_ok[t] && k + 2 * i < d_in ? 0x0000FFFFu : 0u) |
+                       (tok_ok[t] && k + 2 * i + 1 < d_in ? 0xFFFF0000u : 0u);
+            return u32x4_t{o.x[t].x & m[0], o.x[t].y & m[1], o.x[t].z & m[2], o.x[t].w & m[3]};
+        }
+    };
+    auto window = [&](uint32_t kb, const Ops& o) -> uint64_t {
+        if constexpr (BITS == 4) {
+            return o.w.x;
+        } else {
+            const uint32_t bit = (uint32_t)BITS * (kb * 32 + 8 * q);
+            return ((((uint64_t)o.w.y) << 32) | o.w.x) >> (bit & 31);
+        }
+    };
+
+    f4_t acc[TT], accg[TT];
+    float xpart[TT];
+#pragma unroll
+    for (int t = 0; t < TT; ++t) {
+        acc[t] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        accg[t] = acc[t];
+        xpart[t] = 0.0f;
+    }
+    float sv = 0.0f, ov = 0.0f;
+
+    // group end (or the end of this wave's part of a group): acc += s (P -
+    // (2^b + z) sum x); element r of lane l is token 4 (l / 16) + r of the tile
+    auto close_group = [&]() {
+#pragma unroll
+        for (int t = 0; t < TT; ++t) {
+            float xt = xpart[t] + __shfl_xor(xpart[t], 16, 64);
+            xt += __shfl_xor(xt, 32, 64);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float x = __shfl(xt, 4 * q + r, 64);
+                acc[t][r] = fmaf(sv, fmaf(-ov, x, accg[t][r]), acc[t][r]);
+            }
+        }
+    };
+
+    Ops ring[DEPTH];
+    const uint32_t kb_last = kb_hi > kb_lo ? kb_hi - 1 : kb_lo;
+#pragma unroll
+    for (int p = 0; p < DEPTH; ++p) load(kb_lo + p < kb_hi ? kb_lo + p : kb_last, ring[p]);
+    bool open = false;
+    for (uint32_t kb0 = kb_lo; kb0 < kb_hi; kb0 += DEPTH) {
+#pragma unroll
+        for (int p = 0; p < DEPTH; ++p) {
+            const uint32_t kb = kb0 + p;
+            if (kb < kb_hi) {
+                if (kb == kb_lo || kb % bpg == 0) {
+                    if (open) close_group();
+                    sv = row_ok ? ring[p].s : 0.0f;
+                    ov = OFF + (row_ok ? ring[p].z : 0.0f);
+                    open = true;
+#pragma unroll
+                    for (int t = 0; t < TT; ++t) {
+                        xpart[t] = 0.0f;
+                        accg[t] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+                    }
+                }
+                const u32x4_t bop = codes8_operand<BITS, T>(window(kb, ring[p]));
+#pragma unroll
+                for (int t = 0; t < TT; ++t) {
+                    const u32x4_t xa = acts(kb, ring[p], t);
+                    accg[t] = mfma_16x16x32(xa, bop, accg[t], (typename T::mfma_tag*)nullptr);
+                    float x = T::dot2(xa.x, T::ONES, xpart[t]);
+                    x = T::dot2(xa.y, T::ONES, x);
+                    x = T::dot2(xa.z, T::ONES, x);
+                    xpart[t] = T::dot2(xa.w, T::ONES, x);
+                }
+            }
+            // refill this slot DEPTH blocks ahead (past the range: reload the last block)
+            load(kb + DEPTH < kb_hi ? kb + DEPTH : kb_last, ring[p]);
+        }
+    }
+    if (open) close_group();
+
+    // the waves' tiles added in wave order; element r of lane l is token
+    // 4 (l / 16) + r of the tile, row l % 16
+    if (wave > 0) {
+#pragma unroll
+        for (int t = 0; t < TT; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) red[wave - 1][t][r][lane] = acc[t][r];
+    }
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+        for (int t = 0; t < TT; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float y = acc[t][r];
+#pragma unroll
+                for (int w = 0; w < FW_WAVES - 1; ++w) y += red[w][t][r][lane];
+                const int64_t tk = t0 + 16 * t + 4 * q + r;
+                if (tk < a.n_tok && row_ok) a.Y[tk * a.ld_y + row] = y;
+            }
+    }
+}
+
+template <int BITS, typename T, int TT>
+gptq_status launch_mfma_few_tt(const DqArgs& a, hipStream_t s) {
+    const int64_t n_rt = ceil_div(a.d_out, 16), n_mt = ceil_div(a.n_tok, 16 * TT);
+    const int64_t per_xcd = ceil_div(n_rt * n_mt, 8);
+    if (per_xcd * 8 > INT32_MAX) return GPTQ_ERR_UNSUPPORTED;
+    const dim3 grid((unsigned)(per_xcd * 8)), block(FW_THREADS);
+    if (a.xvec && a.d_in % 8 == 0)
+        hipLaunchKernelGGL((dequant_mfma_few_kernel<BITS, T, true, TT>), grid, block, 0, s, a, n_rt, n_mt, per_xcd);
+    else
+        hipLaunchKernelGGL((dequant_mfma_few_kernel<BITS, T, false, TT>), grid, block, 0, s, a, n_rt, n_mt, per_xcd);
+    GPTQ_LAUNCH_CHECK();
+    return GPTQ_OK;
+}
+
+// 16 tokens per tile; up to 16: one tile, up to 32: two, more: four per workgroup
+template <int BITS, typename T>
+gptq_status launch_mfma_few(const DqArgs& a, hipStream_t s) {
+    if (a.n_tok <= 16) return launch_mfma_few_tt<BITS, T, 1>(a, s);
+    if (a.n_tok <= 32) return launch_mfma_few_tt<BITS, T, 2>(a, s);
+    return launch_mfma_few_tt<BITS, T, 4>(a, s);
+}
+
+template <typename T>
+gptq_status by_bits_mfma_few(const DqArgs& a, int bits, hipStream_t s) {
+    switch (bits) {
+        case 2: return launch_mfma_few<2, T>(a, s);
+        case 3: return launch_mfma_few<3, T>(a, s);
+        case 4: return launch_mfma_few<4, T>(a, s);
+        case 8:
+            if constexpr (T::MB - 8 >= 0) return launch_mfma_few<8, T>(a, s);
+            break;
+    }
+    return GPTQ_ERR_INVALID_ARG;
+}
+
 template <int BITS, int TM, typename T>
 gptq_status launch_block(const DqArgs& a, hipStream_t s) {
     const dim3 grid((unsigned)ceil_div(a.d_out, RW), (unsigned)ceil_div(a.n_tok, TM));
@@ -1095,33 +1375,35 @@ gptq_status dispatch_block(const DqArgs& a, gptq_dtype dt, int bits, hipStream_t
 // ---------------------------------------------------------------------------
 // Column gather Xg[t][k] = X[t][perm[k]] ("GPTQ量化算法深度解析" §3.3: with
 // act-order, inference gathers the activations into the quantization order).
-// A workgroup owns 16 token rows and walks the columns in chunks of 4096:
-// the chunk's perm entries go to LDS once, then every row is gathered with
-// coalesced writes (the reads stay inside one row).
+// A workgroup owns `rows` token rows and one chunk of `chunk` columns (a
+// grid of token tiles x chunks): the chunk's perm entries go to LDS once,
+// then every row is gathered with coalesced writes (the reads stay inside
+// one row).  Many tokens: 16 rows x 4096 columns, which spreads the perm
+// reads over many rows; fewer than 1024 tokens: 4 rows x 512 columns, so
+// that a few long rows still spread over the chip.
 // ---------------------------------------------------------------------------
-constexpr int GA_ROWS = 16, GA_CHUNK = 4096;
+constexpr int GA_CHUNK_MAX = 4096;
 
 template <typename E>
 __global__ __launch_bounds__(256) void gather_columns_kernel(const E* __restrict__ X, int64_t n_tok, int64_t d_in,
                                                              int64_t ld_x, const int32_t* __restrict__ perm,
-                                                             E* __restrict__ Xg, int64_t ld_g, E nan_value) {
-    __shared__ int32_t pl[GA_CHUNK];
+                                                             E* __restrict__ Xg, int64_t ld_g, E nan_value, int rows,
+                                                             int chunk) {
+    __shared__ int32_t pl[GA_CHUNK_MAX];
     const int tid = threadIdx.x;
-    const int64_t r0 = (int64_t)blockIdx.x * GA_ROWS;
-    for (int64_t c0 = 0; c0 < d_in; c0 += GA_CHUNK) {
-        const int nc = (d_in - c0 < GA_CHUNK) ? (int)(d_in - c0) : GA_CHUNK;
-        __syncthreads();
-        for (int k = tid; k < nc; k += 256) pl[k] = perm[c0 + k];
-        __syncthreads();
-        for (int rr = 0; rr < GA_ROWS; ++rr) {
-            const int64_t t = r0 + rr;
-            if (t >= n_tok) break;
-            const E* xr = X + t * ld_x;
-            E* gr = Xg + t * ld_g + c0;
-            for (int k = tid; k < nc; k += 256) {
-                const int32_t p = pl[k];
-                gr[k] = ((uint32_t)p < (uint64_t)d_in) ? xr[p] : nan_value;
-            }
+    const int64_t r0 = (int64_t)blockIdx.x * rows;
+    const int64_t c0 = (int64_t)blockIdx.y * chunk;
+    const int nc = (d_in - c0 < chunk) ? (int)(d_in - c0) : chunk;
+    for (int k = tid; k < nc; k += 256) pl[k] = perm[c0 + k];
+    __syncthreads();
+    for (int rr = 0; rr < rows; ++rr) {
+        const int64_t t = r0 + rr;
+        if (t >= n_tok) break;
+        const E* xr = X + t * ld_x;
+        E* gr = Xg + t * ld_g + c0;
+        for (int k = tid; k < nc; k += 256) {
+            const int32_t p = pl[k];
+            gr[k] = ((uint32_t)p < (uint64_t)d_in) ? xr[p] : nan_value;
         }
     }
 }
@@ -1131,14 +1413,17 @@ __global__ __launch_bounds__(256) void gather_columns_kernel(const E* __restrict
 gptq_status gather_columns_launch(const void* X, gptq_dtype dt, int64_t n_tok, int64_t d_in, int64_t ld_x,
                                   const int32_t* perm, void* Xg, int64_t ld_g, hipStream_t s) {
     if (n_tok == 0) return GPTQ_OK;
-    const dim3 grid((unsigned)ceil_div(n_tok, GA_ROWS));
+    const int rows = n_tok >= 1024 ? 16 : 4;
+    const int chunk = n_tok >= 1024 ? GA_CHUNK_MAX : 512;
+    if (ceil_div(d_in, chunk) > 65535 || ceil_div(n_tok, rows) > INT32_MAX) return GPTQ_ERR_UNSUPPORTED;
+    const dim3 grid((unsigned)ceil_div(n_tok, rows), (unsigned)ceil_div(d_in, chunk));
     if (dt == GPTQ_F32) {
         hipLaunchKernelGGL(gather_columns_kernel<float>, grid, dim3(256), 0, s, (const float*)X, n_tok, d_in, ld_x,
-                           perm, (float*)Xg, ld_g, __builtin_nanf(""));
+                           perm, (float*)Xg, ld_g, __builtin_nanf(""), rows, chunk);
     } else {
         const uint16_t nan16 = dt == GPTQ_BF16 ? (uint16_t)Bf16::NAN_BITS : (uint16_t)F16::NAN_BITS;
         hipLaunchKernelGGL(gather_columns_kernel<uint16_t>, grid, dim3(256), 0, s, (const uint16_t*)X, n_tok, d_in,
-                           ld_x, perm, (uint16_t*)Xg, ld_g, nan16);
+                           ld_x, perm, (uint16_t*)Xg, ld_g, nan16, rows, chunk);
     }
     GPTQ_LAUNCH_CHECK();
     return GPTQ_OK;
@@ -1181,6 +1466,11 @@ gptq_status dequant_matmul_launch(const void* X, gptq_dtype dt, int64_t n_tok, i
         // many tokens in natural order: matrix cores (grid in x only)
         if (dt == GPTQ_BF16) return by_bits_mfma<Bf16>(a, bits, s);
         return by_bits_mfma<F16>(a, bits, s);
+    }
+    if (block_path && !perm && n_tok >= FW_MIN_TOKENS) {
+        // a few tokens in natural order: matrix cores, 32 rows x 32 tokens per workgroup
+        if (dt == GPTQ_BF16) return by_bits_mfma_few<Bf16>(a, bits, s);
+        return by_bits_mfma_few<F16>(a, bits, s);
     }
     // the grid's y dimension (token tiles) stays below 65536: larger token
     // counts go in several launches

@@ -54,7 +54,7 @@ def _stream_order(L, mode, group_size):
     return L.codes, np.arange(d_in) // gs, np.arange(d_in)
 
 
-MM_MIN_TOKENS = 128   # natural order, block route: the matrix-core route from this many tokens
+MM_MIN_TOKENS = 2     # natural order, block route: the matrix-core routes from this many tokens
 
 
 def _mfma_route(L, mode, group_size, dtype, bits):
@@ -71,12 +71,15 @@ def _bound(L, X64, mode, group_size, bits, dtype=None):
     mag = S * (c.astype(np.float64) + Z + 2.0 ** (bits + 1))
     A = np.abs(X64[:, a]) @ mag.T
     d_in = L.codes.shape[1]
-    if dtype is not None and _mfma_route(L, mode, group_size, dtype, bits):
-        # matrix cores: a group's products summed in float32 (<= glen roundings),
-        # its sum of x by v_dot2 (<= glen), two FMAs, one addition per group
+    dtype = L.dtype if dtype is None else dtype
+    if _mfma_route(L, mode, group_size, dtype, bits):
+        # matrix cores: a group's products summed in float32 (<= glen
+        # roundings), its sum of x by v_dot2 (<= glen), two FMAs, one addition
+        # per group; under 128 tokens a group may be cut in two parts (one
+        # more correction) and eight partial tiles are added at the end
         glen = group_size if 0 < group_size < d_in else d_in
         ng = -(-d_in // glen)
-        return (2 * glen + ng + 8) * U32 * A
+        return (2 * glen + ng + 16) * U32 * A
     nb = -(-(-(-d_in // 32)) // 256)
     return (96 + 32 * nb) * U32 * A
 
@@ -118,12 +121,12 @@ def _run(L, mode, bits, group_size, x_view=None):
 CASES = [
     # bits, dtype, mode, group_size, n_tok, d_out, d_in
     (4, "bf16", "perm", 128, 1, 72, 1000),      # block route, gather, ragged last block
-    (4, "bf16", "natural", 128, 5, 37, 4100),   # block route, 4-token tiles + 1, ragged rows
+    (4, "bf16", "natural", 128, 5, 37, 4100),   # few-token matrix cores, ragged rows and last block
     (3, "f16", "natural", 64, 1, 40, 777),      # 3-bit pairs, straddling codes
     (2, "bf16", "perm", 32, 3, 16, 2048),
     (8, "f16", "natural", -1, 2, 24, 513),      # 8-bit in f16 pairs, one group
     (3, "bf16", "perm", 96, 4, 48, 2000),
-    (4, "bf16", "natural", 128, 9, 64, 8192),   # aligned vector loads, 3 token tiles
+    (4, "bf16", "natural", 128, 9, 64, 8192),   # few-token matrix cores, aligned vector loads
     (4, "bf16", "perm", 128, 1, 64, 16384),     # two blocks per thread
     (8, "bf16", "natural", 128, 1, 16, 640),    # column route (8-bit codes, bf16)
     (4, "bf16", "g_idx", 128, 3, 33, 1500),     # column route, act-order original order
@@ -131,6 +134,16 @@ CASES = [
     (4, "f16", "natural", 25, 1, 19, 500),      # column route, group size not a multiple of 32
     (2, "f32", "perm", 16, 4, 8, 300),          # column route with the gather
     (4, "f16", "g_idx", 32, 2, 9, 33),          # tiny: one full block plus one column
+    # a few tokens in natural order: 32 rows x 32 tokens per workgroup, the
+    # row's blocks split over eight waves (groups cut between waves)
+    (4, "bf16", "natural", 128, 16, 4096, 11008 // 4),
+    (3, "f16", "natural", 64, 33, 70, 1000),        # two token tiles, ragged
+    (2, "bf16", "natural", -1, 31, 45, 700),        # one group per row, cut eight ways
+    (8, "f16", "natural", 32, 7, 33, 129),          # fewer blocks than waves
+    (4, "f16", "natural", 96, 127, 100, 1200),
+    (4, "bf16", "natural", 128, 2, 300, 4096 + 8),
+    (4, "bf16", "natural", 128, 50, 40, 1001),     # four 16-token tiles per workgroup, element-wise loads
+    (3, "bf16", "natural", 32, 20, 18, 515),       # two tiles, ragged
     # many tokens in natural order: the matrix-core route (128x128 tiles)
     (4, "bf16", "natural", 128, 300, 200, 1000),    # ragged token, row and column tiles
     (3, "f16", "natural", 64, 129, 130, 777),
@@ -262,9 +275,10 @@ def test_quantized_layer_product_end_to_end():
         assert np.all(np.abs(got.double().cpu().numpy() - want) <= 1e-5 * scale)
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
-def test_gather_columns_exact(dtype):
-    n_tok, d_in = 37, 5000      # two column chunks of 4096, ragged rows
+@pytest.mark.parametrize("dtype,n_tok", [("bf16", 37), ("f16", 37), ("f32", 37), ("bf16", 1030)])
+def test_gather_columns_exact(dtype, n_tok):
+    # 37 tokens: tiles of 4 rows x 512 columns; 1030: 16 rows x 4096; ragged both ways
+    d_in = 5000
     L = synth.make_packed_layer(4, d_in, n_tok, bits=4, group_size=128, dtype=dtype, seed=41)
     X = to_torch(L.X, dtype)
     perm = torch.from_numpy(L.perm).to(DEV)

@@ -153,6 +153,14 @@ def phase_rooflines(d_out, d_in, n_tok, bits, block, phases_ms, x_bytes=2):
     gbs = pack_bytes / (phases_ms["pack"] * 1e-3) / 1e9
     out["pack"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                    "frac": round(gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": pack_bytes}
+    # the column sweep's bytes: every weight's float64 running value read and
+    # its code byte written once (9 B per weight), over the whole quantize
+    # phase (the sweep kernels alone: the kernel statistics under profiles/)
+    sweep_bytes = 9.0 * d_out * d_in
+    gbs = sweep_bytes / (phases_ms["quantize_layer"] * 1e-3) / 1e9
+    out["column_sweep"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                           "frac": round(gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": sweep_bytes,
+                           "timed": "quantize_layer phase"}
     return out
 
 

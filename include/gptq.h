@@ -30,7 +30,7 @@
  *     return from validation no device memory has been touched.
  *   - The solver computes in float64 (codes are decided in float64, the
  *     precision of the reference oracle); the Hessian's token products are
- *     accumulated in float32 over chunks of tokens and summed in float64,
+ *     accumulated in float32 over runs of 256 tokens and summed in float64,
  *     and its diagonal in float64.
  *   - Calls that share a workspace must not overlap.
  */
@@ -97,17 +97,22 @@ void gptq_config_default(gptq_config* cfg);
  * read or written; the strict lower triangle is left untouched.  The caller
  * zeroes H before the first call; repeated calls over token chunks sum up.
  * X: n_tok x d_in of x_dtype with row stride ld_x elements (ld_x >= d_in).
- * Token products are exact in float32 for bf16/fp16 inputs and accumulated
- * in float32 over chunks of at most 32768 tokens (fewer when d_in > 16384),
- * then added to H in float64 in token order; the diagonal is summed in
- * float64 (per 512 tokens, then in order).  fp32 inputs are accumulated in
- * float64 throughout.  Deterministic (bit-reproducible).
+ * Token products are exact in float32 for bf16/fp16 inputs; they are summed
+ * in float32 over runs of 256 tokens, the runs in float64 over windows of
+ * up to 32768 tokens, and each window is added to H in float64 in token
+ * order (every entry within 32 * 2^-24 * 2 * sum_t |X[t][i] X[t][j]| of the
+ * exact sum); the diagonal is summed from exact float64 squares.  fp32
+ * inputs are accumulated in float64 throughout.  Deterministic
+ * (bit-reproducible).
  * NaN/Inf in X propagate into diag(H) and are reported by gptq_prepare_hinv.
- * workspace: gptq_hessian_workspace(n_tok, d_in) bytes (a transposed copy of
- * one token chunk and float64 column sums; two such slots when n_tok spans
- * more than one chunk, the next chunk being transposed while the current
- * one is multiplied; may be NULL for fp32 inputs or n_tok = 0).  Calls on
- * one workspace must not overlap.
+ * workspace: gptq_hessian_workspace(n_tok, d_in) bytes, which covers both
+ * uses (the query does not know X's alignment): float64 partial tiles of
+ * shorter windows when the layer has fewer than 256 tiles of 256 x 128
+ * (d_in below about 4000), and a zero-padded aligned copy of up to 64 MiB
+ * of tokens when the rows are not 16-byte aligned (d_in or ld_x not a
+ * multiple of 8, or X misaligned).  Aligned rows of a wide layer use none
+ * of it.  May be NULL for fp32 inputs or n_tok = 0.  Calls on one
+ * workspace must not overlap.
  * ------------------------------------------------------------------------ */
 size_t gptq_hessian_workspace(int64_t n_tok, int64_t d_in);
 gptq_status gptq_hessian_accumulate(double* H, const void* X, gptq_dtype x_dtype,
@@ -116,7 +121,8 @@ gptq_status gptq_hessian_accumulate(double* H, const void* X, gptq_dtype x_dtype
 
 /* Measurement variant of gptq_hessian_accumulate: the same kernels in the
  * same launch configuration on the same stream, with HIP events recorded
- * around each launch of the Hessian product kernel (one per token chunk).
+ * around each launch of the Hessian product kernel (up to one window of
+ * tiles per launch).
  * Synchronous.  On OK, *syrk_ms (host) holds the mean duration of those
  * launches in milliseconds and *n_launches (host) their number.  Returns
  * GPTQ_ERR_INVALID_ARG for null output pointers, otherwise as

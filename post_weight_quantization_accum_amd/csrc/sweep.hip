@@ -744,8 +744,6 @@ gptq_status sweep_launch(const void* W, gptq_dtype dt, int64_t d_out, int64_t d_
     }
     const unsigned grid = (unsigned)ceil_div(d_out, ROWS);
 #define SWEEP_ATTR(n, f) GPTQ_HIP(ensure_lds_limit((const void*)sweep_block_kernel<n, f, false>, (int)SWEEP_LDS));
-    SWEEP_ATTR(16, true)
-    SWEEP_ATTR(16, false)
     SWEEP_ATTR(8, true)
     SWEEP_ATTR(8, false)
     SWEEP_ATTR(4, true)
@@ -755,8 +753,8 @@ gptq_status sweep_launch(const void* W, gptq_dtype dt, int64_t d_out, int64_t d_
     SWEEP_ATTR(1, true)
     SWEEP_ATTR(1, false)
 #undef SWEEP_ATTR
-    GPTQ_HIP(ensure_lds_limit((const void*)sweep_block_kernel<16, true, true>, (int)SWEEP_LDS));
-    GPTQ_HIP(ensure_lds_limit((const void*)sweep_block_kernel<16, false, true>, (int)SWEEP_LDS));
+    GPTQ_HIP(ensure_lds_limit((const void*)sweep_block_kernel<CPL, true, true>, (int)SWEEP_LDS));
+    GPTQ_HIP(ensure_lds_limit((const void*)sweep_block_kernel<CPL, false, true>, (int)SWEEP_LDS));
     const int64_t S = superblock_cols(d_in, cfg);
     // A group that runs past the end of its superblock (groups wider than a
     // superblock, or superblocks of one block when lcm(B, g) exceeds the
@@ -784,10 +782,8 @@ gptq_status sweep_launch(const void* W, gptq_dtype dt, int64_t d_out, int64_t d_
                            zeros, w.loss64, w.gsw);                                                           \
         break;
 #define SWEEP_CASE(n, f) SWEEP_CASE_T(n, f, false, n * 2 + f)
-                SWEEP_CASE_T(16, true, true, -2)
-                SWEEP_CASE_T(16, false, true, -1)
-                SWEEP_CASE(16, 1)
-                SWEEP_CASE(16, 0)
+                SWEEP_CASE_T(CPL, true, true, -2)
+                SWEEP_CASE_T(CPL, false, true, -1)
                 SWEEP_CASE(8, 1)
                 SWEEP_CASE(8, 0)
                 SWEEP_CASE(4, 1)

@@ -202,6 +202,19 @@ def test_dequant_matmul_exact_on_integer_data(bits, dtype, mode, gs, d_in, n_tok
     assert np.array_equal(Y, ref)
 
 
+@pytest.mark.parametrize("n_tok", [16, 64])
+def test_dequant_matmul_headline_layer_few_tokens(n_tok):
+    # 4096 x 11008, 4-bit g128, natural order (static groups or no act-order):
+    # the few-token matrix-core route, every output compared
+    d_out, d_in, bits, gs = 4096, 11008, 4, 128
+    L = synth.make_packed_layer(d_out, d_in, n_tok, bits=bits, group_size=gs, dtype="bf16", seed=77 + n_tok)
+    Y, ref, X64 = _run(L, "natural", bits, gs)
+    err = np.abs(Y - ref)
+    tol = _bound(L, X64, "natural", gs, bits, "bf16")
+    assert np.all(err <= tol), f"max err/tol {np.max(err / tol):.3g}"
+    assert np.median(err / np.maximum(np.abs(ref), 1e-30)) < 1e-5
+
+
 def test_dequant_matmul_headline_layer_many_tokens():
     # 4096 x 11008, 4-bit g128, natural order, 512 tokens: the matrix-core route
     d_out, d_in, bits, gs, n_tok = 4096, 11008, 4, 128, 512

@@ -13,7 +13,7 @@ and the blocked sweep):
   reproduces the row), and after the replay the scales are within 1e-5
   relative and the zero points equal.
 Layers: workload 3's headline down projection (4096x11008, bf16, 4-bit g128
-act-order, 1024 sampled rows), workload 4's down projection (5120x13824, 3-
+act-order, 1024 sampled rows; and with static groups, 512 rows), workload 4's down projection (5120x13824, 3-
 and 2-bit g64 act-order, 512 sampled rows each) and workload 2 at its recipe
 (OPT-125m shapes 768x768, 3072x768 and 768x3072, fp16, 4-bit g128, every
 row).  Rows are independent given U, so a row sample is checked exactly as
@@ -40,9 +40,9 @@ def _oracle_hessian(L, chunk=16384):
     return O.hessian(synth.to_f64(L.X[t0:t0 + chunk], L.dtype) for t0 in range(0, n, chunk))
 
 
-def _gpu_quantize(L, q):
+def _gpu_quantize(L, q, static_groups=False):
     cfg = P.make_config(bits=q.bits, group_size=q.group_size, sym=q.sym, act_order=q.act_order, block=q.block,
-                        damp=q.damp)
+                        damp=q.damp, static_groups=static_groups)
     W = to_torch(L.W, L.dtype)
     X = to_torch(L.X, L.dtype)
     out = P.quantize(W, X=X, cfg=cfg)
@@ -63,14 +63,14 @@ def _layer(cfg_id, name):
     return wl, L
 
 
-def _check(L, H, got, q, name, rows=None):
+def _check(L, H, got, q, name, rows=None, static_groups=False):
     W64 = L.W_f64()
     if rows is not None:
         W64 = W64[rows]
         got = dict(got, codes=got["codes"][rows], scales=got["scales"][:, rows], zeros=got["zeros"][:, rows],
                    w_hat=got["w_hat"][rows])
     rp = assert_from_x_parity(O, W64, H, got, q.bits, q.group_size, q.act_order, sym=q.sym, block=q.block,
-                              damp=q.damp, name=name)
+                              damp=q.damp, name=name, static_groups=static_groups)
     assert rp["same_raw"] >= 0.999 and rp["maxdiff_raw"] <= 1, name
     assert abs(rp["loss_gpu"] - rp["loss_oracle"]) <= 1e-3 * rp["loss_oracle"], name
     return rp
@@ -87,6 +87,23 @@ def test_headline_down_from_x():
     print(f"  oracle Hessian over {L.X.shape[0]} tokens in {time.time() - t0:.1f} s", flush=True)
     rows = np.sort(np.random.default_rng(3).choice(L.W.shape[0], 1024, replace=False))
     _check(L, H, got, q, "workload 3 down 4096x11008 4-bit g128 act-order", rows=rows)
+
+
+@pytest.mark.timeout(900)
+def test_headline_down_static_groups_from_x():
+    """The headline layer with the static-groups option (groups of original
+    columns, parameters from W before the sweep, act-order sweep order)."""
+    cfg_id, name = HEADLINE
+    wl, L = _layer(cfg_id, name)
+    q = wl.quants[0]
+    got = _gpu_quantize(L, q, static_groups=True)
+    assert np.array_equal(got["g_idx"], np.arange(L.W.shape[1]) // q.group_size)
+    t0 = time.time()
+    H = _oracle_hessian(L)
+    print(f"  oracle Hessian over {L.X.shape[0]} tokens in {time.time() - t0:.1f} s", flush=True)
+    rows = np.sort(np.random.default_rng(5).choice(L.W.shape[0], 512, replace=False))
+    _check(L, H, got, q, "workload 3 down 4096x11008 4-bit g128 act-order, static groups", rows=rows,
+           static_groups=True)
 
 
 @pytest.mark.timeout(900)

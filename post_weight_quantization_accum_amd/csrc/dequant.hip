@@ -1306,9 +1306,229 @@ gptq_status launch_mfma_few_tt(const DqArgs& a, hipStream_t s) {
     return GPTQ_OK;
 }
 
-// 16 tokens per tile; up to 16: one tile, up to 32: two, more: four per workgroup
+// The same with whole 128-column super-blocks (4 blocks) per lane step,
+// when every group is made of whole super-blocks (group size a multiple of
+// 128, or one group per row): lane l holds, for super-block sb, row l % 16's
+// whole block 4 sb + l / 16 (one load of 4 b contiguous bytes, so the four
+// lanes of a row read 16 b contiguous bytes instead of four scattered
+// b-byte pieces) and token l % 16's 32 activations of that block. MFMA j
+// (j = 0..3) takes the lane's codes and activations 8j .. 8j + 7: its 32
+// K-values are columns 8j .. 8j + 7 of the four blocks, all in one group.
+template <int BITS, typename T, bool XV, int TT>
+__global__ __launch_bounds__(FW_THREADS) void dequant_mfma_few4_kernel(DqArgs a, int64_t n_rt, int64_t n_mt,
+                                                                       int64_t per_xcd) {
+    constexpr int DEPTH = TT >= 4 ? 1 : 2;   // super-blocks whose loads are in flight per wave
+    __shared__ float red[FW_WAVES - 1][TT][4][64];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t b = blockIdx.x;
+    const int64_t lin = (b % 8) * per_xcd + b / 8;
+    if (lin >= n_rt * n_mt) return;
+    const int64_t rt = lin / n_mt, mt = lin % n_mt;
+    const int64_t n0 = rt * 16, t0 = mt * 16 * TT;
+    const int li = lane & 15, q = lane >> 4;          // token / row, and the lane's block of a super-block
+    const uint32_t d_in = (uint32_t)a.d_in;
+    const uint32_t nkb = (uint32_t)ceil_div(a.d_in, 32);
+    const uint32_t nsb = (nkb + 3) / 4;
+    const uint32_t bpg = a.gsize >= a.d_in ? 4 * nsb : (uint32_t)(a.gsize >> 5);   // a multiple of 4
+    const uint32_t sb_lo = (uint32_t)((uint64_t)nsb * wave / FW_WAVES);
+    const uint32_t sb_hi = (uint32_t)((uint64_t)nsb * (wave + 1) / FW_WAVES);
+    constexpr float OFF = (float)(1 << BITS);
+
+    bool tok_ok[TT];
+    const uint16_t* xrow[TT];
+#pragma unroll
+    for (int t = 0; t < TT; ++t) {
+        const int64_t tok = t0 + 16 * t + li;
+        tok_ok[t] = tok < a.n_tok;
+        xrow[t] = (const uint16_t*)a.X + (tok_ok[t] ? tok : 0) * a.ld_x;
+    }
+    const __amdgpu_buffer_rsrc_t rs = words_rsrc(a, n0 < a.d_out ? n0 : a.d_out);
+    const uint32_t row_off = (uint32_t)li * (uint32_t)a.wpr * 4;   // rows past d_out: past the buffer's end
+    const int64_t row = n0 + li;
+    const bool row_ok = row < a.d_out;
+
+    // raw loads of super-block sb for this lane (unconditional, clamped;
+    // masked and decoded only when used, as in the block-wise kernel)
+    struct Ops {
+        u32x4_t x[TT][4];
+        uint32_t w[BITS];
+        float s, z;
+    };
+    auto load = [&](uint32_t sb, Ops& o) {
+        const uint32_t blk = 4 * sb + q;
+        const uint32_t k0 = 32 * blk;
+#pragma unroll
+        for (int t = 0; t < TT; ++t)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t k = k0 + 8 * j;
+                if constexpr (XV) {
+                    o.x[t][j] = *(const u32x4_t*)(xrow[t] + (k < d_in ? k : 0));
+                } else {
+                    uint32_t e[8];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) e[i] = xrow[t][k + i < d_in ? k + i : 0];
+                    o.x[t][j] = u32x4_t{e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16)};
+                }
+            }
+        const uint32_t off = row_off + blk * (uint32_t)(BITS * 4);
+        if constexpr (BITS == 2) {
+            const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0);
+            o.w[0] = v.x;
+            o.w[1] = v.y;
+        } else if constexpr (BITS == 3) {
+            const u32x3_t v = __builtin_amdgcn_raw_buffer_load_b96(rs, off, 0, 0);
+            o.w[0] = v.x;
+            o.w[1] = v.y;
+            o.w[2] = v.z;
+        } else {
+#pragma unroll
+            for (int u = 0; u < BITS; u += 4) {
+                const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rs, off + 4 * u, 0, 0);
+                o.w[u] = v.x;
+                o.w[u + 1] = v.y;
+                o.w[u + 2] = v.z;
+                o.w[u + 3] = v.w;
+            }
+        }
+        const int64_t idx = (int64_t)((4 * sb) / bpg) * a.d_out + (row_ok ? row : 0);
+        o.s = a.scales[idx];
+        o.z = a.zeros[idx];
+    };
+    // the lane's activations 8j .. 8j + 7 of its block (zeros past d_in or past the last token)
+    auto acts = [&](uint32_t sb, const Ops& o, int t, int j) -> u32x4_t {
+        const uint32_t k = 32 * (4 * sb + q) + 8 * j;
+        if constexpr (XV) {
+            return (tok_ok[t] && k < d_in) ? o.x[t][j] : u32x4_t{0u, 0u, 0u, 0u};
+        } else {
+            uint32_t m[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                m[i] = (tok_ok[t] && k + 2 * i < d_in ? 0x0000FFFFu : 0u) |
+                       (tok_ok[t] && k + 2 * i + 1 < d_in ? 0xFFFF0000u : 0u);
+            return u32x4_t{o.x[t][j].x & m[0], o.x[t][j].y & m[1], o.x[t][j].z & m[2], o.x[t][j].w & m[3]};
+        }
+    };
+    // the 64-bit window whose low bits hold codes 8j .. 8j + 7 of the lane's block
+    auto window = [&](const Ops& o, int j) -> uint64_t {
+        const int bit = BITS * 8 * j, wi = bit >> 5, sh = bit & 31;
+        const uint64_t lo = o.w[wi];
+        const uint64_t hi = (wi + 1 < BITS) ? (uint64_t)o.w[wi + 1 < BITS ? wi + 1 : wi] : 0u;
+        return ((hi << 32) | lo) >> sh;
+    };
+
+    f4_t acc[TT], accg[TT];
+    float xpart[TT];
+#pragma unroll
+    for (int t = 0; t < TT; ++t) {
+        acc[t] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        accg[t] = acc[t];
+        xpart[t] = 0.0f;
+    }
+    float sv = 0.0f, ov = 0.0f;
+    auto close_group = [&]() {
+#pragma unroll
+        for (int t = 0; t < TT; ++t) {
+            float xt = xpart[t] + __shfl_xor(xpart[t], 16, 64);
+            xt += __shfl_xor(xt, 32, 64);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float x = __shfl(xt, 4 * q + r, 64);
+                acc[t][r] = fmaf(sv, fmaf(-ov, x, accg[t][r]), acc[t][r]);
+            }
+        }
+    };
+
+    Ops ring[DEPTH];
+    const uint32_t sb_last = sb_hi > sb_lo ? sb_hi - 1 : sb_lo;
+#pragma unroll
+    for (int p = 0; p < DEPTH; ++p) load(sb_lo + p < sb_hi ? sb_lo + p : sb_last, ring[p]);
+    bool open = false;
+    for (uint32_t sb0 = sb_lo; sb0 < sb_hi; sb0 += DEPTH) {
+#pragma unroll
+        for (int p = 0; p < DEPTH; ++p) {
+            const uint32_t sb = sb0 + p;
+            if (sb < sb_hi) {
+                if (sb == sb_lo || (4 * sb) % bpg == 0) {
+                    if (open) close_group();
+                    sv = row_ok ? ring[p].s : 0.0f;
+                    ov = OFF + (row_ok ? ring[p].z : 0.0f);
+                    open = true;
+#pragma unroll
+                    for (int t = 0; t < TT; ++t) {
+                        xpart[t] = 0.0f;
+                        accg[t] = f4_t{0.0f, 0.0f, 0.0f, 0.0f};
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const u32x4_t bop = codes8_operand<BITS, T>(window(ring[p], j));
+#pragma unroll
+                    for (int t = 0; t < TT; ++t) {
+                        const u32x4_t xa = acts(sb, ring[p], t, j);
+                        accg[t] = mfma_16x16x32(xa, bop, accg[t], (typename T::mfma_tag*)nullptr);
+                        float x = T::dot2(xa.x, T::ONES, xpart[t]);
+                        x = T::dot2(xa.y, T::ONES, x);
+                        x = T::dot2(xa.z, T::ONES, x);
+                        xpart[t] = T::dot2(xa.w, T::ONES, x);
+                    }
+                }
+            }
+            load(sb + DEPTH < sb_hi ? sb + DEPTH : sb_last, ring[p]);
+        }
+    }
+    if (open) close_group();
+
+    if (wave > 0) {
+#pragma unroll
+        for (int t = 0; t < TT; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) red[wave - 1][t][r][lane] = acc[t][r];
+    }
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+        for (int t = 0; t < TT; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float y = acc[t][r];
+#pragma unroll
+                for (int w = 0; w < FW_WAVES - 1; ++w) y += red[w][t][r][lane];
+                const int64_t tk = t0 + 16 * t + 4 * q + r;
+                if (tk < a.n_tok && row_ok) a.Y[tk * a.ld_y + row] = y;
+            }
+    }
+}
+
+template <int BITS, typename T, int TT>
+gptq_status launch_mfma_few4_tt(const DqArgs& a, hipStream_t s) {
+    const int64_t n_rt = ceil_div(a.d_out, 16), n_mt = ceil_div(a.n_tok, 16 * TT);
+    const int64_t per_xcd = ceil_div(n_rt * n_mt, 8);
+    if (per_xcd * 8 > INT32_MAX) return GPTQ_ERR_UNSUPPORTED;
+    const dim3 grid((unsigned)(per_xcd * 8)), block(FW_THREADS);
+    if (a.xvec && a.d_in % 8 == 0)
+        hipLaunchKernelGGL((dequant_mfma_few4_kernel<BITS, T, true, TT>), grid, block, 0, s, a, n_rt, n_mt, per_xcd);
+    else
+        hipLaunchKernelGGL((dequant_mfma_few4_kernel<BITS, T, false, TT>), grid, block, 0, s, a, n_rt, n_mt, per_xcd);
+    GPTQ_LAUNCH_CHECK();
+    return GPTQ_OK;
+}
+
+#ifndef GPTQ_FEW4
+#define GPTQ_FEW4 1
+#endif
+// 16 tokens per tile; up to 16: one tile, up to 32: two, more: four per
+// workgroup.  Groups of whole 128-column super-blocks take the super-block
+// kernel.
 template <int BITS, typename T>
 gptq_status launch_mfma_few(const DqArgs& a, hipStream_t s) {
+    const bool whole = a.gsize >= a.d_in || a.gsize % 128 == 0;
+    if (GPTQ_FEW4 && whole) {
+        if (a.n_tok <= 16) return launch_mfma_few4_tt<BITS, T, 1>(a, s);
+        if (a.n_tok <= 32) return launch_mfma_few4_tt<BITS, T, 2>(a, s);
+        return launch_mfma_few4_tt<BITS, T, 4>(a, s);
+    }
     if (a.n_tok <= 16) return launch_mfma_few_tt<BITS, T, 1>(a, s);
     if (a.n_tok <= 32) return launch_mfma_few_tt<BITS, T, 2>(a, s);
     return launch_mfma_few_tt<BITS, T, 4>(a, s);

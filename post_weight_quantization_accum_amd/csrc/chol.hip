@@ -558,6 +558,17 @@ __global__ __launch_bounds__(256) void rotate_inplace_kernel(double* M, int64_t 
 // has its own L21 scratch, so the recursion below cannot overwrite the
 // operand of a T still in flight; the events of a depth are reused only
 // after the main stream has waited for that depth's previous T.
+//
+// A T product launched with one workgroup per tile would fill every CU and
+// keep workgroups queued until it drains; the leaves and small products
+// that the main stream launches meanwhile then wait behind them (a leaf
+// needs most of a CU's LDS).  T therefore runs with fewer workgroups than
+// CUs, each looping over tiles, and CUs stay free for the main stream.
+#ifndef GPTQ_T_FREE
+#define GPTQ_T_FREE 8
+#endif
+constexpr int T_FREE = GPTQ_T_FREE;   // CUs left to the main stream
+
 struct Rec {
     hipStream_t s = nullptr, side = nullptr;
     double* L = nullptr;    // Hr, lower; T blocks replace A21 blocks
@@ -566,10 +577,16 @@ struct Rec {
     int64_t d = 0;
     int* flags = nullptr;
     hipEvent_t l21_ready[MAX_DEPTH] = {}, t_done[MAX_DEPTH] = {};
+    int64_t t_wg = 0;   // workgroups of a T product
     // created on first use: factors of at most 1024 columns never need them
     hipError_t init() {
         if (side) return hipSuccess;
-        hipError_t e = hipStreamCreateWithFlags(&side, hipStreamNonBlocking);
+        int dev = 0, n_cu = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e == hipSuccess) e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        t_wg = n_cu - T_FREE >= 64 ? n_cu - T_FREE : 0;
+        e = hipStreamCreateWithFlags(&side, hipStreamNonBlocking);
         for (int k = 0; k < MAX_DEPTH && e == hipSuccess; ++k) {
             e = hipEventCreateWithFlags(&l21_ready[k], hipEventDisableTiming);
             if (e == hipSuccess) e = hipEventCreateWithFlags(&t_done[k], hipEventDisableTiming);
@@ -627,7 +644,8 @@ gptq_status chol_inv(Rec& c, int64_t o, int64_t n, int depth) {
     GPTQ_HIP(c.init());
     GPTQ_HIP(hipEventRecord(c.l21_ready[depth], c.s));
     GPTQ_HIP(hipStreamWaitEvent(c.side, c.l21_ready[depth], 0));
-    st = launch_gemm_f64(c.side, n2, n1, n1, 1.0, L21, n1, M11, d, false, 0.0, A21, d, false, GEMM_TRI_KBEG_COL);
+    st = launch_gemm_f64(c.side, n2, n1, n1, 1.0, L21, n1, M11, d, false, 0.0, A21, d, false, GEMM_TRI_KBEG_COL,
+                         false, c.t_wg);
     if (st != GPTQ_OK) return st;
     GPTQ_HIP(hipEventRecord(c.t_done[depth], c.side));
     st = chol_inv(c, o + n1, n2, depth + 1);

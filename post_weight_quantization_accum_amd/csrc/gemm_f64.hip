@@ -109,21 +109,17 @@ __device__ __forceinline__ void store_kcols(double (*lds)[Cfg<TILE>::LD], const 
     for (int i = 0; i < EPT; ++i) lds[k][n + i] = v[i];
 }
 
+// Tile of virtual workgroup b (the mapping below assumes that b % 8 is the
+// XCD the workgroup runs on, which holds for any grid of a multiple of 8
+// workgroups looping over b = blockIdx.x + i * gridDim.x).
 template <int TILE, bool TRANS_B, bool LOWER, bool VEC>
-__global__ __launch_bounds__(256, 2) void gemm_f64_kernel(int64_t M, int64_t N, int64_t K, double alpha,
-                                                          const double* __restrict__ A, int64_t lda,
-                                                          const double* __restrict__ B, int64_t ldb,
-                                                          double beta, double* C, int64_t ldc,
-                                                          int64_t tiles_m, int64_t tiles_n, int64_t n_tiles,
-                                                          int64_t per_xcd, int tri, int prio) {
+__device__ __forceinline__ void gemm_tile(int64_t M, int64_t N, int64_t K, double alpha,
+                                          const double* __restrict__ A, int64_t lda,
+                                          const double* __restrict__ B, int64_t ldb, double beta, double* C,
+                                          int64_t ldc, int64_t tiles_m, int64_t tiles_n, int64_t n_tiles,
+                                          int64_t per_xcd, int tri, const int64_t b,
+                                          double (&sA)[2][KC][Cfg<TILE>::LD], double (&sB)[2][KC][Cfg<TILE>::LD]) {
     using G = Cfg<TILE>;
-    __shared__ double sA[2][KC][G::LD];
-    // prio: issue priority over the waves of a one-per-CU launch (the far
-    // lazy update on a second stream, which shares every CU with this one)
-    if (prio) __builtin_amdgcn_s_setprio(2);
-    __shared__ double sB[2][KC][G::LD];
-
-    const int64_t b = blockIdx.x;
     int64_t tm, tn;
     if (LOWER) {
         const int64_t lin = (b % 8) * per_xcd + b / 8;
@@ -273,6 +269,28 @@ __global__ __launch_bounds__(256, 2) void gemm_f64_kernel(int64_t M, int64_t N, 
     }
 }
 
+// n_virtual: the tile enumeration's workgroup count; a smaller grid (a
+// multiple of 8) loops over it, so that the launch holds at most that many
+// workgroups at any time.  The last LDS access of a tile is followed by a
+// barrier, and the epilogue uses no LDS, so the next tile may refill it.
+template <int TILE, bool TRANS_B, bool LOWER, bool VEC>
+__global__ __launch_bounds__(256, 2) void gemm_f64_kernel(int64_t M, int64_t N, int64_t K, double alpha,
+                                                          const double* __restrict__ A, int64_t lda,
+                                                          const double* __restrict__ B, int64_t ldb,
+                                                          double beta, double* C, int64_t ldc,
+                                                          int64_t tiles_m, int64_t tiles_n, int64_t n_tiles,
+                                                          int64_t per_xcd, int tri, int prio, int64_t n_virtual) {
+    using G = Cfg<TILE>;
+    __shared__ double sA[2][KC][G::LD];
+    __shared__ double sB[2][KC][G::LD];
+    // prio: issue priority over the waves of a one-per-CU launch (the far
+    // lazy update on a second stream, which shares every CU with this one)
+    if (prio) __builtin_amdgcn_s_setprio(2);
+    for (int64_t b = blockIdx.x; b < n_virtual; b += gridDim.x)
+        gemm_tile<TILE, TRANS_B, LOWER, VEC>(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, tiles_m, tiles_n, n_tiles,
+                                             per_xcd, tri, b, sA, sB);
+}
+
 // Small products (M, N <= SMALL_MN: the lower levels of the recursive
 // factorisation): one wave per 16x16 tile of C, operands straight from
 // memory (L2) into MFMA registers, 64 values of K per group with the next
@@ -394,36 +412,42 @@ constexpr size_t CU_LDS = 160 * 1024;
 
 template <int TILE, bool TRANS_B, bool LOWER>
 void launch_t(hipStream_t s, bool vec, int64_t M, int64_t N, int64_t K, double alpha, const double* A, int64_t lda,
-              const double* B, int64_t ldb, double beta, double* C, int64_t ldc, int tri, bool one_per_cu) {
+              const double* B, int64_t ldb, double beta, double* C, int64_t ldc, int tri, bool one_per_cu,
+              int64_t max_wg) {
     const int64_t tiles_m = ceil_div(M, TILE), tiles_n = ceil_div(N, TILE);
     const int64_t n_tiles = LOWER ? tiles_m * (tiles_m + 1) / 2 : tiles_m * tiles_n;
     // per XCD: whole bands plus at most one leftover tile per column (triangular case)
     const int64_t per_xcd = (!LOWER && tri != GEMM_TRI_NONE && tiles_m >= 16) ? (tiles_m / 8 + 1) * tiles_n
                                                                               : ceil_div(n_tiles, 8);
-    const dim3 grid((unsigned)(per_xcd * 8));
+    const int64_t n_virtual = per_xcd * 8;
+    const int64_t bounded = (max_wg / 8) * 8;
+    const dim3 grid((unsigned)((bounded > 0 && bounded < n_virtual) ? bounded : n_virtual));
     // one_per_cu: unused dynamic LDS beyond half a CU's, so that a second
     // workgroup of this launch never shares the CU (room for other streams)
     constexpr size_t static_lds = 2 * 2 * KC * Cfg<TILE>::LD * sizeof(double);
     const size_t pad = one_per_cu ? CU_LDS / 2 + 1024 - static_lds : 0;
     if (vec)
         hipLaunchKernelGGL((gemm_f64_kernel<TILE, TRANS_B, LOWER, true>), grid, dim3(256), pad, s, M, N, K, alpha,
-                           A, lda, B, ldb, beta, C, ldc, tiles_m, tiles_n, n_tiles, per_xcd, tri, one_per_cu ? 0 : 1);
+                           A, lda, B, ldb, beta, C, ldc, tiles_m, tiles_n, n_tiles, per_xcd, tri, one_per_cu ? 0 : 1,
+                           n_virtual);
     else
         hipLaunchKernelGGL((gemm_f64_kernel<TILE, TRANS_B, LOWER, false>), grid, dim3(256), pad, s, M, N, K, alpha,
-                           A, lda, B, ldb, beta, C, ldc, tiles_m, tiles_n, n_tiles, per_xcd, tri, one_per_cu ? 0 : 1);
+                           A, lda, B, ldb, beta, C, ldc, tiles_m, tiles_n, n_tiles, per_xcd, tri, one_per_cu ? 0 : 1,
+                           n_virtual);
 }
 
 template <bool TRANS_B, bool LOWER>
 void launch_sel(hipStream_t s, bool vec, int64_t M, int64_t N, int64_t K, double alpha, const double* A, int64_t lda,
-                const double* B, int64_t ldb, double beta, double* C, int64_t ldc, int tri, bool one_per_cu) {
+                const double* B, int64_t ldb, double beta, double* C, int64_t ldc, int tri, bool one_per_cu,
+                int64_t max_wg) {
     // 128x128 tiles when there are enough of them to fill the chip twice,
     // else 64x64 tiles (4x the workgroups)
     const int64_t tm = ceil_div(M, 128), tn = ceil_div(N, 128);
     const int64_t t128 = LOWER ? tm * (tm + 1) / 2 : tm * tn;
     if (t128 >= 512)
-        launch_t<128, TRANS_B, LOWER>(s, vec, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, tri, one_per_cu);
+        launch_t<128, TRANS_B, LOWER>(s, vec, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, tri, one_per_cu, max_wg);
     else
-        launch_t<64, TRANS_B, LOWER>(s, vec, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, tri, one_per_cu);
+        launch_t<64, TRANS_B, LOWER>(s, vec, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, tri, one_per_cu, max_wg);
 }
 
 }  // namespace
@@ -431,7 +455,7 @@ void launch_sel(hipStream_t s, bool vec, int64_t M, int64_t N, int64_t K, double
 gptq_status launch_gemm_f64(hipStream_t s, int64_t M, int64_t N, int64_t K, double alpha,
                             const double* A, int64_t lda, const double* B, int64_t ldb,
                             bool transB, double beta, double* C, int64_t ldc, bool lower_tiles, GemmTri tri,
-                            bool one_per_cu) {
+                            bool one_per_cu, int64_t max_wg) {
     if (M <= 0 || N <= 0) return GPTQ_OK;
     if (lower_tiles && tri != GEMM_TRI_NONE) return GPTQ_ERR_INVALID_ARG;
     if (K <= 0) {
@@ -453,14 +477,14 @@ gptq_status launch_gemm_f64(hipStream_t s, int64_t M, int64_t N, int64_t K, doub
     const bool vec = ((uintptr_t)A % 16 == 0) && (lda % 2 == 0) && ((uintptr_t)B % 16 == 0) && (ldb % 2 == 0);
     if (transB) {
         if (lower_tiles)
-            launch_sel<true, true>(s, vec, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, (int)tri, one_per_cu);
+            launch_sel<true, true>(s, vec, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, (int)tri, one_per_cu, max_wg);
         else
-            launch_sel<true, false>(s, vec, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, (int)tri, one_per_cu);
+            launch_sel<true, false>(s, vec, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, (int)tri, one_per_cu, max_wg);
     } else {
         if (lower_tiles)
-            launch_sel<false, true>(s, vec, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, (int)tri, one_per_cu);
+            launch_sel<false, true>(s, vec, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, (int)tri, one_per_cu, max_wg);
         else
-            launch_sel<false, false>(s, vec, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, (int)tri, one_per_cu);
+            launch_sel<false, false>(s, vec, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, (int)tri, one_per_cu, max_wg);
     }
     GPTQ_LAUNCH_CHECK();
     return GPTQ_OK;

@@ -27,10 +27,15 @@ enum GemmTri : int { GEMM_TRI_NONE = 0, GEMM_TRI_KEND_ROW = 1, GEMM_TRI_KEND_COL
 // B): each tile reads all of K before it writes.
 // one_per_cu: at most one workgroup of this launch per CU, which leaves
 // registers and LDS on every CU to kernels of other streams.
+// max_wg > 0 (products with M or N above 512): at most that many workgroups
+// (rounded down to a multiple of 8), each looping over several tiles, so
+// that the launch never holds workgroups waiting for a CU: work that other
+// streams launch meanwhile is dispatched at once instead of queueing behind
+// them.
 gptq_status launch_gemm_f64(hipStream_t s, int64_t M, int64_t N, int64_t K, double alpha,
                             const double* A, int64_t lda, const double* B, int64_t ldb,
                             bool transB, double beta, double* C, int64_t ldc, bool lower_tiles,
-                            GemmTri tri = GEMM_TRI_NONE, bool one_per_cu = false);
+                            GemmTri tri = GEMM_TRI_NONE, bool one_per_cu = false, int64_t max_wg = 0);
 
 // Two independent small products (both with M, N <= 512) in one launch:
 // x a symmetric update (lower_tiles, transB, no triangular range), y a plain

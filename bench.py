@@ -129,12 +129,33 @@ def cpu_baseline(layer_w, layer_x, d_out, d_in, n_tok, q):
     }
 
 
-def phase_rooflines(d_out, d_in, n_tok, bits, block, phases_ms, x_bytes=2):
+def factored_prepare_flops(d, leaf=128):
+    """Flops of the factored form's preparation: the recursion of the
+    Cholesky factorisation with the inverse products only where a parent
+    reads them (left children), plus the products R[K_k, K_l] U_ll (K = 128
+    each, taken whole)."""
+    def rec(n, need_m):
+        if n <= leaf:
+            return 2.0 / 3.0 * n ** 3
+        nb = -(-n // leaf)
+        n1 = leaf * ((nb + 1) // 2)
+        n2 = n - n1
+        f = rec(n1, True) + n2 * n1 * n1 + n2 * n2 * n1   # L21 (triangular operand), Schur update (half)
+        if need_m:
+            f += n2 * n1 * n1 + n2 * n2 * n1                # T, M21
+        return f + rec(n2, need_m)
+    nb = d // leaf
+    return rec(float(d), False) + nb * (nb - 1) / 2 * 2.0 * leaf ** 3
+
+
+def phase_rooflines(d_out, d_in, n_tok, bits, block, phases_ms, x_bytes=2, factored=False):
     """Each phase's algorithmic work over its measured time, against the peak
     that bounds it (the solver runs in float64: its phases are priced at the
     float64 peak)."""
     h_flops = float(n_tok) * d_in * (d_in + 1)
-    chol_flops = 2.0 / 3.0 * float(d_in) ** 3              # Cholesky + triangular inverse
+    # Cholesky + triangular inverse; the factored form skips the inverse
+    # products that nothing reads
+    chol_flops = factored_prepare_flops(d_in) if factored else 2.0 / 3.0 * float(d_in) ** 3
     lazy = 0.0
     for i1 in range(0, d_in, block):
         i2 = min(i1 + block, d_in)
@@ -346,9 +367,15 @@ def shapes_main(a):
                     H.zero_()
                     P.hessian_accumulate(H, X)
                     ev[1].record()
-                    perm = P.prepare_hinv(H, cfg)
-                    ev[2].record()
-                    out = P.quantize_layer(W, H, perm, cfg, want_w_hat=False, want_row_loss=False)
+                    fac = P.factored_supported(d_out, d_in, cfg)
+                    if fac:
+                        perm = P.prepare_hinv_factored(H, cfg)
+                        ev[2].record()
+                        out = P.quantize_layer_factored(W, H, perm, cfg, want_w_hat=False, want_row_loss=False)
+                    else:
+                        perm = P.prepare_hinv(H, cfg)
+                        ev[2].record()
+                        out = P.quantize_layer(W, H, perm, cfg, want_w_hat=False, want_row_loss=False)
                     ev[3].record()
                     P.pack(out["codes"], q.bits)
                     ev[4].record()
@@ -364,8 +391,10 @@ def shapes_main(a):
                              "solver_only_ms": round(total - ph["hessian"], 3),
                              "phases_ms": {k: round(v, 3) for k, v in ph.items()},
                              "weights_per_s": d_out * d_in / (total * 1e-3),
+                             "hinv_form": "factored" if fac else "U",
                              "phase_roofline": phase_rooflines(d_out, d_in, wl.n_tok, q.bits, q.block, ph,
-                                                               x_bytes=4 if wl.dtype == "f32" else 2)})
+                                                               x_bytes=4 if wl.dtype == "f32" else 2,
+                                                               factored=fac)})
                 log(f"  {total:.2f} ms (H {ph['hessian']:.2f}, prepare {ph['prepare_hinv']:.2f}, "
                     f"quantize {ph['quantize_layer']:.2f}, pack {ph['pack']:.3f})")
                 del X, W, H, out, perm
@@ -465,9 +494,15 @@ def main():
     import ctypes
     H = torch.empty((d_in, d_in), dtype=torch.float64, device=dev)
     perm = torch.empty(d_in, dtype=torch.int32, device=dev)
-    ws_h = torch.empty(lib.gptq_prepare_hinv_workspace(d_in), dtype=torch.uint8, device=dev)
-    ws_q = torch.empty(lib.gptq_quantize_layer_workspace(d_out, d_in, ctypes.byref(cfg)), dtype=torch.uint8,
-                       device=dev)
+    # the factored form of the inverse's factor where the shape allows it
+    # (the headline layer does), else U
+    factored = P.factored_supported(d_out, d_in, cfg)
+    prep, quant = ((P.prepare_hinv_factored, P.quantize_layer_factored) if factored
+                   else (P.prepare_hinv, P.quantize_layer))
+    ws_h = torch.empty((lib.gptq_prepare_hinv_factored_workspace if factored else lib.gptq_prepare_hinv_workspace)(d_in),
+                       dtype=torch.uint8, device=dev)
+    ws_q = torch.empty((lib.gptq_quantize_layer_factored_workspace if factored else lib.gptq_quantize_layer_workspace)(
+        d_out, d_in, ctypes.byref(cfg)), dtype=torch.uint8, device=dev)
     ng = P.n_groups(d_in, q.group_size)
     out = dict(codes=torch.empty((d_out, d_in), dtype=torch.uint8, device=dev),
                scales=torch.empty((ng, d_out), dtype=torch.float32, device=dev),
@@ -485,10 +520,10 @@ def main():
         P.hessian_accumulate(H, X)
         if record:
             ev[1].record(stream)
-        P.prepare_hinv(H, cfg, perm=perm, workspace=ws_h)
+        prep(H, cfg, perm=perm, workspace=ws_h)
         if record:
             ev[2].record(stream)
-        P.quantize_layer(W, H, perm, cfg, workspace=ws_q, out=out)
+        quant(W, H, perm, cfg, workspace=ws_q, out=out)
         if record:
             ev[3].record(stream)
         P.pack(out["codes"], q.bits, out=packed)
@@ -550,10 +585,11 @@ def main():
                                f"{wl.outlier_frac * 100:g}% outlier channels x{wl.outlier_scale:g}; {q.bits}-bit "
                                f"asym g{q.group_size} act-order B{q.block} damp {q.damp}",
                    "d_out": d_out, "d_in": d_in, "tokens": n_tok, "bits": q.bits, "group_size": q.group_size,
-                   "act_order": bool(q.act_order), "parallelism": "single GPU"},
+                   "act_order": bool(q.act_order), "parallelism": "single GPU",
+                   "hinv_form": "factored" if factored else "U"},
         "phases_ms": {k: round(v, 3) for k, v in phases.items()},
         "solver_only_ms": round(phases["prepare_hinv"] + phases["quantize_layer"] + phases["pack"], 3),
-        "phase_roofline": phase_rooflines(d_out, d_in, n_tok, q.bits, q.block, phases),
+        "phase_roofline": phase_rooflines(d_out, d_in, n_tok, q.bits, q.block, phases, factored=factored),
         "roofline": roofline,
     }
     log(f"timed {a.steps} steps: {ms_per_step:.2f} ms/step; phases {res['phases_ms']}")

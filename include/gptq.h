@@ -218,6 +218,52 @@ gptq_status gptq_quantize_layer(const void* W, gptq_dtype w_dtype, int64_t d_out
                                 void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Steps 2-3 in factored form: the same quantization without forming the
+ * off-diagonal blocks of U ("GPTQ量化算法深度解析" §2.2 compensation, §2.4
+ * lazy batch updates, §3.1 steps 2-3).
+ *
+ * With R = U^{-1} (upper; H_d = R R^T, the Cholesky factorisation of the
+ * index-reversed matrix that gptq_prepare_hinv also computes), E the scaled
+ * errors of the sweep and Q the quantized weights, the sweep satisfies
+ * W0 - Q = E U (W0: the weights before the sweep, in sweep order).  For the
+ * 128-column blocks K_k, the compensation that block l receives from the
+ * earlier blocks, E[:, <l] U[<l, K_l], then equals
+ *   -(W0 - Q)[:, <l] R[<l, K_l] U_ll,   U_ll = U[K_l, K_l] = R_ll^{-1},
+ * so the lazy update after block k is W[:, K_l] += (W0 - Q)[:, K_k] F[K_k, K_l]
+ * with F[K_k, K_l] = R[K_k, K_l] U_ll, and the sweep inside a block uses U_ll
+ * as before.  Only the inverses of R's diagonal blocks are formed: the
+ * factorisation skips the inverse products that nothing reads (the
+ * off-diagonal blocks of U), about 40 % of its flops.
+ *
+ * gptq_prepare_hinv_factored: as gptq_prepare_hinv (same inputs, perm and
+ * errors) but on OK H holds F (row stride d_in, sweep order): the diagonal
+ * 128 x 128 blocks are those of U, the blocks above them R[K_k, K_l] U_ll,
+ * the strict lower triangle zero.  d_in must be a multiple of 128
+ * (GPTQ_ERR_UNSUPPORTED otherwise).  workspace:
+ * gptq_prepare_hinv_factored_workspace(d_in) bytes (0 when unsupported).
+ *
+ * gptq_quantize_layer_factored: as gptq_quantize_layer (same arguments and
+ * outputs, equal to those given U up to float64 rounding) with F in U's
+ * place.  Needs cfg->block_size == 128 and every group inside one block:
+ * static_groups, or group_size <= 0 or >= d_in (one group per row, a
+ * multiple of 8), or a divisor of 128 that is a multiple of 8; otherwise
+ * GPTQ_ERR_UNSUPPORTED.  workspace:
+ * gptq_quantize_layer_factored_workspace(d_out, d_in, cfg) bytes (that of
+ * gptq_quantize_layer plus a float64 copy of W; 0 when unsupported).
+ * ------------------------------------------------------------------------ */
+size_t gptq_prepare_hinv_factored_workspace(int64_t d_in);
+gptq_status gptq_prepare_hinv_factored(double* H, int64_t d_in, const gptq_config* cfg,
+                                       int32_t* perm, void* workspace, size_t ws_bytes,
+                                       hipStream_t stream);
+size_t gptq_quantize_layer_factored_workspace(int64_t d_out, int64_t d_in, const gptq_config* cfg);
+gptq_status gptq_quantize_layer_factored(const void* W, gptq_dtype w_dtype, int64_t d_out,
+                                         int64_t d_in, int64_t ld_w, const double* F,
+                                         const int32_t* perm, const gptq_config* cfg,
+                                         uint8_t* codes, float* scales, float* zeros,
+                                         int32_t* g_idx, float* w_hat, double* row_loss,
+                                         void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Step 4 -- packing ("gptq-for-llama" article, "工程细节").
  *
  * Per row, code k occupies bits [bits*k, bits*k + bits) of a little-endian

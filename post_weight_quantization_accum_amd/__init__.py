@@ -19,7 +19,7 @@ from ._lib import (  # noqa: F401
     Unsupported, WorkspaceError, make_config, load, version, status_string,
 )
 
-__all__ = ["hessian_accumulate", "hessian_accumulate_timed", "hessian_accumulate_noalloc", "prepare_hinv", "quantize_layer", "pack", "quantize",
+__all__ = ["hessian_accumulate", "hessian_accumulate_timed", "hessian_accumulate_noalloc", "prepare_hinv", "quantize_layer", "prepare_hinv_factored", "quantize_layer_factored", "factored_supported", "pack", "quantize",
            "pack_permuted", "dequant_matmul", "dequant_max_groups", "gather_columns", "packed_words_per_row", "make_config",
            "Config", "load"]
 
@@ -135,23 +135,32 @@ def hessian_accumulate_noalloc(H, X, stream=None):
     return H
 
 
-def prepare_hinv(H, cfg: Config, perm=None, workspace=None, stream=None):
-    """In place H -> U (upper Cholesky factor of the damped, permuted inverse); returns perm."""
+def _prepare(name, H, cfg, perm, workspace, stream):
     lib = load()
     torch = _torch()
     _require_cuda(H)
     if H.dtype != torch.float64 or not H.is_contiguous() or H.dim() != 2 or H.shape[0] != H.shape[1]:
         raise TypeError("H must be a square contiguous float64 tensor")
     d = H.shape[0]
-    nws = lib.gptq_prepare_hinv_workspace(d)
+    nws = getattr(lib, name + "_workspace")(d)
     with _alloc_on(stream):
         if perm is None:
             perm = torch.empty(d, dtype=torch.int32, device=H.device)
         ws = workspace if workspace is not None else _workspace(nws, H.device)
-    st = lib.gptq_prepare_hinv(_ptr(H), d, ctypes.byref(cfg), _ptr(perm), _ptr(ws),
-                               ws.numel() if ws is not None else 0, _stream(stream))
-    _lib.check(st, "gptq_prepare_hinv")
+    st = getattr(lib, name)(_ptr(H), d, ctypes.byref(cfg), _ptr(perm), _ptr(ws),
+                            ws.numel() if ws is not None else 0, _stream(stream))
+    _lib.check(st, name)
     return perm
+
+
+def prepare_hinv(H, cfg: Config, perm=None, workspace=None, stream=None):
+    """In place H -> U (upper Cholesky factor of the damped, permuted inverse); returns perm."""
+    return _prepare("gptq_prepare_hinv", H, cfg, perm, workspace, stream)
+
+
+def prepare_hinv_factored(H, cfg: Config, perm=None, workspace=None, stream=None):
+    """In place H -> F, the factored form read by quantize_layer_factored (d_in a multiple of 128); returns perm."""
+    return _prepare("gptq_prepare_hinv_factored", H, cfg, perm, workspace, stream)
 
 
 def n_groups(d_in: int, group_size: int) -> int:
@@ -161,6 +170,17 @@ def n_groups(d_in: int, group_size: int) -> int:
 def quantize_layer(W, U, perm, cfg: Config, want_w_hat=True, want_row_loss=True, workspace=None,
                    out=None, stream=None):
     """Column sweep; returns dict(codes, scales, zeros, g_idx[, w_hat][, row_loss]) in original order."""
+    return _quantize("gptq_quantize_layer", W, U, perm, cfg, want_w_hat, want_row_loss, workspace, out, stream)
+
+
+def quantize_layer_factored(W, F, perm, cfg: Config, want_w_hat=True, want_row_loss=True, workspace=None,
+                            out=None, stream=None):
+    """The column sweep given F from prepare_hinv_factored; the same outputs as quantize_layer."""
+    return _quantize("gptq_quantize_layer_factored", W, F, perm, cfg, want_w_hat, want_row_loss, workspace, out,
+                     stream)
+
+
+def _quantize(name, W, U, perm, cfg, want_w_hat, want_row_loss, workspace, out, stream):
     lib = load()
     torch = _torch()
     _require_cuda(W, U, perm)
@@ -173,9 +193,9 @@ def quantize_layer(W, U, perm, cfg: Config, want_w_hat=True, want_row_loss=True,
         raise TypeError("perm must be int32 of length d_in")
     dev = W.device
     ng = n_groups(d_in, cfg.group_size)
-    nws = lib.gptq_quantize_layer_workspace(d_out, d_in, ctypes.byref(cfg))
+    nws = getattr(lib, name + "_workspace")(d_out, d_in, ctypes.byref(cfg))
     if nws == 0:
-        raise InvalidArgument(_lib.ERR_INVALID_ARG, "gptq_quantize_layer_workspace", "invalid shape or config")
+        raise InvalidArgument(_lib.ERR_INVALID_ARG, name + "_workspace", "invalid or unsupported shape or config")
     with _alloc_on(stream):
         if out is None:
             out = dict(codes=torch.empty((d_out, d_in), dtype=torch.uint8, device=dev),
@@ -187,11 +207,11 @@ def quantize_layer(W, U, perm, cfg: Config, want_w_hat=True, want_row_loss=True,
             if want_row_loss:
                 out["row_loss"] = torch.empty(d_out, dtype=torch.float64, device=dev)
         ws = workspace if workspace is not None else _workspace(nws, dev)
-    st = lib.gptq_quantize_layer(_ptr(W), _dtype_code(W), d_out, d_in, W.stride(0), _ptr(U), _ptr(perm),
-                                 ctypes.byref(cfg), _ptr(out["codes"]), _ptr(out["scales"]), _ptr(out["zeros"]),
-                                 _ptr(out["g_idx"]), _ptr(out.get("w_hat")), _ptr(out.get("row_loss")),
-                                 _ptr(ws), ws.numel(), _stream(stream))
-    _lib.check(st, "gptq_quantize_layer")
+    st = getattr(lib, name)(_ptr(W), _dtype_code(W), d_out, d_in, W.stride(0), _ptr(U), _ptr(perm),
+                            ctypes.byref(cfg), _ptr(out["codes"]), _ptr(out["scales"]), _ptr(out["zeros"]),
+                            _ptr(out["g_idx"]), _ptr(out.get("w_hat")), _ptr(out.get("row_loss")),
+                            _ptr(ws), ws.numel(), _stream(stream))
+    _lib.check(st, name)
     return out
 
 
@@ -298,23 +318,38 @@ def gather_columns(X, perm, out=None, stream=None):
     return out
 
 
-def quantize(W, *, X=None, H=None, cfg: Config | None = None, packed=True, stream=None):
-    """One layer end to end: Hessian (from X unless H is given), prepare_hinv, sweep, pack.
+def factored_supported(d_out: int, d_in: int, cfg: Config) -> bool:
+    """Whether prepare_hinv_factored / quantize_layer_factored take this shape and config."""
+    lib = load()
+    return (lib.gptq_prepare_hinv_factored_workspace(d_in) != 0 and
+            lib.gptq_quantize_layer_factored_workspace(d_out, d_in, ctypes.byref(cfg)) != 0)
 
-    Returns the dict of quantize_layer plus ``perm`` and (if packed) ``packed``.
-    H, when given, is consumed (overwritten with U).
+
+def quantize(W, *, X=None, H=None, cfg: Config | None = None, packed=True, factored=None, stream=None):
+    """One layer end to end: Hessian (from X unless H is given), prepare, sweep, pack.
+
+    factored: None takes the factored form (prepare_hinv_factored,
+    quantize_layer_factored) where it is supported, else U; True or False
+    forces one of them.  Returns the dict of quantize_layer plus ``perm``
+    and (if packed) ``packed``.  H, when given, is consumed (overwritten).
     """
     torch = _torch()
     cfg = cfg or make_config()
-    d_in = W.shape[1]
+    d_out, d_in = W.shape
+    if factored is None:
+        factored = factored_supported(d_out, d_in, cfg)
     if H is None:
         if X is None:
             raise ValueError("give X or H")
         with _alloc_on(stream):
             H = torch.zeros((d_in, d_in), dtype=torch.float64, device=W.device)
         hessian_accumulate(H, X, stream=stream)
-    perm = prepare_hinv(H, cfg, stream=stream)
-    out = quantize_layer(W, H, perm, cfg, stream=stream)
+    if factored:
+        perm = prepare_hinv_factored(H, cfg, stream=stream)
+        out = quantize_layer_factored(W, H, perm, cfg, stream=stream)
+    else:
+        perm = prepare_hinv(H, cfg, stream=stream)
+        out = quantize_layer(W, H, perm, cfg, stream=stream)
     out["perm"] = perm
     if packed:
         out["packed"] = pack(out["codes"], cfg.bits, stream=stream)

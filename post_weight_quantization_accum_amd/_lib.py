@@ -23,7 +23,9 @@ EXPORTS = (
     "gptq_config_default", "gptq_hessian_workspace", "gptq_hessian_accumulate", "gptq_hessian_accumulate_timed",
     "gptq_hessian_accumulate_noalloc",
     "gptq_prepare_hinv_workspace", "gptq_prepare_hinv", "gptq_quantize_layer_workspace",
-    "gptq_quantize_layer", "gptq_packed_words_per_row", "gptq_pack", "gptq_pack_permuted",
+    "gptq_quantize_layer", "gptq_prepare_hinv_factored_workspace", "gptq_prepare_hinv_factored",
+    "gptq_quantize_layer_factored_workspace", "gptq_quantize_layer_factored",
+    "gptq_packed_words_per_row", "gptq_pack", "gptq_pack_permuted",
     "gptq_dequant_max_groups", "gptq_dequant_matmul", "gptq_gather_columns", "gptq_status_string",
     "gptq_version",
 )
@@ -110,6 +112,15 @@ def load(path: str | None = None):
     lib.gptq_quantize_layer.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, vp, cfgp, vp, vp, vp, vp, vp, vp,
                                         vp, sz, vp]
     lib.gptq_quantize_layer.restype = ctypes.c_int
+    lib.gptq_prepare_hinv_factored_workspace.argtypes = [i64]
+    lib.gptq_prepare_hinv_factored_workspace.restype = sz
+    lib.gptq_prepare_hinv_factored.argtypes = [vp, i64, cfgp, vp, vp, sz, vp]
+    lib.gptq_prepare_hinv_factored.restype = ctypes.c_int
+    lib.gptq_quantize_layer_factored_workspace.argtypes = [i64, i64, cfgp]
+    lib.gptq_quantize_layer_factored_workspace.restype = sz
+    lib.gptq_quantize_layer_factored.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, vp, cfgp, vp, vp, vp, vp, vp,
+                                                 vp, vp, sz, vp]
+    lib.gptq_quantize_layer_factored.restype = ctypes.c_int
     lib.gptq_packed_words_per_row.argtypes = [i64, i32]
     lib.gptq_packed_words_per_row.restype = i64
     lib.gptq_pack.argtypes = [vp, i64, i64, i32, vp, vp]

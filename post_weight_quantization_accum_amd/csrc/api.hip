@@ -140,6 +140,54 @@ gptq_status gptq_prepare_hinv(double* H, int64_t d_in, const gptq_config* cfg, i
     return GPTQ_OK;
 }
 
+size_t gptq_prepare_hinv_factored_workspace(int64_t d_in) {
+    if (d_in <= 0 || d_in > MAX_DIM || d_in % 128 != 0) return 0;
+    return hinv_workspace_bytes(d_in);
+}
+
+gptq_status gptq_prepare_hinv_factored(double* H, int64_t d_in, const gptq_config* cfg, int32_t* perm,
+                                       void* workspace, size_t ws_bytes, hipStream_t stream) {
+    if (!H || !perm) return GPTQ_ERR_INVALID_ARG;
+    if (d_in <= 0 || d_in > MAX_DIM) return GPTQ_ERR_INVALID_ARG;
+    gptq_status st = check_config(cfg);
+    if (st != GPTQ_OK) return st;
+    if (d_in % 128 != 0) return GPTQ_ERR_UNSUPPORTED;
+    if (!workspace || ws_bytes < hinv_workspace_bytes(d_in)) return GPTQ_ERR_WORKSPACE;
+    int flags[N_FLAGS] = {0, 0, 0, 0};
+    st = hinv_launch(H, d_in, cfg, perm, workspace, stream, flags, true);
+    if (st != GPTQ_OK) return st;
+    if (flags[FLAG_NONFINITE]) return GPTQ_ERR_NONFINITE;
+    if (flags[FLAG_NOT_PD]) return GPTQ_ERR_NOT_PD;
+    return GPTQ_OK;
+}
+
+size_t gptq_quantize_layer_factored_workspace(int64_t d_out, int64_t d_in, const gptq_config* cfg) {
+    if (d_out <= 0 || d_in <= 0 || d_out > MAX_DIM || d_in > MAX_DIM) return 0;
+    if (check_config(cfg) != GPTQ_OK || !sweep_factored_supported(d_in, cfg)) return 0;
+    return sweep_workspace_bytes(d_out, d_in, cfg, true);
+}
+
+gptq_status gptq_quantize_layer_factored(const void* W, gptq_dtype w_dtype, int64_t d_out, int64_t d_in,
+                                         int64_t ld_w, const double* F, const int32_t* perm,
+                                         const gptq_config* cfg, uint8_t* codes, float* scales, float* zeros,
+                                         int32_t* g_idx, float* w_hat, double* row_loss, void* workspace,
+                                         size_t ws_bytes, hipStream_t stream) {
+    if (!W || !F || !perm || !codes || !scales || !zeros || !g_idx) return GPTQ_ERR_INVALID_ARG;
+    if (!valid_dtype(w_dtype)) return GPTQ_ERR_INVALID_ARG;
+    if (d_out <= 0 || d_in <= 0 || d_out > MAX_DIM || d_in > MAX_DIM || ld_w < d_in) return GPTQ_ERR_INVALID_ARG;
+    gptq_status st = check_config(cfg);
+    if (st != GPTQ_OK) return st;
+    if (!sweep_factored_supported(d_in, cfg)) return GPTQ_ERR_UNSUPPORTED;
+    if (!workspace || ws_bytes < sweep_workspace_bytes(d_out, d_in, cfg, true)) return GPTQ_ERR_WORKSPACE;
+    int flags[N_FLAGS] = {0, 0, 0, 0};
+    st = sweep_launch(W, w_dtype, d_out, d_in, ld_w, F, perm, cfg, codes, scales, zeros, g_idx, w_hat, row_loss,
+                      workspace, stream, flags, true);
+    if (st != GPTQ_OK) return st;
+    if (flags[FLAG_BAD_PERM]) return GPTQ_ERR_INVALID_ARG;
+    if (flags[FLAG_NONFINITE]) return GPTQ_ERR_NONFINITE;
+    return GPTQ_OK;
+}
+
 size_t gptq_quantize_layer_workspace(int64_t d_out, int64_t d_in, const gptq_config* cfg) {
     if (d_out <= 0 || d_in <= 0 || d_out > MAX_DIM || d_in > MAX_DIM) return 0;
     if (check_config(cfg) != GPTQ_OK) return 0;

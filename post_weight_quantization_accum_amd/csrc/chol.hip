@@ -64,10 +64,12 @@ struct Ws {
     int32_t* pinv;
     double* L;
     double* tmp[MAX_DEPTH];
+    double* mrev;   // factored form: the diagonal blocks of M, columns reversed
 };
 
 // Layout: flags/lambda | diag (d doubles) | pinv (d ints) | Hr (d*d) | one L21
-// scratch per depth; returns the total size.
+// scratch per depth | the diagonal blocks of M (factored form); returns the
+// total size.
 size_t layout(int64_t d, Ws* w, char* p) {
     size_t off = 256;
     if (w) w->diag = (double*)(p + off);
@@ -82,6 +84,8 @@ size_t layout(int64_t d, Ws* w, char* p) {
         if (w) w->tmp[k] = (double*)(p + off);
         off = align_up(off + sz[k] * sizeof(double), 256);
     }
+    if (w) w->mrev = (double*)(p + off);
+    off = align_up(off + (size_t)ceil_div(d, LEAF) * LEAF * LEAF * sizeof(double), 256);
     if (w) {
         w->flags = (int*)p;
         w->lambda = (double*)(p + 64);
@@ -578,6 +582,7 @@ struct Rec {
     int* flags = nullptr;
     hipEvent_t l21_ready[MAX_DEPTH] = {}, t_done[MAX_DEPTH] = {};
     int64_t t_wg = 0;   // workgroups of a T product
+    bool keep_l = false;
     // created on first use: factors of at most 1024 columns never need them
     hipError_t init() {
         if (side) return hipSuccess;
@@ -605,7 +610,14 @@ struct Rec {
     }
 };
 
-gptq_status chol_inv(Rec& c, int64_t o, int64_t n, int depth) {
+// need_m: the caller reads this node's whole inverse M (a left child: its
+// M11 feeds the parent's L21).  Without it (the root and the right children
+// below it, in the factored form) T and M21 are skipped: only the diagonal
+// blocks of M, which the leaves form, are read afterwards.
+// c.keep_l (factored form): each node's L21 stays in A21's place for the
+// end; A21 is copied to the depth's scratch first (the product may not
+// write over its own operand) and T goes to that scratch instead.
+gptq_status chol_inv(Rec& c, int64_t o, int64_t n, int depth, bool need_m = true) {
     const int64_t d = c.d;
     if (n <= LEAF) {
         hipLaunchKernelGGL(leaf_blocked_kernel, dim3(1), dim3(512), LEAF_LDS, c.s, c.L, c.M, d, o, (int)n, c.flags);
@@ -615,44 +627,78 @@ gptq_status chol_inv(Rec& c, int64_t o, int64_t n, int depth) {
     if (depth >= MAX_DEPTH) return GPTQ_ERR_UNSUPPORTED;
     int64_t n1, n2;
     split(n, n1, n2);
-    double* A21 = c.L + (o + n1) * d + o;   // becomes T
+    double* A21 = c.L + (o + n1) * d + o;
     double* A22 = c.L + (o + n1) * d + o + n1;
     const double* M11 = c.M + o * d + o;
     const double* M22 = c.M + (o + n1) * d + o + n1;
     double* M21 = c.M + (o + n1) * d + o;
-    double* L21 = c.tmp[depth];
-    gptq_status st = chol_inv(c, o, n1, depth + 1);
+    const double* Asrc = A21;
+    int64_t ld_a = d;
+    double* L21 = c.tmp[depth];   // L21's place
+    int64_t ld_l = n1;
+    double* T = A21;              // T's place
+    int64_t ld_t = d;
+    gptq_status st = chol_inv(c, o, n1, depth + 1, true);
     if (st != GPTQ_OK) return st;
+    if (c.keep_l) {
+        GPTQ_HIP(hipMemcpy2DAsync(c.tmp[depth], (size_t)n1 * sizeof(double), A21, (size_t)d * sizeof(double),
+                                  (size_t)n1 * sizeof(double), (size_t)n2, hipMemcpyDeviceToDevice, c.s));
+        Asrc = c.tmp[depth];
+        ld_a = n1;
+        L21 = A21;
+        ld_l = d;
+        T = c.tmp[depth];
+        ld_t = n1;
+    }
     // L21 = A21 M11^T
-    st = launch_gemm_f64(c.s, n2, n1, n1, 1.0, A21, d, M11, d, true, 0.0, L21, n1, false, GEMM_TRI_KEND_COL);
+    st = launch_gemm_f64(c.s, n2, n1, n1, 1.0, Asrc, ld_a, M11, d, true, 0.0, L21, ld_l, false, GEMM_TRI_KEND_COL);
     if (st != GPTQ_OK) return st;
     if (n1 <= 512 && n2 <= 512) {
         // small node: A22 -= L21 L21^T and T = L21 M11 in one launch, all on
         // the main stream (no cross-stream events on the short chain)
-        const GemmCall syrk{n2, n2, n1, -1.0, L21, n1, L21, n1, true, 1.0, A22, d, true, GEMM_TRI_NONE};
-        const GemmCall tprod{n2, n1, n1, 1.0, L21, n1, M11, d, false, 0.0, A21, d, false, GEMM_TRI_KBEG_COL};
-        st = launch_gemm_f64_pair(c.s, syrk, tprod);
+        const GemmCall syrk{n2, n2, n1, -1.0, L21, ld_l, L21, ld_l, true, 1.0, A22, d, true, GEMM_TRI_NONE};
+        if (need_m) {
+            const GemmCall tprod{n2, n1, n1, 1.0, L21, ld_l, M11, d, false, 0.0, T, ld_t, false, GEMM_TRI_KBEG_COL};
+            st = launch_gemm_f64_pair(c.s, syrk, tprod);
+        } else {
+            st = launch_gemm_f64(c.s, n2, n2, n1, -1.0, L21, ld_l, L21, ld_l, true, 1.0, A22, d, true);
+        }
         if (st != GPTQ_OK) return st;
-        st = chol_inv(c, o + n1, n2, depth + 1);
+        st = chol_inv(c, o + n1, n2, depth + 1, need_m);
         if (st != GPTQ_OK) return st;
-        return launch_gemm_f64(c.s, n2, n1, n2, -1.0, M22, d, A21, d, false, 0.0, M21, d, false, GEMM_TRI_KEND_ROW);
+        if (!need_m) return GPTQ_OK;
+        return launch_gemm_f64(c.s, n2, n1, n2, -1.0, M22, d, T, ld_t, false, 0.0, M21, d, false, GEMM_TRI_KEND_ROW);
     }
     // A22 -= L21 L21^T
-    st = launch_gemm_f64(c.s, n2, n2, n1, -1.0, L21, n1, L21, n1, true, 1.0, A22, d, true);
+    st = launch_gemm_f64(c.s, n2, n2, n1, -1.0, L21, ld_l, L21, ld_l, true, 1.0, A22, d, true);
     if (st != GPTQ_OK) return st;
-    // T = L21 M11 (into A21's place), on the side stream
+    if (!need_m) return chol_inv(c, o + n1, n2, depth + 1, false);
+    // T = L21 M11, on the side stream
     GPTQ_HIP(c.init());
     GPTQ_HIP(hipEventRecord(c.l21_ready[depth], c.s));
     GPTQ_HIP(hipStreamWaitEvent(c.side, c.l21_ready[depth], 0));
-    st = launch_gemm_f64(c.side, n2, n1, n1, 1.0, L21, n1, M11, d, false, 0.0, A21, d, false, GEMM_TRI_KBEG_COL,
+    st = launch_gemm_f64(c.side, n2, n1, n1, 1.0, L21, ld_l, M11, d, false, 0.0, T, ld_t, false, GEMM_TRI_KBEG_COL,
                          false, c.t_wg);
     if (st != GPTQ_OK) return st;
     GPTQ_HIP(hipEventRecord(c.t_done[depth], c.side));
-    st = chol_inv(c, o + n1, n2, depth + 1);
+    st = chol_inv(c, o + n1, n2, depth + 1, true);
     if (st != GPTQ_OK) return st;
     // M21 = -M22 T
     GPTQ_HIP(hipStreamWaitEvent(c.s, c.t_done[depth], 0));
-    return launch_gemm_f64(c.s, n2, n1, n2, -1.0, M22, d, A21, d, false, 0.0, M21, d, false, GEMM_TRI_KEND_ROW);
+    return launch_gemm_f64(c.s, n2, n1, n2, -1.0, M22, d, T, ld_t, false, 0.0, M21, d, false, GEMM_TRI_KEND_ROW);
+}
+
+// Each 128 x 128 diagonal block of M (lower) with its columns reversed:
+// Mrev[l][k][n] = M_ll[k][127 - n], zero above the diagonal.
+__global__ __launch_bounds__(256) void diag_blocks_rev_kernel(const double* __restrict__ M, int64_t d,
+                                                              double* __restrict__ Mrev) {
+    const int64_t l = blockIdx.x;
+    const double* src = M + (l * LEAF) * d + l * LEAF;
+    double* dst = Mrev + l * LEAF * LEAF;
+    for (int e = threadIdx.x; e < LEAF * LEAF; e += 256) {
+        const int k = e / LEAF, n = e % LEAF, col = LEAF - 1 - n;
+        dst[e] = (col <= k) ? src[(int64_t)k * d + col] : 0.0;
+    }
 }
 
 }  // namespace
@@ -660,7 +706,8 @@ gptq_status chol_inv(Rec& c, int64_t o, int64_t n, int depth) {
 size_t hinv_workspace_bytes(int64_t d) { return layout(d, nullptr, nullptr); }
 
 gptq_status hinv_launch(double* H, int64_t d, const gptq_config* cfg, int32_t* perm, void* ws,
-                        hipStream_t s, int* host_flags) {
+                        hipStream_t s, int* host_flags, bool factored) {
+    if (factored && (d % LEAF) != 0) return GPTQ_ERR_UNSUPPORTED;
     Ws w;
     layout(d, &w, (char*)ws);
     GPTQ_HIP(ensure_lds_limit((const void*)leaf_blocked_kernel, (int)LEAF_LDS));
@@ -694,10 +741,18 @@ gptq_status hinv_launch(double* H, int64_t d, const gptq_config* cfg, int32_t* p
     for (int k = 0; k < MAX_DEPTH; ++k) c.tmp[k] = w.tmp[k];
     c.d = d;
     c.flags = w.flags;
-    gptq_status st = chol_inv(c, 0, d, 0);
+    c.keep_l = factored;
+    gptq_status st = chol_inv(c, 0, d, 0, !factored);
     if (st != GPTQ_OK) return st;
-    hipLaunchKernelGGL(rotate_inplace_kernel, dim3((unsigned)d), dim3(256), 0, s, H, d);
-    GPTQ_LAUNCH_CHECK();
+    if (factored) {
+        hipLaunchKernelGGL(diag_blocks_rev_kernel, dim3((unsigned)(d / LEAF)), dim3(256), 0, s, H, d, w.mrev);
+        GPTQ_LAUNCH_CHECK();
+        st = launch_factor_blocks(s, w.L, w.mrev, H, d);
+        if (st != GPTQ_OK) return st;
+    } else {
+        hipLaunchKernelGGL(rotate_inplace_kernel, dim3((unsigned)d), dim3(256), 0, s, H, d);
+        GPTQ_LAUNCH_CHECK();
+    }
     GPTQ_HIP(hipMemcpyAsync(host_flags, w.flags, N_FLAGS * sizeof(int), hipMemcpyDeviceToHost, s));
     GPTQ_HIP(hipStreamSynchronize(s));
     return GPTQ_OK;

@@ -399,6 +399,44 @@ __global__ __launch_bounds__(256) void gemm_f64_small_pair_kernel(SmallArgs p1, 
     else small_tile<false, false>(p2, (b - nb1) * 4 + w, lane);
 }
 
+// The factored form of the inverse's Cholesky factor (sweep order): for
+// 128-column blocks k < l, F[K_k, K_l] = R[K_k, K_l] U_ll with R = J L J
+// (L the lower factor of the reversed matrix, in Lf) and U_ll = J M_ll J
+// (M_ll the inverse of L's diagonal block); F's diagonal blocks are U_ll,
+// its strict lower triangle zero.  Mrev holds each M_ll with its columns
+// reversed ([block][k][127 - n] = M_ll[k][n]), so that one product per
+// block pair writes F rotated: row r' of L goes to row d - 1 - r' of F and
+// column n of the product to column d - 128 - 128 l + n.  One workgroup per
+// block pair (j >= l, reversed order): j > l computes its block and zeroes
+// the mirrored block below F's diagonal; j == l writes U_ll.
+__global__ __launch_bounds__(256, 2) void factor_blocks_kernel(const double* __restrict__ Lf,
+                                                               const double* __restrict__ Mrev, double* F,
+                                                               int64_t d) {
+    constexpr int T = 128;
+    __shared__ double sA[2][KC][Cfg<T>::LD];
+    __shared__ double sB[2][KC][Cfg<T>::LD];
+    int64_t j, l;
+    tri_index(blockIdx.x, j, l);
+    const int64_t nb = d / T;
+    const double* Ml = Mrev + l * T * T;
+    if (j == l) {
+        const int64_t k = nb - 1 - l;   // F's block
+        for (int e = threadIdx.x; e < T * T; e += 256) {
+            const int i = e / T, jj = e % T;
+            F[(k * T + i) * d + k * T + jj] = (i <= jj) ? Ml[(T - 1 - i) * T + jj] : 0.0;
+        }
+        return;
+    }
+    // the mirrored block under F's diagonal: rows of F's block nb-1-l, columns of nb-1-j
+    {
+        const int64_t br = nb - 1 - l, bc = nb - 1 - j;
+        for (int e = threadIdx.x; e < T * T; e += 256) F[(br * T + e / T) * d + bc * T + e % T] = 0.0;
+    }
+    double* C = F + (d - 1 - j * T) * d + (d - T - l * T);
+    gemm_tile<T, false, false, true>(T, T, T, 1.0, Lf + (j * T) * d + l * T, d, Ml, T, 0.0, C, -d, 1, 1, 1, 1,
+                                     GEMM_TRI_NONE, 0, sA, sB);
+}
+
 template <bool TRANS_B, bool LOWER>
 void launch_small(hipStream_t s, int64_t M, int64_t N, int64_t K, double alpha, const double* A, int64_t lda,
                   const double* B, int64_t ldb, double beta, double* C, int64_t ldc, int tri) {
@@ -486,6 +524,16 @@ gptq_status launch_gemm_f64(hipStream_t s, int64_t M, int64_t N, int64_t K, doub
         else
             launch_sel<false, false>(s, vec, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, (int)tri, one_per_cu, max_wg);
     }
+    GPTQ_LAUNCH_CHECK();
+    return GPTQ_OK;
+}
+
+gptq_status launch_factor_blocks(hipStream_t s, const double* L, const double* Mrev, double* F, int64_t d) {
+    if (d <= 0 || d % 128 != 0) return GPTQ_ERR_UNSUPPORTED;
+    const int64_t nb = d / 128;
+    if (nb * (nb + 1) / 2 > INT32_MAX) return GPTQ_ERR_UNSUPPORTED;
+    if ((uintptr_t)L % 16 != 0 || (uintptr_t)Mrev % 16 != 0) return GPTQ_ERR_INVALID_ARG;
+    hipLaunchKernelGGL(factor_blocks_kernel, dim3((unsigned)(nb * (nb + 1) / 2)), dim3(256), 0, s, L, Mrev, F, d);
     GPTQ_LAUNCH_CHECK();
     return GPTQ_OK;
 }

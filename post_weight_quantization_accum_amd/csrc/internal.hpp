@@ -58,6 +58,13 @@ struct GemmCall {
 };
 gptq_status launch_gemm_f64_pair(hipStream_t s, const GemmCall& x, const GemmCall& y);
 
+// F (sweep order, row stride d, d a multiple of 128) from the lower factor L
+// of the reversed damped matrix (row stride d; its off-diagonal 128-blocks
+// are read) and Mrev (d/128 blocks of 128 x 128: the inverse of each of L's
+// diagonal blocks, columns reversed): F[K_k, K_l] = R[K_k, K_l] U_ll for
+// k < l, U_kk on the diagonal, zero below (R = J L J, U_ll = J M_ll J).
+gptq_status launch_factor_blocks(hipStream_t s, const double* L, const double* Mrev, double* F, int64_t d);
+
 // Hessian: H (upper) += 2 X^T X.  ws: hessian_workspace_bytes(n_tok, d)
 // bytes (float64 partial tiles of narrow layers; an aligned copy of a token
 // chunk for inputs whose rows are not 16-byte aligned); unused for fp32
@@ -75,18 +82,21 @@ gptq_status hessian_launch_scratch(double* H, const void* X, gptq_dtype dt, int6
                                    int64_t ld_x, void* scratch, size_t scratch_bytes, hipStream_t s);
 
 // Column order, damping, Cholesky of the reversed matrix, triangular inverse,
-// rotation into U.  ws layout described in chol.hip.
+// rotation into U; factored: the factored form F instead of U (d a multiple
+// of 128).  ws layout described in chol.hip.
 size_t hinv_workspace_bytes(int64_t d);
 gptq_status hinv_launch(double* H, int64_t d, const gptq_config* cfg, int32_t* perm,
-                        void* ws, hipStream_t s, int* host_flags);
+                        void* ws, hipStream_t s, int* host_flags, bool factored = false);
 
 // Column sweep with lazy updates; ws layout described in sweep.hip.
-size_t sweep_workspace_bytes(int64_t d_out, int64_t d_in, const gptq_config* cfg);
+// factored: U is the factored form F (and the lazy updates use it).
+size_t sweep_workspace_bytes(int64_t d_out, int64_t d_in, const gptq_config* cfg, bool factored = false);
+bool sweep_factored_supported(int64_t d_in, const gptq_config* cfg);
 gptq_status sweep_launch(const void* W, gptq_dtype dt, int64_t d_out, int64_t d_in, int64_t ld_w,
                          const double* U, const int32_t* perm, const gptq_config* cfg,
                          uint8_t* codes, float* scales, float* zeros, int32_t* g_idx,
                          float* w_hat, double* row_loss, void* ws, hipStream_t s,
-                         int* host_flags);
+                         int* host_flags, bool factored = false);
 
 // perm: null (stream order = column order) or stream position -> column.
 gptq_status pack_launch(const uint8_t* codes, int64_t d_out, int64_t d_in, int32_t bits, const int32_t* perm,

@@ -70,6 +70,7 @@ struct SweepWs {
     int* flags;
     double* Wwork;
     double* Err;
+    double* W0;   // factored form: the weights before the sweep (sweep order)
     uint8_t* codes_s;
     double* scale64;
     double* zero64;
@@ -108,7 +109,7 @@ int64_t superblock_cols(int64_t d_in, const gptq_config* cfg) {
     return B;
 }
 
-SweepWs carve(void* ws, int64_t d_out, int64_t d_in, const gptq_config* cfg) {
+SweepWs carve(void* ws, int64_t d_out, int64_t d_in, const gptq_config* cfg, bool factored) {
     char* p = (char*)ws;
     SweepWs w;
     size_t off = 0;
@@ -130,10 +131,12 @@ SweepWs carve(void* ws, int64_t d_out, int64_t d_in, const gptq_config* cfg) {
     w.pinv = (int32_t*)(p + off);
     off = align_up(off + (size_t)d_in * 4, 256);
     w.gsw = (int32_t*)(p + off);
+    off = align_up(off + (size_t)d_in * 4, 256);
+    w.W0 = factored ? (double*)(p + off) : nullptr;
     return w;
 }
 
-size_t carve_size(int64_t d_out, int64_t d_in, const gptq_config* cfg) {
+size_t carve_size(int64_t d_out, int64_t d_in, const gptq_config* cfg, bool factored) {
     size_t off = 256;
     off = align_up(off + (size_t)d_out * d_in * 8, 256);
     off = align_up(off + 2 * (size_t)d_out * superblock_cols(d_in, cfg) * 8, 256);
@@ -144,6 +147,7 @@ size_t carve_size(int64_t d_out, int64_t d_in, const gptq_config* cfg) {
     off = align_up(off + (size_t)d_out * 8, 256);
     off = align_up(off + (size_t)d_in * 4, 256);
     off = align_up(off + (size_t)d_in * 4, 256);
+    if (factored) off = align_up(off + (size_t)d_out * d_in * 8, 256);
     return off;
 }
 
@@ -361,14 +365,20 @@ __device__ __forceinline__ double row_max16(double x) {
     return fmax(x, dpp_f64<DPP_MIRROR>(x));
 }
 
-template <int SEG, bool FULL, bool STATIC>
+// FACT (the factored form of the lazy updates): the stored per-column value
+// is W0_c - q_c (W0: the weights before the sweep) instead of the scaled
+// error.  The owner lane stores q_c in the column loop (one store, no extra
+// register live across the loop: a register copy of q or of W0 pushed the
+// kernel past 256 VGPRs) and the epilogue subtracts it from W0.
+template <int SEG, bool FULL, bool STATIC, bool FACT = false>
 __global__ __launch_bounds__(SWAVES * 64) void sweep_block_kernel(double* __restrict__ Wwork, int64_t d_out, int64_t d_in,
                                                          int64_t i1, int nb, const double* __restrict__ U,
                                                          int64_t g, QParams qp, double* __restrict__ Err,
                                                          int ldE, int errc, uint8_t* __restrict__ codes_s,
                                                          double* __restrict__ scale64, double* __restrict__ zero64,
                                                          float* __restrict__ scales, float* __restrict__ zeros,
-                                                         double* __restrict__ loss64, const int32_t* __restrict__ gsw) {
+                                                         double* __restrict__ loss64, const int32_t* __restrict__ gsw,
+                                                         const double* __restrict__ W0) {
     extern __shared__ __attribute__((aligned(16))) double sweep_lds[];
     // the sweep is the serial chain of the layer: its waves take issue
     // priority over GEMM waves of the other stream on the same SIMD
@@ -395,6 +405,7 @@ __global__ __launch_bounds__(SWAVES * 64) void sweep_block_kernel(double* __rest
             w[mm] = (live && (FULL || j < nb)) ? x : 0.0;
         }
     }
+
     const int64_t rem = i1 % g;
     const int64_t rrow = live ? row : 0;
     const double scale_in = scale64[(i1 / g) * d_out + rrow], zero_in = zero64[(i1 / g) * d_out + rrow];
@@ -598,6 +609,11 @@ __global__ __launch_bounds__(SWAVES * 64) void sweep_block_kernel(double* __rest
         for (int mm = 0; mm < CPL; ++mm)
             if (mm >= m) w[mm] = fma(-err, u[mm], w[mm]);
         if (c + 1 < BMAX) xn = w[(c + 1) / LPR];
+        if constexpr (FACT) {
+            // q of the column to its place in Err now (the owner lane); the
+            // epilogue turns it into W0 - q
+            if (own && live) Err[row * ldE + errc + c] = cs * (code - cz);
+        }
         w[m] = own ? err : w[m];
         if (c + 2 < BMAX) {
             load_urow(u, c + 2);
@@ -610,15 +626,18 @@ __global__ __launch_bounds__(SWAVES * 64) void sweep_block_kernel(double* __rest
         asm volatile("" ::: "memory");
     });
 
-    // errors and codes of this row's columns back to HBM
+    // errors (FACT: W0 - q, W0 read now) and codes of this row's columns back to HBM
     if (live) {
         double* erow = Err + row * ldE + errc;
         uint8_t* crow = codes_s + row * d_in + i1;
+        const double* w0row = W0 + row * d_in + i1;
 #pragma unroll
         for (int mm = 0; mm < CPL; ++mm) {
             const int col = p + LPR * mm;
             if (FULL || col < nb) {
-                erow[col] = w[mm];
+                // FACT: this lane stored q of its own columns above (a
+                // thread reads its own earlier stores)
+                erow[col] = FACT ? w0row[col] - erow[col] : w[mm];
                 crow[col] = (uint8_t)(pk[mm >> 2] >> (8 * (mm & 3)));
             }
         }
@@ -699,15 +718,26 @@ __global__ void copy_loss_kernel(const double* __restrict__ src, double* dst, in
 
 }  // namespace
 
-size_t sweep_workspace_bytes(int64_t d_out, int64_t d_in, const gptq_config* cfg) {
-    return carve_size(d_out, d_in, cfg);
+size_t sweep_workspace_bytes(int64_t d_out, int64_t d_in, const gptq_config* cfg, bool factored) {
+    return carve_size(d_out, d_in, cfg, factored);
+}
+
+bool sweep_factored_supported(int64_t d_in, const gptq_config* cfg) {
+    if (d_in % BMAX != 0 || cfg->block_size != BMAX) return false;
+    if (cfg->static_groups != 0 && cfg->group_size > 0) return true;
+    const int64_t g = cfg->group_size > 0 ? cfg->group_size : d_in;
+    // every group inside one block (or one group per row), and group starts
+    // on multiples of CPL block columns
+    if (g % CPL != 0) return false;
+    return g >= d_in || BMAX % g == 0;
 }
 
 gptq_status sweep_launch(const void* W, gptq_dtype dt, int64_t d_out, int64_t d_in, int64_t ld_w,
                          const double* U, const int32_t* perm, const gptq_config* cfg, uint8_t* codes,
                          float* scales, float* zeros, int32_t* g_idx, float* w_hat, double* row_loss, void* ws,
-                         hipStream_t s, int* host_flags) {
-    SweepWs w = carve(ws, d_out, d_in, cfg);
+                         hipStream_t s, int* host_flags, bool factored) {
+    if (factored && !sweep_factored_supported(d_in, cfg)) return GPTQ_ERR_UNSUPPORTED;
+    SweepWs w = carve(ws, d_out, d_in, cfg, factored);
     const int64_t g = cfg->group_size > 0 ? cfg->group_size : d_in;
     const int B = cfg->block_size;
     // per-row static groups are the dynamic per-row group (taken at column 0
@@ -730,6 +760,8 @@ gptq_status sweep_launch(const void* W, gptq_dtype dt, int64_t d_out, int64_t d_
                            w.Wwork, w.loss64, w.flags);
     }
     GPTQ_LAUNCH_CHECK();
+    if (factored)
+        GPTQ_HIP(hipMemcpyAsync(w.W0, w.Wwork, (size_t)d_out * d_in * sizeof(double), hipMemcpyDeviceToDevice, s));
     hipLaunchKernelGGL(fill_neg_kernel, dim3(gx), dim3(256), 0, s, w.pinv, d_in);
     GPTQ_LAUNCH_CHECK();
     hipLaunchKernelGGL(pinv_kernel, dim3(gx), dim3(256), 0, s, perm, d_in, g, stat, w.pinv, g_idx, w.gsw);
@@ -755,6 +787,14 @@ gptq_status sweep_launch(const void* W, gptq_dtype dt, int64_t d_out, int64_t d_
 #undef SWEEP_ATTR
     GPTQ_HIP(ensure_lds_limit((const void*)sweep_block_kernel<CPL, true, true>, (int)SWEEP_LDS));
     GPTQ_HIP(ensure_lds_limit((const void*)sweep_block_kernel<CPL, false, true>, (int)SWEEP_LDS));
+    if (factored) {
+        GPTQ_HIP(ensure_lds_limit((const void*)sweep_block_kernel<CPL, true, false, true>, (int)SWEEP_LDS));
+        GPTQ_HIP(ensure_lds_limit((const void*)sweep_block_kernel<CPL, true, true, true>, (int)SWEEP_LDS));
+    }
+    // lazy updates: W[:, later] -= Err U[block, later]; factored: W[:, later]
+    // += (W0 - Q)[:, block] F[block, later] (the same columns, from the
+    // factored form F in U's place)
+    const double lz = factored ? 1.0 : -1.0;
     const int64_t S = superblock_cols(d_in, cfg);
     // A group that runs past the end of its superblock (groups wider than a
     // superblock, or superblocks of one block when lcm(B, g) exceeds the
@@ -773,17 +813,19 @@ gptq_status sweep_launch(const void* W, gptq_dtype dt, int64_t d_out, int64_t d_
         for (int64_t i1 = a; i1 < e; i1 += B) {
             const int nb = (int)((e - i1 < B) ? e - i1 : B);
             const bool full = nb == BMAX;
-            switch (stat ? -1 - (full ? 1 : 0) : SEG * 2 + (full ? 1 : 0)) {
-#define SWEEP_CASE_T(n, f, t, label)                                                                         \
+            switch (factored ? (stat ? -4 : -3) : stat ? -1 - (full ? 1 : 0) : SEG * 2 + (full ? 1 : 0)) {
+#define SWEEP_CASE_T(n, f, t, x, label)                                                                      \
     case label:                                                                                               \
-        hipLaunchKernelGGL((sweep_block_kernel<n, f, t>), dim3(grid), dim3(SWAVES * 64), SWEEP_LDS, s, w.Wwork,  \
-                           d_out, d_in, i1,                                                                 \
+        hipLaunchKernelGGL((sweep_block_kernel<n, f, t, x>), dim3(grid), dim3(SWAVES * 64), SWEEP_LDS, s,       \
+                           w.Wwork, d_out, d_in, i1,                                                        \
                            nb, U, g, qp, Ek, (int)S, (int)(i1 - a), w.codes_s, w.scale64, w.zero64, scales,  \
-                           zeros, w.loss64, w.gsw);                                                           \
+                           zeros, w.loss64, w.gsw, w.W0);                                                     \
         break;
-#define SWEEP_CASE(n, f) SWEEP_CASE_T(n, f, false, n * 2 + f)
-                SWEEP_CASE_T(CPL, true, true, -2)
-                SWEEP_CASE_T(CPL, false, true, -1)
+#define SWEEP_CASE(n, f) SWEEP_CASE_T(n, f, false, false, n * 2 + f)
+                SWEEP_CASE_T(CPL, true, true, true, -4)
+                SWEEP_CASE_T(CPL, true, false, true, -3)
+                SWEEP_CASE_T(CPL, true, true, false, -2)
+                SWEEP_CASE_T(CPL, false, true, false, -1)
                 SWEEP_CASE(8, 1)
                 SWEEP_CASE(8, 0)
                 SWEEP_CASE(4, 1)
@@ -798,7 +840,7 @@ gptq_status sweep_launch(const void* W, gptq_dtype dt, int64_t d_out, int64_t d_
             GPTQ_LAUNCH_CHECK();
             const int64_t i2 = i1 + nb;
             if (i2 < e) {  // rest of this superblock, K = nb
-                gptq_status st = launch_gemm_f64(s, d_out, e - i2, nb, -1.0, Ek + (i1 - a), S, U + i1 * d_in + i2,
+                gptq_status st = launch_gemm_f64(s, d_out, e - i2, nb, lz, Ek + (i1 - a), S, U + i1 * d_in + i2,
                                                  d_in, false, 1.0, w.Wwork + i2, d_in, false);
                 if (st != GPTQ_OK) return st;
             }
@@ -808,7 +850,7 @@ gptq_status sweep_launch(const void* W, gptq_dtype dt, int64_t d_out, int64_t d_
         // after the previous far update (which also wrote them) is done
         if (far_pending) GPTQ_HIP(hipStreamWaitEvent(s, side.far_done, 0));
         const int64_t n_near = (S < d_in - e) ? S : d_in - e;
-        gptq_status st = launch_gemm_f64(s, d_out, n_near, e - a, -1.0, Ek, S, U + a * d_in + e, d_in, false, 1.0,
+        gptq_status st = launch_gemm_f64(s, d_out, n_near, e - a, lz, Ek, S, U + a * d_in + e, d_in, false, 1.0,
                                          w.Wwork + e, d_in, false);
         if (st != GPTQ_OK) return st;
         far_pending = false;
@@ -816,7 +858,7 @@ gptq_status sweep_launch(const void* W, gptq_dtype dt, int64_t d_out, int64_t d_
             GPTQ_HIP(side.init());
             GPTQ_HIP(hipEventRecord(side.err_ready, s));
             GPTQ_HIP(hipStreamWaitEvent(side.s, side.err_ready, 0));
-            st = launch_gemm_f64(side.s, d_out, d_in - e - n_near, e - a, -1.0, Ek, S, U + a * d_in + e + n_near,
+            st = launch_gemm_f64(side.s, d_out, d_in - e - n_near, e - a, lz, Ek, S, U + a * d_in + e + n_near,
                                  d_in, false, 1.0, w.Wwork + e + n_near, d_in, false, GEMM_TRI_NONE, true);
             if (st != GPTQ_OK) return st;
             GPTQ_HIP(hipEventRecord(side.far_done, side.s));

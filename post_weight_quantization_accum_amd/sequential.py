@@ -27,8 +27,8 @@ from __future__ import annotations
 
 import dataclasses
 
-from . import (dequant_matmul, gather_columns, hessian_accumulate, load, pack, pack_permuted, prepare_hinv,
-               quantize_layer)
+from . import (dequant_matmul, factored_supported, gather_columns, hessian_accumulate, load, pack, pack_permuted,
+               prepare_hinv, prepare_hinv_factored, quantize_layer, quantize_layer_factored)
 
 LAYERS = ("q", "k", "v", "out", "fc1", "fc2")
 
@@ -67,10 +67,12 @@ def _quantize_shared(Ws: dict, X, cfg, stats: dict | None, want_w_hat: bool = Tr
     H = _hessian(X)
     if ev:
         ev[1].record()
-    perm = prepare_hinv(H, cfg)
+    d_in = H.shape[0]
+    factored = all(factored_supported(W.shape[0], d_in, cfg) for W in Ws.values())
+    perm = (prepare_hinv_factored if factored else prepare_hinv)(H, cfg)
     res = {}
     for name, W in Ws.items():
-        out = quantize_layer(W, H, perm, cfg, want_w_hat=want_w_hat)
+        out = (quantize_layer_factored if factored else quantize_layer)(W, H, perm, cfg, want_w_hat=want_w_hat)
         out["perm"] = perm
         if cfg.act_order:
             out["packed"] = pack_permuted(out["codes"], cfg.bits, perm)

@@ -62,6 +62,19 @@ def test_workspace_queries():
     assert lib.gptq_quantize_layer_workspace(8, 384, ctypes.byref(bad)) == 0
     st = P.make_config(group_size=96, block=128, static_groups=True)
     assert lib.gptq_quantize_layer_workspace(8, 384, ctypes.byref(st)) >= 8 * 384 * 9
+    # factored form: workspace 0 where unsupported; the sweep's plus a float64 copy of W otherwise
+    assert lib.gptq_prepare_hinv_factored_workspace(1000) == 0
+    assert lib.gptq_prepare_hinv_factored_workspace(1024) >= lib.gptq_prepare_hinv_workspace(1024)
+    c128 = P.make_config(group_size=128)
+    assert lib.gptq_quantize_layer_factored_workspace(8, 1024, ctypes.byref(c128)) >= \
+        lib.gptq_quantize_layer_workspace(8, 1024, ctypes.byref(c128)) + 8 * 1024 * 8
+    for g, ok in ((128, True), (64, True), (8, True), (-1, True), (4096, True), (96, False), (256, False),
+                  (4, False)):
+        cg = P.make_config(group_size=g)
+        assert (lib.gptq_quantize_layer_factored_workspace(8, 1024, ctypes.byref(cg)) > 0) == ok, g
+    assert lib.gptq_quantize_layer_factored_workspace(
+        8, 1024, ctypes.byref(P.make_config(group_size=256, static_groups=True))) > 0
+    assert lib.gptq_quantize_layer_factored_workspace(8, 1024, ctypes.byref(P.make_config(block=64))) == 0
     assert lib.gptq_packed_words_per_row(11, 3) == 2
     assert lib.gptq_packed_words_per_row(8, 4) == 1
     assert lib.gptq_packed_words_per_row(8, 5) == -1
@@ -92,6 +105,19 @@ def test_argument_validation_before_any_launch():
     neg = P.make_config(damp=-0.1)
     args = [fake, 2, 8, 384, 384, fake, fake, ctypes.byref(neg), fake, fake, fake, fake, n, n, fake, 1 << 30, n]
     assert lib.gptq_quantize_layer(*args) == _lib.ERR_INVALID_ARG
+    # the factored form: 128-column blocks only, every group inside one block
+    assert lib.gptq_prepare_hinv_factored(fake, 1000, ctypes.byref(c), fake, fake, 1 << 40, n) == \
+        _lib.ERR_UNSUPPORTED
+    assert lib.gptq_prepare_hinv_factored(n, 1024, ctypes.byref(c), fake, fake, 1 << 40, n) == _lib.ERR_INVALID_ARG
+    assert lib.gptq_prepare_hinv_factored(fake, 1024, ctypes.byref(c), fake, fake, 16, n) == _lib.ERR_WORKSPACE
+    for bad_cfg in (P.make_config(group_size=96), P.make_config(block=64), P.make_config(group_size=4)):
+        args = [fake, 2, 8, 1024, 1024, fake, fake, ctypes.byref(bad_cfg), fake, fake, fake, fake, n, n, fake,
+                1 << 40, n]
+        assert lib.gptq_quantize_layer_factored(*args) == _lib.ERR_UNSUPPORTED
+    args = [fake, 2, 8, 1000, 1000, fake, fake, ctypes.byref(c), fake, fake, fake, fake, n, n, fake, 1 << 40, n]
+    assert lib.gptq_quantize_layer_factored(*args) == _lib.ERR_UNSUPPORTED   # d_in not a multiple of 128
+    args = [fake, 2, 8, 1024, 1024, fake, fake, ctypes.byref(c), fake, fake, fake, fake, n, n, fake, 10, n]
+    assert lib.gptq_quantize_layer_factored(*args) == _lib.ERR_WORKSPACE
     assert lib.gptq_pack(n, 4, 8, 4, fake, n) == _lib.ERR_INVALID_ARG
     assert lib.gptq_pack(fake, 4, 8, 5, fake, n) == _lib.ERR_INVALID_ARG
     assert lib.gptq_pack(fake, 0, 8, 4, fake, n) == _lib.ERR_INVALID_ARG

@@ -166,7 +166,7 @@ def test_fc2_full_size_solver():
     H0 = H.clone()
     torch.cuda.synchronize()
     t0 = time.time()
-    out = P.quantize(W, H=H, cfg=cfg)
+    out = P.quantize(W, H=H, cfg=cfg, factored=False)  # U is read back below
     torch.cuda.synchronize()
     print(f"fc2 prepare + quantize + pack on the GPU {time.time() - t0:.1f} s", flush=True)
 

@@ -176,7 +176,7 @@ constexpr size_t CONVERT_LDS_MAX = 64 * 1024;
 __global__ __launch_bounds__(256) void convert_rows_lds_kernel(const void* __restrict__ W, gptq_dtype dt,
                                                                int64_t d_in, int64_t ld_w,
                                                                const int32_t* __restrict__ perm, double* Wwork,
-                                                               double* loss64, int* flags) {
+                                                               double* loss64, int* flags, double* W0) {
     extern __shared__ uint32_t crow[];
     const int64_t r = blockIdx.x;
     const int tid = threadIdx.x;
@@ -207,6 +207,7 @@ __global__ __launch_bounds__(256) void convert_rows_lds_kernel(const void* __res
         const double v = load_as_f64(crow, p, dt);
         nonfinite |= !isfinite(v);
         Wwork[r * d_in + k] = v;
+        if (W0) W0[r * d_in + k] = v;   // factored form: the weights before the sweep
     }
     if (bad_perm) raise_flag(flags, FLAG_BAD_PERM);
     if (nonfinite) raise_flag(flags, FLAG_NONFINITE);
@@ -367,9 +368,9 @@ __device__ __forceinline__ double row_max16(double x) {
 
 // FACT (the factored form of the lazy updates): the stored per-column value
 // is W0_c - q_c (W0: the weights before the sweep) instead of the scaled
-// error.  The owner lane stores q_c in the column loop (one store, no extra
-// register live across the loop: a register copy of q or of W0 pushed the
-// kernel past 256 VGPRs) and the epilogue subtracts it from W0.
+// error.  The owner lane keeps q_c in a register of its own (pinned by an
+// empty asm: without it the compiler's schedule for the unrolled loop grew
+// past 256 VGPRs) and the epilogue subtracts it from W0.
 template <int SEG, bool FULL, bool STATIC, bool FACT = false>
 __global__ __launch_bounds__(SWAVES * 64) void sweep_block_kernel(double* __restrict__ Wwork, int64_t d_out, int64_t d_in,
                                                          int64_t i1, int nb, const double* __restrict__ U,
@@ -412,7 +413,7 @@ __global__ __launch_bounds__(SWAVES * 64) void sweep_block_kernel(double* __rest
     double scale = (rem != 0 && live) ? scale_in : 1.0, zero = (rem != 0 && live) ? zero_in : 0.0, rscale = 1.0;
     // static groups: the parameters of this lane's columns (the group of
     // each sweep column, then that group's scale and zero for this row)
-    double sc[STATIC ? CPL : 1], ze[STATIC ? CPL : 1], rsc[STATIC ? CPL : 1];
+    double sc[STATIC ? CPL : 1], ze[STATIC ? CPL : 1];
     if constexpr (STATIC) {
         int32_t gc[CPL];
 #pragma unroll
@@ -481,10 +482,6 @@ __global__ __launch_bounds__(SWAVES * 64) void sweep_block_kernel(double* __rest
     static_assert(BMAX <= SWAVES * 64, "one diagonal entry per thread");
     if (tid < nb) rinv[tid] = 1.0 / udiag;
     if (rem != 0 && live) rscale = 1.0 / scale;
-    if constexpr (STATIC) {
-#pragma unroll
-        for (int mm = 0; mm < CPL; ++mm) rsc[mm] = 1.0 / sc[mm];
-    }
     __syncthreads();
     // U row c's entries for this lane's registers m' >= c / 16
     auto load_urow = [&](double (&u)[CPL], int c) __attribute__((always_inline)) {
@@ -499,6 +496,7 @@ __global__ __launch_bounds__(SWAVES * 64) void sweep_block_kernel(double* __rest
     int next_gs = (int)(rem == 0 ? 0 : g - rem);      // block column of the next group start
     int64_t next_gi = i1 / g + (rem == 0 ? 0 : 1);  // and its group index
 
+    double qr[FACT ? CPL : 1] = {};   // FACT: q of this lane's columns
     // U rows of the next two columns in registers
     double ua[CPL], ub[CPL];
     load_urow(ua, 0);
@@ -580,19 +578,28 @@ __global__ __launch_bounds__(SWAVES * 64) void sweep_block_kernel(double* __rest
         // this column's grid (static groups: the owner lane's column m)
         const double cs = STATIC ? sc[STATIC ? m : 0] : scale;
         const double cz = STATIC ? ze[STATIC ? m : 0] : zero;
-        const double cr = STATIC ? rsc[STATIC ? m : 0] : rscale;
-        const double y = x * cr;
-        const double ry = rint(y);
-        double code = fmin(fmax(ry + cz, 0.0), qp.maxq);
-        double t = (x - cs * (code - cz)) * ri;
-        // the common path's result is formed before the rare branch, which
-        // then stays off the dependency chain
-        asm volatile("" : "+v"(t), "+v"(code));
-        // distance of y to the nearest half-integer: 0.5 - |y - rint(y)| (exact)
-        if (fabs(y - ry) >= fma(-0x1p-40, fmax(1.0, fabs(y)), 0.5)) {
-            asm volatile("");   // a real branch: the division is not worth computing in every column
+        double code, t;
+        if constexpr (STATIC) {
+            // static groups: the quotient in every column.  With a grid per
+            // column the rare branch below made the compiler keep the 128
+            // columns' values live across it (256 VGPRs, 256 AGPRs and
+            // scratch spills, 16.0 ms for the headline layer's sweep).
             code = fmin(fmax(rint(x / cs) + cz, 0.0), qp.maxq);
             t = (x - cs * (code - cz)) * ri;
+        } else {
+            const double y = x * rscale;
+            const double ry = rint(y);
+            code = fmin(fmax(ry + cz, 0.0), qp.maxq);
+            t = (x - cs * (code - cz)) * ri;
+            // the common path's result is formed before the rare branch, which
+            // then stays off the dependency chain
+            asm volatile("" : "+v"(t), "+v"(code));
+            // distance of y to the nearest half-integer: 0.5 - |y - rint(y)| (exact)
+            if (fabs(y - ry) >= fma(-0x1p-40, fmax(1.0, fabs(y)), 0.5)) {
+                asm volatile("");   // a real branch: the division is not worth computing in every column
+                code = fmin(fmax(rint(x / cs) + cz, 0.0), qp.maxq);
+                t = (x - cs * (code - cz)) * ri;
+            }
         }
         const bool own = p == j;
         // the owner's scaled error to its whole row (DPP row broadcast)
@@ -610,9 +617,9 @@ __global__ __launch_bounds__(SWAVES * 64) void sweep_block_kernel(double* __rest
             if (mm >= m) w[mm] = fma(-err, u[mm], w[mm]);
         if (c + 1 < BMAX) xn = w[(c + 1) / LPR];
         if constexpr (FACT) {
-            // q of the column to its place in Err now (the owner lane); the
-            // epilogue turns it into W0 - q
-            if (own && live) Err[row * ldE + errc + c] = cs * (code - cz);
+            // the owner keeps q of its column (off the dependency chain)
+            qr[FACT ? m : 0] = own ? cs * (code - cz) : qr[FACT ? m : 0];
+            asm volatile("" : "+v"(qr[FACT ? m : 0]));
         }
         w[m] = own ? err : w[m];
         if (c + 2 < BMAX) {
@@ -626,7 +633,7 @@ __global__ __launch_bounds__(SWAVES * 64) void sweep_block_kernel(double* __rest
         asm volatile("" ::: "memory");
     });
 
-    // errors (FACT: W0 - q, W0 read now) and codes of this row's columns back to HBM
+    // errors (FACT: W0 - q) and codes of this row's columns back to HBM
     if (live) {
         double* erow = Err + row * ldE + errc;
         uint8_t* crow = codes_s + row * d_in + i1;
@@ -635,9 +642,7 @@ __global__ __launch_bounds__(SWAVES * 64) void sweep_block_kernel(double* __rest
         for (int mm = 0; mm < CPL; ++mm) {
             const int col = p + LPR * mm;
             if (FULL || col < nb) {
-                // FACT: this lane stored q of its own columns above (a
-                // thread reads its own earlier stores)
-                erow[col] = FACT ? w0row[col] - erow[col] : w[mm];
+                erow[col] = FACT ? w0row[col] - qr[FACT ? mm : 0] : w[mm];
                 crow[col] = (uint8_t)(pk[mm >> 2] >> (8 * (mm & 3)));
             }
         }
@@ -754,13 +759,13 @@ gptq_status sweep_launch(const void* W, gptq_dtype dt, int64_t d_out, int64_t d_
     if (row_bytes <= CONVERT_LDS_MAX) {
         const size_t lds = align_up(row_bytes, 4);
         hipLaunchKernelGGL(convert_rows_lds_kernel, dim3((unsigned)d_out), dim3(256), lds, s, W, dt, d_in, ld_w, perm,
-                           w.Wwork, w.loss64, w.flags);
+                           w.Wwork, w.loss64, w.flags, w.W0);
     } else {
         hipLaunchKernelGGL(convert_kernel, dim3(gx, (unsigned)d_out), dim3(256), 0, s, W, dt, d_out, d_in, ld_w, perm,
                            w.Wwork, w.loss64, w.flags);
     }
     GPTQ_LAUNCH_CHECK();
-    if (factored)
+    if (factored && row_bytes > CONVERT_LDS_MAX)
         GPTQ_HIP(hipMemcpyAsync(w.W0, w.Wwork, (size_t)d_out * d_in * sizeof(double), hipMemcpyDeviceToDevice, s));
     hipLaunchKernelGGL(fill_neg_kernel, dim3(gx), dim3(256), 0, s, w.pinv, d_in);
     GPTQ_LAUNCH_CHECK();

@@ -142,7 +142,7 @@ gptq_status gptq_prepare_hinv(double* H, int64_t d_in, const gptq_config* cfg, i
 
 size_t gptq_prepare_hinv_factored_workspace(int64_t d_in) {
     if (d_in <= 0 || d_in > MAX_DIM || d_in % 128 != 0) return 0;
-    return hinv_workspace_bytes(d_in);
+    return hinv_workspace_bytes(d_in, true);
 }
 
 gptq_status gptq_prepare_hinv_factored(double* H, int64_t d_in, const gptq_config* cfg, int32_t* perm,
@@ -152,7 +152,7 @@ gptq_status gptq_prepare_hinv_factored(double* H, int64_t d_in, const gptq_confi
     gptq_status st = check_config(cfg);
     if (st != GPTQ_OK) return st;
     if (d_in % 128 != 0) return GPTQ_ERR_UNSUPPORTED;
-    if (!workspace || ws_bytes < hinv_workspace_bytes(d_in)) return GPTQ_ERR_WORKSPACE;
+    if (!workspace || ws_bytes < hinv_workspace_bytes(d_in, true)) return GPTQ_ERR_WORKSPACE;
     int flags[N_FLAGS] = {0, 0, 0, 0};
     st = hinv_launch(H, d_in, cfg, perm, workspace, stream, flags, true);
     if (st != GPTQ_OK) return st;

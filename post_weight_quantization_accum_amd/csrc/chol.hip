@@ -65,12 +65,13 @@ struct Ws {
     double* L;
     double* tmp[MAX_DEPTH];
     double* mrev;   // factored form: the diagonal blocks of M, columns reversed
+    double* lst;    // factored form: the off-diagonal blocks of L (row stride d)
 };
 
 // Layout: flags/lambda | diag (d doubles) | pinv (d ints) | Hr (d*d) | one L21
-// scratch per depth | the diagonal blocks of M (factored form); returns the
-// total size.
-size_t layout(int64_t d, Ws* w, char* p) {
+// scratch per depth | factored form: the diagonal blocks of M, the factor's
+// off-diagonal blocks (d*d); returns the total size.
+size_t layout(int64_t d, Ws* w, char* p, bool factored) {
     size_t off = 256;
     if (w) w->diag = (double*)(p + off);
     off = align_up(off + (size_t)d * sizeof(double), 256);
@@ -84,8 +85,10 @@ size_t layout(int64_t d, Ws* w, char* p) {
         if (w) w->tmp[k] = (double*)(p + off);
         off = align_up(off + sz[k] * sizeof(double), 256);
     }
-    if (w) w->mrev = (double*)(p + off);
-    off = align_up(off + (size_t)ceil_div(d, LEAF) * LEAF * LEAF * sizeof(double), 256);
+    if (w) w->mrev = factored ? (double*)(p + off) : nullptr;
+    if (factored) off = align_up(off + (size_t)ceil_div(d, LEAF) * LEAF * LEAF * sizeof(double), 256);
+    if (w) w->lst = factored ? (double*)(p + off) : nullptr;
+    if (factored) off = align_up(off + (size_t)d * (size_t)d * sizeof(double), 256);
     if (w) {
         w->flags = (int*)p;
         w->lambda = (double*)(p + 64);
@@ -582,7 +585,7 @@ struct Rec {
     int* flags = nullptr;
     hipEvent_t l21_ready[MAX_DEPTH] = {}, t_done[MAX_DEPTH] = {};
     int64_t t_wg = 0;   // workgroups of a T product
-    bool keep_l = false;
+    double* lst = nullptr;   // factored form: the factor's off-diagonal blocks (row stride d)
     // created on first use: factors of at most 1024 columns never need them
     hipError_t init() {
         if (side) return hipSuccess;
@@ -614,9 +617,9 @@ struct Rec {
 // M11 feeds the parent's L21).  Without it (the root and the right children
 // below it, in the factored form) T and M21 are skipped: only the diagonal
 // blocks of M, which the leaves form, are read afterwards.
-// c.keep_l (factored form): each node's L21 stays in A21's place for the
-// end; A21 is copied to the depth's scratch first (the product may not
-// write over its own operand) and T goes to that scratch instead.
+// c.lst (factored form): each node's L21 goes to its place in a d x d store
+// of the factor's off-diagonal blocks (read at the end) instead of the
+// depth's scratch.
 gptq_status chol_inv(Rec& c, int64_t o, int64_t n, int depth, bool need_m = true) {
     const int64_t d = c.d;
     if (n <= LEAF) {
@@ -632,26 +635,14 @@ gptq_status chol_inv(Rec& c, int64_t o, int64_t n, int depth, bool need_m = true
     const double* M11 = c.M + o * d + o;
     const double* M22 = c.M + (o + n1) * d + o + n1;
     double* M21 = c.M + (o + n1) * d + o;
-    const double* Asrc = A21;
-    int64_t ld_a = d;
-    double* L21 = c.tmp[depth];   // L21's place
-    int64_t ld_l = n1;
-    double* T = A21;              // T's place
-    int64_t ld_t = d;
+    double* const L21 = c.lst ? c.lst + (o + n1) * d + o : c.tmp[depth];
+    const int64_t ld_l = c.lst ? d : n1;
+    double* const T = A21;   // T replaces A21
+    const int64_t ld_t = d;
     gptq_status st = chol_inv(c, o, n1, depth + 1, true);
     if (st != GPTQ_OK) return st;
-    if (c.keep_l) {
-        GPTQ_HIP(hipMemcpy2DAsync(c.tmp[depth], (size_t)n1 * sizeof(double), A21, (size_t)d * sizeof(double),
-                                  (size_t)n1 * sizeof(double), (size_t)n2, hipMemcpyDeviceToDevice, c.s));
-        Asrc = c.tmp[depth];
-        ld_a = n1;
-        L21 = A21;
-        ld_l = d;
-        T = c.tmp[depth];
-        ld_t = n1;
-    }
     // L21 = A21 M11^T
-    st = launch_gemm_f64(c.s, n2, n1, n1, 1.0, Asrc, ld_a, M11, d, true, 0.0, L21, ld_l, false, GEMM_TRI_KEND_COL);
+    st = launch_gemm_f64(c.s, n2, n1, n1, 1.0, A21, d, M11, d, true, 0.0, L21, ld_l, false, GEMM_TRI_KEND_COL);
     if (st != GPTQ_OK) return st;
     if (n1 <= 512 && n2 <= 512) {
         // small node: A22 -= L21 L21^T and T = L21 M11 in one launch, all on
@@ -703,13 +694,13 @@ __global__ __launch_bounds__(256) void diag_blocks_rev_kernel(const double* __re
 
 }  // namespace
 
-size_t hinv_workspace_bytes(int64_t d) { return layout(d, nullptr, nullptr); }
+size_t hinv_workspace_bytes(int64_t d, bool factored) { return layout(d, nullptr, nullptr, factored); }
 
 gptq_status hinv_launch(double* H, int64_t d, const gptq_config* cfg, int32_t* perm, void* ws,
                         hipStream_t s, int* host_flags, bool factored) {
     if (factored && (d % LEAF) != 0) return GPTQ_ERR_UNSUPPORTED;
     Ws w;
-    layout(d, &w, (char*)ws);
+    layout(d, &w, (char*)ws, factored);
     GPTQ_HIP(ensure_lds_limit((const void*)leaf_blocked_kernel, (int)LEAF_LDS));
     GPTQ_HIP(hipMemsetAsync(w.flags, 0, 256, s));
 
@@ -741,13 +732,13 @@ gptq_status hinv_launch(double* H, int64_t d, const gptq_config* cfg, int32_t* p
     for (int k = 0; k < MAX_DEPTH; ++k) c.tmp[k] = w.tmp[k];
     c.d = d;
     c.flags = w.flags;
-    c.keep_l = factored;
+    c.lst = w.lst;
     gptq_status st = chol_inv(c, 0, d, 0, !factored);
     if (st != GPTQ_OK) return st;
     if (factored) {
         hipLaunchKernelGGL(diag_blocks_rev_kernel, dim3((unsigned)(d / LEAF)), dim3(256), 0, s, H, d, w.mrev);
         GPTQ_LAUNCH_CHECK();
-        st = launch_factor_blocks(s, w.L, w.mrev, H, d);
+        st = launch_factor_blocks(s, w.lst, w.mrev, H, d);
         if (st != GPTQ_OK) return st;
     } else {
         hipLaunchKernelGGL(rotate_inplace_kernel, dim3((unsigned)d), dim3(256), 0, s, H, d);

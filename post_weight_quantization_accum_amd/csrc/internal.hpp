@@ -84,7 +84,7 @@ gptq_status hessian_launch_scratch(double* H, const void* X, gptq_dtype dt, int6
 // Column order, damping, Cholesky of the reversed matrix, triangular inverse,
 // rotation into U; factored: the factored form F instead of U (d a multiple
 // of 128).  ws layout described in chol.hip.
-size_t hinv_workspace_bytes(int64_t d);
+size_t hinv_workspace_bytes(int64_t d, bool factored = false);
 gptq_status hinv_launch(double* H, int64_t d, const gptq_config* cfg, int32_t* perm,
                         void* ws, hipStream_t s, int* host_flags, bool factored = false);
 

@@ -14,9 +14,10 @@ and the blocked sweep):
   relative and the zero points equal.
 Layers: workload 3's headline down projection (4096x11008, bf16, 4-bit g128
 act-order, 1024 sampled rows; and with static groups, 512 rows), workload 4's down projection (5120x13824, 3-
-and 2-bit g64 act-order, 512 sampled rows each) and workload 2 at its recipe
+and 2-bit g64 act-order, 512 sampled rows each), workload 2 at its recipe
 (OPT-125m shapes 768x768, 3072x768 and 768x3072, fp16, 4-bit g128, every
-row).  Rows are independent given U, so a row sample is checked exactly as
+row) and workload 5's first layer (q, 12288x12288, fp16, 3-bit g128 natural
+order, from the block's input, 512 sampled rows).  Rows are independent given U, so a row sample is checked exactly as
 the whole layer would be.
 """
 import time
@@ -127,3 +128,20 @@ def test_workload2_from_x(name):
     H = _oracle_hessian(L)
     _check(L, H, got, q, f"workload 2 {name} {L.W.shape[0]}x{L.W.shape[1]} fp16 4-bit g128")
     assert WORKLOADS[2].n_tok == L.X.shape[0] == 262144
+
+
+@pytest.mark.timeout(900)
+def test_workload5_q_from_x():
+    """Workload 5's first layer at full size: the block's input X0 (262144
+    fp16 tokens, Student-t with 0.1% outlier channels x100), 12288 x 12288
+    fp16 weights, 3-bit g128 in natural order."""
+    wl, L = _layer(5, "q")
+    q = wl.quants[0]
+    assert L.X.shape == (262144, 12288) and L.W.shape == (12288, 12288)
+    got = _gpu_quantize(L, q)
+    t0 = time.time()
+    H = _oracle_hessian(L)
+    print(f"  oracle Hessian over {L.X.shape[0]} tokens in {time.time() - t0:.1f} s", flush=True)
+    assert np.array_equal(got["perm"], np.arange(L.W.shape[1]))
+    rows = np.sort(np.random.default_rng(6).choice(L.W.shape[0], 512, replace=False))
+    _check(L, H, got, q, "workload 5 q 12288x12288 fp16 3-bit g128", rows=rows)

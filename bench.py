@@ -5,7 +5,7 @@ zero H, Hessian accumulation over 262144 bf16 tokens, act-order + damping +
 Cholesky/inverse, the blocked column sweep with lazy updates (4-bit, group
 128), and packing.  Prints one JSON line (see the keys below).
 
-    python bench.py [--gpus 1] [--steps 5] [--warmup 2] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--no-cpu-baseline]
     python bench.py --workload dequant [--steps 5] [--no-cpu-baseline]
 
 The second form measures the product with the packed layer instead (decode:
@@ -77,8 +77,8 @@ def log(msg):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=5)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dequant", action="store_true", help="skip the summary of the packed-layer product")
     ap.add_argument("--tokens", type=int, default=None, help="override the token count (testing only)")
@@ -545,6 +545,7 @@ def main():
     wall = time.perf_counter() - t_start
     ms_per_step = wall * 1000.0 / a.steps
     phases = {k: float(np.mean(v)) for k, v in phase_ms.items()}
+    phases_median = {k: float(np.median(v)) for k, v in phase_ms.items()}
 
     # Dominant kernel: the Hessian product (hess_tile_kernel).  One launch
     # runs up to 1792 (256x128 tile, 32768-token window) work items; the
@@ -588,6 +589,7 @@ def main():
                    "act_order": bool(q.act_order), "parallelism": "single GPU",
                    "hinv_form": "factored" if factored else "U"},
         "phases_ms": {k: round(v, 3) for k, v in phases.items()},
+        "phases_ms_median": {k: round(v, 3) for k, v in phases_median.items()},
         "solver_only_ms": round(phases["prepare_hinv"] + phases["quantize_layer"] + phases["pack"], 3),
         "phase_roofline": phase_rooflines(d_out, d_in, n_tok, q.bits, q.block, phases, factored=factored),
         "roofline": roofline,

@@ -331,8 +331,12 @@ gptq_status gptq_pack_permuted(const uint8_t* codes, int64_t d_out, int64_t d_in
 /* Column gather Xg[t][k] = X[t][perm[k]] ("GPTQ量化算法深度解析" §3.3:
  * act-order puts a gather in front of inference).  With the words from
  * gptq_pack_permuted, gptq_dequant_matmul(Xg, ..., perm = NULL, g_idx =
- * NULL) computes the same product as with perm, and from 128 tokens on it
- * takes the matrix-core route.  X: device, n_tok x d_in, row stride ld_x;
+ * NULL) computes the same product as with perm, and from 2 tokens on it
+ * takes the matrix-core routes (with perm, gptq_dequant_matmul reads the
+ * activations through perm token by token): for 2 or more tokens the gather
+ * followed by the product without perm is the faster form (at 4096 x 11008,
+ * 4-bit g128: 24 us against 99 us for 16 tokens).  X: device, n_tok x d_in,
+ * row stride ld_x;
  * Xg: device, n_tok x d_in, row stride ld_g (caller-owned, not aliasing X);
  * both of x_dtype.  perm entries outside [0, d_in) give NaN.
  * Errors: GPTQ_ERR_INVALID_ARG for a bad dtype, sizes, strides or a null

@@ -266,7 +266,9 @@ def dequant_matmul(X, packed, bits: int, scales, zeros, *, g_idx=None, perm=None
     X: tokens x d_in (bf16 / f16 / f32, unit column stride); packed: d_out x
     words-per-row int32/uint32 words; scales, zeros: [n_groups][d_out] float32.
     g_idx (original order) or perm (words from pack_permuted) select the
-    column order, as in gptq_dequant_matmul.
+    column order, as in gptq_dequant_matmul.  With perm and two or more
+    tokens, dequant_matmul(gather_columns(X, perm), packed, ...) without perm
+    is the faster form (the matrix-core routes read activations in order).
     """
     lib = load()
     torch = _torch()

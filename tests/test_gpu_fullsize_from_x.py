@@ -77,31 +77,35 @@ def _check(L, H, got, q, name, rows=None, static_groups=False):
     return rp
 
 
-@pytest.mark.timeout(900)
-def test_headline_down_from_x():
+@pytest.fixture(scope="module")
+def headline_inputs():
+    """The headline layer's inputs and the oracle's float64 Hessian of its
+    262144 tokens, computed once for the tests that share them."""
     cfg_id, name = HEADLINE
     wl, L = _layer(cfg_id, name)
-    q = wl.quants[0]
-    got = _gpu_quantize(L, q)
     t0 = time.time()
     H = _oracle_hessian(L)
     print(f"  oracle Hessian over {L.X.shape[0]} tokens in {time.time() - t0:.1f} s", flush=True)
+    return wl, L, H
+
+
+@pytest.mark.timeout(900)
+def test_headline_down_from_x(headline_inputs):
+    wl, L, H = headline_inputs
+    q = wl.quants[0]
+    got = _gpu_quantize(L, q)
     rows = np.sort(np.random.default_rng(3).choice(L.W.shape[0], 1024, replace=False))
     _check(L, H, got, q, "workload 3 down 4096x11008 4-bit g128 act-order", rows=rows)
 
 
 @pytest.mark.timeout(900)
-def test_headline_down_static_groups_from_x():
+def test_headline_down_static_groups_from_x(headline_inputs):
     """The headline layer with the static-groups option (groups of original
     columns, parameters from W before the sweep, act-order sweep order)."""
-    cfg_id, name = HEADLINE
-    wl, L = _layer(cfg_id, name)
+    wl, L, H = headline_inputs
     q = wl.quants[0]
     got = _gpu_quantize(L, q, static_groups=True)
     assert np.array_equal(got["g_idx"], np.arange(L.W.shape[1]) // q.group_size)
-    t0 = time.time()
-    H = _oracle_hessian(L)
-    print(f"  oracle Hessian over {L.X.shape[0]} tokens in {time.time() - t0:.1f} s", flush=True)
     rows = np.sort(np.random.default_rng(5).choice(L.W.shape[0], 512, replace=False))
     _check(L, H, got, q, "workload 3 down 4096x11008 4-bit g128 act-order, static groups", rows=rows,
            static_groups=True)

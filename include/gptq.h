@@ -317,9 +317,10 @@ gptq_status gptq_pack_permuted(const uint8_t* codes, int64_t d_out, int64_t d_in
  * a group size that is a multiple of 32 (or one group), the codes enter
  * half-precision dot products exactly as 2^bits + c and the offset is
  * removed per 32 columns in float32 (8-bit codes with bf16 activations take
- * the per-column route); from 128 tokens on, without perm, the same values
- * go through the matrix cores with float32 sums per group; otherwise each
- * weight is formed once in float32.
+ * the per-column route); from 2 tokens on, without perm, the same values
+ * go through the matrix cores with float32 sums per group (16 rows x 16-64
+ * tokens per workgroup below 128 tokens, 128 x 128 tiles from 128 on);
+ * otherwise each weight is formed once in float32.
  * Errors (before any launch): GPTQ_ERR_INVALID_ARG for a bad dtype or bits,
  * sizes outside [0, 2^20] (d_in >= 1), ld_x < d_in, ld_y < d_out, both perm
  * and g_idx given, an n_groups that does not match, or a null pointer;

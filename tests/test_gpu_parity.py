@@ -415,6 +415,43 @@ def test_static_groups_end_to_end(d_out, d_in, n, dtype, bits, g):
     assert np.all(np.abs(Y.cpu().numpy() - want) <= tol)
 
 
+@pytest.mark.parametrize("factored", [True, False])
+@pytest.mark.parametrize("d_out,d_in,n,dtype,bits,g,act", [
+    (1, 256, 1024, "bf16", 4, 128, True),    # one row: one workgroup with a single live row
+    (3, 128, 300, "f16", 3, 64, False),      # one block: no lazy update at all
+    (2, 128, 200, "bf16", 2, -1, True),      # one block, one group per row
+])
+def test_degenerate_layers(d_out, d_in, n, dtype, bits, g, act, factored):
+    print(f"degenerate {d_out}x{d_in} n={n} {dtype} b{bits} g{g} act{act} factored {factored}", flush=True)
+    L = _layer(d_out, d_in, n, dtype=dtype, frac=0.01, scale=30.0, seed=d_in + d_out)
+    ref = O.gptq_quantize(L.W_f64(), X=L.X_f64(), bits=bits, group_size=g, act_order=act)
+    cfg = P.make_config(bits=bits, group_size=g, act_order=act)
+    out = P.quantize(to_torch(L.W, dtype), X=to_torch(L.X, dtype), cfg=cfg, factored=factored)
+    torch.cuda.synchronize()
+    got = {k: v.cpu().numpy() for k, v in out.items()}
+    assert got["codes"].shape == (d_out, d_in)
+    assert np.array_equal(got["packed"].view(np.uint32), O.pack(got["codes"], bits))
+    assert_from_x_parity(O, L.W_f64(), ref["H"], got, bits, g, act, name=f"degenerate {d_out}x{d_in}")
+
+
+def test_hessian_empty_and_single_token():
+    # no tokens: H unchanged (nothing launched); one token: the outer product
+    L = _layer(4, 200, 1, seed=5)
+    X1 = to_torch(L.X, "bf16")
+    H = torch.full((200, 200), 0.25, dtype=torch.float64, device=DEV)
+    P.hessian_accumulate(H, X1[:0])
+    torch.cuda.synchronize()
+    assert torch.all(H == 0.25)
+    P.hessian_accumulate(H, X1)
+    torch.cuda.synchronize()
+    x = L.X_f64()[0]
+    want = 0.25 + 2.0 * np.outer(x, x)
+    got = H.cpu().numpy()
+    iu = np.triu_indices(200)
+    # bf16 products are exact in float32 and one token is one product per entry
+    np.testing.assert_allclose(got[iu], want[iu], rtol=1e-15, atol=0)
+
+
 def test_scale_invariance_and_row_subset_on_gpu():
     L = _layer(64, 256, 3000, seed=11)
     H = O.hessian(L.X_f64())

@@ -482,8 +482,12 @@ __global__ __launch_bounds__(256) void repack_kernel(const uint16_t* __restrict_
 }
 
 // fp32 activations: float64 products and sums.  64x64 tiles of the upper
-// triangle, 256 threads, each thread a 4x4 block, 16 tokens per stage.
-constexpr int FT = 64, FK = 16;
+// triangle, 256 threads, each thread a 4x4 block, 32 tokens per stage; the
+// next stage's loads are in flight while the current one is multiplied
+// (each thread's elements of a stage go through registers), so a stage
+// costs its arithmetic rather than a memory round trip.
+constexpr int FT = 64, FK = 32;
+constexpr int FE = FK * FT / 256;   // elements of one operand per thread and stage
 
 __global__ __launch_bounds__(256) void hess_f32_kernel(double* __restrict__ H, const float* __restrict__ X,
                                                        int64_t n_tok, int64_t d, int64_t ld) {
@@ -500,16 +504,31 @@ __global__ __launch_bounds__(256) void hess_f32_kernel(double* __restrict__ H, c
     }
     const int t = threadIdx.x;
     const int ty = t >> 4, tx = t & 15;
-    double acc[4][4] = {};
-    for (int64_t t0 = 0; t0 < n_tok; t0 += FK) {
-        for (int e = t; e < FK * FT; e += 256) {
+    // element q of this thread in a stage: token row k = e / FT, column c = e % FT
+    auto load = [&](int64_t t0, float (&va)[FE], float (&vb)[FE]) {
+#pragma unroll
+        for (int q = 0; q < FE; ++q) {
+            const int e = t + 256 * q;
             const int k = e / FT, c = e % FT;
             const int64_t tok = t0 + k;
             const int64_t ca = ti * FT + c, cb = tj * FT + c;
-            sA[k][c] = (tok < n_tok && ca < d) ? (double)X[tok * ld + ca] : 0.0;
-            sB[k][c] = (tok < n_tok && cb < d) ? (double)X[tok * ld + cb] : 0.0;
+            const bool tok_ok = tok < n_tok;
+            va[q] = (tok_ok && ca < d) ? X[tok * ld + ca] : 0.0f;
+            vb[q] = (tok_ok && cb < d) ? X[tok * ld + cb] : 0.0f;
+        }
+    };
+    double acc[4][4] = {};
+    float va[FE], vb[FE];
+    load(0, va, vb);
+    for (int64_t t0 = 0; t0 < n_tok; t0 += FK) {
+#pragma unroll
+        for (int q = 0; q < FE; ++q) {
+            const int e = t + 256 * q;
+            sA[e / FT][e % FT] = (double)va[q];
+            sB[e / FT][e % FT] = (double)vb[q];
         }
         __syncthreads();
+        if (t0 + FK < n_tok) load(t0 + FK, va, vb);
 #pragma unroll
         for (int k = 0; k < FK; ++k) {
             double av[4], bv[4];

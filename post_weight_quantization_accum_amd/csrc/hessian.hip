@@ -85,6 +85,7 @@ constexpr int BAND = 4;                        // row blocks per band of the til
 #endif
 constexpr int64_t WIN_MAX = GPTQ_HWIN / RUN_TOK * RUN_TOK;   // tokens per window (full mode)
 constexpr int64_t PART_TILES = 256;            // fewer tiles: partial-tile mode
+constexpr int64_t ROUND = 256;                 // work items that run at once (one workgroup per CU)
 constexpr size_t PART_ELEMS = (size_t)TR * TC + TR;   // one partial tile + its diagonal sums
 constexpr size_t REPACK_BYTES = (size_t)64 << 20;     // aligned copy of a misaligned input
 
@@ -587,11 +588,19 @@ Plan make_plan(int64_t n_tok, int64_t d, int64_t win_cap, int64_t max_items) {
     p.partial = p.g.n_tiles < PART_TILES && (max_items == 0 || max_items >= p.g.n_tiles);
     int64_t win = WIN_MAX;
     if (p.partial) {
-        int64_t nw = ceil_div(512, p.g.n_tiles);
+        // at most about 512 items (and no more than the runs or the
+        // budget allow); among those window counts, the one whose rounds
+        // of ROUND items (one workgroup per CU) cost least: the time goes
+        // as ceil(nw T / ROUND) rounds of n_tok / nw tokens each
+        const int64_t T = p.g.n_tiles;
+        int64_t nw_max = ceil_div(512, T);
         const int64_t runs = ceil_div(n_tok, RUN_TOK);
-        if (nw > runs) nw = runs;
-        if (max_items > 0 && nw > max_items / p.g.n_tiles) nw = max_items / p.g.n_tiles;
-        if (nw < 1) nw = 1;
+        if (nw_max > runs) nw_max = runs;
+        if (max_items > 0 && nw_max > max_items / T) nw_max = max_items / T;
+        if (nw_max < 1) nw_max = 1;
+        int64_t nw = 1;
+        for (int64_t c = 2; c <= nw_max; ++c)
+            if (ceil_div(c * T, ROUND) * nw < ceil_div(nw * T, ROUND) * c) nw = c;   // cost(c) < cost(nw)
         win = ceil_div(ceil_div(n_tok, nw), RUN_TOK) * RUN_TOK;
     }
     if (win > win_cap) win = win_cap;
